@@ -1,0 +1,124 @@
+"""Planted mistakes in the oracle (on the CPU) must each fail at least one pin.
+
+Each mutation replaces one oracle function by a plausible wrong version (a
+dropped term, a wrong constant, a transposed operand, a wrong rounding) and
+runs the pins that should notice it.
+"""
+
+import numpy as np
+import pytest
+
+import oracle as O
+import oracle.bitlinear_oracle as B
+from tests import test_oracle_pins as P
+
+
+def _gamma_no_abs(w):
+    a = np.asarray(w, dtype=np.float64).ravel()
+    return np.float32(max(np.float32(np.mean(a)), B.EPS_W))
+
+
+def _gamma_max(w):
+    return np.float32(np.max(np.abs(np.asarray(w, dtype=np.float64))))
+
+
+def _codes_threshold_gamma(w, gamma):
+    w = np.asarray(w, dtype=np.float64)
+    return np.where(np.abs(w) > gamma, np.sign(w), 0).astype(np.int8)
+
+
+def _codes_round_half_up(w, gamma):
+    q = np.floor(np.asarray(w, dtype=np.float64) / np.float64(gamma) + 0.5)
+    return np.clip(q, -1, 1).astype(np.int8)
+
+
+def _pack_msb_first(q, Kp=None):
+    q = np.asarray(q, dtype=np.int64)
+    N, K = q.shape
+    Kp = B.k_pad(K) if Kp is None else Kp
+    full = np.zeros((N, Kp), dtype=np.int64)
+    full[:, :K] = q
+    f = (full & 3).reshape(N, Kp // 4, 4)
+    return (f[..., 3] | (f[..., 2] << 2) | (f[..., 1] << 4) | (f[..., 0] << 6)).astype(np.uint8)
+
+
+def _act_128(x, Kp=None):
+    x = np.asarray(x, dtype=np.float64)
+    M, K = x.shape
+    Kp = B.k_pad(K) if Kp is None else Kp
+    s = np.maximum(np.max(np.abs(x), axis=1).astype(np.float32), B.EPS_X)
+    q = np.clip(np.rint(128.0 * x / s[:, None]), -127, 127)
+    out = np.zeros((M, Kp), dtype=np.int8)
+    out[:, :K] = q
+    return out, s
+
+
+def _act_trunc(x, Kp=None):
+    x = np.asarray(x, dtype=np.float64)
+    M, K = x.shape
+    Kp = B.k_pad(K) if Kp is None else Kp
+    s = np.maximum(np.max(np.abs(x), axis=1).astype(np.float32), B.EPS_X)
+    q = np.clip(np.trunc(127.0 * x / s[:, None]), -127, 127)
+    out = np.zeros((M, Kp), dtype=np.int8)
+    out[:, :K] = q
+    return out, s
+
+
+def _y_no_127(acc, s, gamma):
+    return np.asarray(acc, np.float64) * np.asarray(s, np.float64)[:, None] * np.float64(gamma)
+
+
+def _backward_dw_swapped(dY, x_q, s, q, gamma):
+    K = np.asarray(q).shape[1]
+    dY = np.asarray(dY, dtype=np.float64)
+    xh = B.x_hat(x_q, s, K)
+    dX = dY @ B.w_hat(q, gamma)
+    dW = (dY.T @ xh)[::-1]  # rows of dW in the wrong order
+    return dX, dW
+
+
+def _backward_dx_fp32_gamma(dY, x_q, s, q, gamma):
+    K = np.asarray(q).shape[1]
+    dY = np.asarray(dY, dtype=np.float64)
+    dX = dY @ (np.asarray(q, np.float64) * np.float64(gamma))  # bf16(gamma) dropped
+    dW = dY.T @ B.x_hat(x_q, s, K)
+    return dX, dW
+
+
+def _xhat_unrounded(x_q, s, K):
+    return np.asarray(x_q)[:, :K].astype(np.float64) * np.asarray(s, np.float64)[:, None] / 127.0
+
+
+def _bf16_trunc(v):
+    v = np.asarray(v, dtype=np.float64)
+    m, e = np.frexp(v)
+    return np.ldexp(np.trunc(np.ldexp(m, 8)), e - 8)
+
+
+MUTATIONS = [
+    ("absmean_gamma", _gamma_no_abs, ["test_gamma_closed_forms", "test_codes_zero_fraction_statistics"]),
+    ("absmean_gamma", _gamma_max, ["test_gamma_closed_forms", "test_codes_zero_fraction_statistics"]),
+    ("ternary_codes", _codes_threshold_gamma, ["test_codes_hand_examples_and_ties", "test_codes_vs_fraction_bruteforce"]),
+    ("ternary_codes", _codes_round_half_up, ["test_codes_hand_examples_and_ties", "test_codes_vs_fraction_bruteforce"]),
+    ("pack_codes", _pack_msb_first, ["test_pack_hand_bytes"]),
+    ("act_quant", _act_128, ["test_act_quant_invariants", "test_act_quant_exhaustive_bf16_significands"]),
+    ("act_quant", _act_trunc, ["test_act_quant_vs_fraction_and_ties", "test_act_quant_exhaustive_bf16_significands"]),
+    ("forward_y", _y_no_127, ["test_y_dx_dw_exact_fractions", "test_against_torch_autograd_detach_ste"]),
+    ("backward", _backward_dw_swapped, ["test_backward_one_hot_dY_selects_rows", "test_y_dx_dw_exact_fractions"]),
+    ("backward", _backward_dx_fp32_gamma, ["test_y_dx_dw_exact_fractions", "test_against_torch_autograd_detach_ste"]),
+    ("x_hat", _xhat_unrounded, ["test_y_dx_dw_exact_fractions"]),
+    ("bf16_round", _bf16_trunc, ["test_bf16_round_matches_exact_rounding", "test_bf16_bits_roundtrip"]),
+]
+
+
+@pytest.mark.parametrize("name,fn,pins", MUTATIONS, ids=[f"{m[0]}:{m[1].__name__}" for m in MUTATIONS])
+def test_planted_mistake_is_caught(monkeypatch, name, fn, pins):
+    monkeypatch.setattr(B, name, fn)
+    monkeypatch.setattr(O, name, fn)
+    caught = []
+    for pin in pins:
+        try:
+            getattr(P, pin)()
+        except (AssertionError, ValueError):
+            caught.append(pin)
+    assert caught, f"mutation {fn.__name__} of {name} passed every pin in {pins}"
