@@ -1,0 +1,241 @@
+"""Benchmark: one BitLinear forward + STE backward step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--rotate R] [--no-cpu-baseline]
+
+A step is the whole hot path on one batch: ternarize + pack the master
+weights, int8-quantize the activations, the INT8 forward GEMM, and the two
+bf16 STE backward GEMMs (dX, dW), all through the C ABI of libbitnet.so on
+torch's current stream. Inputs are seeded synthetic tensors of the
+4096 x 2560 -> 6912 layer (x, dY ~ N(0,1) bf16, W ~ U(+-1/sqrt(2560)) bf16),
+resident in HBM before timing starts. R independent copies of all buffers
+are rotated step by step so that the working set (~240 MB per copy) does not
+sit in the 256 MB Infinity Cache between steps.
+
+Prints one JSON line: throughput in effective TOPS (6*M*N*K per step), the
+step time, per-kernel times from HIP events recorded on the launch stream,
+the roofline of the dominant kernel, and the CPU oracle timed on a bounded
+sample of the same workload (rank 0 only).
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "BitLinear fwd+bwd ms & TOPS at 4096×2560→6912; % of MFMA peak"
+# MI355X published dense peaks (no sparsity).
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_INT8_TOPS = 5000.0
+PEAK_HBM_GBS = 8000.0
+# Effective TOPS of the pages' fused kernel at this workload on an NVIDIA L4
+# (8.80 ms for 6*M*N*K ops; context, other hardware).
+PAGES_L4_TOPS = 49.4
+
+KERNEL_SOURCES = ["gemm_kernels.hip", "quant_kernels.hip", "device_common.h"]
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="c2_up_4096x2560x6912")
+    p.add_argument("--rotate", type=int, default=4)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "ternary_weight_quantization_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_hash") != source_hash():
+        return None
+    e = d.get("kernels", {}).get(f"{kernel}@{workload}")
+    return None if e is None else e.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, rows):
+    """The oracle (as it stands) on a bounded sample of the workload: the
+    whole weight ternarization plus the first `rows` tokens through
+    act-quant, forward and both backward products."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle as O
+    from ternary_weight_quantization_amd import workloads as WL
+
+    M, K, N = inp["M"], inp["K"], inp["N"]
+    x = WL.bf16_bits_to_f32(inp["x"][:rows]).astype(np.float64)
+    dY = WL.bf16_bits_to_f32(inp["dY"][:rows]).astype(np.float64)
+    w = WL.bf16_bits_to_f32(inp["W"]).astype(np.float64)
+    t0 = time.perf_counter()
+    O.layer_fwd_bwd(x, w, dY)
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    ops = 6.0 * rows * N * K
+    return {
+        "value": ops / dt / 1e12,
+        "unit": "TOPS",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"full weight ternarization ({N}x{K}) + first {rows} of {M} tokens through "
+                  f"act-quant, forward and STE backward; {dt:.2f} s wall, {ops / 1e9:.1f} G ops "
+                  f"(6*rows*N*K) on {os.cpu_count()} visible cpus",
+        "seconds": dt,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (the layer is not sharded); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from ternary_weight_quantization_amd import binding as B
+    from ternary_weight_quantization_amd import workloads as WL
+
+    B.lib()
+    dev = torch.device("cuda:0")
+    inp = WL.layer_inputs(args.workload, seed=0)
+    M, K, N = inp["M"], inp["K"], inp["N"]
+    Kp = B.bitnet_k_pad(K)
+    wdt = torch.bfloat16 if inp["w_dtype"] == "bf16" else torch.float32
+
+    def to_dev(a, dtype):
+        if dtype == torch.bfloat16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    sets = []
+    base = dict(x=to_dev(inp["x"], torch.bfloat16), W=to_dev(inp["W"], wdt), dY=to_dev(inp["dY"], torch.bfloat16))
+    for r in range(args.rotate):
+        s = {k: v.clone() for k, v in base.items()}
+        s.update(
+            w_packed=torch.empty((N, Kp // 4), dtype=torch.uint8, device=dev),
+            gamma=torch.empty((1,), dtype=torch.float32, device=dev),
+            ws=torch.empty((B.bitnet_ternarize_workspace_bytes(N, K),), dtype=torch.uint8, device=dev),
+            x_q=torch.empty((M, Kp), dtype=torch.int8, device=dev),
+            s_x=torch.empty((M,), dtype=torch.float32, device=dev),
+            y=torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+            dX=torch.empty((M, K), dtype=torch.bfloat16, device=dev),
+            dW=torch.empty((N, K), dtype=wdt, device=dev),
+        )
+        sets.append(s)
+    del base
+    torch.cuda.synchronize()
+
+    names = ["ternarize_pack", "act_quant", "fwd_i8", "bwd_dx_bf16", "bwd_dw_bf16"]
+
+    def step(s, ev=None):
+        calls = [
+            lambda: B.bitnet_ternarize_pack(s["W"], s["w_packed"], s["gamma"], s["ws"]),
+            lambda: B.bitnet_act_quant(s["x"], s["x_q"], s["s_x"]),
+            lambda: B.bitlinear_fwd(s["x_q"], s["s_x"], s["w_packed"], s["gamma"], K, s["y"]),
+            lambda: B.bitlinear_bwd(s["dY"], s["x_q"], s["s_x"], s["w_packed"], s["gamma"], K, dX=s["dX"]),
+            lambda: B.bitlinear_bwd(s["dY"], s["x_q"], s["s_x"], s["w_packed"], s["gamma"], K, dW=s["dW"]),
+        ]
+        for i, c in enumerate(calls):
+            if ev is not None:
+                ev[i][0].record()
+            c()
+            if ev is not None:
+                ev[i][1].record()
+
+    for i in range(args.warmup):
+        step(sets[i % len(sets)])
+    torch.cuda.synchronize()
+
+    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in names]
+           for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        step(sets[i % len(sets)], evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    per_kernel = {n: float(np.mean([evs[i][j][0].elapsed_time(evs[i][j][1]) for i in range(args.steps)]))
+                  for j, n in enumerate(names)}
+
+    gemm_ops = 2.0 * M * N * K
+    tops = 3 * gemm_ops / (ms_per_step * 1e-3) / 1e12
+    # roofline of each kernel (algorithmic work per launch)
+    w_bytes = 2 if wdt == torch.bfloat16 else 4
+    roof = {
+        "fwd_i8": ("mfma", gemm_ops / 1e12, PEAK_INT8_TOPS, "TOP/s"),
+        "bwd_dx_bf16": ("mfma", gemm_ops / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"),
+        "bwd_dw_bf16": ("mfma", gemm_ops / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"),
+        # two reads of W plus the 2-bit write
+        "ternarize_pack": ("hbm", (2 * w_bytes * N * K + N * Kp / 4) / 1e9, PEAK_HBM_GBS, "GB/s"),
+        # read x (bf16), write x_q (int8, padded) and s
+        "act_quant": ("hbm", (2.0 * M * K + M * Kp + 4 * M) / 1e9, PEAK_HBM_GBS, "GB/s"),
+    }
+    fracs = {}
+    for n, (bound, work, peak, unit) in roof.items():
+        achieved = work / (per_kernel[n] * 1e-3)
+        fracs[n] = dict(bound=bound, achieved=achieved, peak=peak, unit=unit, frac=achieved / peak,
+                        ms=per_kernel[n])
+    dom = max(per_kernel, key=per_kernel.get)
+    d = fracs[dom]
+    traffic = load_traffic(dom, args.workload)
+    roofline = {"kernel": dom, "bound": d["bound"], "achieved": round(d["achieved"], 3), "peak": d["peak"],
+                "unit": d["unit"], "frac": round(d["frac"], 4), "traffic": traffic}
+
+    out = {
+        "metric": METRIC,
+        "value": round(tops, 3),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(tops / PAGES_L4_TOPS, 3),
+        "dtype": "int8+bf16",
+        "data": "synthetic",
+        "config": {"workload": f"bitlinear_fwd_bwd_{M}x{K}x{N}", "M": M, "K": K, "N": N,
+                   "w_dtype": inp["w_dtype"], "rotating_buffer_sets": args.rotate},
+        "roofline": roofline,
+        "kernels": {n: {"ms": round(f["ms"], 4), "frac": round(f["frac"], 4), "bound": f["bound"],
+                        "achieved": round(f["achieved"], 2), "unit": f["unit"]} for n, f in fracs.items()},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, rows=256)
+        out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 6)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,170 @@
+/*
+ * bitnet.h - C ABI of the MI355X (gfx950) BitLinear library, libbitnet.so.
+ *
+ * One BitNet b1.58 linear layer with ternary weights and int8 activations
+ * (W1.58 / A8), for quantization-aware training: the weight ternarization
+ * and 2-bit packing, the per-token int8 activation quantization, the INT8
+ * forward GEMM and the straight-through-estimator (STE) backward GEMMs.
+ * The operations are those of the "bitnet-qat-train" page (Hugging Face
+ * kernels, phanerozoic): its opening bullets and its "Semantics" section,
+ * with the quantizers of "bitlinear.py" (h4-polytopic-attention:
+ * ternary_quantize, activation_quant_int8) and "1BitTraining.md" (Codys12
+ * gist: weight_quant, activation_quant).
+ *
+ * Conventions for every entry point:
+ *  - Tensors are dense and row-major. bf16 data is passed as its raw 16-bit
+ *    patterns (uint16_t). Every array pointer is a DEVICE pointer and must be
+ *    16-byte aligned, except `gamma` (4-byte aligned).
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Work is enqueued on it asynchronously; nothing synchronizes the host.
+ *  - The caller owns every buffer (inputs, outputs, workspace) and keeps it
+ *    alive until the stream work completes. The library allocates no device
+ *    memory and keeps no pointer after it returns.
+ *  - Arguments are validated before any launch; a validation failure returns
+ *    its code and enqueues nothing. A failed launch returns BITNET_ERR_HIP.
+ *  - Sizes are int64_t and must be >= 1 (M, N, K). Any K is accepted: the
+ *    reduction axis of the int8 and 2-bit state is padded to
+ *    Kp = bitnet_k_pad(K) (a multiple of 64) with zero codes and values;
+ *    reductions and scales use the true K only.
+ *  - Non-finite inputs (inf, NaN) give unspecified results.
+ */
+#ifndef BITNET_H
+#define BITNET_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    BITNET_OK = 0,
+    BITNET_ERR_NULL = 1,      /* a required pointer is NULL */
+    BITNET_ERR_SHAPE = 2,     /* a size is < 1 or too large */
+    BITNET_ERR_DTYPE = 3,     /* unsupported dtype enum */
+    BITNET_ERR_ALIGN = 4,     /* a pointer is not aligned as required */
+    BITNET_ERR_WORKSPACE = 5, /* workspace NULL or smaller than required */
+    BITNET_ERR_HIP = 6        /* the HIP runtime reported an error */
+} bitnet_status;
+
+typedef enum {
+    BITNET_BF16 = 0,
+    BITNET_F32 = 1
+} bitnet_dtype;
+
+/* Human-readable name of a status code (static storage). */
+const char* bitnet_status_string(bitnet_status status);
+
+/* Padded reduction length: K rounded up to a multiple of 64 (K >= 1). */
+int64_t bitnet_k_pad(int64_t K);
+
+/* Bytes of workspace bitnet_ternarize_pack needs (fixed, a few KiB). */
+size_t bitnet_ternarize_workspace_bytes(int64_t N, int64_t K);
+
+/* Bytes of workspace bitlinear_fwd / bitlinear_bwd need for these sizes.
+ * 0 means the call takes no workspace (the pointer may then be NULL). */
+size_t bitlinear_fwd_workspace_bytes(int64_t M, int64_t N, int64_t K);
+size_t bitlinear_bwd_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
+ * bitnet_ternarize_pack - per-tensor absmean scale, RoundClip ternarization
+ * and 2-bit packing of the master weight, in one fused pass over W plus a
+ * reduction pass ("bitnet-qat-train", opening bullets; "bitlinear.py",
+ * ternary_quantize; "1BitTraining.md", weight_quant).
+ *
+ *   gamma = max(fp32(S / (N*K)), 1e-8f), S = sum |W| accumulated in fp64 in
+ *           a fixed order (bitwise deterministic across calls);
+ *   q[n,k] = clip(round_half_even(W[n,k] / gamma), -1, 1), evaluated exactly
+ *           (equivalently q = sign(w) if |w| > gamma/2, else 0).
+ *
+ * W         [N][K] master weights, bf16 bits (w_dtype BITNET_BF16) or float
+ *           (BITNET_F32).
+ * w_packed  [N][Kp/4] output bytes. The code of W[n,k] sits in byte
+ *           n*(Kp/4) + k/4 at bits 2*(k%4)..2*(k%4)+1 as a 2-bit two's
+ *           complement value: +1 = 0b01, 0 = 0b00, -1 = 0b11 (0b10 is never
+ *           written). Padding codes (k >= K) are 0. A little-endian 32-bit
+ *           word therefore holds 16 consecutive codes, code k%16 at bits 2k.
+ * gamma     [1] output float (device).
+ * workspace device scratch of at least bitnet_ternarize_workspace_bytes();
+ *           no initialization needed; clobbered.
+ */
+bitnet_status bitnet_ternarize_pack(const void* W, bitnet_dtype w_dtype,
+                                    int64_t N, int64_t K,
+                                    uint8_t* w_packed, float* gamma,
+                                    void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
+/*
+ * bitnet_act_quant - per-token absmax int8 quantization ("bitlinear.py",
+ * activation_quant_int8; "1BitTraining.md", activation_quant;
+ * "bitnet-qat-train", opening paragraph).
+ *
+ *   s[m]      = max(max_k |x[m,k]|, 1e-8f)             (the row absmax)
+ *   x_q[m,k]  = clip(round_half_even(127 * x[m,k] / s[m]), -127, 127),
+ *               evaluated exactly.
+ *
+ * x    [M][K] bf16 bits.
+ * x_q  [M][Kp] int8 output; columns K..Kp-1 are written as 0.
+ * s_x  [M] float output: the floored absmax. The dequantization scale is
+ *      s_x/127; it is applied where the int8 values are used.
+ */
+bitnet_status bitnet_act_quant(const uint16_t* x, int64_t M, int64_t K,
+                               int8_t* x_q, float* s_x, void* stream);
+
+/*
+ * bitlinear_fwd - INT8 forward GEMM with exact INT32 accumulation and a
+ * fused rescale ("bitnet-qat-train", Semantics):
+ *
+ *   acc[m,n] = sum_{k<Kp} x_q[m,k] * q[n,k]        (int32, exact)
+ *   y[m,n]   = bf16_rne(acc[m,n] * (s_x[m]/127) * gamma)   (fp32 rescale)
+ *
+ * x_q, s_x  as written by bitnet_act_quant (x_q [M][Kp]).
+ * w_packed, gamma as written by bitnet_ternarize_pack (w_packed [N][Kp/4]).
+ * y        [M][N] bf16 bits output.
+ * acc_out  [M][N] int32 output of the raw accumulators, or NULL (the
+ *          production setting; it exists for bit-exact checks).
+ * K        the true reduction length (Kp = bitnet_k_pad(K)).
+ * workspace device scratch of bitlinear_fwd_workspace_bytes(M, N, K) bytes
+ *          (NULL allowed when that is 0); clobbered.
+ */
+bitnet_status bitlinear_fwd(const int8_t* x_q, const float* s_x,
+                            const uint8_t* w_packed, const float* gamma,
+                            int64_t M, int64_t N, int64_t K,
+                            uint16_t* y, int32_t* acc_out,
+                            void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/*
+ * bitlinear_bwd - straight-through-estimator backward with the operands
+ * rebuilt from the saved 2-bit and int8 state ("bitnet-qat-train",
+ * Semantics and opening bullets; gamma is treated as a constant):
+ *
+ *   dX[m,k] = sum_n dY[m,n] * W_hat[n,k],  W_hat = q * bf16_rne(gamma)
+ *   dW[n,k] = sum_m dY[m,n] * x_hat[m,k],  x_hat = bf16_rne(x_q * s_x/127)
+ *
+ * Products are exact in fp32 (bf16 x bf16); sums accumulate in fp32; the
+ * results are rounded once to the output dtype.
+ *
+ * dY        [M][N] bf16 bits.
+ * x_q, s_x  saved activation state (x_q [M][Kp]); may be NULL if dW is NULL.
+ * w_packed, gamma saved weight state; may be NULL if dX is NULL.
+ * dX        [M][K] bf16 bits output, or NULL to skip the dX GEMM.
+ * dW        [N][K] output in dW_dtype (BITNET_BF16 bits or BITNET_F32), or
+ *           NULL to skip the dW GEMM. At least one of dX, dW is non-NULL.
+ * workspace device scratch of bitlinear_bwd_workspace_bytes(M, N, K) bytes
+ *           (NULL allowed when that is 0); clobbered.
+ */
+bitnet_status bitlinear_bwd(const uint16_t* dY,
+                            const int8_t* x_q, const float* s_x,
+                            const uint8_t* w_packed, const float* gamma,
+                            int64_t M, int64_t N, int64_t K,
+                            uint16_t* dX, void* dW, bitnet_dtype dW_dtype,
+                            void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITNET_H */

@@ -1,0 +1,188 @@
+"""ctypes binding of libbitnet.so: the C entry points under the same names.
+
+Argument marshalling only: every function takes torch tensors that already
+live on the GPU, checks that dtypes, shapes and contiguity match what the C
+ABI documents, and passes raw device pointers and the current HIP stream.
+All computation happens in the library's kernels. Outputs are preallocated
+by the caller, as in the C ABI. If the library is not built this module
+raises; there is no other compute path.
+"""
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libbitnet.so")
+
+BITNET_OK = 0
+BITNET_BF16 = 0
+BITNET_F32 = 1
+
+_lib = None
+
+
+def _hip_runtimes_mapped():
+    """Paths of the libamdhip64 copies mapped into this process."""
+    paths = set()
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    paths.add(os.path.realpath(line.split()[-1]))
+    except OSError:
+        pass
+    return paths
+
+
+def lib():
+    """Load libbitnet.so (after torch, so that both share torch's HIP
+    runtime) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is not built; run `python -m ternary_weight_quantization_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    i64, sz, vp, st = ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int
+    L.bitnet_status_string.argtypes = [st]
+    L.bitnet_status_string.restype = ctypes.c_char_p
+    L.bitnet_k_pad.argtypes = [i64]
+    L.bitnet_k_pad.restype = i64
+    L.bitnet_ternarize_workspace_bytes.argtypes = [i64, i64]
+    L.bitnet_ternarize_workspace_bytes.restype = sz
+    L.bitlinear_fwd_workspace_bytes.argtypes = [i64, i64, i64]
+    L.bitlinear_fwd_workspace_bytes.restype = sz
+    L.bitlinear_bwd_workspace_bytes.argtypes = [i64, i64, i64]
+    L.bitlinear_bwd_workspace_bytes.restype = sz
+    L.bitnet_ternarize_pack.argtypes = [vp, st, i64, i64, vp, vp, vp, sz, vp]
+    L.bitnet_ternarize_pack.restype = st
+    L.bitnet_act_quant.argtypes = [vp, i64, i64, vp, vp, vp]
+    L.bitnet_act_quant.restype = st
+    L.bitlinear_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp, vp, sz, vp]
+    L.bitlinear_fwd.restype = st
+    L.bitlinear_bwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp, vp, st, vp, sz, vp]
+    L.bitlinear_bwd.restype = st
+    if len(_hip_runtimes_mapped()) > 1:
+        raise RuntimeError("more than one libamdhip64 is mapped into this process: "
+                           f"{sorted(_hip_runtimes_mapped())}")
+    _lib = L
+    return _lib
+
+
+def _check(code):
+    if code != BITNET_OK:
+        msg = lib().bitnet_status_string(code).decode()
+        raise RuntimeError(f"libbitnet: {msg}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, dtype, shape, name):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a GPU tensor")
+
+
+# --- size queries ----------------------------------------------------------
+
+def bitnet_k_pad(K):
+    return int(lib().bitnet_k_pad(int(K)))
+
+
+def bitnet_ternarize_workspace_bytes(N, K):
+    return int(lib().bitnet_ternarize_workspace_bytes(int(N), int(K)))
+
+
+def bitlinear_fwd_workspace_bytes(M, N, K):
+    return int(lib().bitlinear_fwd_workspace_bytes(int(M), int(N), int(K)))
+
+
+def bitlinear_bwd_workspace_bytes(M, N, K):
+    return int(lib().bitlinear_bwd_workspace_bytes(int(M), int(N), int(K)))
+
+
+# --- entry points ----------------------------------------------------------
+
+def bitnet_ternarize_pack(W, w_packed, gamma, workspace, stream=None):
+    """W [N, K] bf16 or float32 -> w_packed uint8 [N, Kp/4], gamma float32 [1]."""
+    N, K = W.shape
+    Kp = bitnet_k_pad(K)
+    if W.dtype == torch.bfloat16:
+        wd = BITNET_BF16
+    elif W.dtype == torch.float32:
+        wd = BITNET_F32
+    else:
+        raise TypeError(f"W: expected bfloat16 or float32, got {W.dtype}")
+    _need(W, W.dtype, (N, K), "W")
+    _need(w_packed, torch.uint8, (N, Kp // 4), "w_packed")
+    _need(gamma, torch.float32, (1,), "gamma")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().bitnet_ternarize_pack(_ptr(W), wd, N, K, _ptr(w_packed), _ptr(gamma),
+                                       _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def bitnet_act_quant(x, x_q, s_x, stream=None):
+    """x [M, K] bf16 -> x_q int8 [M, Kp], s_x float32 [M]."""
+    M, K = x.shape
+    _need(x, torch.bfloat16, (M, K), "x")
+    _need(x_q, torch.int8, (M, bitnet_k_pad(K)), "x_q")
+    _need(s_x, torch.float32, (M,), "s_x")
+    _check(lib().bitnet_act_quant(_ptr(x), M, K, _ptr(x_q), _ptr(s_x), _stream(stream)))
+
+
+def bitlinear_fwd(x_q, s_x, w_packed, gamma, K, y, acc_out=None, workspace=None, stream=None):
+    """INT8 forward: y [M, N] bf16 (and optionally acc_out int32 [M, N])."""
+    M, Kp = x_q.shape
+    N = w_packed.shape[0]
+    if Kp != bitnet_k_pad(K):
+        raise ValueError("x_q: second dimension must be bitnet_k_pad(K)")
+    _need(x_q, torch.int8, (M, Kp), "x_q")
+    _need(s_x, torch.float32, (M,), "s_x")
+    _need(w_packed, torch.uint8, (N, Kp // 4), "w_packed")
+    _need(gamma, torch.float32, (1,), "gamma")
+    _need(y, torch.bfloat16, (M, N), "y")
+    if acc_out is not None:
+        _need(acc_out, torch.int32, (M, N), "acc_out")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().bitlinear_fwd(_ptr(x_q), _ptr(s_x), _ptr(w_packed), _ptr(gamma), M, N, int(K),
+                               _ptr(y), _ptr(acc_out), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def bitlinear_bwd(dY, x_q, s_x, w_packed, gamma, K, dX=None, dW=None, workspace=None, stream=None):
+    """STE backward: dX [M, K] bf16 and/or dW [N, K] (bf16 or float32)."""
+    M, N = dY.shape
+    Kp = bitnet_k_pad(K)
+    _need(dY, torch.bfloat16, (M, N), "dY")
+    if dX is not None:
+        _need(w_packed, torch.uint8, (N, Kp // 4), "w_packed")
+        _need(gamma, torch.float32, (1,), "gamma")
+        _need(dX, torch.bfloat16, (M, int(K)), "dX")
+    dw_dtype = BITNET_BF16
+    if dW is not None:
+        _need(x_q, torch.int8, (M, Kp), "x_q")
+        _need(s_x, torch.float32, (M,), "s_x")
+        if dW.dtype == torch.float32:
+            dw_dtype = BITNET_F32
+        _need(dW, dW.dtype, (N, int(K)), "dW")
+        if dW.dtype not in (torch.bfloat16, torch.float32):
+            raise TypeError("dW: expected bfloat16 or float32")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().bitlinear_bwd(_ptr(dY), _ptr(x_q), _ptr(s_x), _ptr(w_packed), _ptr(gamma),
+                               M, N, int(K), _ptr(dX), _ptr(dW), dw_dtype, _ptr(workspace), ws_bytes,
+                               _stream(stream)))

@@ -1,0 +1,123 @@
+// C ABI of libbitnet.so (declared in include/bitnet.h): argument
+// validation, then the launches on the caller's stream. Nothing here
+// allocates device memory or synchronizes the host.
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/bitnet.h"
+#include "internal.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = int64_t(1) << 30;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bitnet_status from_hip(hipError_t e) { return e == hipSuccess ? BITNET_OK : BITNET_ERR_HIP; }
+
+bitnet_status check_sizes(int64_t a, int64_t b) {
+  if (a < 1 || b < 1 || a > kMaxDim || b > kMaxDim) return BITNET_ERR_SHAPE;
+  return BITNET_OK;
+}
+
+// Sizes of the GEMMs: M, N, K >= 1; the int8 accumulation stays below 2^31
+// (127 * Kp < 2^31); tile and element counts fit the kernels' int indexing.
+bitnet_status check_gemm_sizes(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || N < 1 || K < 1) return BITNET_ERR_SHAPE;
+  if (M > kMaxDim || N > kMaxDim || K > (int64_t(1) << 24)) return BITNET_ERR_SHAPE;
+  const int64_t ti = (N + 255) / 256, tk = (bitnet::k_pad(K) + 255) / 256, tm = (M + 255) / 256;
+  if (ti * tm > (int64_t(1) << 30) || tk * tm > (int64_t(1) << 30) || tk * ti > (int64_t(1) << 30))
+    return BITNET_ERR_SHAPE;
+  return BITNET_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* bitnet_status_string(bitnet_status status) {
+  switch (status) {
+    case BITNET_OK: return "BITNET_OK";
+    case BITNET_ERR_NULL: return "BITNET_ERR_NULL: a required pointer is NULL";
+    case BITNET_ERR_SHAPE: return "BITNET_ERR_SHAPE: a size is out of range";
+    case BITNET_ERR_DTYPE: return "BITNET_ERR_DTYPE: unsupported dtype";
+    case BITNET_ERR_ALIGN: return "BITNET_ERR_ALIGN: a pointer is not aligned as required";
+    case BITNET_ERR_WORKSPACE: return "BITNET_ERR_WORKSPACE: workspace missing or too small";
+    case BITNET_ERR_HIP: return "BITNET_ERR_HIP: the HIP runtime reported an error";
+  }
+  return "BITNET_ERR_UNKNOWN";
+}
+
+int64_t bitnet_k_pad(int64_t K) { return K < 1 ? 0 : bitnet::k_pad(K); }
+
+size_t bitnet_ternarize_workspace_bytes(int64_t, int64_t) {
+  return sizeof(double) * bitnet::kAbsmeanBlocks;
+}
+
+size_t bitlinear_fwd_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
+size_t bitlinear_bwd_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
+
+bitnet_status bitnet_ternarize_pack(const void* W, bitnet_dtype w_dtype, int64_t N, int64_t K,
+                                    uint8_t* w_packed, float* gamma, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  if (!W || !w_packed || !gamma) return BITNET_ERR_NULL;
+  if (w_dtype != BITNET_BF16 && w_dtype != BITNET_F32) return BITNET_ERR_DTYPE;
+  if (bitnet_status st = check_sizes(N, K)) return st;
+  if (N * K > (int64_t(1) << 53)) return BITNET_ERR_SHAPE;
+  if (!aligned(W, 16) || !aligned(w_packed, 16) || !aligned(gamma, 4)) return BITNET_ERR_ALIGN;
+  if (!workspace || workspace_bytes < bitnet_ternarize_workspace_bytes(N, K)) return BITNET_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return BITNET_ERR_ALIGN;
+  return from_hip(bitnet::launch_ternarize_pack(W, w_dtype == BITNET_F32, N, K, w_packed, gamma,
+                                                static_cast<double*>(workspace),
+                                                static_cast<hipStream_t>(stream)));
+}
+
+bitnet_status bitnet_act_quant(const uint16_t* x, int64_t M, int64_t K, int8_t* x_q, float* s_x,
+                               void* stream) {
+  if (!x || !x_q || !s_x) return BITNET_ERR_NULL;
+  if (bitnet_status st = check_sizes(M, K)) return st;
+  if (!aligned(x, 16) || !aligned(x_q, 16) || !aligned(s_x, 16)) return BITNET_ERR_ALIGN;
+  return from_hip(bitnet::launch_act_quant(x, M, K, x_q, s_x, static_cast<hipStream_t>(stream)));
+}
+
+bitnet_status bitlinear_fwd(const int8_t* x_q, const float* s_x, const uint8_t* w_packed,
+                            const float* gamma, int64_t M, int64_t N, int64_t K, uint16_t* y,
+                            int32_t* acc_out, void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  if (!x_q || !s_x || !w_packed || !gamma || !y) return BITNET_ERR_NULL;
+  if (bitnet_status st = check_gemm_sizes(M, N, K)) return st;
+  if (workspace_bytes < bitlinear_fwd_workspace_bytes(M, N, K)) return BITNET_ERR_WORKSPACE;
+  if (!aligned(x_q, 16) || !aligned(s_x, 16) || !aligned(w_packed, 16) || !aligned(gamma, 4) ||
+      !aligned(y, 16) || (acc_out && !aligned(acc_out, 16)))
+    return BITNET_ERR_ALIGN;
+  return from_hip(bitnet::launch_fwd(x_q, s_x, w_packed, gamma, M, N, K, y, acc_out,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+bitnet_status bitlinear_bwd(const uint16_t* dY, const int8_t* x_q, const float* s_x,
+                            const uint8_t* w_packed, const float* gamma, int64_t M, int64_t N,
+                            int64_t K, uint16_t* dX, void* dW, bitnet_dtype dW_dtype,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  if (!dY) return BITNET_ERR_NULL;
+  if (!dX && !dW) return BITNET_ERR_NULL;
+  if (dX && (!w_packed || !gamma)) return BITNET_ERR_NULL;
+  if (dW && (!x_q || !s_x)) return BITNET_ERR_NULL;
+  if (dW && dW_dtype != BITNET_BF16 && dW_dtype != BITNET_F32) return BITNET_ERR_DTYPE;
+  if (bitnet_status st = check_gemm_sizes(M, N, K)) return st;
+  if (workspace_bytes < bitlinear_bwd_workspace_bytes(M, N, K)) return BITNET_ERR_WORKSPACE;
+  if (!aligned(dY, 16)) return BITNET_ERR_ALIGN;
+  if (dX && (!aligned(w_packed, 16) || !aligned(gamma, 4) || !aligned(dX, 16))) return BITNET_ERR_ALIGN;
+  if (dW && (!aligned(x_q, 16) || !aligned(s_x, 16) || !aligned(dW, 16))) return BITNET_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (dX) {
+    if (hipError_t e = bitnet::launch_bwd_dx(dY, w_packed, gamma, M, N, K, dX, st)) return from_hip(e);
+  }
+  if (dW) {
+    if (hipError_t e = bitnet::launch_bwd_dw(dY, x_q, s_x, M, N, K, dW, dW_dtype == BITNET_F32, st))
+      return from_hip(e);
+  }
+  return BITNET_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,39 @@
+// Internal launchers of libbitnet.so. Arguments are validated by the C ABI
+// layer (api.hip) before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bitnet {
+
+// Fixed grid of the absmean partial-sum kernel: the partial order (and so
+// gamma's bits) never depends on the device or the call.
+constexpr int kAbsmeanBlocks = 256;
+constexpr int kAbsmeanThreads = 512;
+
+inline int64_t k_pad(int64_t K) { return ((K + 63) / 64) * 64; }
+
+// Weight ternarization: fp64 absmean partials, then gamma + codes + packing.
+hipError_t launch_ternarize_pack(const void* W, bool w_is_f32, int64_t N, int64_t K,
+                                 uint8_t* w_packed, float* gamma, double* partials,
+                                 hipStream_t stream);
+
+// Per-token absmax int8 activation quantization.
+hipError_t launch_act_quant(const uint16_t* x, int64_t M, int64_t K,
+                            int8_t* x_q, float* s_x, hipStream_t stream);
+
+// INT8 forward GEMM with fused rescale (and optional int32 accumulators).
+hipError_t launch_fwd(const int8_t* x_q, const float* s_x, const uint8_t* w_packed,
+                      const float* gamma, int64_t M, int64_t N, int64_t K,
+                      uint16_t* y, int32_t* acc_out, hipStream_t stream);
+
+// STE backward GEMMs.
+hipError_t launch_bwd_dx(const uint16_t* dY, const uint8_t* w_packed, const float* gamma,
+                         int64_t M, int64_t N, int64_t K, uint16_t* dX, hipStream_t stream);
+hipError_t launch_bwd_dw(const uint16_t* dY, const int8_t* x_q, const float* s_x,
+                         int64_t M, int64_t N, int64_t K, void* dW, bool dw_is_f32,
+                         hipStream_t stream);
+
+}  // namespace bitnet

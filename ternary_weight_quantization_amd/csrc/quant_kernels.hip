@@ -1,0 +1,365 @@
+// Quantization kernels for gfx950: weight absmean + ternarize + 2-bit pack,
+// and per-token absmax int8 activation quantization. Both are HBM-bound
+// streaming passes: 16-byte loads, one pass over each input where possible.
+//
+// Weights ("bitnet-qat-train", opening bullets: one fused ternarize, scale
+// and pack pass; "bitlinear.py", ternary_quantize; "1BitTraining.md",
+// weight_quant):
+//   gamma   = max(fp32(S / (N*K)), 1e-8),  S = sum |W| in fp64
+//   q[n,k]  = clip(RNE(W/gamma), -1, 1)  ==  sign(w) * [|w| > gamma/2]
+// The threshold form is exact: gamma/2 is exact in fp32, both sides are
+// exact fp32 values, and RNE sends |W/gamma| == 1/2 to 0, (1/2, 3/2) to 1
+// and [3/2, inf) to >= 2, which clips to 1.
+//
+// Activations ("bitlinear.py", activation_quant_int8; "1BitTraining.md",
+// activation_quant):
+//   s[m]    = max(max_k |x[m,k]|, 1e-8)
+//   x_q     = clip(RNE(127 x / s), -127, 127), exactly.
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace bitnet {
+
+// ---------------------------------------------------------------------------
+// absmean, phase 1: fixed-grid fp64 partial sums of |W|
+// ---------------------------------------------------------------------------
+
+template <bool F32>
+__device__ __forceinline__ double abs_sum16(uint4 v) {
+  if constexpr (F32) {
+    const double a = fabs((double)__uint_as_float(v.x));
+    const double b = fabs((double)__uint_as_float(v.y));
+    const double c = fabs((double)__uint_as_float(v.z));
+    const double d = fabs((double)__uint_as_float(v.w));
+    return (a + b) + (c + d);
+  } else {
+    const uint32_t x = v.x & 0x7FFF7FFFu, y = v.y & 0x7FFF7FFFu;
+    const uint32_t z = v.z & 0x7FFF7FFFu, w = v.w & 0x7FFF7FFFu;
+    const double s0 = (double)bf16_lo(x) + (double)bf16_hi(x);
+    const double s1 = (double)bf16_lo(y) + (double)bf16_hi(y);
+    const double s2 = (double)bf16_lo(z) + (double)bf16_hi(z);
+    const double s3 = (double)bf16_lo(w) + (double)bf16_hi(w);
+    return (s0 + s1) + (s2 + s3);
+  }
+}
+
+template <bool F32>
+__device__ __forceinline__ float load_elem(const void* w, int64_t i) {
+  if constexpr (F32) return static_cast<const float*>(w)[i];
+  else return bf16_to_f32(static_cast<const uint16_t*>(w)[i]);
+}
+
+template <bool F32>
+__global__ __launch_bounds__(kAbsmeanThreads) void absmean_partials_kernel(
+    const void* __restrict__ w, int64_t n, double* __restrict__ partials) {
+  constexpr int kVec = F32 ? 4 : 8;  // elements per 16 bytes
+  constexpr int kUnroll = 8;
+  const uint4* wv = static_cast<const uint4*>(w);
+  const int64_t nvec = n / kVec;
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+
+  double acc[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) acc[u] = 0.0;
+  int64_t i = tid;
+  for (; i + (kUnroll - 1) * stride < nvec; i += kUnroll * stride) {
+    uint4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) v[u] = wv[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) acc[u] += abs_sum16<F32>(v[u]);
+  }
+  for (; i < nvec; i += stride) acc[0] += abs_sum16<F32>(wv[i]);
+  const int64_t tail = nvec * kVec;
+  if (tid < n - tail) acc[1] += fabs((double)load_elem<F32>(w, tail + tid));
+
+  double v = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+  v = wave_sum_f64(v);
+  __shared__ double sw[kAbsmeanThreads / kWave];
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  if (lane == 0) sw[wave] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double t = 0.0;
+#pragma unroll
+    for (int j = 0; j < kAbsmeanThreads / kWave; ++j) t += sw[j];
+    partials[blockIdx.x] = t;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// absmean, phase 2 + ternarize + pack. Every block reduces the fixed set of
+// partials in the same order, so all blocks hold the same gamma; block 0
+// stores it. Each thread then writes whole 32-bit words of 16 codes.
+// ---------------------------------------------------------------------------
+
+constexpr int kPackThreads = 256;
+static_assert(kAbsmeanBlocks == kPackThreads, "one partial per thread");
+
+template <bool F32, bool VEC>
+__global__ __launch_bounds__(kPackThreads) void ternarize_pack_kernel(
+    const void* __restrict__ w, int64_t N, int64_t K, int64_t words_per_row,
+    const double* __restrict__ partials, uint32_t* __restrict__ packed,
+    float* __restrict__ gamma_out) {
+  __shared__ double sred[kPackThreads / kWave];
+  __shared__ float s_half;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  double v = wave_sum_f64(partials[threadIdx.x]);
+  if (lane == 0) sred[wave] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const double S = (sred[0] + sred[1]) + (sred[2] + sred[3]);
+    const double mean = S / (double)(N * K);
+    const float g = fmaxf((float)mean, 1e-8f);
+    s_half = g * 0.5f;  // exact
+    if (blockIdx.x == 0) *gamma_out = g;
+  }
+  __syncthreads();
+  const float h = s_half;
+
+  const int64_t total = N * words_per_row;
+  for (int64_t wi = (int64_t)blockIdx.x * kPackThreads + threadIdx.x; wi < total;
+       wi += (int64_t)gridDim.x * kPackThreads) {
+    const int64_t n = wi / words_per_row;
+    const int64_t k0 = (wi - n * words_per_row) * 16;
+    float vals[16];
+    if (VEC && k0 + 16 <= K) {
+      if constexpr (F32) {
+        const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(w) + n * K + k0);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint4 d = p[c];
+          vals[4 * c + 0] = __uint_as_float(d.x);
+          vals[4 * c + 1] = __uint_as_float(d.y);
+          vals[4 * c + 2] = __uint_as_float(d.z);
+          vals[4 * c + 3] = __uint_as_float(d.w);
+        }
+      } else {
+        const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(w) + n * K + k0);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const uint4 d = p[c];
+          vals[8 * c + 0] = bf16_lo(d.x); vals[8 * c + 1] = bf16_hi(d.x);
+          vals[8 * c + 2] = bf16_lo(d.y); vals[8 * c + 3] = bf16_hi(d.y);
+          vals[8 * c + 4] = bf16_lo(d.z); vals[8 * c + 5] = bf16_hi(d.z);
+          vals[8 * c + 6] = bf16_lo(d.w); vals[8 * c + 7] = bf16_hi(d.w);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int64_t k = k0 + j;
+        vals[j] = (k < K) ? load_elem<F32>(w, n * K + k) : 0.0f;
+      }
+    }
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint32_t code = (vals[j] > h) ? 1u : ((vals[j] < -h) ? 3u : 0u);
+      word |= code << (2 * j);
+    }
+    packed[wi] = word;
+  }
+}
+
+hipError_t launch_ternarize_pack(const void* W, bool w_is_f32, int64_t N, int64_t K,
+                                 uint8_t* w_packed, float* gamma, double* partials,
+                                 hipStream_t stream) {
+  const int64_t n = N * K;
+  if (w_is_f32)
+    absmean_partials_kernel<true><<<kAbsmeanBlocks, kAbsmeanThreads, 0, stream>>>(W, n, partials);
+  else
+    absmean_partials_kernel<false><<<kAbsmeanBlocks, kAbsmeanThreads, 0, stream>>>(W, n, partials);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  const int64_t wpr = k_pad(K) / 16;
+  const int64_t total = N * wpr;
+  const int64_t want = (total + kPackThreads - 1) / kPackThreads;
+  const int grid = (int)(want < 2048 ? want : 2048);
+  uint32_t* pw = reinterpret_cast<uint32_t*>(w_packed);
+  const bool vec = w_is_f32 ? (K % 4 == 0) : (K % 8 == 0);
+  if (w_is_f32) {
+    if (vec) ternarize_pack_kernel<true, true><<<grid, kPackThreads, 0, stream>>>(W, N, K, wpr, partials, pw, gamma);
+    else ternarize_pack_kernel<true, false><<<grid, kPackThreads, 0, stream>>>(W, N, K, wpr, partials, pw, gamma);
+  } else {
+    if (vec) ternarize_pack_kernel<false, true><<<grid, kPackThreads, 0, stream>>>(W, N, K, wpr, partials, pw, gamma);
+    else ternarize_pack_kernel<false, false><<<grid, kPackThreads, 0, stream>>>(W, N, K, wpr, partials, pw, gamma);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Activation quantization
+// ---------------------------------------------------------------------------
+
+// RNE(127 x / s) for |x| <= s, exactly. Fast path: p = x * fl(127/s) is
+// within 127 * 2^-23 (< 1.6e-5) of the exact quotient Q, so when p is more
+// than 2^-15 away from the nearest half-integer, rint(p) is the integer
+// nearest to Q and no tie is possible. Otherwise Q is recomputed as an fp64
+// quotient of exact operands, whose rounding error (< 2^-46) is far below
+// the smallest nonzero distance of Q from a half-integer (> 2^-33 for fp32
+// operands), so rint of it is exact, ties included.
+__device__ __forceinline__ int quant1(float xv, float r127, float s) {
+  const float p = xv * r127;
+  float c = __builtin_rintf(p);
+  if (fabsf(p - c) > 0.49996948f) {  // 0.5 - 2^-15
+    const double t = 127.0 * (double)xv;
+    c = (float)__builtin_rint(t / (double)s);
+  }
+  c = fminf(fmaxf(c, -127.0f), 127.0f);
+  return (int)c;
+}
+
+__device__ __forceinline__ uint32_t pack_i8x4(int a, int b, int c, int d) {
+  return (uint32_t(a) & 0xFFu) | ((uint32_t(b) & 0xFFu) << 8) | ((uint32_t(c) & 0xFFu) << 16) |
+         (uint32_t(d) << 24);
+}
+
+__device__ __forceinline__ uint2 quant8(uint4 v, float r127, float s) {
+  uint2 o;
+  o.x = pack_i8x4(quant1(bf16_lo(v.x), r127, s), quant1(bf16_hi(v.x), r127, s),
+                  quant1(bf16_lo(v.y), r127, s), quant1(bf16_hi(v.y), r127, s));
+  o.y = pack_i8x4(quant1(bf16_lo(v.z), r127, s), quant1(bf16_hi(v.z), r127, s),
+                  quant1(bf16_lo(v.w), r127, s), quant1(bf16_hi(v.w), r127, s));
+  return o;
+}
+
+__device__ __forceinline__ float absmax8(uint4 v) {
+  const float a = fmaxf(fmaxf(fabsf(bf16_lo(v.x)), fabsf(bf16_hi(v.x))),
+                        fmaxf(fabsf(bf16_lo(v.y)), fabsf(bf16_hi(v.y))));
+  const float b = fmaxf(fmaxf(fabsf(bf16_lo(v.z)), fabsf(bf16_hi(v.z))),
+                        fmaxf(fabsf(bf16_lo(v.w)), fabsf(bf16_hi(v.w))));
+  return fmaxf(a, b);
+}
+
+// Loads the 8 bf16 of chunk `ch` of a row (zeros past K).
+template <bool VEC>
+__device__ __forceinline__ uint4 load_chunk(const uint16_t* xr, int64_t ch, int64_t K) {
+  const int64_t k0 = ch * 8;
+  if (VEC && k0 + 8 <= K) return *reinterpret_cast<const uint4*>(xr + k0);
+  uint32_t d[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t k = k0 + 2 * j;
+    const uint32_t lo = (k < K) ? xr[k] : 0u;
+    const uint32_t hi = (k + 1 < K) ? xr[k + 1] : 0u;
+    d[j] = lo | (hi << 16);
+  }
+  return make_uint4(d[0], d[1], d[2], d[3]);
+}
+
+// TPR threads (whole waves) per row, CPT chunks of 8 values per thread kept
+// in registers: one HBM read of x, one write of x_q.
+template <int TPR, int CPT, bool VEC>
+__global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restrict__ x, int64_t M,
+                                                        int64_t K, int64_t Kp,
+                                                        int8_t* __restrict__ xq,
+                                                        float* __restrict__ s_out) {
+  static_assert(TPR % kWave == 0 && 256 % TPR == 0, "whole waves per row");
+  constexpr int RPB = 256 / TPR;
+  constexpr int WPR = TPR / kWave;
+  __shared__ float smax[256 / kWave];
+  const int r_local = threadIdx.x / TPR;
+  const int t = threadIdx.x % TPR;
+  const int64_t row = (int64_t)blockIdx.x * RPB + r_local;
+  const bool row_ok = row < M;
+  const int64_t nchunks = Kp / 8;
+  const uint16_t* xr = x + row * K;
+
+  uint4 v[CPT];
+  float amax = 0.0f;
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int64_t ch = t + (int64_t)c * TPR;
+    v[c] = (row_ok && ch * 8 < K) ? load_chunk<VEC>(xr, ch, K) : make_uint4(0, 0, 0, 0);
+    amax = fmaxf(amax, absmax8(v[c]));
+  }
+  amax = wave_max_f32(amax);
+  if constexpr (WPR > 1) {
+    if (threadIdx.x % kWave == 0) smax[threadIdx.x / kWave] = amax;
+    __syncthreads();
+    const int w0 = r_local * WPR;
+    amax = smax[w0];
+#pragma unroll
+    for (int j = 1; j < WPR; ++j) amax = fmaxf(amax, smax[w0 + j]);
+  }
+  const float s = fmaxf(amax, 1e-8f);
+  if (row_ok && t == 0) s_out[row] = s;
+  const float r127 = 127.0f / s;
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int64_t ch = t + (int64_t)c * TPR;
+    if (row_ok && ch < nchunks)
+      *reinterpret_cast<uint2*>(xq + row * Kp + ch * 8) = quant8(v[c], r127, s);
+  }
+}
+
+// Rows longer than the register-resident variant allows: two passes over the
+// row (the second read is served by the caches).
+template <bool VEC>
+__global__ __launch_bounds__(256) void act_quant_long_kernel(const uint16_t* __restrict__ x,
+                                                             int64_t M, int64_t K, int64_t Kp,
+                                                             int8_t* __restrict__ xq,
+                                                             float* __restrict__ s_out) {
+  __shared__ float smax[256 / kWave];
+  const int64_t row = blockIdx.x;
+  const uint16_t* xr = x + row * K;
+  const int64_t nchunks = Kp / 8;
+  float amax = 0.0f;
+  for (int64_t ch = threadIdx.x; ch * 8 < K; ch += 256) amax = fmaxf(amax, absmax8(load_chunk<VEC>(xr, ch, K)));
+  amax = wave_max_f32(amax);
+  if (threadIdx.x % kWave == 0) smax[threadIdx.x / kWave] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3]));
+  const float s = fmaxf(amax, 1e-8f);
+  if (threadIdx.x == 0) s_out[row] = s;
+  const float r127 = 127.0f / s;
+  for (int64_t ch = threadIdx.x; ch < nchunks; ch += 256) {
+    const uint4 v = (ch * 8 < K) ? load_chunk<VEC>(xr, ch, K) : make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint2*>(xq + row * Kp + ch * 8) = quant8(v, r127, s);
+  }
+}
+
+template <int TPR, bool VEC>
+static void launch_aq_tpr(int cpt, const uint16_t* x, int64_t M, int64_t K, int64_t Kp,
+                          int8_t* xq, float* s, hipStream_t st) {
+  const int grid = (int)((M + (256 / TPR) - 1) / (256 / TPR));
+  switch (cpt) {
+    case 1: act_quant_kernel<TPR, 1, VEC><<<grid, 256, 0, st>>>(x, M, K, Kp, xq, s); break;
+    case 2: act_quant_kernel<TPR, 2, VEC><<<grid, 256, 0, st>>>(x, M, K, Kp, xq, s); break;
+    case 3: act_quant_kernel<TPR, 3, VEC><<<grid, 256, 0, st>>>(x, M, K, Kp, xq, s); break;
+    case 4: act_quant_kernel<TPR, 4, VEC><<<grid, 256, 0, st>>>(x, M, K, Kp, xq, s); break;
+    case 5: act_quant_kernel<TPR, 5, VEC><<<grid, 256, 0, st>>>(x, M, K, Kp, xq, s); break;
+    case 6: act_quant_kernel<TPR, 6, VEC><<<grid, 256, 0, st>>>(x, M, K, Kp, xq, s); break;
+    case 7: act_quant_kernel<TPR, 7, VEC><<<grid, 256, 0, st>>>(x, M, K, Kp, xq, s); break;
+    default: act_quant_kernel<TPR, 8, VEC><<<grid, 256, 0, st>>>(x, M, K, Kp, xq, s); break;
+  }
+}
+
+template <bool VEC>
+static void launch_aq(const uint16_t* x, int64_t M, int64_t K, int64_t Kp, int8_t* xq, float* s,
+                      hipStream_t st) {
+  const int64_t nchunks = Kp / 8;
+  if (nchunks <= 64 * 8) {
+    launch_aq_tpr<64, VEC>((int)((nchunks + 63) / 64), x, M, K, Kp, xq, s, st);
+  } else if (nchunks <= 128 * 8) {
+    launch_aq_tpr<128, VEC>((int)((nchunks + 127) / 128), x, M, K, Kp, xq, s, st);
+  } else if (nchunks <= 256 * 8) {
+    launch_aq_tpr<256, VEC>((int)((nchunks + 255) / 256), x, M, K, Kp, xq, s, st);
+  } else {
+    act_quant_long_kernel<VEC><<<(int)M, 256, 0, st>>>(x, M, K, Kp, xq, s);
+  }
+}
+
+hipError_t launch_act_quant(const uint16_t* x, int64_t M, int64_t K, int8_t* x_q, float* s_x,
+                            hipStream_t stream) {
+  const int64_t Kp = k_pad(K);
+  if (K % 8 == 0) launch_aq<true>(x, M, K, Kp, x_q, s_x, stream);
+  else launch_aq<false>(x, M, K, Kp, x_q, s_x, stream);
+  return hipGetLastError();
+}
+
+}  // namespace bitnet

@@ -1,0 +1,112 @@
+"""torch autograd wrapper and drop-in module over the C ABI.
+
+``QATBitLinear`` mirrors the layer of the "bitnet-qat-train" page (Usage:
+bf16 master weights [out, in], ``y = layer(x)``, STE gradients on
+``layer.weight``; ``from_linear``; ``export_inference`` returning the packed
+weights and their scale). The forward saves only the int8 activations, their
+scales, the 2-bit weights and gamma ("bitnet-qat-train", opening bullets);
+the backward rebuilds the operands from them inside the library's kernels.
+torch provides memory and the stream; every step runs in libbitnet.so.
+"""
+
+import math
+
+import torch
+
+from . import binding as B
+
+
+def ternarize(weight):
+    """weight [N, K] (bf16 or f32, on the GPU) -> (w_packed uint8 [N, Kp/4],
+    gamma float32 [1])."""
+    N, K = weight.shape
+    Kp = B.bitnet_k_pad(K)
+    w_packed = torch.empty((N, Kp // 4), dtype=torch.uint8, device=weight.device)
+    gamma = torch.empty((1,), dtype=torch.float32, device=weight.device)
+    ws = torch.empty((B.bitnet_ternarize_workspace_bytes(N, K),), dtype=torch.uint8, device=weight.device)
+    B.bitnet_ternarize_pack(weight.contiguous(), w_packed, gamma, ws)
+    return w_packed, gamma
+
+
+def act_quant(x2d):
+    """x [M, K] bf16 -> (x_q int8 [M, Kp], s_x float32 [M])."""
+    M, K = x2d.shape
+    x_q = torch.empty((M, B.bitnet_k_pad(K)), dtype=torch.int8, device=x2d.device)
+    s_x = torch.empty((M,), dtype=torch.float32, device=x2d.device)
+    B.bitnet_act_quant(x2d, x_q, s_x)
+    return x_q, s_x
+
+
+def _workspace(nbytes, device):
+    return None if nbytes == 0 else torch.empty((nbytes,), dtype=torch.uint8, device=device)
+
+
+class BitLinearFunction(torch.autograd.Function):
+    """y = BitLinear(x, W) with the STE backward. x [..., K] bf16, W [N, K]
+    bf16 or float32; y [..., N] bf16. Gradients: dX bf16, dW in W's dtype."""
+
+    @staticmethod
+    def forward(ctx, x, weight):
+        if x.dtype != torch.bfloat16:
+            raise TypeError("BitLinear expects bf16 activations")
+        N, K = weight.shape
+        lead = x.shape[:-1]
+        x2 = x.reshape(-1, K).contiguous()
+        M = x2.shape[0]
+        w_packed, gamma = ternarize(weight)
+        x_q, s_x = act_quant(x2)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+        B.bitlinear_fwd(x_q, s_x, w_packed, gamma, K, y,
+                        workspace=_workspace(B.bitlinear_fwd_workspace_bytes(M, N, K), x.device))
+        ctx.save_for_backward(x_q, s_x, w_packed, gamma)
+        ctx.shape = (M, N, K, lead, weight.dtype)
+        return y.reshape(*lead, N)
+
+    @staticmethod
+    def backward(ctx, dy):
+        x_q, s_x, w_packed, gamma = ctx.saved_tensors
+        M, N, K, lead, wdtype = ctx.shape
+        dY = dy.reshape(M, N).to(torch.bfloat16).contiguous()
+        need_x, need_w = ctx.needs_input_grad
+        dX = torch.empty((M, K), dtype=torch.bfloat16, device=dy.device) if need_x else None
+        dW = torch.empty((N, K), dtype=wdtype, device=dy.device) if need_w else None
+        if dX is not None or dW is not None:
+            B.bitlinear_bwd(dY, x_q, s_x, w_packed, gamma, K, dX=dX, dW=dW,
+                            workspace=_workspace(B.bitlinear_bwd_workspace_bytes(M, N, K), dy.device))
+        return (None if dX is None else dX.reshape(*lead, K)), dW
+
+
+class QATBitLinear(torch.nn.Module):
+    """Ternary-weight, int8-activation linear layer for quantization-aware
+    training. Master weights [out_features, in_features] in bf16 (or f32),
+    kaiming-uniform(a=sqrt(5)) init as in "bitlinear.py" BitLinear.__init__,
+    no bias."""
+
+    def __init__(self, in_features, out_features, device="cuda", dtype=torch.bfloat16):
+        super().__init__()
+        self.in_features = in_features
+        self.out_features = out_features
+        w = torch.empty((out_features, in_features), dtype=torch.float32)
+        torch.nn.init.kaiming_uniform_(w, a=math.sqrt(5))
+        self.weight = torch.nn.Parameter(w.to(device=device, dtype=dtype))
+
+    @classmethod
+    def from_linear(cls, linear, dtype=torch.bfloat16):
+        if linear.bias is not None:
+            raise ValueError("QATBitLinear has no bias")
+        m = cls(linear.in_features, linear.out_features, device=linear.weight.device, dtype=dtype)
+        with torch.no_grad():
+            m.weight.copy_(linear.weight.to(dtype))
+        return m
+
+    def forward(self, x):
+        return BitLinearFunction.apply(x, self.weight)
+
+    @torch.no_grad()
+    def export_inference(self):
+        """(w_packed uint8 [out, Kp/4], gamma float32 [1]) of the current
+        master weights."""
+        return ternarize(self.weight.detach())
+
+    def extra_repr(self):
+        return f"{self.in_features}, {self.out_features}, dtype={self.weight.dtype}"

@@ -33,9 +33,9 @@ STACK = dict(M=2048, dims=[2560, 6912] * 4 + [2560], w_dtype="bf16")
 def f32_to_bf16_bits(a):
     """float32 -> bf16 bit patterns (uint16), round half to even.
     Inputs are finite draws; no NaN handling."""
-    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    lsb = (u >> np.uint64(16)) & np.uint64(1)
-    r = (u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    # finite inputs: u + 0x8000 stays below 2^32
+    r = (u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))) >> np.uint32(16)
     return r.astype(np.uint16)
 
 

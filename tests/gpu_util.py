@@ -1,0 +1,83 @@
+"""Helpers of the GPU parity tests: move the seeded inputs to the GPU, run
+the layer through the C ABI (via the binding), and bring results back as
+numpy arrays. No arithmetic of the layer happens here."""
+
+import sys
+
+import numpy as np
+import torch
+
+from ternary_weight_quantization_amd import binding as B
+from ternary_weight_quantization_amd import workloads as WL
+
+
+def note(msg):
+    """Print and flush the case about to run on the GPU."""
+    print(f"[gpu] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def host_bf16_bits(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def dev_weight(W):
+    if W.dtype == np.uint16:
+        return dev_bf16(W)
+    return torch.from_numpy(np.ascontiguousarray(W, dtype=np.float32)).cuda()
+
+
+def w_values(W):
+    """float64 values of the host weight (bf16 bits or float32)."""
+    if W.dtype == np.uint16:
+        return WL.bf16_bits_to_f32(W).astype(np.float64)
+    return W.astype(np.float64)
+
+
+def run_layer(inp, acc=True, dx=True, dw=True, xdev=None):
+    """Run ternarize_pack, act_quant, fwd and bwd on the GPU. Returns numpy
+    copies of every output. `xdev` overrides the input activations (a bf16
+    GPU tensor), e.g. the previous layer's output."""
+    M, K, N = inp["M"], inp["K"], inp["N"]
+    Kp = B.bitnet_k_pad(K)
+    dev = torch.device("cuda")
+    W = dev_weight(inp["W"])
+    x = dev_bf16(inp["x"]) if xdev is None else xdev
+    dY = dev_bf16(inp["dY"])
+    w_packed = torch.empty((N, Kp // 4), dtype=torch.uint8, device=dev)
+    gamma = torch.empty((1,), dtype=torch.float32, device=dev)
+    ws = torch.empty((B.bitnet_ternarize_workspace_bytes(N, K),), dtype=torch.uint8, device=dev)
+    x_q = torch.empty((M, Kp), dtype=torch.int8, device=dev)
+    s_x = torch.empty((M,), dtype=torch.float32, device=dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    acc_out = torch.empty((M, N), dtype=torch.int32, device=dev) if acc else None
+    B.bitnet_ternarize_pack(W, w_packed, gamma, ws)
+    B.bitnet_act_quant(x, x_q, s_x)
+    B.bitlinear_fwd(x_q, s_x, w_packed, gamma, K, y, acc_out)
+    dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev) if dx else None
+    dW = torch.empty((N, K), dtype=W.dtype, device=dev) if dw else None
+    if dx or dw:
+        B.bitlinear_bwd(dY, x_q, s_x, w_packed, gamma, K, dX=dX, dW=dW)
+    torch.cuda.synchronize()
+    out = dict(
+        gamma=gamma.cpu().numpy()[0],
+        packed=w_packed.cpu().numpy(),
+        x_q=x_q.cpu().numpy(),
+        s=s_x.cpu().numpy(),
+        y_bits=host_bf16_bits(y),
+        y_dev=y,
+    )
+    if acc:
+        out["acc"] = acc_out.cpu().numpy()
+    if dx:
+        out["dX"] = WL.bf16_bits_to_f32(host_bf16_bits(dX)).astype(np.float64)
+    if dw:
+        if dW.dtype == torch.float32:
+            out["dW"] = dW.cpu().numpy().astype(np.float64)
+        else:
+            out["dW"] = WL.bf16_bits_to_f32(host_bf16_bits(dW)).astype(np.float64)
+    return out

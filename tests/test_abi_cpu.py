@@ -1,0 +1,111 @@
+"""The C ABI without a GPU: the library loads, exports every entry point the
+header declares, answers its size queries, and rejects bad arguments with
+the documented codes before touching the GPU (no compute call here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bitnet.h")
+LIB = os.path.join(ROOT, "ternary_weight_quantization_amd", "libbitnet.so")
+
+OK, ENULL, ESHAPE, EDTYPE, EALIGN, EWS, EHIP = range(7)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bit(?:net|linear)_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(LIB):
+        pytest.fail("libbitnet.so is not built (run `python -m ternary_weight_quantization_amd.build`)")
+    lib = ctypes.CDLL(LIB)
+    i64, sz, vp, st = ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int
+    lib.bitnet_status_string.restype = ctypes.c_char_p
+    lib.bitnet_k_pad.argtypes = [i64]
+    lib.bitnet_k_pad.restype = i64
+    lib.bitnet_ternarize_workspace_bytes.argtypes = [i64, i64]
+    lib.bitnet_ternarize_workspace_bytes.restype = sz
+    lib.bitlinear_fwd_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.bitlinear_fwd_workspace_bytes.restype = sz
+    lib.bitlinear_bwd_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.bitlinear_bwd_workspace_bytes.restype = sz
+    lib.bitnet_ternarize_pack.argtypes = [vp, st, i64, i64, vp, vp, vp, sz, vp]
+    lib.bitnet_act_quant.argtypes = [vp, i64, i64, vp, vp, vp]
+    lib.bitlinear_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp, vp, sz, vp]
+    lib.bitlinear_bwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp, vp, st, vp, sz, vp]
+    return lib
+
+
+def test_header_declares_the_four_entry_points():
+    names = declared_functions()
+    for n in ("bitnet_ternarize_pack", "bitnet_act_quant", "bitlinear_fwd", "bitlinear_bwd"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_size_queries(L):
+    assert [L.bitnet_k_pad(k) for k in (1, 7, 63, 64, 65, 2560, 6912)] == [64, 64, 64, 64, 128, 2560, 6912]
+    assert L.bitnet_k_pad(0) == 0
+    assert L.bitnet_ternarize_workspace_bytes(6912, 2560) >= 8 * 256
+    assert L.bitlinear_fwd_workspace_bytes(4096, 6912, 2560) == 0
+    assert L.bitlinear_bwd_workspace_bytes(4096, 6912, 2560) == 0
+    for code in range(7):
+        assert L.bitnet_status_string(code).decode().startswith("BITNET_")
+
+
+# Fake, never dereferenced device addresses: validation fails before any use.
+A = 0x10000000
+MISALIGNED = 0x10000008
+
+
+def test_ternarize_validation(L):
+    ws = L.bitnet_ternarize_workspace_bytes(8, 8)
+    assert L.bitnet_ternarize_pack(None, 0, 8, 8, A, A, A, ws, None) == ENULL
+    assert L.bitnet_ternarize_pack(A, 0, 8, 8, None, A, A, ws, None) == ENULL
+    assert L.bitnet_ternarize_pack(A, 0, 8, 8, A, None, A, ws, None) == ENULL
+    assert L.bitnet_ternarize_pack(A, 7, 8, 8, A, A, A, ws, None) == EDTYPE
+    assert L.bitnet_ternarize_pack(A, 0, 0, 8, A, A, A, ws, None) == ESHAPE
+    assert L.bitnet_ternarize_pack(A, 0, 8, -1, A, A, A, ws, None) == ESHAPE
+    assert L.bitnet_ternarize_pack(MISALIGNED, 0, 8, 8, A, A, A, ws, None) == EALIGN
+    assert L.bitnet_ternarize_pack(A, 0, 8, 8, A, A, None, ws, None) == EWS
+    assert L.bitnet_ternarize_pack(A, 0, 8, 8, A, A, A, ws - 1, None) == EWS
+
+
+def test_act_quant_validation(L):
+    assert L.bitnet_act_quant(None, 4, 4, A, A, None) == ENULL
+    assert L.bitnet_act_quant(A, 0, 4, A, A, None) == ESHAPE
+    assert L.bitnet_act_quant(A, 4, 0, A, A, None) == ESHAPE
+    assert L.bitnet_act_quant(A, 4, 4, MISALIGNED, A, None) == EALIGN
+    assert L.bitnet_act_quant(A, 4, 4, A, MISALIGNED, None) == EALIGN
+
+
+def test_fwd_validation(L):
+    assert L.bitlinear_fwd(None, A, A, A, 4, 4, 4, A, None, None, 0, None) == ENULL
+    assert L.bitlinear_fwd(A, A, A, A, 4, 4, 4, None, None, None, 0, None) == ENULL
+    assert L.bitlinear_fwd(A, A, A, A, 0, 4, 4, A, None, None, 0, None) == ESHAPE
+    assert L.bitlinear_fwd(A, A, A, A, 4, 4, 1 << 25, A, None, None, 0, None) == ESHAPE
+    assert L.bitlinear_fwd(A, A, A, A, 4, 4, 4, MISALIGNED, None, None, 0, None) == EALIGN
+    assert L.bitlinear_fwd(A, A, A, A, 4, 4, 4, A, MISALIGNED, None, 0, None) == EALIGN
+    assert L.bitlinear_fwd(A, A, A, A + 2, 4, 4, 4, A, None, None, 0, None) == EALIGN
+
+
+def test_bwd_validation(L):
+    assert L.bitlinear_bwd(None, A, A, A, A, 4, 4, 4, A, A, 0, None, 0, None) == ENULL
+    assert L.bitlinear_bwd(A, A, A, A, A, 4, 4, 4, None, None, 0, None, 0, None) == ENULL
+    assert L.bitlinear_bwd(A, None, A, A, A, 4, 4, 4, None, A, 0, None, 0, None) == ENULL
+    assert L.bitlinear_bwd(A, A, A, None, A, 4, 4, 4, A, None, 0, None, 0, None) == ENULL
+    assert L.bitlinear_bwd(A, A, A, A, A, 4, 4, 4, None, A, 5, None, 0, None) == EDTYPE
+    assert L.bitlinear_bwd(A, A, A, A, A, 4, 0, 4, A, A, 0, None, 0, None) == ESHAPE
+    assert L.bitlinear_bwd(MISALIGNED, A, A, A, A, 4, 4, 4, A, A, 0, None, 0, None) == EALIGN
+    assert L.bitlinear_bwd(A, A, A, A, A, 4, 4, 4, MISALIGNED, None, 0, None, 0, None) == EALIGN
