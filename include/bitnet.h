@@ -80,11 +80,13 @@ size_t bitlinear_bwd_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *
  * W         [N][K] master weights, bf16 bits (w_dtype BITNET_BF16) or float
  *           (BITNET_F32).
- * w_packed  [N][Kp/4] output bytes. The code of W[n,k] sits in byte
- *           n*(Kp/4) + k/4 at bits 2*(k%4)..2*(k%4)+1 as a 2-bit two's
- *           complement value: +1 = 0b01, 0 = 0b00, -1 = 0b11 (0b10 is never
- *           written). Padding codes (k >= K) are 0. A little-endian 32-bit
- *           word therefore holds 16 consecutive codes, code k%16 at bits 2k.
+ * w_packed  [N][Kp/4] output bytes: row n holds Kp/16 little-endian 32-bit
+ *           words of 16 codes; word w holds k = 16w..16w+15, the code of
+ *           k = 16w + j at bit 8*(j%4) + 2*(j/4), as a 2-bit two's complement
+ *           value: +1 = 0b01, 0 = 0b00, -1 = 0b11 (0b10 is never written).
+ *           Padding codes (k >= K) are 0. (Byte b of a word holds the codes
+ *           j = b, b+4, b+8, b+12, so (word >> 2t) & 0x03030303 gives the
+ *           codes of k = 16w+4t..16w+4t+3 in its four bytes.)
  * gamma     [1] output float (device).
  * workspace device scratch of at least bitnet_ternarize_workspace_bytes();
  *           no initialization needed; clobbered.

@@ -31,10 +31,12 @@ notes of the repository):
   applied where it is used;
 * backward operands: W_hat = q * bf16(gamma), x_hat = bf16(x_q * s / 127)
   (round half to even), both exactly rounded from the exact product;
-* the 2-bit format is this project's own (the pages do not give one): the
-  code of W[n, k] sits in byte n*(Kp/4) + k//4 at bits 2*(k%4)..+1 as a 2-bit
-  two's-complement value (+1 -> 0b01, 0 -> 0b00, -1 -> 0b11), Kp = K rounded
-  up to a multiple of 64, padding codes 0.
+* the 2-bit format is this project's own (the pages do not give one): row n
+  of W is Kp/4 bytes (Kp = K rounded up to a multiple of 64), read as
+  little-endian 32-bit words of 16 codes each; the code of W[n, k] sits in
+  word k//16 of the row at bit 8*(j%4) + 2*(j//4), j = k%16, as a 2-bit
+  two's-complement value (+1 -> 0b01, 0 -> 0b00, -1 -> 0b11); padding codes
+  are 0. (Byte b of a word holds the codes j = b, b+4, b+8, b+12.)
 """
 
 import math
@@ -117,13 +119,19 @@ def k_pad(K):
     return ((int(K) + 63) // 64) * 64
 
 
+def code_bit(j):
+    """Bit offset of code j (0..15) inside its 32-bit word."""
+    return 8 * (j % 4) + 2 * (j // 4)
+
+
 def pack_codes(q, Kp=None):
     """2-bit packing of ternary codes [N, K] into bytes [N, Kp/4].
 
     The pages state that the fused pass packs 2 bits per weight
     ("bitnet-qat-train", opening bullets) but give no format; the format here
-    is this project's: byte n*(Kp/4) + k//4, bits 2*(k%4)..+1, two's
-    complement (+1 -> 01, 0 -> 00, -1 -> 11), zero codes in the padding.
+    is this project's: 16 codes per little-endian 32-bit word, code j of word
+    w (k = 16w + j) at bit 8*(j%4) + 2*(j//4), two's complement (+1 -> 01,
+    0 -> 00, -1 -> 11), zero codes in the padding.
     """
     q = np.asarray(q, dtype=np.int64)
     N, K = q.shape
@@ -131,17 +139,20 @@ def pack_codes(q, Kp=None):
         Kp = k_pad(K)
     full = np.zeros((N, Kp), dtype=np.int64)
     full[:, :K] = q
-    f = (full & 3).reshape(N, Kp // 4, 4)
-    packed = f[..., 0] | (f[..., 1] << 2) | (f[..., 2] << 4) | (f[..., 3] << 6)
-    return packed.astype(np.uint8)
+    f = (full & 3).reshape(N, Kp // 16, 16)
+    words = np.zeros((N, Kp // 16), dtype=np.int64)
+    for j in range(16):
+        words |= f[..., j] << code_bit(j)
+    return words.astype("<u4").view(np.uint8).reshape(N, Kp // 4)
 
 
 def unpack_codes(packed, K):
     """Inverse of ``pack_codes``: bytes [N, Kp/4] -> codes int8 [N, K].
     The unused field value 0b10 raises."""
-    p = np.asarray(packed, dtype=np.uint8).astype(np.int64)
+    p = np.ascontiguousarray(np.asarray(packed, dtype=np.uint8))
     N = p.shape[0]
-    fields = (p[..., None] >> np.array([0, 2, 4, 6])) & 3
+    words = p.view("<u4").astype(np.int64)
+    fields = np.stack([(words >> code_bit(j)) & 3 for j in range(16)], axis=-1)
     if np.any(fields == 2):
         raise ValueError("unpack_codes: field value 0b10 is never written")
     vals = np.where(fields == 3, -1, fields).reshape(N, -1)

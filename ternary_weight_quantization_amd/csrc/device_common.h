@@ -51,3 +51,34 @@ __device__ __forceinline__ float wave_max_f32(float v) {
 }
 
 }  // namespace bitnet
+
+namespace bitnet {
+
+// Raw buffer access (CDNA buffer resource, stride 0): loads at byte offsets
+// >= num_records return zeros, which gives branch-free zero fill for rows
+// and stages past an operand's end. Offsets are 32-bit, so one operand
+// addressed this way must stay below 2 GiB (checked by the C ABI).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOob = 0x80000000u;  // an offset past every resource
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t num_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)num_bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t off) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ uint2 buf_load8(rsrc_t r, uint32_t off) {
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+  return make_uint2(v.x, v.y);
+}
+
+__device__ __forceinline__ uint32_t buf_load4(rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+
+}  // namespace bitnet

@@ -4,19 +4,18 @@
 //
 //     C[i][j] = sum_r P[i][r] * Q[j][r],      output O[j][i] (i contiguous)
 //
-// with both operand tiles staged in LDS as [row][r] (reduction contiguous,
-// 64 bytes of reduction per row per stage, rows padded to 80 bytes so that
-// 16-byte fragment reads of 8 consecutive rows hit distinct banks). The
-// staging step converts each operand from its stored form into MFMA-ready
-// values once per block:
+// with both operand tiles staged in LDS with the reduction axis contiguous,
+// 64 bf16 or 128 int8 reduction values per row per stage:
 //
 //   forward  y[m][n]  = sum_k x_q[m][k] q[n][k]        i = n, j = m, r = k
-//            P = 2-bit codes unpacked to int8, Q = x_q copied;
-//            v_mfma_i32_32x32x32_i8, exact int32 accumulation
+//            P = the 2-bit codes as stored (expanded to int8 after the
+//            fragment read), Q = x_q copied; v_mfma_i32_32x32x32_i8, exact
+//            int32 accumulation
 //   dX       dX[m][k] = sum_n dY[m][n] W_hat[n][k]     i = k, j = m, r = n
-//            P = codes transposed and unpacked to bf16 (+-1, 0), Q = dY
-//            copied; v_mfma_f32_32x32x16_bf16; bf16(gamma) applied in the
-//            epilogue (exact: q * bf16(gamma) is exact in bf16)
+//            P = the 2-bit codes transposed to [k][n] (expanded to bf16 +-1, 0
+//            after the fragment read), Q = dY copied; v_mfma_f32_32x32x16_bf16;
+//            bf16(gamma) applied in the epilogue (exact: q * bf16(gamma) is
+//            exact in bf16)
 //   dW       dW[n][k] = sum_m dY[m][n] x_hat[m][k]     i = k, j = n, r = m
 //            P = x_q transposed and rescaled to bf16 x_hat, Q = dY
 //            transposed; v_mfma_f32_32x32x16_bf16
@@ -25,17 +24,23 @@
 // rebuilt transiently from the 2-bit / INT8 state; Semantics - forward
 // formula and STE backward dX = dY W_hat, dW = dY^T x_hat.)
 //
-// Block tile 256 x 256, 8 waves in a 2 (i) x 4 (j) grid, wave tile 128 x 64
-// = 4 x 2 fragments of 32 x 32. Two LDS stages (one barrier per stage) with
-// the next stage's global loads held in registers while the current stage's
-// MFMAs run.
+// The LDS traffic, not the MFMA rate, bounds these kernels on gfx950 (about
+// 128 B/clk/CU of 16-byte reads and 64 B/clk/CU of 16-byte writes), so the
+// ternary operand stays 2-bit in LDS and is expanded in registers.
+//
+// Block tile 256 x 256, 4 waves (one per SIMD) in a 2 x 2 grid, wave tile
+// 128 x 128 = 4 x 4 fragments of 32 x 32 (256 accumulator registers per
+// lane, held in AGPRs). Two LDS stages (one barrier per stage); while the
+// MFMAs of stage s run, the registers holding stage s+1 are converted and
+// stored into the other LDS buffer and stage s+2 is fetched into them, one
+// quarter per k-step.
 //
 // MFMA 32x32 output layout (both instructions): lane l, accumulator element
 // v holds row i = 8*(v/4) + 4*(l/32) + (v%4), column j = l%32. Operand
-// fragments: lane l supplies 16 bytes of row (l%32) of its operand at
-// reduction chunk (l/32) of the step; the same slot-to-reduction-index map is
-// used for P and Q, so the hardware's internal order of the reduction index
-// within a step does not matter.
+// fragments: lane l supplies 16 bytes of row (l%32) of its operand for lane
+// half h = l/32 of the k-step; which reduction values those are (red_chunk)
+// is the same for P and Q of a GEMM, so the hardware's internal order of the
+// reduction index within a step does not matter.
 
 #include "device_common.h"
 #include "internal.h"
@@ -43,15 +48,32 @@
 namespace bitnet {
 
 constexpr int kBI = 256, kBJ = 256;
-constexpr int kThreads = 512;
-constexpr int kWavesI = 2, kWavesJ = 4;
+constexpr int kThreads = 256;        // 4 waves, one per SIMD
+constexpr int kWavesI = 2, kWavesJ = 2;
 constexpr int kWTI = kBI / kWavesI;  // 128
-constexpr int kWTJ = kBJ / kWavesJ;  // 64
+constexpr int kWTJ = kBJ / kWavesJ;  // 128
 constexpr int kFI = kWTI / 32;       // 4
-constexpr int kFJ = kWTJ / 32;       // 2
-constexpr int kStageBytes = 64;
-constexpr int kPitch = kStageBytes + 16;
-constexpr int kTileBytes = 256 * kPitch;
+constexpr int kFJ = kWTJ / 32;       // 4
+constexpr int kStageBytes = 128;     // operand bytes per row per stage (bf16 or int8)
+constexpr int kKSteps = kStageBytes / 32;
+constexpr int kPitch = kStageBytes + 16;  // plain tiles: 9 chunks of 16 bytes
+constexpr int kRed16 = kStageBytes / 2;   // bf16 reduction elements per stage
+
+// Byte offset of 16-byte chunk c (0..7) of a plain LDS tile row r. Tiles
+// written by the transposing loaders (one chunk of many rows at a time)
+// XOR-swizzle the chunk index with bits 4..6 of the row so those stores
+// spread over the banks; the other tiles are stored plainly.
+template <bool SWZ>
+__device__ __forceinline__ int lds_off(int r, int c) {
+  return r * kPitch + ((SWZ ? (c ^ ((r >> 4) & 7)) : c) << 4);
+}
+
+// 16-byte reduction chunk (8 bf16 or 16 int8 values) that lane half h
+// supplies at k-step ks. MAP 0: chunk 2ks + h; MAP 1: chunk 4h + ks.
+template <int MAP>
+__device__ __forceinline__ constexpr int red_chunk(int ks, int h) {
+  return MAP == 0 ? 2 * ks + h : 4 * h + ks;
+}
 
 // ---------------------------------------------------------------------------
 // MFMA flavours
@@ -73,235 +95,525 @@ struct MfmaBf16 {
   }
 };
 
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// Fragment readers: per k-step, the kFI (or kFJ) fragments of a wave.
+// prefetch<KS>() issues the LDS reads for k-step KS, get<KS>(f) returns
+// fragment f of k-step KS. init() points the reader at a stage's tile.
+// ---------------------------------------------------------------------------
+
+// 16-byte fragments read directly from a plain tile (pitch kPitch).
+template <class MT, bool SWZ, int MAP>
+struct PlainFrags {
+  typename MT::Frag buf[2][4];
+  const char* base;
+  __device__ __forceinline__ void init(const char* tile, int row0, int lane) {
+    // row0 is a multiple of 128, so the swizzle of row row0 + 32f + (l%32)
+    // is 2f + bit 4 of l (fragment offsets below)
+    const int h = lane >> 5;
+    if constexpr (SWZ) {
+      static_assert(MAP == 0, "swizzled tiles use chunk map 0");
+      base = tile + (row0 + (lane & 31)) * kPitch + 16 * (h ^ ((lane >> 4) & 1));
+    } else {
+      base = tile + (row0 + (lane & 31)) * kPitch + 16 * red_chunk<MAP>(0, h);
+    }
+  }
+  template <int KS>
+  static __device__ __forceinline__ constexpr int off(int f) {
+    return SWZ ? f * 32 * kPitch + 32 * (KS ^ f) : f * 32 * kPitch + 16 * (MAP == 0 ? 2 * KS : KS);
+  }
+  template <int KS>
+  __device__ __forceinline__ void prefetch() {
+#pragma unroll
+    for (int f = 0; f < 4; ++f) buf[KS & 1][f] = *reinterpret_cast<const typename MT::Frag*>(base + off<KS>(f));
+  }
+  template <int KS>
+  __device__ __forceinline__ typename MT::Frag get(int f) const { return buf[KS & 1][f]; }
+};
+
+// Four 2-bit codes in the byte lanes of c (values 0, 1, 3) -> four int8.
+__device__ __forceinline__ uint32_t codes4_to_i8(uint32_t c) {
+  // table: code 0 -> 0x00, 1 -> 0x01, 3 -> 0xFF (code 2 never written)
+  return perm(0u, 0xFF000100u, c);
+}
+
+// Four 2-bit codes in the byte lanes of c -> two words of bf16 (+1 = 0x3F80,
+// -1 = 0xBF80, 0 = 0).
+__device__ __forceinline__ uint2 codes4_to_bf16(uint32_t c) {
+  constexpr uint32_t kLo = 0x80008000u;  // low bytes of bf16(code) for codes 0..3
+  constexpr uint32_t kHi = 0xBF003F00u;  // high bytes
+  const uint32_t s0 = perm(c, c, 0x01010000u) + 0x04000400u;
+  const uint32_t s1 = perm(c, c, 0x03030202u) + 0x04000400u;
+  return make_uint2(perm(kHi, kLo, s0), perm(kHi, kLo, s1));
+}
+
+// Forward P: rows of 2-bit codes in the stored layout (tile pitch 48 bytes,
+// 32 bytes = 8 words = 128 codes per row per stage). Lane half h of k-step
+// ks takes word 4h + ks (codes k = 16(4h+ks)..+15, chunk map 1); one 16-byte
+// read per fragment per stage, expanded with (w >> 2t) & 0x03030303.
+struct CodesI8Frags {
+  static constexpr int kPitchB = 48;
+  uint4 raw[4];
+  const char* base;
+  __device__ __forceinline__ void init(const char* tile, int row0, int lane) {
+    base = tile + (row0 + (lane & 31)) * kPitchB + 16 * (lane >> 5);
+  }
+  template <int KS>
+  __device__ __forceinline__ void prefetch() {
+    if constexpr (KS == 0) {
+#pragma unroll
+      for (int f = 0; f < 4; ++f) raw[f] = *reinterpret_cast<const uint4*>(base + f * 32 * kPitchB);
+    }
+  }
+  template <int KS>
+  __device__ __forceinline__ MfmaI8::Frag get(int f) const {
+    const uint32_t w = KS == 0 ? raw[f].x : KS == 1 ? raw[f].y : KS == 2 ? raw[f].z : raw[f].w;
+    MfmaI8::Frag a;
+    a[0] = (int)codes4_to_i8(w & 0x03030303u);
+    a[1] = (int)codes4_to_i8((w >> 2) & 0x03030303u);
+    a[2] = (int)codes4_to_i8((w >> 4) & 0x03030303u);
+    a[3] = (int)codes4_to_i8((w >> 6) & 0x03030303u);
+    return a;
+  }
+};
+
+// dX P: 2-bit codes transposed to [k][n] (tile pitch 24 bytes, 4 words = 64
+// n-codes per row per stage). Word v holds n = 16v..16v+15 in the stored
+// in-word order (code n' at bit 8(n'%4) + 2(n'/4)). Lane half h of k-step
+// ks takes n = 32h + 8ks..+7 (chunk map 1): word 2h + ks/2, fields
+// t = 2(ks%2), +1. One 8-byte read per fragment per stage.
+struct CodesBf16TFrags {
+  static constexpr int kPitchB = 24;
+  uint2 raw[4];
+  const char* base;
+  __device__ __forceinline__ void init(const char* tile, int row0, int lane) {
+    base = tile + (row0 + (lane & 31)) * kPitchB + 8 * (lane >> 5);
+  }
+  template <int KS>
+  __device__ __forceinline__ void prefetch() {
+    if constexpr (KS == 0) {
+#pragma unroll
+      for (int f = 0; f < 4; ++f) raw[f] = *reinterpret_cast<const uint2*>(base + f * 32 * kPitchB);
+    }
+  }
+  template <int KS>
+  __device__ __forceinline__ MfmaBf16::Frag get(int f) const {
+    const uint32_t w = KS < 2 ? raw[f].x : raw[f].y;
+    constexpr int t0 = 2 * (KS & 1);
+    const uint2 lo = codes4_to_bf16((w >> (2 * t0)) & 0x03030303u);
+    const uint2 hi = codes4_to_bf16((w >> (2 * t0 + 2)) & 0x03030303u);
+    return __builtin_bit_cast(MfmaBf16::Frag, u32x4_t{lo.x, lo.y, hi.x, hi.y});
+  }
+};
+
 // ---------------------------------------------------------------------------
 // Operand loaders. load(): global -> registers for one stage (rows row0..+255
-// of the operand, reduction stage s); store(): registers -> LDS tile.
+// of the operand, reduction stage s); store(): registers -> LDS tile (used
+// for the first stage); stage_part<P>(): quarter P of the staging of the next
+// stage from registers into LDS and of the fetch of the stage after it.
+// Out-of-range data (rows past the operand, reduction past its end, stages
+// past the last) reads as zeros through the buffer resource range check or
+// an out-of-range offset, so the loads of a stage are issued without
+// branches. Each thread's addresses are a per-thread base plus offsets that
+// are uniform or compile-time.
 // ---------------------------------------------------------------------------
 
 // Row-major source already in MFMA element form with the reduction axis
-// contiguous (x_q for the forward, dY for dX). 2 x 16 bytes per thread.
-template <int kElem, bool VEC>
+// contiguous (x_q for the forward, dY for dX). Thread t handles chunk t%8 of
+// rows 8(t/8)+h, h < 8; a wave instruction covers 8 rows x 128 bytes.
+// FULL: the valid reduction extent is a multiple of 16 bytes.
+template <int kElem, bool FULL>
 struct CopyLoader {
+  static constexpr bool kSwz = false;
+  static constexpr int kTileB = 256 * kPitch;
+  template <class MT, int MAP>
+  using Frags = PlainFrags<MT, false, MAP>;
   const char* base;
   int64_t pitch;      // bytes between rows
   int64_t rows;       // valid rows
   int64_t red_bytes;  // valid reduction bytes per row
-  struct Regs { uint4 v[2]; };
+  struct Regs { uint4 v[8]; };
 
   __device__ __forceinline__ void load(Regs& r, int row0, int s, float*) const {
     const int tid = threadIdx.x;
+    const int64_t rowb = row0 + 8 * (tid >> 3);
+    const int64_t kb = (int64_t)s * kStageBytes + (tid & 7) * 16;
+    if constexpr (FULL) {
+      // rows past the end fall outside the resource; chunks past the
+      // reduction (and stages past the last) get an out-of-range offset
+      const rsrc_t rs = make_rsrc(base, (uint32_t)(rows * pitch));
+      const uint32_t off = kb < red_bytes ? (uint32_t)(rowb * pitch + kb) : kOob;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int c = tid + h * kThreads;
-      const int64_t row = row0 + (c >> 2);
-      const int64_t kb = (int64_t)s * kStageBytes + (c & 3) * 16;
-      const char* src = base + row * pitch + kb;
-      if (row < rows && VEC && kb + 16 <= red_bytes) {
-        r.v[h] = *reinterpret_cast<const uint4*>(src);
-      } else if (row < rows && kb < red_bytes) {
+      for (int h = 0; h < 8; ++h) r.v[h] = buf_load16(rs, off + (uint32_t)(h * pitch));
+    } else {
+      const char* p = base + rowb * pitch + kb;
+#pragma unroll
+      for (int h = 0; h < 8; ++h) {
         uint32_t d[4] = {0, 0, 0, 0};
-        if constexpr (kElem == 1) {
+        if (kb < red_bytes && rowb + h < rows) {
+          const char* src = p + h * pitch;
+          if constexpr (kElem == 1) {
 #pragma unroll
-          for (int e = 0; e < 16; ++e)
-            if (kb + e < red_bytes) d[e >> 2] |= uint32_t(uint8_t(src[e])) << (8 * (e & 3));
-        } else {
+            for (int e = 0; e < 16; ++e)
+              if (kb + e < red_bytes) d[e >> 2] |= uint32_t(uint8_t(src[e])) << (8 * (e & 3));
+          } else {
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (kb + 2 * e < red_bytes)
-              d[e >> 1] |= uint32_t(*reinterpret_cast<const uint16_t*>(src + 2 * e)) << (16 * (e & 1));
+            for (int e = 0; e < 8; ++e)
+              if (kb + 2 * e < red_bytes)
+                d[e >> 1] |= uint32_t(*reinterpret_cast<const uint16_t*>(src + 2 * e)) << (16 * (e & 1));
+          }
         }
         r.v[h] = make_uint4(d[0], d[1], d[2], d[3]);
-      } else {
-        r.v[h] = make_uint4(0, 0, 0, 0);
       }
     }
   }
   __device__ __forceinline__ void store(const Regs& r, char* lds, const float*) const {
     const int tid = threadIdx.x;
+    char* dst = lds + lds_off<kSwz>(8 * (tid >> 3), tid & 7);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int c = tid + h * kThreads;
-      *reinterpret_cast<uint4*>(lds + (c >> 2) * kPitch + (c & 3) * 16) = r.v[h];
+    for (int h = 0; h < 8; ++h) *reinterpret_cast<uint4*>(dst + h * kPitch) = r.v[h];
+  }
+
+  // Staging split into 4 parts (one per k-step of the current stage): part
+  // P stores rows 2P, 2P+1 of the thread's block, then refills those
+  // registers with stage s+2.
+  struct Tmp {};
+  template <int P>
+  __device__ __forceinline__ void stage_part(Regs& r, Tmp&, char* lds, const float*, int row0, int s2,
+                                             float*) const {
+    const int tid = threadIdx.x;
+    char* dst = lds + lds_off<kSwz>(8 * (tid >> 3), tid & 7);
+#pragma unroll
+    for (int h = 2 * P; h < 2 * P + 2; ++h) *reinterpret_cast<uint4*>(dst + h * kPitch) = r.v[h];
+    if constexpr (FULL) {
+      const rsrc_t rs = make_rsrc(base, (uint32_t)(rows * pitch));
+      const int64_t rowb = row0 + 8 * (tid >> 3);
+      const int64_t kb = (int64_t)s2 * kStageBytes + (tid & 7) * 16;
+      const uint32_t off = kb < red_bytes ? (uint32_t)(rowb * pitch + kb) : kOob;
+#pragma unroll
+      for (int h = 2 * P; h < 2 * P + 2; ++h) r.v[h] = buf_load16(rs, off + (uint32_t)(h * pitch));
+    } else if (P == 3) {
+      load(r, row0, s2, nullptr);
     }
   }
 };
 
-// 4 codes of one packed byte -> 4 int8 in one word (byte p = code p).
-__device__ __forceinline__ uint32_t unpack4_i8(uint32_t b) {
-  uint32_t s = b | (b << 6) | (b << 12) | (b << 18);
-  s &= 0x03030303u;
-  // table: code 0 -> 0x00, 1 -> 0x01, 3 -> 0xFF (code 2 never written)
-  return perm(0u, 0xFF000100u, s);
-}
-
-// Forward P: packed codes [N][Kp/4], rows n, reduction k contiguous.
-// 8 packed bytes (32 codes) per thread -> 32 int8.
-struct PackedRowLoader {
+// Forward P: the 2-bit codes [N][Kp/4] copied as stored (rows n, 32 bytes
+// per stage). Thread t handles row t: two 16-byte loads.
+struct PackedCodesLoader {
+  static constexpr bool kSwz = false;
+  static constexpr int kTileB = 256 * CodesI8Frags::kPitchB;
+  template <class MT, int MAP>
+  using Frags = CodesI8Frags;
   const uint8_t* packed;
-  int64_t pitch;  // Kp/4
+  int64_t pitch;  // Kp/4 (a multiple of 16)
   int64_t rows;   // N
-  struct Regs { uint2 v; };
+  struct Regs { uint4 v[2]; };
+  struct Tmp {};
 
+  __device__ __forceinline__ uint32_t offset(int row0, int s, int h) const {
+    const int64_t row = row0 + threadIdx.x;
+    const int64_t col = (int64_t)s * (kStageBytes / 4) + 16 * h;
+    return col < pitch ? (uint32_t)(row * pitch + col) : kOob;
+  }
   __device__ __forceinline__ void load(Regs& r, int row0, int s, float*) const {
-    const int tid = threadIdx.x;
-    const int64_t row = row0 + (tid >> 1);
-    if (row < rows)
-      r.v = *reinterpret_cast<const uint2*>(packed + row * pitch + (int64_t)s * 16 + (tid & 1) * 8);
-    else
-      r.v = make_uint2(0, 0);
+    const rsrc_t rs = make_rsrc(packed, (uint32_t)(rows * pitch));
+#pragma unroll
+    for (int h = 0; h < 2; ++h) r.v[h] = buf_load16(rs, offset(row0, s, h));
   }
   __device__ __forceinline__ void store(const Regs& r, char* lds, const float*) const {
-    const int tid = threadIdx.x;
-    char* dst = lds + (tid >> 1) * kPitch + (tid & 1) * 32;
-    uint4 a, b;
-    a.x = unpack4_i8(r.v.x & 0xFF); a.y = unpack4_i8((r.v.x >> 8) & 0xFF);
-    a.z = unpack4_i8((r.v.x >> 16) & 0xFF); a.w = unpack4_i8(r.v.x >> 24);
-    b.x = unpack4_i8(r.v.y & 0xFF); b.y = unpack4_i8((r.v.y >> 8) & 0xFF);
-    b.z = unpack4_i8((r.v.y >> 16) & 0xFF); b.w = unpack4_i8(r.v.y >> 24);
-    reinterpret_cast<uint4*>(dst)[0] = a;
-    reinterpret_cast<uint4*>(dst)[1] = b;
+    char* dst = lds + threadIdx.x * CodesI8Frags::kPitchB;
+    *reinterpret_cast<uint4*>(dst) = r.v[0];
+    *reinterpret_cast<uint4*>(dst + 16) = r.v[1];
+  }
+  // Parts 0 and 1 store one half of the row and refill it with stage s+2.
+  template <int P>
+  __device__ __forceinline__ void stage_part(Regs& r, Tmp&, char* lds, const float*, int row0, int s2,
+                                             float*) const {
+    if constexpr (P < 2) {
+      *reinterpret_cast<uint4*>(lds + threadIdx.x * CodesI8Frags::kPitchB + 16 * P) = r.v[P];
+      const rsrc_t rs = make_rsrc(packed, (uint32_t)(rows * pitch));
+      r.v[P] = buf_load16(rs, offset(row0, s2, P));
+    }
   }
 };
 
-// dX P: W_hat^T from packed codes [N][Kp/4]: rows k, reduction n (strided).
-// Thread (ng = tid/64, kq = tid%64) reads one packed byte (codes of k =
-// 4kq..4kq+3) from each of the rows n = 4ng..4ng+3 and writes, for each of
-// its 4 k, the 4 codes as bf16 (+1 = 0x3F80, -1 = 0xBF80, 0 = 0).
-struct PackedTransposeLoader {
+// The byte selected by `sel` from each of a0..a3 -> one word (a0's lowest).
+__device__ __forceinline__ uint32_t gather_byte(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3,
+                                                uint32_t sel) {
+  const uint32_t t01 = perm(a1, a0, sel);
+  const uint32_t t23 = perm(a3, a2, sel);
+  return perm(t23, t01, 0x05040100u);
+}
+
+// dX P: the 2-bit codes [N][Kp/4] transposed into [k][n] code words. A
+// stage is 64 n-rows x 64 bytes (k0..k0+255). Wave w handles n = 16w..+15
+// (word w of every k row): lane (r = l/16, d = l%16) loads word d (k =
+// k0+16d..+15) of rows n = 16w+4g+r, g < 4. Byte r of such a word holds the
+// codes of k = k0+16d+r+4i (i < 4) at bits 2i; an in-wave byte transpose
+// (ds_bpermute) gives lane (r, d) byte r of the 16 rows, from which it
+// assembles, for each i, the word of row k = 16d+r+4i: code of n = 16w+4g+e
+// at bit 8e+2g. The four rows are written in a lane-rotated order to spread
+// the stores over the banks.
+struct PackedCodesTLoader {
+  static constexpr bool kSwz = false;
+  static constexpr int kTileB = 256 * CodesBf16TFrags::kPitchB;
+  template <class MT, int MAP>
+  using Frags = CodesBf16TFrags;
   const uint8_t* packed;
   int64_t pitch;  // Kp/4 bytes per n row
   int64_t nred;   // N (valid reduction rows)
-  struct Regs { uint32_t b; };
+  struct Regs { uint32_t d[4]; };
+  struct Tmp { uint32_t W[4]; };
 
   __device__ __forceinline__ void load(Regs& r, int row0, int s, float*) const {
     const int tid = threadIdx.x;
-    const int64_t n = (int64_t)s * 32 + 4 * (tid >> 6);
-    const int64_t col = (row0 >> 2) + (tid & 63);  // byte within the row
-    uint32_t b = 0;
-    if (col < pitch) {
-      const uint8_t* src = packed + n * pitch + col;
+    const int lane = tid & 63, w = tid >> 6;
+    const rsrc_t rs = make_rsrc(packed, (uint32_t)(nred * pitch));
+    const int64_t col = (row0 >> 2) + 4 * (lane & 15);  // byte within the row
+    const int64_t n = (int64_t)s * 64 + 16 * w + (lane >> 4);
+    const uint32_t off = col < pitch ? (uint32_t)(n * pitch + col) : kOob;
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (n + e < nred) b |= uint32_t(src[e * pitch]) << (8 * e);
+    for (int g = 0; g < 4; ++g) r.d[g] = buf_load4(rs, off + (uint32_t)(4 * g * pitch));
+  }
+  __device__ __forceinline__ void transpose(const Regs& r, Tmp& t) const {
+    const int lane = threadIdx.x & 63;
+    const int rr = lane >> 4, d = lane & 15;
+    const uint32_t sel = (uint32_t)rr | ((uint32_t)(rr + 4) << 8);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      uint32_t a[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[e] = (uint32_t)__builtin_amdgcn_ds_bpermute((16 * e + d) << 2, (int)r.d[g]);
+      t.W[g] = gather_byte(a[0], a[1], a[2], a[3], sel);
     }
-    r.b = b;
+  }
+  // write row 16d + r + 4i' (i' = (I + d) % 4) of the wave's word column
+  template <int I>
+  __device__ __forceinline__ void write_row(const Tmp& t, char* lds) const {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    const int rr = lane >> 4, d = lane & 15;
+    const int ii = (I + d) & 3;
+    uint32_t out = 0;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) out |= ((t.W[g] >> (2 * ii)) & 0x03030303u) << (2 * g);
+    *reinterpret_cast<uint32_t*>(lds + (16 * d + rr + 4 * ii) * CodesBf16TFrags::kPitchB + 4 * w) = out;
   }
   __device__ __forceinline__ void store(const Regs& r, char* lds, const float*) const {
-    const int tid = threadIdx.x;
-    const int kq = tid & 63, ng = tid >> 6;
-    constexpr uint32_t kLo = 0x80008000u;  // low bytes of bf16(code) for codes 0..3
-    constexpr uint32_t kHi = 0xBF003F00u;  // high bytes
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t c = (r.b >> (2 * p)) & 0x03030303u;  // codes of n0..n3 for k = 4kq+p
-      const uint32_t s0 = perm(c, c, 0x01010000u) + 0x04000400u;
-      const uint32_t s1 = perm(c, c, 0x03030202u) + 0x04000400u;
-      uint2 o;
-      o.x = perm(kHi, kLo, s0);
-      o.y = perm(kHi, kLo, s1);
-      *reinterpret_cast<uint2*>(lds + (4 * kq + p) * kPitch + 8 * ng) = o;
-    }
+    Tmp t;
+    transpose(r, t);
+    write_row<0>(t, lds);
+    write_row<1>(t, lds);
+    write_row<2>(t, lds);
+    write_row<3>(t, lds);
+  }
+  // Part 0 transposes, parts 0..3 each write one row; part 1 refills the
+  // registers with stage s+2.
+  template <int P>
+  __device__ __forceinline__ void stage_part(Regs& r, Tmp& t, char* lds, const float*, int row0, int s2,
+                                             float*) const {
+    if constexpr (P == 0) transpose(r, t);
+    write_row<P>(t, lds);
+    if constexpr (P == 1) load(r, row0, s2, nullptr);
   }
 };
 
-// dW Q: dY^T: rows n, reduction m (strided). Thread (mg = tid/64, nq =
-// tid%64) reads 4 bf16 (n = 4nq..4nq+3) from each of the rows m = 4mg..+3
-// and writes a 4x4 transpose.
+// dW Q: dY^T: rows n, reduction m (strided). Thread (mg = wave, nq = lane)
+// reads 4 bf16 (n = 4nq..4nq+3) from each of the rows m = 16mg..16mg+15 and
+// writes the 16 x 4 transpose as 4 rows of 16 m values.
 template <bool VEC>
 struct RowTransposeBf16Loader {
+  static constexpr bool kSwz = true;
+  static constexpr int kTileB = 256 * kPitch;
+  template <class MT, int MAP>
+  using Frags = PlainFrags<MT, true, MAP>;
   const uint16_t* dy;
   int64_t ld;    // N
   int64_t mred;  // M (valid reduction rows)
   int64_t rows;  // N (valid rows)
-  struct Regs { uint2 v[4]; };
+  struct Regs { uint2 v[16]; };
 
   __device__ __forceinline__ void load(Regs& r, int row0, int s, float*) const {
     const int tid = threadIdx.x;
-    const int64_t m = (int64_t)s * 32 + 4 * (tid >> 6);
+    const int64_t m = (int64_t)s * kRed16 + 16 * (tid >> 6);
     const int64_t n = row0 + 4 * (tid & 63);
+    if constexpr (VEC) {
+      const rsrc_t rs = make_rsrc(dy, (uint32_t)(mred * ld * 2));
+      const uint32_t off = n < rows ? (uint32_t)((m * ld + n) * 2) : kOob;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint16_t* src = dy + (m + e) * ld + n;
-      if (m + e < mred && VEC && n + 4 <= rows) {
-        r.v[e] = *reinterpret_cast<const uint2*>(src);
-      } else if (m + e < mred && n < rows) {
-        uint32_t d[4];
+      for (int e = 0; e < 16; ++e) r.v[e] = buf_load8(rs, off + (uint32_t)(e * ld * 2));
+    } else {
+      const uint16_t* p = dy + m * ld + n;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) d[q] = (n + q < rows) ? src[q] : 0u;
-        r.v[e] = make_uint2(d[0] | (d[1] << 16), d[2] | (d[3] << 16));
-      } else {
-        r.v[e] = make_uint2(0, 0);
+      for (int e = 0; e < 16; ++e) {
+        uint32_t q[4] = {0, 0, 0, 0};
+        if (m + e < mred) {
+          const uint16_t* src = p + e * ld;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) q[j] = (n + j < rows) ? src[j] : 0u;
+        }
+        r.v[e] = make_uint2(q[0] | (q[1] << 16), q[2] | (q[3] << 16));
       }
     }
   }
   __device__ __forceinline__ void store(const Regs& r, char* lds, const float*) const {
     const int tid = threadIdx.x;
     const int nq = tid & 63, mg = tid >> 6;
-    char* dst = lds + (4 * nq) * kPitch + 8 * mg;
-    // column q of the 4x4 block: (m0, m1) from halves of v[0], v[1]; (m2, m3) from v[2], v[3]
-    uint2 o;
-    o.x = perm(r.v[1].x, r.v[0].x, 0x05040100u);
-    o.y = perm(r.v[3].x, r.v[2].x, 0x05040100u);
-    *reinterpret_cast<uint2*>(dst + 0 * kPitch) = o;
-    o.x = perm(r.v[1].x, r.v[0].x, 0x07060302u);
-    o.y = perm(r.v[3].x, r.v[2].x, 0x07060302u);
-    *reinterpret_cast<uint2*>(dst + 1 * kPitch) = o;
-    o.x = perm(r.v[1].y, r.v[0].y, 0x05040100u);
-    o.y = perm(r.v[3].y, r.v[2].y, 0x05040100u);
-    *reinterpret_cast<uint2*>(dst + 2 * kPitch) = o;
-    o.x = perm(r.v[1].y, r.v[0].y, 0x07060302u);
-    o.y = perm(r.v[3].y, r.v[2].y, 0x07060302u);
-    *reinterpret_cast<uint2*>(dst + 3 * kPitch) = o;
+    // element (m = e, n = q) is half (q & 1) of word (q >> 1) of v[e]
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      char* dst = lds + lds_off<kSwz>(4 * nq, 2 * mg + hh);  // rows 4nq..4nq+3 share the swizzle
+      const uint2* v = r.v + 8 * hh;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t sel = (q & 1) ? 0x07060302u : 0x05040100u;
+        uint4 o;
+        o.x = perm((q >> 1) ? v[1].y : v[1].x, (q >> 1) ? v[0].y : v[0].x, sel);
+        o.y = perm((q >> 1) ? v[3].y : v[3].x, (q >> 1) ? v[2].y : v[2].x, sel);
+        o.z = perm((q >> 1) ? v[5].y : v[5].x, (q >> 1) ? v[4].y : v[4].x, sel);
+        o.w = perm((q >> 1) ? v[7].y : v[7].x, (q >> 1) ? v[6].y : v[6].x, sel);
+        *reinterpret_cast<uint4*>(dst + q * kPitch) = o;
+      }
+    }
+  }
+
+  // Part P writes half hh = P/2 (m rows 8hh..8hh+7 of the thread's 16) for
+  // n columns q = 2(P&1), +1; odd parts then refill that half's 8 rows with
+  // stage s+2.
+  struct Tmp {};
+  template <int P>
+  __device__ __forceinline__ void stage_part(Regs& r, Tmp&, char* lds, const float*, int row0, int s2,
+                                             float*) const {
+    constexpr int hh = P >> 1;
+    const int tid = threadIdx.x;
+    const int nq = tid & 63, mg = tid >> 6;
+    char* dst = lds + lds_off<kSwz>(4 * nq, 2 * mg + hh);
+    const uint2* v = r.v + 8 * hh;
+#pragma unroll
+    for (int q = 2 * (P & 1); q < 2 * (P & 1) + 2; ++q) {
+      const uint32_t sel = (q & 1) ? 0x07060302u : 0x05040100u;
+      uint4 o;
+      o.x = perm((q >> 1) ? v[1].y : v[1].x, (q >> 1) ? v[0].y : v[0].x, sel);
+      o.y = perm((q >> 1) ? v[3].y : v[3].x, (q >> 1) ? v[2].y : v[2].x, sel);
+      o.z = perm((q >> 1) ? v[5].y : v[5].x, (q >> 1) ? v[4].y : v[4].x, sel);
+      o.w = perm((q >> 1) ? v[7].y : v[7].x, (q >> 1) ? v[6].y : v[6].x, sel);
+      *reinterpret_cast<uint4*>(dst + q * kPitch) = o;
+    }
+    if constexpr (P & 1) {
+      if constexpr (VEC) {
+        const rsrc_t rs = make_rsrc(dy, (uint32_t)(mred * ld * 2));
+        const int64_t m = (int64_t)s2 * kRed16 + 16 * mg;
+        const int64_t n = row0 + 4 * nq;
+        const uint32_t off = n < rows ? (uint32_t)((m * ld + n) * 2) : kOob;
+#pragma unroll
+        for (int e = 8 * hh; e < 8 * hh + 8; ++e) r.v[e] = buf_load8(rs, off + (uint32_t)(e * ld * 2));
+      } else if (P == 3) {
+        load(r, row0, s2, nullptr);
+      }
+    }
   }
 };
 
 // dW P: x_hat^T from x_q [M][Kp] and s[M]: rows k, reduction m (strided).
-// x_hat = bf16(fl32(x_q * fl32(s/127))); for bf16 scales this equals the
-// exactly rounded bf16(x_q * s / 127). Thread (mg, kq) reads 4 int8 (k =
-// 4kq..+3) from rows m = 4mg..+3. The 32 scales of a stage are computed by
-// the first 32 threads when the stage is loaded and published in LDS.
+// x_hat = bf16(fl32(x_q * fl32(s/127))); for the scales act-quant produces
+// this equals the exactly rounded bf16(x_q * s / 127). Thread (mg = wave, kq
+// = lane) reads 4 int8 (k = 4kq..+3) from each of the rows m = 16mg..+15.
+// The 64 scales of a stage are computed by wave 0 when the stage is loaded
+// and published in LDS.
 struct Int8TransposeScaleLoader {
+  static constexpr bool kSwz = true;
+  static constexpr int kTileB = 256 * kPitch;
+  template <class MT, int MAP>
+  using Frags = PlainFrags<MT, true, MAP>;
   const int8_t* xq;
   const float* s;
   int64_t pitch;  // Kp
   int64_t mred;   // M
-  struct Regs { uint32_t d[4]; };
+  struct Regs { uint32_t d[16]; };
 
   __device__ __forceinline__ void load(Regs& r, int row0, int st, float* scale_out) const {
     const int tid = threadIdx.x;
-    const int64_t m = (int64_t)st * 32 + 4 * (tid >> 6);
+    const rsrc_t rs = make_rsrc(xq, (uint32_t)(mred * pitch));
+    const int64_t m = (int64_t)st * kRed16 + 16 * (tid >> 6);
     const int64_t k = row0 + 4 * (tid & 63);
+    const uint32_t off = k < pitch ? (uint32_t)(m * pitch + k) : kOob;
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      r.d[e] = (m + e < mred && k < pitch) ? *reinterpret_cast<const uint32_t*>(xq + (m + e) * pitch + k) : 0u;
-    if (tid < 32) {
-      const int64_t mm = (int64_t)st * 32 + tid;
-      scale_out[tid] = (mm < mred) ? s[mm] / 127.0f : 0.0f;
-    }
+    for (int e = 0; e < 16; ++e) r.d[e] = buf_load4(rs, off + (uint32_t)(e * pitch));
+    // every wave computes the stage's 64 scales (identical values, so the
+    // four stores of each entry agree); rows past M get 0
+    const rsrc_t rsc = make_rsrc(s, (uint32_t)(mred * 4));
+    const uint32_t mm = (uint32_t)(st * kRed16 + (tid & 63));
+    scale_out[tid & 63] = __uint_as_float(buf_load4(rsc, mm * 4)) / 127.0f;
   }
   __device__ __forceinline__ void store(const Regs& r, char* lds, const float* scale_in) const {
     const int tid = threadIdx.x;
     const int kq = tid & 63, mg = tid >> 6;
-    float rs[4], off[4];
-    uint32_t u[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      rs[e] = scale_in[4 * mg + e];
-      off[e] = -128.0f * rs[e];       // exact
-      u[e] = r.d[e] ^ 0x80808080u;    // bytes x_q + 128 in [1, 255]
-    }
+    for (int hh = 0; hh < 2; ++hh) {
+      char* dst = lds + lds_off<kSwz>(4 * kq, 2 * mg + hh);  // rows 4kq..4kq+3 share the swizzle
+      const float4 sa = *reinterpret_cast<const float4*>(scale_in + 16 * mg + 8 * hh);
+      const float4 sb = *reinterpret_cast<const float4*>(scale_in + 16 * mg + 8 * hh + 4);
+      const float rs[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      float v[4];
+      for (int p = 0; p < 4; ++p) {
+        float v[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float f = (float)((u[e] >> (8 * p)) & 0xFFu);
-        v[e] = fmaf(f, rs[e], off[e]);  // = fl32(x_q * r): single rounding of the exact value
+        for (int e = 0; e < 8; ++e) {
+          // byte p of row e biased to [1, 255]: f*r - 128r = x_q*r exactly
+          // before the single rounding of the fma
+          const float f = (float)(((r.d[8 * hh + e] ^ 0x80808080u) >> (8 * p)) & 0xFFu);
+          v[e] = fmaf(f, rs[e], -128.0f * rs[e]);
+        }
+        *reinterpret_cast<uint4*>(dst + p * kPitch) =
+            make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                       pack_bf16x2(v[6], v[7]));
       }
-      uint2 o;
-      o.x = pack_bf16x2(v[0], v[1]);
-      o.y = pack_bf16x2(v[2], v[3]);
-      *reinterpret_cast<uint2*>(lds + (4 * kq + p) * kPitch + 8 * mg) = o;
+    }
+  }
+
+  // Part P converts half hh = P/2 (m rows 8hh..8hh+7 of the thread's 16) for
+  // k rows p = 2(P&1), +1; odd parts refill that half with stage s+2, and
+  // the last part also publishes stage s+2's scales.
+  struct Tmp { float rs[8]; };
+  template <int P>
+  __device__ __forceinline__ void stage_part(Regs& r, Tmp& t, char* lds, const float* scale_in, int row0,
+                                             int s2, float* scale_out) const {
+    constexpr int hh = P >> 1;
+    const int tid = threadIdx.x;
+    const int kq = tid & 63, mg = tid >> 6;
+    if constexpr ((P & 1) == 0) {
+      const float4 sa = *reinterpret_cast<const float4*>(scale_in + 16 * mg + 8 * hh);
+      const float4 sb = *reinterpret_cast<const float4*>(scale_in + 16 * mg + 8 * hh + 4);
+      t.rs[0] = sa.x; t.rs[1] = sa.y; t.rs[2] = sa.z; t.rs[3] = sa.w;
+      t.rs[4] = sb.x; t.rs[5] = sb.y; t.rs[6] = sb.z; t.rs[7] = sb.w;
+    }
+    char* dst = lds + lds_off<kSwz>(4 * kq, 2 * mg + hh);
+#pragma unroll
+    for (int p = 2 * (P & 1); p < 2 * (P & 1) + 2; ++p) {
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float f = (float)(((r.d[8 * hh + e] ^ 0x80808080u) >> (8 * p)) & 0xFFu);
+        v[e] = fmaf(f, t.rs[e], -128.0f * t.rs[e]);
+      }
+      *reinterpret_cast<uint4*>(dst + p * kPitch) =
+          make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                     pack_bf16x2(v[6], v[7]));
+    }
+    if constexpr (P & 1) {
+      const rsrc_t rs = make_rsrc(xq, (uint32_t)(mred * pitch));
+      const int64_t m = (int64_t)s2 * kRed16 + 16 * mg;
+      const int64_t k = row0 + 4 * kq;
+      const uint32_t off = k < pitch ? (uint32_t)(m * pitch + k) : kOob;
+#pragma unroll
+      for (int e = 8 * hh; e < 8 * hh + 8; ++e) r.d[e] = buf_load4(rs, off + (uint32_t)(e * pitch));
+    }
+    if constexpr (P == 3) {
+      const rsrc_t rsc = make_rsrc(s, (uint32_t)(mred * 4));
+      const uint32_t mm = (uint32_t)(s2 * kRed16 + (tid & 63));
+      scale_out[tid & 63] = __uint_as_float(buf_load4(rsc, mm * 4)) / 127.0f;
     }
   }
 };
@@ -427,11 +739,93 @@ __device__ __forceinline__ void zero_acc(Acc& a) {
   for (int e = 0; e < 16; ++e) a[e] = 0;
 }
 
-template <class MT, class PL, class QL, class EP>
+// Instruction classes of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSgMfma = 0x008, kSgValu = 0x002, kSgVmemRead = 0x020, kSgDsRead = 0x100,
+              kSgDsWrite = 0x200;
+
+// Order inside one k-step, after its fragment reads: the 16 MFMAs, each
+// followed by a share of the VALU work (fragment expansion, staging), with
+// the staging's LDS stores, LDS reads and global loads spread between them.
+__device__ __forceinline__ void kstep_schedule() {
+#pragma unroll
+  for (int m = 0; m < kFI * kFJ; ++m) {
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgValu, 3, 0);
+    if ((m & 3) == 0) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+    if ((m & 3) == 1) __builtin_amdgcn_sched_group_barrier(kSgDsWrite, 1, 0);
+    if ((m & 3) == 3) __builtin_amdgcn_sched_group_barrier(kSgVmemRead, 2, 0);
+  }
+}
+
+template <int KS, class MT, class PL, class QL, class FP, class FQ>
+__device__ __forceinline__ void gemm_kstep(const PL& pl, const QL& ql, typename PL::Regs& pr,
+                                           typename QL::Regs& qr, typename PL::Tmp& pt,
+                                           typename QL::Tmp& qt, FP& fp, FQ& fq, char* Pn, char* Qn,
+                                           const float* sc_next, float* sc_after,
+                                           typename MT::Acc (&acc)[kFI][kFJ], int i0, int j0, int s2) {
+  if constexpr (KS + 1 < kKSteps) {
+    fp.template prefetch<KS + 1>();
+    fq.template prefetch<KS + 1>();
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  typename MT::Frag a[kFI], b[kFJ];
+#pragma unroll
+  for (int fi = 0; fi < kFI; ++fi) a[fi] = fp.template get<KS>(fi);
+#pragma unroll
+  for (int fj = 0; fj < kFJ; ++fj) b[fj] = fq.template get<KS>(fj);
+#pragma unroll
+  for (int fi = 0; fi < kFI; ++fi)
+#pragma unroll
+    for (int fj = 0; fj < kFJ; ++fj) acc[fi][fj] = MT::mma(a[fi], b[fj], acc[fi][fj]);
+  pl.template stage_part<KS>(pr, pt, Pn, sc_next, i0, s2, sc_after);
+  ql.template stage_part<KS>(qr, qt, Qn, sc_next, j0, s2, sc_after);
+  kstep_schedule();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// LDS: two stages, each a P tile followed by a Q tile; then the per-stage
+// scales of loaders that publish them.
+template <class PL, class QL>
+struct SmemLayout {
+  static constexpr int kStage = PL::kTileB + QL::kTileB;
+  static constexpr int kBytes = 2 * kStage;
+};
+
+// One pipeline stage: MFMAs on LDS buffer CUR for reduction stage s, while
+// staging stage s+1 from registers into buffer CUR^1 and fetching stage s+2
+// into those registers, one quarter per k-step. Past the last stage the
+// staging runs on zeros and is never read.
+template <int CUR, class MT, int MAP, class PL, class QL>
+__device__ __forceinline__ void gemm_stage(const PL& pl, const QL& ql, typename PL::Regs& pr,
+                                           typename QL::Regs& qr, char* smem, float (*sscale)[kRed16],
+                                           typename MT::Acc (&acc)[kFI][kFJ], int i0, int j0, int s,
+                                           int prow0, int qrow0, int lane) {
+  typedef SmemLayout<PL, QL> L;
+  char* cur = smem + CUR * L::kStage;
+  char* nxt = smem + (CUR ^ 1) * L::kStage;
+  typename PL::template Frags<MT, MAP> fp;
+  typename QL::template Frags<MT, MAP> fq;
+  fp.init(cur, prow0, lane);
+  fq.init(cur + PL::kTileB, qrow0, lane);
+  fp.template prefetch<0>();
+  fq.template prefetch<0>();
+  typename PL::Tmp pt;
+  typename QL::Tmp qt;
+  char* Pn = nxt;
+  char* Qn = nxt + PL::kTileB;
+  gemm_kstep<0, MT>(pl, ql, pr, qr, pt, qt, fp, fq, Pn, Qn, sscale[CUR ^ 1], sscale[CUR], acc, i0, j0, s + 2);
+  gemm_kstep<1, MT>(pl, ql, pr, qr, pt, qt, fp, fq, Pn, Qn, sscale[CUR ^ 1], sscale[CUR], acc, i0, j0, s + 2);
+  gemm_kstep<2, MT>(pl, ql, pr, qr, pt, qt, fp, fq, Pn, Qn, sscale[CUR ^ 1], sscale[CUR], acc, i0, j0, s + 2);
+  gemm_kstep<3, MT>(pl, ql, pr, qr, pt, qt, fp, fq, Pn, Qn, sscale[CUR ^ 1], sscale[CUR], acc, i0, j0, s + 2);
+  __syncthreads();
+}
+
+template <class MT, int MAP, class PL, class QL, class EP>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(PL pl, QL ql, EP ep, int tiles_i,
                                                           int tiles_j, int nstages) {
-  __shared__ __attribute__((aligned(16))) char smem[2][2][kTileBytes];
-  __shared__ float sscale[2][32];
+  typedef SmemLayout<PL, QL> L;
+  __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
+  __shared__ __attribute__((aligned(16))) float sscale[2][kRed16];
 
   int ti, tj;
   map_tile(blockIdx.x, tiles_i, tiles_j, ti, tj);
@@ -450,54 +844,29 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(PL pl, QL ql, EP ep, 
   pl.load(pr, i0, 0, sscale[0]);
   ql.load(qr, j0, 0, sscale[0]);
   __syncthreads();  // per-stage scales published by load()
-  pl.store(pr, smem[0][0], sscale[0]);
-  ql.store(qr, smem[0][1], sscale[0]);
-  if (nstages > 1) {
-    pl.load(pr, i0, 1, sscale[1]);
-    ql.load(qr, j0, 1, sscale[1]);
-  }
+  pl.store(pr, smem, sscale[0]);
+  ql.store(qr, smem + PL::kTileB, sscale[0]);
+  pl.load(pr, i0, 1, sscale[1]);
+  ql.load(qr, j0, 1, sscale[1]);
   __syncthreads();
 
-  const int prow = wi * kWTI + (lane & 31);
-  const int qrow = wj * kWTJ + (lane & 31);
-  for (int s = 0; s < nstages; ++s) {
-    const char* Pt = smem[s & 1][0];
-    const char* Qt = smem[s & 1][1];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int chunk = 2 * ks + (lane >> 5);
-      typename MT::Frag a[kFI], b[kFJ];
-#pragma unroll
-      for (int fi = 0; fi < kFI; ++fi)
-        a[fi] = *reinterpret_cast<const typename MT::Frag*>(Pt + (prow + 32 * fi) * kPitch + chunk * 16);
-#pragma unroll
-      for (int fj = 0; fj < kFJ; ++fj)
-        b[fj] = *reinterpret_cast<const typename MT::Frag*>(Qt + (qrow + 32 * fj) * kPitch + chunk * 16);
-#pragma unroll
-      for (int fi = 0; fi < kFI; ++fi)
-#pragma unroll
-        for (int fj = 0; fj < kFJ; ++fj) acc[fi][fj] = MT::mma(a[fi], b[fj], acc[fi][fj]);
-    }
-    if (s + 1 < nstages) {
-      pl.store(pr, smem[(s + 1) & 1][0], sscale[(s + 1) & 1]);
-      ql.store(qr, smem[(s + 1) & 1][1], sscale[(s + 1) & 1]);
-    }
-    if (s + 2 < nstages) {
-      pl.load(pr, i0, s + 2, sscale[s & 1]);
-      ql.load(qr, j0, s + 2, sscale[s & 1]);
-    }
-    __syncthreads();
+  const int prow0 = wi * kWTI, qrow0 = wj * kWTJ;
+  int s = 0;
+  for (; s + 1 < nstages; s += 2) {
+    gemm_stage<0, MT, MAP>(pl, ql, pr, qr, smem, sscale, acc, i0, j0, s, prow0, qrow0, lane);
+    gemm_stage<1, MT, MAP>(pl, ql, pr, qr, smem, sscale, acc, i0, j0, s + 1, prow0, qrow0, lane);
   }
+  if (s < nstages) gemm_stage<0, MT, MAP>(pl, ql, pr, qr, smem, sscale, acc, i0, j0, s, prow0, qrow0, lane);
   ep.store(acc, i0 + wi * kWTI, j0 + wj * kWTJ, lane);
 }
 
-template <class MT, class PL, class QL, class EP>
+template <class MT, int MAP, class PL, class QL, class EP>
 static hipError_t run_gemm(const PL& pl, const QL& ql, const EP& ep, int64_t I, int64_t J,
                            int64_t nstages, hipStream_t stream) {
   const int tiles_i = (int)((I + kBI - 1) / kBI);
   const int tiles_j = (int)((J + kBJ - 1) / kBJ);
-  gemm_kernel<MT, PL, QL, EP><<<tiles_i * tiles_j, kThreads, 0, stream>>>(pl, ql, ep, tiles_i, tiles_j,
-                                                                         (int)nstages);
+  gemm_kernel<MT, MAP, PL, QL, EP><<<tiles_i * tiles_j, kThreads, 0, stream>>>(pl, ql, ep, tiles_i,
+                                                                              tiles_j, (int)nstages);
   return hipGetLastError();
 }
 
@@ -509,40 +878,40 @@ hipError_t launch_fwd(const int8_t* x_q, const float* s_x, const uint8_t* w_pack
                       const float* gamma, int64_t M, int64_t N, int64_t K, uint16_t* y,
                       int32_t* acc_out, hipStream_t stream) {
   const int64_t Kp = k_pad(K);
-  PackedRowLoader pl{w_packed, Kp / 4, N};
+  PackedCodesLoader pl{w_packed, Kp / 4, N};
   CopyLoader<1, true> ql{reinterpret_cast<const char*>(x_q), Kp, M, Kp};
   FwdEpilogue ep{y, acc_out, s_x, gamma, N, M, N % 4 == 0};
-  return run_gemm<MfmaI8>(pl, ql, ep, N, M, Kp / 64, stream);
+  return run_gemm<MfmaI8, 1>(pl, ql, ep, N, M, (Kp + kStageBytes - 1) / kStageBytes, stream);
 }
 
 hipError_t launch_bwd_dx(const uint16_t* dY, const uint8_t* w_packed, const float* gamma,
                          int64_t M, int64_t N, int64_t K, uint16_t* dX, hipStream_t stream) {
   const int64_t Kp = k_pad(K);
-  PackedTransposeLoader pl{w_packed, Kp / 4, N};
+  PackedCodesTLoader pl{w_packed, Kp / 4, N};
   Bf16Epilogue<false> ep{dX, gamma, K, M, K % 4 == 0};
-  const int64_t nst = (N + 31) / 32;
+  const int64_t nst = (N + kRed16 - 1) / kRed16;
   if (N % 8 == 0) {
     CopyLoader<2, true> ql{reinterpret_cast<const char*>(dY), 2 * N, M, 2 * N};
-    return run_gemm<MfmaBf16>(pl, ql, ep, K, M, nst, stream);
+    return run_gemm<MfmaBf16, 1>(pl, ql, ep, K, M, nst, stream);
   }
   CopyLoader<2, false> ql{reinterpret_cast<const char*>(dY), 2 * N, M, 2 * N};
-  return run_gemm<MfmaBf16>(pl, ql, ep, K, M, nst, stream);
+  return run_gemm<MfmaBf16, 1>(pl, ql, ep, K, M, nst, stream);
 }
 
 hipError_t launch_bwd_dw(const uint16_t* dY, const int8_t* x_q, const float* s_x, int64_t M,
                          int64_t N, int64_t K, void* dW, bool dw_is_f32, hipStream_t stream) {
   const int64_t Kp = k_pad(K);
   Int8TransposeScaleLoader pl{x_q, s_x, Kp, M};
-  const int64_t nst = (M + 31) / 32;
+  const int64_t nst = (M + kRed16 - 1) / kRed16;
   const bool vec = (N % 4 == 0);
   if (dw_is_f32) {
     Bf16Epilogue<true> ep{dW, nullptr, K, N, K % 4 == 0};
-    if (vec) return run_gemm<MfmaBf16>(pl, RowTransposeBf16Loader<true>{dY, N, M, N}, ep, K, N, nst, stream);
-    return run_gemm<MfmaBf16>(pl, RowTransposeBf16Loader<false>{dY, N, M, N}, ep, K, N, nst, stream);
+    if (vec) return run_gemm<MfmaBf16, 0>(pl, RowTransposeBf16Loader<true>{dY, N, M, N}, ep, K, N, nst, stream);
+    return run_gemm<MfmaBf16, 0>(pl, RowTransposeBf16Loader<false>{dY, N, M, N}, ep, K, N, nst, stream);
   }
   Bf16Epilogue<false> ep{dW, nullptr, K, N, K % 4 == 0};
-  if (vec) return run_gemm<MfmaBf16>(pl, RowTransposeBf16Loader<true>{dY, N, M, N}, ep, K, N, nst, stream);
-  return run_gemm<MfmaBf16>(pl, RowTransposeBf16Loader<false>{dY, N, M, N}, ep, K, N, nst, stream);
+  if (vec) return run_gemm<MfmaBf16, 0>(pl, RowTransposeBf16Loader<true>{dY, N, M, N}, ep, K, N, nst, stream);
+  return run_gemm<MfmaBf16, 0>(pl, RowTransposeBf16Loader<false>{dY, N, M, N}, ep, K, N, nst, stream);
 }
 
 }  // namespace bitnet

@@ -154,11 +154,14 @@ __global__ __launch_bounds__(kPackThreads) void ternarize_pack_kernel(
         vals[j] = (k < K) ? load_elem<F32>(w, n * K + k) : 0.0f;
       }
     }
+    // code j of the word at bit 8*(j%4) + 2*(j/4): byte b holds the codes
+    // j = b, b+4, b+8, b+12, so (word >> 2t) & 0x03030303 lists the codes
+    // 4t..4t+3 in its four bytes
     uint32_t word = 0;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const uint32_t code = (vals[j] > h) ? 1u : ((vals[j] < -h) ? 3u : 0u);
-      word |= code << (2 * j);
+      word |= code << (8 * (j & 3) + 2 * (j >> 2));
     }
     packed[wi] = word;
   }

@@ -192,21 +192,31 @@ def test_codes_zero_fraction_statistics():
 # ---------------------------------------------------------------------------
 
 def test_pack_hand_bytes():
-    # codes +1, 0, -1, +1 -> fields 01, 00, 11, 01 from the low bits up
+    # codes of k = 0..3 are the lowest field of bytes 0..3 of the first word:
+    # +1, 0, -1, +1 -> 0x01, 0x00, 0x03, 0x01
     q = np.array([[1, 0, -1, 1]], dtype=np.int8)
     p = O.pack_codes(q, 64)
     assert p.shape == (1, 16)
-    assert p[0, 0] == 0b01_11_00_01 == 0x71
-    assert np.all(p[0, 1:] == 0)
-    q = np.array([[-1, -1, -1, -1, 1, 1, 1, 1, 0, 0, 0, -1]], dtype=np.int8)
+    assert p[0, :4].tolist() == [0x01, 0x00, 0x03, 0x01]
+    assert np.all(p[0, 4:] == 0)
+    # k = 4..7 go to bits 2..3 of bytes 0..3, k = 8..11 to bits 4..5, k = 12..15
+    # to bits 6..7
+    q = np.array([[-1, -1, -1, -1, 1, 1, 1, 1, 0, 0, 0, -1, 1, 0, 0, 0]], dtype=np.int8)
     p = O.pack_codes(q)
-    assert p[0, :3].tolist() == [0xFF, 0x55, 0xC0]
-    # a little-endian 32-bit word holds 16 consecutive codes, code k at bits 2k
+    assert p[0, :4].tolist() == [0b01_00_01_11, 0b00_00_01_11, 0b00_00_01_11, 0b00_11_01_11]
+    # word w holds k = 16w..16w+15; code j of the word at bit 8*(j%4) + 2*(j//4)
     q = np.zeros((1, 64), dtype=np.int8)
-    q[0, 17] = -1
-    q[0, 30] = 1
-    word = O.pack_codes(q).view(np.uint32)[0, 1]
-    assert word == (3 << 2) | (1 << 28)
+    q[0, 17] = -1   # word 1, j = 1 -> bit 8
+    q[0, 30] = 1    # word 1, j = 14 -> bit 16 + 6 = 22
+    word = O.pack_codes(q).view("<u4")[0, 1]
+    assert word == (3 << 8) | (1 << 22)
+    # byte b of a word holds codes j = b, b+4, b+8, b+12 (the planar property
+    # used to expand 4 codes with one shift and one mask)
+    for t in range(4):
+        q = np.zeros((1, 16), dtype=np.int8)
+        q[0, 4 * t:4 * t + 4] = [1, -1, 1, -1]
+        w = int(O.pack_codes(q).view("<u4")[0, 0])
+        assert (w >> (2 * t)) & 0x03030303 == 0x03010301
 
 
 def test_pack_roundtrip_and_padding():
