@@ -77,10 +77,12 @@ def load_traffic(kernel, workload):
     return None if e is None else e.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(inp, rows):
+def cpu_baseline(inp, target_s=12.0, probe_rows=128):
     """The oracle (as it stands) on a bounded sample of the workload: the
     whole weight ternarization plus the first `rows` tokens through
-    act-quant, forward and both backward products."""
+    act-quant, forward and both backward products. A short probe run sizes
+    `rows` so that the timed run takes about `target_s` seconds (at most all
+    M tokens, which is the whole step)."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -88,12 +90,19 @@ def cpu_baseline(inp, rows):
     from ternary_weight_quantization_amd import workloads as WL
 
     M, K, N = inp["M"], inp["K"], inp["N"]
-    x = WL.bf16_bits_to_f32(inp["x"][:rows]).astype(np.float64)
-    dY = WL.bf16_bits_to_f32(inp["dY"][:rows]).astype(np.float64)
     w = WL.bf16_bits_to_f32(inp["W"]).astype(np.float64)
-    t0 = time.perf_counter()
-    O.layer_fwd_bwd(x, w, dY)
-    dt = time.perf_counter() - t0
+
+    def run(rows):
+        x = WL.bf16_bits_to_f32(inp["x"][:rows]).astype(np.float64)
+        dY = WL.bf16_bits_to_f32(inp["dY"][:rows]).astype(np.float64)
+        t0 = time.perf_counter()
+        O.layer_fwd_bwd(x, w, dY)
+        return time.perf_counter() - t0
+
+    probe = min(M, probe_rows)
+    t_probe = run(probe)
+    rows = int(min(M, max(probe, probe * target_s / max(t_probe, 1e-3))))
+    dt = run(rows) if rows != probe else t_probe
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     ops = 6.0 * rows * N * K
     return {
@@ -103,8 +112,8 @@ def cpu_baseline(inp, rows):
         "kind": "oracle",
         "sample": f"full weight ternarization ({N}x{K}) + first {rows} of {M} tokens through "
                   f"act-quant, forward and STE backward; {dt:.2f} s wall, {ops / 1e9:.1f} G ops "
-                  f"(6*rows*N*K) on {os.cpu_count()} visible cpus",
-        "seconds": dt,
+                  f"(6*rows*N*K), numpy fp64 with {threads} BLAS threads on {os.cpu_count()} visible cpus",
+        "seconds": round(dt, 3),
     }
 
 
@@ -232,7 +241,7 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(inp, rows=256)
+        out["cpu_baseline"] = cpu_baseline(inp)
         out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 6)
     print(json.dumps(out), flush=True)
 

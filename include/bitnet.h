@@ -27,6 +27,11 @@
  *    Kp = bitnet_k_pad(K) (a multiple of 64) with zero codes and values;
  *    reductions and scales use the true K only.
  *  - Non-finite inputs (inf, NaN) give unspecified results.
+ *  - Size limits (BITNET_ERR_SHAPE beyond them): M, N <= 2^30, K <= 2^24;
+ *    for the GEMM entry points every operand the call reads among x_q,
+ *    w_packed and dY satisfies (rows + 256) * row_bytes <= 2^31, i.e.
+ *    (M + 256) * Kp, (N + 256) * Kp/4 and (M + 256) * 2N bytes (the kernels
+ *    address them with 32-bit offsets).
  */
 #ifndef BITNET_H
 #define BITNET_H

@@ -31,6 +31,21 @@ bitnet_status check_gemm_sizes(int64_t M, int64_t N, int64_t K) {
   return BITNET_OK;
 }
 
+// The GEMM kernels address x_q, w_packed, dY and s_x through buffer
+// resources with 32-bit offsets, including rows up to 256 past an operand's
+// end (read as zeros); each such range must stay below 2 GiB.
+bool buffer_range_ok(int64_t rows, int64_t pitch_bytes) {
+  return (rows + 256) * pitch_bytes <= (int64_t(1) << 31);
+}
+
+bitnet_status check_gemm_ranges(int64_t M, int64_t N, int64_t K, bool need_xq, bool need_w, bool need_dy) {
+  const int64_t Kp = bitnet::k_pad(K);
+  if (need_xq && !buffer_range_ok(M, Kp)) return BITNET_ERR_SHAPE;
+  if (need_w && !buffer_range_ok(N, Kp / 4)) return BITNET_ERR_SHAPE;
+  if (need_dy && !buffer_range_ok(M, 2 * N)) return BITNET_ERR_SHAPE;
+  return BITNET_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -86,6 +101,7 @@ bitnet_status bitlinear_fwd(const int8_t* x_q, const float* s_x, const uint8_t* 
   (void)workspace;
   if (!x_q || !s_x || !w_packed || !gamma || !y) return BITNET_ERR_NULL;
   if (bitnet_status st = check_gemm_sizes(M, N, K)) return st;
+  if (bitnet_status st = check_gemm_ranges(M, N, K, true, true, false)) return st;
   if (workspace_bytes < bitlinear_fwd_workspace_bytes(M, N, K)) return BITNET_ERR_WORKSPACE;
   if (!aligned(x_q, 16) || !aligned(s_x, 16) || !aligned(w_packed, 16) || !aligned(gamma, 4) ||
       !aligned(y, 16) || (acc_out && !aligned(acc_out, 16)))
@@ -105,6 +121,7 @@ bitnet_status bitlinear_bwd(const uint16_t* dY, const int8_t* x_q, const float* 
   if (dW && (!x_q || !s_x)) return BITNET_ERR_NULL;
   if (dW && dW_dtype != BITNET_BF16 && dW_dtype != BITNET_F32) return BITNET_ERR_DTYPE;
   if (bitnet_status st = check_gemm_sizes(M, N, K)) return st;
+  if (bitnet_status st = check_gemm_ranges(M, N, K, dW != nullptr, dX != nullptr, true)) return st;
   if (workspace_bytes < bitlinear_bwd_workspace_bytes(M, N, K)) return BITNET_ERR_WORKSPACE;
   if (!aligned(dY, 16)) return BITNET_ERR_ALIGN;
   if (dX && (!aligned(w_packed, 16) || !aligned(gamma, 4) || !aligned(dX, 16))) return BITNET_ERR_ALIGN;

@@ -95,6 +95,10 @@ def test_fwd_validation(L):
     assert L.bitlinear_fwd(A, A, A, A, 4, 4, 4, None, None, None, 0, None) == ENULL
     assert L.bitlinear_fwd(A, A, A, A, 0, 4, 4, A, None, None, 0, None) == ESHAPE
     assert L.bitlinear_fwd(A, A, A, A, 4, 4, 1 << 25, A, None, None, 0, None) == ESHAPE
+    # operands addressed with 32-bit offsets: (M + 256) * Kp bytes of x_q and
+    # (N + 256) * Kp/4 bytes of w_packed must stay within 2^31
+    assert L.bitlinear_fwd(A, A, A, A, 1 << 20, 4, 1 << 12, A, None, None, 0, None) == ESHAPE
+    assert L.bitlinear_fwd(A, A, A, A, 4, 1 << 22, 1 << 12, A, None, None, 0, None) == ESHAPE
     assert L.bitlinear_fwd(A, A, A, A, 4, 4, 4, MISALIGNED, None, None, 0, None) == EALIGN
     assert L.bitlinear_fwd(A, A, A, A, 4, 4, 4, A, MISALIGNED, None, 0, None) == EALIGN
     assert L.bitlinear_fwd(A, A, A, A + 2, 4, 4, 4, A, None, None, 0, None) == EALIGN
@@ -107,5 +111,8 @@ def test_bwd_validation(L):
     assert L.bitlinear_bwd(A, A, A, None, A, 4, 4, 4, A, None, 0, None, 0, None) == ENULL
     assert L.bitlinear_bwd(A, A, A, A, A, 4, 4, 4, None, A, 5, None, 0, None) == EDTYPE
     assert L.bitlinear_bwd(A, A, A, A, A, 4, 0, 4, A, A, 0, None, 0, None) == ESHAPE
+    # dY is addressed with 32-bit offsets: (M + 256) * 2N bytes within 2^31
+    assert L.bitlinear_bwd(A, A, A, A, A, 1 << 16, 1 << 15, 64, A, None, 0, None, 0, None) == ESHAPE
+    assert L.bitlinear_bwd(A, A, A, A, A, 1 << 16, 1 << 15, 64, None, A, 0, None, 0, None) == ESHAPE
     assert L.bitlinear_bwd(MISALIGNED, A, A, A, A, 4, 4, 4, A, A, 0, None, 0, None) == EALIGN
     assert L.bitlinear_bwd(A, A, A, A, A, 4, 4, 4, MISALIGNED, None, 0, None, 0, None) == EALIGN
