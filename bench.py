@@ -49,7 +49,90 @@ def parse():
     p.add_argument("--workload", default="c2_up_4096x2560x6912")
     p.add_argument("--rotate", type=int, default=4)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="run only a plain device copy of known size (for counter calibration)")
+    p.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR"),
+                   help="turn rocprofv3 FETCH_SIZE / WRITE_SIZE runs of the bench and of --copy-calibration "
+                        "into profiles/pmc_traffic.json (no GPU needed)")
     return p.parse_args()
+
+
+# bench kernel name -> substrings of the device kernel names it launches
+KERNEL_MATCH = {
+    "ternarize_pack": ["absmean_partials_kernel", "ternarize_pack_kernel"],
+    "act_quant": ["act_quant"],
+    "fwd_i8": ["PackedCodesLoader"],
+    "bwd_dx_bf16": ["PackedCodesTLoader"],
+    "bwd_dw_bf16": ["Int8TransposeScaleLoader"],
+}
+COPY_BYTES = 256 << 20
+
+
+def copy_calibration():
+    """A plain device-to-device copy of COPY_BYTES, three times: the
+    counters of this kernel calibrate FETCH_SIZE / WRITE_SIZE (it must read
+    and write exactly COPY_BYTES each)."""
+    import torch
+
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 3}), flush=True)
+
+
+def _pmc_rows(d):
+    import glob
+    import sqlite3
+
+    rows = []
+    for db in sorted(glob.glob(os.path.join(d, "**", "*.db"), recursive=True)):
+        con = sqlite3.connect(db)
+        rows += list(con.execute("select name, counter_name, counter_value from pmc_events"))
+        con.close()
+    if not rows:
+        raise SystemExit(f"no pmc_events in {d}")
+    return rows
+
+
+def _per_dispatch_mean(rows, counter, match):
+    vals = [v for name, cn, v in rows if cn == counter and any(m in name for m in match)]
+    return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
+
+
+def summarize_pmc(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of each bench kernel,
+    scaled by copy_bytes / (the copy kernel's reading): HBM bytes per launch."""
+    cal = {}
+    for counter, d in (("FETCH_SIZE", cal_fetch_dir), ("WRITE_SIZE", cal_write_dir)):
+        rows = _pmc_rows(d)
+        # torch's same-dtype device copy runs the runtime's copy kernel
+        vals = [v for name, cn, v in rows if cn == counter and "copyBuffer" in name]
+        if not vals:
+            raise SystemExit(f"no copy kernel counters in {d}")
+        name = next(n for n, cn, _ in rows if cn == counter and "copyBuffer" in n)
+        kib = sum(vals) / len(vals)
+        cal[counter] = {"kernel": name[:120], "kib_per_dispatch": kib, "factor": COPY_BYTES / (kib * 1024.0)}
+    fetch_rows, write_rows = _pmc_rows(fetch_dir), _pmc_rows(write_dir)
+    kernels = {}
+    for bname, match in KERNEL_MATCH.items():
+        # a bench call may launch several kernels: sum their per-dispatch means
+        f_total = w_total = 0.0
+        n_f = n_w = 0
+        for m in match:
+            f, nf = _per_dispatch_mean(fetch_rows, "FETCH_SIZE", [m])
+            w, nw = _per_dispatch_mean(write_rows, "WRITE_SIZE", [m])
+            if f is None or w is None:
+                raise SystemExit(f"no counters for {m}")
+            f_total += f * 1024.0 * cal["FETCH_SIZE"]["factor"]
+            w_total += w * 1024.0 * cal["WRITE_SIZE"]["factor"]
+            n_f += nf
+            n_w += nw
+        kernels[bname] = {"fetch_bytes": round(f_total), "write_bytes": round(w_total),
+                          "hbm_bytes_per_launch": round(f_total + w_total), "dispatches": [n_f, n_w]}
+    return {"source_hash": source_hash(), "calibration": cal, "kernels": kernels}
 
 
 def source_hash():
@@ -60,10 +143,14 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
+def traffic_path(workload):
+    return os.path.join(ROOT, "profiles", f"pmc_traffic_{workload}.json")
+
+
 def load_traffic(kernel, workload):
     """HBM bytes per launch from the committed rocprofv3 counter summary,
     if it was taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    path = traffic_path(workload)
     if not os.path.exists(path):
         return None
     try:
@@ -73,16 +160,18 @@ def load_traffic(kernel, workload):
         return None
     if d.get("source_hash") != source_hash():
         return None
-    e = d.get("kernels", {}).get(f"{kernel}@{workload}")
+    e = d.get("kernels", {}).get(kernel)
     return None if e is None else e.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(inp, target_s=12.0, probe_rows=128):
-    """The oracle (as it stands) on a bounded sample of the workload: the
-    whole weight ternarization plus the first `rows` tokens through
-    act-quant, forward and both backward products. A short probe run sizes
-    `rows` so that the timed run takes about `target_s` seconds (at most all
-    M tokens, which is the whole step)."""
+def cpu_baseline(inp, target_s=12.0, chunk=256):
+    """The oracle (as it stands) timed on a bounded sample of the workload.
+    The sample is whole steps repeated: each pass ternarizes the full weight
+    and then runs the M tokens, `chunk` rows at a time, through act-quant,
+    forward and both backward products (dW summed over the chunks). Timing
+    stops at the first chunk boundary after `target_s` seconds, so the
+    sample is bounded on any host; the rate counts 6*rows*N*K ops for the
+    rows processed."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -90,39 +179,63 @@ def cpu_baseline(inp, target_s=12.0, probe_rows=128):
     from ternary_weight_quantization_amd import workloads as WL
 
     M, K, N = inp["M"], inp["K"], inp["N"]
-    w = WL.bf16_bits_to_f32(inp["W"]).astype(np.float64)
-
-    def run(rows):
-        x = WL.bf16_bits_to_f32(inp["x"][:rows]).astype(np.float64)
-        dY = WL.bf16_bits_to_f32(inp["dY"][:rows]).astype(np.float64)
-        t0 = time.perf_counter()
-        O.layer_fwd_bwd(x, w, dY)
-        return time.perf_counter() - t0
-
-    probe = min(M, probe_rows)
-    t_probe = run(probe)
-    rows = int(min(M, max(probe, probe * target_s / max(t_probe, 1e-3))))
-    dt = run(rows) if rows != probe else t_probe
+    Kp = O.k_pad(K)
+    w = WL.bf16_bits_to_f32(inp["W"]).astype(np.float64) if inp["w_dtype"] == "bf16" \
+        else np.asarray(inp["W"], dtype=np.float64)
+    rows_done = passes = 0
+    t0 = time.perf_counter()
+    while True:
+        gamma = O.absmean_gamma(w)
+        q = O.ternary_codes(w, gamma)
+        O.pack_codes(q, Kp)
+        dW = np.zeros((N, K))
+        passes += 1
+        for r0 in range(0, M, chunk):
+            x = WL.bf16_bits_to_f32(inp["x"][r0:r0 + chunk]).astype(np.float64)
+            dY = WL.bf16_bits_to_f32(inp["dY"][r0:r0 + chunk]).astype(np.float64)
+            x_q, sx = O.act_quant(x, Kp)
+            O.forward_y(O.forward_acc(x_q, q), sx, gamma)
+            _, dW_part = O.backward(dY, x_q, sx, q, gamma)
+            dW += dW_part
+            rows_done += x.shape[0]
+            if time.perf_counter() - t0 >= target_s:
+                break
+        if time.perf_counter() - t0 >= target_s:
+            break
+    dt = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    ops = 6.0 * rows * N * K
+    ops = 6.0 * rows_done * N * K
     return {
         "value": ops / dt / 1e12,
         "unit": "TOPS",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"full weight ternarization ({N}x{K}) + first {rows} of {M} tokens through "
-                  f"act-quant, forward and STE backward; {dt:.2f} s wall, {ops / 1e9:.1f} G ops "
-                  f"(6*rows*N*K), numpy fp64 with {threads} BLAS threads on {os.cpu_count()} visible cpus",
+        "sample": f"{passes} pass(es) of the step (full {N}x{K} weight ternarization + the {M} tokens in "
+                  f"chunks of {chunk} through act-quant, forward and STE backward), stopped after "
+                  f"{rows_done} token rows; {dt:.2f} s wall, {ops / 1e9:.1f} G ops (6*rows*N*K), numpy fp64 "
+                  f"with {threads} BLAS threads on {os.cpu_count()} visible cpus",
         "seconds": round(dt, 3),
     }
 
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        out = summarize_pmc(*args.summarize_pmc)
+        out["workload"] = args.workload
+        out["command"] = " ".join(sys.argv)
+        with open(traffic_path(args.workload), "w") as f:
+            json.dump(out, f, indent=1)
+        print(json.dumps(out["kernels"]))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (the layer is not sharded); "
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import numpy as np
     import torch
