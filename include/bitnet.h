@@ -67,8 +67,15 @@ int64_t bitnet_k_pad(int64_t K);
 /* Bytes of workspace bitnet_ternarize_pack needs (fixed, a few KiB). */
 size_t bitnet_ternarize_workspace_bytes(int64_t N, int64_t K);
 
-/* Bytes of workspace bitlinear_fwd / bitlinear_bwd need for these sizes.
- * 0 means the call takes no workspace (the pointer may then be NULL). */
+/* Bytes of workspace bitlinear_fwd / bitlinear_bwd need for these sizes
+ * (0 for sizes the call rejects). 0 means the call takes no workspace (the
+ * pointer may then be NULL). The GEMMs need workspace when they split
+ * output tiles over several workgroups so that all CUs stay busy: 16 bytes
+ * of tagged counters per 256 x 256 output tile and 256 KiB of partial sums
+ * per workgroup piece, at most about 128 MiB. The contents need no
+ * initialization; a workspace must not be shared by calls that may run at
+ * the same time (calls on one stream may share it). bitlinear_bwd's size
+ * covers both of its products, which run one after the other. */
 size_t bitlinear_fwd_workspace_bytes(int64_t M, int64_t N, int64_t K);
 size_t bitlinear_bwd_workspace_bytes(int64_t M, int64_t N, int64_t K);
 

@@ -117,6 +117,27 @@ def bitlinear_bwd_workspace_bytes(M, N, K):
     return int(lib().bitlinear_bwd_workspace_bytes(int(M), int(N), int(K)))
 
 
+# --- GEMM workspace ----------------------------------------------------------
+
+_workspaces = {}
+
+
+def _workspace(nbytes, like, stream):
+    """A cached device buffer of at least nbytes for the GEMM calls, one per
+    (device, stream): calls on one stream run in order and may share it.
+    The library needs no particular contents."""
+    if nbytes == 0:
+        return None
+    if stream is None:
+        stream = torch.cuda.current_stream(like.device)
+    key = (like.device.index, stream.cuda_stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty((nbytes,), dtype=torch.uint8, device=like.device)
+        _workspaces[key] = ws
+    return ws
+
+
 # --- entry points ----------------------------------------------------------
 
 def bitnet_ternarize_pack(W, w_packed, gamma, workspace, stream=None):
@@ -159,6 +180,8 @@ def bitlinear_fwd(x_q, s_x, w_packed, gamma, K, y, acc_out=None, workspace=None,
     _need(y, torch.bfloat16, (M, N), "y")
     if acc_out is not None:
         _need(acc_out, torch.int32, (M, N), "acc_out")
+    if workspace is None:
+        workspace = _workspace(bitlinear_fwd_workspace_bytes(M, N, K), y, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().bitlinear_fwd(_ptr(x_q), _ptr(s_x), _ptr(w_packed), _ptr(gamma), M, N, int(K),
                                _ptr(y), _ptr(acc_out), _ptr(workspace), ws_bytes, _stream(stream)))
@@ -182,6 +205,8 @@ def bitlinear_bwd(dY, x_q, s_x, w_packed, gamma, K, dX=None, dW=None, workspace=
         _need(dW, dW.dtype, (N, int(K)), "dW")
         if dW.dtype not in (torch.bfloat16, torch.float32):
             raise TypeError("dW: expected bfloat16 or float32")
+    if workspace is None:
+        workspace = _workspace(bitlinear_bwd_workspace_bytes(M, N, K), dY, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().bitlinear_bwd(_ptr(dY), _ptr(x_q), _ptr(s_x), _ptr(w_packed), _ptr(gamma),
                                M, N, int(K), _ptr(dX), _ptr(dW), dw_dtype, _ptr(workspace), ws_bytes,

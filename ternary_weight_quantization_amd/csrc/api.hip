@@ -69,8 +69,18 @@ size_t bitnet_ternarize_workspace_bytes(int64_t, int64_t) {
   return sizeof(double) * bitnet::kAbsmeanBlocks;
 }
 
-size_t bitlinear_fwd_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
-size_t bitlinear_bwd_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
+size_t bitlinear_fwd_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (check_gemm_sizes(M, N, K) != BITNET_OK) return 0;
+  return bitnet::gemm_workspace_bytes(bitnet::GemmKind::kFwd, M, N, K);
+}
+
+size_t bitlinear_bwd_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (check_gemm_sizes(M, N, K) != BITNET_OK) return 0;
+  // dX and dW run one after the other on the stream and share the workspace
+  const size_t a = bitnet::gemm_workspace_bytes(bitnet::GemmKind::kBwdDx, M, N, K);
+  const size_t b = bitnet::gemm_workspace_bytes(bitnet::GemmKind::kBwdDw, M, N, K);
+  return a > b ? a : b;
+}
 
 bitnet_status bitnet_ternarize_pack(const void* W, bitnet_dtype w_dtype, int64_t N, int64_t K,
                                     uint8_t* w_packed, float* gamma, void* workspace,
@@ -98,23 +108,23 @@ bitnet_status bitnet_act_quant(const uint16_t* x, int64_t M, int64_t K, int8_t* 
 bitnet_status bitlinear_fwd(const int8_t* x_q, const float* s_x, const uint8_t* w_packed,
                             const float* gamma, int64_t M, int64_t N, int64_t K, uint16_t* y,
                             int32_t* acc_out, void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace;
   if (!x_q || !s_x || !w_packed || !gamma || !y) return BITNET_ERR_NULL;
   if (bitnet_status st = check_gemm_sizes(M, N, K)) return st;
   if (bitnet_status st = check_gemm_ranges(M, N, K, true, true, false)) return st;
   if (workspace_bytes < bitlinear_fwd_workspace_bytes(M, N, K)) return BITNET_ERR_WORKSPACE;
+  if (workspace_bytes > 0 && !workspace) return BITNET_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return BITNET_ERR_ALIGN;
   if (!aligned(x_q, 16) || !aligned(s_x, 16) || !aligned(w_packed, 16) || !aligned(gamma, 4) ||
       !aligned(y, 16) || (acc_out && !aligned(acc_out, 16)))
     return BITNET_ERR_ALIGN;
-  return from_hip(bitnet::launch_fwd(x_q, s_x, w_packed, gamma, M, N, K, y, acc_out,
-                                     static_cast<hipStream_t>(stream)));
+  return from_hip(bitnet::launch_fwd(x_q, s_x, w_packed, gamma, M, N, K, y, acc_out, workspace,
+                                     workspace_bytes, static_cast<hipStream_t>(stream)));
 }
 
 bitnet_status bitlinear_bwd(const uint16_t* dY, const int8_t* x_q, const float* s_x,
                             const uint8_t* w_packed, const float* gamma, int64_t M, int64_t N,
                             int64_t K, uint16_t* dX, void* dW, bitnet_dtype dW_dtype,
                             void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace;
   if (!dY) return BITNET_ERR_NULL;
   if (!dX && !dW) return BITNET_ERR_NULL;
   if (dX && (!w_packed || !gamma)) return BITNET_ERR_NULL;
@@ -123,15 +133,18 @@ bitnet_status bitlinear_bwd(const uint16_t* dY, const int8_t* x_q, const float* 
   if (bitnet_status st = check_gemm_sizes(M, N, K)) return st;
   if (bitnet_status st = check_gemm_ranges(M, N, K, dW != nullptr, dX != nullptr, true)) return st;
   if (workspace_bytes < bitlinear_bwd_workspace_bytes(M, N, K)) return BITNET_ERR_WORKSPACE;
+  if (workspace_bytes > 0 && !workspace) return BITNET_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return BITNET_ERR_ALIGN;
   if (!aligned(dY, 16)) return BITNET_ERR_ALIGN;
   if (dX && (!aligned(w_packed, 16) || !aligned(gamma, 4) || !aligned(dX, 16))) return BITNET_ERR_ALIGN;
   if (dW && (!aligned(x_q, 16) || !aligned(s_x, 16) || !aligned(dW, 16))) return BITNET_ERR_ALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (dX) {
-    if (hipError_t e = bitnet::launch_bwd_dx(dY, w_packed, gamma, M, N, K, dX, st)) return from_hip(e);
+    if (hipError_t e = bitnet::launch_bwd_dx(dY, w_packed, gamma, M, N, K, dX, workspace, workspace_bytes, st)) return from_hip(e);
   }
   if (dW) {
-    if (hipError_t e = bitnet::launch_bwd_dw(dY, x_q, s_x, M, N, K, dW, dW_dtype == BITNET_F32, st))
+    if (hipError_t e = bitnet::launch_bwd_dw(dY, x_q, s_x, M, N, K, dW, dW_dtype == BITNET_F32, workspace,
+                                                  workspace_bytes, st))
       return from_hip(e);
   }
   return BITNET_OK;

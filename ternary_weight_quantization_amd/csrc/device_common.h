@@ -81,4 +81,25 @@ __device__ __forceinline__ uint32_t buf_load4(rsrc_t r, uint32_t off) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
 }
 
+// Device-coherent 16-byte access (cache policy sc1): stores write through
+// and loads read past the XCD-private L2 caches, so data exchanged between
+// workgroups on different XCDs needs no cache-wide writeback or invalidate.
+constexpr int kDeviceCoherent = 16;
+
+__device__ __forceinline__ void buf_store16_coherent(rsrc_t r, uint32_t off, uint4 v) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  __builtin_amdgcn_raw_buffer_store_b128(u32x4{v.x, v.y, v.z, v.w}, r, (int)off, 0, kDeviceCoherent);
+}
+
+__device__ __forceinline__ uint4 buf_load16_coherent(rsrc_t r, uint32_t off) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kDeviceCoherent));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Wait until every vector memory access of this wave has completed
+// (s_waitcnt vmcnt(0)); for device-coherent stores, until they are visible
+// to every workgroup on the device.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 }  // namespace bitnet

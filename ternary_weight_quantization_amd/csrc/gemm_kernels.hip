@@ -42,6 +42,12 @@
 // is the same for P and Q of a GEMM, so the hardware's internal order of the
 // reduction index within a step does not matter.
 
+#include <atomic>
+#include <cstdlib>
+#include <mutex>
+#include <random>
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -82,6 +88,9 @@ __device__ __forceinline__ constexpr int red_chunk(int ks, int h) {
 struct MfmaI8 {
   typedef i32x4_t Frag;
   typedef i32x16_t Acc;
+  typedef int Elem;
+  static __device__ __forceinline__ Elem from_bits(uint32_t b) { return (int)b; }
+  static __device__ __forceinline__ uint32_t to_bits(Elem e) { return (uint32_t)e; }
   static __device__ __forceinline__ Acc mma(Frag a, Frag b, Acc c) {
     return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
   }
@@ -90,6 +99,9 @@ struct MfmaI8 {
 struct MfmaBf16 {
   typedef bf16x8_t Frag;
   typedef f32x16_t Acc;
+  typedef float Elem;
+  static __device__ __forceinline__ Elem from_bits(uint32_t b) { return __uint_as_float(b); }
+  static __device__ __forceinline__ uint32_t to_bits(Elem e) { return __float_as_uint(e); }
   static __device__ __forceinline__ Acc mma(Frag a, Frag b, Acc c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
@@ -718,19 +730,88 @@ struct Bf16Epilogue {
 };
 
 // ---------------------------------------------------------------------------
-// Block -> tile. Workgroups are dispatched round-robin over the 8 XCDs
-// (block b on XCD b % 8); each XCD gets a contiguous range of tiles so that
-// the blocks sharing an L2 share operand panels. Within the range, i varies
-// fastest.
+// Work split. The T output tiles of a product, each of S reduction stages,
+// are T*S iterations in tile-major order (tile t = (ti, tj) with ti fastest).
+// A grid of G workgroups shares them out: virtual workgroup v takes
+// iterations [lo(v), lo(v+1)), lo(v) = floor(v * T * S / G). With G = T each
+// workgroup gets one whole tile. With G below T (or not dividing it) a tile
+// can be split between consecutive workgroups (stream-K): each piece
+// accumulates its stages, and the last piece to arrive adds the partial
+// tiles of the others in piece order, so the sum does not depend on the
+// arrival order, and runs the epilogue.
+//
+// Workgroups are dispatched round-robin over the 8 XCDs (block b on XCD
+// b % 8); virtual indices are numbered XCD by XCD, so an XCD owns a
+// contiguous range of iterations and its blocks share operand panels in its
+// L2 (and the pieces of a split tile are usually on one XCD).
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ void map_tile(int b, int tiles_i, int tiles_j, int& ti, int& tj) {
-  const int T = tiles_i * tiles_j;
-  const int q = T / 8, r = T % 8;
+struct SplitPlan {
+  int64_t total;       // T * S
+  int grid;            // G
+  int tiles_i;
+  int nstages;         // S
+  uint64_t gen;        // tag of this launch in the counters (0 < gen < 2^48)
+  uint64_t* counters;  // [T][2] tagged counters (pieces arrived, partials
+                       // published); NULL when no tile is split
+  uint4* partials;     // [2G][64][kThreads] 16-byte chunks of partial tiles
+};
+
+__device__ __forceinline__ int cta_order(int b, int G) {
+  const int q = G / 8, r = G % 8;
   const int x = b % 8, k = b / 8;
-  const int v = (x < r) ? x * (q + 1) + k : r * (q + 1) + (x - r) * q + k;
-  ti = v % tiles_i;
-  tj = v / tiles_i;
+  return (x < r) ? x * (q + 1) + k : r * (q + 1) + (x - r) * q + k;
+}
+
+__device__ __forceinline__ int64_t split_lo(const SplitPlan& p, int v) {
+  return (int64_t)v * p.total / p.grid;
+}
+
+// The virtual workgroup whose range holds iteration it.
+__device__ __forceinline__ int split_owner(const SplitPlan& p, int64_t it) {
+  return (int)(((it + 1) * p.grid - 1) / p.total);
+}
+
+// Partial-tile slot of workgroup v's piece of tile t: 2v for the tile its
+// range starts in, 2v + 1 for the tile it ends in.
+__device__ __forceinline__ int64_t piece_slot(const SplitPlan& p, int v, int t) {
+  return 2 * (int64_t)v + ((int64_t)t == split_lo(p, v) / p.nstages ? 0 : 1);
+}
+
+// Tagged counters: a 64-bit word gen << 16 | count. A word written by
+// another launch (another tag) counts as zero, so the counters never need
+// clearing between launches. The counters only order the exchange of
+// partial tiles, whose stores and loads are device-coherent and complete
+// (wait_vmem) before the counter moves, so relaxed device-scope atomics
+// suffice and no cache-wide fence is needed.
+constexpr uint64_t kCountMask = 0xFFFF;
+
+__device__ __forceinline__ uint32_t tagged_arrive(uint64_t* c, uint64_t gen) {
+  uint64_t old = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (;;) {
+    const bool same = (old >> 16) == gen;
+    const uint64_t nw = same ? old + 1 : ((gen << 16) | 1u);
+    if (__hip_atomic_compare_exchange_strong(c, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT))
+      return same ? (uint32_t)(old & kCountMask) : 0u;
+  }
+}
+
+__device__ __forceinline__ uint32_t tagged_count(const uint64_t* c, uint64_t gen) {
+  const uint64_t v = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return (v >> 16) == gen ? (uint32_t)(v & kCountMask) : 0u;
+}
+
+// Wait until `want` partials of a tile are published. Only pieces that have
+// already arrived (so are running and only have their stores left) are
+// waited for; the bound is a safety net, never reached in practice.
+constexpr uint32_t kSpinLimit = 1u << 24;
+
+__device__ __forceinline__ void wait_published(const uint64_t* c, uint64_t gen, uint32_t want) {
+  for (uint32_t i = 0; i < kSpinLimit; ++i) {
+    if (tagged_count(c, gen) >= want) return;
+    __builtin_amdgcn_s_sleep(2);
+  }
 }
 
 template <class Acc>
@@ -820,53 +901,270 @@ __device__ __forceinline__ void gemm_stage(const PL& pl, const QL& ql, typename 
   __syncthreads();
 }
 
-template <class MT, int MAP, class PL, class QL, class EP>
-__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(PL pl, QL ql, EP ep, int tiles_i,
-                                                          int tiles_j, int nstages) {
-  typedef SmemLayout<PL, QL> L;
-  __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
-  __shared__ __attribute__((aligned(16))) float sscale[2][kRed16];
-
-  int ti, tj;
-  map_tile(blockIdx.x, tiles_i, tiles_j, ti, tj);
-  const int i0 = ti * kBI, j0 = tj * kBJ;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wi = wave % kWavesI, wj = wave / kWavesI;
-
-  typename MT::Acc acc[kFI][kFJ];
-#pragma unroll
-  for (int fi = 0; fi < kFI; ++fi)
-#pragma unroll
-    for (int fj = 0; fj < kFJ; ++fj) zero_acc(acc[fi][fj]);
-
+// The stages [s0, s1) of tile (i0, j0), accumulated into acc. LDS and the
+// per-stage scales are free on entry and on return.
+template <class MT, int MAP, class PL, class QL>
+__device__ __forceinline__ void run_stages(const PL& pl, const QL& ql, char* smem, float (*sscale)[kRed16],
+                                           typename MT::Acc (&acc)[kFI][kFJ], int i0, int j0, int s0,
+                                           int s1, int prow0, int qrow0, int lane) {
   typename PL::Regs pr;
   typename QL::Regs qr;
-  pl.load(pr, i0, 0, sscale[0]);
-  ql.load(qr, j0, 0, sscale[0]);
+  pl.load(pr, i0, s0, sscale[0]);
+  ql.load(qr, j0, s0, sscale[0]);
   __syncthreads();  // per-stage scales published by load()
   pl.store(pr, smem, sscale[0]);
   ql.store(qr, smem + PL::kTileB, sscale[0]);
-  pl.load(pr, i0, 1, sscale[1]);
-  ql.load(qr, j0, 1, sscale[1]);
+  pl.load(pr, i0, s0 + 1, sscale[1]);
+  ql.load(qr, j0, s0 + 1, sscale[1]);
   __syncthreads();
-
-  const int prow0 = wi * kWTI, qrow0 = wj * kWTJ;
-  int s = 0;
-  for (; s + 1 < nstages; s += 2) {
+  int s = s0;
+  for (; s + 1 < s1; s += 2) {
     gemm_stage<0, MT, MAP>(pl, ql, pr, qr, smem, sscale, acc, i0, j0, s, prow0, qrow0, lane);
     gemm_stage<1, MT, MAP>(pl, ql, pr, qr, smem, sscale, acc, i0, j0, s + 1, prow0, qrow0, lane);
   }
-  if (s < nstages) gemm_stage<0, MT, MAP>(pl, ql, pr, qr, smem, sscale, acc, i0, j0, s, prow0, qrow0, lane);
-  ep.store(acc, i0 + wi * kWTI, j0 + wj * kWTJ, lane);
+  if (s < s1) gemm_stage<0, MT, MAP>(pl, ql, pr, qr, smem, sscale, acc, i0, j0, s, prow0, qrow0, lane);
+}
+
+// Element e (0..3) of 16-byte chunk c (0..63) of a thread's accumulators:
+// chunk c = 4 * (kFJ * fi + fj) + q holds acc[fi][fj][4q .. 4q + 3].
+template <class MT>
+__device__ __forceinline__ uint4 acc_chunk(const typename MT::Acc (&acc)[kFI][kFJ], int c) {
+  const int fi = c / (4 * kFJ), fj = (c / 4) % kFJ, q = c % 4;
+  return make_uint4(MT::to_bits(acc[fi][fj][4 * q]), MT::to_bits(acc[fi][fj][4 * q + 1]),
+                    MT::to_bits(acc[fi][fj][4 * q + 2]), MT::to_bits(acc[fi][fj][4 * q + 3]));
+}
+
+template <class MT>
+__device__ __forceinline__ void acc_chunk_add(typename MT::Acc (&acc)[kFI][kFJ], int c, uint4 v) {
+  const int fi = c / (4 * kFJ), fj = (c / 4) % kFJ, q = c % 4;
+  acc[fi][fj][4 * q] += MT::from_bits(v.x);
+  acc[fi][fj][4 * q + 1] += MT::from_bits(v.y);
+  acc[fi][fj][4 * q + 2] += MT::from_bits(v.z);
+  acc[fi][fj][4 * q + 3] += MT::from_bits(v.w);
+}
+
+__device__ __forceinline__ uint4 chunk_add_f32(uint4 a, uint4 b) {
+  return make_uint4(__float_as_uint(__uint_as_float(a.x) + __uint_as_float(b.x)),
+                    __float_as_uint(__uint_as_float(a.y) + __uint_as_float(b.y)),
+                    __float_as_uint(__uint_as_float(a.z) + __uint_as_float(b.z)),
+                    __float_as_uint(__uint_as_float(a.w) + __uint_as_float(b.w)));
+}
+
+template <class MT>
+__device__ __forceinline__ uint4 chunk_add(uint4 a, uint4 b) {
+  if constexpr (std::is_same<typename MT::Elem, float>::value) {
+    return chunk_add_f32(a, b);
+  } else {
+    return make_uint4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+  }
+}
+
+// End of a piece of a split tile. Arrive; a piece that is not the last
+// publishes its partial tile and returns false; the last one waits for the
+// others' partials, adds them in piece order into acc and returns true (the
+// caller then runs the epilogue). With pieces p_0..p_{n-1} and this one at
+// position me, the sum is ((p_0 + ... + p_{me-1}) + own) + p_{me+1} + ...
+// evaluated left to right (own + L == L + own exactly).
+template <class MT>
+__device__ __forceinline__ bool finish_piece(const SplitPlan& p, typename MT::Acc (&acc)[kFI][kFJ],
+                                             int v, int t, int* s_flag) {
+  const int tid = threadIdx.x;
+  const int64_t S = p.nstages;
+  const int va = split_owner(p, (int64_t)t * S);
+  const int vb = split_owner(p, (int64_t)t * S + S - 1);
+  const int n = vb - va + 1, me = v - va;
+  uint64_t* cnt = p.counters + 2 * (int64_t)t;
+  if (tid == 0) *s_flag = (int)tagged_arrive(cnt, p.gen);
+  __syncthreads();
+  const bool last = (*s_flag == n - 1);
+  __syncthreads();
+  const rsrc_t pr = make_rsrc(p.partials, (uint32_t)(2 * (int64_t)p.grid * 64 * kThreads * 16));
+  if (!last) {
+    const uint32_t base = (uint32_t)(piece_slot(p, v, t) * 64 * kThreads + tid) * 16;
+#pragma unroll
+    for (int c = 0; c < 64; ++c) buf_store16_coherent(pr, base + c * kThreads * 16, acc_chunk<MT>(acc, c));
+    wait_vmem();
+    __syncthreads();
+    if (tid == 0) tagged_arrive(cnt + 1, p.gen);
+    return false;
+  }
+  if (tid == 0) wait_published(cnt + 1, p.gen, (uint32_t)(n - 1));
+  __syncthreads();
+  constexpr int kBatch = 8;
+#pragma unroll
+  for (int c0 = 0; c0 < 64; c0 += kBatch) {
+    if (me > 0) {
+      uint4 L[kBatch];
+      const uint32_t b0 = (uint32_t)(piece_slot(p, va, t) * 64 * kThreads + tid) * 16;
+#pragma unroll
+      for (int c = 0; c < kBatch; ++c) L[c] = buf_load16_coherent(pr, b0 + (c0 + c) * kThreads * 16);
+      for (int j = 1; j < me; ++j) {
+        const uint32_t bj = (uint32_t)(piece_slot(p, va + j, t) * 64 * kThreads + tid) * 16;
+#pragma unroll
+        for (int c = 0; c < kBatch; ++c)
+          L[c] = chunk_add<MT>(L[c], buf_load16_coherent(pr, bj + (c0 + c) * kThreads * 16));
+      }
+#pragma unroll
+      for (int c = 0; c < kBatch; ++c) acc_chunk_add<MT>(acc, c0 + c, L[c]);
+    }
+    for (int j = me + 1; j < n; ++j) {
+      const uint32_t bj = (uint32_t)(piece_slot(p, va + j, t) * 64 * kThreads + tid) * 16;
+      uint4 R[kBatch];
+#pragma unroll
+      for (int c = 0; c < kBatch; ++c) R[c] = buf_load16_coherent(pr, bj + (c0 + c) * kThreads * 16);
+#pragma unroll
+      for (int c = 0; c < kBatch; ++c) acc_chunk_add<MT>(acc, c0 + c, R[c]);
+    }
+  }
+  return true;
 }
 
 template <class MT, int MAP, class PL, class QL, class EP>
-static hipError_t run_gemm(const PL& pl, const QL& ql, const EP& ep, int64_t I, int64_t J,
-                           int64_t nstages, hipStream_t stream) {
-  const int tiles_i = (int)((I + kBI - 1) / kBI);
-  const int tiles_j = (int)((J + kBJ - 1) / kBJ);
-  gemm_kernel<MT, MAP, PL, QL, EP><<<tiles_i * tiles_j, kThreads, 0, stream>>>(pl, ql, ep, tiles_i,
-                                                                              tiles_j, (int)nstages);
+__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(PL pl, QL ql, EP ep, SplitPlan plan) {
+  typedef SmemLayout<PL, QL> L;
+  __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
+  __shared__ __attribute__((aligned(16))) float sscale[2][kRed16];
+  __shared__ int s_flag;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wi = wave % kWavesI, wj = wave / kWavesI;
+  const int prow0 = wi * kWTI, qrow0 = wj * kWTJ;
+  const int v = cta_order(blockIdx.x, plan.grid);
+  if (plan.counters == nullptr) {
+    // one whole tile per workgroup
+    const int i0 = (v % plan.tiles_i) * kBI, j0 = (v / plan.tiles_i) * kBJ;
+    typename MT::Acc acc[kFI][kFJ];
+#pragma unroll
+    for (int fi = 0; fi < kFI; ++fi)
+#pragma unroll
+      for (int fj = 0; fj < kFJ; ++fj) zero_acc(acc[fi][fj]);
+    run_stages<MT, MAP>(pl, ql, smem, sscale, acc, i0, j0, 0, plan.nstages, prow0, qrow0, lane);
+    ep.store(acc, i0 + prow0, j0 + qrow0, lane);
+    return;
+  }
+
+  const int64_t hi = split_lo(plan, v + 1);
+  for (int64_t it = split_lo(plan, v); it < hi;) {
+    const int t = (int)(it / plan.nstages);
+    const int s0 = (int)(it - (int64_t)t * plan.nstages);
+    const int s1 = (int)((int64_t)plan.nstages < s0 + (hi - it) ? (int64_t)plan.nstages : s0 + (hi - it));
+    const int i0 = (t % plan.tiles_i) * kBI, j0 = (t / plan.tiles_i) * kBJ;
+
+    typename MT::Acc acc[kFI][kFJ];
+#pragma unroll
+    for (int fi = 0; fi < kFI; ++fi)
+#pragma unroll
+      for (int fj = 0; fj < kFJ; ++fj) zero_acc(acc[fi][fj]);
+
+    run_stages<MT, MAP>(pl, ql, smem, sscale, acc, i0, j0, s0, s1, prow0, qrow0, lane);
+    if ((s0 == 0 && s1 == plan.nstages) || finish_piece<MT>(plan, acc, v, t, &s_flag))
+      ep.store(acc, i0 + prow0, j0 + qrow0, lane);
+    it += s1 - s0;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side: choice of the split, workspace, launch.
+// ---------------------------------------------------------------------------
+
+constexpr int kMaxGrid = 256;  // workgroups of a split launch (one per CU)
+constexpr size_t kPartialBytes = (size_t)64 * kThreads * 16;  // one partial tile
+
+struct GemmShape {
+  int64_t tiles_i, tiles_j, nstages;
+  int overhead;  // cost of a split piece's publish / fix-up, in stages
+  int64_t tiles() const { return tiles_i * tiles_j; }
+};
+
+static GemmShape shape_of(GemmKind kind, int64_t M, int64_t N, int64_t K) {
+  const int64_t Kp = k_pad(K);
+  switch (kind) {
+    case GemmKind::kFwd: return {(N + kBI - 1) / kBI, (M + kBJ - 1) / kBJ, (Kp + kStageBytes - 1) / kStageBytes, 7};
+    case GemmKind::kBwdDx: return {(K + kBI - 1) / kBI, (M + kBJ - 1) / kBJ, (N + kRed16 - 1) / kRed16, 3};
+    case GemmKind::kBwdDw: break;
+  }
+  return {(K + kBI - 1) / kBI, (N + kBJ - 1) / kBJ, (M + kRed16 - 1) / kRed16, 3};
+}
+
+// Workgroups of a split launch, or 0 for one whole tile per workgroup.
+// A split pays when T tiles leave the last round of whole tiles on `cus`
+// CUs partly idle; it spreads the T*S stages evenly over at most `cus`
+// workgroups and about 4 pieces per tile. BITNET_SPLIT_CTAS=<G> forces G
+// workgroups (a test knob).
+static int split_grid(const GemmShape& g, int cus) {
+  const int64_t T = g.tiles(), S = g.nstages, W = T * S;
+  if (const char* e = getenv("BITNET_SPLIT_CTAS")) {
+    const long f = strtol(e, nullptr, 10);
+    if (f > 0) {
+      const int64_t G = f < kMaxGrid ? f : kMaxGrid;
+      return (int)(G < W ? G : W);
+    }
+  }
+  if (W < 2 || cus < 1) return 0;
+  const int64_t G = (int64_t)cus < 4 * T ? (int64_t)cus : 4 * T;
+  const int64_t whole = (T + cus - 1) / cus * S;
+  const int64_t split = (W + G - 1) / G + g.overhead;
+  return split < whole ? (int)G : 0;
+}
+
+static size_t split_workspace(const GemmShape& g, int grid) {
+  if (grid == 0) return 0;
+  const size_t counters = ((size_t)g.tiles() * 16 + 255) / 256 * 256;
+  return counters + 2 * (size_t)grid * kPartialBytes;
+}
+
+size_t gemm_workspace_bytes(GemmKind kind, int64_t M, int64_t N, int64_t K) {
+  const GemmShape g = shape_of(kind, M, N, K);
+  return split_workspace(g, split_grid(g, kMaxGrid));
+}
+
+static int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kMaxGrid;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = kMaxGrid;
+    cached[dev] = n < kMaxGrid ? n : kMaxGrid;
+  }
+  return cached[dev];
+}
+
+// Launch tags: a 48-bit counter started at a random value, so tags of
+// different launches (and processes) differ.
+static uint64_t next_gen() {
+  static std::atomic<uint64_t> gen{0};
+  static std::once_flag once;
+  std::call_once(once, [] {
+    std::random_device rd;
+    gen.store(((uint64_t)rd() << 20) ^ (uint64_t)rd());
+  });
+  uint64_t g;
+  do {
+    g = gen.fetch_add(1) & ((uint64_t(1) << 48) - 1);
+  } while (g == 0);
+  return g;
+}
+
+template <class MT, int MAP, class PL, class QL, class EP>
+static hipError_t run_gemm(const PL& pl, const QL& ql, const EP& ep, const GemmShape& g, void* ws,
+                           size_t ws_bytes, hipStream_t stream) {
+  SplitPlan plan{};
+  plan.total = g.tiles() * g.nstages;
+  plan.tiles_i = (int)g.tiles_i;
+  plan.nstages = (int)g.nstages;
+  int grid = split_grid(g, device_cus());
+  if (grid > 0 && (ws == nullptr || ws_bytes < split_workspace(g, grid))) grid = 0;
+  if (grid > 0) {
+    const size_t counters = split_workspace(g, grid) - 2 * (size_t)grid * kPartialBytes;
+    plan.grid = grid;
+    plan.gen = next_gen();
+    plan.counters = static_cast<uint64_t*>(ws);
+    plan.partials = reinterpret_cast<uint4*>(static_cast<char*>(ws) + counters);
+  } else {
+    plan.grid = (int)g.tiles();
+  }
+  gemm_kernel<MT, MAP, PL, QL, EP><<<plan.grid, kThreads, 0, stream>>>(pl, ql, ep, plan);
   return hipGetLastError();
 }
 
@@ -876,42 +1174,44 @@ static hipError_t run_gemm(const PL& pl, const QL& ql, const EP& ep, int64_t I, 
 
 hipError_t launch_fwd(const int8_t* x_q, const float* s_x, const uint8_t* w_packed,
                       const float* gamma, int64_t M, int64_t N, int64_t K, uint16_t* y,
-                      int32_t* acc_out, hipStream_t stream) {
+                      int32_t* acc_out, void* ws, size_t ws_bytes, hipStream_t stream) {
   const int64_t Kp = k_pad(K);
   PackedCodesLoader pl{w_packed, Kp / 4, N};
   CopyLoader<1, true> ql{reinterpret_cast<const char*>(x_q), Kp, M, Kp};
   FwdEpilogue ep{y, acc_out, s_x, gamma, N, M, N % 4 == 0};
-  return run_gemm<MfmaI8, 1>(pl, ql, ep, N, M, (Kp + kStageBytes - 1) / kStageBytes, stream);
+  return run_gemm<MfmaI8, 1>(pl, ql, ep, shape_of(GemmKind::kFwd, M, N, K), ws, ws_bytes, stream);
 }
 
 hipError_t launch_bwd_dx(const uint16_t* dY, const uint8_t* w_packed, const float* gamma,
-                         int64_t M, int64_t N, int64_t K, uint16_t* dX, hipStream_t stream) {
+                         int64_t M, int64_t N, int64_t K, uint16_t* dX, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
   const int64_t Kp = k_pad(K);
   PackedCodesTLoader pl{w_packed, Kp / 4, N};
   Bf16Epilogue<false> ep{dX, gamma, K, M, K % 4 == 0};
-  const int64_t nst = (N + kRed16 - 1) / kRed16;
+  const GemmShape g = shape_of(GemmKind::kBwdDx, M, N, K);
   if (N % 8 == 0) {
     CopyLoader<2, true> ql{reinterpret_cast<const char*>(dY), 2 * N, M, 2 * N};
-    return run_gemm<MfmaBf16, 1>(pl, ql, ep, K, M, nst, stream);
+    return run_gemm<MfmaBf16, 1>(pl, ql, ep, g, ws, ws_bytes, stream);
   }
   CopyLoader<2, false> ql{reinterpret_cast<const char*>(dY), 2 * N, M, 2 * N};
-  return run_gemm<MfmaBf16, 1>(pl, ql, ep, K, M, nst, stream);
+  return run_gemm<MfmaBf16, 1>(pl, ql, ep, g, ws, ws_bytes, stream);
 }
 
 hipError_t launch_bwd_dw(const uint16_t* dY, const int8_t* x_q, const float* s_x, int64_t M,
-                         int64_t N, int64_t K, void* dW, bool dw_is_f32, hipStream_t stream) {
+                         int64_t N, int64_t K, void* dW, bool dw_is_f32, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
   const int64_t Kp = k_pad(K);
   Int8TransposeScaleLoader pl{x_q, s_x, Kp, M};
-  const int64_t nst = (M + kRed16 - 1) / kRed16;
+  const GemmShape g = shape_of(GemmKind::kBwdDw, M, N, K);
   const bool vec = (N % 4 == 0);
   if (dw_is_f32) {
     Bf16Epilogue<true> ep{dW, nullptr, K, N, K % 4 == 0};
-    if (vec) return run_gemm<MfmaBf16, 0>(pl, RowTransposeBf16Loader<true>{dY, N, M, N}, ep, K, N, nst, stream);
-    return run_gemm<MfmaBf16, 0>(pl, RowTransposeBf16Loader<false>{dY, N, M, N}, ep, K, N, nst, stream);
+    if (vec) return run_gemm<MfmaBf16, 0>(pl, RowTransposeBf16Loader<true>{dY, N, M, N}, ep, g, ws, ws_bytes, stream);
+    return run_gemm<MfmaBf16, 0>(pl, RowTransposeBf16Loader<false>{dY, N, M, N}, ep, g, ws, ws_bytes, stream);
   }
   Bf16Epilogue<false> ep{dW, nullptr, K, N, K % 4 == 0};
-  if (vec) return run_gemm<MfmaBf16, 0>(pl, RowTransposeBf16Loader<true>{dY, N, M, N}, ep, K, N, nst, stream);
-  return run_gemm<MfmaBf16, 0>(pl, RowTransposeBf16Loader<false>{dY, N, M, N}, ep, K, N, nst, stream);
+  if (vec) return run_gemm<MfmaBf16, 0>(pl, RowTransposeBf16Loader<true>{dY, N, M, N}, ep, g, ws, ws_bytes, stream);
+  return run_gemm<MfmaBf16, 0>(pl, RowTransposeBf16Loader<false>{dY, N, M, N}, ep, g, ws, ws_bytes, stream);
 }
 
 }  // namespace bitnet

@@ -24,16 +24,24 @@ hipError_t launch_ternarize_pack(const void* W, bool w_is_f32, int64_t N, int64_
 hipError_t launch_act_quant(const uint16_t* x, int64_t M, int64_t K,
                             int8_t* x_q, float* s_x, hipStream_t stream);
 
+// The three GEMMs. Each may split output tiles over workgroups (stream-K)
+// when its tile count leaves the CUs partly idle; that needs the workspace
+// gemm_workspace_bytes() gives (fewer bytes: whole tiles, no split).
+enum class GemmKind { kFwd, kBwdDx, kBwdDw };
+size_t gemm_workspace_bytes(GemmKind kind, int64_t M, int64_t N, int64_t K);
+
 // INT8 forward GEMM with fused rescale (and optional int32 accumulators).
 hipError_t launch_fwd(const int8_t* x_q, const float* s_x, const uint8_t* w_packed,
                       const float* gamma, int64_t M, int64_t N, int64_t K,
-                      uint16_t* y, int32_t* acc_out, hipStream_t stream);
+                      uint16_t* y, int32_t* acc_out, void* ws, size_t ws_bytes,
+                      hipStream_t stream);
 
 // STE backward GEMMs.
 hipError_t launch_bwd_dx(const uint16_t* dY, const uint8_t* w_packed, const float* gamma,
-                         int64_t M, int64_t N, int64_t K, uint16_t* dX, hipStream_t stream);
+                         int64_t M, int64_t N, int64_t K, uint16_t* dX, void* ws,
+                         size_t ws_bytes, hipStream_t stream);
 hipError_t launch_bwd_dw(const uint16_t* dY, const int8_t* x_q, const float* s_x,
                          int64_t M, int64_t N, int64_t K, void* dW, bool dw_is_f32,
-                         hipStream_t stream);
+                         void* ws, size_t ws_bytes, hipStream_t stream);
 
 }  // namespace bitnet

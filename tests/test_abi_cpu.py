@@ -58,8 +58,16 @@ def test_size_queries(L):
     assert [L.bitnet_k_pad(k) for k in (1, 7, 63, 64, 65, 2560, 6912)] == [64, 64, 64, 64, 128, 2560, 6912]
     assert L.bitnet_k_pad(0) == 0
     assert L.bitnet_ternarize_workspace_bytes(6912, 2560) >= 8 * 256
+    # whole output tiles need no workspace; split tiles need tagged counters
+    # (16 bytes per tile, rounded to 256) and two 256 KiB partial tiles per
+    # workgroup of the 256-workgroup grid
     assert L.bitlinear_fwd_workspace_bytes(4096, 6912, 2560) == 0
-    assert L.bitlinear_bwd_workspace_bytes(4096, 6912, 2560) == 0
+    assert L.bitlinear_fwd_workspace_bytes(64, 128, 256) == 0
+    assert L.bitlinear_bwd_workspace_bytes(64, 128, 256) == 0
+    tile = 64 * 256 * 16
+    assert L.bitlinear_bwd_workspace_bytes(4096, 6912, 2560) == 4352 + 2 * 256 * tile
+    assert L.bitlinear_fwd_workspace_bytes(4096, 2560, 6912) == 2560 + 2 * 256 * tile
+    assert L.bitlinear_fwd_workspace_bytes(0, 4, 4) == 0
     for code in range(7):
         assert L.bitnet_status_string(code).decode().startswith("BITNET_")
 
@@ -102,6 +110,15 @@ def test_fwd_validation(L):
     assert L.bitlinear_fwd(A, A, A, A, 4, 4, 4, MISALIGNED, None, None, 0, None) == EALIGN
     assert L.bitlinear_fwd(A, A, A, A, 4, 4, 4, A, MISALIGNED, None, 0, None) == EALIGN
     assert L.bitlinear_fwd(A, A, A, A + 2, 4, 4, 4, A, None, None, 0, None) == EALIGN
+
+
+def test_gemm_workspace_validation(L):
+    need = L.bitlinear_bwd_workspace_bytes(4096, 6912, 2560)
+    assert L.bitlinear_bwd(A, A, A, A, A, 4096, 6912, 2560, A, A, 0, A, need - 1, None) == EWS
+    assert L.bitlinear_bwd(A, A, A, A, A, 4096, 6912, 2560, A, A, 0, None, need, None) == EWS
+    assert L.bitlinear_bwd(A, A, A, A, A, 4096, 6912, 2560, A, A, 0, MISALIGNED + 4, need, None) == EALIGN
+    need = L.bitlinear_fwd_workspace_bytes(4096, 2560, 6912)
+    assert L.bitlinear_fwd(A, A, A, A, 4096, 2560, 6912, A, None, A, need - 1, None) == EWS
 
 
 def test_bwd_validation(L):

@@ -191,6 +191,28 @@ def test_tiny_net_through_the_abi():
         assert np.array_equal(np.sign(grads[i]), np.sign(Q[i].grad.numpy())), i
 
 
+@pytest.mark.parametrize("M,K,N,wd,G", [
+    (300, 1000, 777, "bf16", 3),      # 2 pieces per tile
+    (300, 1000, 777, "bf16", 13),     # 2-3 pieces per tile
+    (300, 1000, 777, "bf16", 64),     # fwd: one stage per workgroup, 8 pieces per tile
+    (520, 1001, 263, "f32", 5),       # f32 dW, ragged tails
+    (1024, 2560, 1536, "bf16", 256),  # a full grid
+])
+def test_split_tiles_forced(M, K, N, wd, G, monkeypatch):
+    """Output tiles split over G workgroups (stream-K) on all three GEMMs:
+    integer state and accumulators stay bit-exact, the bf16 outputs stay
+    within tolerance, and a repeat gives identical bits (the partial tiles
+    are added in a fixed order whatever the arrival order)."""
+    monkeypatch.setenv("BITNET_SPLIT_CTAS", str(G))
+    inp = WL.custom_inputs(M, K, N, seed=M + K + N + G, w_dtype=wd)
+    note(f"split tiles G={G} M={M} K={K} N={N} W={wd}")
+    g = run_layer(inp)
+    check_layer(inp, g, full=True)
+    g2 = run_layer(inp)
+    assert np.array_equal(g["acc"], g2["acc"]) and np.array_equal(g["y_bits"], g2["y_bits"])
+    assert np.array_equal(g["dX"], g2["dX"]) and np.array_equal(g["dW"], g2["dW"])
+
+
 def test_determinism_repeated_calls():
     inp = WL.custom_inputs(512, 1536, 640, seed=9)
     note("determinism")
