@@ -990,7 +990,7 @@ __device__ __forceinline__ bool finish_piece(const SplitPlan& p, typename MT::Ac
   }
   if (tid == 0) wait_published(cnt + 1, p.gen, (uint32_t)(n - 1));
   __syncthreads();
-  constexpr int kBatch = 8;
+  constexpr int kBatch = 16;
 #pragma unroll
   for (int c0 = 0; c0 < 64; c0 += kBatch) {
     if (me > 0) {
@@ -1089,12 +1089,14 @@ static GemmShape shape_of(GemmKind kind, int64_t M, int64_t N, int64_t K) {
 // Workgroups of a split launch, or 0 for one whole tile per workgroup.
 // A split pays when T tiles leave the last round of whole tiles on `cus`
 // CUs partly idle; it spreads the T*S stages evenly over at most `cus`
-// workgroups and about 4 pieces per tile. BITNET_SPLIT_CTAS=<G> forces G
-// workgroups (a test knob).
+// workgroups and about 4 pieces per tile. BITNET_SPLIT_CTAS=<G> forces a
+// split over G workgroups, a negative value forces whole tiles (test and
+// tuning knobs).
 static int split_grid(const GemmShape& g, int cus) {
   const int64_t T = g.tiles(), S = g.nstages, W = T * S;
   if (const char* e = getenv("BITNET_SPLIT_CTAS")) {
     const long f = strtol(e, nullptr, 10);
+    if (f < 0) return 0;
     if (f > 0) {
       const int64_t G = f < kMaxGrid ? f : kMaxGrid;
       return (int)(G < W ? G : W);

@@ -198,27 +198,34 @@ hipError_t launch_ternarize_pack(const void* W, bool w_is_f32, int64_t N, int64_
 // Activation quantization
 // ---------------------------------------------------------------------------
 
-// RNE(127 x / s) for |x| <= s, exactly. Fast path: p = x * fl(127/s) is
-// within 127 * 2^-23 (< 1.6e-5) of the exact quotient Q, so when p is more
-// than 2^-15 away from the nearest half-integer, rint(p) is the integer
-// nearest to Q and no tie is possible. Otherwise Q is recomputed as an fp64
+// RNE(127 x / s) for |x| <= s, exactly, returned as the fp32 value
+// 1.5 * 2^23 + q, whose low byte is q as a two's complement int8.
+// Fast path: p = x * fl(127/s) is within 127 * 2^-23 (< 1.6e-5) of the
+// exact quotient Q, so when p is more than 2^-15 away from the nearest
+// half-integer, the integer nearest to p is the one nearest to Q and no tie
+// is possible; adding 1.5 * 2^23 rounds p to that integer (RNE, |p| < 2^22)
+// and subtracting it again is exact. Otherwise Q is recomputed as an fp64
 // quotient of exact operands, whose rounding error (< 2^-46) is far below
 // the smallest nonzero distance of Q from a half-integer (> 2^-33 for fp32
-// operands), so rint of it is exact, ties included.
-__device__ __forceinline__ int quant1(float xv, float r127, float s) {
+// operands), so rint of it is exact, ties included. No clamp is needed:
+// |x| <= s gives |p| <= 127 (1 + 2^-24) and |Q| <= 127.
+constexpr float kRoundMagic = 12582912.0f;  // 1.5 * 2^23
+
+__device__ __forceinline__ float quant1(float xv, float r127, float s) {
   const float p = xv * r127;
-  float c = __builtin_rintf(p);
-  if (fabsf(p - c) > 0.49996948f) {  // 0.5 - 2^-15
-    const double t = 127.0 * (double)xv;
-    c = (float)__builtin_rint(t / (double)s);
+  const float t = p + kRoundMagic;
+  if (fabsf(p - (t - kRoundMagic)) > 0.49996948f) {  // 0.5 - 2^-15
+    const double q = __builtin_rint(127.0 * (double)xv / (double)s);
+    return (float)q + kRoundMagic;
   }
-  c = fminf(fmaxf(c, -127.0f), 127.0f);
-  return (int)c;
+  return t;
 }
 
-__device__ __forceinline__ uint32_t pack_i8x4(int a, int b, int c, int d) {
-  return (uint32_t(a) & 0xFFu) | ((uint32_t(b) & 0xFFu) << 8) | ((uint32_t(c) & 0xFFu) << 16) |
-         (uint32_t(d) << 24);
+// Low bytes of four quant1 results -> four int8 in one word (a's lowest).
+__device__ __forceinline__ uint32_t pack_i8x4(float a, float b, float c, float d) {
+  const uint32_t lo = perm(__float_as_uint(b), __float_as_uint(a), 0x0C0C0400u);
+  const uint32_t hi = perm(__float_as_uint(d), __float_as_uint(c), 0x0C0C0400u);
+  return perm(hi, lo, 0x05040100u);
 }
 
 __device__ __forceinline__ uint2 quant8(uint4 v, float r127, float s) {
