@@ -110,9 +110,14 @@ struct MfmaBf16 {
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
-// Fragment readers: per k-step, the kFI (or kFJ) fragments of a wave.
-// prefetch<KS>() issues the LDS reads for k-step KS, get<KS>(f) returns
-// fragment f of k-step KS. init() points the reader at a stage's tile.
+// Fragment readers: the kFI (or kFJ) fragments of a wave for each k-step.
+// A k-step is 16 MFMA slots (see gemm_kstep); start<KS>() runs before its
+// first slot, slot<KS, U>() runs after the MFMA of slot U and issues this
+// reader's share of the work for later slots: the LDS reads of the next
+// k-step's fragments and, for code operands, the expansion of fragment
+// f + 1 during the slots of fragment f (and of the next k-step's fragment 0
+// during the last four). frag<KS>(f) is fragment f of k-step KS, ready by
+// the first slot that uses it. init() points the reader at a stage's tile.
 // ---------------------------------------------------------------------------
 
 // 16-byte fragments read directly from a plain tile (pitch kPitch).
@@ -136,12 +141,22 @@ struct PlainFrags {
     return SWZ ? f * 32 * kPitch + 32 * (KS ^ f) : f * 32 * kPitch + 16 * (MAP == 0 ? 2 * KS : KS);
   }
   template <int KS>
-  __device__ __forceinline__ void prefetch() {
-#pragma unroll
-    for (int f = 0; f < 4; ++f) buf[KS & 1][f] = *reinterpret_cast<const typename MT::Frag*>(base + off<KS>(f));
+  __device__ __forceinline__ void read(int f) {
+    buf[KS & 1][f] = *reinterpret_cast<const typename MT::Frag*>(base + off<KS>(f));
   }
   template <int KS>
-  __device__ __forceinline__ typename MT::Frag get(int f) const { return buf[KS & 1][f]; }
+  __device__ __forceinline__ void start() {
+    if constexpr (KS == 0) {
+#pragma unroll
+      for (int f = 0; f < 4; ++f) read<0>(f);
+    }
+  }
+  template <int KS, int U>
+  __device__ __forceinline__ void slot() {
+    if constexpr (KS + 1 < kKSteps && U % 4 == 0) read<KS + 1>(U / 4);
+  }
+  template <int KS>
+  __device__ __forceinline__ typename MT::Frag frag(int f) const { return buf[KS & 1][f]; }
 };
 
 // Four 2-bit codes in the byte lanes of c (values 0, 1, 3) -> four int8.
@@ -150,80 +165,96 @@ __device__ __forceinline__ uint32_t codes4_to_i8(uint32_t c) {
   return perm(0u, 0xFF000100u, c);
 }
 
-// Four 2-bit codes in the byte lanes of c -> two words of bf16 (+1 = 0x3F80,
-// -1 = 0xBF80, 0 = 0).
-__device__ __forceinline__ uint2 codes4_to_bf16(uint32_t c) {
+// Four 2-bit codes in the byte lanes of c -> bf16 (+1 = 0x3F80, -1 = 0xBF80,
+// 0 = 0) of the codes in bytes 0, 1 (HALF 0) or 2, 3 (HALF 1), one word.
+template <int HALF>
+__device__ __forceinline__ uint32_t codes2_to_bf16(uint32_t c) {
   constexpr uint32_t kLo = 0x80008000u;  // low bytes of bf16(code) for codes 0..3
   constexpr uint32_t kHi = 0xBF003F00u;  // high bytes
-  const uint32_t s0 = perm(c, c, 0x01010000u) + 0x04000400u;
-  const uint32_t s1 = perm(c, c, 0x03030202u) + 0x04000400u;
-  return make_uint2(perm(kHi, kLo, s0), perm(kHi, kLo, s1));
+  const uint32_t sel = perm(c, c, HALF ? 0x03030202u : 0x01010000u) + 0x04000400u;
+  return perm(kHi, kLo, sel);
 }
 
 // Forward P: rows of 2-bit codes in the stored layout (tile pitch 48 bytes,
 // 32 bytes = 8 words = 128 codes per row per stage). Lane half h of k-step
 // ks takes word 4h + ks (codes k = 16(4h+ks)..+15, chunk map 1); one 16-byte
-// read per fragment per stage, expanded with (w >> 2t) & 0x03030303.
+// read per fragment per stage, expanded word by word with
+// (w >> 2t) & 0x03030303.
 struct CodesI8Frags {
   static constexpr int kPitchB = 48;
   uint4 raw[4];
+  MfmaI8::Frag cur[2][4];
   const char* base;
   __device__ __forceinline__ void init(const char* tile, int row0, int lane) {
     base = tile + (row0 + (lane & 31)) * kPitchB + 16 * (lane >> 5);
   }
+  template <int KS, int F, int T>
+  __device__ __forceinline__ void expand() {
+    const uint32_t w = KS == 0 ? raw[F].x : KS == 1 ? raw[F].y : KS == 2 ? raw[F].z : raw[F].w;
+    cur[KS & 1][F][T] = (int)codes4_to_i8((w >> (2 * T)) & 0x03030303u);
+  }
   template <int KS>
-  __device__ __forceinline__ void prefetch() {
+  __device__ __forceinline__ void start() {
     if constexpr (KS == 0) {
 #pragma unroll
       for (int f = 0; f < 4; ++f) raw[f] = *reinterpret_cast<const uint4*>(base + f * 32 * kPitchB);
+      expand<0, 0, 0>(); expand<0, 0, 1>(); expand<0, 0, 2>(); expand<0, 0, 3>();
     }
   }
-  template <int KS>
-  __device__ __forceinline__ MfmaI8::Frag get(int f) const {
-    const uint32_t w = KS == 0 ? raw[f].x : KS == 1 ? raw[f].y : KS == 2 ? raw[f].z : raw[f].w;
-    MfmaI8::Frag a;
-    a[0] = (int)codes4_to_i8(w & 0x03030303u);
-    a[1] = (int)codes4_to_i8((w >> 2) & 0x03030303u);
-    a[2] = (int)codes4_to_i8((w >> 4) & 0x03030303u);
-    a[3] = (int)codes4_to_i8((w >> 6) & 0x03030303u);
-    return a;
+  template <int KS, int U>
+  __device__ __forceinline__ void slot() {
+    if constexpr (U / 4 < 3) expand<KS, U / 4 + 1, U % 4>();
+    else if constexpr (KS + 1 < kKSteps) expand<KS + 1, 0, U % 4>();
   }
+  template <int KS>
+  __device__ __forceinline__ MfmaI8::Frag frag(int f) const { return cur[KS & 1][f]; }
 };
 
 // dX P: 2-bit codes transposed to [k][n] (tile pitch 24 bytes, 4 words = 64
 // n-codes per row per stage). Word v holds n = 16v..16v+15 in the stored
 // in-word order (code n' at bit 8(n'%4) + 2(n'/4)). Lane half h of k-step
 // ks takes n = 32h + 8ks..+7 (chunk map 1): word 2h + ks/2, fields
-// t = 2(ks%2), +1. One 8-byte read per fragment per stage.
+// t = 2(ks%2), +1. One 8-byte read per fragment per stage; a fragment is
+// expanded one output word per slot.
 struct CodesBf16TFrags {
   static constexpr int kPitchB = 24;
   uint2 raw[4];
+  u32x4_t cur[2][4];
   const char* base;
   __device__ __forceinline__ void init(const char* tile, int row0, int lane) {
     base = tile + (row0 + (lane & 31)) * kPitchB + 8 * (lane >> 5);
   }
+  template <int KS, int F, int T>
+  __device__ __forceinline__ void expand() {
+    const uint32_t w = KS < 2 ? raw[F].x : raw[F].y;
+    constexpr int fld = 2 * (KS & 1) + (T >> 1);
+    cur[KS & 1][F][T] = codes2_to_bf16<T & 1>((w >> (2 * fld)) & 0x03030303u);
+  }
   template <int KS>
-  __device__ __forceinline__ void prefetch() {
+  __device__ __forceinline__ void start() {
     if constexpr (KS == 0) {
 #pragma unroll
       for (int f = 0; f < 4; ++f) raw[f] = *reinterpret_cast<const uint2*>(base + f * 32 * kPitchB);
+      expand<0, 0, 0>(); expand<0, 0, 1>(); expand<0, 0, 2>(); expand<0, 0, 3>();
     }
   }
+  template <int KS, int U>
+  __device__ __forceinline__ void slot() {
+    if constexpr (U / 4 < 3) expand<KS, U / 4 + 1, U % 4>();
+    else if constexpr (KS + 1 < kKSteps) expand<KS + 1, 0, U % 4>();
+  }
   template <int KS>
-  __device__ __forceinline__ MfmaBf16::Frag get(int f) const {
-    const uint32_t w = KS < 2 ? raw[f].x : raw[f].y;
-    constexpr int t0 = 2 * (KS & 1);
-    const uint2 lo = codes4_to_bf16((w >> (2 * t0)) & 0x03030303u);
-    const uint2 hi = codes4_to_bf16((w >> (2 * t0 + 2)) & 0x03030303u);
-    return __builtin_bit_cast(MfmaBf16::Frag, u32x4_t{lo.x, lo.y, hi.x, hi.y});
+  __device__ __forceinline__ MfmaBf16::Frag frag(int f) const {
+    return __builtin_bit_cast(MfmaBf16::Frag, cur[KS & 1][f]);
   }
 };
 
 // ---------------------------------------------------------------------------
 // Operand loaders. load(): global -> registers for one stage (rows row0..+255
 // of the operand, reduction stage s); store(): registers -> LDS tile (used
-// for the first stage); stage_part<P>(): quarter P of the staging of the next
-// stage from registers into LDS and of the fetch of the stage after it.
+// for the first stage); slot<KS, U>(): the share of MFMA slot U of k-step KS
+// in staging the next stage from registers into LDS and fetching the stage
+// after it.
 // Out-of-range data (rows past the operand, reduction past its end, stages
 // past the last) reads as zeros through the buffer resource range check or
 // an out-of-range offset, so the loads of a stage are issued without
@@ -287,27 +318,27 @@ struct CopyLoader {
     for (int h = 0; h < 8; ++h) *reinterpret_cast<uint4*>(dst + h * kPitch) = r.v[h];
   }
 
-  // Staging split into 4 parts (one per k-step of the current stage): part
-  // P stores rows 2P, 2P+1 of the thread's block, then refills those
-  // registers with stage s+2.
+  // Staging of the next stage, spread over the slots of k-step KS: rows
+  // 2KS, 2KS+1 of the thread's block are stored (slots 1, 3), then refilled
+  // with stage s+2 (slots 9, 11).
   struct Tmp {};
-  template <int P>
-  __device__ __forceinline__ void stage_part(Regs& r, Tmp&, char* lds, const float*, int row0, int s2,
-                                             float*) const {
+  template <int KS, int U>
+  __device__ __forceinline__ void slot(Regs& r, Tmp&, char* lds, const float*, int row0, int s2,
+                                       float*) const {
     const int tid = threadIdx.x;
-    char* dst = lds + lds_off<kSwz>(8 * (tid >> 3), tid & 7);
-#pragma unroll
-    for (int h = 2 * P; h < 2 * P + 2; ++h) *reinterpret_cast<uint4*>(dst + h * kPitch) = r.v[h];
-    if constexpr (FULL) {
+    if constexpr (U == 1 || U == 3) {
+      constexpr int h = 2 * KS + (U == 3);
+      *reinterpret_cast<uint4*>(lds + lds_off<kSwz>(8 * (tid >> 3), tid & 7) + h * kPitch) = r.v[h];
+    }
+    if constexpr (FULL && (U == 9 || U == 11)) {
+      constexpr int h = 2 * KS + (U == 11);
       const rsrc_t rs = make_rsrc(base, (uint32_t)(rows * pitch));
       const int64_t rowb = row0 + 8 * (tid >> 3);
       const int64_t kb = (int64_t)s2 * kStageBytes + (tid & 7) * 16;
       const uint32_t off = kb < red_bytes ? (uint32_t)(rowb * pitch + kb) : kOob;
-#pragma unroll
-      for (int h = 2 * P; h < 2 * P + 2; ++h) r.v[h] = buf_load16(rs, off + (uint32_t)(h * pitch));
-    } else if (P == 3) {
-      load(r, row0, s2, nullptr);
+      r.v[h] = buf_load16(rs, off + (uint32_t)(h * pitch));
     }
+    if constexpr (!FULL && KS == kKSteps - 1 && U == 9) load(r, row0, s2, nullptr);
   }
 };
 
@@ -339,14 +370,16 @@ struct PackedCodesLoader {
     *reinterpret_cast<uint4*>(dst) = r.v[0];
     *reinterpret_cast<uint4*>(dst + 16) = r.v[1];
   }
-  // Parts 0 and 1 store one half of the row and refill it with stage s+2.
-  template <int P>
-  __device__ __forceinline__ void stage_part(Regs& r, Tmp&, char* lds, const float*, int row0, int s2,
-                                             float*) const {
-    if constexpr (P < 2) {
-      *reinterpret_cast<uint4*>(lds + threadIdx.x * CodesI8Frags::kPitchB + 16 * P) = r.v[P];
+  // K-steps 0 and 1 store one half of the row (slot 5) and refill it with
+  // stage s+2 (slot 13).
+  template <int KS, int U>
+  __device__ __forceinline__ void slot(Regs& r, Tmp&, char* lds, const float*, int row0, int s2,
+                                       float*) const {
+    if constexpr (KS < 2 && U == 5)
+      *reinterpret_cast<uint4*>(lds + threadIdx.x * CodesI8Frags::kPitchB + 16 * KS) = r.v[KS];
+    if constexpr (KS < 2 && U == 13) {
       const rsrc_t rs = make_rsrc(packed, (uint32_t)(rows * pitch));
-      r.v[P] = buf_load16(rs, offset(row0, s2, P));
+      r.v[KS] = buf_load16(rs, offset(row0, s2, KS));
     }
   }
 };
@@ -377,7 +410,7 @@ struct PackedCodesTLoader {
   int64_t pitch;  // Kp/4 bytes per n row
   int64_t nred;   // N (valid reduction rows)
   struct Regs { uint32_t d[4]; };
-  struct Tmp { uint32_t W[4]; };
+  struct Tmp { uint32_t a[8]; uint32_t W[4]; };
 
   __device__ __forceinline__ void load(Regs& r, int row0, int s, float*) const {
     const int tid = threadIdx.x;
@@ -388,18 +421,6 @@ struct PackedCodesTLoader {
     const uint32_t off = col < pitch ? (uint32_t)(n * pitch + col) : kOob;
 #pragma unroll
     for (int g = 0; g < 4; ++g) r.d[g] = buf_load4(rs, off + (uint32_t)(4 * g * pitch));
-  }
-  __device__ __forceinline__ void transpose(const Regs& r, Tmp& t) const {
-    const int lane = threadIdx.x & 63;
-    const int rr = lane >> 4, d = lane & 15;
-    const uint32_t sel = (uint32_t)rr | ((uint32_t)(rr + 4) << 8);
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      uint32_t a[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) a[e] = (uint32_t)__builtin_amdgcn_ds_bpermute((16 * e + d) << 2, (int)r.d[g]);
-      t.W[g] = gather_byte(a[0], a[1], a[2], a[3], sel);
-    }
   }
   // write row 16d + r + 4i' (i' = (I + d) % 4) of the wave's word column
   template <int I>
@@ -415,20 +436,51 @@ struct PackedCodesTLoader {
   }
   __device__ __forceinline__ void store(const Regs& r, char* lds, const float*) const {
     Tmp t;
-    transpose(r, t);
+    transpose_bperm<0>(r, t);
+    transpose_gather<0>(t);
+    transpose_bperm<1>(r, t);
+    transpose_gather<1>(t);
     write_row<0>(t, lds);
     write_row<1>(t, lds);
     write_row<2>(t, lds);
     write_row<3>(t, lds);
   }
-  // Part 0 transposes, parts 0..3 each write one row; part 1 refills the
-  // registers with stage s+2.
-  template <int P>
-  __device__ __forceinline__ void stage_part(Regs& r, Tmp& t, char* lds, const float*, int row0, int s2,
-                                             float*) const {
-    if constexpr (P == 0) transpose(r, t);
-    write_row<P>(t, lds);
-    if constexpr (P == 1) load(r, row0, s2, nullptr);
+  // Byte transpose of words g = 2G, 2G + 1 (ds_bpermute), then the gather.
+  template <int G>
+  __device__ __forceinline__ void transpose_bperm(const Regs& r, Tmp& t) const {
+    const int d = threadIdx.x & 15;
+#pragma unroll
+    for (int g = 2 * G; g < 2 * G + 2; ++g)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        t.a[4 * (g - 2 * G) + e] = (uint32_t)__builtin_amdgcn_ds_bpermute((16 * e + d) << 2, (int)r.d[g]);
+  }
+  template <int G>
+  __device__ __forceinline__ void transpose_gather(Tmp& t) const {
+    const uint32_t rr = (threadIdx.x & 63) >> 4;
+    const uint32_t sel = rr | ((rr + 4) << 8);
+#pragma unroll
+    for (int g = 2 * G; g < 2 * G + 2; ++g) {
+      const int o = 4 * (g - 2 * G);
+      t.W[g] = gather_byte(t.a[o], t.a[o + 1], t.a[o + 2], t.a[o + 3], sel);
+    }
+  }
+  // K-step 0 transposes (slots 2, 6, 8, 12) and writes row 0 (slot 14);
+  // k-steps 1..3 write one row each (slot 2); k-step 1 refills the
+  // registers with stage s+2 (slot 10).
+  template <int KS, int U>
+  __device__ __forceinline__ void slot(Regs& r, Tmp& t, char* lds, const float*, int row0, int s2,
+                                       float*) const {
+    if constexpr (KS == 0) {
+      if constexpr (U == 2) transpose_bperm<0>(r, t);
+      if constexpr (U == 6) transpose_gather<0>(t);
+      if constexpr (U == 8) transpose_bperm<1>(r, t);
+      if constexpr (U == 12) transpose_gather<1>(t);
+      if constexpr (U == 14) write_row<0>(t, lds);
+    } else {
+      if constexpr (U == 2) write_row<KS>(t, lds);
+      if constexpr (KS == 1 && U == 10) load(r, row0, s2, nullptr);
+    }
   }
 };
 
@@ -491,37 +543,40 @@ struct RowTransposeBf16Loader {
     }
   }
 
-  // Part P writes half hh = P/2 (m rows 8hh..8hh+7 of the thread's 16) for
-  // n columns q = 2(P&1), +1; odd parts then refill that half's 8 rows with
-  // stage s+2.
+  // Staging in the slots of k-step KS: half hh = KS/2 (m rows 8hh..8hh+7 of
+  // the thread's 16), n columns q = 2(KS&1), +1 (slots 11, 12; each uses
+  // all 8 rows); odd k-steps then refill that half's 8 rows with stage s+2
+  // (slots 13, 14).
   struct Tmp {};
-  template <int P>
-  __device__ __forceinline__ void stage_part(Regs& r, Tmp&, char* lds, const float*, int row0, int s2,
-                                             float*) const {
-    constexpr int hh = P >> 1;
+  __device__ __forceinline__ void write_q(const Regs& r, char* lds, int hh, int q) const {
     const int tid = threadIdx.x;
     const int nq = tid & 63, mg = tid >> 6;
     char* dst = lds + lds_off<kSwz>(4 * nq, 2 * mg + hh);
     const uint2* v = r.v + 8 * hh;
-#pragma unroll
-    for (int q = 2 * (P & 1); q < 2 * (P & 1) + 2; ++q) {
-      const uint32_t sel = (q & 1) ? 0x07060302u : 0x05040100u;
-      uint4 o;
-      o.x = perm((q >> 1) ? v[1].y : v[1].x, (q >> 1) ? v[0].y : v[0].x, sel);
-      o.y = perm((q >> 1) ? v[3].y : v[3].x, (q >> 1) ? v[2].y : v[2].x, sel);
-      o.z = perm((q >> 1) ? v[5].y : v[5].x, (q >> 1) ? v[4].y : v[4].x, sel);
-      o.w = perm((q >> 1) ? v[7].y : v[7].x, (q >> 1) ? v[6].y : v[6].x, sel);
-      *reinterpret_cast<uint4*>(dst + q * kPitch) = o;
-    }
-    if constexpr (P & 1) {
+    const uint32_t sel = (q & 1) ? 0x07060302u : 0x05040100u;
+    uint4 o;
+    o.x = perm((q >> 1) ? v[1].y : v[1].x, (q >> 1) ? v[0].y : v[0].x, sel);
+    o.y = perm((q >> 1) ? v[3].y : v[3].x, (q >> 1) ? v[2].y : v[2].x, sel);
+    o.z = perm((q >> 1) ? v[5].y : v[5].x, (q >> 1) ? v[4].y : v[4].x, sel);
+    o.w = perm((q >> 1) ? v[7].y : v[7].x, (q >> 1) ? v[6].y : v[6].x, sel);
+    *reinterpret_cast<uint4*>(dst + q * kPitch) = o;
+  }
+  template <int KS, int U>
+  __device__ __forceinline__ void slot(Regs& r, Tmp&, char* lds, const float*, int row0, int s2,
+                                       float*) const {
+    constexpr int hh = KS >> 1;
+    if constexpr (U == 11 || U == 12) write_q(r, lds, hh, 2 * (KS & 1) + (U == 12));
+    if constexpr ((KS & 1) && (U == 13 || U == 14)) {
       if constexpr (VEC) {
+        const int tid = threadIdx.x;
         const rsrc_t rs = make_rsrc(dy, (uint32_t)(mred * ld * 2));
-        const int64_t m = (int64_t)s2 * kRed16 + 16 * mg;
-        const int64_t n = row0 + 4 * nq;
+        const int64_t m = (int64_t)s2 * kRed16 + 16 * (tid >> 6);
+        const int64_t n = row0 + 4 * (tid & 63);
         const uint32_t off = n < rows ? (uint32_t)((m * ld + n) * 2) : kOob;
+        constexpr int e0 = 8 * hh + (U == 14 ? 4 : 0);
 #pragma unroll
-        for (int e = 8 * hh; e < 8 * hh + 8; ++e) r.v[e] = buf_load8(rs, off + (uint32_t)(e * ld * 2));
-      } else if (P == 3) {
+        for (int e = e0; e < e0 + 4; ++e) r.v[e] = buf_load8(rs, off + (uint32_t)(e * ld * 2));
+      } else if constexpr (KS == kKSteps - 1 && U == 14) {
         load(r, row0, s2, nullptr);
       }
     }
@@ -585,48 +640,59 @@ struct Int8TransposeScaleLoader {
     }
   }
 
-  // Part P converts half hh = P/2 (m rows 8hh..8hh+7 of the thread's 16) for
-  // k rows p = 2(P&1), +1; odd parts refill that half with stage s+2, and
-  // the last part also publishes stage s+2's scales.
-  struct Tmp { float rs[8]; };
-  template <int P>
-  __device__ __forceinline__ void stage_part(Regs& r, Tmp& t, char* lds, const float* scale_in, int row0,
-                                             int s2, float* scale_out) const {
-    constexpr int hh = P >> 1;
+  // Staging in the slots of k-step KS: half hh = KS/2 (m rows 8hh..8hh+7
+  // of the thread's 16), k rows p = 2(KS&1) (slots 1..4 convert, slot 5
+  // stores) and p + 1 (slots 6..9, 10); the scales of the half are read at
+  // slot 0 of even k-steps; odd k-steps refill the half with stage s+2
+  // (slots 11..14); stage s+2's scales are fetched in k-step 1 and
+  // published in k-step 3 (slot 15).
+  struct Tmp { float rs[8]; float bias[8]; uint32_t o[4]; float s_raw; };
+  __device__ __forceinline__ void convert2(const Regs& r, Tmp& t, int hh, int p, int e) const {
+    // byte p of rows e, e+1 biased to [1, 255]: f*r - 128r = x_q*r exactly
+    // before the single rounding of the fma
+    const float f0 = (float)(((r.d[8 * hh + e] ^ 0x80808080u) >> (8 * p)) & 0xFFu);
+    const float f1 = (float)(((r.d[8 * hh + e + 1] ^ 0x80808080u) >> (8 * p)) & 0xFFu);
+    t.o[e >> 1] = pack_bf16x2(fmaf(f0, t.rs[e], t.bias[e]), fmaf(f1, t.rs[e + 1], t.bias[e + 1]));
+  }
+  __device__ __forceinline__ void write_p(const Tmp& t, char* lds, int hh, int p) const {
     const int tid = threadIdx.x;
     const int kq = tid & 63, mg = tid >> 6;
-    if constexpr ((P & 1) == 0) {
+    char* dst = lds + lds_off<kSwz>(4 * kq, 2 * mg + hh);
+    *reinterpret_cast<uint4*>(dst + p * kPitch) = make_uint4(t.o[0], t.o[1], t.o[2], t.o[3]);
+  }
+  template <int KS, int U>
+  __device__ __forceinline__ void slot(Regs& r, Tmp& t, char* lds, const float* scale_in, int row0, int s2,
+                                       float* scale_out) const {
+    constexpr int hh = KS >> 1;
+    const int tid = threadIdx.x;
+    const int kq = tid & 63, mg = tid >> 6;
+    if constexpr ((KS & 1) == 0 && U == 0) {
       const float4 sa = *reinterpret_cast<const float4*>(scale_in + 16 * mg + 8 * hh);
       const float4 sb = *reinterpret_cast<const float4*>(scale_in + 16 * mg + 8 * hh + 4);
       t.rs[0] = sa.x; t.rs[1] = sa.y; t.rs[2] = sa.z; t.rs[3] = sa.w;
       t.rs[4] = sb.x; t.rs[5] = sb.y; t.rs[6] = sb.z; t.rs[7] = sb.w;
-    }
-    char* dst = lds + lds_off<kSwz>(4 * kq, 2 * mg + hh);
 #pragma unroll
-    for (int p = 2 * (P & 1); p < 2 * (P & 1) + 2; ++p) {
-      float v[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float f = (float)(((r.d[8 * hh + e] ^ 0x80808080u) >> (8 * p)) & 0xFFu);
-        v[e] = fmaf(f, t.rs[e], -128.0f * t.rs[e]);
-      }
-      *reinterpret_cast<uint4*>(dst + p * kPitch) =
-          make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-                     pack_bf16x2(v[6], v[7]));
+      for (int e = 0; e < 8; ++e) t.bias[e] = -128.0f * t.rs[e];
     }
-    if constexpr (P & 1) {
+    constexpr int p0 = 2 * (KS & 1);
+    if constexpr (U >= 1 && U <= 4) convert2(r, t, hh, p0, 2 * (U - 1));
+    if constexpr (U == 5) write_p(t, lds, hh, p0);
+    if constexpr (U >= 6 && U <= 9) convert2(r, t, hh, p0 + 1, 2 * (U - 6));
+    if constexpr (U == 10) write_p(t, lds, hh, p0 + 1);
+    if constexpr ((KS & 1) && U >= 11 && U <= 14) {
       const rsrc_t rs = make_rsrc(xq, (uint32_t)(mred * pitch));
       const int64_t m = (int64_t)s2 * kRed16 + 16 * mg;
       const int64_t k = row0 + 4 * kq;
       const uint32_t off = k < pitch ? (uint32_t)(m * pitch + k) : kOob;
+      constexpr int e0 = 8 * hh + 2 * (U - 11);
 #pragma unroll
-      for (int e = 8 * hh; e < 8 * hh + 8; ++e) r.d[e] = buf_load4(rs, off + (uint32_t)(e * pitch));
+      for (int e = e0; e < e0 + 2; ++e) r.d[e] = buf_load4(rs, off + (uint32_t)(e * pitch));
     }
-    if constexpr (P == 3) {
+    if constexpr (KS == 1 && U == 15) {
       const rsrc_t rsc = make_rsrc(s, (uint32_t)(mred * 4));
-      const uint32_t mm = (uint32_t)(s2 * kRed16 + (tid & 63));
-      scale_out[tid & 63] = __uint_as_float(buf_load4(rsc, mm * 4)) / 127.0f;
+      t.s_raw = __uint_as_float(buf_load4(rsc, (uint32_t)(s2 * kRed16 + (tid & 63)) * 4));
     }
+    if constexpr (KS == 3 && U == 15) scale_out[tid & 63] = t.s_raw / 127.0f;
   }
 };
 
@@ -820,22 +886,24 @@ __device__ __forceinline__ void zero_acc(Acc& a) {
   for (int e = 0; e < 16; ++e) a[e] = 0;
 }
 
-// Instruction classes of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSgMfma = 0x008, kSgValu = 0x002, kSgVmemRead = 0x020, kSgDsRead = 0x100,
-              kSgDsWrite = 0x200;
-
-// Order inside one k-step, after its fragment reads: the 16 MFMAs, each
-// followed by a share of the VALU work (fragment expansion, staging), with
-// the staging's LDS stores, LDS reads and global loads spread between them.
-__device__ __forceinline__ void kstep_schedule() {
-#pragma unroll
-  for (int m = 0; m < kFI * kFJ; ++m) {
-    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kSgValu, 3, 0);
-    if ((m & 3) == 0) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
-    if ((m & 3) == 1) __builtin_amdgcn_sched_group_barrier(kSgDsWrite, 1, 0);
-    if ((m & 3) == 3) __builtin_amdgcn_sched_group_barrier(kSgVmemRead, 2, 0);
-  }
+// One MFMA slot of a k-step: MFMA (U / 4, U % 4), then each reader's and
+// loader's share of the work for U (issued behind the MFMA so that it
+// overlaps its 32 cycles), fenced from the next slot so that the compiler
+// keeps this interleave.
+template <int KS, int U, class MT, class PL, class QL, class FP, class FQ>
+__device__ __forceinline__ void gemm_slot(const PL& pl, const QL& ql, typename PL::Regs& pr,
+                                          typename QL::Regs& qr, typename PL::Tmp& pt,
+                                          typename QL::Tmp& qt, FP& fp, FQ& fq, char* Pn, char* Qn,
+                                          const float* sc_next, float* sc_after,
+                                          typename MT::Acc (&acc)[kFI][kFJ], int i0, int j0, int s2) {
+  acc[U / 4][U % 4] = MT::mma(fp.template frag<KS>(U / 4), fq.template frag<KS>(U % 4), acc[U / 4][U % 4]);
+  fp.template slot<KS, U>();
+  fq.template slot<KS, U>();
+  pl.template slot<KS, U>(pr, pt, Pn, sc_next, i0, s2, sc_after);
+  ql.template slot<KS, U>(qr, qt, Qn, sc_next, j0, s2, sc_after);
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (U + 1 < kFI * kFJ)
+    gemm_slot<KS, U + 1, MT>(pl, ql, pr, qr, pt, qt, fp, fq, Pn, Qn, sc_next, sc_after, acc, i0, j0, s2);
 }
 
 template <int KS, class MT, class PL, class QL, class FP, class FQ>
@@ -844,24 +912,10 @@ __device__ __forceinline__ void gemm_kstep(const PL& pl, const QL& ql, typename 
                                            typename QL::Tmp& qt, FP& fp, FQ& fq, char* Pn, char* Qn,
                                            const float* sc_next, float* sc_after,
                                            typename MT::Acc (&acc)[kFI][kFJ], int i0, int j0, int s2) {
-  if constexpr (KS + 1 < kKSteps) {
-    fp.template prefetch<KS + 1>();
-    fq.template prefetch<KS + 1>();
-  }
+  fp.template start<KS>();
+  fq.template start<KS>();
   __builtin_amdgcn_sched_barrier(0);
-  typename MT::Frag a[kFI], b[kFJ];
-#pragma unroll
-  for (int fi = 0; fi < kFI; ++fi) a[fi] = fp.template get<KS>(fi);
-#pragma unroll
-  for (int fj = 0; fj < kFJ; ++fj) b[fj] = fq.template get<KS>(fj);
-#pragma unroll
-  for (int fi = 0; fi < kFI; ++fi)
-#pragma unroll
-    for (int fj = 0; fj < kFJ; ++fj) acc[fi][fj] = MT::mma(a[fi], b[fj], acc[fi][fj]);
-  pl.template stage_part<KS>(pr, pt, Pn, sc_next, i0, s2, sc_after);
-  ql.template stage_part<KS>(qr, qt, Qn, sc_next, j0, s2, sc_after);
-  kstep_schedule();
-  __builtin_amdgcn_sched_barrier(0);
+  gemm_slot<KS, 0, MT>(pl, ql, pr, qr, pt, qt, fp, fq, Pn, Qn, sc_next, sc_after, acc, i0, j0, s2);
 }
 
 // LDS: two stages, each a P tile followed by a Q tile; then the per-stage
@@ -888,8 +942,6 @@ __device__ __forceinline__ void gemm_stage(const PL& pl, const QL& ql, typename 
   typename QL::template Frags<MT, MAP> fq;
   fp.init(cur, prow0, lane);
   fq.init(cur + PL::kTileB, qrow0, lane);
-  fp.template prefetch<0>();
-  fq.template prefetch<0>();
   typename PL::Tmp pt;
   typename QL::Tmp qt;
   char* Pn = nxt;
