@@ -165,16 +165,6 @@ __device__ __forceinline__ uint32_t codes4_to_i8(uint32_t c) {
   return perm(0u, 0xFF000100u, c);
 }
 
-// Four 2-bit codes in the byte lanes of c -> bf16 (+1 = 0x3F80, -1 = 0xBF80,
-// 0 = 0) of the codes in bytes 0, 1 (HALF 0) or 2, 3 (HALF 1), one word.
-template <int HALF>
-__device__ __forceinline__ uint32_t codes2_to_bf16(uint32_t c) {
-  constexpr uint32_t kLo = 0x80008000u;  // low bytes of bf16(code) for codes 0..3
-  constexpr uint32_t kHi = 0xBF003F00u;  // high bytes
-  const uint32_t sel = perm(c, c, HALF ? 0x03030202u : 0x01010000u) + 0x04000400u;
-  return perm(kHi, kLo, sel);
-}
-
 // Forward P: rows of 2-bit codes in the stored layout (tile pitch 48 bytes,
 // 32 bytes = 8 words = 128 codes per row per stage). Lane half h of k-step
 // ks takes word 4h + ks (codes k = 16(4h+ks)..+15, chunk map 1); one 16-byte
@@ -210,31 +200,30 @@ struct CodesI8Frags {
   __device__ __forceinline__ MfmaI8::Frag frag(int f) const { return cur[KS & 1][f]; }
 };
 
-// dX P: 2-bit codes transposed to [k][n] (tile pitch 24 bytes, 4 words = 64
-// n-codes per row per stage). Word v holds n = 16v..16v+15 in the stored
-// in-word order (code n' at bit 8(n'%4) + 2(n'/4)). Lane half h of k-step
-// ks takes n = 32h + 8ks..+7 (chunk map 1): word 2h + ks/2, fields
-// t = 2(ks%2), +1. One 8-byte read per fragment per stage; a fragment is
-// expanded one output word per slot.
-struct CodesBf16TFrags {
-  static constexpr int kPitchB = 24;
-  uint2 raw[4];
+// dX P: the ternary codes transposed to [k][n] as fp4 (E2M1) nibbles in n
+// order (tile pitch 48 bytes, 32 bytes = 64 n per row per stage): +1 = 0x2,
+// -1 = 0xA, 0 = 0x0, n even in the low nibble. Lane half h of k-step ks
+// takes n = 32h + 8ks..+7 (chunk map 1), dword ks of the 16 bytes at 16h:
+// one 16-byte read per fragment per stage. A fragment is expanded by four
+// v_cvt_scalef32_pk_bf16_fp4 (scale 1: exact +-1, 0), one per slot.
+struct CodesFp4Frags {
+  static constexpr int kPitchB = 48;
+  uint4 raw[4];
   u32x4_t cur[2][4];
   const char* base;
   __device__ __forceinline__ void init(const char* tile, int row0, int lane) {
-    base = tile + (row0 + (lane & 31)) * kPitchB + 8 * (lane >> 5);
+    base = tile + (row0 + (lane & 31)) * kPitchB + 16 * (lane >> 5);
   }
   template <int KS, int F, int T>
   __device__ __forceinline__ void expand() {
-    const uint32_t w = KS < 2 ? raw[F].x : raw[F].y;
-    constexpr int fld = 2 * (KS & 1) + (T >> 1);
-    cur[KS & 1][F][T] = codes2_to_bf16<T & 1>((w >> (2 * fld)) & 0x03030303u);
+    const uint32_t w = KS == 0 ? raw[F].x : KS == 1 ? raw[F].y : KS == 2 ? raw[F].z : raw[F].w;
+    cur[KS & 1][F][T] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, T));
   }
   template <int KS>
   __device__ __forceinline__ void start() {
     if constexpr (KS == 0) {
 #pragma unroll
-      for (int f = 0; f < 4; ++f) raw[f] = *reinterpret_cast<const uint2*>(base + f * 32 * kPitchB);
+      for (int f = 0; f < 4; ++f) raw[f] = *reinterpret_cast<const uint4*>(base + f * 32 * kPitchB);
       expand<0, 0, 0>(); expand<0, 0, 1>(); expand<0, 0, 2>(); expand<0, 0, 3>();
     }
   }
@@ -392,25 +381,24 @@ __device__ __forceinline__ uint32_t gather_byte(uint32_t a0, uint32_t a1, uint32
   return perm(t23, t01, 0x05040100u);
 }
 
-// dX P: the 2-bit codes [N][Kp/4] transposed into [k][n] code words. A
-// stage is 64 n-rows x 64 bytes (k0..k0+255). Wave w handles n = 16w..+15
-// (word w of every k row): lane (r = l/16, d = l%16) loads word d (k =
-// k0+16d..+15) of rows n = 16w+4g+r, g < 4. Byte r of such a word holds the
-// codes of k = k0+16d+r+4i (i < 4) at bits 2i; an in-wave byte transpose
-// (ds_bpermute) gives lane (r, d) byte r of the 16 rows, from which it
-// assembles, for each i, the word of row k = 16d+r+4i: code of n = 16w+4g+e
-// at bit 8e+2g. The four rows are written in a lane-rotated order to spread
-// the stores over the banks.
+// dX P: the 2-bit codes [N][Kp/4] transposed into [k][n] fp4 rows. A stage
+// is 64 n-rows x 64 bytes (k0..k0+255). Wave w handles n = 16w..+15: lane
+// (r = l/16, d = l%16) loads word d (k = k0+16d..+15) of rows n = 16w+4g+r,
+// g < 4. Byte r of such a word holds the codes of k = k0+16d+r+4i (i < 4) at
+// bits 2i; an in-wave byte transpose (ds_bpermute) gives lane (r, d) byte r
+// of the 16 rows; for each i it then writes row k = 16d+r+4i: the fp4
+// nibbles of n = 16w..16w+15 (8 bytes at 8w). The four rows are written in
+// a lane-rotated order to spread the stores over the banks.
 struct PackedCodesTLoader {
   static constexpr bool kSwz = false;
-  static constexpr int kTileB = 256 * CodesBf16TFrags::kPitchB;
+  static constexpr int kTileB = 256 * CodesFp4Frags::kPitchB;
   template <class MT, int MAP>
-  using Frags = CodesBf16TFrags;
+  using Frags = CodesFp4Frags;
   const uint8_t* packed;
   int64_t pitch;  // Kp/4 bytes per n row
   int64_t nred;   // N (valid reduction rows)
   struct Regs { uint32_t d[4]; };
-  struct Tmp { uint32_t a[8]; uint32_t W[4]; };
+  struct Tmp { uint32_t a[8]; uint32_t W[4]; uint32_t lo; };
 
   __device__ __forceinline__ void load(Regs& r, int row0, int s, float*) const {
     const int tid = threadIdx.x;
@@ -422,17 +410,32 @@ struct PackedCodesTLoader {
 #pragma unroll
     for (int g = 0; g < 4; ++g) r.d[g] = buf_load4(rs, off + (uint32_t)(4 * g * pitch));
   }
-  // write row 16d + r + 4i' (i' = (I + d) % 4) of the wave's word column
-  template <int I>
-  __device__ __forceinline__ void write_row(const Tmp& t, char* lds) const {
+  // fp4 nibbles (n order) of the codes of n = 16w + 4g + 0..3 for row
+  // k = 16d + r + 4ii: field ii of t.W[g] holds them in bytes 0..3
+  __device__ __forceinline__ uint32_t fp4_pair(const Tmp& t, int g, int ii) const {
+    const uint32_t x = (t.W[g] >> (2 * ii)) & 0x03030303u;
+    const uint32_t nib = perm(0u, 0x0A000200u, x);  // code 0, 1, 3 -> fp4 0x0, 0x2, 0xA
+    return nib | (nib >> 4);  // bytes 0 and 2: two nibbles each
+  }
+  // half H (n = 16w + 8H..+7) of row 16d + r + 4i' (i' = (I + d) % 4) of the
+  // wave's 8-byte column; half 1 also stores the row
+  template <int I, int H>
+  __device__ __forceinline__ void write_row_half(Tmp& t, char* lds) const {
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
     const int rr = lane >> 4, d = lane & 15;
     const int ii = (I + d) & 3;
-    uint32_t out = 0;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) out |= ((t.W[g] >> (2 * ii)) & 0x03030303u) << (2 * g);
-    *reinterpret_cast<uint32_t*>(lds + (16 * d + rr + 4 * ii) * CodesBf16TFrags::kPitchB + 4 * w) = out;
+    const uint32_t v = perm(fp4_pair(t, 2 * H + 1, ii), fp4_pair(t, 2 * H, ii), 0x06040200u);
+    if constexpr (H == 0) {
+      t.lo = v;
+    } else {
+      *reinterpret_cast<uint2*>(lds + (16 * d + rr + 4 * ii) * CodesFp4Frags::kPitchB + 8 * w) = make_uint2(t.lo, v);
+    }
+  }
+  template <int I>
+  __device__ __forceinline__ void write_row(Tmp& t, char* lds) const {
+    write_row_half<I, 0>(t, lds);
+    write_row_half<I, 1>(t, lds);
   }
   __device__ __forceinline__ void store(const Regs& r, char* lds, const float*) const {
     Tmp t;
@@ -465,8 +468,8 @@ struct PackedCodesTLoader {
       t.W[g] = gather_byte(t.a[o], t.a[o + 1], t.a[o + 2], t.a[o + 3], sel);
     }
   }
-  // K-step 0 transposes (slots 2, 6, 8, 12) and writes row 0 (slot 14);
-  // k-steps 1..3 write one row each (slot 2); k-step 1 refills the
+  // K-step 0 transposes (slots 2, 6, 8, 12) and writes row 0 (slots 14,
+  // 15); k-steps 1..3 write one row each (slots 2, 4); k-step 1 refills the
   // registers with stage s+2 (slot 10).
   template <int KS, int U>
   __device__ __forceinline__ void slot(Regs& r, Tmp& t, char* lds, const float*, int row0, int s2,
@@ -476,9 +479,11 @@ struct PackedCodesTLoader {
       if constexpr (U == 6) transpose_gather<0>(t);
       if constexpr (U == 8) transpose_bperm<1>(r, t);
       if constexpr (U == 12) transpose_gather<1>(t);
-      if constexpr (U == 14) write_row<0>(t, lds);
+      if constexpr (U == 14) write_row_half<0, 0>(t, lds);
+      if constexpr (U == 15) write_row_half<0, 1>(t, lds);
     } else {
-      if constexpr (U == 2) write_row<KS>(t, lds);
+      if constexpr (U == 2) write_row_half<KS, 0>(t, lds);
+      if constexpr (U == 4) write_row_half<KS, 1>(t, lds);
       if constexpr (KS == 1 && U == 10) load(r, row0, s2, nullptr);
     }
   }
