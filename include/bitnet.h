@@ -30,8 +30,9 @@
  *  - Size limits (BITNET_ERR_SHAPE beyond them): M, N <= 2^30, K <= 2^24;
  *    for the GEMM entry points every operand the call reads among x_q,
  *    w_packed and dY satisfies (rows + 256) * row_bytes <= 2^31, i.e.
- *    (M + 256) * Kp, (N + 256) * Kp/4 and (M + 256) * 2N bytes (the kernels
- *    address them with 32-bit offsets).
+ *    (M + 256) * Kp, (N + 256) * Kp/4 and (M + 256) * 2N bytes, and with dW
+ *    also (M + 256) * 2Kp for its bf16 x_hat (the kernels address them with
+ *    32-bit offsets).
  */
 #ifndef BITNET_H
 #define BITNET_H
@@ -75,7 +76,9 @@ size_t bitnet_ternarize_workspace_bytes(int64_t N, int64_t K);
  * per workgroup piece, at most about 128 MiB. The contents need no
  * initialization; a workspace must not be shared by calls that may run at
  * the same time (calls on one stream may share it). bitlinear_bwd's size
- * covers both of its products, which run one after the other. */
+ * covers both of its products, which run one after the other; with dW it
+ * includes a transient bf16 x_hat = bf16(x_q * s/127) [M][Kp] (2*M*Kp bytes)
+ * built at the start of the dW product. */
 size_t bitlinear_fwd_workspace_bytes(int64_t M, int64_t N, int64_t K);
 size_t bitlinear_bwd_workspace_bytes(int64_t M, int64_t N, int64_t K);
 

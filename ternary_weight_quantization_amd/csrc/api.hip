@@ -41,6 +41,7 @@ bool buffer_range_ok(int64_t rows, int64_t pitch_bytes) {
 bitnet_status check_gemm_ranges(int64_t M, int64_t N, int64_t K, bool need_xq, bool need_w, bool need_dy) {
   const int64_t Kp = bitnet::k_pad(K);
   if (need_xq && !buffer_range_ok(M, Kp)) return BITNET_ERR_SHAPE;
+  if (need_xq && !buffer_range_ok(M, 2 * Kp)) return BITNET_ERR_SHAPE;  // dW's bf16 x_hat
   if (need_w && !buffer_range_ok(N, Kp / 4)) return BITNET_ERR_SHAPE;
   if (need_dy && !buffer_range_ok(M, 2 * N)) return BITNET_ERR_SHAPE;
   return BITNET_OK;

@@ -267,7 +267,7 @@ struct CopyLoader {
   int64_t red_bytes;  // valid reduction bytes per row
   struct Regs { uint4 v[8]; };
 
-  __device__ __forceinline__ void load(Regs& r, int row0, int s, float*) const {
+  __device__ __forceinline__ void load(Regs& r, int row0, int s) const {
     const int tid = threadIdx.x;
     const int64_t rowb = row0 + 8 * (tid >> 3);
     const int64_t kb = (int64_t)s * kStageBytes + (tid & 7) * 16;
@@ -300,7 +300,7 @@ struct CopyLoader {
       }
     }
   }
-  __device__ __forceinline__ void store(const Regs& r, char* lds, const float*) const {
+  __device__ __forceinline__ void store(const Regs& r, char* lds) const {
     const int tid = threadIdx.x;
     char* dst = lds + lds_off<kSwz>(8 * (tid >> 3), tid & 7);
 #pragma unroll
@@ -312,8 +312,7 @@ struct CopyLoader {
   // with stage s+2 (slots 9, 11).
   struct Tmp {};
   template <int KS, int U>
-  __device__ __forceinline__ void slot(Regs& r, Tmp&, char* lds, const float*, int row0, int s2,
-                                       float*) const {
+  __device__ __forceinline__ void slot(Regs& r, Tmp&, char* lds, int row0, int s2) const {
     const int tid = threadIdx.x;
     if constexpr (U == 1 || U == 3) {
       constexpr int h = 2 * KS + (U == 3);
@@ -327,7 +326,7 @@ struct CopyLoader {
       const uint32_t off = kb < red_bytes ? (uint32_t)(rowb * pitch + kb) : kOob;
       r.v[h] = buf_load16(rs, off + (uint32_t)(h * pitch));
     }
-    if constexpr (!FULL && KS == kKSteps - 1 && U == 9) load(r, row0, s2, nullptr);
+    if constexpr (!FULL && KS == kKSteps - 1 && U == 9) load(r, row0, s2);
   }
 };
 
@@ -349,12 +348,12 @@ struct PackedCodesLoader {
     const int64_t col = (int64_t)s * (kStageBytes / 4) + 16 * h;
     return col < pitch ? (uint32_t)(row * pitch + col) : kOob;
   }
-  __device__ __forceinline__ void load(Regs& r, int row0, int s, float*) const {
+  __device__ __forceinline__ void load(Regs& r, int row0, int s) const {
     const rsrc_t rs = make_rsrc(packed, (uint32_t)(rows * pitch));
 #pragma unroll
     for (int h = 0; h < 2; ++h) r.v[h] = buf_load16(rs, offset(row0, s, h));
   }
-  __device__ __forceinline__ void store(const Regs& r, char* lds, const float*) const {
+  __device__ __forceinline__ void store(const Regs& r, char* lds) const {
     char* dst = lds + threadIdx.x * CodesI8Frags::kPitchB;
     *reinterpret_cast<uint4*>(dst) = r.v[0];
     *reinterpret_cast<uint4*>(dst + 16) = r.v[1];
@@ -362,8 +361,7 @@ struct PackedCodesLoader {
   // K-steps 0 and 1 store one half of the row (slot 5) and refill it with
   // stage s+2 (slot 13).
   template <int KS, int U>
-  __device__ __forceinline__ void slot(Regs& r, Tmp&, char* lds, const float*, int row0, int s2,
-                                       float*) const {
+  __device__ __forceinline__ void slot(Regs& r, Tmp&, char* lds, int row0, int s2) const {
     if constexpr (KS < 2 && U == 5)
       *reinterpret_cast<uint4*>(lds + threadIdx.x * CodesI8Frags::kPitchB + 16 * KS) = r.v[KS];
     if constexpr (KS < 2 && U == 13) {
@@ -400,7 +398,7 @@ struct PackedCodesTLoader {
   struct Regs { uint32_t d[4]; };
   struct Tmp { uint32_t a[8]; uint32_t W[4]; uint32_t lo; };
 
-  __device__ __forceinline__ void load(Regs& r, int row0, int s, float*) const {
+  __device__ __forceinline__ void load(Regs& r, int row0, int s) const {
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
     const rsrc_t rs = make_rsrc(packed, (uint32_t)(nred * pitch));
@@ -437,7 +435,7 @@ struct PackedCodesTLoader {
     write_row_half<I, 0>(t, lds);
     write_row_half<I, 1>(t, lds);
   }
-  __device__ __forceinline__ void store(const Regs& r, char* lds, const float*) const {
+  __device__ __forceinline__ void store(const Regs& r, char* lds) const {
     Tmp t;
     transpose_bperm<0>(r, t);
     transpose_gather<0>(t);
@@ -472,8 +470,7 @@ struct PackedCodesTLoader {
   // 15); k-steps 1..3 write one row each (slots 2, 4); k-step 1 refills the
   // registers with stage s+2 (slot 10).
   template <int KS, int U>
-  __device__ __forceinline__ void slot(Regs& r, Tmp& t, char* lds, const float*, int row0, int s2,
-                                       float*) const {
+  __device__ __forceinline__ void slot(Regs& r, Tmp& t, char* lds, int row0, int s2) const {
     if constexpr (KS == 0) {
       if constexpr (U == 2) transpose_bperm<0>(r, t);
       if constexpr (U == 6) transpose_gather<0>(t);
@@ -484,14 +481,16 @@ struct PackedCodesTLoader {
     } else {
       if constexpr (U == 2) write_row_half<KS, 0>(t, lds);
       if constexpr (U == 4) write_row_half<KS, 1>(t, lds);
-      if constexpr (KS == 1 && U == 10) load(r, row0, s2, nullptr);
+      if constexpr (KS == 1 && U == 10) load(r, row0, s2);
     }
   }
 };
 
-// dW Q: dY^T: rows n, reduction m (strided). Thread (mg = wave, nq = lane)
-// reads 4 bf16 (n = 4nq..4nq+3) from each of the rows m = 16mg..16mg+15 and
-// writes the 16 x 4 transpose as 4 rows of 16 m values.
+// dW operands from a bf16 [rows m][ld] matrix read transposed: rows j
+// (n of dY for Q, k of x_hat for P), reduction m (strided). Thread
+// (mg = wave, nq = lane) reads 4 bf16 (columns 4nq..4nq+3) from each of the
+// rows m = 16mg..16mg+15 and writes the 16 x 4 transpose as 4 rows of 16 m
+// values.
 template <bool VEC>
 struct RowTransposeBf16Loader {
   static constexpr bool kSwz = true;
@@ -499,12 +498,12 @@ struct RowTransposeBf16Loader {
   template <class MT, int MAP>
   using Frags = PlainFrags<MT, true, MAP>;
   const uint16_t* dy;
-  int64_t ld;    // N
+  int64_t ld;    // elements per source row (N, or Kp for x_hat)
   int64_t mred;  // M (valid reduction rows)
-  int64_t rows;  // N (valid rows)
+  int64_t rows;  // valid operand rows (N, or Kp)
   struct Regs { uint2 v[16]; };
 
-  __device__ __forceinline__ void load(Regs& r, int row0, int s, float*) const {
+  __device__ __forceinline__ void load(Regs& r, int row0, int s) const {
     const int tid = threadIdx.x;
     const int64_t m = (int64_t)s * kRed16 + 16 * (tid >> 6);
     const int64_t n = row0 + 4 * (tid & 63);
@@ -527,7 +526,7 @@ struct RowTransposeBf16Loader {
       }
     }
   }
-  __device__ __forceinline__ void store(const Regs& r, char* lds, const float*) const {
+  __device__ __forceinline__ void store(const Regs& r, char* lds) const {
     const int tid = threadIdx.x;
     const int nq = tid & 63, mg = tid >> 6;
     // element (m = e, n = q) is half (q & 1) of word (q >> 1) of v[e]
@@ -567,8 +566,7 @@ struct RowTransposeBf16Loader {
     *reinterpret_cast<uint4*>(dst + q * kPitch) = o;
   }
   template <int KS, int U>
-  __device__ __forceinline__ void slot(Regs& r, Tmp&, char* lds, const float*, int row0, int s2,
-                                       float*) const {
+  __device__ __forceinline__ void slot(Regs& r, Tmp&, char* lds, int row0, int s2) const {
     constexpr int hh = KS >> 1;
     if constexpr (U == 11 || U == 12) write_q(r, lds, hh, 2 * (KS & 1) + (U == 12));
     if constexpr ((KS & 1) && (U == 13 || U == 14)) {
@@ -582,124 +580,42 @@ struct RowTransposeBf16Loader {
 #pragma unroll
         for (int e = e0; e < e0 + 4; ++e) r.v[e] = buf_load8(rs, off + (uint32_t)(e * ld * 2));
       } else if constexpr (KS == kKSteps - 1 && U == 14) {
-        load(r, row0, s2, nullptr);
+        load(r, row0, s2);
       }
     }
   }
 };
 
-// dW P: x_hat^T from x_q [M][Kp] and s[M]: rows k, reduction m (strided).
-// x_hat = bf16(fl32(x_q * fl32(s/127))); for the scales act-quant produces
-// this equals the exactly rounded bf16(x_q * s / 127). Thread (mg = wave, kq
-// = lane) reads 4 int8 (k = 4kq..+3) from each of the rows m = 16mg..+15.
-// The 64 scales of a stage are computed by wave 0 when the stage is loaded
-// and published in LDS.
-struct Int8TransposeScaleLoader {
-  static constexpr bool kSwz = true;
-  static constexpr int kTileB = 256 * kPitch;
-  template <class MT, int MAP>
-  using Frags = PlainFrags<MT, true, MAP>;
-  const int8_t* xq;
-  const float* s;
-  int64_t pitch;  // Kp
-  int64_t mred;   // M
-  struct Regs { uint32_t d[16]; };
-
-  __device__ __forceinline__ void load(Regs& r, int row0, int st, float* scale_out) const {
-    const int tid = threadIdx.x;
-    const rsrc_t rs = make_rsrc(xq, (uint32_t)(mred * pitch));
-    const int64_t m = (int64_t)st * kRed16 + 16 * (tid >> 6);
-    const int64_t k = row0 + 4 * (tid & 63);
-    const uint32_t off = k < pitch ? (uint32_t)(m * pitch + k) : kOob;
+// dW P: x_hat = bf16(fl32(x_q * fl32(s/127))) is built once per backward
+// call into the workspace ([M][Kp] bf16; for the scales act-quant produces
+// it equals the exactly rounded bf16(x_q * s / 127)) and then staged like dY
+// (RowTransposeBf16Loader). Each element is converted once instead of once
+// per output tile column. Thread t converts 16 int8 of row m: each byte is
+// biased to [1, 255] so that u*r - 128r = x_q*r exactly before the single
+// rounding of the fma.
+__global__ __launch_bounds__(256) void xhat_kernel(const int8_t* __restrict__ xq, const float* __restrict__ s,
+                                                   int64_t M, int64_t Kp, uint16_t* __restrict__ xhat) {
+  const int64_t cpr = Kp / 16;  // 16-byte chunks per row
+  const int64_t total = M * cpr;
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < total;
+       c += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t m = c / cpr;
+    const float r = s[m] / 127.0f;
+    const float bias = -128.0f * r;
+    const uint4 v = reinterpret_cast<const uint4*>(xq)[c];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[8];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) r.d[e] = buf_load4(rs, off + (uint32_t)(e * pitch));
-    // every wave computes the stage's 64 scales (identical values, so the
-    // four stores of each entry agree); rows past M get 0
-    const rsrc_t rsc = make_rsrc(s, (uint32_t)(mred * 4));
-    const uint32_t mm = (uint32_t)(st * kRed16 + (tid & 63));
-    scale_out[tid & 63] = __uint_as_float(buf_load4(rsc, mm * 4)) / 127.0f;
-  }
-  __device__ __forceinline__ void store(const Regs& r, char* lds, const float* scale_in) const {
-    const int tid = threadIdx.x;
-    const int kq = tid & 63, mg = tid >> 6;
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      char* dst = lds + lds_off<kSwz>(4 * kq, 2 * mg + hh);  // rows 4kq..4kq+3 share the swizzle
-      const float4 sa = *reinterpret_cast<const float4*>(scale_in + 16 * mg + 8 * hh);
-      const float4 sb = *reinterpret_cast<const float4*>(scale_in + 16 * mg + 8 * hh + 4);
-      const float rs[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        float v[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          // byte p of row e biased to [1, 255]: f*r - 128r = x_q*r exactly
-          // before the single rounding of the fma
-          const float f = (float)(((r.d[8 * hh + e] ^ 0x80808080u) >> (8 * p)) & 0xFFu);
-          v[e] = fmaf(f, rs[e], -128.0f * rs[e]);
-        }
-        *reinterpret_cast<uint4*>(dst + p * kPitch) =
-            make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-                       pack_bf16x2(v[6], v[7]));
-      }
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t u = w[d] ^ 0x80808080u;
+      o[2 * d] = pack_bf16x2(fmaf((float)(u & 0xFFu), r, bias), fmaf((float)((u >> 8) & 0xFFu), r, bias));
+      o[2 * d + 1] = pack_bf16x2(fmaf((float)((u >> 16) & 0xFFu), r, bias), fmaf((float)(u >> 24), r, bias));
     }
+    uint4* dst = reinterpret_cast<uint4*>(xhat) + 2 * c;
+    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
   }
-
-  // Staging in the slots of k-step KS: half hh = KS/2 (m rows 8hh..8hh+7
-  // of the thread's 16), k rows p = 2(KS&1) (slots 1..4 convert, slot 5
-  // stores) and p + 1 (slots 6..9, 10); the scales of the half are read at
-  // slot 0 of even k-steps; odd k-steps refill the half with stage s+2
-  // (slots 11..14); stage s+2's scales are fetched in k-step 1 and
-  // published in k-step 3 (slot 15).
-  struct Tmp { float rs[8]; float bias[8]; uint32_t o[4]; float s_raw; };
-  __device__ __forceinline__ void convert2(const Regs& r, Tmp& t, int hh, int p, int e) const {
-    // byte p of rows e, e+1 biased to [1, 255]: f*r - 128r = x_q*r exactly
-    // before the single rounding of the fma
-    const float f0 = (float)(((r.d[8 * hh + e] ^ 0x80808080u) >> (8 * p)) & 0xFFu);
-    const float f1 = (float)(((r.d[8 * hh + e + 1] ^ 0x80808080u) >> (8 * p)) & 0xFFu);
-    t.o[e >> 1] = pack_bf16x2(fmaf(f0, t.rs[e], t.bias[e]), fmaf(f1, t.rs[e + 1], t.bias[e + 1]));
-  }
-  __device__ __forceinline__ void write_p(const Tmp& t, char* lds, int hh, int p) const {
-    const int tid = threadIdx.x;
-    const int kq = tid & 63, mg = tid >> 6;
-    char* dst = lds + lds_off<kSwz>(4 * kq, 2 * mg + hh);
-    *reinterpret_cast<uint4*>(dst + p * kPitch) = make_uint4(t.o[0], t.o[1], t.o[2], t.o[3]);
-  }
-  template <int KS, int U>
-  __device__ __forceinline__ void slot(Regs& r, Tmp& t, char* lds, const float* scale_in, int row0, int s2,
-                                       float* scale_out) const {
-    constexpr int hh = KS >> 1;
-    const int tid = threadIdx.x;
-    const int kq = tid & 63, mg = tid >> 6;
-    if constexpr ((KS & 1) == 0 && U == 0) {
-      const float4 sa = *reinterpret_cast<const float4*>(scale_in + 16 * mg + 8 * hh);
-      const float4 sb = *reinterpret_cast<const float4*>(scale_in + 16 * mg + 8 * hh + 4);
-      t.rs[0] = sa.x; t.rs[1] = sa.y; t.rs[2] = sa.z; t.rs[3] = sa.w;
-      t.rs[4] = sb.x; t.rs[5] = sb.y; t.rs[6] = sb.z; t.rs[7] = sb.w;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) t.bias[e] = -128.0f * t.rs[e];
-    }
-    constexpr int p0 = 2 * (KS & 1);
-    if constexpr (U >= 1 && U <= 4) convert2(r, t, hh, p0, 2 * (U - 1));
-    if constexpr (U == 5) write_p(t, lds, hh, p0);
-    if constexpr (U >= 6 && U <= 9) convert2(r, t, hh, p0 + 1, 2 * (U - 6));
-    if constexpr (U == 10) write_p(t, lds, hh, p0 + 1);
-    if constexpr ((KS & 1) && U >= 11 && U <= 14) {
-      const rsrc_t rs = make_rsrc(xq, (uint32_t)(mred * pitch));
-      const int64_t m = (int64_t)s2 * kRed16 + 16 * mg;
-      const int64_t k = row0 + 4 * kq;
-      const uint32_t off = k < pitch ? (uint32_t)(m * pitch + k) : kOob;
-      constexpr int e0 = 8 * hh + 2 * (U - 11);
-#pragma unroll
-      for (int e = e0; e < e0 + 2; ++e) r.d[e] = buf_load4(rs, off + (uint32_t)(e * pitch));
-    }
-    if constexpr (KS == 1 && U == 15) {
-      const rsrc_t rsc = make_rsrc(s, (uint32_t)(mred * 4));
-      t.s_raw = __uint_as_float(buf_load4(rsc, (uint32_t)(s2 * kRed16 + (tid & 63)) * 4));
-    }
-    if constexpr (KS == 3 && U == 15) scale_out[tid & 63] = t.s_raw / 127.0f;
-  }
-};
+}
 
 // ---------------------------------------------------------------------------
 // Epilogues: acc (wave tile origin i0, j0) -> memory. Lane l holds, for each
@@ -899,28 +815,26 @@ template <int KS, int U, class MT, class PL, class QL, class FP, class FQ>
 __device__ __forceinline__ void gemm_slot(const PL& pl, const QL& ql, typename PL::Regs& pr,
                                           typename QL::Regs& qr, typename PL::Tmp& pt,
                                           typename QL::Tmp& qt, FP& fp, FQ& fq, char* Pn, char* Qn,
-                                          const float* sc_next, float* sc_after,
                                           typename MT::Acc (&acc)[kFI][kFJ], int i0, int j0, int s2) {
   acc[U / 4][U % 4] = MT::mma(fp.template frag<KS>(U / 4), fq.template frag<KS>(U % 4), acc[U / 4][U % 4]);
   fp.template slot<KS, U>();
   fq.template slot<KS, U>();
-  pl.template slot<KS, U>(pr, pt, Pn, sc_next, i0, s2, sc_after);
-  ql.template slot<KS, U>(qr, qt, Qn, sc_next, j0, s2, sc_after);
+  pl.template slot<KS, U>(pr, pt, Pn, i0, s2);
+  ql.template slot<KS, U>(qr, qt, Qn, j0, s2);
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (U + 1 < kFI * kFJ)
-    gemm_slot<KS, U + 1, MT>(pl, ql, pr, qr, pt, qt, fp, fq, Pn, Qn, sc_next, sc_after, acc, i0, j0, s2);
+    gemm_slot<KS, U + 1, MT>(pl, ql, pr, qr, pt, qt, fp, fq, Pn, Qn, acc, i0, j0, s2);
 }
 
 template <int KS, class MT, class PL, class QL, class FP, class FQ>
 __device__ __forceinline__ void gemm_kstep(const PL& pl, const QL& ql, typename PL::Regs& pr,
                                            typename QL::Regs& qr, typename PL::Tmp& pt,
                                            typename QL::Tmp& qt, FP& fp, FQ& fq, char* Pn, char* Qn,
-                                           const float* sc_next, float* sc_after,
-                                           typename MT::Acc (&acc)[kFI][kFJ], int i0, int j0, int s2) {
+                                            typename MT::Acc (&acc)[kFI][kFJ], int i0, int j0, int s2) {
   fp.template start<KS>();
   fq.template start<KS>();
   __builtin_amdgcn_sched_barrier(0);
-  gemm_slot<KS, 0, MT>(pl, ql, pr, qr, pt, qt, fp, fq, Pn, Qn, sc_next, sc_after, acc, i0, j0, s2);
+  gemm_slot<KS, 0, MT>(pl, ql, pr, qr, pt, qt, fp, fq, Pn, Qn, acc, i0, j0, s2);
 }
 
 // LDS: two stages, each a P tile followed by a Q tile; then the per-stage
@@ -937,7 +851,7 @@ struct SmemLayout {
 // staging runs on zeros and is never read.
 template <int CUR, class MT, int MAP, class PL, class QL>
 __device__ __forceinline__ void gemm_stage(const PL& pl, const QL& ql, typename PL::Regs& pr,
-                                           typename QL::Regs& qr, char* smem, float (*sscale)[kRed16],
+                                           typename QL::Regs& qr, char* smem,
                                            typename MT::Acc (&acc)[kFI][kFJ], int i0, int j0, int s,
                                            int prow0, int qrow0, int lane) {
   typedef SmemLayout<PL, QL> L;
@@ -951,35 +865,35 @@ __device__ __forceinline__ void gemm_stage(const PL& pl, const QL& ql, typename 
   typename QL::Tmp qt;
   char* Pn = nxt;
   char* Qn = nxt + PL::kTileB;
-  gemm_kstep<0, MT>(pl, ql, pr, qr, pt, qt, fp, fq, Pn, Qn, sscale[CUR ^ 1], sscale[CUR], acc, i0, j0, s + 2);
-  gemm_kstep<1, MT>(pl, ql, pr, qr, pt, qt, fp, fq, Pn, Qn, sscale[CUR ^ 1], sscale[CUR], acc, i0, j0, s + 2);
-  gemm_kstep<2, MT>(pl, ql, pr, qr, pt, qt, fp, fq, Pn, Qn, sscale[CUR ^ 1], sscale[CUR], acc, i0, j0, s + 2);
-  gemm_kstep<3, MT>(pl, ql, pr, qr, pt, qt, fp, fq, Pn, Qn, sscale[CUR ^ 1], sscale[CUR], acc, i0, j0, s + 2);
+  gemm_kstep<0, MT>(pl, ql, pr, qr, pt, qt, fp, fq, Pn, Qn, acc, i0, j0, s + 2);
+  gemm_kstep<1, MT>(pl, ql, pr, qr, pt, qt, fp, fq, Pn, Qn, acc, i0, j0, s + 2);
+  gemm_kstep<2, MT>(pl, ql, pr, qr, pt, qt, fp, fq, Pn, Qn, acc, i0, j0, s + 2);
+  gemm_kstep<3, MT>(pl, ql, pr, qr, pt, qt, fp, fq, Pn, Qn, acc, i0, j0, s + 2);
   __syncthreads();
 }
 
-// The stages [s0, s1) of tile (i0, j0), accumulated into acc. LDS and the
-// per-stage scales are free on entry and on return.
+// The stages [s0, s1) of tile (i0, j0), accumulated into acc. LDS is free
+// on entry and on return.
 template <class MT, int MAP, class PL, class QL>
-__device__ __forceinline__ void run_stages(const PL& pl, const QL& ql, char* smem, float (*sscale)[kRed16],
+__device__ __forceinline__ void run_stages(const PL& pl, const QL& ql, char* smem,
                                            typename MT::Acc (&acc)[kFI][kFJ], int i0, int j0, int s0,
                                            int s1, int prow0, int qrow0, int lane) {
   typename PL::Regs pr;
   typename QL::Regs qr;
-  pl.load(pr, i0, s0, sscale[0]);
-  ql.load(qr, j0, s0, sscale[0]);
-  __syncthreads();  // per-stage scales published by load()
-  pl.store(pr, smem, sscale[0]);
-  ql.store(qr, smem + PL::kTileB, sscale[0]);
-  pl.load(pr, i0, s0 + 1, sscale[1]);
-  ql.load(qr, j0, s0 + 1, sscale[1]);
+  pl.load(pr, i0, s0);
+  ql.load(qr, j0, s0);
+  __syncthreads();
+  pl.store(pr, smem);
+  ql.store(qr, smem + PL::kTileB);
+  pl.load(pr, i0, s0 + 1);
+  ql.load(qr, j0, s0 + 1);
   __syncthreads();
   int s = s0;
   for (; s + 1 < s1; s += 2) {
-    gemm_stage<0, MT, MAP>(pl, ql, pr, qr, smem, sscale, acc, i0, j0, s, prow0, qrow0, lane);
-    gemm_stage<1, MT, MAP>(pl, ql, pr, qr, smem, sscale, acc, i0, j0, s + 1, prow0, qrow0, lane);
+    gemm_stage<0, MT, MAP>(pl, ql, pr, qr, smem, acc, i0, j0, s, prow0, qrow0, lane);
+    gemm_stage<1, MT, MAP>(pl, ql, pr, qr, smem, acc, i0, j0, s + 1, prow0, qrow0, lane);
   }
-  if (s < s1) gemm_stage<0, MT, MAP>(pl, ql, pr, qr, smem, sscale, acc, i0, j0, s, prow0, qrow0, lane);
+  if (s < s1) gemm_stage<0, MT, MAP>(pl, ql, pr, qr, smem, acc, i0, j0, s, prow0, qrow0, lane);
 }
 
 // Element e (0..3) of 16-byte chunk c (0..63) of a thread's accumulators:
@@ -1080,7 +994,6 @@ template <class MT, int MAP, class PL, class QL, class EP>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(PL pl, QL ql, EP ep, SplitPlan plan) {
   typedef SmemLayout<PL, QL> L;
   __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
-  __shared__ __attribute__((aligned(16))) float sscale[2][kRed16];
   __shared__ int s_flag;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1095,7 +1008,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(PL pl, QL ql, EP ep, 
     for (int fi = 0; fi < kFI; ++fi)
 #pragma unroll
       for (int fj = 0; fj < kFJ; ++fj) zero_acc(acc[fi][fj]);
-    run_stages<MT, MAP>(pl, ql, smem, sscale, acc, i0, j0, 0, plan.nstages, prow0, qrow0, lane);
+    run_stages<MT, MAP>(pl, ql, smem, acc, i0, j0, 0, plan.nstages, prow0, qrow0, lane);
     ep.store(acc, i0 + prow0, j0 + qrow0, lane);
     return;
   }
@@ -1113,7 +1026,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(PL pl, QL ql, EP ep, 
 #pragma unroll
       for (int fj = 0; fj < kFJ; ++fj) zero_acc(acc[fi][fj]);
 
-    run_stages<MT, MAP>(pl, ql, smem, sscale, acc, i0, j0, s0, s1, prow0, qrow0, lane);
+    run_stages<MT, MAP>(pl, ql, smem, acc, i0, j0, s0, s1, prow0, qrow0, lane);
     if ((s0 == 0 && s1 == plan.nstages) || finish_piece<MT>(plan, acc, v, t, &s_flag))
       ep.store(acc, i0 + prow0, j0 + qrow0, lane);
     it += s1 - s0;
@@ -1172,9 +1085,13 @@ static size_t split_workspace(const GemmShape& g, int grid) {
   return counters + 2 * (size_t)grid * kPartialBytes;
 }
 
+// dW's x_hat buffer at the start of its workspace.
+static size_t xhat_bytes(int64_t M, int64_t K) { return ((size_t)M * k_pad(K) * 2 + 255) / 256 * 256; }
+
 size_t gemm_workspace_bytes(GemmKind kind, int64_t M, int64_t N, int64_t K) {
   const GemmShape g = shape_of(kind, M, N, K);
-  return split_workspace(g, split_grid(g, kMaxGrid));
+  const size_t split = split_workspace(g, split_grid(g, kMaxGrid));
+  return kind == GemmKind::kBwdDw ? xhat_bytes(M, K) + split : split;
 }
 
 static int device_cus() {
@@ -1260,17 +1177,27 @@ hipError_t launch_bwd_dw(const uint16_t* dY, const int8_t* x_q, const float* s_x
                          int64_t N, int64_t K, void* dW, bool dw_is_f32, void* ws, size_t ws_bytes,
                          hipStream_t stream) {
   const int64_t Kp = k_pad(K);
-  Int8TransposeScaleLoader pl{x_q, s_x, Kp, M};
+  const size_t xb = xhat_bytes(M, K);
+  if (ws == nullptr || ws_bytes < xb) return hipErrorInvalidValue;  // the C ABI sized it
+  uint16_t* xhat = static_cast<uint16_t*>(ws);
+  void* split_ws = static_cast<char*>(ws) + xb;
+  const size_t split_bytes = ws_bytes - xb;
+  const int64_t chunks = M * (Kp / 16);
+  const int64_t want = (chunks + 255) / 256;
+  xhat_kernel<<<(int)(want < 4096 ? want : 4096), 256, 0, stream>>>(x_q, s_x, M, Kp, xhat);
+  if (hipError_t e = hipGetLastError()) return e;
+
+  RowTransposeBf16Loader<true> pl{xhat, Kp, M, Kp};
   const GemmShape g = shape_of(GemmKind::kBwdDw, M, N, K);
   const bool vec = (N % 4 == 0);
   if (dw_is_f32) {
     Bf16Epilogue<true> ep{dW, nullptr, K, N, K % 4 == 0};
-    if (vec) return run_gemm<MfmaBf16, 0>(pl, RowTransposeBf16Loader<true>{dY, N, M, N}, ep, g, ws, ws_bytes, stream);
-    return run_gemm<MfmaBf16, 0>(pl, RowTransposeBf16Loader<false>{dY, N, M, N}, ep, g, ws, ws_bytes, stream);
+    if (vec) return run_gemm<MfmaBf16, 0>(pl, RowTransposeBf16Loader<true>{dY, N, M, N}, ep, g, split_ws, split_bytes, stream);
+    return run_gemm<MfmaBf16, 0>(pl, RowTransposeBf16Loader<false>{dY, N, M, N}, ep, g, split_ws, split_bytes, stream);
   }
   Bf16Epilogue<false> ep{dW, nullptr, K, N, K % 4 == 0};
-  if (vec) return run_gemm<MfmaBf16, 0>(pl, RowTransposeBf16Loader<true>{dY, N, M, N}, ep, g, ws, ws_bytes, stream);
-  return run_gemm<MfmaBf16, 0>(pl, RowTransposeBf16Loader<false>{dY, N, M, N}, ep, g, ws, ws_bytes, stream);
+  if (vec) return run_gemm<MfmaBf16, 0>(pl, RowTransposeBf16Loader<true>{dY, N, M, N}, ep, g, split_ws, split_bytes, stream);
+  return run_gemm<MfmaBf16, 0>(pl, RowTransposeBf16Loader<false>{dY, N, M, N}, ep, g, split_ws, split_bytes, stream);
 }
 
 }  // namespace bitnet

@@ -60,12 +60,12 @@ def test_size_queries(L):
     assert L.bitnet_ternarize_workspace_bytes(6912, 2560) >= 8 * 256
     # whole output tiles need no workspace; split tiles need tagged counters
     # (16 bytes per tile, rounded to 256) and two 256 KiB partial tiles per
-    # workgroup of the 256-workgroup grid
+    # workgroup of the 256-workgroup grid; dW adds its bf16 x_hat [M][Kp]
     assert L.bitlinear_fwd_workspace_bytes(4096, 6912, 2560) == 0
     assert L.bitlinear_fwd_workspace_bytes(64, 128, 256) == 0
-    assert L.bitlinear_bwd_workspace_bytes(64, 128, 256) == 0
+    assert L.bitlinear_bwd_workspace_bytes(64, 128, 256) == 2 * 64 * 256
     tile = 64 * 256 * 16
-    assert L.bitlinear_bwd_workspace_bytes(4096, 6912, 2560) == 4352 + 2 * 256 * tile
+    assert L.bitlinear_bwd_workspace_bytes(4096, 6912, 2560) == 2 * 4096 * 2560 + 4352 + 2 * 256 * tile
     assert L.bitlinear_fwd_workspace_bytes(4096, 2560, 6912) == 2560 + 2 * 256 * tile
     assert L.bitlinear_fwd_workspace_bytes(0, 4, 4) == 0
     for code in range(7):
@@ -131,5 +131,6 @@ def test_bwd_validation(L):
     # dY is addressed with 32-bit offsets: (M + 256) * 2N bytes within 2^31
     assert L.bitlinear_bwd(A, A, A, A, A, 1 << 16, 1 << 15, 64, A, None, 0, None, 0, None) == ESHAPE
     assert L.bitlinear_bwd(A, A, A, A, A, 1 << 16, 1 << 15, 64, None, A, 0, None, 0, None) == ESHAPE
-    assert L.bitlinear_bwd(MISALIGNED, A, A, A, A, 4, 4, 4, A, A, 0, None, 0, None) == EALIGN
-    assert L.bitlinear_bwd(A, A, A, A, A, 4, 4, 4, MISALIGNED, None, 0, None, 0, None) == EALIGN
+    ws = L.bitlinear_bwd_workspace_bytes(4, 4, 4)  # dW's x_hat
+    assert L.bitlinear_bwd(MISALIGNED, A, A, A, A, 4, 4, 4, A, A, 0, A, ws, None) == EALIGN
+    assert L.bitlinear_bwd(A, A, A, A, A, 4, 4, 4, MISALIGNED, None, 0, A, ws, None) == EALIGN
