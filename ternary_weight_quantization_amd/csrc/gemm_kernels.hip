@@ -111,13 +111,16 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
 // Fragment readers: the kFI (or kFJ) fragments of a wave for each k-step.
-// A k-step is 16 MFMA slots (see gemm_kstep); start<KS>() runs before its
-// first slot, slot<KS, U>() runs after the MFMA of slot U and issues this
-// reader's share of the work for later slots: the LDS reads of the next
-// k-step's fragments and, for code operands, the expansion of fragment
-// f + 1 during the slots of fragment f (and of the next k-step's fragment 0
-// during the last four). frag<KS>(f) is fragment f of k-step KS, ready by
-// the first slot that uses it. init() points the reader at a stage's tile.
+// A k-step is 16 MFMA slots (see gemm_slot); slot<KS, U>() runs after the
+// MFMA of slot U and issues this reader's share of the work for later
+// slots: the LDS reads of the next k-step's fragments and, for code
+// operands, the expansion of fragment f + 1 during the slots of fragment f
+// (and of the next k-step's fragment 0 during the last four). k-step 0 of a
+// stage is prepared during the last k-step of the previous stage, by the
+// reader of the other LDS buffer: issue() reads what k-step 0 needs (after
+// the stage's barrier), prep<U>() is the share of slot U >= 12 of the rest.
+// frag<KS>(f) is fragment f of k-step KS, ready by the first slot that uses
+// it. init() points the reader at the tile of one LDS buffer.
 // ---------------------------------------------------------------------------
 
 // 16-byte fragments read directly from a plain tile (pitch kPitch).
@@ -144,13 +147,12 @@ struct PlainFrags {
   __device__ __forceinline__ void read(int f) {
     buf[KS & 1][f] = *reinterpret_cast<const typename MT::Frag*>(base + off<KS>(f));
   }
-  template <int KS>
-  __device__ __forceinline__ void start() {
-    if constexpr (KS == 0) {
+  __device__ __forceinline__ void issue() {
 #pragma unroll
-      for (int f = 0; f < 4; ++f) read<0>(f);
-    }
+    for (int f = 0; f < 4; ++f) read<0>(f);
   }
+  template <int U>
+  __device__ __forceinline__ void prep() {}
   template <int KS, int U>
   __device__ __forceinline__ void slot() {
     if constexpr (KS + 1 < kKSteps && U % 4 == 0) read<KS + 1>(U / 4);
@@ -183,13 +185,13 @@ struct CodesI8Frags {
     const uint32_t w = KS == 0 ? raw[F].x : KS == 1 ? raw[F].y : KS == 2 ? raw[F].z : raw[F].w;
     cur[KS & 1][F][T] = (int)codes4_to_i8((w >> (2 * T)) & 0x03030303u);
   }
-  template <int KS>
-  __device__ __forceinline__ void start() {
-    if constexpr (KS == 0) {
+  __device__ __forceinline__ void issue() {
 #pragma unroll
-      for (int f = 0; f < 4; ++f) raw[f] = *reinterpret_cast<const uint4*>(base + f * 32 * kPitchB);
-      expand<0, 0, 0>(); expand<0, 0, 1>(); expand<0, 0, 2>(); expand<0, 0, 3>();
-    }
+    for (int f = 0; f < 4; ++f) raw[f] = *reinterpret_cast<const uint4*>(base + f * 32 * kPitchB);
+  }
+  template <int U>
+  __device__ __forceinline__ void prep() {
+    if constexpr (U >= 12) expand<0, 0, U - 12>();
   }
   template <int KS, int U>
   __device__ __forceinline__ void slot() {
@@ -219,13 +221,13 @@ struct CodesFp4Frags {
     const uint32_t w = KS == 0 ? raw[F].x : KS == 1 ? raw[F].y : KS == 2 ? raw[F].z : raw[F].w;
     cur[KS & 1][F][T] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, T));
   }
-  template <int KS>
-  __device__ __forceinline__ void start() {
-    if constexpr (KS == 0) {
+  __device__ __forceinline__ void issue() {
 #pragma unroll
-      for (int f = 0; f < 4; ++f) raw[f] = *reinterpret_cast<const uint4*>(base + f * 32 * kPitchB);
-      expand<0, 0, 0>(); expand<0, 0, 1>(); expand<0, 0, 2>(); expand<0, 0, 3>();
-    }
+    for (int f = 0; f < 4; ++f) raw[f] = *reinterpret_cast<const uint4*>(base + f * 32 * kPitchB);
+  }
+  template <int U>
+  __device__ __forceinline__ void prep() {
+    if constexpr (U >= 12) expand<0, 0, U - 12>();
   }
   template <int KS, int U>
   __device__ __forceinline__ void slot() {
@@ -311,6 +313,7 @@ struct CopyLoader {
   // 2KS, 2KS+1 of the thread's block are stored (slots 1, 3), then refilled
   // with stage s+2 (slots 9, 11).
   struct Tmp {};
+  static constexpr int kLastStoreSlot = 3;
   template <int KS, int U>
   __device__ __forceinline__ void slot(Regs& r, Tmp&, char* lds, int row0, int s2) const {
     const int tid = threadIdx.x;
@@ -360,6 +363,7 @@ struct PackedCodesLoader {
   }
   // K-steps 0 and 1 store one half of the row (slot 5) and refill it with
   // stage s+2 (slot 13).
+  static constexpr int kLastStoreSlot = -1;
   template <int KS, int U>
   __device__ __forceinline__ void slot(Regs& r, Tmp&, char* lds, int row0, int s2) const {
     if constexpr (KS < 2 && U == 5)
@@ -469,6 +473,7 @@ struct PackedCodesTLoader {
   // K-step 0 transposes (slots 2, 6, 8, 12) and writes row 0 (slots 14,
   // 15); k-steps 1..3 write one row each (slots 2, 4); k-step 1 refills the
   // registers with stage s+2 (slot 10).
+  static constexpr int kLastStoreSlot = 4;
   template <int KS, int U>
   __device__ __forceinline__ void slot(Regs& r, Tmp& t, char* lds, int row0, int s2) const {
     if constexpr (KS == 0) {
@@ -491,7 +496,7 @@ struct PackedCodesTLoader {
 // (mg = wave, nq = lane) reads 4 bf16 (columns 4nq..4nq+3) from each of the
 // rows m = 16mg..16mg+15 and writes the 16 x 4 transpose as 4 rows of 16 m
 // values.
-template <bool VEC>
+template <bool VEC, int W0>
 struct RowTransposeBf16Loader {
   static constexpr bool kSwz = true;
   static constexpr int kTileB = 256 * kPitch;
@@ -548,10 +553,12 @@ struct RowTransposeBf16Loader {
   }
 
   // Staging in the slots of k-step KS: half hh = KS/2 (m rows 8hh..8hh+7 of
-  // the thread's 16), n columns q = 2(KS&1), +1 (slots 11, 12; each uses
+  // the thread's 16), n columns q = 2(KS&1), +1 (slots W0, W0+1; each uses
   // all 8 rows); odd k-steps then refill that half's 8 rows with stage s+2
-  // (slots 13, 14).
+  // (slots W0+8, W0+9: late enough that the LDS stores have read the
+  // registers). W0 = 3 for the P operand and 5 for Q.
   struct Tmp {};
+  static constexpr int kLastStoreSlot = W0 + 1;
   __device__ __forceinline__ void write_q(const Regs& r, char* lds, int hh, int q) const {
     const int tid = threadIdx.x;
     const int nq = tid & 63, mg = tid >> 6;
@@ -568,18 +575,18 @@ struct RowTransposeBf16Loader {
   template <int KS, int U>
   __device__ __forceinline__ void slot(Regs& r, Tmp&, char* lds, int row0, int s2) const {
     constexpr int hh = KS >> 1;
-    if constexpr (U == 11 || U == 12) write_q(r, lds, hh, 2 * (KS & 1) + (U == 12));
-    if constexpr ((KS & 1) && (U == 13 || U == 14)) {
+    if constexpr (U == W0 || U == W0 + 1) write_q(r, lds, hh, 2 * (KS & 1) + (U == W0 + 1));
+    if constexpr ((KS & 1) && (U == W0 + 8 || U == W0 + 9)) {
       if constexpr (VEC) {
         const int tid = threadIdx.x;
         const rsrc_t rs = make_rsrc(dy, (uint32_t)(mred * ld * 2));
         const int64_t m = (int64_t)s2 * kRed16 + 16 * (tid >> 6);
         const int64_t n = row0 + 4 * (tid & 63);
         const uint32_t off = n < rows ? (uint32_t)((m * ld + n) * 2) : kOob;
-        constexpr int e0 = 8 * hh + (U == 14 ? 4 : 0);
+        constexpr int e0 = 8 * hh + (U == W0 + 9 ? 4 : 0);
 #pragma unroll
         for (int e = e0; e < e0 + 4; ++e) r.v[e] = buf_load8(rs, off + (uint32_t)(e * ld * 2));
-      } else if constexpr (KS == kKSteps - 1 && U == 14) {
+      } else if constexpr (KS == kKSteps - 1 && U == W0 + 9) {
         load(r, row0, s2);
       }
     }
@@ -631,13 +638,27 @@ struct FwdEpilogue {
   int64_t I, J;  // N, M
   bool vec;      // N % 4 == 0
 
-  __device__ __forceinline__ void store(MfmaI8::Acc (&acc)[kFI][kFJ], int i0, int j0, int lane) const {
-    const float g = *gamma;
+  // The scales this lane's columns need, loaded before the main loop so
+  // that their latency is hidden (raw values; combined in store()).
+  struct Pre { float g; float sj[kFJ]; };
+  __device__ __forceinline__ Pre prefetch(int j0, int lane) const {
+    Pre pre;
+    pre.g = *gamma;
+#pragma unroll
+    for (int fj = 0; fj < kFJ; ++fj) {
+      const int64_t j = j0 + 32 * fj + (lane & 31);
+      pre.sj[fj] = j < J ? s[j] : 0.0f;
+    }
+    return pre;
+  }
+  __device__ __forceinline__ void store(MfmaI8::Acc (&acc)[kFI][kFJ], const Pre& pre, int i0, int j0,
+                                        int lane) const {
+    const float g = pre.g;
 #pragma unroll
     for (int fj = 0; fj < kFJ; ++fj) {
       const int64_t j = j0 + 32 * fj + (lane & 31);
       if (j >= J) continue;
-      const float c = s[j] * g / 127.0f;
+      const float c = pre.sj[fj] * g / 127.0f;
 #pragma unroll
       for (int fi = 0; fi < kFI; ++fi) {
 #pragma unroll
@@ -675,9 +696,12 @@ struct Bf16Epilogue {
   int64_t I, J;        // output [J][I]
   bool vec;            // I % 4 == 0
 
-  __device__ __forceinline__ void store(MfmaBf16::Acc (&acc)[kFI][kFJ], int i0, int j0, int lane) const {
+  struct Pre { float g; };
+  __device__ __forceinline__ Pre prefetch(int, int) const { return Pre{gamma ? *gamma : 1.0f}; }
+  __device__ __forceinline__ void store(MfmaBf16::Acc (&acc)[kFI][kFJ], const Pre& pre, int i0, int j0,
+                                        int lane) const {
     float sc = 1.0f;
-    if (gamma) sc = bf16_to_f32(f32_to_bf16_bits(*gamma));  // bf16(gamma), exact in fp32
+    if (gamma) sc = bf16_to_f32(f32_to_bf16_bits(pre.g));  // bf16(gamma), exact in fp32
 #pragma unroll
     for (int fj = 0; fj < kFJ; ++fj) {
       const int64_t j = j0 + 32 * fj + (lane & 31);
@@ -807,69 +831,76 @@ __device__ __forceinline__ void zero_acc(Acc& a) {
   for (int e = 0; e < 16; ++e) a[e] = 0;
 }
 
+// The end-of-stage barrier sits in slot kBarrierSlot of the last k-step:
+// by then every LDS store of the staged next stage has been issued (each
+// loader's kLastStoreSlot is earlier) and the last k-step reads no LDS, so
+// the next stage's k-step 0 reads can start right after it and overlap the
+// remaining MFMAs of this stage.
+constexpr int kBarrierSlot = 8;
+
 // One MFMA slot of a k-step: MFMA (U / 4, U % 4), then each reader's and
 // loader's share of the work for U (issued behind the MFMA so that it
 // overlaps its 32 cycles), fenced from the next slot so that the compiler
-// keeps this interleave.
+// keeps this interleave. fpn/fqn read the other LDS buffer (the next
+// stage); `more` says whether there is a next stage.
 template <int KS, int U, class MT, class PL, class QL, class FP, class FQ>
 __device__ __forceinline__ void gemm_slot(const PL& pl, const QL& ql, typename PL::Regs& pr,
                                           typename QL::Regs& qr, typename PL::Tmp& pt,
-                                          typename QL::Tmp& qt, FP& fp, FQ& fq, char* Pn, char* Qn,
-                                          typename MT::Acc (&acc)[kFI][kFJ], int i0, int j0, int s2) {
+                                          typename QL::Tmp& qt, FP& fp, FQ& fq, FP& fpn, FQ& fqn,
+                                          char* Pn, char* Qn, typename MT::Acc (&acc)[kFI][kFJ],
+                                          int i0, int j0, int s2, bool more) {
   acc[U / 4][U % 4] = MT::mma(fp.template frag<KS>(U / 4), fq.template frag<KS>(U % 4), acc[U / 4][U % 4]);
   fp.template slot<KS, U>();
   fq.template slot<KS, U>();
   pl.template slot<KS, U>(pr, pt, Pn, i0, s2);
   ql.template slot<KS, U>(qr, qt, Qn, j0, s2);
+  if constexpr (KS == kKSteps - 1) {
+    if constexpr (U == kBarrierSlot) __syncthreads();
+    if constexpr (U == kBarrierSlot + 1) {
+      if (more) {
+        fpn.issue();
+        fqn.issue();
+      }
+    }
+    if constexpr (U >= 12) {
+      if (more) {
+        fpn.template prep<U>();
+        fqn.template prep<U>();
+      }
+    }
+  }
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (U + 1 < kFI * kFJ)
-    gemm_slot<KS, U + 1, MT>(pl, ql, pr, qr, pt, qt, fp, fq, Pn, Qn, acc, i0, j0, s2);
+    gemm_slot<KS, U + 1, MT>(pl, ql, pr, qr, pt, qt, fp, fq, fpn, fqn, Pn, Qn, acc, i0, j0, s2, more);
 }
 
-template <int KS, class MT, class PL, class QL, class FP, class FQ>
-__device__ __forceinline__ void gemm_kstep(const PL& pl, const QL& ql, typename PL::Regs& pr,
-                                           typename QL::Regs& qr, typename PL::Tmp& pt,
-                                           typename QL::Tmp& qt, FP& fp, FQ& fq, char* Pn, char* Qn,
-                                            typename MT::Acc (&acc)[kFI][kFJ], int i0, int j0, int s2) {
-  fp.template start<KS>();
-  fq.template start<KS>();
-  __builtin_amdgcn_sched_barrier(0);
-  gemm_slot<KS, 0, MT>(pl, ql, pr, qr, pt, qt, fp, fq, Pn, Qn, acc, i0, j0, s2);
-}
-
-// LDS: two stages, each a P tile followed by a Q tile; then the per-stage
-// scales of loaders that publish them.
+// LDS: two stages, each a P tile followed by a Q tile.
 template <class PL, class QL>
 struct SmemLayout {
   static constexpr int kStage = PL::kTileB + QL::kTileB;
   static constexpr int kBytes = 2 * kStage;
 };
 
-// One pipeline stage: MFMAs on LDS buffer CUR for reduction stage s, while
-// staging stage s+1 from registers into buffer CUR^1 and fetching stage s+2
-// into those registers, one quarter per k-step. Past the last stage the
-// staging runs on zeros and is never read.
-template <int CUR, class MT, int MAP, class PL, class QL>
+// One pipeline stage: MFMAs on LDS buffer CUR (readers fp, fq) for
+// reduction stage s, while staging stage s+1 from registers into buffer
+// CUR^1 and fetching stage s+2 into those registers, one quarter per
+// k-step, and, when `more`, preparing k-step 0 of stage s+1 (readers fpn,
+// fqn of buffer CUR^1). Past the last stage the staging runs on zeros and
+// is never read.
+template <int CUR, class MT, class PL, class QL, class FP, class FQ>
 __device__ __forceinline__ void gemm_stage(const PL& pl, const QL& ql, typename PL::Regs& pr,
-                                           typename QL::Regs& qr, char* smem,
-                                           typename MT::Acc (&acc)[kFI][kFJ], int i0, int j0, int s,
-                                           int prow0, int qrow0, int lane) {
+                                           typename QL::Regs& qr, char* smem, FP& fp, FQ& fq,
+                                           FP& fpn, FQ& fqn, typename MT::Acc (&acc)[kFI][kFJ],
+                                           int i0, int j0, int s, bool more) {
   typedef SmemLayout<PL, QL> L;
-  char* cur = smem + CUR * L::kStage;
-  char* nxt = smem + (CUR ^ 1) * L::kStage;
-  typename PL::template Frags<MT, MAP> fp;
-  typename QL::template Frags<MT, MAP> fq;
-  fp.init(cur, prow0, lane);
-  fq.init(cur + PL::kTileB, qrow0, lane);
+  char* Pn = smem + (CUR ^ 1) * L::kStage;
+  char* Qn = Pn + PL::kTileB;
   typename PL::Tmp pt;
   typename QL::Tmp qt;
-  char* Pn = nxt;
-  char* Qn = nxt + PL::kTileB;
-  gemm_kstep<0, MT>(pl, ql, pr, qr, pt, qt, fp, fq, Pn, Qn, acc, i0, j0, s + 2);
-  gemm_kstep<1, MT>(pl, ql, pr, qr, pt, qt, fp, fq, Pn, Qn, acc, i0, j0, s + 2);
-  gemm_kstep<2, MT>(pl, ql, pr, qr, pt, qt, fp, fq, Pn, Qn, acc, i0, j0, s + 2);
-  gemm_kstep<3, MT>(pl, ql, pr, qr, pt, qt, fp, fq, Pn, Qn, acc, i0, j0, s + 2);
-  __syncthreads();
+  gemm_slot<0, 0, MT>(pl, ql, pr, qr, pt, qt, fp, fq, fpn, fqn, Pn, Qn, acc, i0, j0, s + 2, more);
+  gemm_slot<1, 0, MT>(pl, ql, pr, qr, pt, qt, fp, fq, fpn, fqn, Pn, Qn, acc, i0, j0, s + 2, more);
+  gemm_slot<2, 0, MT>(pl, ql, pr, qr, pt, qt, fp, fq, fpn, fqn, Pn, Qn, acc, i0, j0, s + 2, more);
+  gemm_slot<3, 0, MT>(pl, ql, pr, qr, pt, qt, fp, fq, fpn, fqn, Pn, Qn, acc, i0, j0, s + 2, more);
 }
 
 // The stages [s0, s1) of tile (i0, j0), accumulated into acc. LDS is free
@@ -878,6 +909,9 @@ template <class MT, int MAP, class PL, class QL>
 __device__ __forceinline__ void run_stages(const PL& pl, const QL& ql, char* smem,
                                            typename MT::Acc (&acc)[kFI][kFJ], int i0, int j0, int s0,
                                            int s1, int prow0, int qrow0, int lane) {
+  static_assert(PL::kLastStoreSlot < kBarrierSlot && QL::kLastStoreSlot < kBarrierSlot,
+                "staging stores must precede the end-of-stage barrier");
+  typedef SmemLayout<PL, QL> L;
   typename PL::Regs pr;
   typename QL::Regs qr;
   pl.load(pr, i0, s0);
@@ -888,12 +922,23 @@ __device__ __forceinline__ void run_stages(const PL& pl, const QL& ql, char* sme
   pl.load(pr, i0, s0 + 1);
   ql.load(qr, j0, s0 + 1);
   __syncthreads();
+  typename PL::template Frags<MT, MAP> fp0, fp1;
+  typename QL::template Frags<MT, MAP> fq0, fq1;
+  fp0.init(smem, prow0, lane);
+  fq0.init(smem + PL::kTileB, qrow0, lane);
+  fp1.init(smem + L::kStage, prow0, lane);
+  fq1.init(smem + L::kStage + PL::kTileB, qrow0, lane);
+  fp0.issue();
+  fq0.issue();
+  fp0.template prep<12>(); fp0.template prep<13>(); fp0.template prep<14>(); fp0.template prep<15>();
+  fq0.template prep<12>(); fq0.template prep<13>(); fq0.template prep<14>(); fq0.template prep<15>();
+  __builtin_amdgcn_sched_barrier(0);
   int s = s0;
   for (; s + 1 < s1; s += 2) {
-    gemm_stage<0, MT, MAP>(pl, ql, pr, qr, smem, acc, i0, j0, s, prow0, qrow0, lane);
-    gemm_stage<1, MT, MAP>(pl, ql, pr, qr, smem, acc, i0, j0, s + 1, prow0, qrow0, lane);
+    gemm_stage<0, MT>(pl, ql, pr, qr, smem, fp0, fq0, fp1, fq1, acc, i0, j0, s, true);
+    gemm_stage<1, MT>(pl, ql, pr, qr, smem, fp1, fq1, fp0, fq0, acc, i0, j0, s + 1, s + 2 < s1);
   }
-  if (s < s1) gemm_stage<0, MT, MAP>(pl, ql, pr, qr, smem, acc, i0, j0, s, prow0, qrow0, lane);
+  if (s < s1) gemm_stage<0, MT>(pl, ql, pr, qr, smem, fp0, fq0, fp1, fq1, acc, i0, j0, s, false);
 }
 
 // Element e (0..3) of 16-byte chunk c (0..63) of a thread's accumulators:
@@ -1008,8 +1053,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(PL pl, QL ql, EP ep, 
     for (int fi = 0; fi < kFI; ++fi)
 #pragma unroll
       for (int fj = 0; fj < kFJ; ++fj) zero_acc(acc[fi][fj]);
+    const typename EP::Pre pre = ep.prefetch(j0 + qrow0, lane);
     run_stages<MT, MAP>(pl, ql, smem, acc, i0, j0, 0, plan.nstages, prow0, qrow0, lane);
-    ep.store(acc, i0 + prow0, j0 + qrow0, lane);
+    ep.store(acc, pre, i0 + prow0, j0 + qrow0, lane);
     return;
   }
 
@@ -1026,9 +1072,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(PL pl, QL ql, EP ep, 
 #pragma unroll
       for (int fj = 0; fj < kFJ; ++fj) zero_acc(acc[fi][fj]);
 
+    const typename EP::Pre pre = ep.prefetch(j0 + qrow0, lane);
     run_stages<MT, MAP>(pl, ql, smem, acc, i0, j0, s0, s1, prow0, qrow0, lane);
     if ((s0 == 0 && s1 == plan.nstages) || finish_piece<MT>(plan, acc, v, t, &s_flag))
-      ep.store(acc, i0 + prow0, j0 + qrow0, lane);
+      ep.store(acc, pre, i0 + prow0, j0 + qrow0, lane);
     it += s1 - s0;
   }
 }
@@ -1187,17 +1234,17 @@ hipError_t launch_bwd_dw(const uint16_t* dY, const int8_t* x_q, const float* s_x
   xhat_kernel<<<(int)(want < 4096 ? want : 4096), 256, 0, stream>>>(x_q, s_x, M, Kp, xhat);
   if (hipError_t e = hipGetLastError()) return e;
 
-  RowTransposeBf16Loader<true> pl{xhat, Kp, M, Kp};
+  RowTransposeBf16Loader<true, 3> pl{xhat, Kp, M, Kp};
   const GemmShape g = shape_of(GemmKind::kBwdDw, M, N, K);
   const bool vec = (N % 4 == 0);
   if (dw_is_f32) {
     Bf16Epilogue<true> ep{dW, nullptr, K, N, K % 4 == 0};
-    if (vec) return run_gemm<MfmaBf16, 0>(pl, RowTransposeBf16Loader<true>{dY, N, M, N}, ep, g, split_ws, split_bytes, stream);
-    return run_gemm<MfmaBf16, 0>(pl, RowTransposeBf16Loader<false>{dY, N, M, N}, ep, g, split_ws, split_bytes, stream);
+    if (vec) return run_gemm<MfmaBf16, 0>(pl, RowTransposeBf16Loader<true, 5>{dY, N, M, N}, ep, g, split_ws, split_bytes, stream);
+    return run_gemm<MfmaBf16, 0>(pl, RowTransposeBf16Loader<false, 5>{dY, N, M, N}, ep, g, split_ws, split_bytes, stream);
   }
   Bf16Epilogue<false> ep{dW, nullptr, K, N, K % 4 == 0};
-  if (vec) return run_gemm<MfmaBf16, 0>(pl, RowTransposeBf16Loader<true>{dY, N, M, N}, ep, g, split_ws, split_bytes, stream);
-  return run_gemm<MfmaBf16, 0>(pl, RowTransposeBf16Loader<false>{dY, N, M, N}, ep, g, split_ws, split_bytes, stream);
+  if (vec) return run_gemm<MfmaBf16, 0>(pl, RowTransposeBf16Loader<true, 5>{dY, N, M, N}, ep, g, split_ws, split_bytes, stream);
+  return run_gemm<MfmaBf16, 0>(pl, RowTransposeBf16Loader<false, 5>{dY, N, M, N}, ep, g, split_ws, split_bytes, stream);
 }
 
 }  // namespace bitnet
