@@ -117,11 +117,19 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 // operands, the expansion of fragment f + 1 during the slots of fragment f
 // (and of the next k-step's fragment 0 during the last four). k-step 0 of a
 // stage is prepared during the last k-step of the previous stage, by the
-// reader of the other LDS buffer: issue() reads what k-step 0 needs (after
-// the stage's barrier), prep<U>() is the share of slot U >= 12 of the rest.
+// reader of the other LDS buffer: ahead<U>() is the share of slot U (after
+// the stage's barrier) of the LDS reads and expansion k-step 0 needs.
 // frag<KS>(f) is fragment f of k-step KS, ready by the first slot that uses
 // it. init() points the reader at the tile of one LDS buffer.
 // ---------------------------------------------------------------------------
+
+// The end-of-stage barrier sits in slot kBarrierSlot of the last k-step:
+// by then every LDS store of the staged next stage has been issued (each
+// loader's kLastStoreSlot is earlier) and the last k-step reads no LDS, so
+// the next stage's k-step 0 reads can start right after it and overlap the
+// remaining MFMAs of this stage.
+constexpr int kBarrierSlot = 8;
+static_assert(kBarrierSlot + 7 == 15, "ahead<U> covers the slots after the barrier");
 
 // 16-byte fragments read directly from a plain tile (pitch kPitch).
 template <class MT, bool SWZ, int MAP>
@@ -147,12 +155,10 @@ struct PlainFrags {
   __device__ __forceinline__ void read(int f) {
     buf[KS & 1][f] = *reinterpret_cast<const typename MT::Frag*>(base + off<KS>(f));
   }
-  __device__ __forceinline__ void issue() {
-#pragma unroll
-    for (int f = 0; f < 4; ++f) read<0>(f);
-  }
   template <int U>
-  __device__ __forceinline__ void prep() {}
+  __device__ __forceinline__ void ahead() {
+    if constexpr (U >= kBarrierSlot + 1 && U < kBarrierSlot + 5) read<0>(U - kBarrierSlot - 1);
+  }
   template <int KS, int U>
   __device__ __forceinline__ void slot() {
     if constexpr (KS + 1 < kKSteps && U % 4 == 0) read<KS + 1>(U / 4);
@@ -185,12 +191,14 @@ struct CodesI8Frags {
     const uint32_t w = KS == 0 ? raw[F].x : KS == 1 ? raw[F].y : KS == 2 ? raw[F].z : raw[F].w;
     cur[KS & 1][F][T] = (int)codes4_to_i8((w >> (2 * T)) & 0x03030303u);
   }
-  __device__ __forceinline__ void issue() {
-#pragma unroll
-    for (int f = 0; f < 4; ++f) raw[f] = *reinterpret_cast<const uint4*>(base + f * 32 * kPitchB);
-  }
   template <int U>
-  __device__ __forceinline__ void prep() {
+  __device__ __forceinline__ void ahead() {
+    static_assert(kBarrierSlot + 2 < 12, "raw words must be read before slot 12");
+    if constexpr (U == kBarrierSlot + 1 || U == kBarrierSlot + 2) {
+      constexpr int f0 = 2 * (U - kBarrierSlot - 1);
+      raw[f0] = *reinterpret_cast<const uint4*>(base + f0 * 32 * kPitchB);
+      raw[f0 + 1] = *reinterpret_cast<const uint4*>(base + (f0 + 1) * 32 * kPitchB);
+    }
     if constexpr (U >= 12) expand<0, 0, U - 12>();
   }
   template <int KS, int U>
@@ -221,12 +229,14 @@ struct CodesFp4Frags {
     const uint32_t w = KS == 0 ? raw[F].x : KS == 1 ? raw[F].y : KS == 2 ? raw[F].z : raw[F].w;
     cur[KS & 1][F][T] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, T));
   }
-  __device__ __forceinline__ void issue() {
-#pragma unroll
-    for (int f = 0; f < 4; ++f) raw[f] = *reinterpret_cast<const uint4*>(base + f * 32 * kPitchB);
-  }
   template <int U>
-  __device__ __forceinline__ void prep() {
+  __device__ __forceinline__ void ahead() {
+    static_assert(kBarrierSlot + 2 < 12, "raw words must be read before slot 12");
+    if constexpr (U == kBarrierSlot + 1 || U == kBarrierSlot + 2) {
+      constexpr int f0 = 2 * (U - kBarrierSlot - 1);
+      raw[f0] = *reinterpret_cast<const uint4*>(base + f0 * 32 * kPitchB);
+      raw[f0 + 1] = *reinterpret_cast<const uint4*>(base + (f0 + 1) * 32 * kPitchB);
+    }
     if constexpr (U >= 12) expand<0, 0, U - 12>();
   }
   template <int KS, int U>
@@ -506,17 +516,24 @@ struct RowTransposeBf16Loader {
   int64_t ld;    // elements per source row (N, or Kp for x_hat)
   int64_t mred;  // M (valid reduction rows)
   int64_t rows;  // valid operand rows (N, or Kp)
-  struct Regs { uint2 v[16]; };
+  // lane_off: byte offset of the thread's first element in stage 0, or an
+  // out-of-range offset for columns past the operand (adding a stage's
+  // offset, below 2^31, keeps it out of range)
+  struct Regs { uint2 v[16]; uint32_t lane_off; };
 
+  // Byte offset of row e of the thread's 16 in stage s (uniform part).
+  __device__ __forceinline__ uint32_t stage_off(int s, int e) const {
+    return (uint32_t)(((int64_t)s * kRed16 + e) * ld * 2);
+  }
   __device__ __forceinline__ void load(Regs& r, int row0, int s) const {
     const int tid = threadIdx.x;
     const int64_t m = (int64_t)s * kRed16 + 16 * (tid >> 6);
     const int64_t n = row0 + 4 * (tid & 63);
     if constexpr (VEC) {
       const rsrc_t rs = make_rsrc(dy, (uint32_t)(mred * ld * 2));
-      const uint32_t off = n < rows ? (uint32_t)((m * ld + n) * 2) : kOob;
+      r.lane_off = n < rows ? (uint32_t)((16 * (tid >> 6) * ld + n) * 2) : kOob;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) r.v[e] = buf_load8(rs, off + (uint32_t)(e * ld * 2));
+      for (int e = 0; e < 16; ++e) r.v[e] = buf_load8(rs, r.lane_off + stage_off(s, e));
     } else {
       const uint16_t* p = dy + m * ld + n;
 #pragma unroll
@@ -554,9 +571,10 @@ struct RowTransposeBf16Loader {
 
   // Staging in the slots of k-step KS: half hh = KS/2 (m rows 8hh..8hh+7 of
   // the thread's 16), n columns q = 2(KS&1), +1 (slots W0, W0+1; each uses
-  // all 8 rows); odd k-steps then refill that half's 8 rows with stage s+2
-  // (slots W0+8, W0+9: late enough that the LDS stores have read the
-  // registers). W0 = 3 for the P operand and 5 for Q.
+  // all 8 rows); odd k-steps then refill that half's 8 rows with stage s+2,
+  // one row per slot (slots W0+2 .. W0+9) so that the loads of the two
+  // operands do not arrive at the memory pipeline in bursts. W0 = 3 for the
+  // P operand and 5 for Q.
   struct Tmp {};
   static constexpr int kLastStoreSlot = W0 + 1;
   __device__ __forceinline__ void write_q(const Regs& r, char* lds, int hh, int q) const {
@@ -576,16 +594,11 @@ struct RowTransposeBf16Loader {
   __device__ __forceinline__ void slot(Regs& r, Tmp&, char* lds, int row0, int s2) const {
     constexpr int hh = KS >> 1;
     if constexpr (U == W0 || U == W0 + 1) write_q(r, lds, hh, 2 * (KS & 1) + (U == W0 + 1));
-    if constexpr ((KS & 1) && (U == W0 + 8 || U == W0 + 9)) {
+    if constexpr ((KS & 1) && U >= W0 + 2 && U < W0 + 10) {
       if constexpr (VEC) {
-        const int tid = threadIdx.x;
         const rsrc_t rs = make_rsrc(dy, (uint32_t)(mred * ld * 2));
-        const int64_t m = (int64_t)s2 * kRed16 + 16 * (tid >> 6);
-        const int64_t n = row0 + 4 * (tid & 63);
-        const uint32_t off = n < rows ? (uint32_t)((m * ld + n) * 2) : kOob;
-        constexpr int e0 = 8 * hh + (U == W0 + 9 ? 4 : 0);
-#pragma unroll
-        for (int e = e0; e < e0 + 4; ++e) r.v[e] = buf_load8(rs, off + (uint32_t)(e * ld * 2));
+        constexpr int e = 8 * hh + (U - W0 - 2);
+        r.v[e] = buf_load8(rs, r.lane_off + stage_off(s2, e));
       } else if constexpr (KS == kKSteps - 1 && U == W0 + 9) {
         load(r, row0, s2);
       }
@@ -831,12 +844,14 @@ __device__ __forceinline__ void zero_acc(Acc& a) {
   for (int e = 0; e < 16; ++e) a[e] = 0;
 }
 
-// The end-of-stage barrier sits in slot kBarrierSlot of the last k-step:
-// by then every LDS store of the staged next stage has been issued (each
-// loader's kLastStoreSlot is earlier) and the last k-step reads no LDS, so
-// the next stage's k-step 0 reads can start right after it and overlap the
-// remaining MFMAs of this stage.
-constexpr int kBarrierSlot = 8;
+// All of ahead<U>() of a reader at once (the first stage of a run).
+template <class F>
+__device__ __forceinline__ void prime(F& f) {
+  f.template ahead<kBarrierSlot + 1>(); f.template ahead<kBarrierSlot + 2>();
+  f.template ahead<kBarrierSlot + 3>(); f.template ahead<kBarrierSlot + 4>();
+  f.template ahead<kBarrierSlot + 5>(); f.template ahead<kBarrierSlot + 6>();
+  f.template ahead<kBarrierSlot + 7>();
+}
 
 // One MFMA slot of a k-step: MFMA (U / 4, U % 4), then each reader's and
 // loader's share of the work for U (issued behind the MFMA so that it
@@ -856,16 +871,10 @@ __device__ __forceinline__ void gemm_slot(const PL& pl, const QL& ql, typename P
   ql.template slot<KS, U>(qr, qt, Qn, j0, s2);
   if constexpr (KS == kKSteps - 1) {
     if constexpr (U == kBarrierSlot) __syncthreads();
-    if constexpr (U == kBarrierSlot + 1) {
+    if constexpr (U > kBarrierSlot) {
       if (more) {
-        fpn.issue();
-        fqn.issue();
-      }
-    }
-    if constexpr (U >= 12) {
-      if (more) {
-        fpn.template prep<U>();
-        fqn.template prep<U>();
+        fpn.template ahead<U>();
+        fqn.template ahead<U>();
       }
     }
   }
@@ -928,10 +937,8 @@ __device__ __forceinline__ void run_stages(const PL& pl, const QL& ql, char* sme
   fq0.init(smem + PL::kTileB, qrow0, lane);
   fp1.init(smem + L::kStage, prow0, lane);
   fq1.init(smem + L::kStage + PL::kTileB, qrow0, lane);
-  fp0.issue();
-  fq0.issue();
-  fp0.template prep<12>(); fp0.template prep<13>(); fp0.template prep<14>(); fp0.template prep<15>();
-  fq0.template prep<12>(); fq0.template prep<13>(); fq0.template prep<14>(); fq0.template prep<15>();
+  prime(fp0);
+  prime(fq0);
   __builtin_amdgcn_sched_barrier(0);
   int s = s0;
   for (; s + 1 < s1; s += 2) {
