@@ -32,7 +32,8 @@
  *    w_packed and dY satisfies (rows + 256) * row_bytes <= 2^31, i.e.
  *    (M + 256) * Kp, (N + 256) * Kp/4 and (M + 256) * 2N bytes, and with dW
  *    also (M + 256) * 2Kp for its bf16 x_hat (the kernels address them with
- *    32-bit offsets).
+ *    32-bit offsets); the forward also needs N <= 2^24 (its epilogue
+ *    addresses 32 output rows of up to 4-byte elements the same way).
  */
 #ifndef BITNET_H
 #define BITNET_H

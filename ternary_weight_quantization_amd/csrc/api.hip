@@ -38,8 +38,13 @@ bool buffer_range_ok(int64_t rows, int64_t pitch_bytes) {
   return (rows + 256) * pitch_bytes <= (int64_t(1) << 31);
 }
 
-bitnet_status check_gemm_ranges(int64_t M, int64_t N, int64_t K, bool need_xq, bool need_w, bool need_dy) {
+// out_elems: elements per output row (N for the forward, K for dX and dW).
+// The epilogue addresses 32 output rows of up to 4-byte elements with 32-bit
+// offsets.
+bitnet_status check_gemm_ranges(int64_t M, int64_t N, int64_t K, bool need_xq, bool need_w, bool need_dy,
+                                int64_t out_elems) {
   const int64_t Kp = bitnet::k_pad(K);
+  if (32 * 4 * out_elems > (int64_t(1) << 31)) return BITNET_ERR_SHAPE;
   if (need_xq && !buffer_range_ok(M, Kp)) return BITNET_ERR_SHAPE;
   if (need_xq && !buffer_range_ok(M, 2 * Kp)) return BITNET_ERR_SHAPE;  // dW's bf16 x_hat
   if (need_w && !buffer_range_ok(N, Kp / 4)) return BITNET_ERR_SHAPE;
@@ -111,7 +116,7 @@ bitnet_status bitlinear_fwd(const int8_t* x_q, const float* s_x, const uint8_t* 
                             int32_t* acc_out, void* workspace, size_t workspace_bytes, void* stream) {
   if (!x_q || !s_x || !w_packed || !gamma || !y) return BITNET_ERR_NULL;
   if (bitnet_status st = check_gemm_sizes(M, N, K)) return st;
-  if (bitnet_status st = check_gemm_ranges(M, N, K, true, true, false)) return st;
+  if (bitnet_status st = check_gemm_ranges(M, N, K, true, true, false, N)) return st;
   if (workspace_bytes < bitlinear_fwd_workspace_bytes(M, N, K)) return BITNET_ERR_WORKSPACE;
   if (workspace_bytes > 0 && !workspace) return BITNET_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return BITNET_ERR_ALIGN;
@@ -132,7 +137,7 @@ bitnet_status bitlinear_bwd(const uint16_t* dY, const int8_t* x_q, const float* 
   if (dW && (!x_q || !s_x)) return BITNET_ERR_NULL;
   if (dW && dW_dtype != BITNET_BF16 && dW_dtype != BITNET_F32) return BITNET_ERR_DTYPE;
   if (bitnet_status st = check_gemm_sizes(M, N, K)) return st;
-  if (bitnet_status st = check_gemm_ranges(M, N, K, dW != nullptr, dX != nullptr, true)) return st;
+  if (bitnet_status st = check_gemm_ranges(M, N, K, dW != nullptr, dX != nullptr, true, K)) return st;
   if (workspace_bytes < bitlinear_bwd_workspace_bytes(M, N, K)) return BITNET_ERR_WORKSPACE;
   if (workspace_bytes > 0 && !workspace) return BITNET_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return BITNET_ERR_ALIGN;

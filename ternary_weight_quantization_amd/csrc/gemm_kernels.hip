@@ -641,15 +641,91 @@ __global__ __launch_bounds__(256) void xhat_kernel(const int8_t* __restrict__ xq
 // Epilogues: acc (wave tile origin i0, j0) -> memory. Lane l holds, for each
 // fragment (fi, fj) and group g, the 4 consecutive i = i0 + 32fi + 8g +
 // 4(l/32) + 0..3 at j = j0 + 32fj + l%32.
+//
+// Stored from the accumulator layout, one instruction would write 16-byte
+// pieces of 32 output rows, which runs at about half the HBM write rate of
+// whole-row stores. The block goes through LDS instead (EpStage): in four
+// passes of 32 rows j (one fragment column fj), each lane puts its 4-value
+// pieces into a per-wave LDS buffer of 32 rows, and every store instruction
+// then writes whole 128-value row segments (4 rows of bf16 or 2 of 32-bit
+// values). LDS rows are padded by 16 bytes: the 16 rows a half-wave puts to
+// start 4 banks apart, and a row read by 16 or 32 lanes covers every bank
+// once; all LDS offsets are a per-lane base plus a constant. LDS is free
+// when the epilogue runs: the last stage's reads and staging stores all
+// precede its barrier.
 // ---------------------------------------------------------------------------
+
+template <int EB>  // bytes per output element: 2 (bf16) or 4 (f32, int32)
+struct EpStage {
+  static constexpr int kRowB = 128 * EB;
+  static constexpr int kPitch = kRowB + 16;
+  static constexpr int kChunks = kRowB / 16;
+  static constexpr int kWaveBytes = 32 * kPitch;
+  static constexpr int kRowsPerGet = 1024 / kRowB;  // rows per wave instruction
+  static constexpr int kGets = 32 / kRowsPerGet;
+  // The lane's piece of (fi, g): 4 values of row l%32 at i = 32fi + 8g + 4(l/32).
+  template <class V>
+  static __device__ __forceinline__ void put(char* w, int lane, int fi, int g, V v) {
+    char* base = w + (lane & 31) * kPitch + 4 * EB * (lane >> 5);
+    *reinterpret_cast<V*>(base + (32 * fi + 8 * g) * EB) = v;
+  }
+  // Row-wise read-out of the 32 rows into out[j][i] (rows of I elements):
+  // get k is the 16 bytes of row k * kRowsPerGet + lane / kChunks, chunk
+  // lane % kChunks, i.e. out[j0 + row][i0 + chunk * 16 / EB ..]. All gets
+  // are issued first. When I is a multiple of 16 / EB (a chunk then lies
+  // all inside or all outside a row), each get is one 16-byte store through
+  // a buffer resource based at the pass's first row, with the row offset as
+  // the uniform soffset and an out-of-range voffset for rows at or past J
+  // and chunks at or past I (32 * I * EB < 2^31, checked by the C ABI);
+  // otherwise rows are not 16-byte aligned and the valid elements are
+  // stored one by one. i0, j0 are uniform in the wave.
+  static __device__ __forceinline__ void drain(const char* w, char* out, int64_t I, int64_t J, int i0, int j0,
+                                               int lane) {
+    i0 = __builtin_amdgcn_readfirstlane(i0);
+    j0 = __builtin_amdgcn_readfirstlane(j0);
+    int c = lane % kChunks, rl = lane / kChunks;
+    // opaque to the optimizer: keeps the per-get row terms from being
+    // computed once per kernel and spilled across the main loop
+    asm volatile("" : "+v"(c), "+v"(rl));
+    const char* src = w + rl * kPitch + 16 * c;
+    uint4 v[kGets];
+#pragma unroll
+    for (int k = 0; k < kGets; ++k) v[k] = *reinterpret_cast<const uint4*>(src + k * kRowsPerGet * kPitch);
+    const int rows_in = J - j0 < 32 ? (int)(J - j0) : 32;
+    if ((I & (16 / EB - 1)) == 0) {
+      const uint32_t row_b = (uint32_t)I * EB;
+      const rsrc_t rs = make_rsrc(out + ((int64_t)j0 * I + i0) * EB, 32u * row_b);
+      const uint32_t lane_off = i0 + c * (16 / EB) < I ? rl * row_b + 16 * c : kOob;
+#pragma unroll
+      for (int k = 0; k < kGets; ++k)
+        buf_store16(rs, rl < rows_in - k * kRowsPerGet ? lane_off : kOob, (uint32_t)(k * kRowsPerGet) * row_b,
+                    v[k]);
+    } else {
+      const int64_t i = i0 + c * (16 / EB);
+#pragma unroll
+      for (int k = 0; k < kGets; ++k) {
+        if (k * kRowsPerGet + rl >= rows_in) continue;
+        char* row = out + (int64_t)(j0 + k * kRowsPerGet + rl) * I * EB;
+        const uint32_t wv[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+        for (int e = 0; e < 16 / EB; ++e) {
+          if (i + e >= I) continue;
+          if constexpr (EB == 2)
+            reinterpret_cast<uint16_t*>(row)[i + e] = (uint16_t)(wv[e >> 1] >> (16 * (e & 1)));
+          else
+            reinterpret_cast<uint32_t*>(row)[i + e] = wv[e];
+        }
+      }
+    }
+  }
+};
 
 struct FwdEpilogue {
   uint16_t* y;
-  int32_t* acc_out;
+  int32_t* acc_out;  // NULL: not written
   const float* s;
   const float* gamma;
   int64_t I, J;  // N, M
-  bool vec;      // N % 4 == 0
 
   // The scales this lane's columns need, loaded before the main loop so
   // that their latency is hidden (raw values; combined in store()).
@@ -664,38 +740,30 @@ struct FwdEpilogue {
     }
     return pre;
   }
+  static constexpr int kWaveLds = EpStage<4>::kWaveBytes;  // the int32 pass needs the larger buffer
   __device__ __forceinline__ void store(MfmaI8::Acc (&acc)[kFI][kFJ], const Pre& pre, int i0, int j0,
-                                        int lane) const {
+                                        int lane, char* wlds) const {
     const float g = pre.g;
 #pragma unroll
     for (int fj = 0; fj < kFJ; ++fj) {
-      const int64_t j = j0 + 32 * fj + (lane & 31);
-      if (j >= J) continue;
       const float c = pre.sj[fj] * g / 127.0f;
 #pragma unroll
-      for (int fi = 0; fi < kFI; ++fi) {
+      for (int fi = 0; fi < kFI; ++fi)
 #pragma unroll
-        for (int gi = 0; gi < 4; ++gi) {
-          const int64_t i = i0 + 32 * fi + 8 * gi + 4 * (lane >> 5);
-          if (i >= I) continue;
-          const int a0 = acc[fi][fj][4 * gi + 0], a1 = acc[fi][fj][4 * gi + 1];
-          const int a2 = acc[fi][fj][4 * gi + 2], a3 = acc[fi][fj][4 * gi + 3];
-          const float v0 = (float)a0 * c, v1 = (float)a1 * c, v2 = (float)a2 * c, v3 = (float)a3 * c;
-          uint16_t* dst = y + j * I + i;
-          if (vec && i + 4 <= I) {
-            *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
-            if (acc_out) *reinterpret_cast<int4*>(acc_out + j * I + i) = make_int4(a0, a1, a2, a3);
-          } else {
-            const float vv[4] = {v0, v1, v2, v3};
-            const int aa[4] = {a0, a1, a2, a3};
+        for (int gi = 0; gi < 4; ++gi)
+          EpStage<2>::put(wlds, lane, fi, gi,
+                          make_uint2(pack_bf16x2((float)acc[fi][fj][4 * gi] * c, (float)acc[fi][fj][4 * gi + 1] * c),
+                                     pack_bf16x2((float)acc[fi][fj][4 * gi + 2] * c, (float)acc[fi][fj][4 * gi + 3] * c)));
+      EpStage<2>::drain(wlds, reinterpret_cast<char*>(y), I, J, i0, j0 + 32 * fj, lane);
+      if (acc_out != nullptr) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-              if (i + q < I) {
-                dst[q] = f32_to_bf16_bits(vv[q]);
-                if (acc_out) acc_out[j * I + i + q] = aa[q];
-              }
-          }
-        }
+        for (int fi = 0; fi < kFI; ++fi)
+#pragma unroll
+          for (int gi = 0; gi < 4; ++gi)
+            EpStage<4>::put(wlds, lane, fi, gi,
+                            make_uint4((uint32_t)acc[fi][fj][4 * gi], (uint32_t)acc[fi][fj][4 * gi + 1],
+                                       (uint32_t)acc[fi][fj][4 * gi + 2], (uint32_t)acc[fi][fj][4 * gi + 3]));
+        EpStage<4>::drain(wlds, reinterpret_cast<char*>(acc_out), I, J, i0, j0 + 32 * fj, lane);
       }
     }
   }
@@ -707,48 +775,30 @@ struct Bf16Epilogue {
   void* out;
   const float* gamma;  // NULL: no scale
   int64_t I, J;        // output [J][I]
-  bool vec;            // I % 4 == 0
 
   struct Pre { float g; };
+  static constexpr int kEB = OUT_F32 ? 4 : 2;
+  static constexpr int kWaveLds = EpStage<kEB>::kWaveBytes;
   __device__ __forceinline__ Pre prefetch(int, int) const { return Pre{gamma ? *gamma : 1.0f}; }
   __device__ __forceinline__ void store(MfmaBf16::Acc (&acc)[kFI][kFJ], const Pre& pre, int i0, int j0,
-                                        int lane) const {
+                                        int lane, char* wlds) const {
     float sc = 1.0f;
     if (gamma) sc = bf16_to_f32(f32_to_bf16_bits(pre.g));  // bf16(gamma), exact in fp32
 #pragma unroll
     for (int fj = 0; fj < kFJ; ++fj) {
-      const int64_t j = j0 + 32 * fj + (lane & 31);
-      if (j >= J) continue;
 #pragma unroll
-      for (int fi = 0; fi < kFI; ++fi) {
+      for (int fi = 0; fi < kFI; ++fi)
 #pragma unroll
         for (int gi = 0; gi < 4; ++gi) {
-          const int64_t i = i0 + 32 * fi + 8 * gi + 4 * (lane >> 5);
-          if (i >= I) continue;
-          float v[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) v[q] = acc[fi][fj][4 * gi + q] * sc;
-          if constexpr (OUT_F32) {
-            float* dst = static_cast<float*>(out) + j * I + i;
-            if (vec && i + 4 <= I) {
-              *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
-            } else {
-#pragma unroll
-              for (int q = 0; q < 4; ++q)
-                if (i + q < I) dst[q] = v[q];
-            }
-          } else {
-            uint16_t* dst = static_cast<uint16_t*>(out) + j * I + i;
-            if (vec && i + 4 <= I) {
-              *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-            } else {
-#pragma unroll
-              for (int q = 0; q < 4; ++q)
-                if (i + q < I) dst[q] = f32_to_bf16_bits(v[q]);
-            }
-          }
+          const float v0 = acc[fi][fj][4 * gi] * sc, v1 = acc[fi][fj][4 * gi + 1] * sc;
+          const float v2 = acc[fi][fj][4 * gi + 2] * sc, v3 = acc[fi][fj][4 * gi + 3] * sc;
+          if constexpr (OUT_F32)
+            EpStage<4>::put(wlds, lane, fi, gi, make_uint4(__float_as_uint(v0), __float_as_uint(v1),
+                                                           __float_as_uint(v2), __float_as_uint(v3)));
+          else
+            EpStage<2>::put(wlds, lane, fi, gi, make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)));
         }
-      }
+      EpStage<kEB>::drain(wlds, static_cast<char*>(out), I, J, i0, j0 + 32 * fj, lane);
     }
   }
 };
@@ -1045,6 +1095,7 @@ __device__ __forceinline__ bool finish_piece(const SplitPlan& p, typename MT::Ac
 template <class MT, int MAP, class PL, class QL, class EP>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(PL pl, QL ql, EP ep, SplitPlan plan) {
   typedef SmemLayout<PL, QL> L;
+  static_assert(kThreads / 64 * EP::kWaveLds <= L::kBytes, "epilogue staging fits in the stage buffers");
   __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
   __shared__ int s_flag;
 
@@ -1062,7 +1113,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(PL pl, QL ql, EP ep, 
       for (int fj = 0; fj < kFJ; ++fj) zero_acc(acc[fi][fj]);
     const typename EP::Pre pre = ep.prefetch(j0 + qrow0, lane);
     run_stages<MT, MAP>(pl, ql, smem, acc, i0, j0, 0, plan.nstages, prow0, qrow0, lane);
-    ep.store(acc, pre, i0 + prow0, j0 + qrow0, lane);
+    ep.store(acc, pre, i0 + prow0, j0 + qrow0, lane, smem + wave * EP::kWaveLds);
     return;
   }
 
@@ -1082,7 +1133,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(PL pl, QL ql, EP ep, 
     const typename EP::Pre pre = ep.prefetch(j0 + qrow0, lane);
     run_stages<MT, MAP>(pl, ql, smem, acc, i0, j0, s0, s1, prow0, qrow0, lane);
     if ((s0 == 0 && s1 == plan.nstages) || finish_piece<MT>(plan, acc, v, t, &s_flag))
-      ep.store(acc, pre, i0 + prow0, j0 + qrow0, lane);
+      ep.store(acc, pre, i0 + prow0, j0 + qrow0, lane, smem + wave * EP::kWaveLds);
     it += s1 - s0;
   }
 }
@@ -1208,7 +1259,7 @@ hipError_t launch_fwd(const int8_t* x_q, const float* s_x, const uint8_t* w_pack
   const int64_t Kp = k_pad(K);
   PackedCodesLoader pl{w_packed, Kp / 4, N};
   CopyLoader<1, true> ql{reinterpret_cast<const char*>(x_q), Kp, M, Kp};
-  FwdEpilogue ep{y, acc_out, s_x, gamma, N, M, N % 4 == 0};
+  FwdEpilogue ep{y, acc_out, s_x, gamma, N, M};
   return run_gemm<MfmaI8, 1>(pl, ql, ep, shape_of(GemmKind::kFwd, M, N, K), ws, ws_bytes, stream);
 }
 
@@ -1217,7 +1268,7 @@ hipError_t launch_bwd_dx(const uint16_t* dY, const uint8_t* w_packed, const floa
                          hipStream_t stream) {
   const int64_t Kp = k_pad(K);
   PackedCodesTLoader pl{w_packed, Kp / 4, N};
-  Bf16Epilogue<false> ep{dX, gamma, K, M, K % 4 == 0};
+  Bf16Epilogue<false> ep{dX, gamma, K, M};
   const GemmShape g = shape_of(GemmKind::kBwdDx, M, N, K);
   if (N % 8 == 0) {
     CopyLoader<2, true> ql{reinterpret_cast<const char*>(dY), 2 * N, M, 2 * N};
@@ -1245,11 +1296,11 @@ hipError_t launch_bwd_dw(const uint16_t* dY, const int8_t* x_q, const float* s_x
   const GemmShape g = shape_of(GemmKind::kBwdDw, M, N, K);
   const bool vec = (N % 4 == 0);
   if (dw_is_f32) {
-    Bf16Epilogue<true> ep{dW, nullptr, K, N, K % 4 == 0};
+    Bf16Epilogue<true> ep{dW, nullptr, K, N};
     if (vec) return run_gemm<MfmaBf16, 0>(pl, RowTransposeBf16Loader<true, 5>{dY, N, M, N}, ep, g, split_ws, split_bytes, stream);
     return run_gemm<MfmaBf16, 0>(pl, RowTransposeBf16Loader<false, 5>{dY, N, M, N}, ep, g, split_ws, split_bytes, stream);
   }
-  Bf16Epilogue<false> ep{dW, nullptr, K, N, K % 4 == 0};
+  Bf16Epilogue<false> ep{dW, nullptr, K, N};
   if (vec) return run_gemm<MfmaBf16, 0>(pl, RowTransposeBf16Loader<true, 5>{dY, N, M, N}, ep, g, split_ws, split_bytes, stream);
   return run_gemm<MfmaBf16, 0>(pl, RowTransposeBf16Loader<false, 5>{dY, N, M, N}, ep, g, split_ws, split_bytes, stream);
 }

@@ -107,6 +107,8 @@ def test_fwd_validation(L):
     # (N + 256) * Kp/4 bytes of w_packed must stay within 2^31
     assert L.bitlinear_fwd(A, A, A, A, 1 << 20, 4, 1 << 12, A, None, None, 0, None) == ESHAPE
     assert L.bitlinear_fwd(A, A, A, A, 4, 1 << 22, 1 << 12, A, None, None, 0, None) == ESHAPE
+    # the epilogue addresses 32 output rows of N 4-byte values with 32-bit offsets: N <= 2^24
+    assert L.bitlinear_fwd(A, A, A, A, 4, (1 << 24) + 64, 64, A, None, None, 0, None) == ESHAPE
     assert L.bitlinear_fwd(A, A, A, A, 4, 4, 4, MISALIGNED, None, None, 0, None) == EALIGN
     assert L.bitlinear_fwd(A, A, A, A, 4, 4, 4, A, MISALIGNED, None, 0, None) == EALIGN
     assert L.bitlinear_fwd(A, A, A, A + 2, 4, 4, 4, A, None, None, 0, None) == EALIGN
