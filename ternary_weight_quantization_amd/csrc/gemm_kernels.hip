@@ -606,6 +606,106 @@ struct RowTransposeBf16Loader {
   }
 };
 
+// dW operands kept in their memory orientation. The tile of a stage is 64
+// reduction rows m x 256 operand rows (columns of the source), copied as
+// stored into LDS rows of kTrPitch bytes, and the fragments are read with
+// ds_read_b64_tr_b16, which transposes 4 x 16 blocks of 16-bit values on
+// the way out: in each 16-lane group, lane 4e + q addresses LDS row e,
+// columns 4q..4q+3, and lane 4q + p receives column 4q + p of rows 0..3.
+// A 32 x 16 MFMA fragment is two such reads per lane (reduction rows
+// 16KS + 8h + 0..3 and + 4..7 for lane half h). The 64-byte row padding puts
+// the 4 rows a 32-lane half reads 16 banks apart, so a read is free of bank
+// conflicts, and a staging store (one 512-byte row per half-wave) is too.
+constexpr int kTrPitch = 512 + 64;
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+
+struct TrFrags {
+  MfmaBf16::Frag buf[2][4];
+  const char* base;
+  __device__ __forceinline__ void init(const char* tile, int row0, int lane) {
+    const int g = lane >> 4, e = (lane >> 2) & 3, q = lane & 3;
+    base = tile + (8 * (g >> 1) + e) * kTrPitch + 2 * (row0 + 16 * (g & 1) + 4 * q);
+  }
+  static __device__ __forceinline__ v4i16_t tr(const char* p) {
+    typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(__attribute__((address_space(3))) char*)p);
+  }
+  template <int KS>
+  __device__ __forceinline__ void read(int f) {
+    const char* a = base + 16 * KS * kTrPitch + 64 * f;
+    const v4i16_t lo = tr(a), hi = tr(a + 4 * kTrPitch);
+    typedef short v8i16_t __attribute__((ext_vector_type(8)));
+    const v8i16_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    buf[KS & 1][f] = __builtin_bit_cast(MfmaBf16::Frag, v);
+  }
+  template <int U>
+  __device__ __forceinline__ void ahead() {
+    if constexpr (U >= kBarrierSlot + 1 && U < kBarrierSlot + 5) read<0>(U - kBarrierSlot - 1);
+  }
+  template <int KS, int U>
+  __device__ __forceinline__ void slot() {
+    if constexpr (KS + 1 < kKSteps && U % 4 == 0) read<KS + 1>(U / 4);
+  }
+  template <int KS>
+  __device__ __forceinline__ MfmaBf16::Frag frag(int f) const { return buf[KS & 1][f]; }
+};
+
+// Copy loader for TrFrags tiles from a bf16 [m][ld] matrix whose first
+// `cols` columns are the operand rows (x_hat: ld = cols = Kp; dY: ld = cols
+// = N), ld a multiple of 8 so that 16-byte pieces never straddle a row end.
+// Thread t handles 16-byte chunk t % 32 of reduction rows t / 32 + 8h,
+// h < 8 (a wave instruction covers 2 rows x 512 bytes). Staging in k-step
+// KS: rows h = 2KS, 2KS + 1 are stored (slots S0, S0 + 2) and refilled with
+// stage s+2 (slots S0 + 8, S0 + 10). S0 = 1 for P and 5 for Q.
+template <int S0>
+struct RowCopyBf16Loader {
+  static constexpr bool kSwz = false;
+  static constexpr int kTileB = 64 * kTrPitch;
+  static constexpr int kLastStoreSlot = S0 + 2;
+  template <class MT, int MAP>
+  using Frags = TrFrags;
+  const uint16_t* src;
+  int64_t ld;    // elements per source row
+  int64_t mred;  // valid reduction rows (M)
+  int64_t cols;  // valid operand rows (columns of the source)
+  // lane_off: byte offset of the thread's chunk in stage 0, row t/32, or an
+  // out-of-range offset for chunks past `cols`
+  struct Regs { uint4 v[8]; uint32_t lane_off; };
+  struct Tmp {};
+
+  __device__ __forceinline__ uint32_t stage_off(int s, int h) const {
+    return (uint32_t)(((int64_t)s * kRed16 + 8 * h) * ld * 2);
+  }
+  __device__ __forceinline__ void load(Regs& r, int row0, int s) const {
+    const int tid = threadIdx.x;
+    const int64_t col = row0 + 8 * (tid & 31);
+    r.lane_off = col < cols ? (uint32_t)(((tid >> 5) * ld + col) * 2) : kOob;
+    const rsrc_t rs = make_rsrc(src, (uint32_t)(mred * ld * 2));
+#pragma unroll
+    for (int h = 0; h < 8; ++h) r.v[h] = buf_load16(rs, r.lane_off + stage_off(s, h));
+  }
+  __device__ __forceinline__ void store(const Regs& r, char* lds) const {
+    const int tid = threadIdx.x;
+    char* dst = lds + (tid >> 5) * kTrPitch + 16 * (tid & 31);
+#pragma unroll
+    for (int h = 0; h < 8; ++h) *reinterpret_cast<uint4*>(dst + 8 * h * kTrPitch) = r.v[h];
+  }
+  template <int KS, int U>
+  __device__ __forceinline__ void slot(Regs& r, Tmp&, char* lds, int, int s2) const {
+    const int tid = threadIdx.x;
+    if constexpr (U == S0 || U == S0 + 2) {
+      constexpr int h = 2 * KS + (U == S0 + 2);
+      *reinterpret_cast<uint4*>(lds + ((tid >> 5) + 8 * h) * kTrPitch + 16 * (tid & 31)) = r.v[h];
+    }
+    if constexpr (U == S0 + 8 || U == S0 + 10) {
+      constexpr int h = 2 * KS + (U == S0 + 10);
+      const rsrc_t rs = make_rsrc(src, (uint32_t)(mred * ld * 2));
+      r.v[h] = buf_load16(rs, r.lane_off + stage_off(s2, h));
+    }
+  }
+};
+
 // dW P: x_hat = bf16(fl32(x_q * fl32(s/127))) is built once per backward
 // call into the workspace ([M][Kp] bf16; for the scales act-quant produces
 // it equals the exactly rounded bf16(x_q * s / 127)) and then staged like dY
@@ -1292,8 +1392,15 @@ hipError_t launch_bwd_dw(const uint16_t* dY, const int8_t* x_q, const float* s_x
   xhat_kernel<<<(int)(want < 4096 ? want : 4096), 256, 0, stream>>>(x_q, s_x, M, Kp, xhat);
   if (hipError_t e = hipGetLastError()) return e;
 
-  RowTransposeBf16Loader<true, 3> pl{xhat, Kp, M, Kp};
   const GemmShape g = shape_of(GemmKind::kBwdDw, M, N, K);
+  if (N % 8 == 0) {
+    // both operands copied in their memory orientation, fragments read transposed
+    const RowCopyBf16Loader<1> pc{xhat, Kp, M, Kp};
+    const RowCopyBf16Loader<5> qc{dY, N, M, N};
+    if (dw_is_f32) return run_gemm<MfmaBf16, 0>(pc, qc, Bf16Epilogue<true>{dW, nullptr, K, N}, g, split_ws, split_bytes, stream);
+    return run_gemm<MfmaBf16, 0>(pc, qc, Bf16Epilogue<false>{dW, nullptr, K, N}, g, split_ws, split_bytes, stream);
+  }
+  RowTransposeBf16Loader<true, 3> pl{xhat, Kp, M, Kp};
   const bool vec = (N % 4 == 0);
   if (dw_is_f32) {
     Bf16Epilogue<true> ep{dW, nullptr, K, N};
