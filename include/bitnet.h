@@ -31,9 +31,11 @@
  *    for the GEMM entry points every operand the call reads among x_q,
  *    w_packed and dY satisfies (rows + 256) * row_bytes <= 2^31, i.e.
  *    (M + 256) * Kp, (N + 256) * Kp/4 and (M + 256) * 2N bytes, and with dW
- *    also (M + 256) * 2Kp for its bf16 x_hat (the kernels address them with
- *    32-bit offsets); the forward also needs N <= 2^24 (its epilogue
- *    addresses 32 output rows of up to 4-byte elements the same way).
+ *    also (M + 256) * 2Kp for its bf16 x_hat, with dX also (Kp + 256) * Np/2
+ *    for its fp4 transposed codes (Np = N rounded up to 64) (the kernels
+ *    address them with 32-bit offsets); the forward also needs N <= 2^24
+ *    (its epilogue addresses 32 output rows of up to 4-byte elements the
+ *    same way).
  */
 #ifndef BITNET_H
 #define BITNET_H
@@ -77,9 +79,10 @@ size_t bitnet_ternarize_workspace_bytes(int64_t N, int64_t K);
  * per workgroup piece, at most about 128 MiB. The contents need no
  * initialization; a workspace must not be shared by calls that may run at
  * the same time (calls on one stream may share it). bitlinear_bwd's size
- * covers both of its products, which run one after the other; with dW it
- * includes a transient bf16 x_hat = bf16(x_q * s/127) [M][Kp] (2*M*Kp bytes)
- * built at the start of the dW product. */
+ * covers both of its products, which run one after the other. Each product
+ * first builds a transient operand at the start of the workspace: dX the
+ * ternary codes transposed to fp4 [Kp][Np/2] (Kp*Np/2 bytes, Np = N rounded
+ * up to 64), dW a bf16 x_hat = bf16(x_q * s/127) [M][Kp] (2*M*Kp bytes). */
 size_t bitlinear_fwd_workspace_bytes(int64_t M, int64_t N, int64_t K);
 size_t bitlinear_bwd_workspace_bytes(int64_t M, int64_t N, int64_t K);
 

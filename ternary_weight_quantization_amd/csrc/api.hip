@@ -49,6 +49,8 @@ bitnet_status check_gemm_ranges(int64_t M, int64_t N, int64_t K, bool need_xq, b
   if (need_xq && !buffer_range_ok(M, 2 * Kp)) return BITNET_ERR_SHAPE;  // dW's bf16 x_hat
   if (need_w && !buffer_range_ok(N, Kp / 4)) return BITNET_ERR_SHAPE;
   if (need_dy && !buffer_range_ok(M, 2 * N)) return BITNET_ERR_SHAPE;
+  // dX reads the codes transposed to fp4 [Kp][Np/2] (Np = N rounded up to 64)
+  if (need_w && need_dy && !buffer_range_ok(Kp, (N + 63) / 64 * 32)) return BITNET_ERR_SHAPE;
   return BITNET_OK;
 }
 

@@ -4,21 +4,22 @@
 //
 //     C[i][j] = sum_r P[i][r] * Q[j][r],      output O[j][i] (i contiguous)
 //
-// with both operand tiles staged in LDS with the reduction axis contiguous,
-// 64 bf16 or 128 int8 reduction values per row per stage:
+// with both operand tiles staged in LDS, 64 bf16 or 128 int8 reduction
+// values per row per stage:
 //
 //   forward  y[m][n]  = sum_k x_q[m][k] q[n][k]        i = n, j = m, r = k
 //            P = the 2-bit codes as stored (expanded to int8 after the
 //            fragment read), Q = x_q copied; v_mfma_i32_32x32x32_i8, exact
 //            int32 accumulation
 //   dX       dX[m][k] = sum_n dY[m][n] W_hat[n][k]     i = k, j = m, r = n
-//            P = the 2-bit codes transposed to [k][n] (expanded to bf16 +-1, 0
-//            after the fragment read), Q = dY copied; v_mfma_f32_32x32x16_bf16;
-//            bf16(gamma) applied in the epilogue (exact: q * bf16(gamma) is
-//            exact in bf16)
+//            P = the codes transposed to fp4 [k][n] by a pre-pass (expanded
+//            to bf16 +-1, 0 after the fragment read), Q = dY copied;
+//            v_mfma_f32_32x32x16_bf16; bf16(gamma) applied in the epilogue
+//            (exact: q * bf16(gamma) is exact in bf16)
 //   dW       dW[n][k] = sum_m dY[m][n] x_hat[m][k]     i = k, j = n, r = m
-//            P = x_q transposed and rescaled to bf16 x_hat, Q = dY
-//            transposed; v_mfma_f32_32x32x16_bf16
+//            P = bf16 x_hat built by a pre-pass, Q = dY, both staged in
+//            their [m][.] orientation and read transposed from LDS
+//            (ds_read_b64_tr_b16); v_mfma_f32_32x32x16_bf16
 //
 // ("bitnet-qat-train": opening bullets - INT8 forward, backward operands
 // rebuilt transiently from the 2-bit / INT8 state; Semantics - forward
@@ -343,16 +344,19 @@ struct CopyLoader {
   }
 };
 
-// Forward P: the 2-bit codes [N][Kp/4] copied as stored (rows n, 32 bytes
-// per stage). Thread t handles row t: two 16-byte loads.
-struct PackedCodesLoader {
+// A narrow code operand copied as stored, 32 bytes per row per stage: the
+// forward's 2-bit codes [N][Kp/4] (rows n; F = CodesI8Frags) or dX's fp4
+// transposed codes [Kp][Np/2] (rows k; F = CodesFp4Frags). Thread t handles
+// row t: two 16-byte loads.
+template <class F>
+struct RowCodesLoader {
   static constexpr bool kSwz = false;
-  static constexpr int kTileB = 256 * CodesI8Frags::kPitchB;
+  static constexpr int kTileB = 256 * F::kPitchB;
   template <class MT, int MAP>
-  using Frags = CodesI8Frags;
+  using Frags = F;
   const uint8_t* packed;
-  int64_t pitch;  // Kp/4 (a multiple of 16)
-  int64_t rows;   // N
+  int64_t pitch;  // bytes per row (a multiple of 16)
+  int64_t rows;   // valid rows
   struct Regs { uint4 v[2]; };
   struct Tmp {};
 
@@ -367,7 +371,7 @@ struct PackedCodesLoader {
     for (int h = 0; h < 2; ++h) r.v[h] = buf_load16(rs, offset(row0, s, h));
   }
   __device__ __forceinline__ void store(const Regs& r, char* lds) const {
-    char* dst = lds + threadIdx.x * CodesI8Frags::kPitchB;
+    char* dst = lds + threadIdx.x * F::kPitchB;
     *reinterpret_cast<uint4*>(dst) = r.v[0];
     *reinterpret_cast<uint4*>(dst + 16) = r.v[1];
   }
@@ -377,129 +381,14 @@ struct PackedCodesLoader {
   template <int KS, int U>
   __device__ __forceinline__ void slot(Regs& r, Tmp&, char* lds, int row0, int s2) const {
     if constexpr (KS < 2 && U == 5)
-      *reinterpret_cast<uint4*>(lds + threadIdx.x * CodesI8Frags::kPitchB + 16 * KS) = r.v[KS];
+      *reinterpret_cast<uint4*>(lds + threadIdx.x * F::kPitchB + 16 * KS) = r.v[KS];
     if constexpr (KS < 2 && U == 13) {
       const rsrc_t rs = make_rsrc(packed, (uint32_t)(rows * pitch));
       r.v[KS] = buf_load16(rs, offset(row0, s2, KS));
     }
   }
 };
-
-// The byte selected by `sel` from each of a0..a3 -> one word (a0's lowest).
-__device__ __forceinline__ uint32_t gather_byte(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3,
-                                                uint32_t sel) {
-  const uint32_t t01 = perm(a1, a0, sel);
-  const uint32_t t23 = perm(a3, a2, sel);
-  return perm(t23, t01, 0x05040100u);
-}
-
-// dX P: the 2-bit codes [N][Kp/4] transposed into [k][n] fp4 rows. A stage
-// is 64 n-rows x 64 bytes (k0..k0+255). Wave w handles n = 16w..+15: lane
-// (r = l/16, d = l%16) loads word d (k = k0+16d..+15) of rows n = 16w+4g+r,
-// g < 4. Byte r of such a word holds the codes of k = k0+16d+r+4i (i < 4) at
-// bits 2i; an in-wave byte transpose (ds_bpermute) gives lane (r, d) byte r
-// of the 16 rows; for each i it then writes row k = 16d+r+4i: the fp4
-// nibbles of n = 16w..16w+15 (8 bytes at 8w). The four rows are written in
-// a lane-rotated order to spread the stores over the banks.
-struct PackedCodesTLoader {
-  static constexpr bool kSwz = false;
-  static constexpr int kTileB = 256 * CodesFp4Frags::kPitchB;
-  template <class MT, int MAP>
-  using Frags = CodesFp4Frags;
-  const uint8_t* packed;
-  int64_t pitch;  // Kp/4 bytes per n row
-  int64_t nred;   // N (valid reduction rows)
-  struct Regs { uint32_t d[4]; };
-  struct Tmp { uint32_t a[8]; uint32_t W[4]; uint32_t lo; };
-
-  __device__ __forceinline__ void load(Regs& r, int row0, int s) const {
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;
-    const rsrc_t rs = make_rsrc(packed, (uint32_t)(nred * pitch));
-    const int64_t col = (row0 >> 2) + 4 * (lane & 15);  // byte within the row
-    const int64_t n = (int64_t)s * 64 + 16 * w + (lane >> 4);
-    const uint32_t off = col < pitch ? (uint32_t)(n * pitch + col) : kOob;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) r.d[g] = buf_load4(rs, off + (uint32_t)(4 * g * pitch));
-  }
-  // fp4 nibbles (n order) of the codes of n = 16w + 4g + 0..3 for row
-  // k = 16d + r + 4ii: field ii of t.W[g] holds them in bytes 0..3
-  __device__ __forceinline__ uint32_t fp4_pair(const Tmp& t, int g, int ii) const {
-    const uint32_t x = (t.W[g] >> (2 * ii)) & 0x03030303u;
-    const uint32_t nib = perm(0u, 0x0A000200u, x);  // code 0, 1, 3 -> fp4 0x0, 0x2, 0xA
-    return nib | (nib >> 4);  // bytes 0 and 2: two nibbles each
-  }
-  // half H (n = 16w + 8H..+7) of row 16d + r + 4i' (i' = (I + d) % 4) of the
-  // wave's 8-byte column; half 1 also stores the row
-  template <int I, int H>
-  __device__ __forceinline__ void write_row_half(Tmp& t, char* lds) const {
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;
-    const int rr = lane >> 4, d = lane & 15;
-    const int ii = (I + d) & 3;
-    const uint32_t v = perm(fp4_pair(t, 2 * H + 1, ii), fp4_pair(t, 2 * H, ii), 0x06040200u);
-    if constexpr (H == 0) {
-      t.lo = v;
-    } else {
-      *reinterpret_cast<uint2*>(lds + (16 * d + rr + 4 * ii) * CodesFp4Frags::kPitchB + 8 * w) = make_uint2(t.lo, v);
-    }
-  }
-  template <int I>
-  __device__ __forceinline__ void write_row(Tmp& t, char* lds) const {
-    write_row_half<I, 0>(t, lds);
-    write_row_half<I, 1>(t, lds);
-  }
-  __device__ __forceinline__ void store(const Regs& r, char* lds) const {
-    Tmp t;
-    transpose_bperm<0>(r, t);
-    transpose_gather<0>(t);
-    transpose_bperm<1>(r, t);
-    transpose_gather<1>(t);
-    write_row<0>(t, lds);
-    write_row<1>(t, lds);
-    write_row<2>(t, lds);
-    write_row<3>(t, lds);
-  }
-  // Byte transpose of words g = 2G, 2G + 1 (ds_bpermute), then the gather.
-  template <int G>
-  __device__ __forceinline__ void transpose_bperm(const Regs& r, Tmp& t) const {
-    const int d = threadIdx.x & 15;
-#pragma unroll
-    for (int g = 2 * G; g < 2 * G + 2; ++g)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        t.a[4 * (g - 2 * G) + e] = (uint32_t)__builtin_amdgcn_ds_bpermute((16 * e + d) << 2, (int)r.d[g]);
-  }
-  template <int G>
-  __device__ __forceinline__ void transpose_gather(Tmp& t) const {
-    const uint32_t rr = (threadIdx.x & 63) >> 4;
-    const uint32_t sel = rr | ((rr + 4) << 8);
-#pragma unroll
-    for (int g = 2 * G; g < 2 * G + 2; ++g) {
-      const int o = 4 * (g - 2 * G);
-      t.W[g] = gather_byte(t.a[o], t.a[o + 1], t.a[o + 2], t.a[o + 3], sel);
-    }
-  }
-  // K-step 0 transposes (slots 2, 6, 8, 12) and writes row 0 (slots 14,
-  // 15); k-steps 1..3 write one row each (slots 2, 4); k-step 1 refills the
-  // registers with stage s+2 (slot 10).
-  static constexpr int kLastStoreSlot = 4;
-  template <int KS, int U>
-  __device__ __forceinline__ void slot(Regs& r, Tmp& t, char* lds, int row0, int s2) const {
-    if constexpr (KS == 0) {
-      if constexpr (U == 2) transpose_bperm<0>(r, t);
-      if constexpr (U == 6) transpose_gather<0>(t);
-      if constexpr (U == 8) transpose_bperm<1>(r, t);
-      if constexpr (U == 12) transpose_gather<1>(t);
-      if constexpr (U == 14) write_row_half<0, 0>(t, lds);
-      if constexpr (U == 15) write_row_half<0, 1>(t, lds);
-    } else {
-      if constexpr (U == 2) write_row_half<KS, 0>(t, lds);
-      if constexpr (U == 4) write_row_half<KS, 1>(t, lds);
-      if constexpr (KS == 1 && U == 10) load(r, row0, s2);
-    }
-  }
-};
+using PackedCodesLoader = RowCodesLoader<CodesI8Frags>;
 
 // dW operands from a bf16 [rows m][ld] matrix read transposed: rows j
 // (n of dY for Q, k of x_hat for P), reduction m (strided). Thread
@@ -735,6 +624,46 @@ __global__ __launch_bounds__(256) void xhat_kernel(const int8_t* __restrict__ xq
     dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
     dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
   }
+}
+
+// dX P: the ternary codes transposed to [k][n] as fp4 nibbles (the layout
+// CodesFp4Frags reads: n even in the low nibble, +1 = 0x2, -1 = 0xA, 0 =
+// 0x0), rows of Np/2 bytes with Np = N rounded up to 64 (zero nibbles past
+// N), built once per backward call into the workspace and then copied stage
+// by stage like the forward's codes (RowCodesLoader). A block covers 64 k x
+// 256 n: thread t loads the 64 codes k0..k0+63 of row n0 + t (16 bytes, 4
+// planar words; code j of a word sits at bit 8(j%4) + 2(j/4)), then writes
+// the 64 nibbles n0 + 64(t%4) + 0..63 of row k0 + t/4 (32 bytes).
+__global__ __launch_bounds__(256) void wt_fp4_kernel(const uint8_t* __restrict__ packed, int64_t N, int64_t Kp,
+                                                     int64_t Np, uint8_t* __restrict__ wt) {
+  __shared__ uint32_t tile[256][5];
+  const int t = threadIdx.x;
+  const int64_t k0 = (int64_t)blockIdx.x * 64, n0 = (int64_t)blockIdx.y * 256;
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (n0 + t < N) v = *reinterpret_cast<const uint4*>(packed + (n0 + t) * (Kp / 4) + k0 / 4);
+  tile[t][0] = v.x;
+  tile[t][1] = v.y;
+  tile[t][2] = v.z;
+  tile[t][3] = v.w;
+  __syncthreads();
+  const int kl = t >> 2, w = kl >> 4, j = kl & 15;
+  const int sh = 8 * (j & 3) + 2 * (j >> 2);
+  const int nb = 64 * (t & 3);
+  if (n0 + nb >= Np) return;
+  uint32_t o[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    uint32_t acc = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t c = (tile[nb + 8 * q + e][w] >> sh) & 3u;  // 0, 1 or 3
+      acc |= (((c & 1u) << 1) | ((c & 2u) << 2)) << (4 * e);
+    }
+    o[q] = acc;
+  }
+  uint4* dst = reinterpret_cast<uint4*>(wt + (k0 + kl) * (Np / 2) + (n0 + nb) / 2);
+  dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+  dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
 }
 
 // ---------------------------------------------------------------------------
@@ -1292,11 +1221,15 @@ static size_t split_workspace(const GemmShape& g, int grid) {
 
 // dW's x_hat buffer at the start of its workspace.
 static size_t xhat_bytes(int64_t M, int64_t K) { return ((size_t)M * k_pad(K) * 2 + 255) / 256 * 256; }
+static int64_t n_pad64(int64_t N) { return (N + 63) / 64 * 64; }
+static size_t wt_bytes(int64_t N, int64_t K) { return ((size_t)k_pad(K) * (n_pad64(N) / 2) + 255) / 256 * 256; }
 
 size_t gemm_workspace_bytes(GemmKind kind, int64_t M, int64_t N, int64_t K) {
   const GemmShape g = shape_of(kind, M, N, K);
   const size_t split = split_workspace(g, split_grid(g, kMaxGrid));
-  return kind == GemmKind::kBwdDw ? xhat_bytes(M, K) + split : split;
+  if (kind == GemmKind::kBwdDw) return xhat_bytes(M, K) + split;
+  if (kind == GemmKind::kBwdDx) return wt_bytes(N, K) + split;
+  return split;
 }
 
 static int device_cus() {
@@ -1366,16 +1299,24 @@ hipError_t launch_fwd(const int8_t* x_q, const float* s_x, const uint8_t* w_pack
 hipError_t launch_bwd_dx(const uint16_t* dY, const uint8_t* w_packed, const float* gamma,
                          int64_t M, int64_t N, int64_t K, uint16_t* dX, void* ws, size_t ws_bytes,
                          hipStream_t stream) {
-  const int64_t Kp = k_pad(K);
-  PackedCodesTLoader pl{w_packed, Kp / 4, N};
+  const int64_t Kp = k_pad(K), Np = n_pad64(N);
+  const size_t wb = wt_bytes(N, K);
+  if (ws == nullptr || ws_bytes < wb) return hipErrorInvalidValue;  // the C ABI sized it
+  uint8_t* wt = static_cast<uint8_t*>(ws);
+  void* split_ws = static_cast<char*>(ws) + wb;
+  const size_t split_bytes = ws_bytes - wb;
+  wt_fp4_kernel<<<dim3((unsigned)(Kp / 64), (unsigned)((Np + 255) / 256)), 256, 0, stream>>>(w_packed, N, Kp, Np, wt);
+  if (hipError_t e = hipGetLastError()) return e;
+
+  const RowCodesLoader<CodesFp4Frags> pl{wt, Np / 2, Kp};
   Bf16Epilogue<false> ep{dX, gamma, K, M};
   const GemmShape g = shape_of(GemmKind::kBwdDx, M, N, K);
   if (N % 8 == 0) {
     CopyLoader<2, true> ql{reinterpret_cast<const char*>(dY), 2 * N, M, 2 * N};
-    return run_gemm<MfmaBf16, 1>(pl, ql, ep, g, ws, ws_bytes, stream);
+    return run_gemm<MfmaBf16, 1>(pl, ql, ep, g, split_ws, split_bytes, stream);
   }
   CopyLoader<2, false> ql{reinterpret_cast<const char*>(dY), 2 * N, M, 2 * N};
-  return run_gemm<MfmaBf16, 1>(pl, ql, ep, g, ws, ws_bytes, stream);
+  return run_gemm<MfmaBf16, 1>(pl, ql, ep, g, split_ws, split_bytes, stream);
 }
 
 hipError_t launch_bwd_dw(const uint16_t* dY, const int8_t* x_q, const float* s_x, int64_t M,
