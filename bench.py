@@ -61,9 +61,9 @@ def parse():
 KERNEL_MATCH = {
     "ternarize_pack": ["absmean_partials_kernel", "ternarize_pack_kernel"],
     "act_quant": ["act_quant"],
-    "fwd_i8": ["PackedCodesLoader"],
-    "bwd_dx_bf16": ["PackedCodesTLoader"],
-    "bwd_dw_bf16": ["Int8TransposeScaleLoader"],
+    "fwd_i8": ["MfmaI8"],
+    "bwd_dx_bf16": ["wt_fp4_kernel", "CodesFp4Frags"],
+    "bwd_dw_bf16": ["xhat_kernel", "RowCopyBf16Loader"],
 }
 COPY_BYTES = 256 << 20
 

@@ -132,6 +132,22 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kBarrierSlot = 8;
 static_assert(kBarrierSlot + 7 == 15, "ahead<U> covers the slots after the barrier");
 
+// When the plain (LDS-read) fragments are read. Slot U of k-step KS uses P
+// fragment U/4 and Q fragment U%4, so the Q fragments of a k-step are all
+// needed in its first four slots and the P fragments in slots 0, 4, 8, 12.
+// The next k-step's fragments are read in the first half of the current
+// one, Q first, so that each is requested at least 9 slots before its use:
+// P fragment f in slot next_read_slot<false>(f), Q fragment f in
+// next_read_slot<true>(f); the next stage's k-step 0 fragments are read
+// after the stage barrier in the same order (ahead_slot).
+template <bool Q>
+__device__ __forceinline__ constexpr int next_read_slot(int f) { return Q ? f : (f == 0 ? 0 : 3 + f); }
+template <bool Q>
+__device__ __forceinline__ constexpr int ahead_slot(int f) {
+  return kBarrierSlot + 1 + (Q ? f / 2 : (f == 0 ? 0 : 1 + f));
+}
+static_assert(ahead_slot<false>(3) < 16, "");
+
 // 16-byte fragments read directly from a plain tile (pitch kPitch).
 template <class MT, bool SWZ, int MAP>
 struct PlainFrags {
@@ -156,13 +172,21 @@ struct PlainFrags {
   __device__ __forceinline__ void read(int f) {
     buf[KS & 1][f] = *reinterpret_cast<const typename MT::Frag*>(base + off<KS>(f));
   }
-  template <int U>
+  template <int U, bool Q>
   __device__ __forceinline__ void ahead() {
-    if constexpr (U >= kBarrierSlot + 1 && U < kBarrierSlot + 5) read<0>(U - kBarrierSlot - 1);
+    if constexpr (U == ahead_slot<Q>(0)) read<0>(0);
+    if constexpr (U == ahead_slot<Q>(1)) read<0>(1);
+    if constexpr (U == ahead_slot<Q>(2)) read<0>(2);
+    if constexpr (U == ahead_slot<Q>(3)) read<0>(3);
   }
-  template <int KS, int U>
+  template <int KS, int U, bool Q>
   __device__ __forceinline__ void slot() {
-    if constexpr (KS + 1 < kKSteps && U % 4 == 0) read<KS + 1>(U / 4);
+    if constexpr (KS + 1 < kKSteps) {
+      if constexpr (U == next_read_slot<Q>(0)) read<KS + 1>(0);
+      if constexpr (U == next_read_slot<Q>(1)) read<KS + 1>(1);
+      if constexpr (U == next_read_slot<Q>(2)) read<KS + 1>(2);
+      if constexpr (U == next_read_slot<Q>(3)) read<KS + 1>(3);
+    }
   }
   template <int KS>
   __device__ __forceinline__ typename MT::Frag frag(int f) const { return buf[KS & 1][f]; }
@@ -192,7 +216,7 @@ struct CodesI8Frags {
     const uint32_t w = KS == 0 ? raw[F].x : KS == 1 ? raw[F].y : KS == 2 ? raw[F].z : raw[F].w;
     cur[KS & 1][F][T] = (int)codes4_to_i8((w >> (2 * T)) & 0x03030303u);
   }
-  template <int U>
+  template <int U, bool Q>
   __device__ __forceinline__ void ahead() {
     static_assert(kBarrierSlot + 2 < 12, "raw words must be read before slot 12");
     if constexpr (U == kBarrierSlot + 1 || U == kBarrierSlot + 2) {
@@ -202,7 +226,7 @@ struct CodesI8Frags {
     }
     if constexpr (U >= 12) expand<0, 0, U - 12>();
   }
-  template <int KS, int U>
+  template <int KS, int U, bool Q>
   __device__ __forceinline__ void slot() {
     if constexpr (U / 4 < 3) expand<KS, U / 4 + 1, U % 4>();
     else if constexpr (KS + 1 < kKSteps) expand<KS + 1, 0, U % 4>();
@@ -230,7 +254,7 @@ struct CodesFp4Frags {
     const uint32_t w = KS == 0 ? raw[F].x : KS == 1 ? raw[F].y : KS == 2 ? raw[F].z : raw[F].w;
     cur[KS & 1][F][T] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, T));
   }
-  template <int U>
+  template <int U, bool Q>
   __device__ __forceinline__ void ahead() {
     static_assert(kBarrierSlot + 2 < 12, "raw words must be read before slot 12");
     if constexpr (U == kBarrierSlot + 1 || U == kBarrierSlot + 2) {
@@ -240,7 +264,7 @@ struct CodesFp4Frags {
     }
     if constexpr (U >= 12) expand<0, 0, U - 12>();
   }
-  template <int KS, int U>
+  template <int KS, int U, bool Q>
   __device__ __forceinline__ void slot() {
     if constexpr (U / 4 < 3) expand<KS, U / 4 + 1, U % 4>();
     else if constexpr (KS + 1 < kKSteps) expand<KS + 1, 0, U % 4>();
@@ -528,13 +552,21 @@ struct TrFrags {
     const v8i16_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     buf[KS & 1][f] = __builtin_bit_cast(MfmaBf16::Frag, v);
   }
-  template <int U>
+  template <int U, bool Q>
   __device__ __forceinline__ void ahead() {
-    if constexpr (U >= kBarrierSlot + 1 && U < kBarrierSlot + 5) read<0>(U - kBarrierSlot - 1);
+    if constexpr (U == ahead_slot<Q>(0)) read<0>(0);
+    if constexpr (U == ahead_slot<Q>(1)) read<0>(1);
+    if constexpr (U == ahead_slot<Q>(2)) read<0>(2);
+    if constexpr (U == ahead_slot<Q>(3)) read<0>(3);
   }
-  template <int KS, int U>
+  template <int KS, int U, bool Q>
   __device__ __forceinline__ void slot() {
-    if constexpr (KS + 1 < kKSteps && U % 4 == 0) read<KS + 1>(U / 4);
+    if constexpr (KS + 1 < kKSteps) {
+      if constexpr (U == next_read_slot<Q>(0)) read<KS + 1>(0);
+      if constexpr (U == next_read_slot<Q>(1)) read<KS + 1>(1);
+      if constexpr (U == next_read_slot<Q>(2)) read<KS + 1>(2);
+      if constexpr (U == next_read_slot<Q>(3)) read<KS + 1>(3);
+    }
   }
   template <int KS>
   __device__ __forceinline__ MfmaBf16::Frag frag(int f) const { return buf[KS & 1][f]; }
@@ -924,12 +956,12 @@ __device__ __forceinline__ void zero_acc(Acc& a) {
 }
 
 // All of ahead<U>() of a reader at once (the first stage of a run).
-template <class F>
+template <bool Q, class F>
 __device__ __forceinline__ void prime(F& f) {
-  f.template ahead<kBarrierSlot + 1>(); f.template ahead<kBarrierSlot + 2>();
-  f.template ahead<kBarrierSlot + 3>(); f.template ahead<kBarrierSlot + 4>();
-  f.template ahead<kBarrierSlot + 5>(); f.template ahead<kBarrierSlot + 6>();
-  f.template ahead<kBarrierSlot + 7>();
+  f.template ahead<kBarrierSlot + 1, Q>(); f.template ahead<kBarrierSlot + 2, Q>();
+  f.template ahead<kBarrierSlot + 3, Q>(); f.template ahead<kBarrierSlot + 4, Q>();
+  f.template ahead<kBarrierSlot + 5, Q>(); f.template ahead<kBarrierSlot + 6, Q>();
+  f.template ahead<kBarrierSlot + 7, Q>();
 }
 
 // One MFMA slot of a k-step: MFMA (U / 4, U % 4), then each reader's and
@@ -944,16 +976,16 @@ __device__ __forceinline__ void gemm_slot(const PL& pl, const QL& ql, typename P
                                           char* Pn, char* Qn, typename MT::Acc (&acc)[kFI][kFJ],
                                           int i0, int j0, int s2, bool more) {
   acc[U / 4][U % 4] = MT::mma(fp.template frag<KS>(U / 4), fq.template frag<KS>(U % 4), acc[U / 4][U % 4]);
-  fp.template slot<KS, U>();
-  fq.template slot<KS, U>();
+  fp.template slot<KS, U, false>();
+  fq.template slot<KS, U, true>();
   pl.template slot<KS, U>(pr, pt, Pn, i0, s2);
   ql.template slot<KS, U>(qr, qt, Qn, j0, s2);
   if constexpr (KS == kKSteps - 1) {
     if constexpr (U == kBarrierSlot) __syncthreads();
     if constexpr (U > kBarrierSlot) {
       if (more) {
-        fpn.template ahead<U>();
-        fqn.template ahead<U>();
+        fpn.template ahead<U, false>();
+        fqn.template ahead<U, true>();
       }
     }
   }
@@ -992,11 +1024,16 @@ __device__ __forceinline__ void gemm_stage(const PL& pl, const QL& ql, typename 
 }
 
 // The stages [s0, s1) of tile (i0, j0), accumulated into acc. LDS is free
-// on entry and on return.
+// on entry and on return. `arrive`, when not NULL, is the published-partials
+// counter of this workgroup's previous piece, whose partial stores were
+// issued but not waited for: it is incremented (tag gen) once every wave
+// has waited for its first stage's loads, which were issued after those
+// stores, so the stores are complete by then.
 template <class MT, int MAP, class PL, class QL>
 __device__ __forceinline__ void run_stages(const PL& pl, const QL& ql, char* smem,
                                            typename MT::Acc (&acc)[kFI][kFJ], int i0, int j0, int s0,
-                                           int s1, int prow0, int qrow0, int lane) {
+                                           int s1, int prow0, int qrow0, int lane, uint64_t* arrive,
+                                           uint64_t gen) {
   static_assert(PL::kLastStoreSlot < kBarrierSlot && QL::kLastStoreSlot < kBarrierSlot,
                 "staging stores must precede the end-of-stage barrier");
   typedef SmemLayout<PL, QL> L;
@@ -1010,14 +1047,15 @@ __device__ __forceinline__ void run_stages(const PL& pl, const QL& ql, char* sme
   pl.load(pr, i0, s0 + 1);
   ql.load(qr, j0, s0 + 1);
   __syncthreads();
+  if (arrive != nullptr && threadIdx.x == 0) tagged_arrive(arrive, gen);
   typename PL::template Frags<MT, MAP> fp0, fp1;
   typename QL::template Frags<MT, MAP> fq0, fq1;
   fp0.init(smem, prow0, lane);
   fq0.init(smem + PL::kTileB, qrow0, lane);
   fp1.init(smem + L::kStage, prow0, lane);
   fq1.init(smem + L::kStage + PL::kTileB, qrow0, lane);
-  prime(fp0);
-  prime(fq0);
+  prime<false>(fp0);
+  prime<true>(fq0);
   __builtin_amdgcn_sched_barrier(0);
   int s = s0;
   for (; s + 1 < s1; s += 2) {
@@ -1062,9 +1100,10 @@ __device__ __forceinline__ uint4 chunk_add(uint4 a, uint4 b) {
 }
 
 // End of a piece of a split tile. Arrive; a piece that is not the last
-// publishes its partial tile and returns false; the last one waits for the
-// others' partials, adds them in piece order into acc and returns true (the
-// caller then runs the epilogue). With pieces p_0..p_{n-1} and this one at
+// issues the stores of its partial tile and returns false (the caller
+// signals them published once they are complete); the last one waits for
+// the others' partials, adds them in piece order into acc and returns true
+// (the caller then runs the epilogue). With pieces p_0..p_{n-1} and this one at
 // position me, the sum is ((p_0 + ... + p_{me-1}) + own) + p_{me+1} + ...
 // evaluated left to right (own + L == L + own exactly).
 template <class MT>
@@ -1085,9 +1124,7 @@ __device__ __forceinline__ bool finish_piece(const SplitPlan& p, typename MT::Ac
     const uint32_t base = (uint32_t)(piece_slot(p, v, t) * 64 * kThreads + tid) * 16;
 #pragma unroll
     for (int c = 0; c < 64; ++c) buf_store16_coherent(pr, base + c * kThreads * 16, acc_chunk<MT>(acc, c));
-    wait_vmem();
-    __syncthreads();
-    if (tid == 0) tagged_arrive(cnt + 1, p.gen);
+    asm volatile("" ::: "memory");  // keep the stores ahead of the next piece's loads
     return false;
   }
   if (tid == 0) wait_published(cnt + 1, p.gen, (uint32_t)(n - 1));
@@ -1141,12 +1178,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(PL pl, QL ql, EP ep, 
 #pragma unroll
       for (int fj = 0; fj < kFJ; ++fj) zero_acc(acc[fi][fj]);
     const typename EP::Pre pre = ep.prefetch(j0 + qrow0, lane);
-    run_stages<MT, MAP>(pl, ql, smem, acc, i0, j0, 0, plan.nstages, prow0, qrow0, lane);
+    run_stages<MT, MAP>(pl, ql, smem, acc, i0, j0, 0, plan.nstages, prow0, qrow0, lane, nullptr, 0);
     ep.store(acc, pre, i0 + prow0, j0 + qrow0, lane, smem + wave * EP::kWaveLds);
     return;
   }
 
   const int64_t hi = split_lo(plan, v + 1);
+  uint64_t* pending = nullptr;  // published-partials counter to signal
   for (int64_t it = split_lo(plan, v); it < hi;) {
     const int t = (int)(it / plan.nstages);
     const int s0 = (int)(it - (int64_t)t * plan.nstages);
@@ -1160,10 +1198,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(PL pl, QL ql, EP ep, 
       for (int fj = 0; fj < kFJ; ++fj) zero_acc(acc[fi][fj]);
 
     const typename EP::Pre pre = ep.prefetch(j0 + qrow0, lane);
-    run_stages<MT, MAP>(pl, ql, smem, acc, i0, j0, s0, s1, prow0, qrow0, lane);
+    run_stages<MT, MAP>(pl, ql, smem, acc, i0, j0, s0, s1, prow0, qrow0, lane, pending, plan.gen);
+    pending = nullptr;
     if ((s0 == 0 && s1 == plan.nstages) || finish_piece<MT>(plan, acc, v, t, &s_flag))
       ep.store(acc, pre, i0 + prow0, j0 + qrow0, lane, smem + wave * EP::kWaveLds);
+    else
+      pending = plan.counters + 2 * (int64_t)t + 1;
     it += s1 - s0;
+  }
+  if (pending != nullptr) {
+    // the last piece published: wait for its stores, then signal
+    wait_vmem();
+    __syncthreads();
+    if (tid == 0) tagged_arrive(pending, plan.gen);
   }
 }
 
@@ -1213,10 +1260,14 @@ static int split_grid(const GemmShape& g, int cus) {
   return split < whole ? (int)G : 0;
 }
 
+// Split-launch workspace: the tile counters [T][2] (8 bytes each, rounded
+// up to 256 bytes), then the partial tiles [2G].
+static size_t split_control_bytes(const GemmShape& g, int) {
+  return ((size_t)g.tiles() * 16 + 255) / 256 * 256;
+}
 static size_t split_workspace(const GemmShape& g, int grid) {
   if (grid == 0) return 0;
-  const size_t counters = ((size_t)g.tiles() * 16 + 255) / 256 * 256;
-  return counters + 2 * (size_t)grid * kPartialBytes;
+  return split_control_bytes(g, grid) + 2 * (size_t)grid * kPartialBytes;
 }
 
 // dW's x_hat buffer at the start of its workspace.
@@ -1270,11 +1321,10 @@ static hipError_t run_gemm(const PL& pl, const QL& ql, const EP& ep, const GemmS
   int grid = split_grid(g, device_cus());
   if (grid > 0 && (ws == nullptr || ws_bytes < split_workspace(g, grid))) grid = 0;
   if (grid > 0) {
-    const size_t counters = split_workspace(g, grid) - 2 * (size_t)grid * kPartialBytes;
     plan.grid = grid;
     plan.gen = next_gen();
     plan.counters = static_cast<uint64_t*>(ws);
-    plan.partials = reinterpret_cast<uint4*>(static_cast<char*>(ws) + counters);
+    plan.partials = reinterpret_cast<uint4*>(static_cast<char*>(ws) + split_control_bytes(g, grid));
   } else {
     plan.grid = (int)g.tiles();
   }
