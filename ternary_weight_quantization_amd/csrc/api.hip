@@ -84,10 +84,13 @@ size_t bitlinear_fwd_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 
 size_t bitlinear_bwd_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (check_gemm_sizes(M, N, K) != BITNET_OK) return 0;
-  // dX and dW run one after the other on the stream and share the workspace
+  // dX and dW run either in one launch (N % 8 == 0, both requested) or one
+  // after the other, sharing the workspace
   const size_t a = bitnet::gemm_workspace_bytes(bitnet::GemmKind::kBwdDx, M, N, K);
   const size_t b = bitnet::gemm_workspace_bytes(bitnet::GemmKind::kBwdDw, M, N, K);
-  return a > b ? a : b;
+  const size_t c = bitnet::gemm_workspace_bytes(bitnet::GemmKind::kBwdPair, M, N, K);
+  const size_t ab = a > b ? a : b;
+  return ab > c ? ab : c;
 }
 
 bitnet_status bitnet_ternarize_pack(const void* W, bitnet_dtype w_dtype, int64_t N, int64_t K,
@@ -147,6 +150,11 @@ bitnet_status bitlinear_bwd(const uint16_t* dY, const int8_t* x_q, const float* 
   if (dX && (!aligned(w_packed, 16) || !aligned(gamma, 4) || !aligned(dX, 16))) return BITNET_ERR_ALIGN;
   if (dW && (!aligned(x_q, 16) || !aligned(s_x, 16) || !aligned(dW, 16))) return BITNET_ERR_ALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (dX && dW) {
+    const hipError_t e = bitnet::launch_bwd_pair(dY, w_packed, gamma, x_q, s_x, M, N, K, dX, dW, dW_dtype == BITNET_F32,
+                                                 workspace, workspace_bytes, st);
+    if (e != hipErrorNotSupported) return from_hip(e);
+  }
   if (dX) {
     if (hipError_t e = bitnet::launch_bwd_dx(dY, w_packed, gamma, M, N, K, dX, workspace, workspace_bytes, st)) return from_hip(e);
   }

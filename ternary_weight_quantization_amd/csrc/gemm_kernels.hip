@@ -1158,17 +1158,17 @@ __device__ __forceinline__ bool finish_piece(const SplitPlan& p, typename MT::Ac
   return true;
 }
 
+// The work of virtual workgroup v of a product: one whole tile (no split),
+// or its range of (tile, stage) iterations (stream-K).
 template <class MT, int MAP, class PL, class QL, class EP>
-__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(PL pl, QL ql, EP ep, SplitPlan plan) {
+__device__ __forceinline__ void gemm_body(const PL& pl, const QL& ql, const EP& ep, const SplitPlan& plan,
+                                          int v, char* smem, int* s_flag_p) {
   typedef SmemLayout<PL, QL> L;
   static_assert(kThreads / 64 * EP::kWaveLds <= L::kBytes, "epilogue staging fits in the stage buffers");
-  __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
-  __shared__ int s_flag;
-
+  int& s_flag = *s_flag_p;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wi = wave % kWavesI, wj = wave / kWavesI;
   const int prow0 = wi * kWTI, qrow0 = wj * kWTJ;
-  const int v = cta_order(blockIdx.x, plan.grid);
   if (plan.counters == nullptr) {
     // one whole tile per workgroup
     const int i0 = (v % plan.tiles_i) * kBI, j0 = (v / plan.tiles_i) * kBJ;
@@ -1214,6 +1214,35 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(PL pl, QL ql, EP ep, 
   }
 }
 
+template <class MT, int MAP, class PL, class QL, class EP>
+__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(PL pl, QL ql, EP ep, SplitPlan plan) {
+  typedef SmemLayout<PL, QL> L;
+  __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
+  __shared__ int s_flag;
+  gemm_body<MT, MAP>(pl, ql, ep, plan, cta_order(blockIdx.x, plan.grid), smem, &s_flag);
+}
+
+// Two independent products in one launch, each on its own share of every
+// XCD: of the 8 * kt workgroups (one per CU, workgroup b on XCD b % 8),
+// those with b / 8 < k1 run product 1 (stream-K over 8 * k1 workgroups),
+// the others product 2 (8 * (kt - k1)). Each keeps the XCD-contiguous
+// numbering of its own workgroups. Used for the two STE backward products,
+// which otherwise would each pay their split tail and launch on their own.
+template <class MT, int MAP1, class PL1, class QL1, class EP1, int MAP2, class PL2, class QL2, class EP2>
+__global__ __launch_bounds__(kThreads, 1) void gemm_pair_kernel(PL1 pl1, QL1 ql1, EP1 ep1, SplitPlan plan1,
+                                                                PL2 pl2, QL2 ql2, EP2 ep2, SplitPlan plan2,
+                                                                int k1) {
+  typedef SmemLayout<PL1, QL1> L1;
+  typedef SmemLayout<PL2, QL2> L2;
+  __shared__ __attribute__((aligned(16))) char smem[L1::kBytes > L2::kBytes ? L1::kBytes : L2::kBytes];
+  __shared__ int s_flag;
+  const int x = blockIdx.x % 8, k = blockIdx.x / 8;
+  if (k < k1)
+    gemm_body<MT, MAP1>(pl1, ql1, ep1, plan1, cta_order(8 * k + x, plan1.grid), smem, &s_flag);
+  else
+    gemm_body<MT, MAP2>(pl2, ql2, ep2, plan2, cta_order(8 * (k - k1) + x, plan2.grid), smem, &s_flag);
+}
+
 // ---------------------------------------------------------------------------
 // Host side: choice of the split, workspace, launch.
 // ---------------------------------------------------------------------------
@@ -1243,21 +1272,25 @@ static GemmShape shape_of(GemmKind kind, int64_t M, int64_t N, int64_t K) {
 // workgroups and about 4 pieces per tile. BITNET_SPLIT_CTAS=<G> forces a
 // split over G workgroups, a negative value forces whole tiles (test and
 // tuning knobs).
-static int split_grid(const GemmShape& g, int cus) {
+static int split_pays(const GemmShape& g, int cus) {
   const int64_t T = g.tiles(), S = g.nstages, W = T * S;
-  if (const char* e = getenv("BITNET_SPLIT_CTAS")) {
-    const long f = strtol(e, nullptr, 10);
-    if (f < 0) return 0;
-    if (f > 0) {
-      const int64_t G = f < kMaxGrid ? f : kMaxGrid;
-      return (int)(G < W ? G : W);
-    }
-  }
   if (W < 2 || cus < 1) return 0;
   const int64_t G = (int64_t)cus < 4 * T ? (int64_t)cus : 4 * T;
   const int64_t whole = (T + cus - 1) / cus * S;
   const int64_t split = (W + G - 1) / G + g.overhead;
   return split < whole ? (int)G : 0;
+}
+static int split_grid(const GemmShape& g, int cus) {
+  if (const char* e = getenv("BITNET_SPLIT_CTAS")) {
+    const long f = strtol(e, nullptr, 10);
+    if (f < 0) return 0;
+    if (f > 0) {
+      const int64_t W = g.tiles() * g.nstages;
+      const int64_t G = f < kMaxGrid ? f : kMaxGrid;
+      return (int)(G < W ? G : W);
+    }
+  }
+  return split_pays(g, cus);
 }
 
 // Split-launch workspace: the tile counters [T][2] (8 bytes each, rounded
@@ -1275,7 +1308,22 @@ static size_t xhat_bytes(int64_t M, int64_t K) { return ((size_t)M * k_pad(K) * 
 static int64_t n_pad64(int64_t N) { return (N + 63) / 64 * 64; }
 static size_t wt_bytes(int64_t N, int64_t K) { return ((size_t)k_pad(K) * (n_pad64(N) / 2) + 255) / 256 * 256; }
 
+// The two backward products run in one launch when N % 8 == 0 and each of
+// them would split its tiles on a full device anyway. Workspace: [wt]
+// [x_hat], then the split workspaces of dX and dW, sized for their shares
+// of at most kMaxGrid workgroups.
+static bool pair_eligible(int64_t M, int64_t N, int64_t K) {
+  return N % 8 == 0 && split_pays(shape_of(GemmKind::kBwdDx, M, N, K), kMaxGrid) > 0 &&
+         split_pays(shape_of(GemmKind::kBwdDw, M, N, K), kMaxGrid) > 0;
+}
+static size_t pair_workspace_bound(int64_t M, int64_t N, int64_t K) {
+  const GemmShape g1 = shape_of(GemmKind::kBwdDx, M, N, K), g2 = shape_of(GemmKind::kBwdDw, M, N, K);
+  return wt_bytes(N, K) + xhat_bytes(M, K) + split_control_bytes(g1, kMaxGrid) +
+         split_control_bytes(g2, kMaxGrid) + 2 * (size_t)kMaxGrid * kPartialBytes;
+}
+
 size_t gemm_workspace_bytes(GemmKind kind, int64_t M, int64_t N, int64_t K) {
+  if (kind == GemmKind::kBwdPair) return pair_eligible(M, N, K) ? pair_workspace_bound(M, N, K) : 0;
   const GemmShape g = shape_of(kind, M, N, K);
   const size_t split = split_workspace(g, split_grid(g, kMaxGrid));
   if (kind == GemmKind::kBwdDw) return xhat_bytes(M, K) + split;
@@ -1309,6 +1357,38 @@ static uint64_t next_gen() {
     g = gen.fetch_add(1) & ((uint64_t(1) << 48) - 1);
   } while (g == 0);
   return g;
+}
+
+// The 8-workgroup columns (of kt) that run dX in a pair launch,
+// proportional to the two products' costs: their stages plus a per-tile
+// cost (pipeline fill, partial exchange, epilogue; about kPairTileCost
+// stages, measured at 4096x2560->6912); 0: no pair launch (the split knob
+// is set, or too few CUs). BITNET_PAIR_COLS=<k1> overrides (tuning knob).
+constexpr double kPairTileCost = 24.0;
+static int pair_columns(const GemmShape& g1, const GemmShape& g2, int cus, int* kt) {
+  if (getenv("BITNET_SPLIT_CTAS")) return 0;
+  *kt = (cus < kMaxGrid ? cus : kMaxGrid) / 8;
+  if (*kt < 2) return 0;
+  if (const char* e = getenv("BITNET_PAIR_COLS")) {
+    const long f = strtol(e, nullptr, 10);
+    if (f >= 1 && f < *kt) return (int)f;
+  }
+  const double w1 = (double)g1.tiles() * (g1.nstages + kPairTileCost);
+  const double w2 = (double)g2.tiles() * (g2.nstages + kPairTileCost);
+  const int k1 = (int)(*kt * w1 / (w1 + w2) + 0.5);
+  return k1 < 1 ? 1 : (k1 > *kt - 1 ? *kt - 1 : k1);
+}
+
+static SplitPlan split_plan(const GemmShape& g, int grid, void* ws) {
+  SplitPlan plan{};
+  plan.total = g.tiles() * g.nstages;
+  plan.tiles_i = (int)g.tiles_i;
+  plan.nstages = (int)g.nstages;
+  plan.grid = grid;
+  plan.gen = next_gen();
+  plan.counters = static_cast<uint64_t*>(ws);
+  plan.partials = reinterpret_cast<uint4*>(static_cast<char*>(ws) + split_control_bytes(g, grid));
+  return plan;
 }
 
 template <class MT, int MAP, class PL, class QL, class EP>
@@ -1346,6 +1426,20 @@ hipError_t launch_fwd(const int8_t* x_q, const float* s_x, const uint8_t* w_pack
   return run_gemm<MfmaI8, 1>(pl, ql, ep, shape_of(GemmKind::kFwd, M, N, K), ws, ws_bytes, stream);
 }
 
+static hipError_t launch_wt(const uint8_t* w_packed, int64_t N, int64_t K, uint8_t* wt, hipStream_t stream) {
+  const int64_t Kp = k_pad(K), Np = n_pad64(N);
+  wt_fp4_kernel<<<dim3((unsigned)(Kp / 64), (unsigned)((Np + 255) / 256)), 256, 0, stream>>>(w_packed, N, Kp, Np, wt);
+  return hipGetLastError();
+}
+
+static hipError_t launch_xhat(const int8_t* x_q, const float* s_x, int64_t M, int64_t K, uint16_t* xhat,
+                              hipStream_t stream) {
+  const int64_t Kp = k_pad(K);
+  const int64_t want = (M * (Kp / 16) + 255) / 256;
+  xhat_kernel<<<(int)(want < 4096 ? want : 4096), 256, 0, stream>>>(x_q, s_x, M, Kp, xhat);
+  return hipGetLastError();
+}
+
 hipError_t launch_bwd_dx(const uint16_t* dY, const uint8_t* w_packed, const float* gamma,
                          int64_t M, int64_t N, int64_t K, uint16_t* dX, void* ws, size_t ws_bytes,
                          hipStream_t stream) {
@@ -1355,8 +1449,7 @@ hipError_t launch_bwd_dx(const uint16_t* dY, const uint8_t* w_packed, const floa
   uint8_t* wt = static_cast<uint8_t*>(ws);
   void* split_ws = static_cast<char*>(ws) + wb;
   const size_t split_bytes = ws_bytes - wb;
-  wt_fp4_kernel<<<dim3((unsigned)(Kp / 64), (unsigned)((Np + 255) / 256)), 256, 0, stream>>>(w_packed, N, Kp, Np, wt);
-  if (hipError_t e = hipGetLastError()) return e;
+  if (hipError_t e = launch_wt(w_packed, N, K, wt, stream)) return e;
 
   const RowCodesLoader<CodesFp4Frags> pl{wt, Np / 2, Kp};
   Bf16Epilogue<false> ep{dX, gamma, K, M};
@@ -1378,10 +1471,7 @@ hipError_t launch_bwd_dw(const uint16_t* dY, const int8_t* x_q, const float* s_x
   uint16_t* xhat = static_cast<uint16_t*>(ws);
   void* split_ws = static_cast<char*>(ws) + xb;
   const size_t split_bytes = ws_bytes - xb;
-  const int64_t chunks = M * (Kp / 16);
-  const int64_t want = (chunks + 255) / 256;
-  xhat_kernel<<<(int)(want < 4096 ? want : 4096), 256, 0, stream>>>(x_q, s_x, M, Kp, xhat);
-  if (hipError_t e = hipGetLastError()) return e;
+  if (hipError_t e = launch_xhat(x_q, s_x, M, K, xhat, stream)) return e;
 
   const GemmShape g = shape_of(GemmKind::kBwdDw, M, N, K);
   if (N % 8 == 0) {
@@ -1401,6 +1491,43 @@ hipError_t launch_bwd_dw(const uint16_t* dY, const int8_t* x_q, const float* s_x
   Bf16Epilogue<false> ep{dW, nullptr, K, N};
   if (vec) return run_gemm<MfmaBf16, 0>(pl, RowTransposeBf16Loader<true, 5>{dY, N, M, N}, ep, g, split_ws, split_bytes, stream);
   return run_gemm<MfmaBf16, 0>(pl, RowTransposeBf16Loader<false, 5>{dY, N, M, N}, ep, g, split_ws, split_bytes, stream);
+}
+
+hipError_t launch_bwd_pair(const uint16_t* dY, const uint8_t* w_packed, const float* gamma, const int8_t* x_q,
+                           const float* s_x, int64_t M, int64_t N, int64_t K, uint16_t* dX, void* dW,
+                           bool dw_is_f32, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!pair_eligible(M, N, K) || ws == nullptr) return hipErrorNotSupported;
+  const GemmShape g1 = shape_of(GemmKind::kBwdDx, M, N, K), g2 = shape_of(GemmKind::kBwdDw, M, N, K);
+  int kt = 0;
+  const int k1 = pair_columns(g1, g2, device_cus(), &kt);
+  if (k1 == 0) return hipErrorNotSupported;
+  const int G1 = 8 * k1, G2 = 8 * (kt - k1);
+  const size_t wb = wt_bytes(N, K), xb = xhat_bytes(M, K);
+  const size_t s1 = split_workspace(g1, G1), s2 = split_workspace(g2, G2);
+  if (ws_bytes < wb + xb + s1 + s2) return hipErrorNotSupported;
+  char* base = static_cast<char*>(ws);
+  uint8_t* wt = reinterpret_cast<uint8_t*>(base);
+  uint16_t* xhat = reinterpret_cast<uint16_t*>(base + wb);
+  if (hipError_t e = launch_wt(w_packed, N, K, wt, stream)) return e;
+  if (hipError_t e = launch_xhat(x_q, s_x, M, K, xhat, stream)) return e;
+  const int64_t Kp = k_pad(K), Np = n_pad64(N);
+  const RowCodesLoader<CodesFp4Frags> p1{wt, Np / 2, Kp};
+  const CopyLoader<2, true> q1{reinterpret_cast<const char*>(dY), 2 * N, M, 2 * N};
+  const Bf16Epilogue<false> e1{dX, gamma, K, M};
+  const RowCopyBf16Loader<1> p2{xhat, Kp, M, Kp};
+  const RowCopyBf16Loader<5> q2{dY, N, M, N};
+  const SplitPlan plan1 = split_plan(g1, G1, base + wb + xb);
+  const SplitPlan plan2 = split_plan(g2, G2, base + wb + xb + s1);
+  if (dw_is_f32) {
+    gemm_pair_kernel<MfmaBf16, 1, RowCodesLoader<CodesFp4Frags>, CopyLoader<2, true>, Bf16Epilogue<false>, 0,
+                     RowCopyBf16Loader<1>, RowCopyBf16Loader<5>, Bf16Epilogue<true>>
+        <<<8 * kt, kThreads, 0, stream>>>(p1, q1, e1, plan1, p2, q2, Bf16Epilogue<true>{dW, nullptr, K, N}, plan2, k1);
+  } else {
+    gemm_pair_kernel<MfmaBf16, 1, RowCodesLoader<CodesFp4Frags>, CopyLoader<2, true>, Bf16Epilogue<false>, 0,
+                     RowCopyBf16Loader<1>, RowCopyBf16Loader<5>, Bf16Epilogue<false>>
+        <<<8 * kt, kThreads, 0, stream>>>(p1, q1, e1, plan1, p2, q2, Bf16Epilogue<false>{dW, nullptr, K, N}, plan2, k1);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace bitnet

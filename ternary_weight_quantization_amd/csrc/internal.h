@@ -27,7 +27,7 @@ hipError_t launch_act_quant(const uint16_t* x, int64_t M, int64_t K,
 // The three GEMMs. Each may split output tiles over workgroups (stream-K)
 // when its tile count leaves the CUs partly idle; that needs the workspace
 // gemm_workspace_bytes() gives (fewer bytes: whole tiles, no split).
-enum class GemmKind { kFwd, kBwdDx, kBwdDw };
+enum class GemmKind { kFwd, kBwdDx, kBwdDw, kBwdPair };
 size_t gemm_workspace_bytes(GemmKind kind, int64_t M, int64_t N, int64_t K);
 
 // INT8 forward GEMM with fused rescale (and optional int32 accumulators).
@@ -43,5 +43,14 @@ hipError_t launch_bwd_dx(const uint16_t* dY, const uint8_t* w_packed, const floa
 hipError_t launch_bwd_dw(const uint16_t* dY, const int8_t* x_q, const float* s_x,
                          int64_t M, int64_t N, int64_t K, void* dW, bool dw_is_f32,
                          void* ws, size_t ws_bytes, hipStream_t stream);
+
+// Both STE backward products in one launch, each on its share of the CUs
+// (N % 8 == 0). hipErrorNotSupported (nothing launched) when the shape,
+// the workspace or the device does not allow it; the caller then runs the
+// two products one after the other.
+hipError_t launch_bwd_pair(const uint16_t* dY, const uint8_t* w_packed, const float* gamma,
+                           const int8_t* x_q, const float* s_x, int64_t M, int64_t N, int64_t K,
+                           uint16_t* dX, void* dW, bool dw_is_f32, void* ws, size_t ws_bytes,
+                           hipStream_t stream);
 
 }  // namespace bitnet

@@ -65,7 +65,11 @@ def test_size_queries(L):
     assert L.bitlinear_fwd_workspace_bytes(64, 128, 256) == 0
     assert L.bitlinear_bwd_workspace_bytes(64, 128, 256) == 2 * 64 * 256
     tile = 64 * 256 * 16
-    assert L.bitlinear_bwd_workspace_bytes(4096, 6912, 2560) == 2 * 4096 * 2560 + 4352 + 2 * 256 * tile
+    # at 4096x2560->6912 the two backward products run in one launch: the
+    # fp4 transposed codes [Kp][N/2], x_hat, both products' counters and
+    # the partial tiles of their shares of the 256 workgroups
+    assert L.bitlinear_bwd_workspace_bytes(4096, 6912, 2560) == \
+        2560 * 6912 // 2 + 2 * 4096 * 2560 + 2560 + 4352 + 2 * 256 * tile
     assert L.bitlinear_fwd_workspace_bytes(4096, 2560, 6912) == 2560 + 2 * 256 * tile
     assert L.bitlinear_fwd_workspace_bytes(0, 4, 4) == 0
     for code in range(7):
