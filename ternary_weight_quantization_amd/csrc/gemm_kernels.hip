@@ -668,31 +668,34 @@ __global__ __launch_bounds__(256) void xhat_kernel(const int8_t* __restrict__ xq
 // the 64 nibbles n0 + 64(t%4) + 0..63 of row k0 + t/4 (32 bytes).
 __global__ __launch_bounds__(256) void wt_fp4_kernel(const uint8_t* __restrict__ packed, int64_t N, int64_t Kp,
                                                      int64_t Np, uint8_t* __restrict__ wt) {
-  __shared__ uint32_t tile[256][5];
+  // tile[word][n]: the 4 words of each row, word-major so that the words
+  // of 4 consecutive rows are one 16-byte read
+  __shared__ __attribute__((aligned(16))) uint32_t tile[4][256 + 4];
   const int t = threadIdx.x;
   const int64_t k0 = (int64_t)blockIdx.x * 64, n0 = (int64_t)blockIdx.y * 256;
   uint4 v = make_uint4(0u, 0u, 0u, 0u);
   if (n0 + t < N) v = *reinterpret_cast<const uint4*>(packed + (n0 + t) * (Kp / 4) + k0 / 4);
-  tile[t][0] = v.x;
-  tile[t][1] = v.y;
-  tile[t][2] = v.z;
-  tile[t][3] = v.w;
+  tile[0][t] = v.x;
+  tile[1][t] = v.y;
+  tile[2][t] = v.z;
+  tile[3][t] = v.w;
   __syncthreads();
+  // code j of a word: byte j % 4, bits 2(j / 4)
   const int kl = t >> 2, w = kl >> 4, j = kl & 15;
-  const int sh = 8 * (j & 3) + 2 * (j >> 2);
+  const uint32_t byte = j & 3, sh = 2 * (j >> 2);
+  const uint32_t gsel = byte | ((byte + 4) << 8);
   const int nb = 64 * (t & 3);
   if (n0 + nb >= Np) return;
+  // nibbles of rows n..n+3 (4 words) -> bytes 0 and 2 of the result
+  const auto quad = [&](uint4 a) {
+    const uint32_t g = perm(perm(a.w, a.z, gsel), perm(a.y, a.x, gsel), 0x05040100u);  // byte e: row n+e
+    const uint32_t f = perm(0u, 0x0A000200u, (g >> sh) & 0x03030303u);                 // code 0, 1, 3 -> fp4 0, 2, A
+    return f | (f >> 4);
+  };
+  const uint4* src = reinterpret_cast<const uint4*>(&tile[w][nb]);
   uint32_t o[8];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    uint32_t acc = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t c = (tile[nb + 8 * q + e][w] >> sh) & 3u;  // 0, 1 or 3
-      acc |= (((c & 1u) << 1) | ((c & 2u) << 2)) << (4 * e);
-    }
-    o[q] = acc;
-  }
+  for (int q = 0; q < 8; ++q) o[q] = perm(quad(src[2 * q + 1]), quad(src[2 * q]), 0x06040200u);
   uint4* dst = reinterpret_cast<uint4*>(wt + (k0 + kl) * (Np / 2) + (n0 + nb) / 2);
   dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
   dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
@@ -1224,10 +1227,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(PL pl, QL ql, EP ep, 
 
 // Two independent products in one launch, each on its own share of every
 // XCD: of the 8 * kt workgroups (one per CU, workgroup b on XCD b % 8),
-// those with b / 8 < k1 run product 1 (stream-K over 8 * k1 workgroups),
-// the others product 2 (8 * (kt - k1)). Each keeps the XCD-contiguous
-// numbering of its own workgroups. Used for the two STE backward products,
-// which otherwise would each pay their split tail and launch on their own.
+// those with b / 8 < k1 run product 1, the others product 2, each
+// stream-K over the first plan.grid (at most 8 * k1, resp. 8 * (kt - k1))
+// of its workgroups, numbered XCD-contiguously; the rest of a share has no
+// work. Used for the two STE backward products, which otherwise would each
+// pay their split tail and launch on their own.
 template <class MT, int MAP1, class PL1, class QL1, class EP1, int MAP2, class PL2, class QL2, class EP2>
 __global__ __launch_bounds__(kThreads, 1) void gemm_pair_kernel(PL1 pl1, QL1 ql1, EP1 ep1, SplitPlan plan1,
                                                                 PL2 pl2, QL2 ql2, EP2 ep2, SplitPlan plan2,
@@ -1237,10 +1241,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pair_kernel(PL1 pl1, QL1 ql1
   __shared__ __attribute__((aligned(16))) char smem[L1::kBytes > L2::kBytes ? L1::kBytes : L2::kBytes];
   __shared__ int s_flag;
   const int x = blockIdx.x % 8, k = blockIdx.x / 8;
-  if (k < k1)
-    gemm_body<MT, MAP1>(pl1, ql1, ep1, plan1, cta_order(8 * k + x, plan1.grid), smem, &s_flag);
-  else
-    gemm_body<MT, MAP2>(pl2, ql2, ep2, plan2, cta_order(8 * (k - k1) + x, plan2.grid), smem, &s_flag);
+  if (k < k1) {
+    const int b = 8 * k + x;
+    if (b < plan1.grid) gemm_body<MT, MAP1>(pl1, ql1, ep1, plan1, cta_order(b, plan1.grid), smem, &s_flag);
+  } else {
+    const int b = 8 * (k - k1) + x;
+    if (b < plan2.grid) gemm_body<MT, MAP2>(pl2, ql2, ep2, plan2, cta_order(b, plan2.grid), smem, &s_flag);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1501,7 +1508,13 @@ hipError_t launch_bwd_pair(const uint16_t* dY, const uint8_t* w_packed, const fl
   int kt = 0;
   const int k1 = pair_columns(g1, g2, device_cus(), &kt);
   if (k1 == 0) return hipErrorNotSupported;
-  const int G1 = 8 * k1, G2 = 8 * (kt - k1);
+  // every workgroup of a split needs a non-empty range, and more than about
+  // 4 pieces per tile do not pay
+  const auto cap = [](const GemmShape& g, int64_t G) {
+    const int64_t W = g.tiles() * g.nstages, P = 4 * g.tiles();
+    return (int)(G < W ? (G < P ? G : P) : (W < P ? W : P));
+  };
+  const int G1 = cap(g1, 8 * k1), G2 = cap(g2, 8 * (kt - k1));
   const size_t wb = wt_bytes(N, K), xb = xhat_bytes(M, K);
   const size_t s1 = split_workspace(g1, G1), s2 = split_workspace(g2, G2);
   if (ws_bytes < wb + xb + s1 + s2) return hipErrorNotSupported;
