@@ -43,7 +43,9 @@
 // is the same for P and Q of a GEMM, so the hardware's internal order of the
 // reduction index within a step does not matter.
 
+#include <algorithm>
 #include <atomic>
+#include <cmath>
 #include <cstdlib>
 #include <mutex>
 #include <random>
@@ -1173,16 +1175,19 @@ __device__ __forceinline__ void gemm_body(const PL& pl, const QL& ql, const EP& 
   const int wi = wave % kWavesI, wj = wave / kWavesI;
   const int prow0 = wi * kWTI, qrow0 = wj * kWTJ;
   if (plan.counters == nullptr) {
-    // one whole tile per workgroup
-    const int i0 = (v % plan.tiles_i) * kBI, j0 = (v / plan.tiles_i) * kBJ;
-    typename MT::Acc acc[kFI][kFJ];
+    // whole tiles: v, v + G, v + 2G, ... (one each when G = T)
+    const int T = (int)(plan.total / plan.nstages);
+    for (int t = v; t < T; t += plan.grid) {
+      const int i0 = (t % plan.tiles_i) * kBI, j0 = (t / plan.tiles_i) * kBJ;
+      typename MT::Acc acc[kFI][kFJ];
 #pragma unroll
-    for (int fi = 0; fi < kFI; ++fi)
+      for (int fi = 0; fi < kFI; ++fi)
 #pragma unroll
-      for (int fj = 0; fj < kFJ; ++fj) zero_acc(acc[fi][fj]);
-    const typename EP::Pre pre = ep.prefetch(j0 + qrow0, lane);
-    run_stages<MT, MAP>(pl, ql, smem, acc, i0, j0, 0, plan.nstages, prow0, qrow0, lane, nullptr, 0);
-    ep.store(acc, pre, i0 + prow0, j0 + qrow0, lane, smem + wave * EP::kWaveLds);
+        for (int fj = 0; fj < kFJ; ++fj) zero_acc(acc[fi][fj]);
+      const typename EP::Pre pre = ep.prefetch(j0 + qrow0, lane);
+      run_stages<MT, MAP>(pl, ql, smem, acc, i0, j0, 0, plan.nstages, prow0, qrow0, lane, nullptr, 0);
+      ep.store(acc, pre, i0 + prow0, j0 + qrow0, lane, smem + wave * EP::kWaveLds);
+    }
     return;
   }
 
@@ -1366,12 +1371,30 @@ static uint64_t next_gen() {
   return g;
 }
 
-// The 8-workgroup columns (of kt) that run dX in a pair launch,
-// proportional to the two products' costs: their stages plus a per-tile
-// cost (pipeline fill, partial exchange, epilogue; about kPairTileCost
-// stages, measured at 4096x2560->6912); 0: no pair launch (the split knob
-// is set, or too few CUs). BITNET_PAIR_COLS=<k1> overrides (tuning knob).
-constexpr double kPairTileCost = 24.0;
+// Cost model of one product on G workgroups, in dX stage times (measured
+// at 4096x2560->6912): a dW stage costs about 1.07 of a dX stage, a tile's
+// pipeline fill and epilogue about 5.4 stages, and each piece of a split
+// range about 10 stages (fill, partial exchange, epilogue). Whole tiles
+// taken in turn cost ceil(T/G) tiles; a split costs W/G stages plus its
+// pieces (about W/(G*S) + 1 per workgroup).
+constexpr double kTileCost = 5.4, kPieceCost = 10.0;
+struct PairCost {
+  double t;
+  bool split;
+};
+static PairCost product_cost(const GemmShape& g, int64_t G, double stage) {
+  const double T = (double)g.tiles(), S = (double)g.nstages, W = T * S;
+  const double whole = std::ceil(T / (double)G) * (S * stage + kTileCost);
+  const int64_t Gs = G < 4 * g.tiles() ? G : 4 * g.tiles();
+  const double split = W / (double)Gs * stage + (W / ((double)Gs * S) + 1.0) * kPieceCost;
+  return split < whole ? PairCost{split, true} : PairCost{whole, false};
+}
+constexpr double kDwStageCost = 1.07;
+
+// The 8-workgroup columns (of kt) that run dX in a pair launch: the k1 that
+// minimizes the slower product's modelled cost; 0: no pair launch (the
+// split knob is set, or too few CUs). BITNET_PAIR_COLS=<k1> overrides
+// (tuning knob).
 static int pair_columns(const GemmShape& g1, const GemmShape& g2, int cus, int* kt) {
   if (getenv("BITNET_SPLIT_CTAS")) return 0;
   *kt = (cus < kMaxGrid ? cus : kMaxGrid) / 8;
@@ -1380,10 +1403,16 @@ static int pair_columns(const GemmShape& g1, const GemmShape& g2, int cus, int* 
     const long f = strtol(e, nullptr, 10);
     if (f >= 1 && f < *kt) return (int)f;
   }
-  const double w1 = (double)g1.tiles() * (g1.nstages + kPairTileCost);
-  const double w2 = (double)g2.tiles() * (g2.nstages + kPairTileCost);
-  const int k1 = (int)(*kt * w1 / (w1 + w2) + 0.5);
-  return k1 < 1 ? 1 : (k1 > *kt - 1 ? *kt - 1 : k1);
+  int best = 1;
+  double best_t = 1e300;
+  for (int k1 = 1; k1 < *kt; ++k1) {
+    const double t = std::max(product_cost(g1, 8 * k1, 1.0).t, product_cost(g2, 8 * (*kt - k1), kDwStageCost).t);
+    if (t < best_t) {
+      best_t = t;
+      best = k1;
+    }
+  }
+  return best;
 }
 
 static SplitPlan split_plan(const GemmShape& g, int grid, void* ws) {
@@ -1395,6 +1424,16 @@ static SplitPlan split_plan(const GemmShape& g, int grid, void* ws) {
   plan.gen = next_gen();
   plan.counters = static_cast<uint64_t*>(ws);
   plan.partials = reinterpret_cast<uint4*>(static_cast<char*>(ws) + split_control_bytes(g, grid));
+  return plan;
+}
+
+// Whole tiles taken in turn by `grid` workgroups (no split).
+static SplitPlan whole_plan(const GemmShape& g, int grid) {
+  SplitPlan plan{};
+  plan.total = g.tiles() * g.nstages;
+  plan.tiles_i = (int)g.tiles_i;
+  plan.nstages = (int)g.nstages;
+  plan.grid = grid;
   return plan;
 }
 
@@ -1514,9 +1553,14 @@ hipError_t launch_bwd_pair(const uint16_t* dY, const uint8_t* w_packed, const fl
     const int64_t W = g.tiles() * g.nstages, P = 4 * g.tiles();
     return (int)(G < W ? (G < P ? G : P) : (W < P ? W : P));
   };
-  const int G1 = cap(g1, 8 * k1), G2 = cap(g2, 8 * (kt - k1));
+  // each product splits its tiles only when the cost model says that beats
+  // whole tiles taken in turn on its share of the CUs
+  const int64_t share1 = 8 * k1, share2 = 8 * (kt - k1);
+  const bool sk1 = product_cost(g1, share1, 1.0).split, sk2 = product_cost(g2, share2, kDwStageCost).split;
+  const int G1 = sk1 ? cap(g1, share1) : (int)(g1.tiles() < share1 ? g1.tiles() : share1);
+  const int G2 = sk2 ? cap(g2, share2) : (int)(g2.tiles() < share2 ? g2.tiles() : share2);
   const size_t wb = wt_bytes(N, K), xb = xhat_bytes(M, K);
-  const size_t s1 = split_workspace(g1, G1), s2 = split_workspace(g2, G2);
+  const size_t s1 = sk1 ? split_workspace(g1, G1) : 0, s2 = sk2 ? split_workspace(g2, G2) : 0;
   if (ws_bytes < wb + xb + s1 + s2) return hipErrorNotSupported;
   char* base = static_cast<char*>(ws);
   uint8_t* wt = reinterpret_cast<uint8_t*>(base);
@@ -1529,8 +1573,8 @@ hipError_t launch_bwd_pair(const uint16_t* dY, const uint8_t* w_packed, const fl
   const Bf16Epilogue<false> e1{dX, gamma, K, M};
   const RowCopyBf16Loader<1> p2{xhat, Kp, M, Kp};
   const RowCopyBf16Loader<5> q2{dY, N, M, N};
-  const SplitPlan plan1 = split_plan(g1, G1, base + wb + xb);
-  const SplitPlan plan2 = split_plan(g2, G2, base + wb + xb + s1);
+  const SplitPlan plan1 = sk1 ? split_plan(g1, G1, base + wb + xb) : whole_plan(g1, G1);
+  const SplitPlan plan2 = sk2 ? split_plan(g2, G2, base + wb + xb + s1) : whole_plan(g2, G2);
   if (dw_is_f32) {
     gemm_pair_kernel<MfmaBf16, 1, RowCodesLoader<CodesFp4Frags>, CopyLoader<2, true>, Bf16Epilogue<false>, 0,
                      RowCopyBf16Loader<1>, RowCopyBf16Loader<5>, Bf16Epilogue<true>>
