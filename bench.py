@@ -63,7 +63,7 @@ KERNEL_MATCH = {
     "ternarize_pack": ["absmean_partials_kernel", "ternarize_pack_kernel"],
     "act_quant": ["act_quant"],
     "fwd_i8": ["MfmaI8"],
-    "bwd_bf16": ["wt_fp4_kernel", "xhat_kernel", "gemm_pair_kernel"],
+    "bwd_bf16": ["bwd_prep_kernel", "wt_fp4_kernel", "xhat_kernel", "gemm_pair_kernel"],
 }
 COPY_BYTES = 256 << 20
 

@@ -636,12 +636,11 @@ struct RowCopyBf16Loader {
 // per output tile column. Thread t converts 16 int8 of row m: each byte is
 // biased to [1, 255] so that u*r - 128r = x_q*r exactly before the single
 // rounding of the fma.
-__global__ __launch_bounds__(256) void xhat_kernel(const int8_t* __restrict__ xq, const float* __restrict__ s,
-                                                   int64_t M, int64_t Kp, uint16_t* __restrict__ xhat) {
+__device__ __forceinline__ void xhat_blocks(const int8_t* __restrict__ xq, const float* __restrict__ s, int64_t M,
+                                            int64_t Kp, uint16_t* __restrict__ xhat, int b, int nb) {
   const int64_t cpr = Kp / 16;  // 16-byte chunks per row
   const int64_t total = M * cpr;
-  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < total;
-       c += (int64_t)gridDim.x * blockDim.x) {
+  for (int64_t c = (int64_t)b * 256 + threadIdx.x; c < total; c += (int64_t)nb * 256) {
     const int64_t m = c / cpr;
     const float r = s[m] / 127.0f;
     const float bias = -128.0f * r;
@@ -660,6 +659,11 @@ __global__ __launch_bounds__(256) void xhat_kernel(const int8_t* __restrict__ xq
   }
 }
 
+__global__ __launch_bounds__(256) void xhat_kernel(const int8_t* __restrict__ xq, const float* __restrict__ s,
+                                                   int64_t M, int64_t Kp, uint16_t* __restrict__ xhat) {
+  xhat_blocks(xq, s, M, Kp, xhat, blockIdx.x, gridDim.x);
+}
+
 // dX P: the ternary codes transposed to [k][n] as fp4 nibbles (the layout
 // CodesFp4Frags reads: n even in the low nibble, +1 = 0x2, -1 = 0xA, 0 =
 // 0x0), rows of Np/2 bytes with Np = N rounded up to 64 (zero nibbles past
@@ -668,13 +672,13 @@ __global__ __launch_bounds__(256) void xhat_kernel(const int8_t* __restrict__ xq
 // 256 n: thread t loads the 64 codes k0..k0+63 of row n0 + t (16 bytes, 4
 // planar words; code j of a word sits at bit 8(j%4) + 2(j/4)), then writes
 // the 64 nibbles n0 + 64(t%4) + 0..63 of row k0 + t/4 (32 bytes).
-__global__ __launch_bounds__(256) void wt_fp4_kernel(const uint8_t* __restrict__ packed, int64_t N, int64_t Kp,
-                                                     int64_t Np, uint8_t* __restrict__ wt) {
+__device__ __forceinline__ void wt_fp4_block(const uint8_t* __restrict__ packed, int64_t N, int64_t Kp, int64_t Np,
+                                             uint8_t* __restrict__ wt, int bx, int by) {
   // tile[word][n]: the 4 words of each row, word-major so that the words
   // of 4 consecutive rows are one 16-byte read
   __shared__ __attribute__((aligned(16))) uint32_t tile[4][256 + 4];
   const int t = threadIdx.x;
-  const int64_t k0 = (int64_t)blockIdx.x * 64, n0 = (int64_t)blockIdx.y * 256;
+  const int64_t k0 = (int64_t)bx * 64, n0 = (int64_t)by * 256;
   uint4 v = make_uint4(0u, 0u, 0u, 0u);
   if (n0 + t < N) v = *reinterpret_cast<const uint4*>(packed + (n0 + t) * (Kp / 4) + k0 / 4);
   tile[0][t] = v.x;
@@ -701,6 +705,25 @@ __global__ __launch_bounds__(256) void wt_fp4_kernel(const uint8_t* __restrict__
   uint4* dst = reinterpret_cast<uint4*>(wt + (k0 + kl) * (Np / 2) + (n0 + nb) / 2);
   dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
   dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+}
+
+__global__ __launch_bounds__(256) void wt_fp4_kernel(const uint8_t* __restrict__ packed, int64_t N, int64_t Kp,
+                                                     int64_t Np, uint8_t* __restrict__ wt) {
+  wt_fp4_block(packed, N, Kp, Np, wt, blockIdx.x, blockIdx.y);
+}
+
+// Both backward pre-passes in one launch: the first wt_bx * wt_by blocks
+// transpose the codes, the other xhat_nb blocks build x_hat (the two are
+// independent, and the transpose is ALU-heavy while x_hat is HBM-heavy).
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const uint8_t* __restrict__ packed, int64_t N, int64_t Kp,
+                                                       int64_t Np, uint8_t* __restrict__ wt, int wt_bx, int wt_by,
+                                                       const int8_t* __restrict__ xq, const float* __restrict__ s,
+                                                       int64_t M, uint16_t* __restrict__ xhat, int xhat_nb) {
+  const int b = blockIdx.x, nwt = wt_bx * wt_by;
+  if (b < nwt)
+    wt_fp4_block(packed, N, Kp, Np, wt, b % wt_bx, b / wt_bx);
+  else
+    xhat_blocks(xq, s, M, Kp, xhat, b - nwt, xhat_nb);
 }
 
 // ---------------------------------------------------------------------------
@@ -1565,9 +1588,15 @@ hipError_t launch_bwd_pair(const uint16_t* dY, const uint8_t* w_packed, const fl
   char* base = static_cast<char*>(ws);
   uint8_t* wt = reinterpret_cast<uint8_t*>(base);
   uint16_t* xhat = reinterpret_cast<uint16_t*>(base + wb);
-  if (hipError_t e = launch_wt(w_packed, N, K, wt, stream)) return e;
-  if (hipError_t e = launch_xhat(x_q, s_x, M, K, xhat, stream)) return e;
   const int64_t Kp = k_pad(K), Np = n_pad64(N);
+  {
+    const int wt_bx = (int)(Kp / 64), wt_by = (int)((Np + 255) / 256);
+    const int64_t want = (M * (Kp / 16) + 255) / 256;
+    const int xhat_nb = (int)(want < 4096 ? want : 4096);
+    bwd_prep_kernel<<<wt_bx * wt_by + xhat_nb, 256, 0, stream>>>(w_packed, N, Kp, Np, wt, wt_bx, wt_by, x_q, s_x, M,
+                                                                 xhat, xhat_nb);
+    if (hipError_t e = hipGetLastError()) return e;
+  }
   const RowCodesLoader<CodesFp4Frags> p1{wt, Np / 2, Kp};
   const CopyLoader<2, true> q1{reinterpret_cast<const char*>(dY), 2 * N, M, 2 * N};
   const Bf16Epilogue<false> e1{dX, gamma, K, M};
