@@ -77,8 +77,10 @@ size_t bitnet_ternarize_workspace_bytes(int64_t N, int64_t K);
  * output tiles over several workgroups so that all CUs stay busy: 16 bytes
  * of tagged counters per 256 x 256 output tile and 256 KiB of partial sums
  * per workgroup piece, at most about 128 MiB. The contents need no
- * initialization; a workspace must not be shared by calls that may run at
- * the same time (calls on one stream may share it). bitlinear_bwd's size
+ * initialization, and the calls leave the counters cleared, so a call
+ * captured into a HIP graph may be replayed any number of times; a
+ * workspace must not be shared by calls that may run at the same time
+ * (calls on one stream may share it). bitlinear_bwd's size
  * covers both of its products, which run one after the other. Each product
  * first builds a transient operand at the start of the workspace: dX the
  * ternary codes transposed to fp4 [Kp][Np/2] (Kp*Np/2 bytes, Np = N rounded

@@ -943,10 +943,12 @@ __device__ __forceinline__ int64_t piece_slot(const SplitPlan& p, int v, int t) 
 
 // Tagged counters: a 64-bit word gen << 16 | count. A word written by
 // another launch (another tag) counts as zero, so the counters never need
-// clearing between launches. The counters only order the exchange of
-// partial tiles, whose stores and loads are device-coherent and complete
-// (wait_vmem) before the counter moves, so relaxed device-scope atomics
-// suffice and no cache-wide fence is needed.
+// clearing before a launch; the last piece of a tile clears its two words
+// once they are no longer used, so that a launch repeated with the same tag
+// (a captured graph replayed) also starts from zero. The counters only
+// order the exchange of partial tiles, whose stores and loads are
+// device-coherent and complete (wait_vmem) before the counter moves, so
+// relaxed device-scope atomics suffice and no cache-wide fence is needed.
 constexpr uint64_t kCountMask = 0xFFFF;
 
 __device__ __forceinline__ uint32_t tagged_arrive(uint64_t* c, uint64_t gen) {
@@ -1155,7 +1157,14 @@ __device__ __forceinline__ bool finish_piece(const SplitPlan& p, typename MT::Ac
     asm volatile("" ::: "memory");  // keep the stores ahead of the next piece's loads
     return false;
   }
-  if (tid == 0) wait_published(cnt + 1, p.gen, (uint32_t)(n - 1));
+  if (tid == 0) {
+    wait_published(cnt + 1, p.gen, (uint32_t)(n - 1));
+    // Every piece has arrived and published: nothing else touches this
+    // tile's counters in this launch. Clearing them lets a later launch
+    // with the same tag (a replay of a captured graph) count from zero.
+    __hip_atomic_store(cnt, uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(cnt + 1, uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   __syncthreads();
   constexpr int kBatch = 16;
 #pragma unroll

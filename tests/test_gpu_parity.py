@@ -265,3 +265,60 @@ def test_stack_c4_chain():
         assert np.array_equal(g["dW"], bf(host_bf16_bits(L.weight.grad)))
         assert np.array_equal(g["dX"], bf(host_bf16_bits(acts[i].grad)))
         check_layer(inp, g, full=False, seed=i)
+
+
+@pytest.mark.parametrize("M,K,N,split", [
+    (300, 1000, 777, 13),     # split tiles in all three GEMMs, separate launches
+    (1024, 2560, 1536, None),  # dX and dW in one launch, both split
+])
+def test_graph_replays_match_eager(M, K, N, split, monkeypatch):
+    """The four calls captured once into a HIP graph and replayed three
+    times, with eager calls on the same workspaces between the replays: each
+    replay writes the eager outputs bit for bit (the split-tile counters are
+    left cleared by every launch, so a replay with the captured launch tag
+    counts its pieces from zero)."""
+    if split is not None:
+        monkeypatch.setenv("BITNET_SPLIT_CTAS", str(split))
+    inp = WL.custom_inputs(M, K, N, seed=M + N, w_dtype="bf16")
+    note(f"graph replays M={M} K={K} N={N} split={split}")
+    from ternary_weight_quantization_amd import binding as B
+    dev = torch.device("cuda")
+    Kp = B.bitnet_k_pad(K)
+    W, x, dY = dev_bf16(inp["W"]), dev_bf16(inp["x"]), dev_bf16(inp["dY"])
+    t = dict(w_packed=torch.empty((N, Kp // 4), dtype=torch.uint8, device=dev),
+             gamma=torch.empty((1,), dtype=torch.float32, device=dev),
+             x_q=torch.empty((M, Kp), dtype=torch.int8, device=dev),
+             s_x=torch.empty((M,), dtype=torch.float32, device=dev),
+             y=torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+             acc=torch.empty((M, N), dtype=torch.int32, device=dev),
+             dX=torch.empty((M, K), dtype=torch.bfloat16, device=dev),
+             dW=torch.empty((N, K), dtype=torch.bfloat16, device=dev))
+    ws_t = torch.empty((B.bitnet_ternarize_workspace_bytes(N, K),), dtype=torch.uint8, device=dev)
+    ws_f = torch.empty((max(B.bitlinear_fwd_workspace_bytes(M, N, K), 256),), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty((max(B.bitlinear_bwd_workspace_bytes(M, N, K), 256),), dtype=torch.uint8, device=dev)
+
+    def step():
+        B.bitnet_ternarize_pack(W, t["w_packed"], t["gamma"], ws_t)
+        B.bitnet_act_quant(x, t["x_q"], t["s_x"])
+        B.bitlinear_fwd(t["x_q"], t["s_x"], t["w_packed"], t["gamma"], K, t["y"], t["acc"], workspace=ws_f)
+        B.bitlinear_bwd(dY, t["x_q"], t["s_x"], t["w_packed"], t["gamma"], K, dX=t["dX"], dW=t["dW"],
+                        workspace=ws_b)
+
+    step()
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in t.items()}
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for r in range(3):
+        for v in t.values():
+            v.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, v in t.items():
+            assert torch.equal(v, ref[k]), (r, k)
+        step()  # eager calls on the same workspaces between replays
+        torch.cuda.synchronize()
+        for k in ("y", "dX", "dW"):
+            assert torch.equal(t[k], ref[k]), ("eager", r, k)
