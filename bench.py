@@ -335,6 +335,25 @@ def main():
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
 
+    # The backward with dW as 1-bit signs for a sign-based optimiser (dX and
+    # the dW signs in one call; no bf16 dW is written), timed per call like
+    # the step's calls. Not part of the step.
+    for s in sets:
+        s["dW_sign1"] = torch.empty((N, Kp // 8), dtype=torch.uint8, device=dev)
+
+    def bwd_sign1(s):
+        B.bitlinear_bwd(s["dY"], s["x_q"], s["s_x"], s["w_packed"], s["gamma"], K, dX=s["dX"], dW=s["dW_sign1"])
+
+    for i in range(args.warmup):
+        bwd_sign1(sets[i % len(sets)])
+    ev1 = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        ev1[i][0].record()
+        bwd_sign1(sets[i % len(sets)])
+        ev1[i][1].record()
+    torch.cuda.synchronize()
+    sign1_ms = float(np.mean([a.elapsed_time(b) for a, b in ev1]))
+
     gemm_ops = 2.0 * M * N * K
     tops = 3 * gemm_ops / (ms_per_step * 1e-3) / 1e12
     # roofline of each kernel (algorithmic work per launch)
@@ -377,6 +396,11 @@ def main():
         "roofline": roofline,
         "kernels": {n: {"ms": round(f["ms"], 4), "frac": round(f["frac"], 4), "bound": f["bound"],
                         "achieved": round(f["achieved"], 2), "unit": f["unit"]} for n, f in fracs.items()},
+        "extra_calls": {"bwd_sign1": {
+            "ms": round(sign1_ms, 4), "bound": "mfma", "unit": "TFLOP/s",
+            "achieved": round(2 * gemm_ops / 1e12 / (sign1_ms * 1e-3), 2),
+            "frac": round(2 * gemm_ops / 1e12 / (sign1_ms * 1e-3) / PEAK_BF16_TFLOPS, 4),
+            "dW_bytes_written": N * Kp // 8}},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -59,7 +59,8 @@ typedef enum {
 
 typedef enum {
     BITNET_BF16 = 0,
-    BITNET_F32 = 1
+    BITNET_F32 = 1,
+    BITNET_SIGN1 = 2  /* bitlinear_bwd's dW only: 1-bit signs (see there) */
 } bitnet_dtype;
 
 /* Human-readable name of a status code (static storage). */
@@ -175,6 +176,13 @@ bitnet_status bitlinear_fwd(const int8_t* x_q, const float* s_x,
  * dX        [M][K] bf16 bits output, or NULL to skip the dX GEMM.
  * dW        [N][K] output in dW_dtype (BITNET_BF16 bits or BITNET_F32), or
  *           NULL to skip the dW GEMM. At least one of dX, dW is non-NULL.
+ *           With BITNET_SIGN1, dW is [N][Kp/8] bytes of 1-bit signs for a
+ *           sign-based optimiser ("1BitTraining.md", closing paragraphs: the
+ *           identity-STE gradient has the sign of the gradient with respect
+ *           to the quantised weight, so only 1 bit per weight is needed):
+ *           bit j of byte b of row n is 1 iff the fp32 sum for dW[n, 8b + j]
+ *           is negative, 0 otherwise (zero sums included); bits of k >= K
+ *           are 0. No bf16 or f32 dW is written.
  * workspace device scratch of bitlinear_bwd_workspace_bytes(M, N, K) bytes
  *           (NULL allowed when that is 0); clobbered.
  */

@@ -22,6 +22,8 @@ from .bitlinear_oracle import (  # noqa: F401
     w_hat,
     x_hat,
     backward,
+    sign1_pack,
+    sign1_unpack,
     layer_fwd_bwd,
     acc_elements,
     dx_elements,

@@ -280,6 +280,41 @@ def layer_fwd_bwd(x, w, dY, with_backward=True):
 
 
 # ---------------------------------------------------------------------------
+# 1-bit sign gradients
+# ---------------------------------------------------------------------------
+
+def sign1_pack(dW, Kp=None):
+    """1-bit signs of the weight gradient dW [N, K], packed into bytes
+    [N, Kp/8], for a sign-based optimiser ("1BitTraining.md", the closing
+    paragraphs: the identity-STE gradient has the sign of the gradient with
+    respect to the quantised weight, so a device holding only the 2-bit
+    weights can stream 1-bit gradients). The page's check uses a
+    three-valued sign; with one bit, zero goes with the non-negative side
+    (the reading taken): the bit of dW[n, k] is 1 iff dW[n, k] < 0. Bit j of
+    byte b of row n holds k = 8b + j; columns k >= K are 0."""
+    d = np.asarray(dW, dtype=np.float64)
+    N, K = d.shape
+    if Kp is None:
+        Kp = k_pad(K)
+    neg = np.zeros((N, Kp), dtype=np.int64)
+    neg[:, :K] = d < 0
+    bits = neg.reshape(N, Kp // 8, 8)
+    out = np.zeros((N, Kp // 8), dtype=np.int64)
+    for j in range(8):
+        out |= bits[..., j] << j
+    return out.astype(np.uint8)
+
+
+def sign1_unpack(packed, K):
+    """Inverse of ``sign1_pack`` up to zeros: bytes [N, Kp/8] -> int8 [N, K]
+    with -1 where the bit is set and +1 elsewhere."""
+    p = np.asarray(packed, dtype=np.uint8).astype(np.int64)
+    N = p.shape[0]
+    bits = np.stack([(p >> j) & 1 for j in range(8)], axis=-1).reshape(N, -1)[:, :K]
+    return np.where(bits == 1, -1, 1).astype(np.int8)
+
+
+# ---------------------------------------------------------------------------
 # Single elements, for sampled checks at full size
 # ---------------------------------------------------------------------------
 

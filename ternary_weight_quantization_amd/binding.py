@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(HERE, "libbitnet.so")
 BITNET_OK = 0
 BITNET_BF16 = 0
 BITNET_F32 = 1
+BITNET_SIGN1 = 2
 
 _lib = None
 
@@ -188,7 +189,9 @@ def bitlinear_fwd(x_q, s_x, w_packed, gamma, K, y, acc_out=None, workspace=None,
 
 
 def bitlinear_bwd(dY, x_q, s_x, w_packed, gamma, K, dX=None, dW=None, workspace=None, stream=None):
-    """STE backward: dX [M, K] bf16 and/or dW [N, K] (bf16 or float32)."""
+    """STE backward: dX [M, K] bf16 and/or dW [N, K] (bf16 or float32), or
+    dW as 1-bit signs (uint8 [N, Kp/8]; bit j of byte b of row n set iff
+    dW[n, 8b + j] < 0)."""
     M, N = dY.shape
     Kp = bitnet_k_pad(K)
     _need(dY, torch.bfloat16, (M, N), "dY")
@@ -200,11 +203,15 @@ def bitlinear_bwd(dY, x_q, s_x, w_packed, gamma, K, dX=None, dW=None, workspace=
     if dW is not None:
         _need(x_q, torch.int8, (M, Kp), "x_q")
         _need(s_x, torch.float32, (M,), "s_x")
-        if dW.dtype == torch.float32:
-            dw_dtype = BITNET_F32
-        _need(dW, dW.dtype, (N, int(K)), "dW")
-        if dW.dtype not in (torch.bfloat16, torch.float32):
-            raise TypeError("dW: expected bfloat16 or float32")
+        if dW.dtype == torch.uint8:
+            dw_dtype = BITNET_SIGN1
+            _need(dW, torch.uint8, (N, Kp // 8), "dW")
+        else:
+            if dW.dtype == torch.float32:
+                dw_dtype = BITNET_F32
+            _need(dW, dW.dtype, (N, int(K)), "dW")
+            if dW.dtype not in (torch.bfloat16, torch.float32):
+                raise TypeError("dW: expected bfloat16, float32 or uint8 (1-bit signs)")
     if workspace is None:
         workspace = _workspace(bitlinear_bwd_workspace_bytes(M, N, K), dY, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

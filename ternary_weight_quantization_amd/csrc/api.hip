@@ -140,7 +140,7 @@ bitnet_status bitlinear_bwd(const uint16_t* dY, const int8_t* x_q, const float* 
   if (!dX && !dW) return BITNET_ERR_NULL;
   if (dX && (!w_packed || !gamma)) return BITNET_ERR_NULL;
   if (dW && (!x_q || !s_x)) return BITNET_ERR_NULL;
-  if (dW && dW_dtype != BITNET_BF16 && dW_dtype != BITNET_F32) return BITNET_ERR_DTYPE;
+  if (dW && dW_dtype != BITNET_BF16 && dW_dtype != BITNET_F32 && dW_dtype != BITNET_SIGN1) return BITNET_ERR_DTYPE;
   if (bitnet_status st = check_gemm_sizes(M, N, K)) return st;
   if (bitnet_status st = check_gemm_ranges(M, N, K, dW != nullptr, dX != nullptr, true, K)) return st;
   if (workspace_bytes < bitlinear_bwd_workspace_bytes(M, N, K)) return BITNET_ERR_WORKSPACE;
@@ -150,8 +150,11 @@ bitnet_status bitlinear_bwd(const uint16_t* dY, const int8_t* x_q, const float* 
   if (dX && (!aligned(w_packed, 16) || !aligned(gamma, 4) || !aligned(dX, 16))) return BITNET_ERR_ALIGN;
   if (dW && (!aligned(x_q, 16) || !aligned(s_x, 16) || !aligned(dW, 16))) return BITNET_ERR_ALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  const bitnet::DwOut dw_out = dW_dtype == BITNET_F32     ? bitnet::DwOut::kF32
+                               : dW_dtype == BITNET_SIGN1 ? bitnet::DwOut::kSign1
+                                                          : bitnet::DwOut::kBf16;
   if (dX && dW) {
-    const hipError_t e = bitnet::launch_bwd_pair(dY, w_packed, gamma, x_q, s_x, M, N, K, dX, dW, dW_dtype == BITNET_F32,
+    const hipError_t e = bitnet::launch_bwd_pair(dY, w_packed, gamma, x_q, s_x, M, N, K, dX, dW, dw_out,
                                                  workspace, workspace_bytes, st);
     if (e != hipErrorNotSupported) return from_hip(e);
   }
@@ -159,8 +162,7 @@ bitnet_status bitlinear_bwd(const uint16_t* dY, const int8_t* x_q, const float* 
     if (hipError_t e = bitnet::launch_bwd_dx(dY, w_packed, gamma, M, N, K, dX, workspace, workspace_bytes, st)) return from_hip(e);
   }
   if (dW) {
-    if (hipError_t e = bitnet::launch_bwd_dw(dY, x_q, s_x, M, N, K, dW, dW_dtype == BITNET_F32, workspace,
-                                                  workspace_bytes, st))
+    if (hipError_t e = bitnet::launch_bwd_dw(dY, x_q, s_x, M, N, K, dW, dw_out, workspace, workspace_bytes, st))
       return from_hip(e);
   }
   return BITNET_OK;

@@ -892,6 +892,50 @@ struct Bf16Epilogue {
   }
 };
 
+// dW as 1-bit signs for sign-based optimisers ("1BitTraining.md", closing
+// paragraphs: the identity-STE gradient has the sign of the gradient with
+// respect to the quantised weight, so a sign optimiser needs only 1 bit per
+// weight). out [J][Ip/8] bytes (Ip = Kp): bit b of byte c of row j is set
+// iff the fp32 sum for element (j, 8c + b) is negative (zero sums, and the
+// zero sums of the padding columns, give 0). Nothing is staged: the lane of
+// row j = l % 32 holds, per fragment fi and group g, the sums of
+// i = 32fi + 8g + 4h + 0..3 (h = l / 32). Their flags form a nibble, and the
+// nibbles of lanes l and l ^ 32 make the bytes of i = 32fi + 8g .. +7; lane
+// half h then stores the 8 bytes of i = 64h .. 64h + 63 of the wave tile.
+struct Sign1Epilogue {
+  uint8_t* out;
+  int64_t Ip, J;  // Kp, N
+
+  struct Pre {};
+  static constexpr int kWaveLds = 0;
+  __device__ __forceinline__ Pre prefetch(int, int) const { return Pre{}; }
+  __device__ __forceinline__ void store(MfmaBf16::Acc (&acc)[kFI][kFJ], const Pre&, int i0, int j0, int lane,
+                                        char*) const {
+    const int h = lane >> 5;
+#pragma unroll
+    for (int fj = 0; fj < kFJ; ++fj) {
+      uint32_t word[kFI];
+#pragma unroll
+      for (int fi = 0; fi < kFI; ++fi) {
+        uint32_t mine = 0;  // flag of i = 32fi + 8g + 4h + e at bit 4g + e
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mine |= (acc[fi][fj][r] < 0.0f ? 1u : 0u) << r;
+        const uint32_t other = (uint32_t)__shfl_xor((int)mine, 32, kWave);
+        const uint32_t lo = h ? other : mine, hi = h ? mine : other;
+        uint32_t w = 0;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) w |= (((lo >> (4 * g)) & 0xFu) | (((hi >> (4 * g)) & 0xFu) << 4)) << (8 * g);
+        word[fi] = w;
+      }
+      const int64_t j = j0 + 32 * fj + (lane & 31);
+      const int64_t i = i0 + 64 * h;
+      if (j < J && i < Ip)
+        *reinterpret_cast<uint2*>(out + j * (Ip / 8) + i / 8) =
+            h ? make_uint2(word[2], word[3]) : make_uint2(word[0], word[1]);
+    }
+  }
+};
+
 // ---------------------------------------------------------------------------
 // Work split. The T output tiles of a product, each of S reduction stages,
 // are T*S iterations in tile-major order (tile t = (ti, tj) with ti fastest).
@@ -1540,40 +1584,43 @@ hipError_t launch_bwd_dx(const uint16_t* dY, const uint8_t* w_packed, const floa
   return run_gemm<MfmaBf16, 1>(pl, ql, ep, g, split_ws, split_bytes, stream);
 }
 
-hipError_t launch_bwd_dw(const uint16_t* dY, const int8_t* x_q, const float* s_x, int64_t M,
-                         int64_t N, int64_t K, void* dW, bool dw_is_f32, void* ws, size_t ws_bytes,
-                         hipStream_t stream) {
+// The dW product on x_hat (already built) with epilogue ep.
+template <class EP>
+static hipError_t run_dw(const uint16_t* dY, const uint16_t* xhat, int64_t M, int64_t N, int64_t K, const EP& ep,
+                         void* split_ws, size_t split_bytes, hipStream_t stream) {
   const int64_t Kp = k_pad(K);
+  const GemmShape g = shape_of(GemmKind::kBwdDw, M, N, K);
+  if (N % 8 == 0) {
+    // both operands copied in their memory orientation, fragments read transposed
+    const RowCopyBf16Loader<1> pc{xhat, Kp, M, Kp};
+    const RowCopyBf16Loader<5> qc{dY, N, M, N};
+    return run_gemm<MfmaBf16, 0>(pc, qc, ep, g, split_ws, split_bytes, stream);
+  }
+  const RowTransposeBf16Loader<true, 3> pl{xhat, Kp, M, Kp};
+  if (N % 4 == 0) return run_gemm<MfmaBf16, 0>(pl, RowTransposeBf16Loader<true, 5>{dY, N, M, N}, ep, g, split_ws, split_bytes, stream);
+  return run_gemm<MfmaBf16, 0>(pl, RowTransposeBf16Loader<false, 5>{dY, N, M, N}, ep, g, split_ws, split_bytes, stream);
+}
+
+hipError_t launch_bwd_dw(const uint16_t* dY, const int8_t* x_q, const float* s_x, int64_t M,
+                         int64_t N, int64_t K, void* dW, DwOut dw_out, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
   const size_t xb = xhat_bytes(M, K);
   if (ws == nullptr || ws_bytes < xb) return hipErrorInvalidValue;  // the C ABI sized it
   uint16_t* xhat = static_cast<uint16_t*>(ws);
   void* split_ws = static_cast<char*>(ws) + xb;
   const size_t split_bytes = ws_bytes - xb;
   if (hipError_t e = launch_xhat(x_q, s_x, M, K, xhat, stream)) return e;
-
-  const GemmShape g = shape_of(GemmKind::kBwdDw, M, N, K);
-  if (N % 8 == 0) {
-    // both operands copied in their memory orientation, fragments read transposed
-    const RowCopyBf16Loader<1> pc{xhat, Kp, M, Kp};
-    const RowCopyBf16Loader<5> qc{dY, N, M, N};
-    if (dw_is_f32) return run_gemm<MfmaBf16, 0>(pc, qc, Bf16Epilogue<true>{dW, nullptr, K, N}, g, split_ws, split_bytes, stream);
-    return run_gemm<MfmaBf16, 0>(pc, qc, Bf16Epilogue<false>{dW, nullptr, K, N}, g, split_ws, split_bytes, stream);
+  switch (dw_out) {
+    case DwOut::kF32: return run_dw(dY, xhat, M, N, K, Bf16Epilogue<true>{dW, nullptr, K, N}, split_ws, split_bytes, stream);
+    case DwOut::kSign1:
+      return run_dw(dY, xhat, M, N, K, Sign1Epilogue{static_cast<uint8_t*>(dW), k_pad(K), N}, split_ws, split_bytes, stream);
+    default: return run_dw(dY, xhat, M, N, K, Bf16Epilogue<false>{dW, nullptr, K, N}, split_ws, split_bytes, stream);
   }
-  RowTransposeBf16Loader<true, 3> pl{xhat, Kp, M, Kp};
-  const bool vec = (N % 4 == 0);
-  if (dw_is_f32) {
-    Bf16Epilogue<true> ep{dW, nullptr, K, N};
-    if (vec) return run_gemm<MfmaBf16, 0>(pl, RowTransposeBf16Loader<true, 5>{dY, N, M, N}, ep, g, split_ws, split_bytes, stream);
-    return run_gemm<MfmaBf16, 0>(pl, RowTransposeBf16Loader<false, 5>{dY, N, M, N}, ep, g, split_ws, split_bytes, stream);
-  }
-  Bf16Epilogue<false> ep{dW, nullptr, K, N};
-  if (vec) return run_gemm<MfmaBf16, 0>(pl, RowTransposeBf16Loader<true, 5>{dY, N, M, N}, ep, g, split_ws, split_bytes, stream);
-  return run_gemm<MfmaBf16, 0>(pl, RowTransposeBf16Loader<false, 5>{dY, N, M, N}, ep, g, split_ws, split_bytes, stream);
 }
 
 hipError_t launch_bwd_pair(const uint16_t* dY, const uint8_t* w_packed, const float* gamma, const int8_t* x_q,
                            const float* s_x, int64_t M, int64_t N, int64_t K, uint16_t* dX, void* dW,
-                           bool dw_is_f32, void* ws, size_t ws_bytes, hipStream_t stream) {
+                           DwOut dw_out, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!pair_eligible(M, N, K) || ws == nullptr) return hipErrorNotSupported;
   const GemmShape g1 = shape_of(GemmKind::kBwdDx, M, N, K), g2 = shape_of(GemmKind::kBwdDw, M, N, K);
   int kt = 0;
@@ -1613,14 +1660,16 @@ hipError_t launch_bwd_pair(const uint16_t* dY, const uint8_t* w_packed, const fl
   const RowCopyBf16Loader<5> q2{dY, N, M, N};
   const SplitPlan plan1 = sk1 ? split_plan(g1, G1, base + wb + xb) : whole_plan(g1, G1);
   const SplitPlan plan2 = sk2 ? split_plan(g2, G2, base + wb + xb + s1) : whole_plan(g2, G2);
-  if (dw_is_f32) {
+  const auto launch = [&](const auto& e2) {
+    typedef typename std::decay<decltype(e2)>::type EP2;
     gemm_pair_kernel<MfmaBf16, 1, RowCodesLoader<CodesFp4Frags>, CopyLoader<2, true>, Bf16Epilogue<false>, 0,
-                     RowCopyBf16Loader<1>, RowCopyBf16Loader<5>, Bf16Epilogue<true>>
-        <<<8 * kt, kThreads, 0, stream>>>(p1, q1, e1, plan1, p2, q2, Bf16Epilogue<true>{dW, nullptr, K, N}, plan2, k1);
-  } else {
-    gemm_pair_kernel<MfmaBf16, 1, RowCodesLoader<CodesFp4Frags>, CopyLoader<2, true>, Bf16Epilogue<false>, 0,
-                     RowCopyBf16Loader<1>, RowCopyBf16Loader<5>, Bf16Epilogue<false>>
-        <<<8 * kt, kThreads, 0, stream>>>(p1, q1, e1, plan1, p2, q2, Bf16Epilogue<false>{dW, nullptr, K, N}, plan2, k1);
+                     RowCopyBf16Loader<1>, RowCopyBf16Loader<5>, EP2>
+        <<<8 * kt, kThreads, 0, stream>>>(p1, q1, e1, plan1, p2, q2, e2, plan2, k1);
+  };
+  switch (dw_out) {
+    case DwOut::kF32: launch(Bf16Epilogue<true>{dW, nullptr, K, N}); break;
+    case DwOut::kSign1: launch(Sign1Epilogue{static_cast<uint8_t*>(dW), Kp, N}); break;
+    default: launch(Bf16Epilogue<false>{dW, nullptr, K, N}); break;
   }
   return hipGetLastError();
 }

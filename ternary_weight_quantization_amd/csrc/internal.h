@@ -40,8 +40,10 @@ hipError_t launch_fwd(const int8_t* x_q, const float* s_x, const uint8_t* w_pack
 hipError_t launch_bwd_dx(const uint16_t* dY, const uint8_t* w_packed, const float* gamma,
                          int64_t M, int64_t N, int64_t K, uint16_t* dX, void* ws,
                          size_t ws_bytes, hipStream_t stream);
+// dW output: bf16, f32, or 1-bit signs [N][Kp/8] (bit set: negative sum).
+enum class DwOut { kBf16, kF32, kSign1 };
 hipError_t launch_bwd_dw(const uint16_t* dY, const int8_t* x_q, const float* s_x,
-                         int64_t M, int64_t N, int64_t K, void* dW, bool dw_is_f32,
+                         int64_t M, int64_t N, int64_t K, void* dW, DwOut dw_out,
                          void* ws, size_t ws_bytes, hipStream_t stream);
 
 // Both STE backward products in one launch, each on its share of the CUs
@@ -50,7 +52,7 @@ hipError_t launch_bwd_dw(const uint16_t* dY, const int8_t* x_q, const float* s_x
 // two products one after the other.
 hipError_t launch_bwd_pair(const uint16_t* dY, const uint8_t* w_packed, const float* gamma,
                            const int8_t* x_q, const float* s_x, int64_t M, int64_t N, int64_t K,
-                           uint16_t* dX, void* dW, bool dw_is_f32, void* ws, size_t ws_bytes,
+                           uint16_t* dX, void* dW, DwOut dw_out, void* ws, size_t ws_bytes,
                            hipStream_t stream);
 
 }  // namespace bitnet

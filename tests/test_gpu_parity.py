@@ -322,3 +322,63 @@ def test_graph_replays_match_eager(M, K, N, split, monkeypatch):
         torch.cuda.synchronize()
         for k in ("y", "dX", "dW"):
             assert torch.equal(t[k], ref[k]), ("eager", r, k)
+
+
+@pytest.mark.parametrize("M,K,N,with_dx,split", [
+    (64, 256, 128, False, None),     # one tile
+    (300, 1000, 777, False, None),   # N % 8 != 0: transposing loaders; ragged K
+    (520, 1001, 264, True, None),    # with dX in the same call
+    (1024, 2560, 1536, True, None),  # dX and dW in one launch, both split
+    (300, 1000, 777, False, 13),     # split tiles forced
+])
+def test_dw_sign1(M, K, N, with_dx, split, monkeypatch):
+    """dW as 1-bit signs (dW_dtype BITNET_SIGN1). (a) Bit for bit the signs
+    of the float32 dW the same call writes with dW_dtype BITNET_F32 (same
+    kernels, same summation order), padding bits 0; (b) against the
+    oracle's float64 dW at every element whose magnitude exceeds the bound
+    M * 2^-24 * sum_m |dY[m,n] * x_hat[m,k]| on the float32 summation error
+    (the products are exact), where the sign is fixed whatever the order of
+    the sums; elsewhere both bits are signs of an admissible float32 sum;
+    (c) a dX computed in the same call is unchanged."""
+    if split is not None:
+        monkeypatch.setenv("BITNET_SPLIT_CTAS", str(split))
+    inp = WL.custom_inputs(M, K, N, seed=7 * M + N, w_dtype="bf16")
+    note(f"dW sign1 M={M} K={K} N={N} dx={with_dx} split={split}")
+    from ternary_weight_quantization_amd import binding as B
+    dev = torch.device("cuda")
+    Kp = O.k_pad(K)
+    W, x, dY = dev_bf16(inp["W"]), dev_bf16(inp["x"]), dev_bf16(inp["dY"])
+    w_packed = torch.empty((N, Kp // 4), dtype=torch.uint8, device=dev)
+    gamma = torch.empty((1,), dtype=torch.float32, device=dev)
+    ws = torch.empty((B.bitnet_ternarize_workspace_bytes(N, K),), dtype=torch.uint8, device=dev)
+    x_q = torch.empty((M, Kp), dtype=torch.int8, device=dev)
+    s_x = torch.empty((M,), dtype=torch.float32, device=dev)
+    B.bitnet_ternarize_pack(W, w_packed, gamma, ws)
+    B.bitnet_act_quant(x, x_q, s_x)
+    dX1 = torch.empty((M, K), dtype=torch.bfloat16, device=dev) if with_dx else None
+    dX2 = torch.empty((M, K), dtype=torch.bfloat16, device=dev) if with_dx else None
+    dWf = torch.empty((N, K), dtype=torch.float32, device=dev)
+    bits = torch.full((N, Kp // 8), 0xAB, dtype=torch.uint8, device=dev)
+    B.bitlinear_bwd(dY, x_q, s_x, w_packed, gamma, K, dX=dX1, dW=dWf)
+    B.bitlinear_bwd(dY, x_q, s_x, w_packed, gamma, K, dX=dX2, dW=bits)
+    torch.cuda.synchronize()
+    got = bits.cpu().numpy()
+    # (a) the signs of the same sums
+    assert np.array_equal(got, O.sign1_pack(dWf.cpu().numpy().astype(np.float64), Kp))
+    if with_dx:  # (c)
+        assert torch.equal(dX1, dX2)
+    # (b) the oracle, on its own (bit-exact, checked here) integer state
+    w = w_values(inp["W"])
+    g = O.absmean_gamma(w)
+    q = O.ternary_codes(w, g)
+    xq, s = O.act_quant(bf(inp["x"]), Kp)
+    assert np.array_equal(w_packed.cpu().numpy(), O.pack_codes(q, Kp))
+    assert np.array_equal(x_q.cpu().numpy(), xq)
+    dYv = bf(inp["dY"])
+    _, dW_ref = O.backward(dYv, xq, s, q, g)
+    mag = np.abs(dYv).T @ np.abs(O.x_hat(xq, s, K))
+    sure = np.abs(dW_ref) > M * 2.0 ** -24 * mag
+    sg, sr = O.sign1_unpack(got, K), O.sign1_unpack(O.sign1_pack(dW_ref, Kp), K)
+    assert np.array_equal(sg[sure], sr[sure])
+    print(f"[sign1] {M}x{K}x{N}: {int(sure.sum())} of {sure.size} signs fixed by the bound, "
+          f"{int(np.sum(sg != sr))} differ elsewhere", flush=True)

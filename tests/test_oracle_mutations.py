@@ -95,6 +95,31 @@ def _bf16_trunc(v):
     return np.ldexp(np.trunc(np.ldexp(m, 8)), e - 8)
 
 
+def _sign1_msb_first(dW, Kp=None):
+    d = np.asarray(dW, dtype=np.float64)
+    N, K = d.shape
+    Kp = B.k_pad(K) if Kp is None else Kp
+    neg = np.zeros((N, Kp), dtype=np.int64)
+    neg[:, :K] = d < 0
+    bits = neg.reshape(N, Kp // 8, 8)
+    out = np.zeros((N, Kp // 8), dtype=np.int64)
+    for j in range(8):
+        out |= bits[..., j] << (7 - j)
+    return out.astype(np.uint8)
+
+
+def _sign1_zero_negative(dW, Kp=None):
+    d = np.asarray(dW, dtype=np.float64)
+    return _sign1_ref(np.where(d <= 0, -1.0, 1.0), Kp)
+
+
+def _sign1_inverted(dW, Kp=None):
+    return _sign1_ref(-np.asarray(dW, dtype=np.float64), Kp)
+
+
+_sign1_ref = B.sign1_pack
+
+
 MUTATIONS = [
     ("absmean_gamma", _gamma_no_abs, ["test_gamma_closed_forms", "test_codes_zero_fraction_statistics"]),
     ("absmean_gamma", _gamma_max, ["test_gamma_closed_forms", "test_codes_zero_fraction_statistics"]),
@@ -108,6 +133,9 @@ MUTATIONS = [
     ("backward", _backward_dx_fp32_gamma, ["test_y_dx_dw_exact_fractions", "test_against_torch_autograd_detach_ste"]),
     ("x_hat", _xhat_unrounded, ["test_y_dx_dw_exact_fractions"]),
     ("bf16_round", _bf16_trunc, ["test_bf16_round_matches_exact_rounding", "test_bf16_bits_roundtrip"]),
+    ("sign1_pack", _sign1_msb_first, ["test_sign1_hand_bytes", "test_sign1_matches_numpy_packbits"]),
+    ("sign1_pack", _sign1_zero_negative, ["test_sign1_hand_bytes", "test_sign1_matches_numpy_packbits"]),
+    ("sign1_pack", _sign1_inverted, ["test_sign1_hand_bytes", "test_sign1_of_ste_gradient_matches_quantised_gradient"]),
 ]
 
 

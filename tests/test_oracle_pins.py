@@ -515,6 +515,77 @@ def test_tiny_net_oracle_ste_signs():
 
 
 # ---------------------------------------------------------------------------
+# 1-bit sign gradients
+# ---------------------------------------------------------------------------
+
+def test_sign1_hand_bytes():
+    """Row 0: negatives at k = 0, 4, 7, 8 (and -0.0 at k = 1, zero at k = 2,
+    which are not negative): byte 0 = 1 + 16 + 128 = 0x91, byte 1 = 0x01.
+    Row 1: the only negative at k = 2: byte 0 = 0x04. K = 10 pads to 64
+    columns, 8 bytes per row; the padding bytes are 0."""
+    d = np.array([[-1.0, -0.0, 0.0, 3.0, -2.0, 5.0, 6.0, -7.0, -1e-30, 2.0],
+                  [1.0, 1.0, -4.0, 0.0, 1.0, 1.0, 1.0, 1.0, 1.0, 1.0]])
+    got = O.sign1_pack(d)
+    want = np.zeros((2, 8), dtype=np.uint8)
+    want[0, 0], want[0, 1], want[1, 0] = 0x91, 0x01, 0x04
+    assert got.dtype == np.uint8 and np.array_equal(got, want)
+    assert np.array_equal(O.sign1_unpack(got, 10), np.where(d < 0, -1, 1))
+
+
+def test_sign1_matches_numpy_packbits():
+    """Against numpy's own bit packing (little bit order) of dW < 0 on a
+    random matrix with exact zeros, negative zeros and a ragged K."""
+    rng = np.random.default_rng(5)
+    for N, K in ((3, 1), (7, 70), (16, 128), (5, 1001)):
+        d = rng.standard_normal((N, K))
+        d[rng.random((N, K)) < 0.1] = 0.0
+        d[rng.random((N, K)) < 0.1] = -0.0
+        Kp = O.k_pad(K)
+        full = np.zeros((N, Kp), dtype=bool)
+        full[:, :K] = d < 0
+        ref = np.packbits(full, axis=1, bitorder="little")
+        got = O.sign1_pack(d)
+        assert got.shape == (N, Kp // 8) and np.array_equal(got, ref), (N, K)
+        assert int(np.unpackbits(got).sum()) == int(np.sum(d < 0))
+
+
+def test_sign1_of_ste_gradient_matches_quantised_gradient():
+    """The page's claim in its 1-bit form: on its 3-layer net through the
+    oracle, the packed signs of the STE gradient equal the packed signs of
+    autograd's gradient with respect to the quantised weights."""
+    torch = pytest.importorskip("torch")
+    d = WL.tiny_net_inputs()
+    x = WL.bf16_bits_to_f32(WL.f32_to_bf16_bits(d["x0"].astype(np.float32))).astype(np.float64)
+    saved = []
+    for W in (w.astype(np.float32) for w in d["Ws"]):
+        g = O.absmean_gamma(W)
+        q = O.ternary_codes(W, g)
+        xq, s = O.act_quant(x)
+        saved.append((xq, s, q, g, W.shape[1]))
+        x = O.bf16_round(O.forward_y(O.forward_acc(xq, q), s, g))
+    dY = O.bf16_round(x - d["target"])
+    grads = [None] * 3
+    for i in (2, 1, 0):
+        xq, s, q, g, K = saved[i]
+        dX, grads[i] = O.backward(dY, xq, s, q, g)
+        dY = O.bf16_round(dX)
+    Q = [torch.tensor(O.w_hat(q, g), requires_grad=True) for (_, _, q, g, _) in saved]
+    a = torch.tensor(O.x_hat(saved[0][0], saved[0][1], saved[0][4]))
+    for i in range(3):
+        h = a @ Q[i].T
+        if i < 2:
+            xq, s, _, _, K = saved[i + 1]
+            a = h + (torch.tensor(O.x_hat(xq, s, K)) - h).detach()
+        else:
+            a = h
+    (0.5 * torch.sum((a - torch.tensor(d["target"])) ** 2)).backward()
+    for i in range(3):
+        gq = Q[i].grad.numpy()
+        assert np.all(gq != 0), i  # every sign is determined
+        assert np.array_equal(O.sign1_pack(grads[i]), O.sign1_pack(gq)), i
+
+
+# ---------------------------------------------------------------------------
 # the synthetic weight recipe
 # ---------------------------------------------------------------------------
 
