@@ -97,8 +97,13 @@ def _pmc_rows(d):
     return rows
 
 
+# kernels of calls outside the step (the sign-output backward)
+KERNEL_EXCLUDE = ["Sign1Epilogue"]
+
+
 def _per_dispatch_mean(rows, counter, match):
-    vals = [v for name, cn, v in rows if cn == counter and any(m in name for m in match)]
+    vals = [v for name, cn, v in rows if cn == counter and any(m in name for m in match)
+            and not any(x in name for x in KERNEL_EXCLUDE)]
     return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
 
 
@@ -122,14 +127,17 @@ def summarize_pmc(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir):
         f_total = w_total = 0.0
         n_f = n_w = 0
         for m in match:
+            # the list names every kernel the call may launch; a shape runs a subset
             f, nf = _per_dispatch_mean(fetch_rows, "FETCH_SIZE", [m])
             w, nw = _per_dispatch_mean(write_rows, "WRITE_SIZE", [m])
             if f is None or w is None:
-                raise SystemExit(f"no counters for {m}")
+                continue
             f_total += f * 1024.0 * cal["FETCH_SIZE"]["factor"]
             w_total += w * 1024.0 * cal["WRITE_SIZE"]["factor"]
             n_f += nf
             n_w += nw
+        if n_f == 0 or n_w == 0:
+            raise SystemExit(f"no counters for any kernel of {bname}")
         kernels[bname] = {"fetch_bytes": round(f_total), "write_bytes": round(w_total),
                           "hbm_bytes_per_launch": round(f_total + w_total), "dispatches": [n_f, n_w]}
     return {"source_hash": source_hash(), "calibration": cal, "kernels": kernels}
