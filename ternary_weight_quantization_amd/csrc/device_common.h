@@ -36,6 +36,12 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
+// Four 2-bit codes in the byte lanes of c (values 0, 1, 3) -> four int8.
+__device__ __forceinline__ uint32_t codes4_to_i8(uint32_t c) {
+  // table: code 0 -> 0x00, 1 -> 0x01, 3 -> 0xFF (code 2 never written)
+  return perm(0u, 0xFF000100u, c);
+}
+
 // Sum over the 64 lanes of a wave in a fixed butterfly order; every lane
 // receives a value, lane 0's is the one used (deterministic).
 __device__ __forceinline__ double wave_sum_f64(double v) {

@@ -194,12 +194,6 @@ struct PlainFrags {
   __device__ __forceinline__ typename MT::Frag frag(int f) const { return buf[KS & 1][f]; }
 };
 
-// Four 2-bit codes in the byte lanes of c (values 0, 1, 3) -> four int8.
-__device__ __forceinline__ uint32_t codes4_to_i8(uint32_t c) {
-  // table: code 0 -> 0x00, 1 -> 0x01, 3 -> 0xFF (code 2 never written)
-  return perm(0u, 0xFF000100u, c);
-}
-
 // Forward P: rows of 2-bit codes in the stored layout (tile pitch 48 bytes,
 // 32 bytes = 8 words = 128 codes per row per stage). Lane half h of k-step
 // ks takes word 4h + ks (codes k = 16(4h+ks)..+15, chunk map 1); one 16-byte
@@ -1413,6 +1407,8 @@ static size_t pair_workspace_bound(int64_t M, int64_t N, int64_t K) {
 size_t gemm_workspace_bytes(GemmKind kind, int64_t M, int64_t N, int64_t K) {
   if (kind == GemmKind::kBwdPair) return pair_eligible(M, N, K) ? pair_workspace_bound(M, N, K) : 0;
   const GemmShape g = shape_of(kind, M, N, K);
+  // the few-token forward needs none; the large-M kernel's share stays
+  // reserved so that BITNET_NO_SKINNY (a test knob) can run it at any M
   const size_t split = split_workspace(g, split_grid(g, kMaxGrid));
   if (kind == GemmKind::kBwdDw) return xhat_bytes(M, K) + split;
   if (kind == GemmKind::kBwdDx) return wt_bytes(N, K) + split;
@@ -1541,6 +1537,8 @@ static hipError_t run_gemm(const PL& pl, const QL& ql, const EP& ep, const GemmS
 hipError_t launch_fwd(const int8_t* x_q, const float* s_x, const uint8_t* w_packed,
                       const float* gamma, int64_t M, int64_t N, int64_t K, uint16_t* y,
                       int32_t* acc_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (M <= kSkinnyMaxM && getenv("BITNET_NO_SKINNY") == nullptr)
+    return launch_fwd_skinny(x_q, s_x, w_packed, gamma, M, N, K, y, acc_out, stream);
   const int64_t Kp = k_pad(K);
   PackedCodesLoader pl{w_packed, Kp / 4, N};
   CopyLoader<1, true> ql{reinterpret_cast<const char*>(x_q), Kp, M, Kp};

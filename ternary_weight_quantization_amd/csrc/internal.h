@@ -36,6 +36,13 @@ hipError_t launch_fwd(const int8_t* x_q, const float* s_x, const uint8_t* w_pack
                       uint16_t* y, int32_t* acc_out, void* ws, size_t ws_bytes,
                       hipStream_t stream);
 
+// INT8 forward for few tokens (1 <= M <= kSkinnyMaxM): one pass over the
+// codes, no workspace; same results, bit for bit, as launch_fwd's GEMM.
+constexpr int64_t kSkinnyMaxM = 64;
+hipError_t launch_fwd_skinny(const int8_t* x_q, const float* s_x, const uint8_t* w_packed,
+                             const float* gamma, int64_t M, int64_t N, int64_t K, uint16_t* y,
+                             int32_t* acc_out, hipStream_t stream);
+
 // STE backward GEMMs.
 hipError_t launch_bwd_dx(const uint16_t* dY, const uint8_t* w_packed, const float* gamma,
                          int64_t M, int64_t N, int64_t K, uint16_t* dX, void* ws,

@@ -382,3 +382,37 @@ def test_dw_sign1(M, K, N, with_dx, split, monkeypatch):
     assert np.array_equal(sg[sure], sr[sure])
     print(f"[sign1] {M}x{K}x{N}: {int(sure.sum())} of {sure.size} signs fixed by the bound, "
           f"{int(np.sum(sg != sr))} differ elsewhere", flush=True)
+
+
+@pytest.mark.parametrize("M,K,N", [
+    (1, 64, 1),
+    (1, 2560, 6912),      # one token
+    (17, 1000, 777),      # N % 4 != 0: element stores
+    (32, 6912, 2560),     # the skinny workload's shape
+    (33, 130, 513),       # two token tiles, ragged
+    (64, 6912, 2560),     # the largest M of the few-token path
+    (64, 64, 4096),
+])
+def test_skinny_forward(M, K, N, monkeypatch):
+    """The few-token forward (M <= 64): y and acc against the oracle (acc
+    bit-exact, y within tolerance), and bit for bit the results of the
+    large-M GEMM on the same state (forced with BITNET_NO_SKINNY)."""
+    from ternary_weight_quantization_amd import binding as B
+    inp = WL.custom_inputs(M, K, N, seed=3 * M + K + N)
+    note(f"skinny forward M={M} K={K} N={N}")
+    g = run_layer(inp, dx=False, dw=False)
+    check_layer(inp, g, full=True)
+    dev = torch.device("cuda")
+    Kp = O.k_pad(K)
+    x_q = torch.from_numpy(g["x_q"]).to(dev)
+    s_x = torch.from_numpy(g["s"]).to(dev)
+    wp = torch.from_numpy(g["packed"]).to(dev)
+    gamma = torch.tensor([g["gamma"]], dtype=torch.float32, device=dev)
+    monkeypatch.setenv("BITNET_NO_SKINNY", "1")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    acc = torch.empty((M, N), dtype=torch.int32, device=dev)
+    B.bitlinear_fwd(x_q, s_x, wp, gamma, K, y, acc)
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy(), g["acc"])
+    assert np.array_equal(host_bf16_bits(y), g["y_bits"])
+    assert Kp == x_q.shape[1]
