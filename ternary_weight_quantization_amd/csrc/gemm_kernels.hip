@@ -1534,10 +1534,14 @@ static hipError_t run_gemm(const PL& pl, const QL& ql, const EP& ep, const GemmS
 // launchers
 // ---------------------------------------------------------------------------
 
+// Few tokens run the decode-shaped kernels (BITNET_NO_SKINNY, a test knob,
+// keeps the large-M GEMMs at any M).
+static bool skinny(int64_t M) { return M <= kSkinnyMaxM && getenv("BITNET_NO_SKINNY") == nullptr; }
+
 hipError_t launch_fwd(const int8_t* x_q, const float* s_x, const uint8_t* w_packed,
                       const float* gamma, int64_t M, int64_t N, int64_t K, uint16_t* y,
                       int32_t* acc_out, void* ws, size_t ws_bytes, hipStream_t stream) {
-  if (M <= kSkinnyMaxM && getenv("BITNET_NO_SKINNY") == nullptr)
+  if (skinny(M))
     return launch_fwd_skinny(x_q, s_x, w_packed, gamma, M, N, K, y, acc_out, stream);
   const int64_t Kp = k_pad(K);
   PackedCodesLoader pl{w_packed, Kp / 4, N};
@@ -1570,6 +1574,7 @@ hipError_t launch_bwd_dx(const uint16_t* dY, const uint8_t* w_packed, const floa
   void* split_ws = static_cast<char*>(ws) + wb;
   const size_t split_bytes = ws_bytes - wb;
   if (hipError_t e = launch_wt(w_packed, N, K, wt, stream)) return e;
+  if (skinny(M) && N % 8 == 0) return launch_dx_skinny(wt, dY, gamma, M, N, K, dX, stream);
 
   const RowCodesLoader<CodesFp4Frags> pl{wt, Np / 2, Kp};
   Bf16Epilogue<false> ep{dX, gamma, K, M};
@@ -1619,7 +1624,7 @@ hipError_t launch_bwd_dw(const uint16_t* dY, const int8_t* x_q, const float* s_x
 hipError_t launch_bwd_pair(const uint16_t* dY, const uint8_t* w_packed, const float* gamma, const int8_t* x_q,
                            const float* s_x, int64_t M, int64_t N, int64_t K, uint16_t* dX, void* dW,
                            DwOut dw_out, void* ws, size_t ws_bytes, hipStream_t stream) {
-  if (!pair_eligible(M, N, K) || ws == nullptr) return hipErrorNotSupported;
+  if (!pair_eligible(M, N, K) || ws == nullptr || skinny(M)) return hipErrorNotSupported;
   const GemmShape g1 = shape_of(GemmKind::kBwdDx, M, N, K), g2 = shape_of(GemmKind::kBwdDw, M, N, K);
   int kt = 0;
   const int k1 = pair_columns(g1, g2, device_cus(), &kt);

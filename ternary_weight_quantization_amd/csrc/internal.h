@@ -37,11 +37,17 @@ hipError_t launch_fwd(const int8_t* x_q, const float* s_x, const uint8_t* w_pack
                       hipStream_t stream);
 
 // INT8 forward for few tokens (1 <= M <= kSkinnyMaxM): one pass over the
-// codes, no workspace; same results, bit for bit, as launch_fwd's GEMM.
+// codes, no workspace; same results, bit for bit, as launch_fwd's GEMM
+// (which calls it for such M).
 constexpr int64_t kSkinnyMaxM = 64;
 hipError_t launch_fwd_skinny(const int8_t* x_q, const float* s_x, const uint8_t* w_packed,
                              const float* gamma, int64_t M, int64_t N, int64_t K, uint16_t* y,
                              int32_t* acc_out, hipStream_t stream);
+
+// STE dX for few tokens (M <= kSkinnyMaxM, N % 8 == 0) from the fp4
+// transposed codes wt [Kp][Np/2] (Np = N rounded up to 64).
+hipError_t launch_dx_skinny(const uint8_t* wt, const uint16_t* dY, const float* gamma, int64_t M,
+                            int64_t N, int64_t K, uint16_t* dX, hipStream_t stream);
 
 // STE backward GEMMs.
 hipError_t launch_bwd_dx(const uint16_t* dY, const uint8_t* w_packed, const float* gamma,

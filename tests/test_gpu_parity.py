@@ -416,3 +416,22 @@ def test_skinny_forward(M, K, N, monkeypatch):
     assert np.array_equal(acc.cpu().numpy(), g["acc"])
     assert np.array_equal(host_bf16_bits(y), g["y_bits"])
     assert Kp == x_q.shape[1]
+
+
+@pytest.mark.parametrize("M,K,N", [
+    (1, 64, 8),
+    (17, 1000, 776),
+    (17, 1000, 777),      # N % 8 != 0: the large-M dX
+    (32, 6912, 2560),
+    (33, 130, 520),
+    (64, 2560, 6912),
+])
+def test_skinny_backward(M, K, N):
+    """Few-token backward: dX (the decode-shaped kernel when N % 8 == 0)
+    and dW against the oracle, dX alone and with dW in the same call."""
+    inp = WL.custom_inputs(M, K, N, seed=5 * M + K + N)
+    note(f"skinny backward M={M} K={K} N={N}")
+    g = run_layer(inp)
+    check_layer(inp, g, full=True)
+    g2 = run_layer(inp, dw=False)
+    assert np.array_equal(g["dX"], g2["dX"])
