@@ -38,8 +38,9 @@ PEAK_HBM_GBS = 8000.0
 # Effective TOPS of the pages' fused kernel at this workload on an NVIDIA L4
 # (8.80 ms for 6*M*N*K ops; context, other hardware).
 PAGES_L4_TOPS = 49.4
+HEADLINE = "c2_up_4096x2560x6912"
 
-KERNEL_SOURCES = ["gemm_kernels.hip", "quant_kernels.hip", "device_common.h"]
+KERNEL_SOURCES = ["gemm_kernels.hip", "skinny_kernels.hip", "quant_kernels.hip", "device_common.h"]
 
 
 def parse():
@@ -47,7 +48,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="c2_up_4096x2560x6912")
+    p.add_argument("--workload", default=HEADLINE)
     p.add_argument("--rotate", type=int, default=4)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
@@ -387,7 +388,7 @@ def main():
                 "unit": d["unit"], "frac": round(d["frac"], 4), "traffic": traffic}
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC if args.workload == HEADLINE else METRIC.replace("4096×2560→6912", f"{M}×{K}→{N}"),
         "value": round(tops, 3),
         "unit": "TOPS",
         "n_gpus": 1,
@@ -396,7 +397,8 @@ def main():
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": round(tops / PAGES_L4_TOPS, 3),
+        # the pages' figure is for the headline shape only
+        "vs_baseline": round(tops / PAGES_L4_TOPS, 3) if args.workload == HEADLINE else None,
         "dtype": "int8+bf16",
         "data": "synthetic",
         "config": {"workload": f"bitlinear_fwd_bwd_{M}x{K}x{N}", "M": M, "K": K, "N": N,
