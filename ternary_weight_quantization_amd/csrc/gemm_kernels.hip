@@ -930,6 +930,120 @@ struct Sign1Epilogue {
   }
 };
 
+// dW for few tokens (M <= 64, N % 8 == 0): dW[n][k] = sum_{m < M} dY[m][n] *
+// x_hat[m][k] ("bitnet-qat-train", Semantics). The reduction is at most 4
+// MFMA steps of 16 tokens, so the cost is writing dW: small output tiles
+// (64 n x 256 k per workgroup) keep every CU busy with several tiles whose
+// loads and stores overlap. Both operands are staged as stored, rows m in
+// LDS (rows m >= M as zeros), and read transposed with ds_read_b64_tr_b16
+// (TrFrags): A = x_hat columns k (wave k half 128wk + 32f, f < 4), B = dY
+// columns n (wave n half 32wn). D[k][n] goes back through LDS as rows n and
+// is written as 16-byte row pieces (element by element when K does not
+// keep them aligned). Products are exact in fp32 and each sum runs in
+// token order.
+template <bool OUT_F32>
+__global__ __launch_bounds__(256) void dw_skinny_kernel(const uint16_t* __restrict__ xhat,
+                                                        const uint16_t* __restrict__ dY, int M, int64_t N,
+                                                        int64_t Kp, int64_t K, int ktiles, void* __restrict__ dW) {
+  constexpr int kEB = OUT_F32 ? 4 : 2;
+  constexpr int kOutPitch = 256 * kEB + 16;
+  constexpr int kTileB = 64 * kTrPitch;  // 64 token rows of one operand
+  constexpr int kOutB = 64 * kOutPitch;
+  __shared__ __attribute__((aligned(16))) char smem[2 * kTileB > kOutB ? 2 * kTileB : kOutB];
+  char* xs = smem;           // x_hat [m][256 k]
+  char* ys = smem + kTileB;  // dY [m][64 n]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t k0 = (int64_t)(blockIdx.x % ktiles) * 256, n0 = (int64_t)(blockIdx.x / ktiles) * 64;
+  const int ms = (M + 15) / 16;  // MFMA steps of 16 tokens
+
+  const rsrc_t rxh = make_rsrc(xhat, (uint32_t)(M * Kp * 2));
+  const rsrc_t rdy = make_rsrc(dY, (uint32_t)(M * N * 2));
+  uint4 vx[8], vy[2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {  // x_hat: rows m < 16 ms, 32 pieces of 16 bytes per row
+    const int e = tid + 256 * i, m = e >> 5;
+    const int64_t k = k0 + 8 * (e & 31);
+    vx[i] = buf_load16(rxh, m < M && k < Kp ? (uint32_t)((m * Kp + k) * 2) : kOob);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {  // dY: rows m < 64, 8 pieces per row
+    const int e = tid + 256 * i, m = e >> 3;
+    const int64_t n = n0 + 8 * (e & 7);
+    vy[i] = buf_load16(rdy, m < M && n < N ? (uint32_t)((m * N + n) * 2) : kOob);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int e = tid + 256 * i;
+    if ((e >> 5) < 16 * ms) *reinterpret_cast<uint4*>(xs + (e >> 5) * kTrPitch + 16 * (e & 31)) = vx[i];
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int e = tid + 256 * i;
+    if ((e >> 3) < 16 * ms) *reinterpret_cast<uint4*>(ys + (e >> 3) * kTrPitch + 16 * (e & 7)) = vy[i];
+  }
+  __syncthreads();
+
+  const int wn = wave & 1, wk = wave >> 1;
+  TrFrags fa, fb;
+  fa.init(xs, 128 * wk, lane);
+  fb.init(ys, 32 * wn, lane);
+  MfmaBf16::Acc acc[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[f][e] = 0.0f;
+  const auto step = [&](auto ks) {
+    constexpr int KS = decltype(ks)::value;
+    fb.template read<KS>(0);
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      fa.template read<KS>(f);
+      acc[f] = MfmaBf16::mma(fa.template frag<KS>(f), fb.template frag<KS>(0), acc[f]);
+    }
+  };
+  step(std::integral_constant<int, 0>());
+  if (ms > 1) step(std::integral_constant<int, 1>());
+  if (ms > 2) step(std::integral_constant<int, 2>());
+  if (ms > 3) step(std::integral_constant<int, 3>());
+  __syncthreads();
+
+  // D[k][n]: lane column n = 32wn + l % 32, rows k = 128wk + 32f + 8g + 4h + 0..3
+  const int nl = 32 * wn + (lane & 31), h = lane >> 5;
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      char* dst = smem + nl * kOutPitch + (128 * wk + 32 * f + 8 * g + 4 * h) * kEB;
+      const float v0 = acc[f][4 * g], v1 = acc[f][4 * g + 1], v2 = acc[f][4 * g + 2], v3 = acc[f][4 * g + 3];
+      if constexpr (OUT_F32)
+        *reinterpret_cast<uint4*>(dst) = make_uint4(__float_as_uint(v0), __float_as_uint(v1), __float_as_uint(v2),
+                                                    __float_as_uint(v3));
+      else
+        *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+    }
+  __syncthreads();
+  constexpr int kPieces = 256 * kEB / 16;  // 16-byte pieces per output row of the tile
+  constexpr int kPer = 16 / kEB;           // elements per piece
+  char* out = static_cast<char*>(dW);
+#pragma unroll
+  for (int i = 0; i < 64 * kPieces / 256; ++i) {
+    const int e = tid + 256 * i, r = e / kPieces, c = e % kPieces;
+    const int64_t n = n0 + r, k = k0 + kPer * c;
+    if (n >= N || k >= K) continue;
+    const char* src = smem + r * kOutPitch + 16 * c;
+    if (K % kPer == 0) {
+      *reinterpret_cast<uint4*>(out + (n * K + k) * kEB) = *reinterpret_cast<const uint4*>(src);
+    } else {
+      for (int j = 0; j < kPer && k + j < K; ++j) {
+        if constexpr (OUT_F32)
+          reinterpret_cast<uint32_t*>(out)[n * K + k + j] = reinterpret_cast<const uint32_t*>(src)[j];
+        else
+          reinterpret_cast<uint16_t*>(out)[n * K + k + j] = reinterpret_cast<const uint16_t*>(src)[j];
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Work split. The T output tiles of a product, each of S reduction stages,
 // are T*S iterations in tile-major order (tile t = (ti, tj) with ti fastest).
@@ -1613,6 +1727,16 @@ hipError_t launch_bwd_dw(const uint16_t* dY, const int8_t* x_q, const float* s_x
   void* split_ws = static_cast<char*>(ws) + xb;
   const size_t split_bytes = ws_bytes - xb;
   if (hipError_t e = launch_xhat(x_q, s_x, M, K, xhat, stream)) return e;
+  if (skinny(M) && N % 8 == 0 && dw_out != DwOut::kSign1) {
+    const int64_t Kp = k_pad(K);
+    const int ktiles = (int)((Kp + 255) / 256);
+    const unsigned grid = (unsigned)(ktiles * ((N + 63) / 64));
+    if (dw_out == DwOut::kF32)
+      dw_skinny_kernel<true><<<grid, 256, 0, stream>>>(xhat, dY, (int)M, N, Kp, K, ktiles, dW);
+    else
+      dw_skinny_kernel<false><<<grid, 256, 0, stream>>>(xhat, dY, (int)M, N, Kp, K, ktiles, dW);
+    return hipGetLastError();
+  }
   switch (dw_out) {
     case DwOut::kF32: return run_dw(dY, xhat, M, N, K, Bf16Epilogue<true>{dW, nullptr, K, N}, split_ws, split_bytes, stream);
     case DwOut::kSign1:

@@ -435,3 +435,21 @@ def test_skinny_backward(M, K, N):
     check_layer(inp, g, full=True)
     g2 = run_layer(inp, dw=False)
     assert np.array_equal(g["dX"], g2["dX"])
+
+
+@pytest.mark.parametrize("M,K,N,wd", [
+    (1, 64, 8, "bf16"),
+    (17, 1000, 776, "f32"),    # f32 dW, ragged K (element stores)
+    (32, 6912, 2560, "bf16"),
+    (33, 130, 520, "bf16"),
+    (64, 2560, 6912, "f32"),
+])
+def test_skinny_dw(M, K, N, wd):
+    """Few-token dW (the decode-shaped kernel): against the oracle, alone
+    and with dX in the same call."""
+    inp = WL.custom_inputs(M, K, N, seed=11 * M + K + N, w_dtype=wd)
+    note(f"skinny dW M={M} K={K} N={N} W={wd}")
+    g = run_layer(inp, dx=False)
+    check_layer(inp, g, full=True)
+    g2 = run_layer(inp)
+    assert np.array_equal(g["dW"], g2["dW"])
