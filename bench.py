@@ -312,32 +312,49 @@ def main():
     per_kernel = {n: float(np.mean([evs[i][j][0].elapsed_time(evs[i][j][1]) for i in range(args.steps)]))
                   for j, n in enumerate(names)}
 
-    # Step time: each buffer set's step captured once into a HIP graph and
-    # replayed, so that host-side call overhead stays out of the timed region
-    # (the same kernels and work as the eager step). A replay must reproduce
-    # the eager outputs bit for bit.
+    # Step time: graph replays, so that host-side call overhead stays out of
+    # the timed region (the same kernels and work as the eager step). When
+    # the step count is a multiple of the number of buffer sets, one graph
+    # holds one step on each set in turn (a training loop captures many
+    # layers in one graph, and this keeps the per-launch gap of a graph out
+    # of every step); otherwise each set's step is its own graph. Every
+    # replay pattern is first checked to reproduce the eager outputs bit for
+    # bit.
     outs = ("y", "dX", "dW")
-    ref = {k: sets[0][k].clone() for k in outs}
+    ref = [{k: s[k].clone() for k in outs} for s in sets]
+    R = len(sets)
+    chained = args.steps % R == 0
     graphs = []
-    for s in sets:
+    if chained:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            step(s)
+            for s in sets:
+                step(s)
         graphs.append(g)
-    for k in outs:
-        sets[0][k].zero_()
-    graphs[0].replay()
+    else:
+        for s in sets:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(s)
+            graphs.append(g)
+    for s in sets:
+        for k in outs:
+            s[k].zero_()
+    for g in graphs:
+        g.replay()
     torch.cuda.synchronize()
-    for k in outs:
-        if not torch.equal(sets[0][k], ref[k]):
-            raise SystemExit(f"bench.py: graph replay differs from the eager step in {k}")
-    for i in range(args.warmup):
+    for i, s in enumerate(sets):
+        for k in outs:
+            if not torch.equal(s[k], ref[i][k]):
+                raise SystemExit(f"bench.py: graph replay differs from the eager step in {k} (set {i})")
+    replays = args.steps // R if chained else args.steps
+    for i in range(max(1, args.warmup // R) if chained else args.warmup):
         graphs[i % len(graphs)].replay()
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record()
-    for i in range(args.steps):
+    for i in range(replays):
         graphs[i % len(graphs)].replay()
     t_end.record()
     torch.cuda.synchronize()
