@@ -160,6 +160,38 @@ bitnet_status bitlinear_fwd(const int8_t* x_q, const float* s_x,
                             void* stream);
 
 /*
+ * bitlinear_fwd_bias - bitlinear_fwd with a bias added before the rounding
+ * ("bitlinear.py", BitLinear: an optional bias, zero-initialised, added after
+ * the product):
+ *
+ *   y[m,n] = bf16_rne(fp32(acc[m,n] * (s_x[m]/127) * gamma) + bias[n])
+ *
+ * (the product as in bitlinear_fwd, one fp32 add, one rounding). bias is
+ * [N] bf16 bits, 16-byte aligned, or NULL (then identical to
+ * bitlinear_fwd). Other arguments, the workspace and the errors are those
+ * of bitlinear_fwd.
+ */
+bitnet_status bitlinear_fwd_bias(const int8_t* x_q, const float* s_x,
+                                 const uint8_t* w_packed, const float* gamma,
+                                 const uint16_t* bias,
+                                 int64_t M, int64_t N, int64_t K,
+                                 uint16_t* y, int32_t* acc_out,
+                                 void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/*
+ * bitlinear_bias_grad - gradient of that bias: db[n] = sum_m dY[m,n], the
+ * products of nothing but the bf16 values, summed in fp32 in a fixed order
+ * (bitwise deterministic across calls) and rounded once to db_dtype.
+ *
+ * dY  [M][N] bf16 bits (16-byte aligned).
+ * db  [N] output, BITNET_F32 or BITNET_BF16 bits (16-byte aligned).
+ * No workspace.
+ */
+bitnet_status bitlinear_bias_grad(const uint16_t* dY, int64_t M, int64_t N,
+                                  void* db, bitnet_dtype db_dtype, void* stream);
+
+/*
  * bitlinear_bwd - straight-through-estimator backward with the operands
  * rebuilt from the saved 2-bit and int8 state ("bitnet-qat-train",
  * Semantics and opening bullets; gamma is treated as a constant):

@@ -19,6 +19,8 @@ from .bitlinear_oracle import (  # noqa: F401
     act_quant,
     forward_acc,
     forward_y,
+    forward_y_bias,
+    bias_grad,
     w_hat,
     x_hat,
     backward,

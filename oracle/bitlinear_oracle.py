@@ -280,6 +280,23 @@ def layer_fwd_bwd(x, w, dY, with_backward=True):
 
 
 # ---------------------------------------------------------------------------
+# Bias
+# ---------------------------------------------------------------------------
+
+def forward_y_bias(acc, s, gamma, bias):
+    """y + bias[n]: the optional bias of "bitlinear.py" (BitLinear.forward,
+    added after the product), on bf16 bias values; float64."""
+    return forward_y(acc, s, gamma) + np.asarray(bias, dtype=np.float64)[None, :]
+
+
+def bias_grad(dY):
+    """db[n] = sum over tokens of dY[m, n], the gradient of that bias,
+    exactly rounded (``math.fsum`` per column)."""
+    d = np.asarray(dY, dtype=np.float64)
+    return np.array([math.fsum(d[:, n]) for n in range(d.shape[1])])
+
+
+# ---------------------------------------------------------------------------
 # 1-bit sign gradients
 # ---------------------------------------------------------------------------
 

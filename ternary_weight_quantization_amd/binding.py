@@ -64,6 +64,10 @@ def lib():
     L.bitnet_act_quant.restype = st
     L.bitlinear_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp, vp, sz, vp]
     L.bitlinear_fwd.restype = st
+    L.bitlinear_fwd_bias.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp, vp, vp, sz, vp]
+    L.bitlinear_fwd_bias.restype = st
+    L.bitlinear_bias_grad.argtypes = [vp, i64, i64, vp, st, vp]
+    L.bitlinear_bias_grad.restype = st
     L.bitlinear_bwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp, vp, st, vp, sz, vp]
     L.bitlinear_bwd.restype = st
     if len(_hip_runtimes_mapped()) > 1:
@@ -168,8 +172,10 @@ def bitnet_act_quant(x, x_q, s_x, stream=None):
     _check(lib().bitnet_act_quant(_ptr(x), M, K, _ptr(x_q), _ptr(s_x), _stream(stream)))
 
 
-def bitlinear_fwd(x_q, s_x, w_packed, gamma, K, y, acc_out=None, workspace=None, stream=None):
-    """INT8 forward: y [M, N] bf16 (and optionally acc_out int32 [M, N])."""
+def bitlinear_fwd(x_q, s_x, w_packed, gamma, K, y, acc_out=None, workspace=None, stream=None, bias=None):
+    """INT8 forward: y [M, N] bf16 (and optionally acc_out int32 [M, N]);
+    with `bias` (bf16 [N]) the bias is added before the rounding
+    (bitlinear_fwd_bias)."""
     M, Kp = x_q.shape
     N = w_packed.shape[0]
     if Kp != bitnet_k_pad(K):
@@ -181,11 +187,29 @@ def bitlinear_fwd(x_q, s_x, w_packed, gamma, K, y, acc_out=None, workspace=None,
     _need(y, torch.bfloat16, (M, N), "y")
     if acc_out is not None:
         _need(acc_out, torch.int32, (M, N), "acc_out")
+    if bias is not None:
+        _need(bias, torch.bfloat16, (N,), "bias")
     if workspace is None:
         workspace = _workspace(bitlinear_fwd_workspace_bytes(M, N, K), y, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().bitlinear_fwd(_ptr(x_q), _ptr(s_x), _ptr(w_packed), _ptr(gamma), M, N, int(K),
-                               _ptr(y), _ptr(acc_out), _ptr(workspace), ws_bytes, _stream(stream)))
+    if bias is None:
+        _check(lib().bitlinear_fwd(_ptr(x_q), _ptr(s_x), _ptr(w_packed), _ptr(gamma), M, N, int(K),
+                                   _ptr(y), _ptr(acc_out), _ptr(workspace), ws_bytes, _stream(stream)))
+    else:
+        _check(lib().bitlinear_fwd_bias(_ptr(x_q), _ptr(s_x), _ptr(w_packed), _ptr(gamma), _ptr(bias), M, N,
+                                        int(K), _ptr(y), _ptr(acc_out), _ptr(workspace), ws_bytes,
+                                        _stream(stream)))
+
+
+def bitlinear_bias_grad(dY, db, stream=None):
+    """db [N] (float32 or bf16) = the token sum of dY [M, N] bf16."""
+    M, N = dY.shape
+    _need(dY, torch.bfloat16, (M, N), "dY")
+    if db.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("db: expected float32 or bfloat16")
+    _need(db, db.dtype, (N,), "db")
+    dt = BITNET_F32 if db.dtype == torch.float32 else BITNET_BF16
+    _check(lib().bitlinear_bias_grad(_ptr(dY), M, N, _ptr(db), dt, _stream(stream)))
 
 
 def bitlinear_bwd(dY, x_q, s_x, w_packed, gamma, K, dX=None, dW=None, workspace=None, stream=None):

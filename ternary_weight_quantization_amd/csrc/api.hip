@@ -116,9 +116,10 @@ bitnet_status bitnet_act_quant(const uint16_t* x, int64_t M, int64_t K, int8_t* 
   return from_hip(bitnet::launch_act_quant(x, M, K, x_q, s_x, static_cast<hipStream_t>(stream)));
 }
 
-bitnet_status bitlinear_fwd(const int8_t* x_q, const float* s_x, const uint8_t* w_packed,
-                            const float* gamma, int64_t M, int64_t N, int64_t K, uint16_t* y,
-                            int32_t* acc_out, void* workspace, size_t workspace_bytes, void* stream) {
+bitnet_status bitlinear_fwd_bias(const int8_t* x_q, const float* s_x, const uint8_t* w_packed,
+                                 const float* gamma, const uint16_t* bias, int64_t M, int64_t N, int64_t K,
+                                 uint16_t* y, int32_t* acc_out, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
   if (!x_q || !s_x || !w_packed || !gamma || !y) return BITNET_ERR_NULL;
   if (bitnet_status st = check_gemm_sizes(M, N, K)) return st;
   if (bitnet_status st = check_gemm_ranges(M, N, K, true, true, false, N)) return st;
@@ -126,10 +127,26 @@ bitnet_status bitlinear_fwd(const int8_t* x_q, const float* s_x, const uint8_t* 
   if (workspace_bytes > 0 && !workspace) return BITNET_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return BITNET_ERR_ALIGN;
   if (!aligned(x_q, 16) || !aligned(s_x, 16) || !aligned(w_packed, 16) || !aligned(gamma, 4) ||
-      !aligned(y, 16) || (acc_out && !aligned(acc_out, 16)))
+      !aligned(y, 16) || (acc_out && !aligned(acc_out, 16)) || !aligned(bias, 16))
     return BITNET_ERR_ALIGN;
-  return from_hip(bitnet::launch_fwd(x_q, s_x, w_packed, gamma, M, N, K, y, acc_out, workspace,
+  return from_hip(bitnet::launch_fwd(x_q, s_x, w_packed, gamma, bias, M, N, K, y, acc_out, workspace,
                                      workspace_bytes, static_cast<hipStream_t>(stream)));
+}
+
+bitnet_status bitlinear_fwd(const int8_t* x_q, const float* s_x, const uint8_t* w_packed,
+                            const float* gamma, int64_t M, int64_t N, int64_t K, uint16_t* y,
+                            int32_t* acc_out, void* workspace, size_t workspace_bytes, void* stream) {
+  return bitlinear_fwd_bias(x_q, s_x, w_packed, gamma, nullptr, M, N, K, y, acc_out, workspace, workspace_bytes,
+                            stream);
+}
+
+bitnet_status bitlinear_bias_grad(const uint16_t* dY, int64_t M, int64_t N, void* db, bitnet_dtype db_dtype,
+                                  void* stream) {
+  if (!dY || !db) return BITNET_ERR_NULL;
+  if (db_dtype != BITNET_BF16 && db_dtype != BITNET_F32) return BITNET_ERR_DTYPE;
+  if (bitnet_status st = check_sizes(M, N)) return st;
+  if (!aligned(dY, 16) || !aligned(db, 16)) return BITNET_ERR_ALIGN;
+  return from_hip(bitnet::launch_bias_grad(dY, M, N, db, db_dtype == BITNET_F32, static_cast<hipStream_t>(stream)));
 }
 
 bitnet_status bitlinear_bwd(const uint16_t* dY, const int8_t* x_q, const float* s_x,

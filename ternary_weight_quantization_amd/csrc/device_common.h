@@ -18,6 +18,19 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
+// bf16 values b[n .. n+3] as floats, 0 at or past N (n a multiple of 4,
+// b 8-byte aligned).
+__device__ __forceinline__ float4 bias4(const uint16_t* b, int64_t N, int64_t n) {
+  if (n + 4 <= N) {
+    const uint2 v = *reinterpret_cast<const uint2*>(b + n);
+    return make_float4(bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y));
+  }
+  float r[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r[e] = n + e < N ? bf16_to_f32(b[n + e]) : 0.0f;
+  return make_float4(r[0], r[1], r[2], r[3]);
+}
+
 // Two floats -> packed bf16 pair (lo in bits 0..15), round half to even.
 // gfx950 has a native instruction for this (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {

@@ -808,7 +808,8 @@ struct FwdEpilogue {
   int32_t* acc_out;  // NULL: not written
   const float* s;
   const float* gamma;
-  int64_t I, J;  // N, M
+  int64_t I, J;          // N, M
+  const uint16_t* bias;  // [N] bf16 added before the rounding, or NULL
 
   // The scales this lane's columns need, loaded before the main loop so
   // that their latency is hidden (raw values; combined in store()).
@@ -833,10 +834,15 @@ struct FwdEpilogue {
 #pragma unroll
       for (int fi = 0; fi < kFI; ++fi)
 #pragma unroll
-        for (int gi = 0; gi < 4; ++gi)
-          EpStage<2>::put(wlds, lane, fi, gi,
-                          make_uint2(pack_bf16x2((float)acc[fi][fj][4 * gi] * c, (float)acc[fi][fj][4 * gi + 1] * c),
-                                     pack_bf16x2((float)acc[fi][fj][4 * gi + 2] * c, (float)acc[fi][fj][4 * gi + 3] * c)));
+        for (int gi = 0; gi < 4; ++gi) {
+          float v0 = (float)acc[fi][fj][4 * gi] * c, v1 = (float)acc[fi][fj][4 * gi + 1] * c;
+          float v2 = (float)acc[fi][fj][4 * gi + 2] * c, v3 = (float)acc[fi][fj][4 * gi + 3] * c;
+          if (bias != nullptr) {  // n = i0 + 32fi + 8gi + 4h + 0..3 (EpStage::put)
+            const float4 b = bias4(bias, I, i0 + 32 * fi + 8 * gi + 4 * (lane >> 5));
+            v0 += b.x; v1 += b.y; v2 += b.z; v3 += b.w;
+          }
+          EpStage<2>::put(wlds, lane, fi, gi, make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)));
+        }
       EpStage<2>::drain(wlds, reinterpret_cast<char*>(y), I, J, i0, j0 + 32 * fj, lane);
       if (acc_out != nullptr) {
 #pragma unroll
@@ -1653,14 +1659,14 @@ static hipError_t run_gemm(const PL& pl, const QL& ql, const EP& ep, const GemmS
 static bool skinny(int64_t M) { return M <= kSkinnyMaxM && getenv("BITNET_NO_SKINNY") == nullptr; }
 
 hipError_t launch_fwd(const int8_t* x_q, const float* s_x, const uint8_t* w_packed,
-                      const float* gamma, int64_t M, int64_t N, int64_t K, uint16_t* y,
+                      const float* gamma, const uint16_t* bias, int64_t M, int64_t N, int64_t K, uint16_t* y,
                       int32_t* acc_out, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (skinny(M))
-    return launch_fwd_skinny(x_q, s_x, w_packed, gamma, M, N, K, y, acc_out, stream);
+    return launch_fwd_skinny(x_q, s_x, w_packed, gamma, bias, M, N, K, y, acc_out, stream);
   const int64_t Kp = k_pad(K);
   PackedCodesLoader pl{w_packed, Kp / 4, N};
   CopyLoader<1, true> ql{reinterpret_cast<const char*>(x_q), Kp, M, Kp};
-  FwdEpilogue ep{y, acc_out, s_x, gamma, N, M};
+  FwdEpilogue ep{y, acc_out, s_x, gamma, N, M, bias};
   return run_gemm<MfmaI8, 1>(pl, ql, ep, shape_of(GemmKind::kFwd, M, N, K), ws, ws_bytes, stream);
 }
 

@@ -20,6 +20,11 @@ hipError_t launch_ternarize_pack(const void* W, bool w_is_f32, int64_t N, int64_
                                  uint8_t* w_packed, float* gamma, double* partials,
                                  hipStream_t stream);
 
+// Bias gradient db[n] = sum_m dY[m][n] (fp32, fixed order), db as f32 or
+// bf16 bits.
+hipError_t launch_bias_grad(const uint16_t* dY, int64_t M, int64_t N, void* db, bool db_is_f32,
+                            hipStream_t stream);
+
 // Per-token absmax int8 activation quantization.
 hipError_t launch_act_quant(const uint16_t* x, int64_t M, int64_t K,
                             int8_t* x_q, float* s_x, hipStream_t stream);
@@ -30,9 +35,10 @@ hipError_t launch_act_quant(const uint16_t* x, int64_t M, int64_t K,
 enum class GemmKind { kFwd, kBwdDx, kBwdDw, kBwdPair };
 size_t gemm_workspace_bytes(GemmKind kind, int64_t M, int64_t N, int64_t K);
 
-// INT8 forward GEMM with fused rescale (and optional int32 accumulators).
+// INT8 forward GEMM with fused rescale, an optional bf16 bias [N] (NULL:
+// none) and optional int32 accumulators.
 hipError_t launch_fwd(const int8_t* x_q, const float* s_x, const uint8_t* w_packed,
-                      const float* gamma, int64_t M, int64_t N, int64_t K,
+                      const float* gamma, const uint16_t* bias, int64_t M, int64_t N, int64_t K,
                       uint16_t* y, int32_t* acc_out, void* ws, size_t ws_bytes,
                       hipStream_t stream);
 
@@ -41,8 +47,8 @@ hipError_t launch_fwd(const int8_t* x_q, const float* s_x, const uint8_t* w_pack
 // (which calls it for such M).
 constexpr int64_t kSkinnyMaxM = 64;
 hipError_t launch_fwd_skinny(const int8_t* x_q, const float* s_x, const uint8_t* w_packed,
-                             const float* gamma, int64_t M, int64_t N, int64_t K, uint16_t* y,
-                             int32_t* acc_out, hipStream_t stream);
+                             const float* gamma, const uint16_t* bias, int64_t M, int64_t N, int64_t K,
+                             uint16_t* y, int32_t* acc_out, hipStream_t stream);
 
 // STE dX for few tokens (M <= kSkinnyMaxM, N % 8 == 0) from the fp4
 // transposed codes wt [Kp][Np/2] (Np = N rounded up to 64).

@@ -372,4 +372,56 @@ hipError_t launch_act_quant(const uint16_t* x, int64_t M, int64_t K, int8_t* x_q
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Bias gradient ("bitlinear.py", BitLinear: the optional bias is added after
+// the product, so its gradient is the token sum of dY): db[n] = sum_m dY[m][n]
+// in fp32, in a fixed order. A block of 1024 threads owns 64 columns: thread
+// (g = t / 8, c = t % 8) sums rows g, g + 128, ... of columns 8c .. 8c+7 in
+// row order (16-byte loads; a wave covers 8 rows x 128 bytes), then the 128
+// row groups' partial sums are added in group order.
+// ---------------------------------------------------------------------------
+
+constexpr int kBiasGroups = 128;
+
+__global__ __launch_bounds__(1024) void bias_grad_kernel(const uint16_t* __restrict__ dY, int64_t M, int64_t N,
+                                                         void* __restrict__ db, bool f32) {
+  __shared__ float part[kBiasGroups][64 + 1];
+  const int t = threadIdx.x, g = t >> 3, c = t & 7;
+  const int64_t n0 = (int64_t)blockIdx.x * 64 + 8 * c;
+  float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+  if (N % 8 == 0) {
+    if (n0 < N) {
+#pragma unroll 8
+      for (int64_t m = g; m < M; m += kBiasGroups) {
+        const uint4 v = *reinterpret_cast<const uint4*>(dY + m * N + n0);
+        acc[0] += bf16_lo(v.x); acc[1] += bf16_hi(v.x); acc[2] += bf16_lo(v.y); acc[3] += bf16_hi(v.y);
+        acc[4] += bf16_lo(v.z); acc[5] += bf16_hi(v.z); acc[6] += bf16_lo(v.w); acc[7] += bf16_hi(v.w);
+      }
+    }
+  } else {
+    for (int64_t m = g; m < M; m += kBiasGroups)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (n0 + e < N) acc[e] += bf16_to_f32(dY[m * N + n0 + e]);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) part[g][8 * c + e] = acc[e];
+  __syncthreads();
+  if (t < 64) {
+    float sum = 0.0f;
+    for (int i = 0; i < kBiasGroups; ++i) sum += part[i][t];
+    const int64_t n = (int64_t)blockIdx.x * 64 + t;
+    if (n < N) {
+      if (f32) static_cast<float*>(db)[n] = sum;
+      else static_cast<uint16_t*>(db)[n] = f32_to_bf16_bits(sum);
+    }
+  }
+}
+
+hipError_t launch_bias_grad(const uint16_t* dY, int64_t M, int64_t N, void* db, bool db_is_f32,
+                            hipStream_t stream) {
+  bias_grad_kernel<<<(unsigned)((N + 63) / 64), 1024, 0, stream>>>(dY, M, N, db, db_is_f32);
+  return hipGetLastError();
+}
+
 }  // namespace bitnet

@@ -1,7 +1,7 @@
 // Products for few tokens (M <= 64): the decode-shaped GEMMs of an inference
 // forward or a small training batch ("bitnet-qat-train", Semantics):
 //  - the INT8 forward, acc = sum_k x_q * q (INT32), y = bf16(acc * (s/127) *
-//    gamma);
+//    gamma [+ bias]);
 //  - the STE backward dX = dY * W_hat, W_hat = q * bf16(gamma), products
 //    exact in fp32 and sums in fp32.
 // At these sizes the cost is reading the codes once and the token operand
@@ -183,7 +183,8 @@ constexpr int skinny_lds() {
 // Forward: code rows n, tokens m; y [M][N] bf16, acc_out [M][N] int32 or NULL.
 template <int MT, int W, int P>
 __global__ __launch_bounds__(kWave * W) void fwd_skinny_kernel(SkArgs a, const float* __restrict__ s,
-                                                               const float* __restrict__ gamma, int64_t N,
+                                                               const float* __restrict__ gamma,
+                                                               const uint16_t* __restrict__ bias, int64_t N,
                                                                uint16_t* __restrict__ y,
                                                                int32_t* __restrict__ acc_out) {
   __shared__ __attribute__((aligned(16))) char smem[skinny_lds<MT, W>()];
@@ -194,16 +195,20 @@ __global__ __launch_bounds__(kWave * W) void fwd_skinny_kernel(SkArgs a, const f
   if (mt >= MT || m >= a.M) return;
   const float c = s[m] * *gamma / 127.0f;  // the large-M epilogue's expression
   const int64_t nb = (int64_t)blockIdx.x * 32 + 8 * g + 4 * h;
+  float f[4] = {(float)v[0] * c, (float)v[1] * c, (float)v[2] * c, (float)v[3] * c};
+  if (bias != nullptr) {
+    const float4 b = bias4(bias, N, nb);
+    f[0] += b.x; f[1] += b.y; f[2] += b.z; f[3] += b.w;
+  }
   uint16_t* yr = y + m * N;
   if (N % 4 == 0 && nb + 4 <= N) {
-    *reinterpret_cast<uint2*>(yr + nb) =
-        make_uint2(pack_bf16x2((float)v[0] * c, (float)v[1] * c), pack_bf16x2((float)v[2] * c, (float)v[3] * c));
+    *reinterpret_cast<uint2*>(yr + nb) = make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
     if (acc_out != nullptr) *reinterpret_cast<int4*>(acc_out + m * N + nb) = make_int4(v[0], v[1], v[2], v[3]);
   } else {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       if (nb + e >= N) break;
-      yr[nb + e] = f32_to_bf16_bits((float)v[e] * c);
+      yr[nb + e] = f32_to_bf16_bits(f[e]);
       if (acc_out != nullptr) acc_out[m * N + nb + e] = v[e];
     }
   }
@@ -235,15 +240,16 @@ __global__ __launch_bounds__(kWave * W) void dx_skinny_kernel(SkArgs a, const fl
 }
 
 hipError_t launch_fwd_skinny(const int8_t* x_q, const float* s_x, const uint8_t* w_packed, const float* gamma,
-                             int64_t M, int64_t N, int64_t K, uint16_t* y, int32_t* acc_out, hipStream_t stream) {
+                             const uint16_t* bias, int64_t M, int64_t N, int64_t K, uint16_t* y, int32_t* acc_out,
+                             hipStream_t stream) {
   if (M < 1 || M > kSkinnyMaxM) return hipErrorInvalidValue;
   const int64_t Kp = k_pad(K);
   const SkArgs a{w_packed, N, Kp / 4, Kp / 4, x_q, Kp, Kp, (int)M};
   const unsigned grid = (unsigned)((N + 31) / 32);
   if (M <= 32)
-    fwd_skinny_kernel<1, 16, 3><<<grid, kWave * 16, 0, stream>>>(a, s_x, gamma, N, y, acc_out);
+    fwd_skinny_kernel<1, 16, 3><<<grid, kWave * 16, 0, stream>>>(a, s_x, gamma, bias, N, y, acc_out);
   else
-    fwd_skinny_kernel<2, 8, 3><<<grid, kWave * 8, 0, stream>>>(a, s_x, gamma, N, y, acc_out);
+    fwd_skinny_kernel<2, 8, 3><<<grid, kWave * 8, 0, stream>>>(a, s_x, gamma, bias, N, y, acc_out);
   return hipGetLastError();
 }
 

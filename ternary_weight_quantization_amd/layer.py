@@ -42,11 +42,12 @@ def _workspace(nbytes, device):
 
 
 class BitLinearFunction(torch.autograd.Function):
-    """y = BitLinear(x, W) with the STE backward. x [..., K] bf16, W [N, K]
-    bf16 or float32; y [..., N] bf16. Gradients: dX bf16, dW in W's dtype."""
+    """y = BitLinear(x, W) (+ bias) with the STE backward. x [..., K] bf16,
+    W [N, K] bf16 or float32, bias [N] bf16 or None; y [..., N] bf16.
+    Gradients: dX bf16, dW in W's dtype, db bf16 (token sum of dY)."""
 
     @staticmethod
-    def forward(ctx, x, weight):
+    def forward(ctx, x, weight, bias=None):
         if x.dtype != torch.bfloat16:
             raise TypeError("BitLinear expects bf16 activations")
         N, K = weight.shape
@@ -57,50 +58,61 @@ class BitLinearFunction(torch.autograd.Function):
         x_q, s_x = act_quant(x2)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
         B.bitlinear_fwd(x_q, s_x, w_packed, gamma, K, y,
-                        workspace=_workspace(B.bitlinear_fwd_workspace_bytes(M, N, K), x.device))
+                        workspace=_workspace(B.bitlinear_fwd_workspace_bytes(M, N, K), x.device),
+                        bias=None if bias is None else bias.to(torch.bfloat16).contiguous())
         ctx.save_for_backward(x_q, s_x, w_packed, gamma)
-        ctx.shape = (M, N, K, lead, weight.dtype)
+        ctx.shape = (M, N, K, lead, weight.dtype, None if bias is None else bias.dtype)
         return y.reshape(*lead, N)
 
     @staticmethod
     def backward(ctx, dy):
         x_q, s_x, w_packed, gamma = ctx.saved_tensors
-        M, N, K, lead, wdtype = ctx.shape
+        M, N, K, lead, wdtype, bdtype = ctx.shape
         dY = dy.reshape(M, N).to(torch.bfloat16).contiguous()
-        need_x, need_w = ctx.needs_input_grad
+        need_x, need_w = ctx.needs_input_grad[:2]
         dX = torch.empty((M, K), dtype=torch.bfloat16, device=dy.device) if need_x else None
         dW = torch.empty((N, K), dtype=wdtype, device=dy.device) if need_w else None
         if dX is not None or dW is not None:
             B.bitlinear_bwd(dY, x_q, s_x, w_packed, gamma, K, dX=dX, dW=dW,
                             workspace=_workspace(B.bitlinear_bwd_workspace_bytes(M, N, K), dy.device))
-        return (None if dX is None else dX.reshape(*lead, K)), dW
+        db = None
+        if bdtype is not None and ctx.needs_input_grad[2]:
+            db = torch.empty((N,), dtype=torch.float32, device=dy.device)
+            B.bitlinear_bias_grad(dY, db)
+            db = db.to(bdtype)
+        return (None if dX is None else dX.reshape(*lead, K)), dW, db
 
 
 class QATBitLinear(torch.nn.Module):
     """Ternary-weight, int8-activation linear layer for quantization-aware
     training. Master weights [out_features, in_features] in bf16 (or f32),
     kaiming-uniform(a=sqrt(5)) init as in "bitlinear.py" BitLinear.__init__,
-    no bias."""
+    and, with bias=True, a zero-initialised bf16 bias added before the
+    output rounding (as that layer's optional bias; "bitnet-qat-train" has
+    none, the default)."""
 
-    def __init__(self, in_features, out_features, device="cuda", dtype=torch.bfloat16):
+    def __init__(self, in_features, out_features, device="cuda", dtype=torch.bfloat16, bias=False):
         super().__init__()
         self.in_features = in_features
         self.out_features = out_features
         w = torch.empty((out_features, in_features), dtype=torch.float32)
         torch.nn.init.kaiming_uniform_(w, a=math.sqrt(5))
         self.weight = torch.nn.Parameter(w.to(device=device, dtype=dtype))
+        self.bias = (torch.nn.Parameter(torch.zeros(out_features, device=device, dtype=torch.bfloat16))
+                     if bias else None)
 
     @classmethod
     def from_linear(cls, linear, dtype=torch.bfloat16):
-        if linear.bias is not None:
-            raise ValueError("QATBitLinear has no bias")
-        m = cls(linear.in_features, linear.out_features, device=linear.weight.device, dtype=dtype)
+        m = cls(linear.in_features, linear.out_features, device=linear.weight.device, dtype=dtype,
+                bias=linear.bias is not None)
         with torch.no_grad():
             m.weight.copy_(linear.weight.to(dtype))
+            if linear.bias is not None:
+                m.bias.copy_(linear.bias.to(torch.bfloat16))
         return m
 
     def forward(self, x):
-        return BitLinearFunction.apply(x, self.weight)
+        return BitLinearFunction.apply(x, self.weight, self.bias)
 
     @torch.no_grad()
     def export_inference(self):
@@ -109,4 +121,4 @@ class QATBitLinear(torch.nn.Module):
         return ternarize(self.weight.detach())
 
     def extra_repr(self):
-        return f"{self.in_features}, {self.out_features}, dtype={self.weight.dtype}"
+        return f"{self.in_features}, {self.out_features}, dtype={self.weight.dtype}, bias={self.bias is not None}"

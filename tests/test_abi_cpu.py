@@ -40,12 +40,15 @@ def L():
     lib.bitnet_act_quant.argtypes = [vp, i64, i64, vp, vp, vp]
     lib.bitlinear_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp, vp, sz, vp]
     lib.bitlinear_bwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp, vp, st, vp, sz, vp]
+    lib.bitlinear_fwd_bias.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp, vp, vp, sz, vp]
+    lib.bitlinear_bias_grad.argtypes = [vp, i64, i64, vp, st, vp]
     return lib
 
 
-def test_header_declares_the_four_entry_points():
+def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("bitnet_ternarize_pack", "bitnet_act_quant", "bitlinear_fwd", "bitlinear_bwd"):
+    for n in ("bitnet_ternarize_pack", "bitnet_act_quant", "bitlinear_fwd", "bitlinear_bwd",
+              "bitlinear_fwd_bias", "bitlinear_bias_grad"):
         assert n in names
 
 
@@ -140,3 +143,15 @@ def test_bwd_validation(L):
     ws = L.bitlinear_bwd_workspace_bytes(4, 4, 4)  # dW's x_hat
     assert L.bitlinear_bwd(MISALIGNED, A, A, A, A, 4, 4, 4, A, A, 0, A, ws, None) == EALIGN
     assert L.bitlinear_bwd(A, A, A, A, A, 4, 4, 4, MISALIGNED, None, 0, A, ws, None) == EALIGN
+
+
+def test_bias_validation(L):
+    # bitlinear_fwd_bias checks what bitlinear_fwd checks, plus the bias alignment
+    assert L.bitlinear_fwd_bias(None, A, A, A, A, 4, 4, 4, A, None, None, 0, None) == ENULL
+    assert L.bitlinear_fwd_bias(A, A, A, A, A, 0, 4, 4, A, None, None, 0, None) == ESHAPE
+    assert L.bitlinear_fwd_bias(A, A, A, A, A + 2, 4, 4, 4, A, None, None, 0, None) == EALIGN
+    assert L.bitlinear_bias_grad(None, 4, 4, A, 1, None) == ENULL
+    assert L.bitlinear_bias_grad(A, 4, 4, None, 1, None) == ENULL
+    assert L.bitlinear_bias_grad(A, 4, 4, A, 2, None) == EDTYPE
+    assert L.bitlinear_bias_grad(A, 0, 4, A, 1, None) == ESHAPE
+    assert L.bitlinear_bias_grad(A, 4, 4, MISALIGNED, 1, None) == EALIGN

@@ -120,6 +120,15 @@ def _sign1_inverted(dW, Kp=None):
 _sign1_ref = B.sign1_pack
 
 
+def _bias_grad_rows(dY):
+    d = np.asarray(dY, dtype=np.float64)
+    return d.sum(axis=1)[: d.shape[1]] if d.shape[0] >= d.shape[1] else np.resize(d.sum(axis=1), d.shape[1])
+
+
+def _forward_y_bias_minus(acc, s, gamma, bias):
+    return B.forward_y(acc, s, gamma) - np.asarray(bias, dtype=np.float64)[None, :]
+
+
 MUTATIONS = [
     ("absmean_gamma", _gamma_no_abs, ["test_gamma_closed_forms", "test_codes_zero_fraction_statistics"]),
     ("absmean_gamma", _gamma_max, ["test_gamma_closed_forms", "test_codes_zero_fraction_statistics"]),
@@ -136,6 +145,8 @@ MUTATIONS = [
     ("sign1_pack", _sign1_msb_first, ["test_sign1_hand_bytes", "test_sign1_matches_numpy_packbits"]),
     ("sign1_pack", _sign1_zero_negative, ["test_sign1_hand_bytes", "test_sign1_matches_numpy_packbits"]),
     ("sign1_pack", _sign1_inverted, ["test_sign1_hand_bytes", "test_sign1_of_ste_gradient_matches_quantised_gradient"]),
+    ("bias_grad", _bias_grad_rows, ["test_bias_grad_exact_column_sums", "test_bias_against_torch_autograd"]),
+    ("forward_y_bias", _forward_y_bias_minus, ["test_bias_against_torch_autograd"]),
 ]
 
 

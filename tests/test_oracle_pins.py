@@ -421,6 +421,41 @@ def test_against_torch_autograd_detach_ste():
     assert np.allclose(wt.grad.numpy(), r["dW"], rtol=1e-12, atol=1e-12)
 
 
+def test_bias_against_torch_autograd():
+    """The optional bias of "bitlinear.py" (BitLinear.forward: F.linear of
+    the STE operands with self.bias) in torch float64: its output and the
+    bias gradient torch's autograd gives equal the oracle's forward_y_bias
+    and bias_grad."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(17)
+    M, K, N = 12, 72, 20
+    x = bf16_vals(rng, (M, K))
+    w = rng.uniform(-1 / math.sqrt(K), 1 / math.sqrt(K), (N, K)).astype(np.float32)
+    b = bf16_vals(rng, (N,), 0.1)
+    dY = bf16_vals(rng, (M, N))
+    r = O.layer_fwd_bwd(x, w, dY, with_backward=False)
+    xt = torch.tensor(x)
+    bt = torch.tensor(b, requires_grad=True)
+    x_fq = torch.tensor(r["x_q"][:, :K].astype(np.float64) * r["s"][:, None].astype(np.float64) / 127.0)
+    w_fq = torch.tensor(r["q"].astype(np.float64) * float(r["gamma"]))
+    y = torch.nn.functional.linear(xt + (x_fq - xt).detach(), w_fq, bt)
+    ref = O.forward_y_bias(r["acc"], r["s"], r["gamma"], b)
+    assert np.allclose(y.detach().numpy(), ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+    y.backward(torch.tensor(dY))
+    assert np.allclose(bt.grad.numpy(), O.bias_grad(dY), rtol=1e-12, atol=1e-12)
+
+
+def test_bias_grad_exact_column_sums():
+    """bias_grad against exact Fraction column sums (3 x 5 and a ragged
+    7 x 1), which a row sum or a transposed operand would not give."""
+    rng = np.random.default_rng(19)
+    for M, N in ((3, 5), (7, 1), (64, 9)):
+        d = bf16_vals(rng, (M, N))
+        exact = [float(sum(Fraction(float(d[m, n])) for m in range(M))) for n in range(N)]
+        assert np.array_equal(O.bias_grad(d), np.array(exact)), (M, N)
+    assert np.array_equal(O.bias_grad(np.array([[1.0, 2.0, 3.0], [10.0, 20.0, 30.0]])), [11.0, 22.0, 33.0])
+
+
 # ---------------------------------------------------------------------------
 # the tiny 3-layer net of "1BitTraining.md"
 # ---------------------------------------------------------------------------
