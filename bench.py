@@ -370,15 +370,33 @@ def main():
     def bwd_sign1(s):
         B.bitlinear_bwd(s["dY"], s["x_q"], s["s_x"], s["w_packed"], s["gamma"], K, dX=s["dX"], dW=s["dW_sign1"])
 
-    for i in range(args.warmup):
-        bwd_sign1(sets[i % len(sets)])
-    ev1 = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        ev1[i][0].record()
-        bwd_sign1(sets[i % len(sets)])
-        ev1[i][1].record()
-    torch.cuda.synchronize()
-    sign1_ms = float(np.mean([a.elapsed_time(b) for a, b in ev1]))
+    # The forward with a bias and the bias gradient (the layer's optional
+    # bias), timed the same way; not part of the step.
+    for s in sets:
+        s["bias"] = torch.zeros((N,), dtype=torch.bfloat16, device=dev)
+        s["db"] = torch.empty((N,), dtype=torch.float32, device=dev)
+
+    def fwd_bias(s):
+        B.bitlinear_fwd(s["x_q"], s["s_x"], s["w_packed"], s["gamma"], K, s["y"], bias=s["bias"])
+
+    def bias_grad(s):
+        B.bitlinear_bias_grad(s["dY"], s["db"])
+
+    def per_call_ms(f):
+        for i in range(args.warmup):
+            f(sets[i % len(sets)])
+        ev1 = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+               for _ in range(args.steps)]
+        for i in range(args.steps):
+            ev1[i][0].record()
+            f(sets[i % len(sets)])
+            ev1[i][1].record()
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in ev1]))
+
+    sign1_ms = per_call_ms(bwd_sign1)
+    fwd_bias_ms = per_call_ms(fwd_bias)
+    bias_grad_ms = per_call_ms(bias_grad)
 
     gemm_ops = 2.0 * M * N * K
     tops = 3 * gemm_ops / (ms_per_step * 1e-3) / 1e12
@@ -427,7 +445,15 @@ def main():
             "ms": round(sign1_ms, 4), "bound": "mfma", "unit": "TFLOP/s",
             "achieved": round(2 * gemm_ops / 1e12 / (sign1_ms * 1e-3), 2),
             "frac": round(2 * gemm_ops / 1e12 / (sign1_ms * 1e-3) / PEAK_BF16_TFLOPS, 4),
-            "dW_bytes_written": N * Kp // 8}},
+            "dW_bytes_written": N * Kp // 8},
+            "fwd_bias": {
+                "ms": round(fwd_bias_ms, 4), "bound": "mfma", "unit": "TOP/s",
+                "achieved": round(gemm_ops / 1e12 / (fwd_bias_ms * 1e-3), 2),
+                "frac": round(gemm_ops / 1e12 / (fwd_bias_ms * 1e-3) / PEAK_INT8_TOPS, 4)},
+            "bias_grad": {
+                "ms": round(bias_grad_ms, 4), "bound": "hbm", "unit": "GB/s",
+                "achieved": round((2.0 * M * N + 4 * N) / 1e9 / (bias_grad_ms * 1e-3), 2),
+                "frac": round((2.0 * M * N + 4 * N) / 1e9 / (bias_grad_ms * 1e-3) / PEAK_HBM_GBS, 4)}},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
