@@ -1733,10 +1733,11 @@ hipError_t launch_bwd_dw(const uint16_t* dY, const int8_t* x_q, const float* s_x
   void* split_ws = static_cast<char*>(ws) + xb;
   const size_t split_bytes = ws_bytes - xb;
   if (hipError_t e = launch_xhat(x_q, s_x, M, K, xhat, stream)) return e;
-  if (skinny(M) && N % 8 == 0 && dw_out != DwOut::kSign1) {
+  const int64_t dw_tiles = (k_pad(K) + 255) / 256 * ((N + 63) / 64);
+  if (skinny(M) && N % 8 == 0 && dw_out != DwOut::kSign1 && dw_tiles < (int64_t(1) << 31)) {
     const int64_t Kp = k_pad(K);
     const int ktiles = (int)((Kp + 255) / 256);
-    const unsigned grid = (unsigned)(ktiles * ((N + 63) / 64));
+    const unsigned grid = (unsigned)dw_tiles;
     if (dw_out == DwOut::kF32)
       dw_skinny_kernel<true><<<grid, 256, 0, stream>>>(xhat, dY, (int)M, N, Kp, K, ktiles, dW);
     else
