@@ -98,8 +98,8 @@ def _pmc_rows(d):
     return rows
 
 
-# kernels of calls outside the step (the sign-output backward)
-KERNEL_EXCLUDE = ["Sign1Epilogue"]
+# kernels of calls outside the step (the sign-output backward, the forward with a bias)
+KERNEL_EXCLUDE = ["Sign1Epilogue", "FwdEpilogue<true>"]
 
 
 def _per_dispatch_mean(rows, counter, match):

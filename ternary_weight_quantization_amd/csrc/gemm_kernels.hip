@@ -803,13 +803,16 @@ struct EpStage {
   }
 };
 
+// BIAS: a bf16 bias [N] is added before the rounding (a separate
+// instantiation, so that the plain epilogue keeps its registers).
+template <bool BIAS>
 struct FwdEpilogue {
   uint16_t* y;
   int32_t* acc_out;  // NULL: not written
   const float* s;
   const float* gamma;
   int64_t I, J;          // N, M
-  const uint16_t* bias;  // [N] bf16 added before the rounding, or NULL
+  const uint16_t* bias;  // [N] bf16 (BIAS only)
 
   // The scales this lane's columns need, loaded before the main loop so
   // that their latency is hidden (raw values; combined in store()).
@@ -837,7 +840,7 @@ struct FwdEpilogue {
         for (int gi = 0; gi < 4; ++gi) {
           float v0 = (float)acc[fi][fj][4 * gi] * c, v1 = (float)acc[fi][fj][4 * gi + 1] * c;
           float v2 = (float)acc[fi][fj][4 * gi + 2] * c, v3 = (float)acc[fi][fj][4 * gi + 3] * c;
-          if (bias != nullptr) {  // n = i0 + 32fi + 8gi + 4h + 0..3 (EpStage::put)
+          if constexpr (BIAS) {  // n = i0 + 32fi + 8gi + 4h + 0..3 (EpStage::put)
             const float4 b = bias4(bias, I, i0 + 32 * fi + 8 * gi + 4 * (lane >> 5));
             v0 += b.x; v1 += b.y; v2 += b.z; v3 += b.w;
           }
@@ -1666,8 +1669,11 @@ hipError_t launch_fwd(const int8_t* x_q, const float* s_x, const uint8_t* w_pack
   const int64_t Kp = k_pad(K);
   PackedCodesLoader pl{w_packed, Kp / 4, N};
   CopyLoader<1, true> ql{reinterpret_cast<const char*>(x_q), Kp, M, Kp};
-  FwdEpilogue ep{y, acc_out, s_x, gamma, N, M, bias};
-  return run_gemm<MfmaI8, 1>(pl, ql, ep, shape_of(GemmKind::kFwd, M, N, K), ws, ws_bytes, stream);
+  if (bias != nullptr)
+    return run_gemm<MfmaI8, 1>(pl, ql, FwdEpilogue<true>{y, acc_out, s_x, gamma, N, M, bias},
+                               shape_of(GemmKind::kFwd, M, N, K), ws, ws_bytes, stream);
+  return run_gemm<MfmaI8, 1>(pl, ql, FwdEpilogue<false>{y, acc_out, s_x, gamma, N, M, nullptr},
+                             shape_of(GemmKind::kFwd, M, N, K), ws, ws_bytes, stream);
 }
 
 static hipError_t launch_wt(const uint8_t* w_packed, int64_t N, int64_t K, uint8_t* wt, hipStream_t stream) {
