@@ -228,13 +228,26 @@ __device__ __forceinline__ uint32_t pack_i8x4(float a, float b, float c, float d
   return perm(hi, lo, 0x05040100u);
 }
 
+// quant1 over the 8 values of a chunk: the fast results and one flag for
+// the chunk, then (rarely) the exact recompute of the flagged values, so
+// that the common path has no branch per value. Same decisions and results
+// as quant1 value by value.
 __device__ __forceinline__ uint2 quant8(uint4 v, float r127, float s) {
-  uint2 o;
-  o.x = pack_i8x4(quant1(bf16_lo(v.x), r127, s), quant1(bf16_hi(v.x), r127, s),
-                  quant1(bf16_lo(v.y), r127, s), quant1(bf16_hi(v.y), r127, s));
-  o.y = pack_i8x4(quant1(bf16_lo(v.z), r127, s), quant1(bf16_hi(v.z), r127, s),
-                  quant1(bf16_lo(v.w), r127, s), quant1(bf16_hi(v.w), r127, s));
-  return o;
+  const float x[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                      bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+  float t[8];
+  bool slow = false;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float p = x[e] * r127;
+    t[e] = p + kRoundMagic;
+    slow |= fabsf(p - (t[e] - kRoundMagic)) > 0.49996948f;
+  }
+  if (slow) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t[e] = quant1(x[e], r127, s);
+  }
+  return make_uint2(pack_i8x4(t[0], t[1], t[2], t[3]), pack_i8x4(t[4], t[5], t[6], t[7]));
 }
 
 __device__ __forceinline__ float absmax8(uint4 v) {
