@@ -1,4 +1,5 @@
-"""CPU oracle for the BitNet b1.58 BitLinear (ternary weights, int8 activations).
+"""CPU oracle for the BitNet b1.58 BitLinear (ternary weights, int8 activations)
+and for the TTQ variant (ternary weights with trained asymmetric scales).
 
 TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import or call anything in this
@@ -31,4 +32,15 @@ from .bitlinear_oracle import (  # noqa: F401
     dx_elements,
     dw_elements,
     y_elements,
+)
+from .ttq_oracle import (  # noqa: F401
+    ttq_init,
+    ttq_codes,
+    ttq_values,
+    ttq_forward,
+    ttq_backward,
+    ttq_layer,
+    ttq_y_elements,
+    ttq_dx_elements,
+    ttq_dw_elements,
 )

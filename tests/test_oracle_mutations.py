@@ -161,3 +161,85 @@ def test_planted_mistake_is_caught(monkeypatch, name, fn, pins):
         except (AssertionError, ValueError):
             caught.append(pin)
     assert caught, f"mutation {fn.__name__} of {name} passed every pin in {pins}"
+
+
+# ---------------------------------------------------------------------------
+# TTQ oracle
+# ---------------------------------------------------------------------------
+
+import math  # noqa: E402
+
+import oracle.ttq_oracle as T  # noqa: E402
+
+
+def _ttq_codes_inclusive(w, delta):
+    w = np.asarray(w, dtype=np.float64)
+    d = np.float64(delta)
+    return np.where(w >= d, 1, np.where(w <= -d, -1, 0)).astype(np.int8)
+
+
+def _ttq_init_half(w):
+    e = B.absmean_gamma(w)
+    return np.float32(0.5 * e), np.float32(e), np.float32(e)
+
+
+def _ttq_values_swapped(q, wp, wn):
+    q = np.asarray(q)
+    p = B.bf16_round(np.float64(wn))
+    n = B.bf16_round(np.float64(wp))
+    return np.where(q == 1, p, np.where(q == -1, -n, 0.0))
+
+
+def _ttq_values_unrounded(q, wp, wn):
+    q = np.asarray(q)
+    return np.where(q == 1, np.float64(wp), np.where(q == -1, -np.float64(wn), 0.0))
+
+
+def _ttq_backward_wn_sign(dY, x, q, wp, wn):
+    dX, dW, g_wp, g_wn = _ttq_backward_ref(dY, x, q, wp, wn)
+    return dX, dW, g_wp, -g_wn
+
+
+def _ttq_backward_wp_all_nonzero(dY, x, q, wp, wn):
+    dX, dW, g_wp, g_wn = _ttq_backward_ref(dY, x, q, wp, wn)
+    return dX, dW, math.fsum(dW[np.asarray(q) != 0].tolist()), g_wn
+
+
+def _ttq_backward_dx_unsigned(dY, x, q, wp, wn):
+    dX, dW, g_wp, g_wn = _ttq_backward_ref(dY, x, q, wp, wn)
+    return np.asarray(dY, np.float64) @ np.abs(T.ttq_values(q, wp, wn)), dW, g_wp, g_wn
+
+
+def _ttq_backward_dw_scaled(dY, x, q, wp, wn):
+    # the paper's scaled gradient instead of the page's identity STE
+    dX, dW, g_wp, g_wn = _ttq_backward_ref(dY, x, q, wp, wn)
+    q = np.asarray(q)
+    s = np.where(q == 1, np.float64(wp), np.where(q == -1, np.float64(wn), 1.0))
+    return dX, dW * s, g_wp, g_wn
+
+
+_ttq_backward_ref = T.ttq_backward
+
+TTQ_MUTATIONS = [
+    ("ttq_codes", _ttq_codes_inclusive, ["test_ttq_codes_strict_threshold", "test_ttq_reduces_to_bitnet_quantizer"]),
+    ("ttq_init", _ttq_init_half, ["test_ttq_init_hand_example", "test_ttq_init_is_point_seven_of_mean_abs"]),
+    ("ttq_values", _ttq_values_swapped, ["test_ttq_values_hand", "test_ttq_against_torch_autograd"]),
+    ("ttq_values", _ttq_values_unrounded, ["test_ttq_values_hand", "test_ttq_reduces_to_bitnet_quantizer"]),
+    ("ttq_backward", _ttq_backward_wn_sign, ["test_ttq_against_torch_autograd", "test_ttq_grads_exact_fractions"]),
+    ("ttq_backward", _ttq_backward_wp_all_nonzero, ["test_ttq_against_torch_autograd", "test_ttq_grads_exact_fractions"]),
+    ("ttq_backward", _ttq_backward_dx_unsigned, ["test_ttq_against_torch_autograd", "test_ttq_grads_exact_fractions"]),
+    ("ttq_backward", _ttq_backward_dw_scaled, ["test_ttq_against_torch_autograd", "test_ttq_grads_exact_fractions"]),
+]
+
+
+@pytest.mark.parametrize("name,fn,pins", TTQ_MUTATIONS, ids=[f"{m[0]}:{m[1].__name__}" for m in TTQ_MUTATIONS])
+def test_planted_ttq_mistake_is_caught(monkeypatch, name, fn, pins):
+    monkeypatch.setattr(T, name, fn)
+    monkeypatch.setattr(O, name, fn)
+    caught = []
+    for pin in pins:
+        try:
+            getattr(P, pin)()
+        except (AssertionError, ValueError):
+            caught.append(pin)
+    assert caught, f"mutation {fn.__name__} of {name} passed every pin in {pins}"

@@ -636,3 +636,158 @@ def test_kaiming_bound_matches_printed_init():
     d = WL.custom_inputs(8, 10, 20)
     w = WL.bf16_bits_to_f32(d["W"])
     assert np.all(np.abs(w) <= b * (1 + 2 ** -8))
+
+
+# ---------------------------------------------------------------------------
+# TTQ ("TTQ_VERIFICATION.md")
+# ---------------------------------------------------------------------------
+
+def rne_f32(fr):
+    """Round a nonzero Fraction in the normal fp32 range to 24 significant
+    bits, ties to even."""
+    sgn = -1 if fr < 0 else 1
+    a = abs(fr)
+    e = 0
+    while a >= 2 ** 24:
+        a /= 2
+        e += 1
+    while a < 2 ** 23:
+        a *= 2
+        e -= 1
+    return sgn * Fraction(rne_int(a)) * (Fraction(2) ** e)
+
+
+def test_ttq_init_hand_example():
+    """Initialization (Eq. 2): W = [0.75, -0.25, 0.125, -0.5] has E|W| =
+    1.625 / 4 = 0.40625 (exact), so Wp = Wn = 0.40625 and delta is
+    0.7 (as fp32) times 0.40625, rounded once to fp32; with that delta the
+    codes of Eq. 1 are [+1, 0, 0, -1]."""
+    w = np.array([[0.75, -0.25, 0.125, -0.5]], dtype=np.float32)
+    delta, wp, wn = O.ttq_init(w)
+    assert float(wp) == 0.40625 and float(wn) == 0.40625
+    expect = rne_f32(Fraction(float(np.float32(0.7))) * Fraction(13, 32))
+    assert Fraction(float(delta)) == expect
+    assert 0.28 < float(delta) < 0.29
+    assert O.ttq_codes(w, delta).tolist() == [[1, 0, 0, -1]]
+
+
+def test_ttq_init_is_point_seven_of_mean_abs():
+    """delta / E stays within one fp32 rounding of 0.7, and E is the
+    exactly rounded mean of |W| (compared with a Fraction sum), over
+    random bf16 and fp32 weights of several sizes."""
+    rng = np.random.default_rng(31)
+    for shape in ((3, 5), (17, 64), (64, 130)):
+        w = rng.standard_normal(shape).astype(np.float32) * 0.02
+        delta, wp, wn = O.ttq_init(w)
+        exact = sum(Fraction(float(v)) for v in np.abs(w).ravel()) / w.size
+        assert Fraction(float(wp)) == rne_f32(exact) and wp == wn
+        assert Fraction(float(delta)) == rne_f32(Fraction(float(np.float32(0.7))) * Fraction(float(wp)))
+
+
+def test_ttq_codes_strict_threshold():
+    """Eq. 1 is strict on both sides: |w| == delta gives 0, the next fp32
+    value above gives +-1; brute force against exact comparisons of
+    Fractions on random values near the threshold."""
+    d = np.float32(0.3)
+    up = np.nextafter(d, np.float32(1))
+    dn = np.nextafter(d, np.float32(0))
+    w = np.array([[d, -d, up, -up, dn, -dn, 0.0, 5.0, -5.0]], dtype=np.float32)
+    assert O.ttq_codes(w, d).tolist() == [[0, 0, 1, -1, 0, 0, 0, 1, -1]]
+    rng = np.random.default_rng(37)
+    w = (np.float32(0.3) + rng.integers(-3, 4, (40, 9)).astype(np.float32) * np.float32(2 ** -25)) \
+        * rng.choice([-1, 1], (40, 9)).astype(np.float32)
+    q = O.ttq_codes(w, d)
+    fd = Fraction(float(d))
+    for (i, j), v in np.ndenumerate(w):
+        fv = Fraction(float(v))
+        assert q[i, j] == (1 if fv > fd else -1 if fv < -fd else 0), (v, q[i, j])
+
+
+def test_ttq_values_hand():
+    """Values of Eq. 1 in bf16: code +1 -> bf16(Wp), -1 -> -bf16(Wn), 0 -> 0,
+    with the bf16 rounding taken from exact Fraction arithmetic."""
+    wp, wn = np.float32(0.3), np.float32(0.7)
+    v = O.ttq_values(np.array([[1, 0, -1, 1]]), wp, wn)
+    p = float(rne_bf16(Fraction(float(wp))))
+    n = float(rne_bf16(Fraction(float(wn))))
+    assert v.tolist() == [[p, 0.0, -n, p]]
+    assert p != float(wp) and n != float(wn)  # the rounding is not a no-op here
+
+
+def test_ttq_against_torch_autograd():
+    """Independent route: Eq. 1 written with torch.where on leaf tensors Wp
+    and Wn and an identity straight-through path to W (W_q + W - W.detach()),
+    in torch float64 on the CPU. Autograd's gradients of x, W, Wp and Wn
+    equal the oracle's dX, dW, grad_Wp and grad_Wn, and y matches."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(41)
+    M, K, N = 12, 40, 18
+    x = bf16_vals(rng, (M, K))
+    w = bf16_vals(rng, (N, K), 0.05)
+    dY = bf16_vals(rng, (M, N))
+    wp, wn, delta = np.float32(0.046875), np.float32(0.03515625), np.float32(0.035)  # Wp, Wn bf16-exact
+    r = O.ttq_layer(x, w, dY, params=(delta, wp, wn))
+    xt = torch.tensor(x, requires_grad=True)
+    W = torch.tensor(w, requires_grad=True)
+    tp = torch.tensor(float(wp), dtype=torch.float64, requires_grad=True)
+    tn = torch.tensor(float(wn), dtype=torch.float64, requires_grad=True)
+    d = float(delta)
+    zero = torch.zeros((), dtype=torch.float64)
+    wq = torch.where(W > d, tp, torch.where(W < -d, -tn, zero))
+    y = torch.nn.functional.linear(xt, wq + W - W.detach())
+    y.backward(torch.tensor(dY))
+    assert np.allclose(y.detach().numpy(), r["y"], rtol=1e-12, atol=1e-14)
+    assert np.allclose(xt.grad.numpy(), r["dX"], rtol=1e-12, atol=1e-14)
+    assert np.allclose(W.grad.numpy(), r["dW"], rtol=1e-12, atol=1e-14)
+    assert math.isclose(tp.grad.item(), r["g_wp"], rel_tol=1e-12, abs_tol=1e-12)
+    assert math.isclose(tn.grad.item(), r["g_wn"], rel_tol=1e-12, abs_tol=1e-12)
+    assert (r["q"] == 1).any() and (r["q"] == -1).any() and (r["q"] == 0).any()
+
+
+def test_ttq_reduces_to_bitnet_quantizer():
+    """With Wp = Wn = gamma and delta = gamma / 2 (exact in fp32), TTQ's codes
+    are the BitNet RoundClip codes (ties at |w| = gamma/2 go to 0 in both),
+    its values are q * bf16(gamma) and its dX is the BitNet STE dX."""
+    w = np.array([[1.0, -0.5, 0.25, -0.25]], dtype=np.float32)
+    g = O.absmean_gamma(w)
+    assert float(g) == 0.5  # so +-0.25 sit exactly at gamma / 2
+    half = np.float32(g / np.float32(2))
+    q = O.ttq_codes(w, half)
+    assert q.tolist() == [[1, -1, 0, 0]]
+    assert np.array_equal(q, O.ternary_codes(w, g))
+    assert np.array_equal(O.ttq_values(q, g, g), O.w_hat(q, g))
+    rng = np.random.default_rng(43)
+    w = bf16_vals(rng, (24, 70), 0.05)
+    g = O.absmean_gamma(w)
+    half = np.float32(g / np.float32(2))
+    q = O.ttq_codes(w, half)
+    assert np.array_equal(q, O.ternary_codes(w, g))
+    dY = bf16_vals(rng, (9, 24))
+    x = bf16_vals(rng, (9, 70))
+    dX_ttq = O.ttq_backward(dY, x, q, g, g)[0]
+    x_q, s = O.act_quant(x)
+    dX_bitnet = O.backward(dY, x_q, s, q, g)[0]
+    assert np.array_equal(dX_ttq, dX_bitnet)
+
+
+def test_ttq_grads_exact_fractions():
+    """With small-integer dY and x every dW entry is an exact integer: the
+    oracle's dW, grad_Wp and grad_Wn equal Python integer sums (ragged
+    shapes; the codes pattern from random signs)."""
+    rng = np.random.default_rng(47)
+    for M, N, K in ((5, 3, 7), (33, 17, 65), (64, 40, 130)):
+        dY = rng.integers(-3, 4, (M, N)).astype(np.float64)
+        x = rng.integers(-3, 4, (M, K)).astype(np.float64)
+        q = rng.integers(-1, 2, (N, K)).astype(np.int8)
+        dX, dW, g_wp, g_wn = O.ttq_backward(dY, x, q, np.float32(0.5), np.float32(0.25))
+        dYi = dY.astype(np.int64)
+        xi = x.astype(np.int64)
+        dWi = [[sum(int(dYi[m, n]) * int(xi[m, k]) for m in range(M)) for k in range(K)] for n in range(N)]
+        assert dW.tolist() == [[float(v) for v in row] for row in dWi]
+        ep = sum(dWi[n][k] for n in range(N) for k in range(K) if q[n, k] == 1)
+        en = -sum(dWi[n][k] for n in range(N) for k in range(K) if q[n, k] == -1)
+        assert g_wp == float(ep) and g_wn == float(en)
+        # dX on exact values: 0.5 and 0.25 are bf16-exact
+        ex = [[sum(int(dYi[m, n]) * Fraction(0.5 if q[n, k] == 1 else -0.25 if q[n, k] == -1 else 0)
+                   for n in range(N)) for k in range(K)] for m in range(M)]
+        assert dX.tolist() == [[float(v) for v in row] for row in ex]
