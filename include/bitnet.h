@@ -5,7 +5,9 @@
  * (W1.58 / A8), for quantization-aware training: the weight ternarization
  * and 2-bit packing, the per-token int8 activation quantization, the INT8
  * forward GEMM and the straight-through-estimator (STE) backward GEMMs.
- * The operations are those of the "bitnet-qat-train" page (Hugging Face
+ * A TTQ variant (learned threshold and asymmetric scales, bf16 activations)
+ * is declared at the end. The BitNet operations are those of the
+ * "bitnet-qat-train" page (Hugging Face
  * kernels, phanerozoic): its opening bullets and its "Semantics" section,
  * with the quantizers of "bitlinear.py" (h4-polytopic-attention:
  * ternary_quantize, activation_quant_int8) and "1BitTraining.md" (Codys12
@@ -225,6 +227,94 @@ bitnet_status bitlinear_bwd(const uint16_t* dY,
                             uint16_t* dX, void* dW, bitnet_dtype dW_dtype,
                             void* workspace, size_t workspace_bytes,
                             void* stream);
+
+/*
+ * TTQ: trained ternary quantization ("TTQ_VERIFICATION.md", LabStrangeLoop
+ * bitnet, summarising Zhu et al.), the variant with a learned threshold and
+ * two learned scales per layer. params is a device float[3] =
+ * {delta, Wp, Wn} (positive values; a caller that learns them through a
+ * positivity transform passes the transformed values). Activations are the
+ * layer's bf16 inputs, unquantized ("Bugs Fixed", item 4); the products run
+ * on bf16 operands with fp32 accumulation. The quantized weight is kept as
+ * its 2-bit codes (the w_packed format above) and as bf16 values
+ * wt [N][Kp] = bf16(Wp), -bf16(Wn) or 0 (round half to even; padding 0).
+ */
+
+/* Bytes of workspace ttq_fwd and ttq_bwd need for these sizes (0 for sizes
+ * they reject): the split-tile workspace of their GEMMs, as for
+ * bitlinear_fwd, and for ttq_bwd 8 bytes per 128 x 128 tile of dW for the
+ * scale-gradient partial sums. No initialization needed; graph replays are
+ * safe; not shared by calls that may run at the same time. */
+size_t ttq_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
+ * ttq_init - the initial parameters (Algorithm Summary, Initialization,
+ * Eq. 2): E = mean |W| computed exactly as bitnet_ternarize_pack's gamma
+ * (the same bits, floor 1e-8 included), delta = fl32(0.7f * E) (one fp32
+ * multiplication), Wp = Wn = E.
+ *
+ * W       [N][K] bf16 bits or float (w_dtype), 16-byte aligned.
+ * params  [3] output float (device, 4-byte aligned).
+ * workspace at least bitnet_ternarize_workspace_bytes(N, K); clobbered.
+ */
+bitnet_status ttq_init(const void* W, bitnet_dtype w_dtype, int64_t N, int64_t K,
+                       float* params, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/*
+ * ttq_quantize - Eq. 1 in one pass over W: code +1 where W > delta, -1
+ * where W < -delta, 0 elsewhere (strict, exact comparisons).
+ *
+ * W         [N][K] bf16 bits or float (w_dtype).
+ * params    [3] float (device): delta, Wp, Wn.
+ * w_packed  [N][Kp/4] output codes (the bitnet_ternarize_pack format).
+ * wt        [N][Kp] output bf16 bits: bf16(Wp), -bf16(Wn) or 0.
+ * No workspace.
+ */
+bitnet_status ttq_quantize(const void* W, bitnet_dtype w_dtype, int64_t N, int64_t K,
+                           const float* params, uint8_t* w_packed, uint16_t* wt,
+                           void* stream);
+
+/*
+ * ttq_fwd - y[m,n] = sum_k x[m,k] * wt[n,k] (Eq. 1's weight applied to the
+ * unquantized activations), fp32 sums rounded once to bf16.
+ *
+ * x   [M][K] bf16 bits.  wt [N][Kp] from ttq_quantize.  y [M][N] bf16 bits.
+ * workspace ttq_workspace_bytes(M, N, K) bytes (NULL when that is 0).
+ * Limits as for the GEMMs above, with (M + 256) * 2K and (N + 256) * 2Kp
+ * bytes for x and wt.
+ */
+bitnet_status ttq_fwd(const uint16_t* x, const uint16_t* wt, int64_t M, int64_t N, int64_t K,
+                      uint16_t* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ttq_bwd - the straight-through backward (Algorithm Summary, Backward
+ * Pass; "Bugs Fixed", item 5):
+ *
+ *   dX[m,k] = sum_n dY[m,n] * wt[n,k]
+ *   dW[n,k] = sum_m dY[m,n] * x[m,k]   (the latent weight's gradient is
+ *                                       the quantized weight's, unchanged)
+ *   grads[0] = dL/dWp =   sum of dW[n,k] over the codes +1
+ *   grads[1] = dL/dWn = - sum of dW[n,k] over the codes -1
+ *
+ * The masked sums take the fp32 dW values before rounding, add them per
+ * 128 x 128 tile in fp32 and across tiles in fp64, in a fixed order
+ * (bitwise deterministic across calls), rounded once to fp32. delta gets no
+ * gradient (the hard threshold has none).
+ *
+ * dY  [M][N] bf16 bits.  x [M][K] bf16 bits (needed for dW).
+ * wt  from ttq_quantize (needed for dX); w_packed its codes (needed for
+ *     grads).
+ * dX  [M][K] bf16 bits output, or NULL.
+ * dW  [N][K] output in dW_dtype (BITNET_BF16 or BITNET_F32), or NULL.
+ * grads [2] float output (device, 4-byte aligned), or NULL; needs dW.
+ * At least one of dX, dW is non-NULL.
+ * workspace ttq_workspace_bytes(M, N, K) bytes; clobbered.
+ */
+bitnet_status ttq_bwd(const uint16_t* dY, const uint16_t* x, const uint16_t* wt,
+                      const uint8_t* w_packed, int64_t M, int64_t N, int64_t K,
+                      uint16_t* dX, void* dW, bitnet_dtype dW_dtype, float* grads,
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

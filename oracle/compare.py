@@ -46,9 +46,9 @@ def rel_errors(got, ref, floor_frac):
 
 
 def check(got, ref, what):
-    """Assert the bar for one output: 'y' (no floor) or 'dX'/'dW'/'db' and
-    'y_bias' (floor 2^-8 RMS: sums in fp32, and a bias that can cancel the
-    product). Returns the metrics."""
+    """Assert the bar for one output: 'y' (no floor) or 'dX'/'dW'/'db',
+    'y_bias' and 'y_ttq' (floor 2^-8 RMS: sums in fp32, and a bias or the
+    TTQ forward's fp32 sums that can cancel). Returns the metrics."""
     floor = 0.0 if what == "y" else 2.0 ** -8
     m = rel_errors(got, ref, floor)
     assert m["max_rel"] <= MAX_REL, (what, m)

@@ -70,6 +70,16 @@ def lib():
     L.bitlinear_bias_grad.restype = st
     L.bitlinear_bwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp, vp, st, vp, sz, vp]
     L.bitlinear_bwd.restype = st
+    L.ttq_workspace_bytes.argtypes = [i64, i64, i64]
+    L.ttq_workspace_bytes.restype = sz
+    L.ttq_init.argtypes = [vp, st, i64, i64, vp, vp, sz, vp]
+    L.ttq_init.restype = st
+    L.ttq_quantize.argtypes = [vp, st, i64, i64, vp, vp, vp, vp]
+    L.ttq_quantize.restype = st
+    L.ttq_fwd.argtypes = [vp, vp, i64, i64, i64, vp, vp, sz, vp]
+    L.ttq_fwd.restype = st
+    L.ttq_bwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp, st, vp, vp, sz, vp]
+    L.ttq_bwd.restype = st
     if len(_hip_runtimes_mapped()) > 1:
         raise RuntimeError("more than one libamdhip64 is mapped into this process: "
                            f"{sorted(_hip_runtimes_mapped())}")
@@ -242,3 +252,81 @@ def bitlinear_bwd(dY, x_q, s_x, w_packed, gamma, K, dX=None, dW=None, workspace=
     _check(lib().bitlinear_bwd(_ptr(dY), _ptr(x_q), _ptr(s_x), _ptr(w_packed), _ptr(gamma),
                                M, N, int(K), _ptr(dX), _ptr(dW), dw_dtype, _ptr(workspace), ws_bytes,
                                _stream(stream)))
+
+
+# --- TTQ ---------------------------------------------------------------------
+
+def ttq_workspace_bytes(M, N, K):
+    return int(lib().ttq_workspace_bytes(int(M), int(N), int(K)))
+
+
+def _w_dtype(W):
+    if W.dtype == torch.bfloat16:
+        return BITNET_BF16
+    if W.dtype == torch.float32:
+        return BITNET_F32
+    raise TypeError(f"W: expected bfloat16 or float32, got {W.dtype}")
+
+
+def ttq_init(W, params, workspace, stream=None):
+    """W [N, K] bf16 or float32 -> params float32 [3] = (delta, Wp, Wn)."""
+    N, K = W.shape
+    wd = _w_dtype(W)
+    _need(W, W.dtype, (N, K), "W")
+    _need(params, torch.float32, (3,), "params")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().ttq_init(_ptr(W), wd, N, K, _ptr(params), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def ttq_quantize(W, params, w_packed, wt, stream=None):
+    """W [N, K], params (delta, Wp, Wn) -> codes uint8 [N, Kp/4] and bf16
+    values wt [N, Kp]."""
+    N, K = W.shape
+    Kp = bitnet_k_pad(K)
+    wd = _w_dtype(W)
+    _need(W, W.dtype, (N, K), "W")
+    _need(params, torch.float32, (3,), "params")
+    _need(w_packed, torch.uint8, (N, Kp // 4), "w_packed")
+    _need(wt, torch.bfloat16, (N, Kp), "wt")
+    _check(lib().ttq_quantize(_ptr(W), wd, N, K, _ptr(params), _ptr(w_packed), _ptr(wt), _stream(stream)))
+
+
+def ttq_fwd(x, wt, y, workspace=None, stream=None):
+    """y [M, N] bf16 = x [M, K] bf16 @ wt[:, :K]^T."""
+    M, K = x.shape
+    N, Kp = wt.shape
+    if Kp != bitnet_k_pad(K):
+        raise ValueError("wt: second dimension must be bitnet_k_pad(K)")
+    _need(x, torch.bfloat16, (M, K), "x")
+    _need(wt, torch.bfloat16, (N, Kp), "wt")
+    _need(y, torch.bfloat16, (M, N), "y")
+    if workspace is None:
+        workspace = _workspace(ttq_workspace_bytes(M, N, K), y, stream)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().ttq_fwd(_ptr(x), _ptr(wt), M, N, K, _ptr(y), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def ttq_bwd(dY, x, wt, w_packed, K, dX=None, dW=None, grads=None, workspace=None, stream=None):
+    """dX [M, K] bf16, dW [N, K] (bf16 or float32) and grads float32 [2] =
+    (dL/dWp, dL/dWn), each optional (grads needs dW)."""
+    M, N = dY.shape
+    Kp = bitnet_k_pad(K)
+    _need(dY, torch.bfloat16, (M, N), "dY")
+    if dX is not None:
+        _need(wt, torch.bfloat16, (N, Kp), "wt")
+        _need(dX, torch.bfloat16, (M, int(K)), "dX")
+    dw_dtype = BITNET_BF16
+    if dW is not None:
+        _need(x, torch.bfloat16, (M, int(K)), "x")
+        if dW.dtype not in (torch.bfloat16, torch.float32):
+            raise TypeError("dW: expected bfloat16 or float32")
+        _need(dW, dW.dtype, (N, int(K)), "dW")
+        dw_dtype = BITNET_F32 if dW.dtype == torch.float32 else BITNET_BF16
+    if grads is not None:
+        _need(grads, torch.float32, (2,), "grads")
+        _need(w_packed, torch.uint8, (N, Kp // 4), "w_packed")
+    if workspace is None:
+        workspace = _workspace(ttq_workspace_bytes(M, N, K), dY, stream)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().ttq_bwd(_ptr(dY), _ptr(x), _ptr(wt), _ptr(w_packed), M, N, int(K), _ptr(dX), _ptr(dW),
+                         dw_dtype, _ptr(grads), _ptr(workspace), ws_bytes, _stream(stream)))

@@ -185,4 +185,78 @@ bitnet_status bitlinear_bwd(const uint16_t* dY, const int8_t* x_q, const float* 
   return BITNET_OK;
 }
 
+// ---------------------------------------------------------------------------
+// TTQ
+// ---------------------------------------------------------------------------
+
+size_t ttq_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (check_gemm_sizes(M, N, K) != BITNET_OK) return 0;
+  const size_t a = bitnet::gemm_workspace_bytes(bitnet::GemmKind::kTtqFwd, M, N, K);
+  const size_t b = bitnet::gemm_workspace_bytes(bitnet::GemmKind::kTtqBwd, M, N, K);
+  return a > b ? a : b;
+}
+
+bitnet_status ttq_init(const void* W, bitnet_dtype w_dtype, int64_t N, int64_t K, float* params, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (!W || !params) return BITNET_ERR_NULL;
+  if (w_dtype != BITNET_BF16 && w_dtype != BITNET_F32) return BITNET_ERR_DTYPE;
+  if (bitnet_status st = check_sizes(N, K)) return st;
+  if (N * K > (int64_t(1) << 53)) return BITNET_ERR_SHAPE;
+  if (!aligned(W, 16) || !aligned(params, 4)) return BITNET_ERR_ALIGN;
+  if (!workspace || workspace_bytes < bitnet_ternarize_workspace_bytes(N, K)) return BITNET_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return BITNET_ERR_ALIGN;
+  return from_hip(bitnet::launch_ttq_init(W, w_dtype == BITNET_F32, N, K, params, static_cast<double*>(workspace),
+                                          static_cast<hipStream_t>(stream)));
+}
+
+bitnet_status ttq_quantize(const void* W, bitnet_dtype w_dtype, int64_t N, int64_t K, const float* params,
+                           uint8_t* w_packed, uint16_t* wt, void* stream) {
+  if (!W || !params || !w_packed || !wt) return BITNET_ERR_NULL;
+  if (w_dtype != BITNET_BF16 && w_dtype != BITNET_F32) return BITNET_ERR_DTYPE;
+  if (bitnet_status st = check_sizes(N, K)) return st;
+  if (N * bitnet::k_pad(K) > (int64_t(1) << 53)) return BITNET_ERR_SHAPE;
+  if (!aligned(W, 16) || !aligned(params, 4) || !aligned(w_packed, 16) || !aligned(wt, 16)) return BITNET_ERR_ALIGN;
+  return from_hip(bitnet::launch_ttq_quantize(W, w_dtype == BITNET_F32, N, K, params, w_packed, wt,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+bitnet_status ttq_fwd(const uint16_t* x, const uint16_t* wt, int64_t M, int64_t N, int64_t K, uint16_t* y,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (!x || !wt || !y) return BITNET_ERR_NULL;
+  if (bitnet_status st = check_gemm_sizes(M, N, K)) return st;
+  const int64_t Kp = bitnet::k_pad(K);
+  if (32 * 4 * N > (int64_t(1) << 31) || !buffer_range_ok(M, 2 * K) || !buffer_range_ok(N, 2 * Kp))
+    return BITNET_ERR_SHAPE;
+  if (workspace_bytes < ttq_workspace_bytes(M, N, K)) return BITNET_ERR_WORKSPACE;
+  if (workspace_bytes > 0 && !workspace) return BITNET_ERR_WORKSPACE;
+  if (!aligned(workspace, 16) || !aligned(x, 16) || !aligned(wt, 16) || !aligned(y, 16)) return BITNET_ERR_ALIGN;
+  return from_hip(bitnet::launch_ttq_fwd(x, wt, M, N, K, y, workspace, workspace_bytes,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+bitnet_status ttq_bwd(const uint16_t* dY, const uint16_t* x, const uint16_t* wt, const uint8_t* w_packed, int64_t M,
+                      int64_t N, int64_t K, uint16_t* dX, void* dW, bitnet_dtype dW_dtype, float* grads,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (!dY) return BITNET_ERR_NULL;
+  if (!dX && !dW) return BITNET_ERR_NULL;
+  if (dX && !wt) return BITNET_ERR_NULL;
+  if (dW && !x) return BITNET_ERR_NULL;
+  if (grads && (!dW || !w_packed)) return BITNET_ERR_NULL;
+  if (dW && dW_dtype != BITNET_BF16 && dW_dtype != BITNET_F32) return BITNET_ERR_DTYPE;
+  if (bitnet_status st = check_gemm_sizes(M, N, K)) return st;
+  const int64_t Kp = bitnet::k_pad(K);
+  if (32 * 4 * K > (int64_t(1) << 31) || !buffer_range_ok(M, 2 * N)) return BITNET_ERR_SHAPE;
+  if (dX && !buffer_range_ok(N, 2 * Kp)) return BITNET_ERR_SHAPE;
+  if (dW && !buffer_range_ok(M, 2 * K)) return BITNET_ERR_SHAPE;
+  if (grads && !buffer_range_ok(N, Kp / 4)) return BITNET_ERR_SHAPE;
+  if (workspace_bytes < ttq_workspace_bytes(M, N, K)) return BITNET_ERR_WORKSPACE;
+  if (workspace_bytes > 0 && !workspace) return BITNET_ERR_WORKSPACE;
+  if (!aligned(workspace, 16) || !aligned(dY, 16)) return BITNET_ERR_ALIGN;
+  if (dX && (!aligned(wt, 16) || !aligned(dX, 16))) return BITNET_ERR_ALIGN;
+  if (dW && (!aligned(x, 16) || !aligned(dW, 16))) return BITNET_ERR_ALIGN;
+  if (grads && (!aligned(grads, 4) || !aligned(w_packed, 16))) return BITNET_ERR_ALIGN;
+  return from_hip(bitnet::launch_ttq_bwd(dY, x, wt, w_packed, M, N, K, dX, dW, dW_dtype == BITNET_F32, grads,
+                                         workspace, workspace_bytes, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -287,8 +287,9 @@ struct CodesFp4Frags {
 // Row-major source already in MFMA element form with the reduction axis
 // contiguous (x_q for the forward, dY for dX). Thread t handles chunk t%8 of
 // rows 8(t/8)+h, h < 8; a wave instruction covers 8 rows x 128 bytes.
-// FULL: the valid reduction extent is a multiple of 16 bytes.
-template <int kElem, bool FULL>
+// FULL: the valid reduction extent is a multiple of 16 bytes. S0: first
+// staging slot (1, or 5 when the other operand is a CopyLoader too).
+template <int kElem, bool FULL, int S0 = 1>
 struct CopyLoader {
   static constexpr bool kSwz = false;
   static constexpr int kTileB = 256 * kPitch;
@@ -341,26 +342,27 @@ struct CopyLoader {
   }
 
   // Staging of the next stage, spread over the slots of k-step KS: rows
-  // 2KS, 2KS+1 of the thread's block are stored (slots 1, 3), then refilled
-  // with stage s+2 (slots 9, 11).
+  // 2KS, 2KS+1 of the thread's block are stored (slots S0, S0+2), then
+  // refilled with stage s+2 (slots S0+8, S0+10).
   struct Tmp {};
-  static constexpr int kLastStoreSlot = 3;
+  static constexpr int kLastStoreSlot = S0 + 2;
+  static_assert(S0 + 10 < 16, "the refills fit the k-step");
   template <int KS, int U>
   __device__ __forceinline__ void slot(Regs& r, Tmp&, char* lds, int row0, int s2) const {
     const int tid = threadIdx.x;
-    if constexpr (U == 1 || U == 3) {
-      constexpr int h = 2 * KS + (U == 3);
+    if constexpr (U == S0 || U == S0 + 2) {
+      constexpr int h = 2 * KS + (U == S0 + 2);
       *reinterpret_cast<uint4*>(lds + lds_off<kSwz>(8 * (tid >> 3), tid & 7) + h * kPitch) = r.v[h];
     }
-    if constexpr (FULL && (U == 9 || U == 11)) {
-      constexpr int h = 2 * KS + (U == 11);
+    if constexpr (FULL && (U == S0 + 8 || U == S0 + 10)) {
+      constexpr int h = 2 * KS + (U == S0 + 10);
       const rsrc_t rs = make_rsrc(base, (uint32_t)(rows * pitch));
       const int64_t rowb = row0 + 8 * (tid >> 3);
       const int64_t kb = (int64_t)s2 * kStageBytes + (tid & 7) * 16;
       const uint32_t off = kb < red_bytes ? (uint32_t)(rowb * pitch + kb) : kOob;
       r.v[h] = buf_load16(rs, off + (uint32_t)(h * pitch));
     }
-    if constexpr (!FULL && KS == kKSteps - 1 && U == 9) load(r, row0, s2);
+    if constexpr (!FULL && KS == kKSteps - 1 && U == S0 + 8) load(r, row0, s2);
   }
 };
 
@@ -939,6 +941,108 @@ struct Sign1Epilogue {
   }
 };
 
+// TTQ dW ("TTQ_VERIFICATION.md": Backward Pass, a straight-through
+// estimator, and Bugs Fixed item 5, the gradient of Wp as a masked sum).
+// dW = dY^T x is written as Bf16Epilogue writes it (the latent weight gets
+// the quantized weight's gradient unchanged). With partials set, each wave
+// also adds up its fp32 sums, before any rounding, over the positions whose
+// code is +1 and over those whose code is -1, and writes the two totals to
+// partials[wave tile] (one float2 per 128 x 128 wave tile, row-major over
+// the wave-tile grid; every entry is written once per call, so nothing
+// needs clearing). ttq_grads_kernel adds them up in a fixed order.
+//
+// Lane l holds k = i0 + 32fi + 8g + 4h + e (h = l/32, e < 4) of row
+// n = j0 + 32fj + l%32. i0 + 32fi is a multiple of 32, so the codes of those
+// 32 k are the two 32-bit words at byte (i0 + 32fi)/4 of row n (8 bytes,
+// one load), and code k sits in word g/2 at bit 8e + 2(2(g%2) + h) (code j
+// of a word at bit 8(j%4) + 2(j/4), j = k % 16).
+template <bool OUT_F32>
+struct TtqDwEpilogue {
+  Bf16Epilogue<OUT_F32> out;  // dW [J][I], unscaled
+  const uint8_t* codes;       // [J][code_pitch]
+  uint32_t code_pitch;        // Kp / 4 bytes
+  float2* partials;           // NULL: no sums
+  int wtiles_i;               // wave tiles along i
+
+  typedef typename Bf16Epilogue<OUT_F32>::Pre Pre;
+  static constexpr int kWaveLds = Bf16Epilogue<OUT_F32>::kWaveLds;
+  __device__ __forceinline__ Pre prefetch(int j0, int lane) const { return out.prefetch(j0, lane); }
+  __device__ __forceinline__ void store(MfmaBf16::Acc (&acc)[kFI][kFJ], const Pre& pre, int i0, int j0, int lane,
+                                        char* wlds) const {
+    if (partials == nullptr) {
+      out.store(acc, pre, i0, j0, lane, wlds);
+      return;
+    }
+    const int h = lane >> 5;
+    // rows past J fall outside the resource; words past the row's end get an
+    // out-of-range offset (zeros: no code)
+    const rsrc_t rs = make_rsrc(codes, (uint32_t)out.J * code_pitch);
+    uint2 c[kFI][kFJ];
+#pragma unroll
+    for (int fj = 0; fj < kFJ; ++fj) {
+      const uint32_t n = (uint32_t)(j0 + 32 * fj + (lane & 31));
+#pragma unroll
+      for (int fi = 0; fi < kFI; ++fi) {
+        const uint32_t col = (uint32_t)(i0 + 32 * fi) / 4;
+        c[fi][fj] = buf_load8(rs, col < code_pitch ? n * code_pitch + col : kOob);
+      }
+    }
+    out.store(acc, pre, i0, j0, lane, wlds);
+    float sp = 0.0f, sn = 0.0f;
+#pragma unroll
+    for (int fi = 0; fi < kFI; ++fi)
+#pragma unroll
+      for (int fj = 0; fj < kFJ; ++fj)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const uint32_t w = (g < 2 ? c[fi][fj].x : c[fi][fj].y) >> (4 * (g & 1) + 2 * h);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t code = (w >> (8 * e)) & 3u;
+            const float v = acc[fi][fj][4 * g + e];
+            sp += code == 1u ? v : 0.0f;
+            sn += code == 3u ? v : 0.0f;
+          }
+        }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      sp += __shfl_xor(sp, off, kWave);
+      sn += __shfl_xor(sn, off, kWave);
+    }
+    if (lane == 0) partials[(j0 / kWTJ) * wtiles_i + i0 / kWTI] = make_float2(sp, sn);
+  }
+};
+
+// The two scale gradients from the wave-tile partials: grads[0] = sum of the
+// +1 sums (dL/dWp), grads[1] = -(sum of the -1 sums) (dL/dWn: the weight
+// there is -Wn). Thread t adds partials t, t + 256, ... in fp64, then the
+// block adds the thread sums in a fixed order; rounded once to fp32.
+__global__ __launch_bounds__(256) void ttq_grads_kernel(const float2* __restrict__ partials, int count,
+                                                        float* __restrict__ grads) {
+  double p = 0.0, n = 0.0;
+  for (int i = threadIdx.x; i < count; i += 256) {
+    const float2 v = partials[i];
+    p += (double)v.x;
+    n += (double)v.y;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    p += __shfl_xor(p, off, kWave);
+    n += __shfl_xor(n, off, kWave);
+  }
+  __shared__ double sp[4], sn[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) {
+    sp[wave] = p;
+    sn[wave] = n;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    grads[0] = (float)((sp[0] + sp[1]) + (sp[2] + sp[3]));
+    grads[1] = (float)(-((sn[0] + sn[1]) + (sn[2] + sn[3])));
+  }
+}
+
 // dW for few tokens (M <= 64, N % 8 == 0): dW[n][k] = sum_{m < M} dY[m][n] *
 // x_hat[m][k] ("bitnet-qat-train", Semantics). The reduction is at most 4
 // MFMA steps of 16 tokens, so the cost is writing dW: small output tiles
@@ -1465,8 +1569,9 @@ static GemmShape shape_of(GemmKind kind, int64_t M, int64_t N, int64_t K) {
   const int64_t Kp = k_pad(K);
   switch (kind) {
     case GemmKind::kFwd: return {(N + kBI - 1) / kBI, (M + kBJ - 1) / kBJ, (Kp + kStageBytes - 1) / kStageBytes, 7};
+    case GemmKind::kTtqFwd: return {(N + kBI - 1) / kBI, (M + kBJ - 1) / kBJ, (Kp + kRed16 - 1) / kRed16, 3};
     case GemmKind::kBwdDx: return {(K + kBI - 1) / kBI, (M + kBJ - 1) / kBJ, (N + kRed16 - 1) / kRed16, 3};
-    case GemmKind::kBwdDw: break;
+    case GemmKind::kBwdDw: case GemmKind::kBwdPair: case GemmKind::kTtqBwd: break;
   }
   return {(K + kBI - 1) / kBI, (N + kBJ - 1) / kBJ, (M + kRed16 - 1) / kRed16, 3};
 }
@@ -1527,8 +1632,23 @@ static size_t pair_workspace_bound(int64_t M, int64_t N, int64_t K) {
          split_control_bytes(g2, kMaxGrid) + 2 * (size_t)kMaxGrid * kPartialBytes;
 }
 
+// TTQ backward: the wave-tile partials of the scale gradients, then the
+// split workspace of dX or dW (the two run one after the other).
+static int64_t ttq_wave_tiles(int64_t N, int64_t K) {
+  const GemmShape g = shape_of(GemmKind::kBwdDw, 1, N, K);
+  return 4 * g.tiles();
+}
+static size_t ttq_partials_bytes(int64_t N, int64_t K) {
+  return ((size_t)ttq_wave_tiles(N, K) * sizeof(float2) + 255) / 256 * 256;
+}
+
 size_t gemm_workspace_bytes(GemmKind kind, int64_t M, int64_t N, int64_t K) {
   if (kind == GemmKind::kBwdPair) return pair_eligible(M, N, K) ? pair_workspace_bound(M, N, K) : 0;
+  if (kind == GemmKind::kTtqBwd) {
+    const GemmShape gx = shape_of(GemmKind::kBwdDx, M, N, K), gw = shape_of(GemmKind::kBwdDw, M, N, K);
+    const size_t a = split_workspace(gx, split_grid(gx, kMaxGrid)), b = split_workspace(gw, split_grid(gw, kMaxGrid));
+    return ttq_partials_bytes(N, K) + (a > b ? a : b);
+  }
   const GemmShape g = shape_of(kind, M, N, K);
   // the few-token forward needs none; the large-M kernel's share stays
   // reserved so that BITNET_NO_SKINNY (a test knob) can run it at any M
@@ -1812,6 +1932,78 @@ hipError_t launch_bwd_pair(const uint16_t* dY, const uint8_t* w_packed, const fl
     default: launch(Bf16Epilogue<false>{dW, nullptr, K, N}); break;
   }
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// TTQ products ("TTQ_VERIFICATION.md": pure TTQ, unquantized bf16
+// activations; the quantized weight wt [N][Kp] holds bf16(Wp), -bf16(Wn) or
+// 0). All three are bf16 MFMA GEMMs with fp32 accumulation.
+// ---------------------------------------------------------------------------
+
+// y [M][N] = x [M][K] . wt^T: both operands copied as stored (reduction k
+// contiguous).
+hipError_t launch_ttq_fwd(const uint16_t* x, const uint16_t* wt, int64_t M, int64_t N, int64_t K, uint16_t* y,
+                          void* ws, size_t ws_bytes, hipStream_t stream) {
+  const int64_t Kp = k_pad(K);
+  const CopyLoader<2, true, 1> pl{reinterpret_cast<const char*>(wt), 2 * Kp, N, 2 * Kp};
+  const Bf16Epilogue<false> ep{y, nullptr, N, M};
+  const GemmShape g = shape_of(GemmKind::kTtqFwd, M, N, K);
+  const char* xb = reinterpret_cast<const char*>(x);
+  if (K % 8 == 0) return run_gemm<MfmaBf16, 1>(pl, CopyLoader<2, true, 5>{xb, 2 * K, M, 2 * K}, ep, g, ws, ws_bytes, stream);
+  return run_gemm<MfmaBf16, 1>(pl, CopyLoader<2, false, 5>{xb, 2 * K, M, 2 * K}, ep, g, ws, ws_bytes, stream);
+}
+
+// dX [M][K] = dY [M][N] . wt: wt staged as stored (rows n) and read
+// transposed (TrFrags), dY copied as stored.
+static hipError_t launch_ttq_dx(const uint16_t* dY, const uint16_t* wt, int64_t M, int64_t N, int64_t K,
+                                uint16_t* dX, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const int64_t Kp = k_pad(K);
+  const RowCopyBf16Loader<5> pl{wt, Kp, N, K};
+  const Bf16Epilogue<false> ep{dX, nullptr, K, M};
+  const GemmShape g = shape_of(GemmKind::kBwdDx, M, N, K);
+  const char* db = reinterpret_cast<const char*>(dY);
+  if (N % 8 == 0) return run_gemm<MfmaBf16, 0>(pl, CopyLoader<2, true, 1>{db, 2 * N, M, 2 * N}, ep, g, ws, ws_bytes, stream);
+  return run_gemm<MfmaBf16, 0>(pl, CopyLoader<2, false, 1>{db, 2 * N, M, 2 * N}, ep, g, ws, ws_bytes, stream);
+}
+
+// dW [N][K] = dY^T x with the masked sums (TtqDwEpilogue).
+template <bool OUT_F32>
+static hipError_t launch_ttq_dw(const uint16_t* dY, const uint16_t* x, const uint8_t* w_packed, int64_t M, int64_t N,
+                                int64_t K, void* dW, float2* partials, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const GemmShape g = shape_of(GemmKind::kBwdDw, M, N, K);
+  const TtqDwEpilogue<OUT_F32> ep{Bf16Epilogue<OUT_F32>{dW, nullptr, K, N}, w_packed, (uint32_t)(k_pad(K) / 4),
+                                  partials, (int)(2 * g.tiles_i)};
+  if (K % 8 == 0 && N % 8 == 0)
+    return run_gemm<MfmaBf16, 0>(RowCopyBf16Loader<1>{x, K, M, K}, RowCopyBf16Loader<5>{dY, N, M, N}, ep, g, ws,
+                                 ws_bytes, stream);
+  if (K % 4 == 0 && N % 4 == 0)
+    return run_gemm<MfmaBf16, 0>(RowTransposeBf16Loader<true, 3>{x, K, M, K},
+                                 RowTransposeBf16Loader<true, 5>{dY, N, M, N}, ep, g, ws, ws_bytes, stream);
+  return run_gemm<MfmaBf16, 0>(RowTransposeBf16Loader<false, 3>{x, K, M, K},
+                               RowTransposeBf16Loader<false, 5>{dY, N, M, N}, ep, g, ws, ws_bytes, stream);
+}
+
+hipError_t launch_ttq_bwd(const uint16_t* dY, const uint16_t* x, const uint16_t* wt, const uint8_t* w_packed,
+                          int64_t M, int64_t N, int64_t K, uint16_t* dX, void* dW, bool dw_f32, float* grads,
+                          void* ws, size_t ws_bytes, hipStream_t stream) {
+  const size_t pb = ttq_partials_bytes(N, K);
+  if (ws == nullptr || ws_bytes < pb) return hipErrorInvalidValue;  // the C ABI sized it
+  float2* partials = static_cast<float2*>(ws);
+  void* split_ws = static_cast<char*>(ws) + pb;
+  const size_t split_bytes = ws_bytes - pb;
+  if (dX != nullptr)
+    if (hipError_t e = launch_ttq_dx(dY, wt, M, N, K, dX, split_ws, split_bytes, stream)) return e;
+  if (dW != nullptr) {
+    float2* p = grads != nullptr ? partials : nullptr;
+    const hipError_t e = dw_f32 ? launch_ttq_dw<true>(dY, x, w_packed, M, N, K, dW, p, split_ws, split_bytes, stream)
+                                : launch_ttq_dw<false>(dY, x, w_packed, M, N, K, dW, p, split_ws, split_bytes, stream);
+    if (e != hipSuccess) return e;
+    if (grads != nullptr) {
+      ttq_grads_kernel<<<1, 256, 0, stream>>>(partials, (int)ttq_wave_tiles(N, K), grads);
+      return hipGetLastError();
+    }
+  }
+  return hipSuccess;
 }
 
 }  // namespace bitnet

@@ -29,10 +29,11 @@ hipError_t launch_bias_grad(const uint16_t* dY, int64_t M, int64_t N, void* db, 
 hipError_t launch_act_quant(const uint16_t* x, int64_t M, int64_t K,
                             int8_t* x_q, float* s_x, hipStream_t stream);
 
-// The three GEMMs. Each may split output tiles over workgroups (stream-K)
+// The GEMMs (BitNet forward, dX, dW, the paired backward; TTQ forward and
+// backward). Each may split output tiles over workgroups (stream-K)
 // when its tile count leaves the CUs partly idle; that needs the workspace
 // gemm_workspace_bytes() gives (fewer bytes: whole tiles, no split).
-enum class GemmKind { kFwd, kBwdDx, kBwdDw, kBwdPair };
+enum class GemmKind { kFwd, kBwdDx, kBwdDw, kBwdPair, kTtqFwd, kTtqBwd };
 size_t gemm_workspace_bytes(GemmKind kind, int64_t M, int64_t N, int64_t K);
 
 // INT8 forward GEMM with fused rescale, an optional bf16 bias [N] (NULL:
@@ -73,5 +74,22 @@ hipError_t launch_bwd_pair(const uint16_t* dY, const uint8_t* w_packed, const fl
                            const int8_t* x_q, const float* s_x, int64_t M, int64_t N, int64_t K,
                            uint16_t* dX, void* dW, DwOut dw_out, void* ws, size_t ws_bytes,
                            hipStream_t stream);
+
+// TTQ ("TTQ_VERIFICATION.md"): params = {delta, Wp, Wn} fp32 on the device.
+// Initialization (Eq. 2) from W: E = gamma's absmean, delta = fl32(0.7f E),
+// Wp = Wn = E (partials: the ternarize workspace).
+hipError_t launch_ttq_init(const void* W, bool w_is_f32, int64_t N, int64_t K, float* params, double* partials,
+                           hipStream_t stream);
+// Eq. 1: 2-bit codes [N][Kp/4] and bf16 values wt [N][Kp] in one pass.
+hipError_t launch_ttq_quantize(const void* W, bool w_is_f32, int64_t N, int64_t K, const float* params,
+                               uint8_t* w_packed, uint16_t* wt, hipStream_t stream);
+// y = x wt^T (bf16 x [M][K], no activation quantization).
+hipError_t launch_ttq_fwd(const uint16_t* x, const uint16_t* wt, int64_t M, int64_t N, int64_t K, uint16_t* y,
+                          void* ws, size_t ws_bytes, hipStream_t stream);
+// dX = dY wt, dW = dY^T x (bf16 or f32), grads = {dL/dWp, dL/dWn} (NULL: not
+// computed; needs dW). Workspace: gemm_workspace_bytes(kTtqBwd).
+hipError_t launch_ttq_bwd(const uint16_t* dY, const uint16_t* x, const uint16_t* wt, const uint8_t* w_packed,
+                          int64_t M, int64_t N, int64_t K, uint16_t* dX, void* dW, bool dw_f32, float* grads,
+                          void* ws, size_t ws_bytes, hipStream_t stream);
 
 }  // namespace bitnet

@@ -95,8 +95,58 @@ __global__ __launch_bounds__(kAbsmeanThreads) void absmean_partials_kernel(
 // stores it. Each thread then writes whole 32-bit words of 16 codes.
 // ---------------------------------------------------------------------------
 
+// The 16 weights W[n][k0 .. k0+15] of one code word as fp32 (exact), zeros
+// past K. VEC: every row starts 16-byte aligned (K a multiple of 4 for fp32,
+// of 8 for bf16).
+template <bool F32, bool VEC>
+__device__ __forceinline__ void load_word(const void* __restrict__ w, int64_t n, int64_t K, int64_t k0,
+                                          float (&vals)[16]) {
+  if (VEC && k0 + 16 <= K) {
+    if constexpr (F32) {
+      const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(w) + n * K + k0);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint4 d = p[c];
+        vals[4 * c + 0] = __uint_as_float(d.x);
+        vals[4 * c + 1] = __uint_as_float(d.y);
+        vals[4 * c + 2] = __uint_as_float(d.z);
+        vals[4 * c + 3] = __uint_as_float(d.w);
+      }
+    } else {
+      const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(w) + n * K + k0);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const uint4 d = p[c];
+        vals[8 * c + 0] = bf16_lo(d.x); vals[8 * c + 1] = bf16_hi(d.x);
+        vals[8 * c + 2] = bf16_lo(d.y); vals[8 * c + 3] = bf16_hi(d.y);
+        vals[8 * c + 4] = bf16_lo(d.z); vals[8 * c + 5] = bf16_hi(d.z);
+        vals[8 * c + 6] = bf16_lo(d.w); vals[8 * c + 7] = bf16_hi(d.w);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int64_t k = k0 + j;
+      vals[j] = (k < K) ? load_elem<F32>(w, n * K + k) : 0.0f;
+    }
+  }
+}
+
 constexpr int kPackThreads = 256;
 static_assert(kAbsmeanBlocks == kPackThreads, "one partial per thread");
+static_assert(kPackThreads / kWave == 4, "four wave sums");
+
+// S = the sum of the kAbsmeanBlocks partials in one fixed order (butterfly
+// within each wave, then the four wave sums pairwise), so every block and
+// kernel that needs it gets the same bits. Called by all kPackThreads
+// threads of the block.
+__device__ __forceinline__ double partials_total(const double* __restrict__ partials, double* sred) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const double v = wave_sum_f64(partials[threadIdx.x]);
+  if (lane == 0) sred[wave] = v;
+  __syncthreads();
+  return (sred[0] + sred[1]) + (sred[2] + sred[3]);
+}
 
 template <bool F32, bool VEC>
 __global__ __launch_bounds__(kPackThreads) void ternarize_pack_kernel(
@@ -105,12 +155,8 @@ __global__ __launch_bounds__(kPackThreads) void ternarize_pack_kernel(
     float* __restrict__ gamma_out) {
   __shared__ double sred[kPackThreads / kWave];
   __shared__ float s_half;
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  double v = wave_sum_f64(partials[threadIdx.x]);
-  if (lane == 0) sred[wave] = v;
-  __syncthreads();
+  const double S = partials_total(partials, sred);
   if (threadIdx.x == 0) {
-    const double S = (sred[0] + sred[1]) + (sred[2] + sred[3]);
     const double mean = S / (double)(N * K);
     const float g = fmaxf((float)mean, 1e-8f);
     s_half = g * 0.5f;  // exact
@@ -125,35 +171,7 @@ __global__ __launch_bounds__(kPackThreads) void ternarize_pack_kernel(
     const int64_t n = wi / words_per_row;
     const int64_t k0 = (wi - n * words_per_row) * 16;
     float vals[16];
-    if (VEC && k0 + 16 <= K) {
-      if constexpr (F32) {
-        const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(w) + n * K + k0);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const uint4 d = p[c];
-          vals[4 * c + 0] = __uint_as_float(d.x);
-          vals[4 * c + 1] = __uint_as_float(d.y);
-          vals[4 * c + 2] = __uint_as_float(d.z);
-          vals[4 * c + 3] = __uint_as_float(d.w);
-        }
-      } else {
-        const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(w) + n * K + k0);
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const uint4 d = p[c];
-          vals[8 * c + 0] = bf16_lo(d.x); vals[8 * c + 1] = bf16_hi(d.x);
-          vals[8 * c + 2] = bf16_lo(d.y); vals[8 * c + 3] = bf16_hi(d.y);
-          vals[8 * c + 4] = bf16_lo(d.z); vals[8 * c + 5] = bf16_hi(d.z);
-          vals[8 * c + 6] = bf16_lo(d.w); vals[8 * c + 7] = bf16_hi(d.w);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int64_t k = k0 + j;
-        vals[j] = (k < K) ? load_elem<F32>(w, n * K + k) : 0.0f;
-      }
-    }
+    load_word<F32, VEC>(w, n, K, k0, vals);
     // code j of the word at bit 8*(j%4) + 2*(j/4): byte b holds the codes
     // j = b, b+4, b+8, b+12, so (word >> 2t) & 0x03030303 lists the codes
     // 4t..4t+3 in its four bytes
@@ -434,6 +452,89 @@ __global__ __launch_bounds__(1024) void bias_grad_kernel(const uint16_t* __restr
 hipError_t launch_bias_grad(const uint16_t* dY, int64_t M, int64_t N, void* db, bool db_is_f32,
                             hipStream_t stream) {
   bias_grad_kernel<<<(unsigned)((N + 63) / 64), 1024, 0, stream>>>(dY, M, N, db, db_is_f32);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// TTQ ("TTQ_VERIFICATION.md", Algorithm Summary): Eq. 1 takes +Wp where
+// W > delta, -Wn where W < -delta and 0 elsewhere; the initialization (Eq. 2)
+// sets delta = 0.7 E|W| and Wp = Wn = E|W|. params = {delta, Wp, Wn}, fp32,
+// on the device.
+// ---------------------------------------------------------------------------
+
+// Initialization from the absmean partials: E is gamma's value (the same
+// reduction in the same order, the same floor), delta = fl32(0.7f * E).
+__global__ __launch_bounds__(kPackThreads) void ttq_init_kernel(const double* __restrict__ partials,
+                                                                 int64_t count, float* __restrict__ params) {
+  __shared__ double sred[kPackThreads / kWave];
+  const double S = partials_total(partials, sred);
+  if (threadIdx.x == 0) {
+    const float e = fmaxf((float)(S / (double)count), 1e-8f);
+    params[0] = 0.7f * e;
+    params[1] = e;
+    params[2] = e;
+  }
+}
+
+hipError_t launch_ttq_init(const void* W, bool w_is_f32, int64_t N, int64_t K, float* params, double* partials,
+                           hipStream_t stream) {
+  const int64_t n = N * K;
+  if (w_is_f32)
+    absmean_partials_kernel<true><<<kAbsmeanBlocks, kAbsmeanThreads, 0, stream>>>(W, n, partials);
+  else
+    absmean_partials_kernel<false><<<kAbsmeanBlocks, kAbsmeanThreads, 0, stream>>>(W, n, partials);
+  if (hipError_t e = hipGetLastError()) return e;
+  ttq_init_kernel<<<1, kPackThreads, 0, stream>>>(partials, n, params);
+  return hipGetLastError();
+}
+
+// Eq. 1 on one pass over W: per 16-weight word, the 2-bit codes (the BitNet
+// format: +1 -> 01, -1 -> 11, 0 -> 00 at bit 8*(j%4) + 2*(j/4)) and the bf16
+// values the products use, bf16(Wp), -bf16(Wn) or 0 (round half to even),
+// into wt [N][Kp] (padding columns 0). Both comparisons are strict and exact
+// (fp32 weights or bf16 weights widened exactly, fp32 delta).
+template <bool F32, bool VEC>
+__global__ __launch_bounds__(kPackThreads) void ttq_quantize_kernel(
+    const void* __restrict__ w, int64_t N, int64_t K, int64_t words_per_row, const float* __restrict__ params,
+    uint32_t* __restrict__ packed, uint16_t* __restrict__ wt) {
+  const float d = params[0];
+  const uint32_t vp = f32_to_bf16_bits(params[1]);
+  const uint32_t vn = f32_to_bf16_bits(params[2]) ^ 0x8000u;  // -bf16(Wn)
+  const int64_t total = N * words_per_row, Kp = 16 * words_per_row;
+  for (int64_t wi = (int64_t)blockIdx.x * kPackThreads + threadIdx.x; wi < total;
+       wi += (int64_t)gridDim.x * kPackThreads) {
+    const int64_t n = wi / words_per_row;
+    const int64_t k0 = (wi - n * words_per_row) * 16;
+    float vals[16];
+    load_word<F32, VEC>(w, n, K, k0, vals);
+    uint32_t word = 0, o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const bool pos = vals[j] > d, neg = vals[j] < -d;
+      word |= (pos ? 1u : (neg ? 3u : 0u)) << (8 * (j & 3) + 2 * (j >> 2));
+      o[j >> 1] |= (pos ? vp : (neg ? vn : 0u)) << (16 * (j & 1));
+    }
+    packed[wi] = word;
+    uint4* dst = reinterpret_cast<uint4*>(wt + n * Kp + k0);
+    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+  }
+}
+
+hipError_t launch_ttq_quantize(const void* W, bool w_is_f32, int64_t N, int64_t K, const float* params,
+                               uint8_t* w_packed, uint16_t* wt, hipStream_t stream) {
+  const int64_t wpr = k_pad(K) / 16;
+  const int64_t want = (N * wpr + kPackThreads - 1) / kPackThreads;
+  const int grid = (int)(want < 2048 ? want : 2048);
+  uint32_t* pw = reinterpret_cast<uint32_t*>(w_packed);
+  const bool vec = w_is_f32 ? (K % 4 == 0) : (K % 8 == 0);
+  if (w_is_f32) {
+    if (vec) ttq_quantize_kernel<true, true><<<grid, kPackThreads, 0, stream>>>(W, N, K, wpr, params, pw, wt);
+    else ttq_quantize_kernel<true, false><<<grid, kPackThreads, 0, stream>>>(W, N, K, wpr, params, pw, wt);
+  } else {
+    if (vec) ttq_quantize_kernel<false, true><<<grid, kPackThreads, 0, stream>>>(W, N, K, wpr, params, pw, wt);
+    else ttq_quantize_kernel<false, false><<<grid, kPackThreads, 0, stream>>>(W, N, K, wpr, params, pw, wt);
+  }
   return hipGetLastError();
 }
 

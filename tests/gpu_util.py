@@ -81,3 +81,40 @@ def run_layer(inp, acc=True, dx=True, dw=True, xdev=None):
         else:
             out["dW"] = WL.bf16_bits_to_f32(host_bf16_bits(dW)).astype(np.float64)
     return out
+
+
+def run_ttq(inp, params=None, dx=True, dw=True, grads=True, dw_f32=False):
+    """TTQ through the C ABI: ttq_init (unless `params` = (delta, Wp, Wn) is
+    given), ttq_quantize, ttq_fwd, ttq_bwd. Returns numpy copies."""
+    M, K, N = inp["M"], inp["K"], inp["N"]
+    Kp = B.bitnet_k_pad(K)
+    dev = torch.device("cuda")
+    W = dev_weight(inp["W"])
+    x = dev_bf16(inp["x"])
+    dY = dev_bf16(inp["dY"])
+    if params is None:
+        p = torch.empty((3,), dtype=torch.float32, device=dev)
+        ws = torch.empty((B.bitnet_ternarize_workspace_bytes(N, K),), dtype=torch.uint8, device=dev)
+        B.ttq_init(W, p, ws)
+    else:
+        p = torch.tensor(np.asarray(params, dtype=np.float32), device=dev)
+    w_packed = torch.empty((N, Kp // 4), dtype=torch.uint8, device=dev)
+    wt = torch.empty((N, Kp), dtype=torch.bfloat16, device=dev)
+    B.ttq_quantize(W, p, w_packed, wt)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    B.ttq_fwd(x, wt, y)
+    dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev) if dx else None
+    dW = torch.empty((N, K), dtype=torch.float32 if dw_f32 else torch.bfloat16, device=dev) if dw else None
+    g = torch.full((2,), float("nan"), dtype=torch.float32, device=dev) if grads else None
+    if dx or dw:
+        B.ttq_bwd(dY, x, wt, w_packed, K, dX=dX, dW=dW, grads=g)
+    torch.cuda.synchronize()
+    out = dict(params=p.cpu().numpy(), packed=w_packed.cpu().numpy(), wt_bits=host_bf16_bits(wt),
+               y_bits=host_bf16_bits(y))
+    if dx:
+        out["dX"] = WL.bf16_bits_to_f32(host_bf16_bits(dX)).astype(np.float64)
+    if dw:
+        out["dW"] = (dW.cpu().numpy() if dw_f32 else WL.bf16_bits_to_f32(host_bf16_bits(dW))).astype(np.float64)
+    if grads:
+        out["grads"] = g.cpu().numpy()
+    return out

@@ -18,7 +18,7 @@ OK, ENULL, ESHAPE, EDTYPE, EALIGN, EWS, EHIP = range(7)
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(bit(?:net|linear)_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b((?:bitnet|bitlinear|ttq)_\w+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -42,13 +42,20 @@ def L():
     lib.bitlinear_bwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp, vp, st, vp, sz, vp]
     lib.bitlinear_fwd_bias.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp, vp, vp, sz, vp]
     lib.bitlinear_bias_grad.argtypes = [vp, i64, i64, vp, st, vp]
+    lib.ttq_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.ttq_workspace_bytes.restype = sz
+    lib.ttq_init.argtypes = [vp, st, i64, i64, vp, vp, sz, vp]
+    lib.ttq_quantize.argtypes = [vp, st, i64, i64, vp, vp, vp, vp]
+    lib.ttq_fwd.argtypes = [vp, vp, i64, i64, i64, vp, vp, sz, vp]
+    lib.ttq_bwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp, st, vp, vp, sz, vp]
     return lib
 
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("bitnet_ternarize_pack", "bitnet_act_quant", "bitlinear_fwd", "bitlinear_bwd",
-              "bitlinear_fwd_bias", "bitlinear_bias_grad"):
+              "bitlinear_fwd_bias", "bitlinear_bias_grad", "ttq_workspace_bytes", "ttq_init", "ttq_quantize",
+              "ttq_fwd", "ttq_bwd"):
         assert n in names
 
 
@@ -155,3 +162,50 @@ def test_bias_validation(L):
     assert L.bitlinear_bias_grad(A, 4, 4, A, 2, None) == EDTYPE
     assert L.bitlinear_bias_grad(A, 0, 4, A, 1, None) == ESHAPE
     assert L.bitlinear_bias_grad(A, 4, 4, MISALIGNED, 1, None) == EALIGN
+
+
+def test_ttq_size_queries(L):
+    tile = 64 * 256 * 16
+    # no split at a single tile: only the scale-gradient partials (one float2
+    # per 128 x 128 tile of dW, rounded up to 256 bytes)
+    assert L.ttq_workspace_bytes(64, 128, 256) == 256
+    # 4096x2560->6912: dW has 10 x 27 tiles (4 partials each); both
+    # backward products and the forward split over 256 workgroups
+    partials = (4 * 270 * 8 + 255) // 256 * 256
+    assert L.ttq_workspace_bytes(4096, 6912, 2560) == partials + 4352 + 2 * 256 * tile
+    assert L.ttq_workspace_bytes(0, 4, 4) == 0
+
+
+def test_ttq_validation(L):
+    ws = L.bitnet_ternarize_workspace_bytes(8, 8)
+    assert L.ttq_init(None, 0, 8, 8, A, A, ws, None) == ENULL
+    assert L.ttq_init(A, 0, 8, 8, None, A, ws, None) == ENULL
+    assert L.ttq_init(A, 2, 8, 8, A, A, ws, None) == EDTYPE
+    assert L.ttq_init(A, 0, 0, 8, A, A, ws, None) == ESHAPE
+    assert L.ttq_init(MISALIGNED, 0, 8, 8, A, A, ws, None) == EALIGN
+    assert L.ttq_init(A, 0, 8, 8, A + 2, A, ws, None) == EALIGN
+    assert L.ttq_init(A, 0, 8, 8, A, A, ws - 1, None) == EWS
+    assert L.ttq_quantize(A, 0, 8, 8, A, None, A, None) == ENULL
+    assert L.ttq_quantize(A, 0, 8, 8, A, A, None, None) == ENULL
+    assert L.ttq_quantize(A, 1, 8, -8, A, A, A, None) == ESHAPE
+    assert L.ttq_quantize(A, 0, 8, 8, A, A, MISALIGNED, None) == EALIGN
+    assert L.ttq_fwd(None, A, 4, 4, 4, A, None, 0, None) == ENULL
+    assert L.ttq_fwd(A, A, 4, 0, 4, A, None, 0, None) == ESHAPE
+    # x is addressed with 32-bit offsets: (M + 256) * 2K bytes within 2^31
+    assert L.ttq_fwd(A, A, 1 << 20, 4, 1 << 11, A, None, 0, None) == ESHAPE
+    ws = L.ttq_workspace_bytes(4, 4, 4)  # one size for both calls
+    assert L.ttq_fwd(A, A, 4, 4, 4, A, None, ws, None) == EWS
+    assert L.ttq_fwd(A, A, 4, 4, 4, MISALIGNED, A, ws, None) == EALIGN
+    need = L.ttq_workspace_bytes(4096, 6912, 2560)
+    assert L.ttq_fwd(A, A, 4096, 6912, 2560, A, A, need - 1, None) == EWS
+    ws = L.ttq_workspace_bytes(4, 4, 4)
+    assert L.ttq_bwd(A, A, A, A, 4, 4, 4, None, None, 0, None, A, ws, None) == ENULL
+    assert L.ttq_bwd(A, A, None, A, 4, 4, 4, A, None, 0, None, A, ws, None) == ENULL
+    assert L.ttq_bwd(A, None, A, A, 4, 4, 4, None, A, 0, None, A, ws, None) == ENULL
+    # the scale gradients come from dW's epilogue and need the codes
+    assert L.ttq_bwd(A, A, A, A, 4, 4, 4, A, None, 0, A, A, ws, None) == ENULL
+    assert L.ttq_bwd(A, A, A, None, 4, 4, 4, None, A, 0, A, A, ws, None) == ENULL
+    assert L.ttq_bwd(A, A, A, A, 4, 4, 4, None, A, 2, None, A, ws, None) == EDTYPE
+    assert L.ttq_bwd(A, A, A, A, 4, 4, 4, None, A, 0, None, A, ws - 1, None) == EWS
+    assert L.ttq_bwd(A, A, A, A, 4, 4, 4, None, A, 0, A + 2, A, ws, None) == EALIGN
+    assert L.ttq_bwd(A, A, A, A, 4, 4, 4, MISALIGNED, None, 0, None, A, ws, None) == EALIGN

@@ -1,0 +1,237 @@
+"""GPU parity of the TTQ path ("TTQ_VERIFICATION.md") against the CPU oracle,
+through the C ABI.
+
+Bit-exact: the initial (delta, Wp, Wn), the 2-bit codes and the bf16 weight
+values. Within tolerance (``oracle.compare`` with the 2^-8 RMS floor: the
+products are fp32 sums of bf16 products, which can cancel): y, dX, dW. The
+scale gradients are fp32 sums (per 128 x 128 tile, then fp64 across tiles)
+of the fp32 dW values; their error is bounded by the recursive-summation
+bound (M + 512) * 2^-24 * B, B = the sum over the masked positions of
+sum_m |dY[m, n] x[m, k]|, and they are exact for integer-valued inputs.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from oracle import compare as C
+from ternary_weight_quantization_amd import workloads as WL
+from tests.gpu_util import note, run_ttq, w_values
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    from ternary_weight_quantization_amd import binding
+    binding.lib()
+
+
+def bf(bits):
+    return WL.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def f32_bits(v):
+    return np.float32(v).view(np.uint32)
+
+
+def grads_bound(dY, x, q, M):
+    """(M + 512) * 2^-24 * B for the +1 and the -1 masks."""
+    B = np.abs(dY).T @ np.abs(x)
+    u = 2.0 ** -24 * (M + 512)
+    return u * float(B[q == 1].sum()), u * float(B[q == -1].sum())
+
+
+def check_ttq(inp, g, given=None):
+    M, K, N = inp["M"], inp["K"], inp["N"]
+    Kp = O.k_pad(K)
+    w = w_values(inp["W"])
+    x = bf(inp["x"])
+    dY = bf(inp["dY"])
+    if given is None:
+        delta, wp, wn = O.ttq_init(w)
+        assert [f32_bits(v) for v in g["params"]] == [f32_bits(delta), f32_bits(wp), f32_bits(wn)], \
+            (g["params"], (delta, wp, wn))
+    else:
+        delta, wp, wn = (np.float32(v) for v in given)
+    q = O.ttq_codes(w, delta)
+    assert np.array_equal(g["packed"], O.pack_codes(q, Kp))
+    wt = O.ttq_values(q, wp, wn)
+    wt_bits = np.zeros((N, Kp), dtype=np.uint16)
+    wt_bits[:, :K] = WL.f32_to_bf16_bits(wt.astype(np.float32))
+    assert np.array_equal(g["wt_bits"], wt_bits)
+    out = {"y": C.check(bf(g["y_bits"]), O.ttq_forward(x, wt), "y_ttq")}
+    dX, dW, g_wp, g_wn = O.ttq_backward(dY, x, q, wp, wn)
+    if "dX" in g:
+        out["dX"] = C.check(g["dX"], dX, "dX")
+    if "dW" in g:
+        out["dW"] = C.check(g["dW"], dW, "dW")
+    if "grads" in g:
+        bp, bn = grads_bound(dY, x, q, M)
+        # the bound plus the final rounding to fp32
+        assert abs(float(g["grads"][0]) - g_wp) <= bp + 2.0 ** -24 * abs(g_wp), (g["grads"], g_wp, bp)
+        assert abs(float(g["grads"][1]) - g_wn) <= bn + 2.0 ** -24 * abs(g_wn), (g["grads"], g_wn, bn)
+        out["grads"] = (float(g["grads"][0]), g_wp, float(g["grads"][1]), g_wn)
+    print(f"[ttq parity] M={M} K={K} N={N}: " + ", ".join(
+        f"{k}=max_rel {v['max_rel']:.2e} norm {v['normwise']:.2e}" if isinstance(v, dict) else f"{k}={v}"
+        for k, v in out.items()), flush=True)
+    fr = np.array([np.mean(q == 1), np.mean(q == 0), np.mean(q == -1)])
+    print(f"[ttq stats] fractions +1/0/-1: {fr.round(3).tolist()}", flush=True)
+    return out
+
+
+@pytest.mark.parametrize("M,K,N,wd", [
+    (1, 1, 1, "bf16"),
+    (2, 7, 6, "f32"),
+    (64, 256, 128, "f32"),
+    (257, 320, 200, "bf16"),
+    (300, 1001, 777, "bf16"),
+    (33, 130, 513, "f32"),
+    (520, 1000, 264, "bf16"),
+    (1024, 512, 96, "bf16"),
+])
+def test_ttq_ragged_shapes(M, K, N, wd):
+    inp = WL.custom_inputs(M, K, N, seed=3 * M + K + N, w_dtype=wd)
+    note(f"ttq ragged M={M} K={K} N={N} W={wd}")
+    check_ttq(inp, run_ttq(inp))
+
+
+@pytest.mark.parametrize("dw_f32", [False, True])
+def test_ttq_given_params(dw_f32):
+    """Asymmetric Wp != Wn and a threshold that is not 0.7 E (the values a
+    trained layer holds), neither bf16-exact; dW in bf16 and in f32."""
+    inp = WL.custom_inputs(384, 576, 320, seed=11)
+    w = w_values(inp["W"])
+    e = float(np.mean(np.abs(w)))
+    params = (np.float32(0.55 * e), np.float32(1.37 * e), np.float32(0.81 * e))
+    note(f"ttq given params {params} dW f32={dw_f32}")
+    check_ttq(inp, run_ttq(inp, params=params, dw_f32=dw_f32), given=params)
+
+
+def test_ttq_grads_exact_for_integer_inputs():
+    """Integer-valued x and dY (|v| <= 3) make every dW entry, every partial
+    and every total an exact integer in fp32: grads, and the f32 dW, equal the
+    oracle exactly. Codes from random weights in {-1, -0.25, 0, 0.25, 1}."""
+    M, K, N = 320, 520, 300
+    rng = np.random.default_rng(23)
+    inp = WL.custom_inputs(M, K, N, seed=23)
+    inp["x"] = WL.f32_to_bf16_bits(rng.integers(-3, 4, (M, K)).astype(np.float32))
+    inp["dY"] = WL.f32_to_bf16_bits(rng.integers(-3, 4, (M, N)).astype(np.float32))
+    inp["W"] = WL.f32_to_bf16_bits(rng.choice([-1.0, -0.25, 0.0, 0.25, 1.0], (N, K)).astype(np.float32))
+    params = (np.float32(0.5), np.float32(0.75), np.float32(0.375))
+    note("ttq integer inputs")
+    g = run_ttq(inp, params=params, dw_f32=True)
+    x, dY = bf(inp["x"]), bf(inp["dY"])
+    q = O.ttq_codes(w_values(inp["W"]), params[0])
+    dX, dW, g_wp, g_wn = O.ttq_backward(dY, x, q, params[1], params[2])
+    assert np.array_equal(g["dW"], dW)
+    assert float(g["grads"][0]) == g_wp and float(g["grads"][1]) == g_wn, (g["grads"], g_wp, g_wn)
+    # y: exact fp32 sums (multiples of 1/8 below 2^11), rounded once to bf16
+    assert np.array_equal(bf(g["y_bits"]), O.bf16_round(O.ttq_forward(x, O.ttq_values(q, *params[1:]))))
+
+
+def test_ttq_edge_all_zero_weight():
+    """All-zero W: E is floored at 1e-8 as gamma is, delta = fl32(0.7 * 1e-8);
+    every code is 0 (|0| > delta fails), so wt, y and dX are zero and the
+    scale gradients are 0."""
+    inp = WL.custom_inputs(64, 192, 96, seed=5)
+    inp["W"] = np.zeros_like(inp["W"])
+    note("ttq edge: all-zero W")
+    g = run_ttq(inp)
+    assert f32_bits(g["params"][1]) == f32_bits(np.float32(1e-8))
+    assert np.all(g["packed"] == 0) and np.all(g["wt_bits"] == 0)
+    assert np.all(g["y_bits"] == 0) and np.all(g["dX"] == 0)
+    assert np.all(g["grads"] == 0)
+    check_ttq(inp, g)
+
+
+def test_ttq_optional_outputs():
+    """dX alone, dW alone (with and without the scale gradients) give the
+    same values as the full call."""
+    inp = WL.custom_inputs(200, 320, 136, seed=29)
+    note("ttq optional outputs")
+    full = run_ttq(inp)
+    a = run_ttq(inp, dw=False, grads=False)
+    b = run_ttq(inp, dx=False)
+    c = run_ttq(inp, dx=False, grads=False)
+    assert np.array_equal(a["dX"], full["dX"])
+    assert np.array_equal(b["dW"], full["dW"]) and np.array_equal(c["dW"], full["dW"])
+    assert np.array_equal(b["grads"].view(np.uint32), full["grads"].view(np.uint32))
+
+
+def test_ttq_full_size_sampled():
+    """The 4096 x 2560 -> 6912 layer in the launch configuration the
+    benchmark times: bit-exact parameters, codes and values; y, dX, dW on
+    sampled elements; the scale gradients against the masked sums of the
+    GPU's own f32 dW (a property at any size), and that f32 dW sampled
+    against the oracle."""
+    inp = WL.layer_inputs("c2_up_4096x2560x6912", seed=0)
+    M, K, N = inp["M"], inp["K"], inp["N"]
+    note(f"ttq full size M={M} K={K} N={N}")
+    g = run_ttq(inp, dw_f32=True)
+    w = w_values(inp["W"])
+    delta, wp, wn = O.ttq_init(w)
+    assert [f32_bits(v) for v in g["params"]] == [f32_bits(delta), f32_bits(wp), f32_bits(wn)]
+    q = O.ttq_codes(w, delta)
+    assert np.array_equal(g["packed"], O.pack_codes(q))
+    wt = O.ttq_values(q, wp, wn)
+    assert np.array_equal(g["wt_bits"][:, :K], WL.f32_to_bf16_bits(wt.astype(np.float32)))
+    x, dY = bf(inp["x"]), bf(inp["dY"])
+    rng = np.random.default_rng(7)
+    n = 4000
+    r, c = rng.integers(0, M, n), rng.integers(0, N, n)
+    C.check(bf(g["y_bits"])[r, c], O.ttq_y_elements(x, wt, r, c), "y_ttq")
+    rk = rng.integers(0, K, n)
+    C.check(g["dX"][r, rk], O.ttq_dx_elements(dY, wt, r, rk), "dX")
+    rn, rk2 = rng.integers(0, N, n), rng.integers(0, K, n)
+    C.check(g["dW"][rn, rk2], O.ttq_dw_elements(dY, x, rn, rk2), "dW")
+    dW = g["dW"]
+    sp = math.fsum(dW[q == 1].tolist())
+    sn = -math.fsum(dW[q == -1].tolist())
+    # the kernel sums the same fp32 values (the f32 store is exact): 256 per
+    # lane in order, then a 6-level butterfly over the wave, then fp64, so
+    # the error is within (256 + 6 + 1) * 2^-24 of the sum of |values|
+    tol_p = 263 * 2.0 ** -24 * float(np.abs(dW[q == 1]).sum())
+    tol_n = 263 * 2.0 ** -24 * float(np.abs(dW[q == -1]).sum())
+    assert abs(float(g["grads"][0]) - sp) <= tol_p + 2.0 ** -24 * abs(sp), (g["grads"], sp, tol_p)
+    assert abs(float(g["grads"][1]) - sn) <= tol_n + 2.0 ** -24 * abs(sn), (g["grads"], sn, tol_n)
+    print(f"[ttq full] grads {g['grads'].tolist()} vs sums of dW {sp:.6g} {sn:.6g}", flush=True)
+
+
+def test_ttq_module():
+    """TTQLinear: the forward and the gradients of x, the weight and the raw
+    scale parameters (softplus chain) against the oracle on the parameters
+    the module passes."""
+    from ternary_weight_quantization_amd.ttq_layer import TTQLinear
+    torch.manual_seed(0)
+    M, K, N = 96, 320, 200
+    note("ttq module")
+    layer = TTQLinear(K, N)
+    p = layer.params().detach().cpu().numpy()
+    w = layer.weight.detach().float().cpu().numpy().astype(np.float64)
+    delta0, e0, _ = O.ttq_init(w)
+    # after the softplus round trip the scales are within a few ulps of Eq. 2
+    assert np.allclose(p, [delta0, e0, e0], rtol=1e-5)
+    x = torch.randn(M, K, device="cuda").to(torch.bfloat16).requires_grad_(True)
+    y = layer(x)
+    dy = torch.randn(M, N, device="cuda").to(torch.bfloat16)
+    y.backward(dy)
+    xs = x.detach().float().cpu().numpy().astype(np.float64)
+    dys = dy.float().cpu().numpy().astype(np.float64)
+    r = O.ttq_layer(xs, w, dys, params=tuple(np.float32(v) for v in p))
+    C.check(y.detach().float().cpu().numpy(), r["y"], "y_ttq")
+    C.check(x.grad.float().cpu().numpy(), r["dX"], "dX")
+    C.check(layer.weight.grad.float().cpu().numpy(), r["dW"], "dW")
+    sig = 1.0 / (1.0 + np.exp(-layer.raw.detach().double().cpu().numpy()))
+    graw = layer.raw.grad.double().cpu().numpy()
+    assert graw[0] == 0.0
+    bp, bn = grads_bound(dys, xs, r["q"], M)
+    assert abs(graw[1] - r["g_wp"] * sig[1]) <= (bp + 1e-6 * abs(r["g_wp"])) * sig[1] + 1e-6 * abs(graw[1])
+    assert abs(graw[2] - r["g_wn"] * sig[2]) <= (bn + 1e-6 * abs(r["g_wn"])) * sig[2] + 1e-6 * abs(graw[2])
+    codes, params = layer.export_inference()
+    assert np.array_equal(codes.cpu().numpy(), O.pack_codes(O.ttq_codes(w, np.float32(p[0]))))
