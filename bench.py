@@ -382,6 +382,28 @@ def main():
     def bias_grad(s):
         B.bitlinear_bias_grad(s["dY"], s["db"])
 
+    # The TTQ variant on the same shape ("TTQ_VERIFICATION.md": bf16
+    # activations, a bf16 weight of {Wp, 0, -Wn}): quantize, forward, and the
+    # backward with dX, dW and the two scale gradients; parameters from its
+    # initialization. Timed the same way; not part of the step.
+    for s in sets:
+        s["ttq_params"] = torch.empty((3,), dtype=torch.float32, device=dev)
+        B.ttq_init(s["W"], s["ttq_params"], s["ws"])
+        s["ttq_codes"] = torch.empty((N, Kp // 4), dtype=torch.uint8, device=dev)
+        s["ttq_wt"] = torch.empty((N, Kp), dtype=torch.bfloat16, device=dev)
+        s["ttq_grads"] = torch.empty((2,), dtype=torch.float32, device=dev)
+    ttq_ws = torch.empty((max(B.ttq_workspace_bytes(M, N, K), 1),), dtype=torch.uint8, device=dev)
+
+    def ttq_quantize(s):
+        B.ttq_quantize(s["W"], s["ttq_params"], s["ttq_codes"], s["ttq_wt"])
+
+    def ttq_fwd(s):
+        B.ttq_fwd(s["x"], s["ttq_wt"], s["y"], workspace=ttq_ws)
+
+    def ttq_bwd(s):
+        B.ttq_bwd(s["dY"], s["x"], s["ttq_wt"], s["ttq_codes"], K, dX=s["dX"], dW=s["dW"], grads=s["ttq_grads"],
+                  workspace=ttq_ws)
+
     def per_call_ms(f):
         for i in range(args.warmup):
             f(sets[i % len(sets)])
@@ -397,6 +419,9 @@ def main():
     sign1_ms = per_call_ms(bwd_sign1)
     fwd_bias_ms = per_call_ms(fwd_bias)
     bias_grad_ms = per_call_ms(bias_grad)
+    ttq_quantize(sets[0])
+    torch.cuda.synchronize()
+    ttq_ms = {n: per_call_ms(f) for n, f in (("quantize", ttq_quantize), ("fwd", ttq_fwd), ("bwd", ttq_bwd))}
 
     gemm_ops = 2.0 * M * N * K
     tops = 3 * gemm_ops / (ms_per_step * 1e-3) / 1e12
@@ -453,7 +478,21 @@ def main():
             "bias_grad": {
                 "ms": round(bias_grad_ms, 4), "bound": "hbm", "unit": "GB/s",
                 "achieved": round((2.0 * M * N + 4 * N) / 1e9 / (bias_grad_ms * 1e-3), 2),
-                "frac": round((2.0 * M * N + 4 * N) / 1e9 / (bias_grad_ms * 1e-3) / PEAK_HBM_GBS, 4)}},
+                "frac": round((2.0 * M * N + 4 * N) / 1e9 / (bias_grad_ms * 1e-3) / PEAK_HBM_GBS, 4)},
+            # read W, write the codes and the bf16 weight
+            "ttq_quantize": {
+                "ms": round(ttq_ms["quantize"], 4), "bound": "hbm", "unit": "GB/s",
+                "achieved": round((w_bytes * N * K + N * Kp / 4 + 2 * N * Kp) / 1e9 / (ttq_ms["quantize"] * 1e-3), 2),
+                "frac": round((w_bytes * N * K + N * Kp / 4 + 2 * N * Kp) / 1e9 / (ttq_ms["quantize"] * 1e-3)
+                              / PEAK_HBM_GBS, 4)},
+            "ttq_fwd": {
+                "ms": round(ttq_ms["fwd"], 4), "bound": "mfma", "unit": "TFLOP/s",
+                "achieved": round(gemm_ops / 1e12 / (ttq_ms["fwd"] * 1e-3), 2),
+                "frac": round(gemm_ops / 1e12 / (ttq_ms["fwd"] * 1e-3) / PEAK_BF16_TFLOPS, 4)},
+            "ttq_bwd": {
+                "ms": round(ttq_ms["bwd"], 4), "bound": "mfma", "unit": "TFLOP/s",
+                "achieved": round(2 * gemm_ops / 1e12 / (ttq_ms["bwd"] * 1e-3), 2),
+                "frac": round(2 * gemm_ops / 1e12 / (ttq_ms["bwd"] * 1e-3) / PEAK_BF16_TFLOPS, 4)}},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

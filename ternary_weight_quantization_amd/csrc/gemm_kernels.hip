@@ -1641,13 +1641,21 @@ static int64_t ttq_wave_tiles(int64_t N, int64_t K) {
 static size_t ttq_partials_bytes(int64_t N, int64_t K) {
   return ((size_t)ttq_wave_tiles(N, K) * sizeof(float2) + 255) / 256 * 256;
 }
+// dX and dW of TTQ in one launch: both operands copied as stored (N, K
+// multiples of 8) and each product splitting its tiles on a full device.
+static bool ttq_pair_eligible(int64_t M, int64_t N, int64_t K) {
+  return N % 8 == 0 && K % 8 == 0 && split_pays(shape_of(GemmKind::kBwdDx, M, N, K), kMaxGrid) > 0 &&
+         split_pays(shape_of(GemmKind::kBwdDw, M, N, K), kMaxGrid) > 0;
+}
+static size_t pair_split_bound(const GemmShape& g1, const GemmShape& g2);
 
 size_t gemm_workspace_bytes(GemmKind kind, int64_t M, int64_t N, int64_t K) {
   if (kind == GemmKind::kBwdPair) return pair_eligible(M, N, K) ? pair_workspace_bound(M, N, K) : 0;
   if (kind == GemmKind::kTtqBwd) {
     const GemmShape gx = shape_of(GemmKind::kBwdDx, M, N, K), gw = shape_of(GemmKind::kBwdDw, M, N, K);
     const size_t a = split_workspace(gx, split_grid(gx, kMaxGrid)), b = split_workspace(gw, split_grid(gw, kMaxGrid));
-    return ttq_partials_bytes(N, K) + (a > b ? a : b);
+    const size_t c = ttq_pair_eligible(M, N, K) ? pair_split_bound(gx, gw) : 0;
+    return ttq_partials_bytes(N, K) + std::max(std::max(a, b), c);
   }
   const GemmShape g = shape_of(kind, M, N, K);
   // the few-token forward needs none; the large-M kernel's share stays
@@ -1710,7 +1718,7 @@ constexpr double kDwStageCost = 1.07;
 // minimizes the slower product's modelled cost; 0: no pair launch (the
 // split knob is set, or too few CUs). BITNET_PAIR_COLS=<k1> overrides
 // (tuning knob).
-static int pair_columns(const GemmShape& g1, const GemmShape& g2, int cus, int* kt) {
+static int pair_columns(const GemmShape& g1, const GemmShape& g2, int cus, int* kt, double c1, double c2) {
   if (getenv("BITNET_SPLIT_CTAS")) return 0;
   *kt = (cus < kMaxGrid ? cus : kMaxGrid) / 8;
   if (*kt < 2) return 0;
@@ -1721,7 +1729,7 @@ static int pair_columns(const GemmShape& g1, const GemmShape& g2, int cus, int* 
   int best = 1;
   double best_t = 1e300;
   for (int k1 = 1; k1 < *kt; ++k1) {
-    const double t = std::max(product_cost(g1, 8 * k1, 1.0).t, product_cost(g2, 8 * (*kt - k1), kDwStageCost).t);
+    const double t = std::max(product_cost(g1, 8 * k1, c1).t, product_cost(g2, 8 * (*kt - k1), c2).t);
     if (t < best_t) {
       best_t = t;
       best = k1;
@@ -1878,13 +1886,21 @@ hipError_t launch_bwd_dw(const uint16_t* dY, const int8_t* x_q, const float* s_x
   }
 }
 
-hipError_t launch_bwd_pair(const uint16_t* dY, const uint8_t* w_packed, const float* gamma, const int8_t* x_q,
-                           const float* s_x, int64_t M, int64_t N, int64_t K, uint16_t* dX, void* dW,
-                           DwOut dw_out, void* ws, size_t ws_bytes, hipStream_t stream) {
-  if (!pair_eligible(M, N, K) || ws == nullptr || skinny(M)) return hipErrorNotSupported;
-  const GemmShape g1 = shape_of(GemmKind::kBwdDx, M, N, K), g2 = shape_of(GemmKind::kBwdDw, M, N, K);
+// Two products in one gemm_pair_kernel launch, each on its own share of the
+// CUs (pair_columns), each splitting its tiles only when the cost model says
+// that beats whole tiles taken in turn on its share (stage costs c1, c2).
+// ws holds the two split workspaces (pair_split_bound bytes suffice).
+// hipErrorNotSupported (nothing launched): the device or the workspace does
+// not allow it.
+static size_t pair_split_bound(const GemmShape& g1, const GemmShape& g2) {
+  return split_control_bytes(g1, kMaxGrid) + split_control_bytes(g2, kMaxGrid) + 2 * (size_t)kMaxGrid * kPartialBytes;
+}
+template <int MAP1, int MAP2, class PL1, class QL1, class EP1, class PL2, class QL2, class EP2>
+static hipError_t run_pair(const PL1& p1, const QL1& q1, const EP1& e1, const GemmShape& g1, double c1,
+                           const PL2& p2, const QL2& q2, const EP2& e2, const GemmShape& g2, double c2, char* ws,
+                           size_t ws_bytes, hipStream_t stream) {
   int kt = 0;
-  const int k1 = pair_columns(g1, g2, device_cus(), &kt);
+  const int k1 = pair_columns(g1, g2, device_cus(), &kt, c1, c2);
   if (k1 == 0) return hipErrorNotSupported;
   // every workgroup of a split needs a non-empty range, and more than about
   // 4 pieces per tile do not pay
@@ -1892,15 +1908,28 @@ hipError_t launch_bwd_pair(const uint16_t* dY, const uint8_t* w_packed, const fl
     const int64_t W = g.tiles() * g.nstages, P = 4 * g.tiles();
     return (int)(G < W ? (G < P ? G : P) : (W < P ? W : P));
   };
-  // each product splits its tiles only when the cost model says that beats
-  // whole tiles taken in turn on its share of the CUs
   const int64_t share1 = 8 * k1, share2 = 8 * (kt - k1);
-  const bool sk1 = product_cost(g1, share1, 1.0).split, sk2 = product_cost(g2, share2, kDwStageCost).split;
+  const bool sk1 = product_cost(g1, share1, c1).split, sk2 = product_cost(g2, share2, c2).split;
   const int G1 = sk1 ? cap(g1, share1) : (int)(g1.tiles() < share1 ? g1.tiles() : share1);
   const int G2 = sk2 ? cap(g2, share2) : (int)(g2.tiles() < share2 ? g2.tiles() : share2);
-  const size_t wb = wt_bytes(N, K), xb = xhat_bytes(M, K);
   const size_t s1 = sk1 ? split_workspace(g1, G1) : 0, s2 = sk2 ? split_workspace(g2, G2) : 0;
-  if (ws_bytes < wb + xb + s1 + s2) return hipErrorNotSupported;
+  if (ws_bytes < s1 + s2) return hipErrorNotSupported;
+  const SplitPlan plan1 = sk1 ? split_plan(g1, G1, ws) : whole_plan(g1, G1);
+  const SplitPlan plan2 = sk2 ? split_plan(g2, G2, ws + s1) : whole_plan(g2, G2);
+  gemm_pair_kernel<MfmaBf16, MAP1, PL1, QL1, EP1, MAP2, PL2, QL2, EP2>
+      <<<8 * kt, kThreads, 0, stream>>>(p1, q1, e1, plan1, p2, q2, e2, plan2, k1);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_pair(const uint16_t* dY, const uint8_t* w_packed, const float* gamma, const int8_t* x_q,
+                           const float* s_x, int64_t M, int64_t N, int64_t K, uint16_t* dX, void* dW,
+                           DwOut dw_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!pair_eligible(M, N, K) || ws == nullptr || skinny(M)) return hipErrorNotSupported;
+  const GemmShape g1 = shape_of(GemmKind::kBwdDx, M, N, K), g2 = shape_of(GemmKind::kBwdDw, M, N, K);
+  const size_t wb = wt_bytes(N, K), xb = xhat_bytes(M, K);
+  if (ws_bytes < wb + xb) return hipErrorNotSupported;
+  int kt = 0;
+  if (pair_columns(g1, g2, device_cus(), &kt, 1.0, kDwStageCost) == 0) return hipErrorNotSupported;
   char* base = static_cast<char*>(ws);
   uint8_t* wt = reinterpret_cast<uint8_t*>(base);
   uint16_t* xhat = reinterpret_cast<uint16_t*>(base + wb);
@@ -1918,20 +1947,27 @@ hipError_t launch_bwd_pair(const uint16_t* dY, const uint8_t* w_packed, const fl
   const Bf16Epilogue<false> e1{dX, gamma, K, M};
   const RowCopyBf16Loader<1> p2{xhat, Kp, M, Kp};
   const RowCopyBf16Loader<5> q2{dY, N, M, N};
-  const SplitPlan plan1 = sk1 ? split_plan(g1, G1, base + wb + xb) : whole_plan(g1, G1);
-  const SplitPlan plan2 = sk2 ? split_plan(g2, G2, base + wb + xb + s1) : whole_plan(g2, G2);
-  const auto launch = [&](const auto& e2) {
-    typedef typename std::decay<decltype(e2)>::type EP2;
-    gemm_pair_kernel<MfmaBf16, 1, RowCodesLoader<CodesFp4Frags>, CopyLoader<2, true>, Bf16Epilogue<false>, 0,
-                     RowCopyBf16Loader<1>, RowCopyBf16Loader<5>, EP2>
-        <<<8 * kt, kThreads, 0, stream>>>(p1, q1, e1, plan1, p2, q2, e2, plan2, k1);
-  };
+  char* sws = base + wb + xb;
+  const size_t sbytes = ws_bytes - wb - xb;
+  hipError_t e;
   switch (dw_out) {
-    case DwOut::kF32: launch(Bf16Epilogue<true>{dW, nullptr, K, N}); break;
-    case DwOut::kSign1: launch(Sign1Epilogue{static_cast<uint8_t*>(dW), Kp, N}); break;
-    default: launch(Bf16Epilogue<false>{dW, nullptr, K, N}); break;
+    case DwOut::kF32:
+      e = run_pair<1, 0>(p1, q1, e1, g1, 1.0, p2, q2, Bf16Epilogue<true>{dW, nullptr, K, N}, g2, kDwStageCost, sws,
+                         sbytes, stream);
+      break;
+    case DwOut::kSign1:
+      e = run_pair<1, 0>(p1, q1, e1, g1, 1.0, p2, q2, Sign1Epilogue{static_cast<uint8_t*>(dW), Kp, N}, g2,
+                         kDwStageCost, sws, sbytes, stream);
+      break;
+    default:
+      e = run_pair<1, 0>(p1, q1, e1, g1, 1.0, p2, q2, Bf16Epilogue<false>{dW, nullptr, K, N}, g2, kDwStageCost, sws,
+                         sbytes, stream);
+      break;
   }
-  return hipGetLastError();
+  // (the C ABI's workspace covers the pair and pair_columns was checked
+  // above, so this is not NotSupported; if it were, the separate launches
+  // the caller falls back to rebuild both operands)
+  return e;
 }
 
 // ---------------------------------------------------------------------------
@@ -1983,18 +2019,51 @@ static hipError_t launch_ttq_dw(const uint16_t* dY, const uint16_t* x, const uin
                                RowTransposeBf16Loader<false, 5>{dY, N, M, N}, ep, g, ws, ws_bytes, stream);
 }
 
+// dX and dW in one gemm_pair_kernel launch (as the BitNet backward):
+// hipErrorNotSupported when the shape or the device does not allow it.
+template <bool OUT_F32>
+static hipError_t launch_ttq_pair(const uint16_t* dY, const uint16_t* x, const uint16_t* wt, const uint8_t* w_packed,
+                                  int64_t M, int64_t N, int64_t K, uint16_t* dX, void* dW, float2* partials,
+                                  char* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!ttq_pair_eligible(M, N, K)) return hipErrorNotSupported;
+  const int64_t Kp = k_pad(K);
+  const GemmShape g1 = shape_of(GemmKind::kBwdDx, M, N, K), g2 = shape_of(GemmKind::kBwdDw, M, N, K);
+  const RowCopyBf16Loader<5> p1{wt, Kp, N, K};
+  const CopyLoader<2, true, 1> q1{reinterpret_cast<const char*>(dY), 2 * N, M, 2 * N};
+  const Bf16Epilogue<false> e1{dX, nullptr, K, M};
+  const RowCopyBf16Loader<1> p2{x, K, M, K};
+  const RowCopyBf16Loader<5> q2{dY, N, M, N};
+  const TtqDwEpilogue<OUT_F32> e2{Bf16Epilogue<OUT_F32>{dW, nullptr, K, N}, w_packed, (uint32_t)(Kp / 4), partials,
+                                  (int)(2 * g2.tiles_i)};
+  // stage costs as for the BitNet pair: measured alone at 4096x2560->6912,
+  // this dX (bf16 weight) takes 158-166 us and dW 176-189 us, about the
+  // BitNet products' ratio; 15 of 32 columns for dX then give 260 us, 16
+  // give 325 us (equal costs chose 16)
+  return run_pair<0, 0>(p1, q1, e1, g1, 1.0, p2, q2, e2, g2, kDwStageCost, ws, ws_bytes, stream);
+}
+
 hipError_t launch_ttq_bwd(const uint16_t* dY, const uint16_t* x, const uint16_t* wt, const uint8_t* w_packed,
                           int64_t M, int64_t N, int64_t K, uint16_t* dX, void* dW, bool dw_f32, float* grads,
                           void* ws, size_t ws_bytes, hipStream_t stream) {
   const size_t pb = ttq_partials_bytes(N, K);
   if (ws == nullptr || ws_bytes < pb) return hipErrorInvalidValue;  // the C ABI sized it
   float2* partials = static_cast<float2*>(ws);
-  void* split_ws = static_cast<char*>(ws) + pb;
+  char* split_ws = static_cast<char*>(ws) + pb;
   const size_t split_bytes = ws_bytes - pb;
+  float2* p = grads != nullptr ? partials : nullptr;
+  if (dX != nullptr && dW != nullptr) {
+    const hipError_t e =
+        dw_f32 ? launch_ttq_pair<true>(dY, x, wt, w_packed, M, N, K, dX, dW, p, split_ws, split_bytes, stream)
+               : launch_ttq_pair<false>(dY, x, wt, w_packed, M, N, K, dX, dW, p, split_ws, split_bytes, stream);
+    if (e != hipErrorNotSupported) {
+      if (e != hipSuccess || grads == nullptr) return e;
+      ttq_grads_kernel<<<1, 256, 0, stream>>>(partials, (int)ttq_wave_tiles(N, K), grads);
+      return hipGetLastError();
+    }
+  }
   if (dX != nullptr)
     if (hipError_t e = launch_ttq_dx(dY, wt, M, N, K, dX, split_ws, split_bytes, stream)) return e;
   if (dW != nullptr) {
-    float2* p = grads != nullptr ? partials : nullptr;
     const hipError_t e = dw_f32 ? launch_ttq_dw<true>(dY, x, w_packed, M, N, K, dW, p, split_ws, split_bytes, stream)
                                 : launch_ttq_dw<false>(dY, x, w_packed, M, N, K, dW, p, split_ws, split_bytes, stream);
     if (e != hipSuccess) return e;

@@ -169,10 +169,11 @@ def test_ttq_size_queries(L):
     # no split at a single tile: only the scale-gradient partials (one float2
     # per 128 x 128 tile of dW, rounded up to 256 bytes)
     assert L.ttq_workspace_bytes(64, 128, 256) == 256
-    # 4096x2560->6912: dW has 10 x 27 tiles (4 partials each); both
-    # backward products and the forward split over 256 workgroups
+    # 4096x2560->6912: dW has 10 x 27 tiles (4 partials each); dX and dW run
+    # in one launch: both products' counters (160 and 270 tiles) and the
+    # partial tiles of their shares of the 256 workgroups
     partials = (4 * 270 * 8 + 255) // 256 * 256
-    assert L.ttq_workspace_bytes(4096, 6912, 2560) == partials + 4352 + 2 * 256 * tile
+    assert L.ttq_workspace_bytes(4096, 6912, 2560) == partials + 2560 + 4352 + 2 * 256 * tile
     assert L.ttq_workspace_bytes(0, 4, 4) == 0
 
 

@@ -164,6 +164,18 @@ def test_ttq_optional_outputs():
     assert np.array_equal(b["grads"].view(np.uint32), full["grads"].view(np.uint32))
 
 
+@pytest.mark.parametrize("knob", [None, "-1"])
+def test_ttq_paired_backward(monkeypatch, knob):
+    """2048 x 1024 -> 1024: dX and dW split their tiles, so they run in one
+    paired launch; BITNET_SPLIT_CTAS=-1 (a test knob) forces whole tiles,
+    one product after the other. Both against the oracle."""
+    if knob is not None:
+        monkeypatch.setenv("BITNET_SPLIT_CTAS", knob)
+    inp = WL.custom_inputs(2048, 1024, 1024, seed=31)
+    note(f"ttq paired backward, BITNET_SPLIT_CTAS={knob}")
+    check_ttq(inp, run_ttq(inp))
+
+
 def test_ttq_full_size_sampled():
     """The 4096 x 2560 -> 6912 layer in the launch configuration the
     benchmark times: bit-exact parameters, codes and values; y, dX, dW on
