@@ -98,8 +98,9 @@ def _pmc_rows(d):
     return rows
 
 
-# kernels of calls outside the step (the sign-output backward, the forward with a bias)
-KERNEL_EXCLUDE = ["Sign1Epilogue", "FwdEpilogue<true>"]
+# kernels of calls outside the step (the sign-output backward, the forward with a
+# bias, the TTQ backward's pair launch)
+KERNEL_EXCLUDE = ["Sign1Epilogue", "FwdEpilogue<true>", "TtqDwEpilogue"]
 
 
 def _per_dispatch_mean(rows, counter, match):
