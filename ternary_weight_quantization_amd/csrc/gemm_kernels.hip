@@ -1569,7 +1569,10 @@ static GemmShape shape_of(GemmKind kind, int64_t M, int64_t N, int64_t K) {
   const int64_t Kp = k_pad(K);
   switch (kind) {
     case GemmKind::kFwd: return {(N + kBI - 1) / kBI, (M + kBJ - 1) / kBJ, (Kp + kStageBytes - 1) / kStageBytes, 7};
-    case GemmKind::kTtqFwd: return {(N + kBI - 1) / kBI, (M + kBJ - 1) / kBJ, (Kp + kRed16 - 1) / kRed16, 3};
+    // a split piece costs the bf16 forward about 20 of its stages (measured
+    // at 4096x2560->6912: whole tiles in two rounds 171 us, split over 256
+    // workgroups 185 us)
+    case GemmKind::kTtqFwd: return {(N + kBI - 1) / kBI, (M + kBJ - 1) / kBJ, (Kp + kRed16 - 1) / kRed16, 20};
     case GemmKind::kBwdDx: return {(K + kBI - 1) / kBI, (M + kBJ - 1) / kBJ, (N + kRed16 - 1) / kRed16, 3};
     case GemmKind::kBwdDw: case GemmKind::kBwdPair: case GemmKind::kTtqBwd: break;
   }
