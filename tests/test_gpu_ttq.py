@@ -247,3 +247,57 @@ def test_ttq_module():
     assert abs(graw[2] - r["g_wn"] * sig[2]) <= (bn + 1e-6 * abs(r["g_wn"])) * sig[2] + 1e-6 * abs(graw[2])
     codes, params = layer.export_inference()
     assert np.array_equal(codes.cpu().numpy(), O.pack_codes(O.ttq_codes(w, np.float32(p[0]))))
+
+
+@pytest.mark.parametrize("M,K,N,split", [
+    (300, 1000, 776, 13),      # split tiles forced, dX and dW one after the other
+    (2048, 1024, 1024, None),  # dX and dW in one paired launch, both split
+])
+def test_ttq_graph_replays_match_eager(M, K, N, split, monkeypatch):
+    """ttq_quantize, ttq_fwd and ttq_bwd (with the scale gradients) captured
+    once into a HIP graph and replayed three times, with eager calls on the
+    same workspace between the replays: every replay writes the eager
+    outputs bit for bit (split-tile counters are left cleared by every
+    launch; the gradient partials are rewritten in full by every call)."""
+    if split is not None:
+        monkeypatch.setenv("BITNET_SPLIT_CTAS", str(split))
+    from ternary_weight_quantization_amd import binding as B
+    from tests.gpu_util import dev_bf16
+    inp = WL.custom_inputs(M, K, N, seed=M + N + 1)
+    note(f"ttq graph replays M={M} K={K} N={N} split={split}")
+    dev = torch.device("cuda")
+    Kp = B.bitnet_k_pad(K)
+    W, x, dY = dev_bf16(inp["W"]), dev_bf16(inp["x"]), dev_bf16(inp["dY"])
+    params = torch.empty((3,), dtype=torch.float32, device=dev)
+    B.ttq_init(W, params, torch.empty((B.bitnet_ternarize_workspace_bytes(N, K),), dtype=torch.uint8, device=dev))
+    t = dict(codes=torch.empty((N, Kp // 4), dtype=torch.uint8, device=dev),
+             wt=torch.empty((N, Kp), dtype=torch.bfloat16, device=dev),
+             y=torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+             dX=torch.empty((M, K), dtype=torch.bfloat16, device=dev),
+             dW=torch.empty((N, K), dtype=torch.bfloat16, device=dev),
+             grads=torch.empty((2,), dtype=torch.float32, device=dev))
+    ws = torch.empty((max(B.ttq_workspace_bytes(M, N, K), 256),), dtype=torch.uint8, device=dev)
+
+    def step():
+        B.ttq_quantize(W, params, t["codes"], t["wt"])
+        B.ttq_fwd(x, t["wt"], t["y"], workspace=ws)
+        B.ttq_bwd(dY, x, t["wt"], t["codes"], K, dX=t["dX"], dW=t["dW"], grads=t["grads"], workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in t.items()}
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for r in range(3):
+        for v in t.values():
+            v.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, v in t.items():
+            assert torch.equal(v, ref[k]), (r, k)
+        step()
+        torch.cuda.synchronize()
+        for k in ("y", "dX", "dW", "grads"):
+            assert torch.equal(t[k], ref[k]), ("eager", r, k)
