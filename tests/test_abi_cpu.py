@@ -210,3 +210,18 @@ def test_ttq_validation(L):
     assert L.ttq_bwd(A, A, A, A, 4, 4, 4, None, A, 0, None, A, ws - 1, None) == EWS
     assert L.ttq_bwd(A, A, A, A, 4, 4, 4, None, A, 0, A + 2, A, ws, None) == EALIGN
     assert L.ttq_bwd(A, A, A, A, 4, 4, 4, MISALIGNED, None, 0, None, A, ws, None) == EALIGN
+
+
+def test_ttq_inverse_softplus_round_trip():
+    """TTQLinear keeps its three scalars raw and applies softplus; the raw
+    start values are the inverse softplus of the initial (delta, Wp, Wn)
+    ("TTQ_VERIFICATION.md", Bugs Fixed item 5). The round trip returns the
+    values across the range a layer's E|W| takes (CPU, float64 and the
+    float32 the module stores)."""
+    import torch
+    from ternary_weight_quantization_amd.ttq_layer import _inverse_softplus
+    v = torch.tensor([1e-8, 1e-5, 3e-3, 0.02, 0.7, 5.0], dtype=torch.float64)
+    r = _inverse_softplus(v)
+    assert torch.allclose(torch.nn.functional.softplus(r), v, rtol=1e-12, atol=0)
+    r32 = r.float()
+    assert torch.allclose(torch.nn.functional.softplus(r32).double(), v, rtol=1e-5, atol=0)
