@@ -401,6 +401,13 @@ def main():
     def ttq_fwd(s):
         B.ttq_fwd(s["x"], s["ttq_wt"], s["y"], workspace=ttq_ws)
 
+    # the forward from the stored codes and params (the exported state): the
+    # few-token kernel at M <= 64, else the codes expanded and the GEMM
+    ttq_codes_ws = torch.empty((max(B.ttq_fwd_codes_workspace_bytes(M, N, K), 1),), dtype=torch.uint8, device=dev)
+
+    def ttq_fwd_codes(s):
+        B.ttq_fwd_codes(s["x"], s["ttq_codes"], s["ttq_params"], s["y"], workspace=ttq_codes_ws)
+
     def ttq_bwd(s):
         B.ttq_bwd(s["dY"], s["x"], s["ttq_wt"], s["ttq_codes"], K, dX=s["dX"], dW=s["dW"], grads=s["ttq_grads"],
                   workspace=ttq_ws)
@@ -422,7 +429,8 @@ def main():
     bias_grad_ms = per_call_ms(bias_grad)
     ttq_quantize(sets[0])
     torch.cuda.synchronize()
-    ttq_ms = {n: per_call_ms(f) for n, f in (("quantize", ttq_quantize), ("fwd", ttq_fwd), ("bwd", ttq_bwd))}
+    ttq_ms = {n: per_call_ms(f) for n, f in (("quantize", ttq_quantize), ("fwd", ttq_fwd), ("bwd", ttq_bwd),
+                                              ("fwd_codes", ttq_fwd_codes))}
 
     gemm_ops = 2.0 * M * N * K
     tops = 3 * gemm_ops / (ms_per_step * 1e-3) / 1e12
@@ -490,6 +498,14 @@ def main():
                 "ms": round(ttq_ms["fwd"], 4), "bound": "mfma", "unit": "TFLOP/s",
                 "achieved": round(gemm_ops / 1e12 / (ttq_ms["fwd"] * 1e-3), 2),
                 "frac": round(gemm_ops / 1e12 / (ttq_ms["fwd"] * 1e-3) / PEAK_BF16_TFLOPS, 4)},
+            # rate on the forward's flops; at few tokens the bound is reading
+            # the codes (N * Kp / 4 bytes) and x
+            "ttq_fwd_codes": {
+                "ms": round(ttq_ms["fwd_codes"], 4), "bound": "mfma", "unit": "TFLOP/s",
+                "achieved": round(gemm_ops / 1e12 / (ttq_ms["fwd_codes"] * 1e-3), 2),
+                "frac": round(gemm_ops / 1e12 / (ttq_ms["fwd_codes"] * 1e-3) / PEAK_BF16_TFLOPS, 4),
+                "codes_GB_per_s": round((N * Kp / 4 + 2.0 * M * K + 2.0 * M * N) / 1e9 / (ttq_ms["fwd_codes"] * 1e-3),
+                                        2)},
             "ttq_bwd": {
                 "ms": round(ttq_ms["bwd"], 4), "bound": "mfma", "unit": "TFLOP/s",
                 "achieved": round(2 * gemm_ops / 1e12 / (ttq_ms["bwd"] * 1e-3), 2),

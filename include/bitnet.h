@@ -288,6 +288,28 @@ bitnet_status ttq_fwd(const uint16_t* x, const uint16_t* wt, int64_t M, int64_t 
                       uint16_t* y, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * ttq_fwd_codes - the same forward from the stored state (the codes and
+ * params, e.g. an exported layer): y[m,n] = sum_k x[m,k] * v(q[n,k]), with
+ * v(+1) = bf16(Wp), v(-1) = -bf16(Wn), v(0) = 0, fp32 sums rounded once to
+ * bf16. For few tokens (M <= 64, K % 8 == 0) one kernel reads the 2-bit
+ * codes once and expands them in registers; otherwise the codes are
+ * expanded to wt in the workspace and ttq_fwd's GEMM runs on it (the same
+ * bits as ttq_fwd on ttq_quantize's wt).
+ *
+ * x         [M][K] bf16 bits.  w_packed [N][Kp/4] codes.  params [3] float
+ *           (device, 4-byte aligned): delta (unused here), Wp, Wn.
+ * y         [M][N] bf16 bits.
+ * workspace ttq_fwd_codes_workspace_bytes(M, N, K) bytes: 0 (NULL allowed)
+ *           when the few-token kernel applies, else 2*N*Kp for the expanded
+ *           weight plus the GEMM's share; clobbered.
+ * Limits as for ttq_fwd, and (N + 256) * Kp/4 bytes of codes.
+ */
+size_t ttq_fwd_codes_workspace_bytes(int64_t M, int64_t N, int64_t K);
+bitnet_status ttq_fwd_codes(const uint16_t* x, const uint8_t* w_packed, const float* params,
+                            int64_t M, int64_t N, int64_t K, uint16_t* y,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * ttq_bwd - the straight-through backward (Algorithm Summary, Backward
  * Pass; "Bugs Fixed", item 5):
  *

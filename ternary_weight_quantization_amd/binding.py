@@ -80,6 +80,10 @@ def lib():
     L.ttq_fwd.restype = st
     L.ttq_bwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp, st, vp, vp, sz, vp]
     L.ttq_bwd.restype = st
+    L.ttq_fwd_codes_workspace_bytes.argtypes = [i64, i64, i64]
+    L.ttq_fwd_codes_workspace_bytes.restype = sz
+    L.ttq_fwd_codes.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, sz, vp]
+    L.ttq_fwd_codes.restype = st
     if len(_hip_runtimes_mapped()) > 1:
         raise RuntimeError("more than one libamdhip64 is mapped into this process: "
                            f"{sorted(_hip_runtimes_mapped())}")
@@ -304,6 +308,27 @@ def ttq_fwd(x, wt, y, workspace=None, stream=None):
         workspace = _workspace(ttq_workspace_bytes(M, N, K), y, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().ttq_fwd(_ptr(x), _ptr(wt), M, N, K, _ptr(y), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def ttq_fwd_codes_workspace_bytes(M, N, K):
+    return int(lib().ttq_fwd_codes_workspace_bytes(int(M), int(N), int(K)))
+
+
+def ttq_fwd_codes(x, w_packed, params, y, workspace=None, stream=None):
+    """y [M, N] bf16 from x [M, K] bf16, the codes uint8 [N, Kp/4] and params
+    float32 [3] = (delta, Wp, Wn)."""
+    M, K = x.shape
+    N = w_packed.shape[0]
+    Kp = bitnet_k_pad(K)
+    _need(x, torch.bfloat16, (M, K), "x")
+    _need(w_packed, torch.uint8, (N, Kp // 4), "w_packed")
+    _need(params, torch.float32, (3,), "params")
+    _need(y, torch.bfloat16, (M, N), "y")
+    if workspace is None:
+        workspace = _workspace(ttq_fwd_codes_workspace_bytes(M, N, K), y, stream)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().ttq_fwd_codes(_ptr(x), _ptr(w_packed), _ptr(params), M, N, K, _ptr(y), _ptr(workspace), ws_bytes,
+                               _stream(stream)))
 
 
 def ttq_bwd(dY, x, wt, w_packed, K, dX=None, dW=None, grads=None, workspace=None, stream=None):

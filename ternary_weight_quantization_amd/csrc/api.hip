@@ -234,6 +234,28 @@ bitnet_status ttq_fwd(const uint16_t* x, const uint16_t* wt, int64_t M, int64_t 
                                          static_cast<hipStream_t>(stream)));
 }
 
+size_t ttq_fwd_codes_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (check_gemm_sizes(M, N, K) != BITNET_OK) return 0;
+  return bitnet::ttq_codes_workspace_bytes(M, N, K);
+}
+
+bitnet_status ttq_fwd_codes(const uint16_t* x, const uint8_t* w_packed, const float* params, int64_t M, int64_t N,
+                            int64_t K, uint16_t* y, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!x || !w_packed || !params || !y) return BITNET_ERR_NULL;
+  if (bitnet_status st = check_gemm_sizes(M, N, K)) return st;
+  const int64_t Kp = bitnet::k_pad(K);
+  if (32 * 4 * N > (int64_t(1) << 31) || !buffer_range_ok(M, 2 * K) || !buffer_range_ok(N, 2 * Kp) ||
+      !buffer_range_ok(N, Kp / 4))
+    return BITNET_ERR_SHAPE;
+  const size_t need = ttq_fwd_codes_workspace_bytes(M, N, K);
+  if (workspace_bytes < need || (need > 0 && !workspace)) return BITNET_ERR_WORKSPACE;
+  if (!aligned(workspace, 16) || !aligned(x, 16) || !aligned(w_packed, 16) || !aligned(params, 4) ||
+      !aligned(y, 16))
+    return BITNET_ERR_ALIGN;
+  return from_hip(bitnet::launch_ttq_fwd_codes(x, w_packed, params, M, N, K, y, workspace, workspace_bytes,
+                                               static_cast<hipStream_t>(stream)));
+}
+
 bitnet_status ttq_bwd(const uint16_t* dY, const uint16_t* x, const uint16_t* wt, const uint8_t* w_packed, int64_t M,
                       int64_t N, int64_t K, uint16_t* dX, void* dW, bitnet_dtype dW_dtype, float* grads,
                       void* workspace, size_t workspace_bytes, void* stream) {

@@ -1992,6 +1992,31 @@ hipError_t launch_ttq_fwd(const uint16_t* x, const uint16_t* wt, int64_t M, int6
   return run_gemm<MfmaBf16, 1>(pl, CopyLoader<2, false, 5>{xb, 2 * K, M, 2 * K}, ep, g, ws, ws_bytes, stream);
 }
 
+// The forward from the stored codes: few tokens read the 2-bit codes once
+// (launch_ttq_fwd_skinny); otherwise the codes become wt at the start of the
+// workspace and the GEMM above runs on it. BITNET_NO_SKINNY (a test knob)
+// keeps the second route at any M.
+static bool ttq_codes_skinny(int64_t M, int64_t K) { return skinny(M) && K % 8 == 0; }
+static size_t ttq_wt_bytes(int64_t N, int64_t K) { return ((size_t)N * k_pad(K) * 2 + 255) / 256 * 256; }
+
+size_t ttq_codes_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  // none for the few-token route (a decode caller needs no 2*N*Kp buffer);
+  // the knob is read here too, so a size queried under it covers the GEMM
+  // route
+  if (ttq_codes_skinny(M, K)) return 0;
+  return ttq_wt_bytes(N, K) + gemm_workspace_bytes(GemmKind::kTtqFwd, M, N, K);
+}
+
+hipError_t launch_ttq_fwd_codes(const uint16_t* x, const uint8_t* w_packed, const float* params, int64_t M,
+                                int64_t N, int64_t K, uint16_t* y, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (ttq_codes_skinny(M, K)) return launch_ttq_fwd_skinny(x, w_packed, params, M, N, K, y, stream);
+  const size_t wb = ttq_wt_bytes(N, K);
+  if (ws == nullptr || ws_bytes < wb) return hipErrorInvalidValue;  // the C ABI sized it
+  uint16_t* wt = static_cast<uint16_t*>(ws);
+  if (hipError_t e = launch_ttq_expand(w_packed, N, K, params, wt, stream)) return e;
+  return launch_ttq_fwd(x, wt, M, N, K, y, static_cast<char*>(ws) + wb, ws_bytes - wb, stream);
+}
+
 // dX [M][K] = dY [M][N] . wt: wt staged as stored (rows n) and read
 // transposed (TrFrags), dY copied as stored.
 static hipError_t launch_ttq_dx(const uint16_t* dY, const uint16_t* wt, int64_t M, int64_t N, int64_t K,

@@ -83,6 +83,19 @@ hipError_t launch_ttq_init(const void* W, bool w_is_f32, int64_t N, int64_t K, f
 // Eq. 1: 2-bit codes [N][Kp/4] and bf16 values wt [N][Kp] in one pass.
 hipError_t launch_ttq_quantize(const void* W, bool w_is_f32, int64_t N, int64_t K, const float* params,
                                uint8_t* w_packed, uint16_t* wt, hipStream_t stream);
+// wt [N][Kp] from stored codes: the values ttq_quantize writes.
+hipError_t launch_ttq_expand(const uint8_t* w_packed, int64_t N, int64_t K, const float* params, uint16_t* wt,
+                             hipStream_t stream);
+// TTQ forward for few tokens (M <= kSkinnyMaxM, K % 8 == 0) straight from the
+// codes and params.
+hipError_t launch_ttq_fwd_skinny(const uint16_t* x, const uint8_t* w_packed, const float* params, int64_t M,
+                                 int64_t N, int64_t K, uint16_t* y, hipStream_t stream);
+// The TTQ forward from the stored state (codes + params): the few-token
+// kernel when it applies, else the codes expanded to wt at the start of the
+// workspace and the bf16 GEMM. Workspace: ttq_codes_workspace_bytes().
+size_t ttq_codes_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_ttq_fwd_codes(const uint16_t* x, const uint8_t* w_packed, const float* params, int64_t M,
+                                int64_t N, int64_t K, uint16_t* y, void* ws, size_t ws_bytes, hipStream_t stream);
 // y = x wt^T (bf16 x [M][K], no activation quantization).
 hipError_t launch_ttq_fwd(const uint16_t* x, const uint16_t* wt, int64_t M, int64_t N, int64_t K, uint16_t* y,
                           void* ws, size_t ws_bytes, hipStream_t stream);

@@ -521,6 +521,42 @@ __global__ __launch_bounds__(kPackThreads) void ttq_quantize_kernel(
   }
 }
 
+// The bf16 values of Eq. 1 from stored codes (the exported state): wt
+// [N][Kp] = bf16(Wp), -bf16(Wn) or 0 per code, as ttq_quantize writes them.
+__global__ __launch_bounds__(kPackThreads) void ttq_expand_kernel(const uint32_t* __restrict__ packed, int64_t N,
+                                                                   int64_t words_per_row,
+                                                                   const float* __restrict__ params,
+                                                                   uint16_t* __restrict__ wt) {
+  const uint32_t vp = f32_to_bf16_bits(params[1]);
+  const uint32_t vn = f32_to_bf16_bits(params[2]) ^ 0x8000u;
+  const int64_t total = N * words_per_row, Kp = 16 * words_per_row;
+  for (int64_t wi = (int64_t)blockIdx.x * kPackThreads + threadIdx.x; wi < total;
+       wi += (int64_t)gridDim.x * kPackThreads) {
+    const int64_t n = wi / words_per_row;
+    const int64_t k0 = (wi - n * words_per_row) * 16;
+    const uint32_t word = packed[wi];
+    uint32_t o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint32_t c = (word >> (8 * (j & 3) + 2 * (j >> 2))) & 3u;
+      o[j >> 1] |= (c == 1u ? vp : (c == 3u ? vn : 0u)) << (16 * (j & 1));
+    }
+    uint4* dst = reinterpret_cast<uint4*>(wt + n * Kp + k0);
+    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+  }
+}
+
+hipError_t launch_ttq_expand(const uint8_t* w_packed, int64_t N, int64_t K, const float* params, uint16_t* wt,
+                             hipStream_t stream) {
+  const int64_t wpr = k_pad(K) / 16;
+  const int64_t want = (N * wpr + kPackThreads - 1) / kPackThreads;
+  const int grid = (int)(want < 2048 ? want : 2048);
+  ttq_expand_kernel<<<grid, kPackThreads, 0, stream>>>(reinterpret_cast<const uint32_t*>(w_packed), N, wpr, params,
+                                                       wt);
+  return hipGetLastError();
+}
+
 hipError_t launch_ttq_quantize(const void* W, bool w_is_f32, int64_t N, int64_t K, const float* params,
                                uint8_t* w_packed, uint16_t* wt, hipStream_t stream) {
   const int64_t wpr = k_pad(K) / 16;

@@ -39,6 +39,7 @@ namespace bitnet {
 struct SkFwd {
   typedef i32x16_t Acc;
   typedef int Elem;
+  static constexpr int kCodeB = 32;  // code bytes per row per super-step
   static __device__ __forceinline__ Acc mma(uint32_t code_word, uint4 b, Acc acc) {
     i32x4_t a;
 #pragma unroll
@@ -53,6 +54,7 @@ struct SkFwd {
 struct SkDx {
   typedef f32x16_t Acc;
   typedef float Elem;
+  static constexpr int kCodeB = 32;
   static __device__ __forceinline__ Acc mma(uint32_t code_word, uint4 b, Acc acc) {
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
     // byte t of the word: two fp4 values -> two bf16 (scale 1: exact +-1, 0)
@@ -66,15 +68,48 @@ struct SkDx {
   }
 };
 
+// TTQ forward ("TTQ_VERIFICATION.md", Eq. 1): A = the same 2-bit codes
+// [N][Kp/4] (rows i = n), B = x [M][K] bf16, unquantized. 16 code bytes
+// (64 k) per row per super-step match the 128 bytes (64 k) of bf16 tokens.
+// Lane half h's 8 code bytes are two words of 16 codes (k = 32h .. 32h+31
+// of the super-step); step j takes codes 8j .. 8j+7, i.e. word j/2 shifted
+// by 4(j%2), whose bytes hold codes b and b+4 at bits 0 and 2 (code j of a
+// word at bit 8(j%4) + 2(j/4)). Each code becomes its bf16 value through a
+// byte permute of the table {0, bf16(Wp), 0, -bf16(Wn)} (2 bytes per entry,
+// entry c at bytes 2c, 2c+1): selector bytes 2c, 2c+1 are built from the
+// codes with one more permute.
+struct SkTtq {
+  typedef f32x16_t Acc;
+  typedef float Elem;
+  static constexpr int kCodeB = 16;
+  // two bf16 values (codes in bytes b0, b0+1 of d = 2 * codes) -> one dword
+  static __device__ __forceinline__ uint32_t pair(uint32_t d, uint32_t sel, uint32_t tlo, uint32_t thi) {
+    return perm(thi, tlo, perm(d + 0x01010101u, d, sel));
+  }
+  static __device__ __forceinline__ Acc mma(uint32_t w, uint4 b, Acc acc, uint32_t tlo, uint32_t thi) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const uint32_t d0 = (w & 0x03030303u) << 1;         // codes 0..3, doubled
+    const uint32_t d1 = ((w >> 2) & 0x03030303u) << 1;  // codes 4..7, doubled
+    // selector bytes [d.b0, d.b0 + 1, d.b1, d.b1 + 1] and [d.b2, .., d.b3 + 1]
+    const u32x4 a = {pair(d0, 0x05010400u, tlo, thi), pair(d0, 0x07030602u, tlo, thi),
+                     pair(d1, 0x05010400u, tlo, thi), pair(d1, 0x07030602u, tlo, thi)};
+    const u32x4 bx = {b.x, b.y, b.z, b.w};
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, bx),
+                                                   acc, 0, 0, 0);
+  }
+};
+
 // The code operand: `rows` rows of `pitch` bytes, the first `bytes` of
 // each in use; the token operand: M rows of `tpitch` bytes, the first
-// `tbytes` of each valid (both multiples of 16).
+// `tbytes` of each valid (both multiples of 16). tlo, thi: SkTtq's value
+// table (unused by the other policies).
 struct SkArgs {
   const uint8_t* codes;
   int64_t rows, pitch, bytes;
   const void* tok;
   int64_t tpitch, tbytes;
   int M;
+  uint32_t tlo, thi;
 };
 
 template <int MT>  // token tiles of 32: 1 for M <= 32, 2 for M <= 64
@@ -98,7 +133,8 @@ __device__ __forceinline__ void skinny_body(const SkArgs& a, char* smem, typenam
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int h = lane >> 5, r32 = lane & 31;
   const int64_t i0 = (int64_t)blockIdx.x * 32;
-  const int nchunks = (int)((a.bytes + 32 * W - 1) / (32 * W));
+  constexpr int kCB = SK::kCodeB;
+  const int nchunks = (int)((a.bytes + kCB * W - 1) / (kCB * W));
 
   const rsrc_t rc = make_rsrc(a.codes, (uint32_t)(a.rows * a.pitch));
   const uint32_t coff = i0 + r32 < a.rows ? (uint32_t)((i0 + r32) * a.pitch) : kOob;  // the lane's code row
@@ -112,8 +148,14 @@ __device__ __forceinline__ void skinny_body(const SkArgs& a, char* smem, typenam
       const int64_t x = (int64_t)c * kChunkB + col;
       b.x[p] = buf_load16(rx, row < a.M && x < a.tbytes ? (uint32_t)(row * a.tpitch + x) : kOob);
     }
-    const int64_t cb = (int64_t)c * (32 * W) + 32 * wave + 16 * h;
-    b.codes = buf_load16(rc, cb < a.bytes ? coff + (uint32_t)cb : kOob);
+    const int64_t cb = (int64_t)c * (kCB * W) + kCB * wave + (kCB / 2) * h;
+    const uint32_t off = cb < a.bytes ? coff + (uint32_t)cb : kOob;
+    if constexpr (kCB == 32) {
+      b.codes = buf_load16(rc, off);
+    } else {
+      const uint2 c8 = buf_load8(rc, off);
+      b.codes = make_uint4(c8.x, c8.y, 0u, 0u);
+    }
   };
   const auto stage = [&](const SkChunk<MT>& b) {
 #pragma unroll
@@ -134,8 +176,13 @@ __device__ __forceinline__ void skinny_body(const SkArgs& a, char* smem, typenam
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        acc[mt] = SK::mma(w4[j], *reinterpret_cast<const uint4*>(xr + 32 * mt * kPitch + 16 * j), acc[mt]);
+      for (int mt = 0; mt < MT; ++mt) {
+        const uint4 tok = *reinterpret_cast<const uint4*>(xr + 32 * mt * kPitch + 16 * j);
+        if constexpr (kCB == 32)
+          acc[mt] = SK::mma(w4[j], tok, acc[mt]);
+        else
+          acc[mt] = SK::mma(w4[j >> 1] >> (4 * (j & 1)), tok, acc[mt], a.tlo, a.thi);
+      }
   };
 
   SkChunk<MT> buf[P];
@@ -239,12 +286,52 @@ __global__ __launch_bounds__(kWave * W) void dx_skinny_kernel(SkArgs a, const fl
   }
 }
 
+// TTQ forward from the codes: code rows n, tokens m; y [M][N] bf16 = the fp32
+// sum rounded once.
+template <int MT, int W, int P>
+__global__ __launch_bounds__(kWave * W) void ttq_fwd_skinny_kernel(SkArgs a, const float* __restrict__ params,
+                                                                   int64_t N, uint16_t* __restrict__ y) {
+  __shared__ __attribute__((aligned(16))) char smem[skinny_lds<MT, W>()];
+  a.tlo = (uint32_t)f32_to_bf16_bits(params[1]) << 16;               // codes 0, 1: 0, bf16(Wp)
+  a.thi = (uint32_t)(f32_to_bf16_bits(params[2]) ^ 0x8000u) << 16;   // codes 2, 3: 0, -bf16(Wn)
+  float v[4];
+  int mt, g;
+  skinny_body<SkTtq, MT, W, P>(a, smem, v, mt, g);
+  const int lane = threadIdx.x % kWave, h = lane >> 5;
+  const int64_t m = 32 * mt + (lane & 31);
+  if (mt >= MT || m >= a.M) return;
+  const int64_t nb = (int64_t)blockIdx.x * 32 + 8 * g + 4 * h;
+  uint16_t* yr = y + m * N;
+  if (N % 4 == 0 && nb + 4 <= N) {
+    *reinterpret_cast<uint2*>(yr + nb) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (nb + e >= N) break;
+      yr[nb + e] = f32_to_bf16_bits(v[e]);
+    }
+  }
+}
+
+hipError_t launch_ttq_fwd_skinny(const uint16_t* x, const uint8_t* w_packed, const float* params, int64_t M,
+                                 int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
+  if (M < 1 || M > kSkinnyMaxM || K % 8 != 0) return hipErrorInvalidValue;
+  const int64_t Kp = k_pad(K);
+  const SkArgs a{w_packed, N, Kp / 4, Kp / 4, x, 2 * K, 2 * K, (int)M, 0u, 0u};
+  const unsigned grid = (unsigned)((N + 31) / 32);
+  if (M <= 32)
+    ttq_fwd_skinny_kernel<1, 16, 3><<<grid, kWave * 16, 0, stream>>>(a, params, N, y);
+  else
+    ttq_fwd_skinny_kernel<2, 8, 3><<<grid, kWave * 8, 0, stream>>>(a, params, N, y);
+  return hipGetLastError();
+}
+
 hipError_t launch_fwd_skinny(const int8_t* x_q, const float* s_x, const uint8_t* w_packed, const float* gamma,
                              const uint16_t* bias, int64_t M, int64_t N, int64_t K, uint16_t* y, int32_t* acc_out,
                              hipStream_t stream) {
   if (M < 1 || M > kSkinnyMaxM) return hipErrorInvalidValue;
   const int64_t Kp = k_pad(K);
-  const SkArgs a{w_packed, N, Kp / 4, Kp / 4, x_q, Kp, Kp, (int)M};
+  const SkArgs a{w_packed, N, Kp / 4, Kp / 4, x_q, Kp, Kp, (int)M, 0u, 0u};
   const unsigned grid = (unsigned)((N + 31) / 32);
   if (M <= 32)
     fwd_skinny_kernel<1, 16, 3><<<grid, kWave * 16, 0, stream>>>(a, s_x, gamma, bias, N, y, acc_out);
@@ -257,7 +344,7 @@ hipError_t launch_dx_skinny(const uint8_t* wt, const uint16_t* dY, const float* 
                             int64_t K, uint16_t* dX, hipStream_t stream) {
   if (M < 1 || M > kSkinnyMaxM || N % 8 != 0) return hipErrorInvalidValue;
   const int64_t Kp = k_pad(K), Np = (N + 63) / 64 * 64;
-  const SkArgs a{wt, Kp, Np / 2, Np / 2, dY, 2 * N, 2 * N, (int)M};
+  const SkArgs a{wt, Kp, Np / 2, Np / 2, dY, 2 * N, 2 * N, (int)M, 0u, 0u};
   const unsigned grid = (unsigned)(Kp / 32);
   if (M <= 32)
     dx_skinny_kernel<1, 16, 3><<<grid, kWave * 16, 0, stream>>>(a, gamma, K, dX);

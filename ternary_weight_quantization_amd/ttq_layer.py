@@ -47,6 +47,18 @@ def ttq_quantize(weight, params):
     return w_packed, wt
 
 
+def ttq_forward_codes(x, w_packed, params):
+    """Inference forward from the exported state (``TTQLinear.export_inference``):
+    x [..., K] bf16, codes [N, Kp/4], params (delta, Wp, Wn) -> y [..., N]
+    bf16. Few tokens read only the 2-bit codes."""
+    K = x.shape[-1]
+    lead = x.shape[:-1]
+    x2 = x.reshape(-1, K).contiguous()
+    y = torch.empty((x2.shape[0], w_packed.shape[0]), dtype=torch.bfloat16, device=x.device)
+    B.ttq_fwd_codes(x2, w_packed, params.contiguous(), y)
+    return y.reshape(*lead, w_packed.shape[0])
+
+
 def _workspace(nbytes, device):
     return None if nbytes == 0 else torch.empty((nbytes,), dtype=torch.uint8, device=device)
 

@@ -48,6 +48,9 @@ def L():
     lib.ttq_quantize.argtypes = [vp, st, i64, i64, vp, vp, vp, vp]
     lib.ttq_fwd.argtypes = [vp, vp, i64, i64, i64, vp, vp, sz, vp]
     lib.ttq_bwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp, st, vp, vp, sz, vp]
+    lib.ttq_fwd_codes_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.ttq_fwd_codes_workspace_bytes.restype = sz
+    lib.ttq_fwd_codes.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, sz, vp]
     return lib
 
 
@@ -55,7 +58,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("bitnet_ternarize_pack", "bitnet_act_quant", "bitlinear_fwd", "bitlinear_bwd",
               "bitlinear_fwd_bias", "bitlinear_bias_grad", "ttq_workspace_bytes", "ttq_init", "ttq_quantize",
-              "ttq_fwd", "ttq_bwd"):
+              "ttq_fwd", "ttq_bwd", "ttq_fwd_codes", "ttq_fwd_codes_workspace_bytes"):
         assert n in names
 
 
@@ -225,3 +228,23 @@ def test_ttq_inverse_softplus_round_trip():
     assert torch.allclose(torch.nn.functional.softplus(r), v, rtol=1e-12, atol=0)
     r32 = r.float()
     assert torch.allclose(torch.nn.functional.softplus(r32).double(), v, rtol=1e-5, atol=0)
+
+
+def test_ttq_fwd_codes_size_and_validation(L):
+    # few tokens with K % 8 == 0 read the codes directly: no workspace
+    assert L.ttq_fwd_codes_workspace_bytes(32, 2560, 6912) == 0
+    assert L.ttq_fwd_codes_workspace_bytes(64, 128, 256) == 0
+    # otherwise the expanded bf16 weight [N][Kp] (+ the GEMM's split share,
+    # none here: whole tiles)
+    assert L.ttq_fwd_codes_workspace_bytes(4096, 6912, 2560) == 6912 * 2560 * 2
+    assert L.ttq_fwd_codes_workspace_bytes(32, 100, 7) == (100 * 64 * 2 + 255) // 256 * 256
+    assert L.ttq_fwd_codes_workspace_bytes(0, 4, 4) == 0
+    assert L.ttq_fwd_codes(None, A, A, 4, 4, 8, A, None, 0, None) == ENULL
+    assert L.ttq_fwd_codes(A, A, None, 4, 4, 8, A, None, 0, None) == ENULL
+    assert L.ttq_fwd_codes(A, A, A, 4, 0, 8, A, None, 0, None) == ESHAPE
+    assert L.ttq_fwd_codes(A, A, A, 4, 4, 8, MISALIGNED, None, 0, None) == EALIGN
+    assert L.ttq_fwd_codes(A, A, A + 2, 4, 4, 8, A, None, 0, None) == EALIGN
+    need = L.ttq_fwd_codes_workspace_bytes(300, 200, 512)
+    assert need > 0
+    assert L.ttq_fwd_codes(A, A, A, 300, 200, 512, A, None, need, None) == EWS
+    assert L.ttq_fwd_codes(A, A, A, 300, 200, 512, A, A, need - 1, None) == EWS

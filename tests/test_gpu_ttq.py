@@ -301,3 +301,95 @@ def test_ttq_graph_replays_match_eager(M, K, N, split, monkeypatch):
         torch.cuda.synchronize()
         for k in ("y", "dX", "dW", "grads"):
             assert torch.equal(t[k], ref[k]), ("eager", r, k)
+
+
+def _codes_case(M, K, N, seed, params=None):
+    """Inputs, codes and params on the GPU for a ttq_fwd_codes case."""
+    from ternary_weight_quantization_amd import binding as B
+    from tests.gpu_util import dev_bf16, dev_weight
+    inp = WL.custom_inputs(M, K, N, seed=seed)
+    dev = torch.device("cuda")
+    Kp = B.bitnet_k_pad(K)
+    W = dev_weight(inp["W"])
+    if params is None:
+        p = torch.empty((3,), dtype=torch.float32, device=dev)
+        B.ttq_init(W, p, torch.empty((B.bitnet_ternarize_workspace_bytes(N, K),), dtype=torch.uint8, device=dev))
+    else:
+        p = torch.tensor(np.asarray(params, dtype=np.float32), device=dev)
+    codes = torch.empty((N, Kp // 4), dtype=torch.uint8, device=dev)
+    wt = torch.empty((N, Kp), dtype=torch.bfloat16, device=dev)
+    B.ttq_quantize(W, p, codes, wt)
+    return inp, dev_bf16(inp["x"]), codes, wt, p
+
+
+@pytest.mark.parametrize("M,K,N", [
+    (1, 64, 32), (5, 512, 200), (32, 2560, 6912), (33, 640, 96), (64, 6912, 2560), (17, 1000, 77),
+])
+def test_ttq_fwd_codes_few_tokens(M, K, N):
+    """ttq_fwd_codes at M <= 64 (the few-token kernel reading the 2-bit codes
+    once; K % 8 == 0, K = 1000 with a partial last chunk) against the
+    oracle's forward on the values of the same codes; asymmetric
+    parameters."""
+    from ternary_weight_quantization_amd import binding as B
+    note(f"ttq_fwd_codes few tokens M={M} K={K} N={N}")
+    inp0 = WL.custom_inputs(M, K, N, seed=M + K)
+    e = float(np.mean(np.abs(w_values(inp0["W"]))))
+    params = (np.float32(0.6 * e), np.float32(1.3 * e), np.float32(0.7 * e))
+    inp, x, codes, wt, p = _codes_case(M, K, N, seed=M + K, params=params)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    B.ttq_fwd_codes(x, codes, p, y)
+    torch.cuda.synchronize()
+    w = w_values(inp["W"])
+    q = O.ttq_codes(w, params[0])
+    assert np.array_equal(codes.cpu().numpy(), O.pack_codes(q))
+    ref = O.ttq_forward(bf(inp["x"]), O.ttq_values(q, params[1], params[2]))
+    from tests.gpu_util import host_bf16_bits
+    m = C.check(bf(host_bf16_bits(y)), ref, "y_ttq")
+    print(f"[ttq codes] M={M} K={K} N={N}: max_rel {m['max_rel']:.2e} norm {m['normwise']:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("M,K,N,knob", [
+    (300, 512, 200, None),    # the GEMM route: codes expanded, then the bf16 GEMM
+    (48, 1001, 130, None),    # K % 8 != 0: the GEMM route at few tokens
+    (40, 512, 264, "1"),      # BITNET_NO_SKINNY forces the GEMM route
+])
+def test_ttq_fwd_codes_gemm_route_matches_ttq_fwd(M, K, N, knob, monkeypatch):
+    """Through the expanded weight, ttq_fwd_codes gives ttq_fwd's bits on
+    ttq_quantize's wt (the same GEMM on the same values)."""
+    if knob is not None:
+        monkeypatch.setenv("BITNET_NO_SKINNY", knob)
+    from ternary_weight_quantization_amd import binding as B
+    from tests.gpu_util import host_bf16_bits
+    note(f"ttq_fwd_codes GEMM route M={M} K={K} N={N} knob={knob}")
+    inp, x, codes, wt, p = _codes_case(M, K, N, seed=7 * M + N)
+    assert B.ttq_fwd_codes_workspace_bytes(M, N, K) > 0
+    y1 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    y2 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    B.ttq_fwd_codes(x, codes, p, y1)
+    B.ttq_fwd(x, wt, y2)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    w = w_values(inp["W"])
+    delta, wp, wn = (np.float32(v) for v in p.cpu().numpy())
+    q = O.ttq_codes(w, delta)
+    C.check(bf(host_bf16_bits(y1)), O.ttq_forward(bf(inp["x"]), O.ttq_values(q, wp, wn)), "y_ttq")
+
+
+def test_ttq_export_and_forward_codes():
+    """TTQLinear.export_inference + ttq_forward_codes (the inference route
+    from the 2-bit state) against the module's own forward, for a decode
+    batch (few-token kernel) and a prefill batch (GEMM route)."""
+    from ternary_weight_quantization_amd.ttq_layer import TTQLinear, ttq_forward_codes
+    torch.manual_seed(1)
+    layer = TTQLinear(512, 384)
+    codes, params = layer.export_inference()
+    note("ttq export + forward from codes")
+    for M in (8, 200):
+        x = torch.randn(M, 512, device="cuda").to(torch.bfloat16)
+        with torch.no_grad():
+            y_ref = layer(x)
+        y = ttq_forward_codes(x, codes, params)
+        torch.cuda.synchronize()
+        C.check(y.float().cpu().numpy(), y_ref.float().cpu().numpy().astype(np.float64), "y_ttq")
+        if M == 200:  # the same GEMM on the same values
+            assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16))
