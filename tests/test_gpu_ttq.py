@@ -176,13 +176,14 @@ def test_ttq_paired_backward(monkeypatch, knob):
     check_ttq(inp, run_ttq(inp))
 
 
-def test_ttq_full_size_sampled():
-    """The 4096 x 2560 -> 6912 layer in the launch configuration the
-    benchmark times: bit-exact parameters, codes and values; y, dX, dW on
-    sampled elements; the scale gradients against the masked sums of the
-    GPU's own f32 dW (a property at any size), and that f32 dW sampled
-    against the oracle."""
-    inp = WL.layer_inputs("c2_up_4096x2560x6912", seed=0)
+@pytest.mark.parametrize("name", ["c2_up_4096x2560x6912", "c3_down_4096x6912x2560"])
+def test_ttq_full_size_sampled(name):
+    """The 4096 x 2560 -> 6912 layer (in the launch configuration the
+    benchmark times) and the 4096 x 6912 -> 2560 one: bit-exact parameters,
+    codes and values; y, dX, dW on sampled elements; the scale gradients
+    against the masked sums of the GPU's own f32 dW (a property at any
+    size), and that f32 dW sampled against the oracle."""
+    inp = WL.layer_inputs(name, seed=0)
     M, K, N = inp["M"], inp["K"], inp["N"]
     note(f"ttq full size M={M} K={K} N={N}")
     g = run_ttq(inp, dw_f32=True)
