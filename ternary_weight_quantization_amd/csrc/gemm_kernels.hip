@@ -1698,30 +1698,38 @@ static uint64_t next_gen() {
 }
 
 // Cost model of one product on G workgroups, in dX stage times (measured
-// at 4096x2560->6912): a dW stage costs about 1.07 of a dX stage, a tile's
-// pipeline fill and epilogue about 5.4 stages, and each piece of a split
-// range about 10 stages (fill, partial exchange, epilogue). Whole tiles
-// taken in turn cost ceil(T/G) tiles; a split costs W/G stages plus its
-// pieces (about W/(G*S) + 1 per workgroup).
-constexpr double kTileCost = 5.4, kPieceCost = 10.0;
+// at 4096x2560->6912): a tile's pipeline fill and epilogue cost about 5.4
+// stages. Per product, the cost of a stage and of each piece of a split
+// range (fill, partial exchange, epilogue): dX 1.0 and 10 stages; dW 1.07
+// and 21 (dW's pieces exchange more: measured at 4096x2560->6912 and
+// 4096x6912->2560, a pair launch whose dW splits over 128 CUs takes
+// 325-370 us where dW in whole tiles on 136 CUs takes 260-340 us, which 10
+// stages per piece did not predict). Whole tiles taken in turn cost
+// ceil(T/G) tiles; a split costs W/G stages plus its pieces (about
+// W/(G*S) + 1 per workgroup).
+constexpr double kTileCost = 5.4;
+struct ProductCosts {
+  double stage, piece;
+};
+constexpr ProductCosts kDxCosts{1.0, 10.0}, kDwCosts{1.07, 21.0};
 struct PairCost {
   double t;
   bool split;
 };
-static PairCost product_cost(const GemmShape& g, int64_t G, double stage) {
+static PairCost product_cost(const GemmShape& g, int64_t G, const ProductCosts& c) {
   const double T = (double)g.tiles(), S = (double)g.nstages, W = T * S;
-  const double whole = std::ceil(T / (double)G) * (S * stage + kTileCost);
+  const double whole = std::ceil(T / (double)G) * (S * c.stage + kTileCost);
   const int64_t Gs = G < 4 * g.tiles() ? G : 4 * g.tiles();
-  const double split = W / (double)Gs * stage + (W / ((double)Gs * S) + 1.0) * kPieceCost;
+  const double split = W / (double)Gs * c.stage + (W / ((double)Gs * S) + 1.0) * c.piece;
   return split < whole ? PairCost{split, true} : PairCost{whole, false};
 }
-constexpr double kDwStageCost = 1.07;
 
 // The 8-workgroup columns (of kt) that run dX in a pair launch: the k1 that
 // minimizes the slower product's modelled cost; 0: no pair launch (the
 // split knob is set, or too few CUs). BITNET_PAIR_COLS=<k1> overrides
 // (tuning knob).
-static int pair_columns(const GemmShape& g1, const GemmShape& g2, int cus, int* kt, double c1, double c2) {
+static int pair_columns(const GemmShape& g1, const GemmShape& g2, int cus, int* kt, const ProductCosts& c1,
+                        const ProductCosts& c2) {
   if (getenv("BITNET_SPLIT_CTAS")) return 0;
   *kt = (cus < kMaxGrid ? cus : kMaxGrid) / 8;
   if (*kt < 2) return 0;
@@ -1899,8 +1907,9 @@ static size_t pair_split_bound(const GemmShape& g1, const GemmShape& g2) {
   return split_control_bytes(g1, kMaxGrid) + split_control_bytes(g2, kMaxGrid) + 2 * (size_t)kMaxGrid * kPartialBytes;
 }
 template <int MAP1, int MAP2, class PL1, class QL1, class EP1, class PL2, class QL2, class EP2>
-static hipError_t run_pair(const PL1& p1, const QL1& q1, const EP1& e1, const GemmShape& g1, double c1,
-                           const PL2& p2, const QL2& q2, const EP2& e2, const GemmShape& g2, double c2, char* ws,
+static hipError_t run_pair(const PL1& p1, const QL1& q1, const EP1& e1, const GemmShape& g1,
+                           const ProductCosts& c1, const PL2& p2, const QL2& q2, const EP2& e2, const GemmShape& g2,
+                           const ProductCosts& c2, char* ws,
                            size_t ws_bytes, hipStream_t stream) {
   int kt = 0;
   const int k1 = pair_columns(g1, g2, device_cus(), &kt, c1, c2);
@@ -1932,7 +1941,7 @@ hipError_t launch_bwd_pair(const uint16_t* dY, const uint8_t* w_packed, const fl
   const size_t wb = wt_bytes(N, K), xb = xhat_bytes(M, K);
   if (ws_bytes < wb + xb) return hipErrorNotSupported;
   int kt = 0;
-  if (pair_columns(g1, g2, device_cus(), &kt, 1.0, kDwStageCost) == 0) return hipErrorNotSupported;
+  if (pair_columns(g1, g2, device_cus(), &kt, kDxCosts, kDwCosts) == 0) return hipErrorNotSupported;
   char* base = static_cast<char*>(ws);
   uint8_t* wt = reinterpret_cast<uint8_t*>(base);
   uint16_t* xhat = reinterpret_cast<uint16_t*>(base + wb);
@@ -1955,15 +1964,15 @@ hipError_t launch_bwd_pair(const uint16_t* dY, const uint8_t* w_packed, const fl
   hipError_t e;
   switch (dw_out) {
     case DwOut::kF32:
-      e = run_pair<1, 0>(p1, q1, e1, g1, 1.0, p2, q2, Bf16Epilogue<true>{dW, nullptr, K, N}, g2, kDwStageCost, sws,
+      e = run_pair<1, 0>(p1, q1, e1, g1, kDxCosts, p2, q2, Bf16Epilogue<true>{dW, nullptr, K, N}, g2, kDwCosts, sws,
                          sbytes, stream);
       break;
     case DwOut::kSign1:
-      e = run_pair<1, 0>(p1, q1, e1, g1, 1.0, p2, q2, Sign1Epilogue{static_cast<uint8_t*>(dW), Kp, N}, g2,
-                         kDwStageCost, sws, sbytes, stream);
+      e = run_pair<1, 0>(p1, q1, e1, g1, kDxCosts, p2, q2, Sign1Epilogue{static_cast<uint8_t*>(dW), Kp, N}, g2,
+                         kDwCosts, sws, sbytes, stream);
       break;
     default:
-      e = run_pair<1, 0>(p1, q1, e1, g1, 1.0, p2, q2, Bf16Epilogue<false>{dW, nullptr, K, N}, g2, kDwStageCost, sws,
+      e = run_pair<1, 0>(p1, q1, e1, g1, kDxCosts, p2, q2, Bf16Epilogue<false>{dW, nullptr, K, N}, g2, kDwCosts, sws,
                          sbytes, stream);
       break;
   }
@@ -2067,7 +2076,7 @@ static hipError_t launch_ttq_pair(const uint16_t* dY, const uint16_t* x, const u
   // this dX (bf16 weight) takes 158-166 us and dW 176-189 us, about the
   // BitNet products' ratio; 15 of 32 columns for dX then give 260 us, 16
   // give 325 us (equal costs chose 16)
-  return run_pair<0, 0>(p1, q1, e1, g1, 1.0, p2, q2, e2, g2, kDwStageCost, ws, ws_bytes, stream);
+  return run_pair<0, 0>(p1, q1, e1, g1, kDxCosts, p2, q2, e2, g2, kDwCosts, ws, ws_bytes, stream);
 }
 
 hipError_t launch_ttq_bwd(const uint16_t* dY, const uint16_t* x, const uint16_t* wt, const uint8_t* w_packed,
