@@ -1,0 +1,40 @@
+"""Seeded random shapes through the whole BitNet layer and the TTQ layer on
+the GPU, each checked against the oracle in full: shapes no fixed case picks
+(few or many tokens, K and N ragged or multiples of 8, f32 or bf16 masters),
+and so the split, pair and few-token choices they lead to."""
+
+import numpy as np
+import pytest
+import torch
+
+from ternary_weight_quantization_amd import workloads as WL
+from tests.gpu_util import note, run_layer, run_ttq
+from tests.test_gpu_parity import check_layer
+from tests.test_gpu_ttq import check_ttq
+
+pytestmark = pytest.mark.gpu
+
+
+def _shapes(seed, n):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        M = int(rng.choice([int(rng.integers(1, 65)), int(rng.integers(65, 1600))]))
+        K = int(rng.choice([int(rng.integers(1, 200)), int(rng.integers(200, 3000)), 8 * int(rng.integers(8, 400))]))
+        N = int(rng.choice([int(rng.integers(1, 200)), int(rng.integers(200, 3000)), 8 * int(rng.integers(8, 400))]))
+        out.append((M, K, N, "f32" if rng.random() < 0.3 else "bf16"))
+    return out
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+
+
+@pytest.mark.parametrize("i,M,K,N,wd", [(i, *s) for i, s in enumerate(_shapes(4242, 16))])
+def test_random_shape(i, M, K, N, wd):
+    note(f"random shape {i}: M={M} K={K} N={N} W={wd}")
+    inp = WL.custom_inputs(M, K, N, seed=5000 + i, w_dtype=wd)
+    check_layer(inp, run_layer(inp), full=True)
+    check_ttq(inp, run_ttq(inp, dw_f32=(wd == "f32")))
