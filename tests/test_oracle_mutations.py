@@ -243,3 +243,125 @@ def test_planted_ttq_mistake_is_caught(monkeypatch, name, fn, pins):
         except (AssertionError, ValueError):
             caught.append(pin)
     assert caught, f"mutation {fn.__name__} of {name} passed every pin in {pins}"
+
+
+# ---------------------------------------------------------------------------
+# the parity gate (oracle/compare.py) and the sampled TTQ references
+# ---------------------------------------------------------------------------
+
+import oracle.compare as CMP  # noqa: E402
+from tests import test_compare_pins as CP  # noqa: E402
+
+_check_ref = CMP.check
+_rel_errors_ref = CMP.rel_errors
+
+
+def _check_always_floors(got, ref, what):
+    m = _rel_errors_ref(got, ref, 2.0 ** -8)
+    assert m["max_rel"] <= CMP.MAX_REL, (what, m)
+    assert m["normwise"] <= CMP.NORMWISE, (what, m)
+    return m
+
+
+def _check_no_normwise(got, ref, what):
+    m = _rel_errors_ref(got, ref, 0.0 if what == "y" else 2.0 ** -8)
+    assert m["max_rel"] <= CMP.MAX_REL, (what, m)
+    return m
+
+
+def _check_mean_rel(got, ref, what):
+    # the mean instead of the maximum of the element errors
+    m = dict(_rel_errors_ref(got, ref, 0.0 if what == "y" else 2.0 ** -8))
+    g = np.asarray(got, np.float64)
+    o = np.asarray(ref, np.float64)
+    m["max_rel"] = float(np.mean(np.abs(g - o) / np.maximum(np.abs(o), 1e-300)))
+    assert m["max_rel"] <= CMP.MAX_REL, (what, m)
+    assert m["normwise"] <= CMP.NORMWISE, (what, m)
+    return m
+
+
+def _rel_errors_zero_over_zero(got, ref, floor_frac):
+    # 0/0 taken as an error instead of an exact match
+    m = dict(_rel_errors_ref(got, ref, floor_frac))
+    g = np.asarray(got, np.float64)
+    o = np.asarray(ref, np.float64)
+    if np.any((g == o) & (o == 0)) and floor_frac == 0:
+        m["max_rel"] = float("inf")
+    return m
+
+
+def _rel_errors_nan_ignored(got, ref, floor_frac):
+    g = np.asarray(got, np.float64)
+    o = np.asarray(ref, np.float64)
+    ok = np.isfinite(g)
+    return _rel_errors_ref(g[ok], o[ok], floor_frac)
+
+
+def _near_w_off_by_gamma(w, gamma):
+    # the boundary taken at gamma instead of gamma / 2
+    h = np.float32(gamma)
+    a = np.abs(np.asarray(w, dtype=np.float64))
+    return int(np.sum(np.abs(a - np.float64(h)) <= np.float64(np.spacing(h))))
+
+
+def _near_a_integers(x, s):
+    # integers instead of half-integers
+    t = 127.0 * np.asarray(x, np.float64) / np.asarray(s, np.float64)[:, None]
+    ulp = np.spacing(np.abs(t).astype(np.float32)).astype(np.float64)
+    return int(np.sum(np.abs(t - np.rint(t)) <= ulp))
+
+
+def _ttq_dx_elements_transposed(dY, wt, rows, cols):
+    dY = np.asarray(dY, dtype=np.float64)
+    wt = np.asarray(wt, dtype=np.float64)
+    return np.array([float(np.dot(dY[m], wt[k])) for m, k in zip(rows, cols)])
+
+
+def _ttq_dw_elements_swapped(dY, x, rows, cols):
+    dY = np.asarray(dY, dtype=np.float64)
+    x = np.asarray(x, dtype=np.float64)
+    return np.array([float(np.dot(dY[:, k], x[:, n])) for n, k in zip(rows, cols)])
+
+
+def _ttq_y_elements_transposed(x, wt, rows, cols):
+    x = np.asarray(x, dtype=np.float64)
+    wt = np.asarray(wt, dtype=np.float64)
+    return np.array([float(np.dot(x[m], wt[:, n])) for m, n in zip(rows, cols)])
+
+
+_SQ = dict(M=6, N=6, K=6)
+GATE_MUTATIONS = [
+    (CMP, "check", _check_always_floors, [("test_y_has_no_floor", {}), ("test_floored_kinds_use_the_floor", {})]),
+    (CMP, "check", _check_no_normwise, [("test_uniform_normwise_offset_fails", {})]),
+    (CMP, "check", _check_mean_rel, [("test_one_element_off_by_one_percent_fails", {})]),
+    (CMP, "rel_errors", _rel_errors_zero_over_zero, [("test_exact_match_and_zeros_pass", {})]),
+    (CMP, "rel_errors", _rel_errors_nan_ignored, [("test_nan_and_inf_fail", {})]),
+    (CMP, "near_boundary_weights", _near_w_off_by_gamma, [("test_near_boundary_weights_hand_count", {})]),
+    (CMP, "near_boundary_acts", _near_a_integers, [("test_near_boundary_acts_hand_count", {}),
+                                                   ("test_near_boundary_acts_zero_is_not_a_boundary", {})]),
+    (T, "ttq_dx_elements", _ttq_dx_elements_transposed, [("test_ttq_element_helpers_match_full_functions", _SQ),
+                                                        ("test_ttq_element_helpers_hand_values", {})]),
+    (T, "ttq_dw_elements", _ttq_dw_elements_swapped, [("test_ttq_element_helpers_match_full_functions", _SQ),
+                                                     ("test_ttq_element_helpers_hand_values", {})]),
+    (T, "ttq_y_elements", _ttq_y_elements_transposed, [("test_ttq_element_helpers_match_full_functions", _SQ),
+                                                      ("test_ttq_element_helpers_hand_values", {})]),
+]
+
+
+@pytest.mark.parametrize("mod,name,fn,pins", GATE_MUTATIONS, ids=[f"{m[1]}:{m[2].__name__}" for m in GATE_MUTATIONS])
+def test_planted_gate_mistake_is_caught(monkeypatch, mod, name, fn, pins):
+    monkeypatch.setattr(mod, name, fn)
+    if hasattr(O, name):
+        monkeypatch.setattr(O, name, fn)
+    caught = []
+    for pin, kw in pins:
+        try:
+            getattr(CP, pin)(**kw)
+        except (AssertionError, ValueError, IndexError):
+            caught.append(pin)
+        except BaseException as e:  # pytest.raises(...) not raised is a Failed, not an AssertionError
+            if type(e).__name__ == "Failed":
+                caught.append(pin)
+            else:
+                raise
+    assert caught, f"mutation {fn.__name__} of {name} passed every pin in {[p for p, _ in pins]}"

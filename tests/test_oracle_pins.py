@@ -470,41 +470,51 @@ def _golden_signs():
     return out
 
 
+def _fake_quant(torch, v, scale, lo, hi):
+    """v on the integer grid of `scale`: round half to even, clip to
+    [lo, hi], divide back (the quantizers of "1BitTraining.md", opening
+    helpers, stated as formulas: activations scale each row so its absmax
+    maps to 127, weights scale by the reciprocal mean of |W|, each scale
+    floored at 1e-5; activations clip to [-128, 127], weights to [-1, 1])."""
+    return torch.clamp(torch.round(v * scale), lo, hi) / scale
+
+
 def test_tiny_net_page_result_reproduces():
-    """The page's own net (its 1e-5 floors, clip to [-128, 127], float64),
-    with gradients taken by torch autograd rather than by hand: the STE
-    gradient of each latent weight has the sign of the gradient of the
-    quantised weight, element by element, as printed on the page."""
+    """The page's own net ("1BitTraining.md", Multilayer check: 7 -> 6 -> 5 ->
+    4, batch 2, float64, every hidden output fake-quantized, the last not,
+    squared-error loss against a random target), with the gradients taken by
+    torch autograd rather than by hand: the STE gradient of each latent
+    weight has the sign of the gradient of the quantised weight, element by
+    element, as printed on the page."""
     torch = pytest.importorskip("torch")
     d = WL.tiny_net_inputs()
+    floor, act_range, w_range = 1e-5, (-128, 127), (-1, 1)
 
-    def aq(x):
-        sc = 127.0 / torch.clamp(x.abs().amax(dim=-1, keepdim=True), min=1e-5)
-        return torch.clamp(torch.round(x * sc), -128, 127) / sc
+    def act_fq(v):
+        return _fake_quant(torch, v, 127.0 / torch.clamp(v.abs().amax(dim=-1, keepdim=True), min=floor), *act_range)
 
-    def wq(w):
-        sc = 1.0 / torch.clamp(w.abs().mean(), min=1e-5)
-        return torch.clamp(torch.round(w * sc), -1, 1) / sc
+    def weight_fq(w):
+        return _fake_quant(torch, w, 1.0 / torch.clamp(w.abs().mean(), min=floor), *w_range)
 
-    Wf = [torch.tensor(w, requires_grad=True) for w in d["Ws"]]
-    Qs = [wq(w.detach()).clone().requires_grad_(True) for w in Wf]
-    x0 = torch.tensor(d["x0"])
-    t = torch.tensor(d["target"])
+    def through(v, fq):  # identity straight-through estimator: value fq, gradient of v
+        return v + (fq - v).detach()
 
-    def net(ws):
-        a = aq(x0)
-        for i, w in enumerate(ws):
-            h = a @ w.T
-            a = h + (aq(h) - h).detach() if i < 2 else h
-        return 0.5 * torch.sum((a - t) ** 2)
+    def loss_of(weights):
+        act = act_fq(torch.tensor(d["x0"]))
+        for depth, w in enumerate(weights):
+            pre = act @ w.T
+            act = pre if depth == len(weights) - 1 else through(pre, act_fq(pre))
+        return 0.5 * ((act - torch.tensor(d["target"])) ** 2).sum()
 
-    net(Qs).backward()
-    net([w + (wq(w) - w).detach() for w in Wf]).backward()
+    latent = [torch.tensor(w, requires_grad=True) for w in d["Ws"]]
+    quantised = [weight_fq(w.detach()).clone().requires_grad_(True) for w in latent]
+    loss_of(quantised).backward()
+    loss_of([through(w, weight_fq(w)) for w in latent]).backward()
     golden = _golden_signs()
-    for i in range(3):
-        same = bool(torch.all(torch.sign(Wf[i].grad) == torch.sign(Qs[i].grad)))
+    for i, (w, q) in enumerate(zip(latent, quantised)):
+        same = bool(torch.all(torch.sign(w.grad) == torch.sign(q.grad)))
         assert same == golden[f"layer{i + 1}"]
-        assert float(Qs[i].grad.abs().min()) > 0.1
+        assert float(q.grad.abs().min()) > 0.1
 
 
 def test_tiny_net_oracle_ste_signs():
