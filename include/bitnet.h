@@ -76,18 +76,21 @@ size_t bitnet_ternarize_workspace_bytes(int64_t N, int64_t K);
 
 /* Bytes of workspace bitlinear_fwd / bitlinear_bwd need for these sizes
  * (0 for sizes the call rejects). 0 means the call takes no workspace (the
- * pointer may then be NULL). The GEMMs need workspace when they split
- * output tiles over several workgroups so that all CUs stay busy: 16 bytes
- * of tagged counters per 256 x 256 output tile and 256 KiB of partial sums
- * per workgroup piece, at most about 128 MiB. The contents need no
+ * pointer may then be NULL). The size is that of the plan the call runs on
+ * the current device: a GEMM needs workspace when it splits output tiles
+ * over several workgroups so that all CUs stay busy (16 bytes of tagged
+ * counters per 256 x 256 output tile and 256 KiB per partial tile, at most
+ * min(2G, G + T - 1) of them for G workgroups and T tiles); few tokens
+ * (M <= 64) need none for the forward. The contents need no
  * initialization, and the calls leave the counters cleared, so a call
  * captured into a HIP graph may be replayed any number of times; a
  * workspace must not be shared by calls that may run at the same time
- * (calls on one stream may share it). bitlinear_bwd's size
- * covers both of its products, which run one after the other. Each product
- * first builds a transient operand at the start of the workspace: dX the
- * ternary codes transposed to fp4 [Kp][Np/2] (Kp*Np/2 bytes, Np = N rounded
- * up to 64), dW a bf16 x_hat = bf16(x_q * s/127) [M][Kp] (2*M*Kp bytes). */
+ * (calls on one stream may share it). bitlinear_bwd's size is that of its
+ * call with both outputs; a call with one output uses the same size (its
+ * split then uses fewer workgroups if it must). Each product first builds a
+ * transient operand at the start of the workspace: dX the ternary codes
+ * transposed to fp4 [Kp][Np/2] (Kp*Np/2 bytes, Np = N rounded up to 64), dW
+ * a bf16 x_hat = bf16(x_q * s/127) [M][Kp] (2*M*Kp bytes). */
 size_t bitlinear_fwd_workspace_bytes(int64_t M, int64_t N, int64_t K);
 size_t bitlinear_bwd_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
@@ -120,6 +123,37 @@ bitnet_status bitnet_ternarize_pack(const void* W, bitnet_dtype w_dtype,
                                     uint8_t* w_packed, float* gamma,
                                     void* workspace, size_t workspace_bytes,
                                     void* stream);
+
+/*
+ * bitnet_quantize - bitnet_ternarize_pack and bitnet_act_quant of one layer
+ * step in one call, with the same results bit for bit (gamma, w_packed,
+ * x_q, s_x). The weight's absmean pass and the activation quantization
+ * share one launch (two independent streams over W and x), then the codes
+ * are packed. The two inputs share the reduction length K: W [N][K], x
+ * [M][K]. Arguments, layouts and errors are those of the two calls;
+ * workspace as bitnet_ternarize_pack's.
+ */
+bitnet_status bitnet_quantize(const void* W, bitnet_dtype w_dtype, int64_t N, int64_t K,
+                              const uint16_t* x, int64_t M,
+                              uint8_t* w_packed, float* gamma, int8_t* x_q, float* s_x,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * bitnet_code_counts - how many weights each ternary value takes, for the
+ * share of -1, 0 and +1 ("bitlinear.py", BitLinear.ternary_stats):
+ *
+ *   counts[0] = #{(n, k) : q[n,k] = -1},  counts[1] = #{(n, k) : q[n,k] = +1}
+ *
+ * over the true N x K weights (padding codes are 0 and count for neither;
+ * the zeros are N*K - counts[0] - counts[1]).
+ *
+ * w_packed  [N][Kp/4] codes as written by bitnet_ternarize_pack (16-byte
+ *           aligned).
+ * counts    [2] uint64 output (device, 8-byte aligned).
+ * No workspace. Exact and repeatable (a fixed summation order).
+ */
+bitnet_status bitnet_code_counts(const uint8_t* w_packed, int64_t N, int64_t K,
+                                 uint64_t* counts, void* stream);
 
 /*
  * bitnet_act_quant - per-token absmax int8 quantization ("bitlinear.py",
@@ -337,6 +371,46 @@ bitnet_status ttq_bwd(const uint16_t* dY, const uint16_t* x, const uint16_t* wt,
                       const uint8_t* w_packed, int64_t M, int64_t N, int64_t K,
                       uint16_t* dX, void* dW, bitnet_dtype dW_dtype, float* grads,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Test hooks (for the library's own tests and tuning; not needed to use it).
+ *
+ * bitnet_set_test_knobs - process-wide knobs read by every later launch:
+ *   split_ctas  0: the cost model chooses how output tiles are shared out;
+ *               > 0: every large-M GEMM splits its tiles over that many
+ *               workgroups (at most 256; no paired backward launch);
+ *               < 0: whole tiles only.
+ *   pair_cols   0: the cost model; k >= 1: a paired backward launch gives
+ *               dX k of its 8-workgroup columns.
+ *   no_skinny   nonzero: the large-M GEMMs also for M <= 64 (workspace
+ *               sizes queried while it is set cover that route).
+ *   spin_limit  polls (each a short sleep) before a workgroup waiting for
+ *               another's partial tile gives up; the default,
+ *               bitnet_default_spin_limit(), is about a second. A wait
+ *               that gives up writes its output tile as NaN (int32
+ *               accumulators: INT32_MIN) and is counted.
+ * bitnet_split_timeouts - the number of such waits that gave up on the
+ *   current device since the last call (then reset to 0). Synchronizes the
+ *   device. BITNET_ERR_HIP if the runtime fails.
+ * bitnet_debug_split_pieces - the pieces a split launch of `tiles` tiles of
+ *   `stages` reduction stages over `grid` workgroups (grid <= tiles*stages)
+ *   runs, computed on the host by the functions the kernels use: for each
+ *   piece in workgroup order, its virtual workgroup v, tile t, stages
+ *   [s0, s1), partial-tile slot, and the first workgroup va and piece count
+ *   n of its tile. Writes at most cap entries per array; returns the number
+ *   of pieces, or -1 for invalid arguments. bitnet_debug_partial_slots: the
+ *   slot count the plan reserves. bitnet_debug_cta_order: the virtual index
+ *   of each of `grid` workgroups (workgroup b runs on XCD b % 8; each XCD
+ *   gets a contiguous range).
+ */
+void bitnet_set_test_knobs(int split_ctas, int pair_cols, int no_skinny, uint32_t spin_limit);
+uint32_t bitnet_default_spin_limit(void);
+bitnet_status bitnet_split_timeouts(uint32_t* count);
+int64_t bitnet_debug_split_pieces(int64_t tiles, int32_t stages, int32_t grid, int32_t* v, int32_t* t,
+                                  int32_t* s0, int32_t* s1, int64_t* slot, int32_t* va, int32_t* n,
+                                  int64_t cap);
+int32_t bitnet_debug_partial_slots(int64_t tiles, int32_t grid);
+void bitnet_debug_cta_order(int32_t grid, int32_t* out);
 
 #ifdef __cplusplus
 }

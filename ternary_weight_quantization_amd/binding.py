@@ -60,6 +60,10 @@ def lib():
     L.bitlinear_bwd_workspace_bytes.restype = sz
     L.bitnet_ternarize_pack.argtypes = [vp, st, i64, i64, vp, vp, vp, sz, vp]
     L.bitnet_ternarize_pack.restype = st
+    L.bitnet_quantize.argtypes = [vp, st, i64, i64, vp, i64, vp, vp, vp, vp, vp, sz, vp]
+    L.bitnet_quantize.restype = st
+    L.bitnet_code_counts.argtypes = [vp, i64, i64, vp, vp]
+    L.bitnet_code_counts.restype = st
     L.bitnet_act_quant.argtypes = [vp, i64, i64, vp, vp, vp]
     L.bitnet_act_quant.restype = st
     L.bitlinear_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp, vp, sz, vp]
@@ -84,6 +88,19 @@ def lib():
     L.ttq_fwd_codes_workspace_bytes.restype = sz
     L.ttq_fwd_codes.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, sz, vp]
     L.ttq_fwd_codes.restype = st
+    i32, u32 = ctypes.c_int32, ctypes.c_uint32
+    L.bitnet_set_test_knobs.argtypes = [st, st, st, u32]
+    L.bitnet_set_test_knobs.restype = None
+    L.bitnet_default_spin_limit.argtypes = []
+    L.bitnet_default_spin_limit.restype = u32
+    L.bitnet_split_timeouts.argtypes = [vp]
+    L.bitnet_split_timeouts.restype = st
+    L.bitnet_debug_split_pieces.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp, vp, vp, i64]
+    L.bitnet_debug_split_pieces.restype = i64
+    L.bitnet_debug_partial_slots.argtypes = [i64, i32]
+    L.bitnet_debug_partial_slots.restype = i32
+    L.bitnet_debug_cta_order.argtypes = [i32, vp]
+    L.bitnet_debug_cta_order.restype = None
     if len(_hip_runtimes_mapped()) > 1:
         raise RuntimeError("more than one libamdhip64 is mapped into this process: "
                            f"{sorted(_hip_runtimes_mapped())}")
@@ -175,6 +192,38 @@ def bitnet_ternarize_pack(W, w_packed, gamma, workspace, stream=None):
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(lib().bitnet_ternarize_pack(_ptr(W), wd, N, K, _ptr(w_packed), _ptr(gamma),
                                        _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def bitnet_quantize(W, x, w_packed, gamma, x_q, s_x, workspace, stream=None):
+    """bitnet_ternarize_pack(W, ...) and bitnet_act_quant(x, ...) in one call
+    (W [N, K] bf16 or float32, x [M, K] bf16)."""
+    N, K = W.shape
+    M = x.shape[0]
+    Kp = bitnet_k_pad(K)
+    if W.dtype == torch.bfloat16:
+        wd = BITNET_BF16
+    elif W.dtype == torch.float32:
+        wd = BITNET_F32
+    else:
+        raise TypeError(f"W: expected bfloat16 or float32, got {W.dtype}")
+    _need(W, W.dtype, (N, K), "W")
+    _need(x, torch.bfloat16, (M, K), "x")
+    _need(w_packed, torch.uint8, (N, Kp // 4), "w_packed")
+    _need(gamma, torch.float32, (1,), "gamma")
+    _need(x_q, torch.int8, (M, Kp), "x_q")
+    _need(s_x, torch.float32, (M,), "s_x")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().bitnet_quantize(_ptr(W), wd, N, K, _ptr(x), M, _ptr(w_packed), _ptr(gamma), _ptr(x_q), _ptr(s_x),
+                                 _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def bitnet_code_counts(w_packed, K, counts, stream=None):
+    """counts int64 [2] = (number of -1 codes, number of +1 codes) in
+    w_packed uint8 [N, Kp/4] over the true N x K weights."""
+    N = w_packed.shape[0]
+    _need(w_packed, torch.uint8, (N, bitnet_k_pad(K) // 4), "w_packed")
+    _need(counts, torch.int64, (2,), "counts")
+    _check(lib().bitnet_code_counts(_ptr(w_packed), N, int(K), _ptr(counts), _stream(stream)))
 
 
 def bitnet_act_quant(x, x_q, s_x, stream=None):
@@ -355,3 +404,52 @@ def ttq_bwd(dY, x, wt, w_packed, K, dX=None, dW=None, grads=None, workspace=None
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().ttq_bwd(_ptr(dY), _ptr(x), _ptr(wt), _ptr(w_packed), M, N, int(K), _ptr(dX), _ptr(dW),
                          dw_dtype, _ptr(grads), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+# --- test hooks --------------------------------------------------------------
+
+def bitnet_set_test_knobs(split_ctas=0, pair_cols=0, no_skinny=0, spin_limit=None):
+    """Process-wide launch knobs (see the header); no arguments restores the
+    defaults (cost models, default spin limit)."""
+    L = lib()
+    if spin_limit is None:
+        spin_limit = int(L.bitnet_default_spin_limit())
+    L.bitnet_set_test_knobs(int(split_ctas), int(pair_cols), int(no_skinny), int(spin_limit))
+
+
+def bitnet_split_timeouts():
+    """Waits for partial tiles that gave up since the last call (synchronizes
+    the device)."""
+    c = ctypes.c_uint32(0)
+    _check(lib().bitnet_split_timeouts(ctypes.byref(c)))
+    return int(c.value)
+
+
+def bitnet_debug_split_pieces(tiles, stages, grid):
+    """The pieces of a split launch, as numpy arrays keyed v, t, s0, s1,
+    slot, va, n (host-side computation; no GPU needed)."""
+    import numpy as np
+
+    L = lib()
+    cap = int(grid) + int(tiles) + 1
+    arrs = {k: np.zeros(cap, dtype=np.int32) for k in ("v", "t", "s0", "s1", "va", "n")}
+    arrs["slot"] = np.zeros(cap, dtype=np.int64)
+    ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p)  # noqa: E731
+    n = int(L.bitnet_debug_split_pieces(int(tiles), int(stages), int(grid), ptr(arrs["v"]), ptr(arrs["t"]),
+                                        ptr(arrs["s0"]), ptr(arrs["s1"]), ptr(arrs["slot"]), ptr(arrs["va"]),
+                                        ptr(arrs["n"]), cap))
+    if n < 0 or n > cap:
+        raise ValueError(f"bitnet_debug_split_pieces({tiles}, {stages}, {grid}) returned {n}")
+    return {k: a[:n] for k, a in arrs.items()}
+
+
+def bitnet_debug_partial_slots(tiles, grid):
+    return int(lib().bitnet_debug_partial_slots(int(tiles), int(grid)))
+
+
+def bitnet_debug_cta_order(grid):
+    import numpy as np
+
+    out = np.zeros(int(grid), dtype=np.int32)
+    lib().bitnet_debug_cta_order(int(grid), out.ctypes.data_as(ctypes.c_void_p))
+    return out

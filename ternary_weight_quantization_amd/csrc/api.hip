@@ -86,11 +86,7 @@ size_t bitlinear_bwd_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (check_gemm_sizes(M, N, K) != BITNET_OK) return 0;
   // dX and dW run either in one launch (N % 8 == 0, both requested) or one
   // after the other, sharing the workspace
-  const size_t a = bitnet::gemm_workspace_bytes(bitnet::GemmKind::kBwdDx, M, N, K);
-  const size_t b = bitnet::gemm_workspace_bytes(bitnet::GemmKind::kBwdDw, M, N, K);
-  const size_t c = bitnet::gemm_workspace_bytes(bitnet::GemmKind::kBwdPair, M, N, K);
-  const size_t ab = a > b ? a : b;
-  return ab > c ? ab : c;
+  return bitnet::gemm_workspace_bytes(bitnet::GemmKind::kBwdPair, M, N, K);
 }
 
 bitnet_status bitnet_ternarize_pack(const void* W, bitnet_dtype w_dtype, int64_t N, int64_t K,
@@ -106,6 +102,31 @@ bitnet_status bitnet_ternarize_pack(const void* W, bitnet_dtype w_dtype, int64_t
   return from_hip(bitnet::launch_ternarize_pack(W, w_dtype == BITNET_F32, N, K, w_packed, gamma,
                                                 static_cast<double*>(workspace),
                                                 static_cast<hipStream_t>(stream)));
+}
+
+bitnet_status bitnet_quantize(const void* W, bitnet_dtype w_dtype, int64_t N, int64_t K, const uint16_t* x,
+                              int64_t M, uint8_t* w_packed, float* gamma, int8_t* x_q, float* s_x, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (!W || !w_packed || !gamma || !x || !x_q || !s_x) return BITNET_ERR_NULL;
+  if (w_dtype != BITNET_BF16 && w_dtype != BITNET_F32) return BITNET_ERR_DTYPE;
+  if (bitnet_status st = check_sizes(N, K)) return st;
+  if (bitnet_status st = check_sizes(M, K)) return st;
+  if (N * K > (int64_t(1) << 53)) return BITNET_ERR_SHAPE;
+  if (!aligned(W, 16) || !aligned(w_packed, 16) || !aligned(gamma, 4) || !aligned(x, 16) || !aligned(x_q, 16) ||
+      !aligned(s_x, 16))
+    return BITNET_ERR_ALIGN;
+  if (!workspace || workspace_bytes < bitnet_ternarize_workspace_bytes(N, K)) return BITNET_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return BITNET_ERR_ALIGN;
+  return from_hip(bitnet::launch_quantize(W, w_dtype == BITNET_F32, N, K, x, M, w_packed, gamma, x_q, s_x,
+                                          static_cast<double*>(workspace), static_cast<hipStream_t>(stream)));
+}
+
+bitnet_status bitnet_code_counts(const uint8_t* w_packed, int64_t N, int64_t K, uint64_t* counts, void* stream) {
+  if (!w_packed || !counts) return BITNET_ERR_NULL;
+  if (bitnet_status st = check_sizes(N, K)) return st;
+  if (!aligned(w_packed, 16) || !aligned(counts, 8)) return BITNET_ERR_ALIGN;
+  return from_hip(bitnet::launch_code_counts(w_packed, N, K, reinterpret_cast<unsigned long long*>(counts),
+                                             static_cast<hipStream_t>(stream)));
 }
 
 bitnet_status bitnet_act_quant(const uint16_t* x, int64_t M, int64_t K, int8_t* x_q, float* s_x,
@@ -279,6 +300,44 @@ bitnet_status ttq_bwd(const uint16_t* dY, const uint16_t* x, const uint16_t* wt,
   if (grads && (!aligned(grads, 4) || !aligned(w_packed, 16))) return BITNET_ERR_ALIGN;
   return from_hip(bitnet::launch_ttq_bwd(dY, x, wt, w_packed, M, N, K, dX, dW, dW_dtype == BITNET_F32, grads,
                                          workspace, workspace_bytes, static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------------------
+// Test hooks
+// ---------------------------------------------------------------------------
+
+void bitnet_set_test_knobs(int split_ctas, int pair_cols, int no_skinny, uint32_t spin_limit) {
+  bitnet::TestKnobs& k = bitnet::test_knobs();
+  k.split_ctas.store(split_ctas);
+  k.pair_cols.store(pair_cols);
+  k.no_skinny.store(no_skinny);
+  k.spin_limit.store(spin_limit);
+}
+
+uint32_t bitnet_default_spin_limit(void) { return bitnet::kDefaultSpinLimit; }
+
+bitnet_status bitnet_split_timeouts(uint32_t* count) {
+  if (!count) return BITNET_ERR_NULL;
+  unsigned int c = 0;
+  const hipError_t e = bitnet::take_split_timeouts(&c);
+  *count = c;
+  return from_hip(e);
+}
+
+int64_t bitnet_debug_split_pieces(int64_t tiles, int32_t stages, int32_t grid, int32_t* v, int32_t* t, int32_t* s0,
+                                  int32_t* s1, int64_t* slot, int32_t* va, int32_t* n, int64_t cap) {
+  if (tiles < 1 || stages < 1 || grid < 1 || grid > tiles * stages || !v || !t || !s0 || !s1 || !slot || !va || !n)
+    return -1;
+  return bitnet::debug_split_pieces(tiles, stages, grid, v, t, s0, s1, slot, va, n, cap);
+}
+
+int32_t bitnet_debug_partial_slots(int64_t tiles, int32_t grid) {
+  const int64_t a = 2 * (int64_t)grid, b = grid + tiles - 1;
+  return (int32_t)(a < b ? a : b);
+}
+
+void bitnet_debug_cta_order(int32_t grid, int32_t* out) {
+  if (grid >= 1 && out) bitnet::debug_cta_order(grid, out);
 }
 
 }  // extern "C"

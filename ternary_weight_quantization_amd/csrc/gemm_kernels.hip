@@ -92,6 +92,7 @@ struct MfmaI8 {
   typedef i32x4_t Frag;
   typedef i32x16_t Acc;
   typedef int Elem;
+  static constexpr uint32_t kPoisonBits = 0x80000000u;  // INT32_MIN
   static __device__ __forceinline__ Elem from_bits(uint32_t b) { return (int)b; }
   static __device__ __forceinline__ uint32_t to_bits(Elem e) { return (uint32_t)e; }
   static __device__ __forceinline__ Acc mma(Frag a, Frag b, Acc c) {
@@ -103,6 +104,7 @@ struct MfmaBf16 {
   typedef bf16x8_t Frag;
   typedef f32x16_t Acc;
   typedef float Elem;
+  static constexpr uint32_t kPoisonBits = 0x7FC00000u;  // quiet NaN
   static __device__ __forceinline__ Elem from_bits(uint32_t b) { return __uint_as_float(b); }
   static __device__ __forceinline__ uint32_t to_bits(Elem e) { return __float_as_uint(e); }
   static __device__ __forceinline__ Acc mma(Frag a, Frag b, Acc c) {
@@ -299,20 +301,32 @@ struct CopyLoader {
   int64_t pitch;      // bytes between rows
   int64_t rows;       // valid rows
   int64_t red_bytes;  // valid reduction bytes per row
-  struct Regs { uint4 v[8]; };
+  // lane_off: byte offset of the thread's chunk of its first row in stage 0
+  // (below 2^31: every operand read this way satisfies
+  // (rows + 256) * pitch <= 2^31)
+  struct Regs { uint4 v[8]; uint32_t lane_off; };
+
+  // Offset of row h of the thread's 8 in stage s, or an out-of-range offset
+  // for a chunk past the reduction (and every chunk of a stage past the
+  // last): 32-bit arithmetic on a per-lane base and uniform terms, so that
+  // the main loop keeps no 64-bit per-lane values.
+  __device__ __forceinline__ uint32_t stage_off(const Regs& r, int s, int h) const {
+    const int lim = (int)red_bytes - s * kStageBytes;
+    return (int)(threadIdx.x & 7) * 16 < lim ? r.lane_off + (uint32_t)(s * kStageBytes) + (uint32_t)(h * pitch) : kOob;
+  }
 
   __device__ __forceinline__ void load(Regs& r, int row0, int s) const {
     const int tid = threadIdx.x;
     const int64_t rowb = row0 + 8 * (tid >> 3);
-    const int64_t kb = (int64_t)s * kStageBytes + (tid & 7) * 16;
     if constexpr (FULL) {
       // rows past the end fall outside the resource; chunks past the
       // reduction (and stages past the last) get an out-of-range offset
       const rsrc_t rs = make_rsrc(base, (uint32_t)(rows * pitch));
-      const uint32_t off = kb < red_bytes ? (uint32_t)(rowb * pitch + kb) : kOob;
+      r.lane_off = (uint32_t)(rowb * pitch) + (uint32_t)((tid & 7) * 16);
 #pragma unroll
-      for (int h = 0; h < 8; ++h) r.v[h] = buf_load16(rs, off + (uint32_t)(h * pitch));
+      for (int h = 0; h < 8; ++h) r.v[h] = buf_load16(rs, stage_off(r, s, h));
     } else {
+      const int64_t kb = (int64_t)s * kStageBytes + (tid & 7) * 16;
       const char* p = base + rowb * pitch + kb;
 #pragma unroll
       for (int h = 0; h < 8; ++h) {
@@ -357,10 +371,7 @@ struct CopyLoader {
     if constexpr (FULL && (U == S0 + 8 || U == S0 + 10)) {
       constexpr int h = 2 * KS + (U == S0 + 10);
       const rsrc_t rs = make_rsrc(base, (uint32_t)(rows * pitch));
-      const int64_t rowb = row0 + 8 * (tid >> 3);
-      const int64_t kb = (int64_t)s2 * kStageBytes + (tid & 7) * 16;
-      const uint32_t off = kb < red_bytes ? (uint32_t)(rowb * pitch + kb) : kOob;
-      r.v[h] = buf_load16(rs, off + (uint32_t)(h * pitch));
+      r.v[h] = buf_load16(rs, stage_off(r, s2, h));
     }
     if constexpr (!FULL && KS == kKSteps - 1 && U == S0 + 8) load(r, row0, s2);
   }
@@ -379,18 +390,22 @@ struct RowCodesLoader {
   const uint8_t* packed;
   int64_t pitch;  // bytes per row (a multiple of 16)
   int64_t rows;   // valid rows
-  struct Regs { uint4 v[2]; };
+  // lane_off: byte offset of the thread's row (below 2^31, as every operand
+  // read through a buffer resource)
+  struct Regs { uint4 v[2]; uint32_t lane_off; };
   struct Tmp {};
 
-  __device__ __forceinline__ uint32_t offset(int row0, int s, int h) const {
-    const int64_t row = row0 + threadIdx.x;
-    const int64_t col = (int64_t)s * (kStageBytes / 4) + 16 * h;
-    return col < pitch ? (uint32_t)(row * pitch + col) : kOob;
+  // Half h of the thread's row in stage s; a column past the row (a stage
+  // past the last) gets an out-of-range offset. The column test is uniform.
+  __device__ __forceinline__ uint32_t offset(const Regs& r, int s, int h) const {
+    const int col = s * (kStageBytes / 4) + 16 * h;
+    return col < (int)pitch ? r.lane_off + (uint32_t)col : kOob;
   }
   __device__ __forceinline__ void load(Regs& r, int row0, int s) const {
     const rsrc_t rs = make_rsrc(packed, (uint32_t)(rows * pitch));
+    r.lane_off = (uint32_t)((row0 + threadIdx.x) * pitch);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) r.v[h] = buf_load16(rs, offset(row0, s, h));
+    for (int h = 0; h < 2; ++h) r.v[h] = buf_load16(rs, offset(r, s, h));
   }
   __device__ __forceinline__ void store(const Regs& r, char* lds) const {
     char* dst = lds + threadIdx.x * F::kPitchB;
@@ -406,7 +421,7 @@ struct RowCodesLoader {
       *reinterpret_cast<uint4*>(lds + threadIdx.x * F::kPitchB + 16 * KS) = r.v[KS];
     if constexpr (KS < 2 && U == 13) {
       const rsrc_t rs = make_rsrc(packed, (uint32_t)(rows * pitch));
-      r.v[KS] = buf_load16(rs, offset(row0, s2, KS));
+      r.v[KS] = buf_load16(rs, offset(r, s2, KS));
     }
   }
 };
@@ -1179,32 +1194,68 @@ struct SplitPlan {
   int grid;            // G
   int tiles_i;
   int nstages;         // S
+  uint32_t spin_limit; // polls before a wait for published partials gives up
   uint64_t gen;        // tag of this launch in the counters (0 < gen < 2^48)
+  int nslots;          // partial-tile slots: min(2G, G + T - 1)
   uint64_t* counters;  // [T][2] tagged counters (pieces arrived, partials
                        // published); NULL when no tile is split
-  uint4* partials;     // [2G][64][kThreads] 16-byte chunks of partial tiles
+  uint4* partials;     // [nslots][64][kThreads] 16-byte chunks of partial tiles
 };
 
-__device__ __forceinline__ int cta_order(int b, int G) {
+__host__ __device__ __forceinline__ int cta_order(int b, int G) {
   const int q = G / 8, r = G % 8;
   const int x = b % 8, k = b / 8;
   return (x < r) ? x * (q + 1) + k : r * (q + 1) + (x - r) * q + k;
 }
 
-__device__ __forceinline__ int64_t split_lo(const SplitPlan& p, int v) {
+__host__ __device__ __forceinline__ int64_t split_lo(const SplitPlan& p, int v) {
   return (int64_t)v * p.total / p.grid;
 }
 
 // The virtual workgroup whose range holds iteration it.
-__device__ __forceinline__ int split_owner(const SplitPlan& p, int64_t it) {
+__host__ __device__ __forceinline__ int split_owner(const SplitPlan& p, int64_t it) {
   return (int)(((it + 1) * p.grid - 1) / p.total);
 }
 
-// Partial-tile slot of workgroup v's piece of tile t: 2v for the tile its
-// range starts in, 2v + 1 for the tile it ends in.
-__device__ __forceinline__ int64_t piece_slot(const SplitPlan& p, int v, int t) {
+// Partial-tile slot of workgroup v's piece of tile t. Two numberings, each
+// giving every piece its own slot; the plan takes the one with fewer slots:
+//  - 2v for the tile v's range starts in, 2v + 1 for the tile it ends in
+//    (a range holds at most two split pieces: any tile strictly inside it
+//    is whole), 2G slots;
+//  - v + t: along the iteration order the next piece has the next
+//    workgroup, the next tile, or both, so v + t strictly increases,
+//    G + T - 1 slots (fewer when G > T).
+__host__ __device__ __forceinline__ int partial_slots(int64_t tiles, int grid) {
+  const int64_t a = 2 * (int64_t)grid, b = (int64_t)grid + tiles - 1;
+  return (int)(a < b ? a : b);
+}
+__host__ __device__ __forceinline__ int64_t piece_slot(const SplitPlan& p, int v, int t) {
+  if (p.nslots < 2 * p.grid) return (int64_t)v + t;
   return 2 * (int64_t)v + ((int64_t)t == split_lo(p, v) / p.nstages ? 0 : 1);
 }
+
+// The piece that starts at iteration it of a range ending at hi: tile t,
+// stages [s0, s1).
+__host__ __device__ __forceinline__ void split_piece(const SplitPlan& p, int64_t it, int64_t hi, int* t, int* s0,
+                                                     int* s1) {
+  *t = (int)(it / p.nstages);
+  *s0 = (int)(it - (int64_t)*t * p.nstages);
+  *s1 = (int)((int64_t)p.nstages < *s0 + (hi - it) ? (int64_t)p.nstages : *s0 + (hi - it));
+}
+
+// The workgroups that hold pieces of tile t: va .. va + n - 1, in stage order.
+__host__ __device__ __forceinline__ void split_tile_owners(const SplitPlan& p, int t, int* va, int* n) {
+  const int64_t S = p.nstages;
+  *va = split_owner(p, (int64_t)t * S);
+  *n = split_owner(p, (int64_t)t * S + S - 1) - *va + 1;
+}
+
+// Waits for published partials that ran out of polls (a piece that never
+// published: it cannot happen while every workgroup makes progress). The
+// tile is then written as NaN (int32 accumulators: INT32_MIN) instead of a
+// sum of unpublished data, and this counter is raised; the host reads and
+// clears it with bitnet_split_timeouts().
+__device__ unsigned int g_split_timeouts;
 
 // Tagged counters: a 64-bit word gen << 16 | count. A word written by
 // another launch (another tag) counts as zero, so the counters never need
@@ -1234,14 +1285,14 @@ __device__ __forceinline__ uint32_t tagged_count(const uint64_t* c, uint64_t gen
 
 // Wait until `want` partials of a tile are published. Only pieces that have
 // already arrived (so are running and only have their stores left) are
-// waited for; the bound is a safety net, never reached in practice.
-constexpr uint32_t kSpinLimit = 1u << 24;
-
-__device__ __forceinline__ void wait_published(const uint64_t* c, uint64_t gen, uint32_t want) {
-  for (uint32_t i = 0; i < kSpinLimit; ++i) {
-    if (tagged_count(c, gen) >= want) return;
+// waited for, so the wait ends; the bound (about a second at the default
+// limit) is a safety net. Returns false when it gave up.
+__device__ __forceinline__ bool wait_published(const uint64_t* c, uint64_t gen, uint32_t want, uint32_t limit) {
+  for (uint32_t i = 0; i < limit; ++i) {
+    if (tagged_count(c, gen) >= want) return true;
     __builtin_amdgcn_s_sleep(2);
   }
+  return tagged_count(c, gen) >= want;
 }
 
 template <class Acc>
@@ -1405,16 +1456,15 @@ template <class MT>
 __device__ __forceinline__ bool finish_piece(const SplitPlan& p, typename MT::Acc (&acc)[kFI][kFJ],
                                              int v, int t, int* s_flag) {
   const int tid = threadIdx.x;
-  const int64_t S = p.nstages;
-  const int va = split_owner(p, (int64_t)t * S);
-  const int vb = split_owner(p, (int64_t)t * S + S - 1);
-  const int n = vb - va + 1, me = v - va;
+  int va, n;
+  split_tile_owners(p, t, &va, &n);
+  const int me = v - va;
   uint64_t* cnt = p.counters + 2 * (int64_t)t;
   if (tid == 0) *s_flag = (int)tagged_arrive(cnt, p.gen);
   __syncthreads();
   const bool last = (*s_flag == n - 1);
   __syncthreads();
-  const rsrc_t pr = make_rsrc(p.partials, (uint32_t)(2 * (int64_t)p.grid * 64 * kThreads * 16));
+  const rsrc_t pr = make_rsrc(p.partials, (uint32_t)((int64_t)p.nslots * 64 * kThreads * 16));
   if (!last) {
     const uint32_t base = (uint32_t)(piece_slot(p, v, t) * 64 * kThreads + tid) * 16;
 #pragma unroll
@@ -1423,7 +1473,9 @@ __device__ __forceinline__ bool finish_piece(const SplitPlan& p, typename MT::Ac
     return false;
   }
   if (tid == 0) {
-    wait_published(cnt + 1, p.gen, (uint32_t)(n - 1));
+    const bool ok = wait_published(cnt + 1, p.gen, (uint32_t)(n - 1), p.spin_limit);
+    *s_flag = ok ? 1 : 0;
+    if (!ok) atomicAdd(&g_split_timeouts, 1u);
     // Every piece has arrived and published: nothing else touches this
     // tile's counters in this launch. Clearing them lets a later launch
     // with the same tag (a replay of a captured graph) count from zero.
@@ -1431,6 +1483,15 @@ __device__ __forceinline__ bool finish_piece(const SplitPlan& p, typename MT::Ac
     __hip_atomic_store(cnt + 1, uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
+  if (*s_flag == 0) {  // gave up: write the tile as a visible sentinel
+#pragma unroll
+    for (int fi = 0; fi < kFI; ++fi)
+#pragma unroll
+      for (int fj = 0; fj < kFJ; ++fj)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[fi][fj][e] = MT::from_bits(MT::kPoisonBits);
+    return true;
+  }
   constexpr int kBatch = 16;
 #pragma unroll
   for (int c0 = 0; c0 < 64; c0 += kBatch) {
@@ -1491,9 +1552,8 @@ __device__ __forceinline__ void gemm_body(const PL& pl, const QL& ql, const EP& 
   const int64_t hi = split_lo(plan, v + 1);
   uint64_t* pending = nullptr;  // published-partials counter to signal
   for (int64_t it = split_lo(plan, v); it < hi;) {
-    const int t = (int)(it / plan.nstages);
-    const int s0 = (int)(it - (int64_t)t * plan.nstages);
-    const int s1 = (int)((int64_t)plan.nstages < s0 + (hi - it) ? (int64_t)plan.nstages : s0 + (hi - it));
+    int t, s0, s1;
+    split_piece(plan, it, hi, &t, &s0, &s1);
     const int i0 = (t % plan.tiles_i) * kBI, j0 = (t / plan.tiles_i) * kBJ;
 
     typename MT::Acc acc[kFI][kFJ];
@@ -1556,6 +1616,54 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pair_kernel(PL1 pl1, QL1 ql1
 // Host side: choice of the split, workspace, launch.
 // ---------------------------------------------------------------------------
 
+TestKnobs& test_knobs() {
+  static TestKnobs knobs;
+  return knobs;
+}
+
+hipError_t take_split_timeouts(unsigned int* count) {
+  unsigned int* d = nullptr;
+  if (hipError_t e = hipGetSymbolAddress(reinterpret_cast<void**>(&d), HIP_SYMBOL(g_split_timeouts))) return e;
+  if (hipError_t e = hipDeviceSynchronize()) return e;
+  if (hipError_t e = hipMemcpy(count, d, sizeof(unsigned int), hipMemcpyDeviceToHost)) return e;
+  const unsigned int zero = 0;
+  return hipMemcpy(d, &zero, sizeof(unsigned int), hipMemcpyHostToDevice);
+}
+
+int64_t debug_split_pieces(int64_t T, int S, int G, int32_t* v, int32_t* t, int32_t* s0, int32_t* s1,
+                           int64_t* slot, int32_t* va, int32_t* n, int64_t cap) {
+  SplitPlan p{};
+  p.total = T * S;
+  p.grid = G;
+  p.nstages = S;
+  p.nslots = partial_slots(T, G);
+  int64_t k = 0;
+  for (int w = 0; w < G; ++w) {
+    const int64_t hi = split_lo(p, w + 1);
+    for (int64_t it = split_lo(p, w); it < hi;) {
+      int tt, a, b, o, c;
+      split_piece(p, it, hi, &tt, &a, &b);
+      split_tile_owners(p, tt, &o, &c);
+      if (k < cap) {
+        v[k] = w;
+        t[k] = tt;
+        s0[k] = a;
+        s1[k] = b;
+        slot[k] = piece_slot(p, w, tt);
+        va[k] = o;
+        n[k] = c;
+      }
+      ++k;
+      it += b - a;
+    }
+  }
+  return k;
+}
+
+void debug_cta_order(int G, int32_t* out) {
+  for (int b = 0; b < G; ++b) out[b] = cta_order(b, G);
+}
+
 constexpr int kMaxGrid = 256;  // workgroups of a split launch (one per CU)
 constexpr size_t kPartialBytes = (size_t)64 * kThreads * 16;  // one partial tile
 
@@ -1582,9 +1690,9 @@ static GemmShape shape_of(GemmKind kind, int64_t M, int64_t N, int64_t K) {
 // Workgroups of a split launch, or 0 for one whole tile per workgroup.
 // A split pays when T tiles leave the last round of whole tiles on `cus`
 // CUs partly idle; it spreads the T*S stages evenly over at most `cus`
-// workgroups and about 4 pieces per tile. BITNET_SPLIT_CTAS=<G> forces a
-// split over G workgroups, a negative value forces whole tiles (test and
-// tuning knobs).
+// workgroups and about 4 pieces per tile. The split_ctas test knob
+// (bitnet_set_test_knobs) forces a split over that many workgroups, or with
+// a negative value whole tiles.
 static int split_pays(const GemmShape& g, int cus) {
   const int64_t T = g.tiles(), S = g.nstages, W = T * S;
   if (W < 2 || cus < 1) return 0;
@@ -1594,26 +1702,22 @@ static int split_pays(const GemmShape& g, int cus) {
   return split < whole ? (int)G : 0;
 }
 static int split_grid(const GemmShape& g, int cus) {
-  if (const char* e = getenv("BITNET_SPLIT_CTAS")) {
-    const long f = strtol(e, nullptr, 10);
-    if (f < 0) return 0;
-    if (f > 0) {
-      const int64_t W = g.tiles() * g.nstages;
-      const int64_t G = f < kMaxGrid ? f : kMaxGrid;
-      return (int)(G < W ? G : W);
-    }
+  const int f = test_knobs().split_ctas.load(std::memory_order_relaxed);
+  if (f < 0) return 0;
+  if (f > 0) {
+    const int64_t W = g.tiles() * g.nstages;
+    const int64_t G = f < kMaxGrid ? f : kMaxGrid;
+    return (int)(G < W ? G : W);
   }
   return split_pays(g, cus);
 }
 
 // Split-launch workspace: the tile counters [T][2] (8 bytes each, rounded
-// up to 256 bytes), then the partial tiles [2G].
-static size_t split_control_bytes(const GemmShape& g, int) {
-  return ((size_t)g.tiles() * 16 + 255) / 256 * 256;
-}
+// up to 256 bytes), then the partial tiles [partial_slots(T, G)].
+static size_t split_control_bytes(const GemmShape& g) { return ((size_t)g.tiles() * 16 + 255) / 256 * 256; }
 static size_t split_workspace(const GemmShape& g, int grid) {
   if (grid == 0) return 0;
-  return split_control_bytes(g, grid) + 2 * (size_t)grid * kPartialBytes;
+  return split_control_bytes(g) + (size_t)partial_slots(g.tiles(), grid) * kPartialBytes;
 }
 
 // dW's x_hat buffer at the start of its workspace.
@@ -1621,52 +1725,33 @@ static size_t xhat_bytes(int64_t M, int64_t K) { return ((size_t)M * k_pad(K) * 
 static int64_t n_pad64(int64_t N) { return (N + 63) / 64 * 64; }
 static size_t wt_bytes(int64_t N, int64_t K) { return ((size_t)k_pad(K) * (n_pad64(N) / 2) + 255) / 256 * 256; }
 
-// The two backward products run in one launch when N % 8 == 0 and each of
-// them would split its tiles on a full device anyway. Workspace: [wt]
-// [x_hat], then the split workspaces of dX and dW, sized for their shares
-// of at most kMaxGrid workgroups.
-static bool pair_eligible(int64_t M, int64_t N, int64_t K) {
-  return N % 8 == 0 && split_pays(shape_of(GemmKind::kBwdDx, M, N, K), kMaxGrid) > 0 &&
-         split_pays(shape_of(GemmKind::kBwdDw, M, N, K), kMaxGrid) > 0;
-}
-static size_t pair_workspace_bound(int64_t M, int64_t N, int64_t K) {
-  const GemmShape g1 = shape_of(GemmKind::kBwdDx, M, N, K), g2 = shape_of(GemmKind::kBwdDw, M, N, K);
-  return wt_bytes(N, K) + xhat_bytes(M, K) + split_control_bytes(g1, kMaxGrid) +
-         split_control_bytes(g2, kMaxGrid) + 2 * (size_t)kMaxGrid * kPartialBytes;
+static int device_cus();
+
+// The split grid a launch given ws_bytes of split workspace runs: the grid
+// split_grid() chooses, or the largest smaller one whose workspace fits and
+// whose split still beats whole tiles on `cus` CUs (a grid forced by the
+// knob: the largest that fits); 0: whole tiles.
+static int fit_split(const GemmShape& g, int cus, size_t ws_bytes) {
+  const int want = split_grid(g, cus);
+  if (want == 0 || split_workspace(g, want) <= ws_bytes) return want;
+  const bool forced = test_knobs().split_ctas.load(std::memory_order_relaxed) > 0;
+  const int64_t T = g.tiles(), S = g.nstages, W = T * S;
+  const int64_t whole = (T + cus - 1) / cus * S;
+  for (int G = want - 1; G >= 2; --G) {
+    if (split_workspace(g, G) > ws_bytes) continue;
+    if (forced) return G;
+    return (W + G - 1) / G + g.overhead < whole ? G : 0;
+  }
+  return 0;
 }
 
-// TTQ backward: the wave-tile partials of the scale gradients, then the
-// split workspace of dX or dW (the two run one after the other).
+// TTQ backward: the wave-tile partials of the scale gradients come first.
 static int64_t ttq_wave_tiles(int64_t N, int64_t K) {
   const GemmShape g = shape_of(GemmKind::kBwdDw, 1, N, K);
   return 4 * g.tiles();
 }
 static size_t ttq_partials_bytes(int64_t N, int64_t K) {
   return ((size_t)ttq_wave_tiles(N, K) * sizeof(float2) + 255) / 256 * 256;
-}
-// dX and dW of TTQ in one launch: both operands copied as stored (N, K
-// multiples of 8) and each product splitting its tiles on a full device.
-static bool ttq_pair_eligible(int64_t M, int64_t N, int64_t K) {
-  return N % 8 == 0 && K % 8 == 0 && split_pays(shape_of(GemmKind::kBwdDx, M, N, K), kMaxGrid) > 0 &&
-         split_pays(shape_of(GemmKind::kBwdDw, M, N, K), kMaxGrid) > 0;
-}
-static size_t pair_split_bound(const GemmShape& g1, const GemmShape& g2);
-
-size_t gemm_workspace_bytes(GemmKind kind, int64_t M, int64_t N, int64_t K) {
-  if (kind == GemmKind::kBwdPair) return pair_eligible(M, N, K) ? pair_workspace_bound(M, N, K) : 0;
-  if (kind == GemmKind::kTtqBwd) {
-    const GemmShape gx = shape_of(GemmKind::kBwdDx, M, N, K), gw = shape_of(GemmKind::kBwdDw, M, N, K);
-    const size_t a = split_workspace(gx, split_grid(gx, kMaxGrid)), b = split_workspace(gw, split_grid(gw, kMaxGrid));
-    const size_t c = ttq_pair_eligible(M, N, K) ? pair_split_bound(gx, gw) : 0;
-    return ttq_partials_bytes(N, K) + std::max(std::max(a, b), c);
-  }
-  const GemmShape g = shape_of(kind, M, N, K);
-  // the few-token forward needs none; the large-M kernel's share stays
-  // reserved so that BITNET_NO_SKINNY (a test knob) can run it at any M
-  const size_t split = split_workspace(g, split_grid(g, kMaxGrid));
-  if (kind == GemmKind::kBwdDw) return xhat_bytes(M, K) + split;
-  if (kind == GemmKind::kBwdDx) return wt_bytes(N, K) + split;
-  return split;
 }
 
 static int device_cus() {
@@ -1726,17 +1811,14 @@ static PairCost product_cost(const GemmShape& g, int64_t G, const ProductCosts& 
 
 // The 8-workgroup columns (of kt) that run dX in a pair launch: the k1 that
 // minimizes the slower product's modelled cost; 0: no pair launch (the
-// split knob is set, or too few CUs). BITNET_PAIR_COLS=<k1> overrides
-// (tuning knob).
+// split_ctas knob is set, or too few CUs). The pair_cols knob overrides k1.
 static int pair_columns(const GemmShape& g1, const GemmShape& g2, int cus, int* kt, const ProductCosts& c1,
                         const ProductCosts& c2) {
-  if (getenv("BITNET_SPLIT_CTAS")) return 0;
+  if (test_knobs().split_ctas.load(std::memory_order_relaxed) != 0) return 0;
   *kt = (cus < kMaxGrid ? cus : kMaxGrid) / 8;
   if (*kt < 2) return 0;
-  if (const char* e = getenv("BITNET_PAIR_COLS")) {
-    const long f = strtol(e, nullptr, 10);
-    if (f >= 1 && f < *kt) return (int)f;
-  }
+  const int f = test_knobs().pair_cols.load(std::memory_order_relaxed);
+  if (f >= 1 && f < *kt) return f;
   int best = 1;
   double best_t = 1e300;
   for (int k1 = 1; k1 < *kt; ++k1) {
@@ -1755,9 +1837,11 @@ static SplitPlan split_plan(const GemmShape& g, int grid, void* ws) {
   plan.tiles_i = (int)g.tiles_i;
   plan.nstages = (int)g.nstages;
   plan.grid = grid;
+  plan.spin_limit = test_knobs().spin_limit.load(std::memory_order_relaxed);
   plan.gen = next_gen();
+  plan.nslots = partial_slots(g.tiles(), grid);
   plan.counters = static_cast<uint64_t*>(ws);
-  plan.partials = reinterpret_cast<uint4*>(static_cast<char*>(ws) + split_control_bytes(g, grid));
+  plan.partials = reinterpret_cast<uint4*>(static_cast<char*>(ws) + split_control_bytes(g));
   return plan;
 }
 
@@ -1774,31 +1858,51 @@ static SplitPlan whole_plan(const GemmShape& g, int grid) {
 template <class MT, int MAP, class PL, class QL, class EP>
 static hipError_t run_gemm(const PL& pl, const QL& ql, const EP& ep, const GemmShape& g, void* ws,
                            size_t ws_bytes, hipStream_t stream) {
-  SplitPlan plan{};
-  plan.total = g.tiles() * g.nstages;
-  plan.tiles_i = (int)g.tiles_i;
-  plan.nstages = (int)g.nstages;
-  int grid = split_grid(g, device_cus());
-  if (grid > 0 && (ws == nullptr || ws_bytes < split_workspace(g, grid))) grid = 0;
-  if (grid > 0) {
-    plan.grid = grid;
-    plan.gen = next_gen();
-    plan.counters = static_cast<uint64_t*>(ws);
-    plan.partials = reinterpret_cast<uint4*>(static_cast<char*>(ws) + split_control_bytes(g, grid));
-  } else {
-    plan.grid = (int)g.tiles();
-  }
+  const int grid = ws == nullptr ? 0 : fit_split(g, device_cus(), ws_bytes);
+  const SplitPlan plan = grid > 0 ? split_plan(g, grid, ws) : whole_plan(g, (int)g.tiles());
   gemm_kernel<MT, MAP, PL, QL, EP><<<plan.grid, kThreads, 0, stream>>>(pl, ql, ep, plan);
   return hipGetLastError();
+}
+
+// Two products in one gemm_pair_kernel launch, each on its own share of the
+// CUs (pair_columns), each splitting its tiles only when the cost model says
+// that beats whole tiles taken in turn on its share (stage costs c1, c2).
+// k1 == 0: no pair launch on this device. s1, s2: split workspace bytes.
+struct PairPlan {
+  int kt = 0, k1 = 0, G1 = 0, G2 = 0;
+  bool sk1 = false, sk2 = false;
+  size_t s1 = 0, s2 = 0;
+};
+static PairPlan plan_pair(const GemmShape& g1, const GemmShape& g2, int cus, const ProductCosts& c1,
+                          const ProductCosts& c2) {
+  PairPlan pp;
+  pp.k1 = pair_columns(g1, g2, cus, &pp.kt, c1, c2);
+  if (pp.k1 == 0) return pp;
+  // every workgroup of a split needs a non-empty range, and more than about
+  // 4 pieces per tile do not pay
+  const auto cap = [](const GemmShape& g, int64_t G) {
+    const int64_t W = g.tiles() * g.nstages, P = 4 * g.tiles();
+    return (int)(G < W ? (G < P ? G : P) : (W < P ? W : P));
+  };
+  const int64_t share1 = 8 * pp.k1, share2 = 8 * (pp.kt - pp.k1);
+  pp.sk1 = product_cost(g1, share1, c1).split;
+  pp.sk2 = product_cost(g2, share2, c2).split;
+  pp.G1 = pp.sk1 ? cap(g1, share1) : (int)(g1.tiles() < share1 ? g1.tiles() : share1);
+  pp.G2 = pp.sk2 ? cap(g2, share2) : (int)(g2.tiles() < share2 ? g2.tiles() : share2);
+  pp.s1 = pp.sk1 ? split_workspace(g1, pp.G1) : 0;
+  pp.s2 = pp.sk2 ? split_workspace(g2, pp.G2) : 0;
+  return pp;
 }
 
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 
-// Few tokens run the decode-shaped kernels (BITNET_NO_SKINNY, a test knob,
-// keeps the large-M GEMMs at any M).
-static bool skinny(int64_t M) { return M <= kSkinnyMaxM && getenv("BITNET_NO_SKINNY") == nullptr; }
+// Few tokens run the decode-shaped kernels (the no_skinny test knob keeps
+// the large-M GEMMs at any M).
+static bool skinny(int64_t M) {
+  return M <= kSkinnyMaxM && test_knobs().no_skinny.load(std::memory_order_relaxed) == 0;
+}
 
 hipError_t launch_fwd(const int8_t* x_q, const float* s_x, const uint8_t* w_packed,
                       const float* gamma, const uint16_t* bias, int64_t M, int64_t N, int64_t K, uint16_t* y,
@@ -1897,51 +2001,84 @@ hipError_t launch_bwd_dw(const uint16_t* dY, const int8_t* x_q, const float* s_x
   }
 }
 
-// Two products in one gemm_pair_kernel launch, each on its own share of the
-// CUs (pair_columns), each splitting its tiles only when the cost model says
-// that beats whole tiles taken in turn on its share (stage costs c1, c2).
-// ws holds the two split workspaces (pair_split_bound bytes suffice).
+// The pair launch of plan_pair on ws (pp.s1 + pp.s2 bytes);
 // hipErrorNotSupported (nothing launched): the device or the workspace does
 // not allow it.
-static size_t pair_split_bound(const GemmShape& g1, const GemmShape& g2) {
-  return split_control_bytes(g1, kMaxGrid) + split_control_bytes(g2, kMaxGrid) + 2 * (size_t)kMaxGrid * kPartialBytes;
-}
 template <int MAP1, int MAP2, class PL1, class QL1, class EP1, class PL2, class QL2, class EP2>
 static hipError_t run_pair(const PL1& p1, const QL1& q1, const EP1& e1, const GemmShape& g1,
                            const ProductCosts& c1, const PL2& p2, const QL2& q2, const EP2& e2, const GemmShape& g2,
-                           const ProductCosts& c2, char* ws,
-                           size_t ws_bytes, hipStream_t stream) {
-  int kt = 0;
-  const int k1 = pair_columns(g1, g2, device_cus(), &kt, c1, c2);
-  if (k1 == 0) return hipErrorNotSupported;
-  // every workgroup of a split needs a non-empty range, and more than about
-  // 4 pieces per tile do not pay
-  const auto cap = [](const GemmShape& g, int64_t G) {
-    const int64_t W = g.tiles() * g.nstages, P = 4 * g.tiles();
-    return (int)(G < W ? (G < P ? G : P) : (W < P ? W : P));
-  };
-  const int64_t share1 = 8 * k1, share2 = 8 * (kt - k1);
-  const bool sk1 = product_cost(g1, share1, c1).split, sk2 = product_cost(g2, share2, c2).split;
-  const int G1 = sk1 ? cap(g1, share1) : (int)(g1.tiles() < share1 ? g1.tiles() : share1);
-  const int G2 = sk2 ? cap(g2, share2) : (int)(g2.tiles() < share2 ? g2.tiles() : share2);
-  const size_t s1 = sk1 ? split_workspace(g1, G1) : 0, s2 = sk2 ? split_workspace(g2, G2) : 0;
-  if (ws_bytes < s1 + s2) return hipErrorNotSupported;
-  const SplitPlan plan1 = sk1 ? split_plan(g1, G1, ws) : whole_plan(g1, G1);
-  const SplitPlan plan2 = sk2 ? split_plan(g2, G2, ws + s1) : whole_plan(g2, G2);
+                           const ProductCosts& c2, char* ws, size_t ws_bytes, hipStream_t stream) {
+  const PairPlan pp = plan_pair(g1, g2, device_cus(), c1, c2);
+  if (pp.k1 == 0 || ws_bytes < pp.s1 + pp.s2) return hipErrorNotSupported;
+  const SplitPlan plan1 = pp.sk1 ? split_plan(g1, pp.G1, ws) : whole_plan(g1, pp.G1);
+  const SplitPlan plan2 = pp.sk2 ? split_plan(g2, pp.G2, ws + pp.s1) : whole_plan(g2, pp.G2);
   gemm_pair_kernel<MfmaBf16, MAP1, PL1, QL1, EP1, MAP2, PL2, QL2, EP2>
-      <<<8 * kt, kThreads, 0, stream>>>(p1, q1, e1, plan1, p2, q2, e2, plan2, k1);
+      <<<8 * pp.kt, kThreads, 0, stream>>>(p1, q1, e1, plan1, p2, q2, e2, plan2, pp.k1);
   return hipGetLastError();
+}
+
+static bool skinny(int64_t M);
+
+// The STE backward products run in one launch when N % 8 == 0, there are
+// more than a few tokens and each product would split its tiles on the full
+// device anyway.
+static bool pair_eligible(int64_t M, int64_t N, int64_t K) {
+  const int cus = device_cus();
+  return N % 8 == 0 && !skinny(M) && split_pays(shape_of(GemmKind::kBwdDx, M, N, K), cus) > 0 &&
+         split_pays(shape_of(GemmKind::kBwdDw, M, N, K), cus) > 0;
+}
+// TTQ's pair: both operands copied as stored (N, K multiples of 8).
+static bool ttq_pair_eligible(int64_t M, int64_t N, int64_t K) {
+  const int cus = device_cus();
+  return N % 8 == 0 && K % 8 == 0 && split_pays(shape_of(GemmKind::kBwdDx, M, N, K), cus) > 0 &&
+         split_pays(shape_of(GemmKind::kBwdDw, M, N, K), cus) > 0;
+}
+static size_t pair_split_bytes(int64_t M, int64_t N, int64_t K) {
+  const PairPlan pp = plan_pair(shape_of(GemmKind::kBwdDx, M, N, K), shape_of(GemmKind::kBwdDw, M, N, K),
+                                device_cus(), kDxCosts, kDwCosts);
+  return pp.k1 == 0 ? 0 : pp.s1 + pp.s2;
+}
+
+// Workspace of each entry point, from the plan its launch runs on this
+// device (the split grids, the pair's shares and modes). A backward call
+// with one output reuses the paired call's workspace: its pre-pass buffer
+// comes first and its split grid fits into the rest (fit_split).
+size_t gemm_workspace_bytes(GemmKind kind, int64_t M, int64_t N, int64_t K) {
+  const int cus = device_cus();
+  const auto alone = [&](GemmKind k) {
+    const GemmShape g = shape_of(k, M, N, K);
+    return split_workspace(g, split_grid(g, cus));
+  };
+  switch (kind) {
+    case GemmKind::kFwd:
+      return skinny(M) ? 0 : alone(kind);  // the few-token forward needs none
+    case GemmKind::kTtqFwd: return alone(kind);
+    case GemmKind::kBwdDx: return wt_bytes(N, K) + (skinny(M) && N % 8 == 0 ? 0 : alone(kind));
+    case GemmKind::kBwdDw: return xhat_bytes(M, K) + alone(kind);
+    case GemmKind::kBwdPair: {
+      if (pair_eligible(M, N, K) && pair_split_bytes(M, N, K) > 0)
+        return std::max(wt_bytes(N, K) + xhat_bytes(M, K) + pair_split_bytes(M, N, K),
+                        std::max(wt_bytes(N, K), xhat_bytes(M, K)));
+      return std::max(gemm_workspace_bytes(GemmKind::kBwdDx, M, N, K),
+                      gemm_workspace_bytes(GemmKind::kBwdDw, M, N, K));
+    }
+    case GemmKind::kTtqBwd: {
+      if (ttq_pair_eligible(M, N, K) && pair_split_bytes(M, N, K) > 0)
+        return ttq_partials_bytes(N, K) + pair_split_bytes(M, N, K);
+      return ttq_partials_bytes(N, K) + std::max(alone(GemmKind::kBwdDx), alone(GemmKind::kBwdDw));
+    }
+  }
+  return 0;
 }
 
 hipError_t launch_bwd_pair(const uint16_t* dY, const uint8_t* w_packed, const float* gamma, const int8_t* x_q,
                            const float* s_x, int64_t M, int64_t N, int64_t K, uint16_t* dX, void* dW,
                            DwOut dw_out, void* ws, size_t ws_bytes, hipStream_t stream) {
-  if (!pair_eligible(M, N, K) || ws == nullptr || skinny(M)) return hipErrorNotSupported;
+  if (!pair_eligible(M, N, K) || ws == nullptr) return hipErrorNotSupported;
   const GemmShape g1 = shape_of(GemmKind::kBwdDx, M, N, K), g2 = shape_of(GemmKind::kBwdDw, M, N, K);
   const size_t wb = wt_bytes(N, K), xb = xhat_bytes(M, K);
-  if (ws_bytes < wb + xb) return hipErrorNotSupported;
-  int kt = 0;
-  if (pair_columns(g1, g2, device_cus(), &kt, kDxCosts, kDwCosts) == 0) return hipErrorNotSupported;
+  const PairPlan pp = plan_pair(g1, g2, device_cus(), kDxCosts, kDwCosts);
+  if (pp.k1 == 0 || ws_bytes < wb + xb + pp.s1 + pp.s2) return hipErrorNotSupported;
   char* base = static_cast<char*>(ws);
   uint8_t* wt = reinterpret_cast<uint8_t*>(base);
   uint16_t* xhat = reinterpret_cast<uint16_t*>(base + wb);
@@ -2003,15 +2140,15 @@ hipError_t launch_ttq_fwd(const uint16_t* x, const uint16_t* wt, int64_t M, int6
 
 // The forward from the stored codes: few tokens read the 2-bit codes once
 // (launch_ttq_fwd_skinny); otherwise the codes become wt at the start of the
-// workspace and the GEMM above runs on it. BITNET_NO_SKINNY (a test knob)
-// keeps the second route at any M.
+// workspace and the GEMM above runs on it. The no_skinny test knob keeps
+// the second route at any M.
 static bool ttq_codes_skinny(int64_t M, int64_t K) { return skinny(M) && K % 8 == 0; }
 static size_t ttq_wt_bytes(int64_t N, int64_t K) { return ((size_t)N * k_pad(K) * 2 + 255) / 256 * 256; }
 
 size_t ttq_codes_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   // none for the few-token route (a decode caller needs no 2*N*Kp buffer);
-  // the knob is read here too, so a size queried under it covers the GEMM
-  // route
+  // the no_skinny knob is read here too, so a size queried under it covers
+  // the GEMM route
   if (ttq_codes_skinny(M, K)) return 0;
   return ttq_wt_bytes(N, K) + gemm_workspace_bytes(GemmKind::kTtqFwd, M, N, K);
 }

@@ -6,7 +6,41 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace bitnet {
+
+// Test and tuning knobs of the GEMM launchers, process-wide, set through
+// bitnet_set_test_knobs(). Defaults: the cost models decide.
+//  split_ctas  0: cost model; > 0: split every GEMM over that many
+//              workgroups (and no paired backward launch); < 0: whole tiles
+//  pair_cols   0: cost model; k >= 1: dX gets k of the 8-workgroup columns
+//              of a paired backward launch
+//  no_skinny   nonzero: the large-M GEMMs also for few tokens
+//  spin_limit  polls before a wait for another workgroup's partial tile
+//              gives up (the tile is then written as a sentinel and counted)
+constexpr uint32_t kDefaultSpinLimit = 1u << 24;
+struct TestKnobs {
+  std::atomic<int> split_ctas{0};
+  std::atomic<int> pair_cols{0};
+  std::atomic<int> no_skinny{0};
+  std::atomic<uint32_t> spin_limit{kDefaultSpinLimit};
+};
+TestKnobs& test_knobs();
+
+// Waits for published partial tiles that gave up since the last call (read
+// and cleared on the current device; synchronizes the device).
+hipError_t take_split_timeouts(unsigned int* count);
+
+// The pieces a split launch of T tiles x S stages over G workgroups runs,
+// computed on the host by the same functions the kernels use: for each
+// piece, in workgroup order, its virtual workgroup v, tile t, stages
+// [s0, s1), partial slot, and the first owner va and piece count n of its
+// tile. Returns the number of pieces (at most cap are written).
+int64_t debug_split_pieces(int64_t T, int S, int G, int32_t* v, int32_t* t, int32_t* s0, int32_t* s1,
+                           int64_t* slot, int32_t* va, int32_t* n, int64_t cap);
+// The virtual index of each of G workgroups (cta_order).
+void debug_cta_order(int G, int32_t* out);
 
 // Fixed grid of the absmean partial-sum kernel: the partial order (and so
 // gamma's bits) never depends on the device or the call.
@@ -20,10 +54,25 @@ hipError_t launch_ternarize_pack(const void* W, bool w_is_f32, int64_t N, int64_
                                  uint8_t* w_packed, float* gamma, double* partials,
                                  hipStream_t stream);
 
+// The pack pass alone (gamma from the partials, codes, packing).
+hipError_t launch_pack(const void* W, bool w_is_f32, int64_t N, int64_t K, uint8_t* w_packed, float* gamma,
+                       const double* partials, hipStream_t stream);
+
+// Weight ternarization + pack and activation quantization together: the
+// absmean partials and the act-quant rows in one launch, then the pack.
+hipError_t launch_quantize(const void* W, bool w_is_f32, int64_t N, int64_t K, const uint16_t* x, int64_t M,
+                           uint8_t* w_packed, float* gamma, int8_t* x_q, float* s_x, double* partials,
+                           hipStream_t stream);
+
 // Bias gradient db[n] = sum_m dY[m][n] (fp32, fixed order), db as f32 or
 // bf16 bits.
 hipError_t launch_bias_grad(const uint16_t* dY, int64_t M, int64_t N, void* db, bool db_is_f32,
                             hipStream_t stream);
+
+// Counts of the codes -1 and +1 in w_packed [N][Kp/4]: counts[0] = #(-1),
+// counts[1] = #(+1) (the zeros are N*K minus both).
+hipError_t launch_code_counts(const uint8_t* w_packed, int64_t N, int64_t K, unsigned long long* counts,
+                              hipStream_t stream);
 
 // Per-token absmax int8 activation quantization.
 hipError_t launch_act_quant(const uint16_t* x, int64_t M, int64_t K,

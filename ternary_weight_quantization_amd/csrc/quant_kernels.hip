@@ -50,15 +50,21 @@ __device__ __forceinline__ float load_elem(const void* w, int64_t i) {
   else return bf16_to_f32(static_cast<const uint16_t*>(w)[i]);
 }
 
+// Partial sum b of the fixed grid: thread t of the kAbsmeanThreads of block
+// b reads the 16-byte vectors b * kAbsmeanThreads + t + j * stride (stride =
+// kAbsmeanBlocks * kAbsmeanThreads, the whole grid), 8 loads in flight, and
+// the block adds its threads' sums in a fixed tree. The order depends only
+// on the grid constants, never on the launch, so every kernel that runs
+// this body (alone or next to other work) gives gamma the same bits.
 template <bool F32>
-__global__ __launch_bounds__(kAbsmeanThreads) void absmean_partials_kernel(
-    const void* __restrict__ w, int64_t n, double* __restrict__ partials) {
+__device__ __forceinline__ void absmean_block(const void* __restrict__ w, int64_t n, double* __restrict__ partials,
+                                              int b) {
   constexpr int kVec = F32 ? 4 : 8;  // elements per 16 bytes
   constexpr int kUnroll = 8;
   const uint4* wv = static_cast<const uint4*>(w);
   const int64_t nvec = n / kVec;
-  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t tid = (int64_t)b * kAbsmeanThreads + threadIdx.x;
+  constexpr int64_t stride = (int64_t)kAbsmeanBlocks * kAbsmeanThreads;
 
   double acc[kUnroll];
 #pragma unroll
@@ -85,8 +91,14 @@ __global__ __launch_bounds__(kAbsmeanThreads) void absmean_partials_kernel(
     double t = 0.0;
 #pragma unroll
     for (int j = 0; j < kAbsmeanThreads / kWave; ++j) t += sw[j];
-    partials[blockIdx.x] = t;
+    partials[b] = t;
   }
+}
+
+template <bool F32>
+__global__ __launch_bounds__(kAbsmeanThreads) void absmean_partials_kernel(
+    const void* __restrict__ w, int64_t n, double* __restrict__ partials) {
+  absmean_block<F32>(w, n, partials, blockIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -185,17 +197,9 @@ __global__ __launch_bounds__(kPackThreads) void ternarize_pack_kernel(
   }
 }
 
-hipError_t launch_ternarize_pack(const void* W, bool w_is_f32, int64_t N, int64_t K,
-                                 uint8_t* w_packed, float* gamma, double* partials,
-                                 hipStream_t stream) {
-  const int64_t n = N * K;
-  if (w_is_f32)
-    absmean_partials_kernel<true><<<kAbsmeanBlocks, kAbsmeanThreads, 0, stream>>>(W, n, partials);
-  else
-    absmean_partials_kernel<false><<<kAbsmeanBlocks, kAbsmeanThreads, 0, stream>>>(W, n, partials);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-
+// The pack pass (gamma from the partials, codes, packing).
+hipError_t launch_pack(const void* W, bool w_is_f32, int64_t N, int64_t K, uint8_t* w_packed, float* gamma,
+                       const double* partials, hipStream_t stream) {
   const int64_t wpr = k_pad(K) / 16;
   const int64_t total = N * wpr;
   const int64_t want = (total + kPackThreads - 1) / kPackThreads;
@@ -209,6 +213,67 @@ hipError_t launch_ternarize_pack(const void* W, bool w_is_f32, int64_t N, int64_
     if (vec) ternarize_pack_kernel<false, true><<<grid, kPackThreads, 0, stream>>>(W, N, K, wpr, partials, pw, gamma);
     else ternarize_pack_kernel<false, false><<<grid, kPackThreads, 0, stream>>>(W, N, K, wpr, partials, pw, gamma);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_ternarize_pack(const void* W, bool w_is_f32, int64_t N, int64_t K,
+                                 uint8_t* w_packed, float* gamma, double* partials,
+                                 hipStream_t stream) {
+  const int64_t n = N * K;
+  if (w_is_f32)
+    absmean_partials_kernel<true><<<kAbsmeanBlocks, kAbsmeanThreads, 0, stream>>>(W, n, partials);
+  else
+    absmean_partials_kernel<false><<<kAbsmeanBlocks, kAbsmeanThreads, 0, stream>>>(W, n, partials);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_pack(W, w_is_f32, N, K, w_packed, gamma, partials, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Code counts ("bitlinear.py", BitLinear.ternary_stats: the share of -1, 0
+// and +1 in the current ternary weight). The two bits of each code are
+// adjacent (bits 2i, 2i+1 of a word hold one code), so with lo = the even
+// bits and hi = the odd bits of a word, +1 (01) is lo & ~hi and -1 (11) is
+// lo & hi; padding codes are 0 and count for neither. One block, a fixed
+// order: the counts are exact and repeatable.
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(1024) void code_counts_kernel(const uint32_t* __restrict__ packed, int64_t words,
+                                                           unsigned long long* __restrict__ counts) {
+  unsigned long long pos = 0, neg = 0;
+  for (int64_t i = threadIdx.x; i < words; i += 1024) {
+    const uint32_t w = packed[i];
+    const uint32_t lo = w & 0x55555555u, hi = (w >> 1) & 0x55555555u;
+    pos += __popc(lo & ~hi);
+    neg += __popc(lo & hi);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    pos += __shfl_xor(pos, off, kWave);
+    neg += __shfl_xor(neg, off, kWave);
+  }
+  __shared__ unsigned long long sp[16], sn[16];
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  if (lane == 0) {
+    sp[wave] = pos;
+    sn[wave] = neg;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long p = 0, n = 0;
+    for (int j = 0; j < 16; ++j) {
+      p += sp[j];
+      n += sn[j];
+    }
+    counts[0] = n;
+    counts[1] = p;
+  }
+}
+
+hipError_t launch_code_counts(const uint8_t* w_packed, int64_t N, int64_t K, unsigned long long* counts,
+                              hipStream_t stream) {
+  code_counts_kernel<<<1, 1024, 0, stream>>>(reinterpret_cast<const uint32_t*>(w_packed), N * (k_pad(K) / 16),
+                                             counts);
   return hipGetLastError();
 }
 
@@ -293,19 +358,19 @@ __device__ __forceinline__ uint4 load_chunk(const uint16_t* xr, int64_t ch, int6
 }
 
 // TPR threads (whole waves) per row, CPT chunks of 8 values per thread kept
-// in registers: one HBM read of x, one write of x_q.
-template <int TPR, int CPT, bool VEC>
-__global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restrict__ x, int64_t M,
-                                                        int64_t K, int64_t Kp,
-                                                        int8_t* __restrict__ xq,
-                                                        float* __restrict__ s_out) {
-  static_assert(TPR % kWave == 0 && 256 % TPR == 0, "whole waves per row");
-  constexpr int RPB = 256 / TPR;
+// in registers: one HBM read of x, one write of x_q. A block of BLOCK
+// threads holds BLOCK / TPR rows; `b` is the block's index among the
+// act-quant blocks of the launch.
+template <int BLOCK, int TPR, int CPT, bool VEC>
+__device__ __forceinline__ void act_quant_rows(const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t Kp,
+                                               int8_t* __restrict__ xq, float* __restrict__ s_out, int b) {
+  static_assert(TPR % kWave == 0 && BLOCK % TPR == 0, "whole waves per row");
+  constexpr int RPB = BLOCK / TPR;
   constexpr int WPR = TPR / kWave;
-  __shared__ float smax[256 / kWave];
+  __shared__ float smax[BLOCK / kWave];
   const int r_local = threadIdx.x / TPR;
   const int t = threadIdx.x % TPR;
-  const int64_t row = (int64_t)blockIdx.x * RPB + r_local;
+  const int64_t row = (int64_t)b * RPB + r_local;
   const bool row_ok = row < M;
   const int64_t nchunks = Kp / 8;
   const uint16_t* xr = x + row * K;
@@ -336,6 +401,14 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restri
     if (row_ok && ch < nchunks)
       *reinterpret_cast<uint2*>(xq + row * Kp + ch * 8) = quant8(v[c], r127, s);
   }
+}
+
+template <int TPR, int CPT, bool VEC>
+__global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restrict__ x, int64_t M,
+                                                        int64_t K, int64_t Kp,
+                                                        int8_t* __restrict__ xq,
+                                                        float* __restrict__ s_out) {
+  act_quant_rows<256, TPR, CPT, VEC>(x, M, K, Kp, xq, s_out, blockIdx.x);
 }
 
 // Rows longer than the register-resident variant allows: two passes over the
@@ -401,6 +474,65 @@ hipError_t launch_act_quant(const uint16_t* x, int64_t M, int64_t K, int8_t* x_q
   if (K % 8 == 0) launch_aq<true>(x, M, K, Kp, x_q, s_x, stream);
   else launch_aq<false>(x, M, K, Kp, x_q, s_x, stream);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Weight absmean partials and activation quantization in one launch. The
+// two are independent HBM streams (W, and x -> x_q, s); sharing a launch
+// lets each fill the CUs while the other ramps up or drains, and saves a
+// launch. Blocks 0 .. kAbsmeanBlocks-1 compute the absmean partials exactly
+// as absmean_partials_kernel does (same grid constants, so gamma gets the
+// same bits); the rest quantize rows, kAbsmeanThreads / TPR per block. The
+// codes are then packed by ternarize_pack_kernel, which needs every partial.
+// Used when the rows fit the register-resident layout with 16-byte loads
+// (K % 8 == 0, K <= 8192).
+// ---------------------------------------------------------------------------
+
+template <bool F32, int TPR, int CPT>
+__global__ __launch_bounds__(kAbsmeanThreads) void quant_front_kernel(
+    const void* __restrict__ w, int64_t n, double* __restrict__ partials, const uint16_t* __restrict__ x,
+    int64_t M, int64_t K, int64_t Kp, int8_t* __restrict__ xq, float* __restrict__ s_out) {
+  if (blockIdx.x < kAbsmeanBlocks)
+    absmean_block<F32>(w, n, partials, blockIdx.x);
+  else
+    act_quant_rows<kAbsmeanThreads, TPR, CPT, true>(x, M, K, Kp, xq, s_out, blockIdx.x - kAbsmeanBlocks);
+}
+
+template <bool F32, int TPR>
+static void launch_front_tpr(int cpt, const void* W, int64_t n, double* partials, const uint16_t* x, int64_t M,
+                             int64_t K, int64_t Kp, int8_t* xq, float* s, hipStream_t st) {
+  constexpr int RPB = kAbsmeanThreads / TPR;
+  const int grid = kAbsmeanBlocks + (int)((M + RPB - 1) / RPB);
+  switch (cpt) {
+#define BITNET_FRONT(C) \
+    case C: quant_front_kernel<F32, TPR, C><<<grid, kAbsmeanThreads, 0, st>>>(W, n, partials, x, M, K, Kp, xq, s); break;
+    BITNET_FRONT(1) BITNET_FRONT(2) BITNET_FRONT(3) BITNET_FRONT(4)
+    BITNET_FRONT(5) BITNET_FRONT(6) BITNET_FRONT(7)
+    default: quant_front_kernel<F32, TPR, 8><<<grid, kAbsmeanThreads, 0, st>>>(W, n, partials, x, M, K, Kp, xq, s);
+#undef BITNET_FRONT
+  }
+}
+
+hipError_t launch_quantize(const void* W, bool w_is_f32, int64_t N, int64_t K, const uint16_t* x, int64_t M,
+                           uint8_t* w_packed, float* gamma, int8_t* x_q, float* s_x, double* partials,
+                           hipStream_t stream) {
+  const int64_t Kp = k_pad(K), nchunks = Kp / 8;
+  if (K % 8 != 0 || nchunks > 128 * 8) {
+    if (hipError_t e = launch_act_quant(x, M, K, x_q, s_x, stream)) return e;
+    return launch_ternarize_pack(W, w_is_f32, N, K, w_packed, gamma, partials, stream);
+  }
+  const int64_t n = N * K;
+  if (nchunks <= 64 * 8) {
+    const int cpt = (int)((nchunks + 63) / 64);
+    if (w_is_f32) launch_front_tpr<true, 64>(cpt, W, n, partials, x, M, K, Kp, x_q, s_x, stream);
+    else launch_front_tpr<false, 64>(cpt, W, n, partials, x, M, K, Kp, x_q, s_x, stream);
+  } else {
+    const int cpt = (int)((nchunks + 127) / 128);
+    if (w_is_f32) launch_front_tpr<true, 128>(cpt, W, n, partials, x, M, K, Kp, x_q, s_x, stream);
+    else launch_front_tpr<false, 128>(cpt, W, n, partials, x, M, K, Kp, x_q, s_x, stream);
+  }
+  if (hipError_t e = hipGetLastError()) return e;
+  return launch_pack(W, w_is_f32, N, K, w_packed, gamma, partials, stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -2,6 +2,7 @@
 the layer through the C ABI (via the binding), and bring results back as
 numpy arrays. No arithmetic of the layer happens here."""
 
+import contextlib
 import sys
 
 import numpy as np
@@ -15,6 +16,18 @@ def note(msg):
     """Print and flush the case about to run on the GPU."""
     print(f"[gpu] {msg}", flush=True)
     sys.stdout.flush()
+
+
+@contextlib.contextmanager
+def knobs(**kw):
+    """Set the library's launch knobs (split_ctas, pair_cols, no_skinny,
+    spin_limit) for the body of the with-statement, then restore the
+    defaults."""
+    B.bitnet_set_test_knobs(**kw)
+    try:
+        yield
+    finally:
+        B.bitnet_set_test_knobs()
 
 
 def dev_bf16(bits):

@@ -72,18 +72,26 @@ def test_size_queries(L):
     assert L.bitnet_k_pad(0) == 0
     assert L.bitnet_ternarize_workspace_bytes(6912, 2560) >= 8 * 256
     # whole output tiles need no workspace; split tiles need tagged counters
-    # (16 bytes per tile, rounded to 256) and two 256 KiB partial tiles per
-    # workgroup of the 256-workgroup grid; dW adds its bf16 x_hat [M][Kp]
+    # (16 bytes per tile, rounded to 256) and 256 KiB partial tiles, as many
+    # as min(2G, G + T - 1) for G workgroups and T tiles; dW adds its bf16
+    # x_hat [M][Kp], dX its fp4 transposed codes [Kp][Np/2]
     assert L.bitlinear_fwd_workspace_bytes(4096, 6912, 2560) == 0
     assert L.bitlinear_fwd_workspace_bytes(64, 128, 256) == 0
     assert L.bitlinear_bwd_workspace_bytes(64, 128, 256) == 2 * 64 * 256
     tile = 64 * 256 * 16
-    # at 4096x2560->6912 the two backward products run in one launch: the
-    # fp4 transposed codes [Kp][N/2], x_hat, both products' counters and
-    # the partial tiles of their shares of the 256 workgroups
+    # at 4096x2560->6912 the two backward products run in one launch: dX
+    # stream-K over 15 columns of 8 workgroups (160 tiles on 120: 240
+    # slots), dW in whole tiles on the other 136 (no partials); plus the fp4
+    # transposed codes [Kp][N/2] and x_hat
     assert L.bitlinear_bwd_workspace_bytes(4096, 6912, 2560) == \
-        2560 * 6912 // 2 + 2 * 4096 * 2560 + 2560 + 4352 + 2 * 256 * tile
-    assert L.bitlinear_fwd_workspace_bytes(4096, 2560, 6912) == 2560 + 2 * 256 * tile
+        2560 * 6912 // 2 + 2 * 4096 * 2560 + 2560 + 240 * tile
+    # 4096x6912->2560 forward: 160 tiles of 54 stages split over 256
+    # workgroups, G + T - 1 = 415 slots
+    assert L.bitlinear_fwd_workspace_bytes(4096, 2560, 6912) == 2560 + 415 * tile
+    # few tokens: the forward needs none; the backward only its transient
+    # operands (the few-token dX and dW do not split)
+    assert L.bitlinear_fwd_workspace_bytes(32, 2560, 6912) == 0
+    assert L.bitlinear_bwd_workspace_bytes(32, 2560, 6912) == 6912 * 2560 // 2
     assert L.bitlinear_fwd_workspace_bytes(0, 4, 4) == 0
     for code in range(7):
         assert L.bitnet_status_string(code).decode().startswith("BITNET_")
@@ -173,10 +181,10 @@ def test_ttq_size_queries(L):
     # per 128 x 128 tile of dW, rounded up to 256 bytes)
     assert L.ttq_workspace_bytes(64, 128, 256) == 256
     # 4096x2560->6912: dW has 10 x 27 tiles (4 partials each); dX and dW run
-    # in one launch: both products' counters (160 and 270 tiles) and the
-    # partial tiles of their shares of the 256 workgroups
+    # in one launch planned as the BitNet pair: dX stream-K on 120
+    # workgroups (its 160 tiles' counters and 240 partial tiles), dW whole
     partials = (4 * 270 * 8 + 255) // 256 * 256
-    assert L.ttq_workspace_bytes(4096, 6912, 2560) == partials + 2560 + 4352 + 2 * 256 * tile
+    assert L.ttq_workspace_bytes(4096, 6912, 2560) == partials + 2560 + 240 * tile
     assert L.ttq_workspace_bytes(0, 4, 4) == 0
 
 

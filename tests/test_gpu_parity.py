@@ -198,12 +198,12 @@ def test_tiny_net_through_the_abi():
     (520, 1001, 263, "f32", 5),       # f32 dW, ragged tails
     (1024, 2560, 1536, "bf16", 256),  # a full grid
 ])
-def test_split_tiles_forced(M, K, N, wd, G, monkeypatch):
+def test_split_tiles_forced(M, K, N, wd, G, set_knobs):
     """Output tiles split over G workgroups (stream-K) on all three GEMMs:
     integer state and accumulators stay bit-exact, the bf16 outputs stay
     within tolerance, and a repeat gives identical bits (the partial tiles
     are added in a fixed order whatever the arrival order)."""
-    monkeypatch.setenv("BITNET_SPLIT_CTAS", str(G))
+    set_knobs(split_ctas=G)
     inp = WL.custom_inputs(M, K, N, seed=M + K + N + G, w_dtype=wd)
     note(f"split tiles G={G} M={M} K={K} N={N} W={wd}")
     g = run_layer(inp)
@@ -211,6 +211,40 @@ def test_split_tiles_forced(M, K, N, wd, G, monkeypatch):
     g2 = run_layer(inp)
     assert np.array_equal(g["acc"], g2["acc"]) and np.array_equal(g["y_bits"], g2["y_bits"])
     assert np.array_equal(g["dX"], g2["dX"]) and np.array_equal(g["dW"], g2["dW"])
+
+
+def test_split_wait_give_up_is_visible(set_knobs):
+    """A wait for another workgroup's partial tile that gives up (forced from
+    the host with a zero spin limit, so every kernel still exits normally)
+    writes its output tile as NaN and is counted by bitnet_split_timeouts;
+    tiles whose partials were all published in time are exact. With the
+    default limit the same call is exact again and counts nothing."""
+    from ternary_weight_quantization_amd import binding as B
+    M, K, N = 1024, 1024, 768
+    inp = WL.custom_inputs(M, K, N, seed=77)
+    note(f"split wait give-up M={M} K={K} N={N}")
+    B.bitnet_split_timeouts()
+    set_knobs(split_ctas=64)  # 16 dX tiles of 12 stages: 4 pieces each
+    ref = run_layer(inp, acc=False, dw=False)
+    assert B.bitnet_split_timeouts() == 0
+    set_knobs(split_ctas=64, spin_limit=0)
+    g = run_layer(inp, acc=False, dw=False)
+    count = B.bitnet_split_timeouts()
+    nan_tiles = 0
+    for mi in range(0, M, 256):
+        for ki in range(0, K, 256):
+            t = g["dX"][mi:mi + 256, ki:ki + 256]
+            if np.isnan(t).any():
+                assert np.isnan(t).all()  # the whole tile, nothing partial
+                nan_tiles += 1
+            else:
+                assert np.array_equal(t, ref["dX"][mi:mi + 256, ki:ki + 256])
+    note(f"  timeouts counted {count}, NaN dX tiles {nan_tiles}")
+    assert count >= nan_tiles
+    set_knobs(split_ctas=64)
+    g = run_layer(inp, acc=False, dw=False)
+    assert B.bitnet_split_timeouts() == 0
+    check_layer(inp, g, full=True)
 
 
 def test_determinism_repeated_calls():
@@ -271,14 +305,14 @@ def test_stack_c4_chain():
     (300, 1000, 777, 13),     # split tiles in all three GEMMs, separate launches
     (1024, 2560, 1536, None),  # dX and dW in one launch, both split
 ])
-def test_graph_replays_match_eager(M, K, N, split, monkeypatch):
+def test_graph_replays_match_eager(M, K, N, split, set_knobs):
     """The four calls captured once into a HIP graph and replayed three
     times, with eager calls on the same workspaces between the replays: each
     replay writes the eager outputs bit for bit (the split-tile counters are
     left cleared by every launch, so a replay with the captured launch tag
     counts its pieces from zero)."""
     if split is not None:
-        monkeypatch.setenv("BITNET_SPLIT_CTAS", str(split))
+        set_knobs(split_ctas=split)
     inp = WL.custom_inputs(M, K, N, seed=M + N, w_dtype="bf16")
     note(f"graph replays M={M} K={K} N={N} split={split}")
     from ternary_weight_quantization_amd import binding as B
@@ -331,7 +365,7 @@ def test_graph_replays_match_eager(M, K, N, split, monkeypatch):
     (1024, 2560, 1536, True, None),  # dX and dW in one launch, both split
     (300, 1000, 777, False, 13),     # split tiles forced
 ])
-def test_dw_sign1(M, K, N, with_dx, split, monkeypatch):
+def test_dw_sign1(M, K, N, with_dx, split, set_knobs):
     """dW as 1-bit signs (dW_dtype BITNET_SIGN1). (a) Bit for bit the signs
     of the float32 dW the same call writes with dW_dtype BITNET_F32 (same
     kernels, same summation order), padding bits 0; (b) against the
@@ -341,7 +375,7 @@ def test_dw_sign1(M, K, N, with_dx, split, monkeypatch):
     the sums; elsewhere both bits are signs of an admissible float32 sum;
     (c) a dX computed in the same call is unchanged."""
     if split is not None:
-        monkeypatch.setenv("BITNET_SPLIT_CTAS", str(split))
+        set_knobs(split_ctas=split)
     inp = WL.custom_inputs(M, K, N, seed=7 * M + N, w_dtype="bf16")
     note(f"dW sign1 M={M} K={K} N={N} dx={with_dx} split={split}")
     from ternary_weight_quantization_amd import binding as B
@@ -393,10 +427,10 @@ def test_dw_sign1(M, K, N, with_dx, split, monkeypatch):
     (64, 6912, 2560),     # the largest M of the few-token path
     (64, 64, 4096),
 ])
-def test_skinny_forward(M, K, N, monkeypatch):
+def test_skinny_forward(M, K, N, set_knobs):
     """The few-token forward (M <= 64): y and acc against the oracle (acc
     bit-exact, y within tolerance), and bit for bit the results of the
-    large-M GEMM on the same state (forced with BITNET_NO_SKINNY)."""
+    large-M GEMM on the same state (forced with the no_skinny knob)."""
     from ternary_weight_quantization_amd import binding as B
     inp = WL.custom_inputs(M, K, N, seed=3 * M + K + N)
     note(f"skinny forward M={M} K={K} N={N}")
@@ -408,7 +442,7 @@ def test_skinny_forward(M, K, N, monkeypatch):
     s_x = torch.from_numpy(g["s"]).to(dev)
     wp = torch.from_numpy(g["packed"]).to(dev)
     gamma = torch.tensor([g["gamma"]], dtype=torch.float32, device=dev)
-    monkeypatch.setenv("BITNET_NO_SKINNY", "1")
+    set_knobs(no_skinny=1)
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     acc = torch.empty((M, N), dtype=torch.int32, device=dev)
     B.bitlinear_fwd(x_q, s_x, wp, gamma, K, y, acc)
@@ -528,3 +562,45 @@ def test_layer_with_bias():
     y.backward(dy)
     ref = O.bias_grad(dy.reshape(-1, 96).float().cpu().numpy().astype(np.float64))
     C.check(L.bias.grad.float().cpu().numpy().astype(np.float64), ref, "db")
+
+
+@pytest.mark.parametrize("M,K,N,wd", [
+    (4096, 2560, 6912, "bf16"),  # the up-projection: 64 threads per row, 8 rows per block
+    (300, 6912, 264, "bf16"),    # 128 threads per row
+    (64, 256, 128, "f32"),       # f32 masters
+    (5, 1000, 33, "bf16"),       # K % 8 != 0: the separate launches
+    (3, 9000, 16, "bf16"),       # rows past the fused layout: the separate launches
+])
+def test_quantize_matches_separate_calls(M, K, N, wd):
+    """bitnet_quantize (weight absmean and activation quantization in one
+    launch, then the pack) gives the bits of bitnet_ternarize_pack +
+    bitnet_act_quant, which the oracle pins."""
+    from ternary_weight_quantization_amd import binding as B
+    from tests.gpu_util import dev_weight
+    inp = WL.custom_inputs(M, K, N, seed=3 * M + K, w_dtype=wd)
+    note(f"fused quantize M={M} K={K} N={N} W={wd}")
+    dev = torch.device("cuda")
+    Kp = B.bitnet_k_pad(K)
+    W, x = dev_weight(inp["W"]), dev_bf16(inp["x"])
+    ws = torch.empty((B.bitnet_ternarize_workspace_bytes(N, K),), dtype=torch.uint8, device=dev)
+    outs = []
+    for fused in (True, False):
+        t = dict(w_packed=torch.full((N, Kp // 4), 0x55, dtype=torch.uint8, device=dev),
+                 gamma=torch.full((1,), -1.0, dtype=torch.float32, device=dev),
+                 x_q=torch.full((M, Kp), 99, dtype=torch.int8, device=dev),
+                 s_x=torch.full((M,), -1.0, dtype=torch.float32, device=dev))
+        if fused:
+            B.bitnet_quantize(W, x, t["w_packed"], t["gamma"], t["x_q"], t["s_x"], ws)
+        else:
+            B.bitnet_ternarize_pack(W, t["w_packed"], t["gamma"], ws)
+            B.bitnet_act_quant(x, t["x_q"], t["s_x"])
+        torch.cuda.synchronize()
+        outs.append({k: v.cpu().numpy() for k, v in t.items()})
+    for k in outs[0]:
+        assert np.array_equal(outs[0][k].view(np.uint8), outs[1][k].view(np.uint8)), k
+    w = w_values(inp["W"])
+    g = O.absmean_gamma(w)
+    assert np.float32(outs[0]["gamma"][0]).view(np.uint32) == np.float32(g).view(np.uint32)
+    assert np.array_equal(outs[0]["w_packed"], O.pack_codes(O.ternary_codes(w, g), Kp))
+    x_q, s = O.act_quant(bf(inp["x"]), Kp)
+    assert np.array_equal(outs[0]["x_q"], x_q) and np.array_equal(outs[0]["s_x"].view(np.uint32), s.view(np.uint32))

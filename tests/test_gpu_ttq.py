@@ -165,14 +165,14 @@ def test_ttq_optional_outputs():
 
 
 @pytest.mark.parametrize("knob", [None, "-1"])
-def test_ttq_paired_backward(monkeypatch, knob):
+def test_ttq_paired_backward(set_knobs, knob):
     """2048 x 1024 -> 1024: dX and dW split their tiles, so they run in one
-    paired launch; BITNET_SPLIT_CTAS=-1 (a test knob) forces whole tiles,
+    paired launch; the split_ctas knob at -1 forces whole tiles,
     one product after the other. Both against the oracle."""
     if knob is not None:
-        monkeypatch.setenv("BITNET_SPLIT_CTAS", knob)
+        set_knobs(split_ctas=int(knob))
     inp = WL.custom_inputs(2048, 1024, 1024, seed=31)
-    note(f"ttq paired backward, BITNET_SPLIT_CTAS={knob}")
+    note(f"ttq paired backward, split_ctas={knob}")
     check_ttq(inp, run_ttq(inp))
 
 
@@ -254,14 +254,14 @@ def test_ttq_module():
     (300, 1000, 776, 13),      # split tiles forced, dX and dW one after the other
     (2048, 1024, 1024, None),  # dX and dW in one paired launch, both split
 ])
-def test_ttq_graph_replays_match_eager(M, K, N, split, monkeypatch):
+def test_ttq_graph_replays_match_eager(M, K, N, split, set_knobs):
     """ttq_quantize, ttq_fwd and ttq_bwd (with the scale gradients) captured
     once into a HIP graph and replayed three times, with eager calls on the
     same workspace between the replays: every replay writes the eager
     outputs bit for bit (split-tile counters are left cleared by every
     launch; the gradient partials are rewritten in full by every call)."""
     if split is not None:
-        monkeypatch.setenv("BITNET_SPLIT_CTAS", str(split))
+        set_knobs(split_ctas=split)
     from ternary_weight_quantization_amd import binding as B
     from tests.gpu_util import dev_bf16
     inp = WL.custom_inputs(M, K, N, seed=M + N + 1)
@@ -352,13 +352,13 @@ def test_ttq_fwd_codes_few_tokens(M, K, N):
 @pytest.mark.parametrize("M,K,N,knob", [
     (300, 512, 200, None),    # the GEMM route: codes expanded, then the bf16 GEMM
     (48, 1001, 130, None),    # K % 8 != 0: the GEMM route at few tokens
-    (40, 512, 264, "1"),      # BITNET_NO_SKINNY forces the GEMM route
+    (40, 512, 264, "1"),      # the no_skinny knob forces the GEMM route
 ])
-def test_ttq_fwd_codes_gemm_route_matches_ttq_fwd(M, K, N, knob, monkeypatch):
+def test_ttq_fwd_codes_gemm_route_matches_ttq_fwd(M, K, N, knob, set_knobs):
     """Through the expanded weight, ttq_fwd_codes gives ttq_fwd's bits on
     ttq_quantize's wt (the same GEMM on the same values)."""
     if knob is not None:
-        monkeypatch.setenv("BITNET_NO_SKINNY", knob)
+        set_knobs(no_skinny=int(knob))
     from ternary_weight_quantization_amd import binding as B
     from tests.gpu_util import host_bf16_bits
     note(f"ttq_fwd_codes GEMM route M={M} K={K} N={N} knob={knob}")
