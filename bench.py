@@ -4,19 +4,24 @@
                     [--rotate R] [--no-cpu-baseline]
 
 A step is the whole hot path on one batch: ternarize + pack the master
-weights, int8-quantize the activations, the INT8 forward GEMM, and the two
-bf16 STE backward GEMMs (dX and dW, one bitlinear_bwd call), all through
-the C ABI of libbitnet.so on torch's current stream. Inputs are seeded synthetic tensors of the
-4096 x 2560 -> 6912 layer (x, dY ~ N(0,1) bf16, W ~ U(+-1/sqrt(2560)) bf16),
-resident in HBM before timing starts. R independent copies of all buffers
-are rotated step by step so that the working set (~240 MB per copy) does not
-sit in the 256 MB Infinity Cache between steps.
+weights and int8-quantize the activations (one bitnet_quantize call), the
+INT8 forward GEMM, and the two bf16 STE backward GEMMs (dX and dW, one
+bitlinear_bwd call), all through the C ABI of libbitnet.so on torch's current
+stream. Inputs are seeded synthetic tensors of the 4096 x 2560 -> 6912 layer
+(x, dY ~ N(0,1) bf16, W ~ U(+-1/sqrt(2560)) bf16), resident in HBM before
+timing starts. R independent copies of all buffers are rotated step by step
+so that the working set (~240 MB per copy) does not sit in the 256 MB
+Infinity Cache between steps (the cold figure); the warm figure repeats one
+copy.
 
 Prints one JSON line: throughput in effective TOPS (6*M*N*K per step), the
-step time (replays of the step captured in HIP graphs, one per buffer set),
-per-call times from HIP events recorded on the launch stream around eager calls,
-the roofline of the dominant kernel, and the CPU oracle timed on a bounded
-sample of the same workload (rank 0 only).
+step time (replays of the step captured in HIP graphs), per-call times (the
+median of `steps` eager calls timed with HIP events on the launch stream),
+each call's fraction of the published peak and of the ceiling measured in
+the same run (a plain device copy; register-only MFMA chains), the combined
+GEMM fraction of the MFMA peak, the same summary for the other layer
+workloads and the 8-layer stack (with its peak allocated bytes), and the CPU
+oracle timed on a bounded sample of the headline workload.
 """
 
 import argparse
@@ -41,6 +46,8 @@ PAGES_L4_TOPS = 49.4
 HEADLINE = "c2_up_4096x2560x6912"
 
 KERNEL_SOURCES = ["gemm_kernels.hip", "skinny_kernels.hip", "quant_kernels.hip", "device_common.h"]
+# the other layer workloads reported in the same line, and the 8-layer stack
+OTHER_WORKLOADS = ["c1_small", "c3_down_4096x6912x2560", "c5_skinny_32x6912x2560"]
 
 
 def parse():
@@ -51,6 +58,8 @@ def parse():
     p.add_argument("--workload", default=HEADLINE)
     p.add_argument("--rotate", type=int, default=4)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--only-headline", action="store_true",
+                   help="skip the other workloads and the stack (e.g. under a profiler)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain device copy of known size (for counter calibration)")
     p.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR"),
@@ -61,8 +70,7 @@ def parse():
 
 # bench kernel name -> substrings of the device kernel names it launches
 KERNEL_MATCH = {
-    "ternarize_pack": ["absmean_partials_kernel", "ternarize_pack_kernel"],
-    "act_quant": ["act_quant"],
+    "quantize": ["quant_front_kernel", "ternarize_pack_kernel"],
     "fwd_i8": ["MfmaI8"],
     "bwd_bf16": ["bwd_prep_kernel", "wt_fp4_kernel", "xhat_kernel", "gemm_pair_kernel"],
 }
@@ -228,6 +236,340 @@ def cpu_baseline(inp, target_s=12.0, chunk=256):
     }
 
 
+def _median_ms(evs):
+    import numpy as np
+
+    return float(np.median([a.elapsed_time(b) for a, b in evs]))
+
+
+def measure_ceilings(dev):
+    """Ceilings measured in the same run: a plain 256 MiB device copy (HBM
+    read + write) and the MFMA probe (register-only chains on every SIMD)
+    for bf16 and int8; medians of 5 timed launches after 2 untimed."""
+    import torch
+
+    from ternary_weight_quantization_amd import binding as B
+
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+
+    def timed(f, n=5, warm=2):
+        for _ in range(warm):
+            f()
+        evs = []
+        for _ in range(n):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            f()
+            b.record()
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        return _median_ms(evs)
+
+    copy_ms = timed(lambda: dst.copy_(src))
+    sink = torch.zeros((2048,), dtype=torch.float32, device=dev)
+    out = {"copy_GBps": round(2 * COPY_BYTES / (copy_ms * 1e-3) / 1e9, 1)}
+    for name, i8 in (("bf16_TFLOPs", False), ("int8_TOPs", True)):
+        ops = B.bitnet_debug_mfma_probe(i8, 4000, sink)
+        ms = timed(lambda: B.bitnet_debug_mfma_probe(i8, 4000, sink))
+        out[name] = round(ops / (ms * 1e-3) / 1e12, 1)
+    del src, dst
+    torch.cuda.synchronize()
+    return out
+
+
+def _to_dev(a, dtype, dev):
+    import numpy as np
+    import torch
+
+    if dtype == torch.bfloat16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def layer_bench(inp, steps, warmup, rotate, dev, extra=False):
+    """One layer workload: per-call medians, the step time from graph
+    replays over `rotate` buffer sets (cold) and over one set (warm)."""
+    import numpy as np
+    import torch
+
+    from ternary_weight_quantization_amd import binding as B
+
+    M, K, N = inp["M"], inp["K"], inp["N"]
+    Kp = B.bitnet_k_pad(K)
+    wdt = torch.bfloat16 if inp["w_dtype"] == "bf16" else torch.float32
+    base = dict(x=_to_dev(inp["x"], torch.bfloat16, dev), W=_to_dev(inp["W"], wdt, dev),
+                dY=_to_dev(inp["dY"], torch.bfloat16, dev))
+    sets = []
+    for _ in range(rotate):
+        s = {k: v.clone() for k, v in base.items()}
+        s.update(
+            w_packed=torch.empty((N, Kp // 4), dtype=torch.uint8, device=dev),
+            gamma=torch.empty((1,), dtype=torch.float32, device=dev),
+            ws=torch.empty((B.bitnet_ternarize_workspace_bytes(N, K),), dtype=torch.uint8, device=dev),
+            x_q=torch.empty((M, Kp), dtype=torch.int8, device=dev),
+            s_x=torch.empty((M,), dtype=torch.float32, device=dev),
+            y=torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+            dX=torch.empty((M, K), dtype=torch.bfloat16, device=dev),
+            dW=torch.empty((N, K), dtype=wdt, device=dev),
+        )
+        sets.append(s)
+    del base
+    torch.cuda.synchronize()
+
+    calls = {
+        "quantize": lambda s: B.bitnet_quantize(s["W"], s["x"], s["w_packed"], s["gamma"], s["x_q"], s["s_x"], s["ws"]),
+        "fwd_i8": lambda s: B.bitlinear_fwd(s["x_q"], s["s_x"], s["w_packed"], s["gamma"], K, s["y"]),
+        "bwd_bf16": lambda s: B.bitlinear_bwd(s["dY"], s["x_q"], s["s_x"], s["w_packed"], s["gamma"], K,
+                                              dX=s["dX"], dW=s["dW"]),
+    }
+    names = list(calls)
+
+    def step(s, ev=None):
+        for i, n in enumerate(names):
+            if ev is not None:
+                ev[i][0].record()
+            calls[n](s)
+            if ev is not None:
+                ev[i][1].record()
+
+    for i in range(warmup):
+        step(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in names]
+           for _ in range(steps)]
+    for i in range(steps):
+        step(sets[i % len(sets)], evs[i])
+    torch.cuda.synchronize()
+    per_call = {n: _median_ms([tuple(evs[i][j]) for i in range(steps)]) for j, n in enumerate(names)}
+    per_call_mean = {n: float(np.mean([evs[i][j][0].elapsed_time(evs[i][j][1]) for i in range(steps)]))
+                     for j, n in enumerate(names)}
+
+    # Step time: graph replays (host call overhead out of the timed region;
+    # the same kernels and work as the eager step). One graph holds a step
+    # on each buffer set in turn (a training loop captures many layers in
+    # one graph); every replay is first checked against the eager outputs.
+    outs = ("y", "dX", "dW", "x_q", "w_packed")
+    ref = [{k: s[k].clone() for k in outs} for s in sets]
+
+    def graph_of(ss):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for s in ss:
+                step(s)
+        return g
+
+    def replay_ms(g, per_graph, n_steps):
+        reps = max(1, n_steps // per_graph)
+        for _ in range(max(1, warmup // per_graph)):
+            g.replay()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / (reps * per_graph)
+
+    cold = graph_of(sets)
+    for s in sets:
+        for k in ("y", "dX", "dW"):
+            s[k].zero_()
+    cold.replay()
+    torch.cuda.synchronize()
+    for i, s in enumerate(sets):
+        for k in outs:
+            if not torch.equal(s[k], ref[i][k]):
+                raise SystemExit(f"bench.py: graph replay differs from the eager step in {k} (set {i})")
+    cold_ms = replay_ms(cold, len(sets), steps)
+    warm = graph_of([sets[0]] * 4)
+    warm_ms = replay_ms(warm, 4, steps)
+    del cold, warm
+    out = dict(M=M, K=K, N=N, w_dtype=inp["w_dtype"], per_call=per_call, per_call_mean=per_call_mean,
+               ms_per_step=cold_ms, ms_per_step_warm=warm_ms, sets=sets)
+    if extra:
+        # the separate quantization entry points (their own rows), per call
+        ex = {
+            "ternarize_pack": lambda s: B.bitnet_ternarize_pack(s["W"], s["w_packed"], s["gamma"], s["ws"]),
+            "act_quant": lambda s: B.bitnet_act_quant(s["x"], s["x_q"], s["s_x"]),
+        }
+        out["per_call"].update({n: per_call_ms(f, sets, steps, warmup) for n, f in ex.items()})
+    if not extra:
+        del out["sets"]
+    return out
+
+
+def per_call_ms(f, sets, steps, warmup):
+    import torch
+
+    for i in range(warmup):
+        f(sets[i % len(sets)])
+    evs = []
+    for i in range(steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        f(sets[i % len(sets)])
+        b.record()
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    return _median_ms(evs)
+
+
+def layer_roofline(r, ceil):
+    """Per-call rates against the published peaks and the measured ceilings."""
+    M, K, N = r["M"], r["K"], r["N"]
+    Kp = (K + 63) // 64 * 64
+    w_bytes = 2 if r["w_dtype"] == "bf16" else 4
+    gemm = 2.0 * M * N * K
+    tern_b = 2 * w_bytes * N * K + N * Kp / 4
+    aq_b = 2.0 * M * K + M * Kp + 4 * M
+    work = {
+        "quantize": ("hbm", (tern_b + aq_b) / 1e9, PEAK_HBM_GBS, ceil["copy_GBps"], "GB/s"),
+        "fwd_i8": ("mfma", gemm / 1e12, PEAK_INT8_TOPS, ceil["int8_TOPs"], "TOP/s"),
+        "bwd_bf16": ("mfma", 2 * gemm / 1e12, PEAK_BF16_TFLOPS, ceil["bf16_TFLOPs"], "TFLOP/s"),
+        "ternarize_pack": ("hbm", tern_b / 1e9, PEAK_HBM_GBS, ceil["copy_GBps"], "GB/s"),
+        "act_quant": ("hbm", aq_b / 1e9, PEAK_HBM_GBS, ceil["copy_GBps"], "GB/s"),
+    }
+    out = {}
+    for n, ms in r["per_call"].items():
+        bound, w, peak, meas, unit = work[n]
+        ach = w / (ms * 1e-3)
+        out[n] = {"ms": round(ms, 4), "bound": bound, "achieved": round(ach, 2), "unit": unit,
+                  "frac": round(ach / peak, 4), "frac_of_measured": round(ach / meas, 4)}
+    t = r["per_call"]["fwd_i8"] + r["per_call"]["bwd_bf16"]
+    # the survey's combined figure: ideal GEMM time at the dtype peaks / measured GEMM time
+    ideal = gemm / (PEAK_INT8_TOPS * 1e12) + 2 * gemm / (PEAK_BF16_TFLOPS * 1e12)
+    ideal_meas = gemm / (ceil["int8_TOPs"] * 1e12) + 2 * gemm / (ceil["bf16_TFLOPs"] * 1e12)
+    return out, round(ideal / (t * 1e-3), 4), round(ideal_meas / (t * 1e-3), 4)
+
+
+def stack_bench(steps, warmup, dev):
+    """The 8-layer 2560 <-> 6912 stack at 4x512 tokens: step time of the
+    forward chain (bitnet_quantize + bitlinear_fwd per layer, each layer's
+    bf16 output the next one's input) and the STE backward chain (one
+    bitlinear_bwd per layer, dX feeding the previous layer) as graph replays
+    through the C ABI; and the peak allocated bytes of one forward + backward
+    of the training module (QATBitLinear, bf16 masters, no retained
+    activations) from a reset of torch's peak statistics."""
+    import torch
+
+    from ternary_weight_quantization_amd import binding as B
+    from ternary_weight_quantization_amd import layer as LY
+    from ternary_weight_quantization_amd import workloads as WL
+
+    d = WL.stack_inputs(seed=0)
+    M, dims = d["M"], d["dims"]
+    L = len(dims) - 1
+    Ws = [_to_dev(w, torch.bfloat16, dev) for w in d["Ws"]]
+    x0 = _to_dev(d["x"], torch.bfloat16, dev)
+    dY = _to_dev(d["dY"], torch.bfloat16, dev)
+    st = []
+    for i in range(L):
+        K, N = dims[i], dims[i + 1]
+        Kp = B.bitnet_k_pad(K)
+        st.append(dict(K=K, N=N, w_packed=torch.empty((N, Kp // 4), dtype=torch.uint8, device=dev),
+                       gamma=torch.empty((1,), dtype=torch.float32, device=dev),
+                       ws=torch.empty((B.bitnet_ternarize_workspace_bytes(N, K),), dtype=torch.uint8, device=dev),
+                       x_q=torch.empty((M, Kp), dtype=torch.int8, device=dev),
+                       s_x=torch.empty((M,), dtype=torch.float32, device=dev),
+                       y=torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+                       dX=torch.empty((M, K), dtype=torch.bfloat16, device=dev),
+                       dW=torch.empty((N, K), dtype=torch.bfloat16, device=dev)))
+
+    def step():
+        a = x0
+        for i, s in enumerate(st):
+            B.bitnet_quantize(Ws[i], a, s["w_packed"], s["gamma"], s["x_q"], s["s_x"], s["ws"])
+            B.bitlinear_fwd(s["x_q"], s["s_x"], s["w_packed"], s["gamma"], s["K"], s["y"])
+            a = s["y"]
+        g = dY
+        for i in range(L - 1, -1, -1):
+            s = st[i]
+            B.bitlinear_bwd(g, s["x_q"], s["s_x"], s["w_packed"], s["gamma"], s["K"], dX=s["dX"], dW=s["dW"])
+            g = s["dX"]
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ref = [(s["y"].clone(), s["dX"].clone(), s["dW"].clone()) for s in st]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for s in st:
+        s["y"].zero_()
+        s["dX"].zero_()
+    g.replay()
+    torch.cuda.synchronize()
+    for i, s in enumerate(st):
+        if not (torch.equal(s["y"], ref[i][0]) and torch.equal(s["dX"], ref[i][1]) and torch.equal(s["dW"], ref[i][2])):
+            raise SystemExit(f"bench.py: stack graph replay differs from the eager step (layer {i})")
+    for _ in range(max(1, warmup)):
+        g.replay()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(steps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    ops = sum(6.0 * M * dims[i] * dims[i + 1] for i in range(L))
+    del g, st, Ws, ref
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+    # peak memory of the training module's forward + backward
+    layers = [LY.QATBitLinear(dims[i], dims[i + 1], device=dev) for i in range(L)]
+    with torch.no_grad():
+        for lay, w in zip(layers, d["Ws"]):
+            lay.weight.copy_(_to_dev(w, torch.bfloat16, dev))
+    for lay in layers:  # warm the caching allocator and the library once
+        lay.weight.grad = None
+    h = x0
+    for lay in layers:
+        h = lay(h)
+    h.backward(dY)
+    for lay in layers:
+        lay.weight.grad = None
+    del h
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    before = torch.cuda.memory_allocated()
+    h = x0
+    for lay in layers:
+        h = lay(h)
+    after_fwd = torch.cuda.memory_allocated()
+    h.backward(dY)
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated()
+    masters = sum(lay.weight.numel() * lay.weight.element_size() for lay in layers)
+    saved = sum(M * B.bitnet_k_pad(dims[i]) + 4 * M + dims[i + 1] * B.bitnet_k_pad(dims[i]) // 4 + 4
+                for i in range(L))
+    ws_max = max(max(B.bitlinear_fwd_workspace_bytes(M, dims[i + 1], dims[i]),
+                     B.bitlinear_bwd_workspace_bytes(M, dims[i + 1], dims[i])) for i in range(L))
+    out = {
+        "workload": f"stack_8x_{dims[0]}_{dims[1]}_M{M}",
+        "ms_per_step": round(ms, 4),
+        "tops": round(ops / (ms * 1e-3) / 1e12, 2),
+        "peak_allocated_bytes": int(peak),
+        "peak_allocated_MB": round(peak / 1e6, 1),
+        "breakdown_MB": {
+            "before_step (bf16 masters, x, dY)": round(before / 1e6, 1),
+            "masters": round(masters / 1e6, 1),
+            "grads (bf16, as the masters)": round(masters / 1e6, 1),
+            "saved state after the forward (int8 x_q + s, 2-bit codes + gamma)": round(saved / 1e6, 1),
+            "allocated after the forward": round(after_fwd / 1e6, 1),
+            "largest library workspace of one call": round(ws_max / 1e6, 1),
+        },
+        "pages_peak_MB": {"fused": 1151, "eager": 1887},
+    }
+    del layers, h
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.summarize_pmc:
@@ -247,7 +589,6 @@ def main():
         copy_calibration()
         return
 
-    import numpy as np
     import torch
 
     from ternary_weight_quantization_amd import binding as B
@@ -255,206 +596,79 @@ def main():
 
     B.lib()
     dev = torch.device("cuda:0")
+    ceil = measure_ceilings(dev)
     inp = WL.layer_inputs(args.workload, seed=0)
     M, K, N = inp["M"], inp["K"], inp["N"]
     Kp = B.bitnet_k_pad(K)
+    r = layer_bench(inp, args.steps, args.warmup, args.rotate, dev, extra=True)
+    sets = r.pop("sets")
+    kernels, gemm_frac, gemm_frac_meas = layer_roofline(r, ceil)
     wdt = torch.bfloat16 if inp["w_dtype"] == "bf16" else torch.float32
 
-    def to_dev(a, dtype):
-        if dtype == torch.bfloat16:
-            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
-        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
-
-    sets = []
-    base = dict(x=to_dev(inp["x"], torch.bfloat16), W=to_dev(inp["W"], wdt), dY=to_dev(inp["dY"], torch.bfloat16))
-    for r in range(args.rotate):
-        s = {k: v.clone() for k, v in base.items()}
-        s.update(
-            w_packed=torch.empty((N, Kp // 4), dtype=torch.uint8, device=dev),
-            gamma=torch.empty((1,), dtype=torch.float32, device=dev),
-            ws=torch.empty((B.bitnet_ternarize_workspace_bytes(N, K),), dtype=torch.uint8, device=dev),
-            x_q=torch.empty((M, Kp), dtype=torch.int8, device=dev),
-            s_x=torch.empty((M,), dtype=torch.float32, device=dev),
-            y=torch.empty((M, N), dtype=torch.bfloat16, device=dev),
-            dX=torch.empty((M, K), dtype=torch.bfloat16, device=dev),
-            dW=torch.empty((N, K), dtype=wdt, device=dev),
-        )
-        sets.append(s)
-    del base
-    torch.cuda.synchronize()
-
-    names = ["ternarize_pack", "act_quant", "fwd_i8", "bwd_bf16"]
-
-    def step(s, ev=None):
-        calls = [
-            lambda: B.bitnet_ternarize_pack(s["W"], s["w_packed"], s["gamma"], s["ws"]),
-            lambda: B.bitnet_act_quant(s["x"], s["x_q"], s["s_x"]),
-            lambda: B.bitlinear_fwd(s["x_q"], s["s_x"], s["w_packed"], s["gamma"], K, s["y"]),
-            lambda: B.bitlinear_bwd(s["dY"], s["x_q"], s["s_x"], s["w_packed"], s["gamma"], K, dX=s["dX"], dW=s["dW"]),
-        ]
-        for i, c in enumerate(calls):
-            if ev is not None:
-                ev[i][0].record()
-            c()
-            if ev is not None:
-                ev[i][1].record()
-
-    for i in range(args.warmup):
-        step(sets[i % len(sets)])
-    torch.cuda.synchronize()
-
-    # Per-call times: eager steps with HIP events around each call, on the
-    # stream the library launches on.
-    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in names]
-           for _ in range(args.steps)]
-    for i in range(args.steps):
-        step(sets[i % len(sets)], evs[i])
-    torch.cuda.synchronize()
-    per_kernel = {n: float(np.mean([evs[i][j][0].elapsed_time(evs[i][j][1]) for i in range(args.steps)]))
-                  for j, n in enumerate(names)}
-
-    # Step time: graph replays, so that host-side call overhead stays out of
-    # the timed region (the same kernels and work as the eager step). When
-    # the step count is a multiple of the number of buffer sets, one graph
-    # holds one step on each set in turn (a training loop captures many
-    # layers in one graph, and this keeps the per-launch gap of a graph out
-    # of every step); otherwise each set's step is its own graph. Every
-    # replay pattern is first checked to reproduce the eager outputs bit for
-    # bit.
-    outs = ("y", "dX", "dW")
-    ref = [{k: s[k].clone() for k in outs} for s in sets]
-    R = len(sets)
-    chained = args.steps % R == 0
-    graphs = []
-    if chained:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for s in sets:
-                step(s)
-        graphs.append(g)
-    else:
-        for s in sets:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                step(s)
-            graphs.append(g)
-    for s in sets:
-        for k in outs:
-            s[k].zero_()
-    for g in graphs:
-        g.replay()
-    torch.cuda.synchronize()
-    for i, s in enumerate(sets):
-        for k in outs:
-            if not torch.equal(s[k], ref[i][k]):
-                raise SystemExit(f"bench.py: graph replay differs from the eager step in {k} (set {i})")
-    replays = args.steps // R if chained else args.steps
-    for i in range(max(1, args.warmup // R) if chained else args.warmup):
-        graphs[i % len(graphs)].replay()
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record()
-    for i in range(replays):
-        graphs[i % len(graphs)].replay()
-    t_end.record()
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms_per_step = total_ms / args.steps
-
-    # The backward with dW as 1-bit signs for a sign-based optimiser (dX and
-    # the dW signs in one call; no bf16 dW is written), timed per call like
-    # the step's calls. Not part of the step.
+    # Calls outside the step, timed per call the same way (medians).
     for s in sets:
         s["dW_sign1"] = torch.empty((N, Kp // 8), dtype=torch.uint8, device=dev)
-
-    def bwd_sign1(s):
-        B.bitlinear_bwd(s["dY"], s["x_q"], s["s_x"], s["w_packed"], s["gamma"], K, dX=s["dX"], dW=s["dW_sign1"])
-
-    # The forward with a bias and the bias gradient (the layer's optional
-    # bias), timed the same way; not part of the step.
-    for s in sets:
         s["bias"] = torch.zeros((N,), dtype=torch.bfloat16, device=dev)
         s["db"] = torch.empty((N,), dtype=torch.float32, device=dev)
-
-    def fwd_bias(s):
-        B.bitlinear_fwd(s["x_q"], s["s_x"], s["w_packed"], s["gamma"], K, s["y"], bias=s["bias"])
-
-    def bias_grad(s):
-        B.bitlinear_bias_grad(s["dY"], s["db"])
-
-    # The TTQ variant on the same shape ("TTQ_VERIFICATION.md": bf16
-    # activations, a bf16 weight of {Wp, 0, -Wn}): quantize, forward, and the
-    # backward with dX, dW and the two scale gradients; parameters from its
-    # initialization. Timed the same way; not part of the step.
-    for s in sets:
         s["ttq_params"] = torch.empty((3,), dtype=torch.float32, device=dev)
         B.ttq_init(s["W"], s["ttq_params"], s["ws"])
         s["ttq_codes"] = torch.empty((N, Kp // 4), dtype=torch.uint8, device=dev)
         s["ttq_wt"] = torch.empty((N, Kp), dtype=torch.bfloat16, device=dev)
         s["ttq_grads"] = torch.empty((2,), dtype=torch.float32, device=dev)
     ttq_ws = torch.empty((max(B.ttq_workspace_bytes(M, N, K), 1),), dtype=torch.uint8, device=dev)
-
-    def ttq_quantize(s):
-        B.ttq_quantize(s["W"], s["ttq_params"], s["ttq_codes"], s["ttq_wt"])
-
-    def ttq_fwd(s):
-        B.ttq_fwd(s["x"], s["ttq_wt"], s["y"], workspace=ttq_ws)
-
-    # the forward from the stored codes and params (the exported state): the
-    # few-token kernel at M <= 64, else the codes expanded and the GEMM
     ttq_codes_ws = torch.empty((max(B.ttq_fwd_codes_workspace_bytes(M, N, K), 1),), dtype=torch.uint8, device=dev)
-
-    def ttq_fwd_codes(s):
-        B.ttq_fwd_codes(s["x"], s["ttq_codes"], s["ttq_params"], s["y"], workspace=ttq_codes_ws)
-
-    def ttq_bwd(s):
-        B.ttq_bwd(s["dY"], s["x"], s["ttq_wt"], s["ttq_codes"], K, dX=s["dX"], dW=s["dW"], grads=s["ttq_grads"],
-                  workspace=ttq_ws)
-
-    def per_call_ms(f):
-        for i in range(args.warmup):
-            f(sets[i % len(sets)])
-        ev1 = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-               for _ in range(args.steps)]
-        for i in range(args.steps):
-            ev1[i][0].record()
-            f(sets[i % len(sets)])
-            ev1[i][1].record()
-        torch.cuda.synchronize()
-        return float(np.mean([a.elapsed_time(b) for a, b in ev1]))
-
-    sign1_ms = per_call_ms(bwd_sign1)
-    fwd_bias_ms = per_call_ms(fwd_bias)
-    bias_grad_ms = per_call_ms(bias_grad)
-    ttq_quantize(sets[0])
+    for s in sets:
+        B.ttq_quantize(s["W"], s["ttq_params"], s["ttq_codes"], s["ttq_wt"])
     torch.cuda.synchronize()
-    ttq_ms = {n: per_call_ms(f) for n, f in (("quantize", ttq_quantize), ("fwd", ttq_fwd), ("bwd", ttq_bwd),
-                                              ("fwd_codes", ttq_fwd_codes))}
+    xc = {
+        # the backward with dW as 1-bit signs for a sign-based optimiser
+        "bwd_sign1": lambda s: B.bitlinear_bwd(s["dY"], s["x_q"], s["s_x"], s["w_packed"], s["gamma"], K,
+                                               dX=s["dX"], dW=s["dW_sign1"]),
+        # the layer's optional bias
+        "fwd_bias": lambda s: B.bitlinear_fwd(s["x_q"], s["s_x"], s["w_packed"], s["gamma"], K, s["y"],
+                                              bias=s["bias"]),
+        "bias_grad": lambda s: B.bitlinear_bias_grad(s["dY"], s["db"]),
+        # the TTQ variant on the same shape, parameters from its initialization
+        "ttq_quantize": lambda s: B.ttq_quantize(s["W"], s["ttq_params"], s["ttq_codes"], s["ttq_wt"]),
+        "ttq_fwd": lambda s: B.ttq_fwd(s["x"], s["ttq_wt"], s["y"], workspace=ttq_ws),
+        "ttq_fwd_codes": lambda s: B.ttq_fwd_codes(s["x"], s["ttq_codes"], s["ttq_params"], s["y"],
+                                                   workspace=ttq_codes_ws),
+        "ttq_bwd": lambda s: B.ttq_bwd(s["dY"], s["x"], s["ttq_wt"], s["ttq_codes"], K, dX=s["dX"], dW=s["dW"],
+                                       grads=s["ttq_grads"], workspace=ttq_ws),
+    }
+    xms = {n: per_call_ms(f, sets, args.steps, args.warmup) for n, f in xc.items()}
+    del sets
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
 
     gemm_ops = 2.0 * M * N * K
-    tops = 3 * gemm_ops / (ms_per_step * 1e-3) / 1e12
-    # roofline of each kernel (algorithmic work per launch)
     w_bytes = 2 if wdt == torch.bfloat16 else 4
-    roof = {
-        "fwd_i8": ("mfma", gemm_ops / 1e12, PEAK_INT8_TOPS, "TOP/s"),
-        # dX and dW in one call (two products)
-        "bwd_bf16": ("mfma", 2 * gemm_ops / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"),
-        # two reads of W plus the 2-bit write
-        "ternarize_pack": ("hbm", (2 * w_bytes * N * K + N * Kp / 4) / 1e9, PEAK_HBM_GBS, "GB/s"),
-        # read x (bf16), write x_q (int8, padded) and s
-        "act_quant": ("hbm", (2.0 * M * K + M * Kp + 4 * M) / 1e9, PEAK_HBM_GBS, "GB/s"),
+
+    def rate(ms, work, peak, bound, unit, **kw):
+        ach = work / (ms * 1e-3)
+        return dict(ms=round(ms, 4), bound=bound, unit=unit, achieved=round(ach, 2), frac=round(ach / peak, 4), **kw)
+
+    extra_calls = {
+        "bwd_sign1": rate(xms["bwd_sign1"], 2 * gemm_ops / 1e12, PEAK_BF16_TFLOPS, "mfma", "TFLOP/s",
+                          dW_bytes_written=N * Kp // 8),
+        "fwd_bias": rate(xms["fwd_bias"], gemm_ops / 1e12, PEAK_INT8_TOPS, "mfma", "TOP/s"),
+        "bias_grad": rate(xms["bias_grad"], (2.0 * M * N + 4 * N) / 1e9, PEAK_HBM_GBS, "hbm", "GB/s"),
+        # read W, write the codes and the bf16 weight
+        "ttq_quantize": rate(xms["ttq_quantize"], (w_bytes * N * K + N * Kp / 4 + 2 * N * Kp) / 1e9, PEAK_HBM_GBS,
+                             "hbm", "GB/s"),
+        "ttq_fwd": rate(xms["ttq_fwd"], gemm_ops / 1e12, PEAK_BF16_TFLOPS, "mfma", "TFLOP/s"),
+        "ttq_fwd_codes": rate(xms["ttq_fwd_codes"], gemm_ops / 1e12, PEAK_BF16_TFLOPS, "mfma", "TFLOP/s"),
+        "ttq_bwd": rate(xms["ttq_bwd"], 2 * gemm_ops / 1e12, PEAK_BF16_TFLOPS, "mfma", "TFLOP/s"),
     }
-    fracs = {}
-    for n, (bound, work, peak, unit) in roof.items():
-        achieved = work / (per_kernel[n] * 1e-3)
-        fracs[n] = dict(bound=bound, achieved=achieved, peak=peak, unit=unit, frac=achieved / peak,
-                        ms=per_kernel[n])
-    dom = max(per_kernel, key=per_kernel.get)
-    d = fracs[dom]
-    traffic = load_traffic(dom, args.workload)
-    roofline = {"kernel": dom, "bound": d["bound"], "achieved": round(d["achieved"], 3), "peak": d["peak"],
-                "unit": d["unit"], "frac": round(d["frac"], 4), "traffic": traffic}
+
+    ms_per_step = r["ms_per_step"]
+    tops = 3 * gemm_ops / (ms_per_step * 1e-3) / 1e12
+    step_calls = ("quantize", "fwd_i8", "bwd_bf16")
+    dom = max(step_calls, key=lambda n: kernels[n]["ms"])
+    d = kernels[dom]
+    peak = {"quantize": PEAK_HBM_GBS, "fwd_i8": PEAK_INT8_TOPS, "bwd_bf16": PEAK_BF16_TFLOPS}[dom]
+    roofline = {"kernel": dom, "bound": d["bound"], "achieved": d["achieved"], "peak": peak, "unit": d["unit"],
+                "frac": d["frac"], "traffic": load_traffic(dom, args.workload)}
 
     out = {
         "metric": METRIC if args.workload == HEADLINE else METRIC.replace("4096×2560→6912", f"{M}×{K}→{N}"),
@@ -473,45 +687,44 @@ def main():
         "config": {"workload": f"bitlinear_fwd_bwd_{M}x{K}x{N}", "M": M, "K": K, "N": N,
                    "w_dtype": inp["w_dtype"], "rotating_buffer_sets": args.rotate},
         "roofline": roofline,
-        "kernels": {n: {"ms": round(f["ms"], 4), "frac": round(f["frac"], 4), "bound": f["bound"],
-                        "achieved": round(f["achieved"], 2), "unit": f["unit"]} for n, f in fracs.items()},
-        "extra_calls": {"bwd_sign1": {
-            "ms": round(sign1_ms, 4), "bound": "mfma", "unit": "TFLOP/s",
-            "achieved": round(2 * gemm_ops / 1e12 / (sign1_ms * 1e-3), 2),
-            "frac": round(2 * gemm_ops / 1e12 / (sign1_ms * 1e-3) / PEAK_BF16_TFLOPS, 4),
-            "dW_bytes_written": N * Kp // 8},
-            "fwd_bias": {
-                "ms": round(fwd_bias_ms, 4), "bound": "mfma", "unit": "TOP/s",
-                "achieved": round(gemm_ops / 1e12 / (fwd_bias_ms * 1e-3), 2),
-                "frac": round(gemm_ops / 1e12 / (fwd_bias_ms * 1e-3) / PEAK_INT8_TOPS, 4)},
-            "bias_grad": {
-                "ms": round(bias_grad_ms, 4), "bound": "hbm", "unit": "GB/s",
-                "achieved": round((2.0 * M * N + 4 * N) / 1e9 / (bias_grad_ms * 1e-3), 2),
-                "frac": round((2.0 * M * N + 4 * N) / 1e9 / (bias_grad_ms * 1e-3) / PEAK_HBM_GBS, 4)},
-            # read W, write the codes and the bf16 weight
-            "ttq_quantize": {
-                "ms": round(ttq_ms["quantize"], 4), "bound": "hbm", "unit": "GB/s",
-                "achieved": round((w_bytes * N * K + N * Kp / 4 + 2 * N * Kp) / 1e9 / (ttq_ms["quantize"] * 1e-3), 2),
-                "frac": round((w_bytes * N * K + N * Kp / 4 + 2 * N * Kp) / 1e9 / (ttq_ms["quantize"] * 1e-3)
-                              / PEAK_HBM_GBS, 4)},
-            "ttq_fwd": {
-                "ms": round(ttq_ms["fwd"], 4), "bound": "mfma", "unit": "TFLOP/s",
-                "achieved": round(gemm_ops / 1e12 / (ttq_ms["fwd"] * 1e-3), 2),
-                "frac": round(gemm_ops / 1e12 / (ttq_ms["fwd"] * 1e-3) / PEAK_BF16_TFLOPS, 4)},
-            # rate on the forward's flops; at few tokens the bound is reading
-            # the codes (N * Kp / 4 bytes) and x
-            "ttq_fwd_codes": {
-                "ms": round(ttq_ms["fwd_codes"], 4), "bound": "mfma", "unit": "TFLOP/s",
-                "achieved": round(gemm_ops / 1e12 / (ttq_ms["fwd_codes"] * 1e-3), 2),
-                "frac": round(gemm_ops / 1e12 / (ttq_ms["fwd_codes"] * 1e-3) / PEAK_BF16_TFLOPS, 4),
-                "codes_GB_per_s": round((N * Kp / 4 + 2.0 * M * K + 2.0 * M * N) / 1e9 / (ttq_ms["fwd_codes"] * 1e-3),
-                                        2)},
-            "ttq_bwd": {
-                "ms": round(ttq_ms["bwd"], 4), "bound": "mfma", "unit": "TFLOP/s",
-                "achieved": round(2 * gemm_ops / 1e12 / (ttq_ms["bwd"] * 1e-3), 2),
-                "frac": round(2 * gemm_ops / 1e12 / (ttq_ms["bwd"] * 1e-3) / PEAK_BF16_TFLOPS, 4)}},
+        "ms_per_step_warm": round(r["ms_per_step_warm"], 4),
+        "gemm_mfma_frac": gemm_frac,
+        "gemm_mfma_frac_of_measured": gemm_frac_meas,
+        "measured_ceilings": ceil,
+        "kernels": kernels,
+        "per_call_mean_ms": {n: round(v, 4) for n, v in r["per_call_mean"].items()},
+        "extra_calls": extra_calls,
         "cpu_baseline": None,
     }
+
+    if not args.only_headline:
+        configs = {}
+        for name in OTHER_WORKLOADS:
+            ci = WL.layer_inputs(name, seed=0)
+            cr = layer_bench(ci, args.steps, args.warmup, 4 if ci["M"] * ci["K"] < 1 << 24 else 2, dev)
+            ck, cf, cfm = layer_roofline(cr, ceil)
+            cM, cK, cN = cr["M"], cr["K"], cr["N"]
+            e = {"ms_per_step": round(cr["ms_per_step"], 4), "ms_per_step_warm": round(cr["ms_per_step_warm"], 4),
+                 "tops": round(6.0 * cM * cN * cK / (cr["ms_per_step"] * 1e-3) / 1e12, 2),
+                 "gemm_mfma_frac": cf, "kernels": ck}
+            if name.startswith("c5"):
+                # few tokens: the step is bound by moving the weight-sized data
+                cKp = B.bitnet_k_pad(cK)
+                wb = 2 * cN * cK
+                step_bytes = (2 * wb + cN * cKp / 4                      # ternarize: W twice, codes
+                              + 2 * cM * cK + cM * cKp + 4 * cM          # act-quant
+                              + cN * cKp / 4 + cM * cKp + 2 * cM * cN    # forward: codes, x_q, y
+                              + cKp * ((cN + 63) // 64 * 32) + 2 * cM * cN + 2 * cM * cK  # dX: codes, dY, dX
+                              + cM * cKp + 2 * cM * cN + wb)             # dW: x_q, dY, dW
+                e["step_bytes"] = int(step_bytes)
+                e["hbm_frac"] = round(step_bytes / (cr["ms_per_step"] * 1e-3) / (PEAK_HBM_GBS * 1e9), 4)
+                e["hbm_frac_of_measured"] = round(step_bytes / (cr["ms_per_step"] * 1e-3) / (ceil["copy_GBps"] * 1e9),
+                                                  4)
+            configs[f"{name}"] = e
+            torch.cuda.empty_cache()
+        configs["c4_stack"] = stack_bench(args.steps, args.warmup, dev)
+        out["configs"] = configs
+
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp)
         out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 6)

@@ -402,6 +402,12 @@ bitnet_status ttq_bwd(const uint16_t* dY, const uint16_t* x, const uint16_t* wt,
  *   slot count the plan reserves. bitnet_debug_cta_order: the virtual index
  *   of each of `grid` workgroups (workgroup b runs on XCD b % 8; each XCD
  *   gets a contiguous range).
+ * bitnet_debug_mfma_probe - enqueues one launch of register-only MFMA chains
+ *   on every SIMD (int8 != 0: v_mfma_i32_32x32x32_i8, else
+ *   v_mfma_f32_32x32x16_bf16), `iters` rounds (1 .. 2^24), and stores in
+ *   *ops (host) the operations it performs; timing it gives the MFMA rate
+ *   the chip sustains under a full load. sink: device float[2048] (not
+ *   written in practice).
  */
 void bitnet_set_test_knobs(int split_ctas, int pair_cols, int no_skinny, uint32_t spin_limit);
 uint32_t bitnet_default_spin_limit(void);
@@ -411,6 +417,7 @@ int64_t bitnet_debug_split_pieces(int64_t tiles, int32_t stages, int32_t grid, i
                                   int64_t cap);
 int32_t bitnet_debug_partial_slots(int64_t tiles, int32_t grid);
 void bitnet_debug_cta_order(int32_t grid, int32_t* out);
+bitnet_status bitnet_debug_mfma_probe(int32_t int8, int32_t iters, float* sink, double* ops, void* stream);
 
 #ifdef __cplusplus
 }

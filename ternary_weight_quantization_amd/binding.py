@@ -99,6 +99,8 @@ def lib():
     L.bitnet_debug_split_pieces.restype = i64
     L.bitnet_debug_partial_slots.argtypes = [i64, i32]
     L.bitnet_debug_partial_slots.restype = i32
+    L.bitnet_debug_mfma_probe.argtypes = [i32, i32, vp, vp, vp]
+    L.bitnet_debug_mfma_probe.restype = st
     L.bitnet_debug_cta_order.argtypes = [i32, vp]
     L.bitnet_debug_cta_order.restype = None
     if len(_hip_runtimes_mapped()) > 1:
@@ -453,3 +455,12 @@ def bitnet_debug_cta_order(grid):
     out = np.zeros(int(grid), dtype=np.int32)
     lib().bitnet_debug_cta_order(int(grid), out.ctypes.data_as(ctypes.c_void_p))
     return out
+
+
+def bitnet_debug_mfma_probe(int8, iters, sink, stream=None):
+    """Enqueue the MFMA rate probe; returns the operations it performs.
+    sink: float32 [2048] on the GPU."""
+    _need(sink, torch.float32, (2048,), "sink")
+    ops = ctypes.c_double(0.0)
+    _check(lib().bitnet_debug_mfma_probe(1 if int8 else 0, int(iters), _ptr(sink), ctypes.byref(ops), _stream(stream)))
+    return float(ops.value)

@@ -336,6 +336,13 @@ int32_t bitnet_debug_partial_slots(int64_t tiles, int32_t grid) {
   return (int32_t)(a < b ? a : b);
 }
 
+bitnet_status bitnet_debug_mfma_probe(int32_t int8, int32_t iters, float* sink, double* ops, void* stream) {
+  if (!sink || !ops) return BITNET_ERR_NULL;
+  if (iters < 1 || iters > (1 << 24)) return BITNET_ERR_SHAPE;
+  *ops = bitnet::mfma_probe_ops(int8 != 0, iters);
+  return from_hip(bitnet::launch_mfma_probe(int8 != 0, iters, sink, static_cast<hipStream_t>(stream)));
+}
+
 void bitnet_debug_cta_order(int32_t grid, int32_t* out) {
   if (grid >= 1 && out) bitnet::debug_cta_order(grid, out);
 }

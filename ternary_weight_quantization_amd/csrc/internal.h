@@ -32,6 +32,13 @@ TestKnobs& test_knobs();
 // and cleared on the current device; synchronizes the device).
 hipError_t take_split_timeouts(unsigned int* count);
 
+// MFMA rate probe: one launch of register-only MFMA chains on every SIMD
+// (bf16 32x32x16 or int8 32x32x32), `iters` rounds; mfma_probe_ops() is the
+// operation count of such a launch. sink: 2048 floats (never written in
+// practice).
+hipError_t launch_mfma_probe(bool int8, int iters, float* sink, hipStream_t stream);
+double mfma_probe_ops(bool int8, int iters);
+
 // The pieces a split launch of T tiles x S stages over G workgroups runs,
 // computed on the host by the same functions the kernels use: for each
 // piece, in workgroup order, its virtual workgroup v, tile t, stages
