@@ -139,6 +139,26 @@ bitnet_status bitnet_quantize(const void* W, bitnet_dtype w_dtype, int64_t N, in
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * bitnet_quantize_static - bitnet_quantize for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): no workspace argument; the scratch
+ * (the weight absmean's fp64 partial sums) lives in a device array of the
+ * library, 4096 bytes per GPU the library runs on, held until the process
+ * ends. Results are bit for bit those of bitnet_quantize. The array keeps
+ * the last call's contents; every call overwrites what it reads, so none
+ * needs clearing, but calls that may run at the same time on one GPU race
+ * on it. Returns BITNET_ERR_WORKSPACE if a call would need more scratch
+ * than the array holds (not the case for any size: the need is fixed at
+ * bitnet_ternarize_workspace_bytes()), BITNET_ERR_HIP if the array's device
+ * address cannot be obtained; otherwise the arguments and errors of
+ * bitnet_quantize. Calls no allocating routine.
+ */
+bitnet_status bitnet_quantize_static(const void* W, bitnet_dtype w_dtype, int64_t N, int64_t K,
+                                     const uint16_t* x, int64_t M,
+                                     uint8_t* w_packed, float* gamma, int8_t* x_q, float* s_x,
+                                     void* stream);
+
+/*
  * bitnet_code_counts - how many weights each ternary value takes, for the
  * share of -1, 0 and +1 ("bitlinear.py", BitLinear.ternary_stats):
  *

@@ -62,6 +62,8 @@ def lib():
     L.bitnet_ternarize_pack.restype = st
     L.bitnet_quantize.argtypes = [vp, st, i64, i64, vp, i64, vp, vp, vp, vp, vp, sz, vp]
     L.bitnet_quantize.restype = st
+    L.bitnet_quantize_static.argtypes = [vp, st, i64, i64, vp, i64, vp, vp, vp, vp, vp]
+    L.bitnet_quantize_static.restype = st
     L.bitnet_code_counts.argtypes = [vp, i64, i64, vp, vp]
     L.bitnet_code_counts.restype = st
     L.bitnet_act_quant.argtypes = [vp, i64, i64, vp, vp, vp]
@@ -217,6 +219,28 @@ def bitnet_quantize(W, x, w_packed, gamma, x_q, s_x, workspace, stream=None):
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(lib().bitnet_quantize(_ptr(W), wd, N, K, _ptr(x), M, _ptr(w_packed), _ptr(gamma), _ptr(x_q), _ptr(s_x),
                                  _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def bitnet_quantize_static(W, x, w_packed, gamma, x_q, s_x, stream=None):
+    """bitnet_quantize with the library's own scratch array: no workspace,
+    nothing allocated."""
+    N, K = W.shape
+    M = x.shape[0]
+    Kp = bitnet_k_pad(K)
+    if W.dtype == torch.bfloat16:
+        wd = BITNET_BF16
+    elif W.dtype == torch.float32:
+        wd = BITNET_F32
+    else:
+        raise TypeError(f"W: expected bfloat16 or float32, got {W.dtype}")
+    _need(W, W.dtype, (N, K), "W")
+    _need(x, torch.bfloat16, (M, K), "x")
+    _need(w_packed, torch.uint8, (N, Kp // 4), "w_packed")
+    _need(gamma, torch.float32, (1,), "gamma")
+    _need(x_q, torch.int8, (M, Kp), "x_q")
+    _need(s_x, torch.float32, (M,), "s_x")
+    _check(lib().bitnet_quantize_static(_ptr(W), wd, N, K, _ptr(x), M, _ptr(w_packed), _ptr(gamma), _ptr(x_q),
+                                        _ptr(s_x), _stream(stream)))
 
 
 def bitnet_code_counts(w_packed, K, counts, stream=None):
