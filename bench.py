@@ -58,6 +58,8 @@ def parse():
     p.add_argument("--workload", default=HEADLINE)
     p.add_argument("--rotate", type=int, default=4)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--stack-memory", action="store_true",
+                   help="only measure the 8-layer stack's peak allocated bytes (run in a child process)")
     p.add_argument("--only-headline", action="store_true",
                    help="skip the other workloads and the stack (e.g. under a profiler)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -451,11 +453,11 @@ def stack_bench(steps, warmup, dev):
     bitlinear_bwd per layer, dX feeding the previous layer) as graph replays
     through the C ABI; and the peak allocated bytes of one forward + backward
     of the training module (QATBitLinear, bf16 masters, no retained
-    activations) from a reset of torch's peak statistics."""
+    activations) from a reset of torch's peak statistics (stack_memory, in a
+    fresh process)."""
     import torch
 
     from ternary_weight_quantization_amd import binding as B
-    from ternary_weight_quantization_amd import layer as LY
     from ternary_weight_quantization_amd import workloads as WL
 
     d = WL.stack_inputs(seed=0)
@@ -519,13 +521,34 @@ def stack_bench(steps, warmup, dev):
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
 
-    # peak memory of the training module's forward + backward
+    out = {
+        "workload": f"stack_8x_{dims[0]}_{dims[1]}_M{M}",
+        "ms_per_step": round(ms, 4),
+        "tops": round(ops / (ms * 1e-3) / 1e12, 2),
+    }
+    return out
+
+
+def stack_memory(dev):
+    """Peak allocated bytes of one forward + backward of the 8-layer training
+    module (QATBitLinear, bf16 masters, no retained activations), measured
+    from a reset of torch's peak statistics in a fresh process (bench.py
+    --stack-memory), after one untimed step that loads the library."""
+    import torch
+
+    from ternary_weight_quantization_amd import binding as B
+    from ternary_weight_quantization_amd import layer as LY
+    from ternary_weight_quantization_amd import workloads as WL
+
+    d = WL.stack_inputs(seed=0)
+    M, dims = d["M"], d["dims"]
+    L = len(dims) - 1
+    x0 = _to_dev(d["x"], torch.bfloat16, dev)
+    dY = _to_dev(d["dY"], torch.bfloat16, dev)
     layers = [LY.QATBitLinear(dims[i], dims[i + 1], device=dev) for i in range(L)]
     with torch.no_grad():
         for lay, w in zip(layers, d["Ws"]):
             lay.weight.copy_(_to_dev(w, torch.bfloat16, dev))
-    for lay in layers:  # warm the caching allocator and the library once
-        lay.weight.grad = None
     h = x0
     for lay in layers:
         h = lay(h)
@@ -548,14 +571,11 @@ def stack_bench(steps, warmup, dev):
                 for i in range(L))
     ws_max = max(max(B.bitlinear_fwd_workspace_bytes(M, dims[i + 1], dims[i]),
                      B.bitlinear_bwd_workspace_bytes(M, dims[i + 1], dims[i])) for i in range(L))
-    out = {
-        "workload": f"stack_8x_{dims[0]}_{dims[1]}_M{M}",
-        "ms_per_step": round(ms, 4),
-        "tops": round(ops / (ms * 1e-3) / 1e12, 2),
+    return {
         "peak_allocated_bytes": int(peak),
         "peak_allocated_MB": round(peak / 1e6, 1),
         "breakdown_MB": {
-            "before_step (bf16 masters, x, dY)": round(before / 1e6, 1),
+            "before the step (bf16 masters, x, dY)": round(before / 1e6, 1),
             "masters": round(masters / 1e6, 1),
             "grads (bf16, as the masters)": round(masters / 1e6, 1),
             "saved state after the forward (int8 x_q + s, 2-bit codes + gamma)": round(saved / 1e6, 1),
@@ -564,10 +584,6 @@ def stack_bench(steps, warmup, dev):
         },
         "pages_peak_MB": {"fused": 1151, "eager": 1887},
     }
-    del layers, h
-    torch.cuda.synchronize()
-    torch.cuda.empty_cache()
-    return out
 
 
 def main():
@@ -596,6 +612,9 @@ def main():
 
     B.lib()
     dev = torch.device("cuda:0")
+    if args.stack_memory:
+        print(json.dumps(stack_memory(dev)), flush=True)
+        return
     ceil = measure_ceilings(dev)
     inp = WL.layer_inputs(args.workload, seed=0)
     M, K, N = inp["M"], inp["K"], inp["N"]
@@ -723,6 +742,15 @@ def main():
             configs[f"{name}"] = e
             torch.cuda.empty_cache()
         configs["c4_stack"] = stack_bench(args.steps, args.warmup, dev)
+        # the peak bytes in a fresh process, so that no buffer of this one counts
+        import subprocess
+
+        r_ = subprocess.run([sys.executable, os.path.abspath(__file__), "--stack-memory"], capture_output=True,
+                            text=True, timeout=600)
+        lines = [ln for ln in r_.stdout.splitlines() if ln.startswith("{")]
+        if r_.returncode != 0 or not lines:
+            raise SystemExit(f"bench.py --stack-memory failed: {r_.stderr[-2000:]}")
+        configs["c4_stack"].update(json.loads(lines[-1]))
         out["configs"] = configs
 
     if not args.no_cpu_baseline:

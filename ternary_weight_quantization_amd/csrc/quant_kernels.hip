@@ -167,6 +167,16 @@ __global__ __launch_bounds__(kPackThreads) void ternarize_pack_kernel(
     float* __restrict__ gamma_out) {
   __shared__ double sred[kPackThreads / kWave];
   __shared__ float s_half;
+  const int64_t total = N * words_per_row;
+  const int64_t stride = (int64_t)gridDim.x * kPackThreads;
+  const int64_t wi0 = (int64_t)blockIdx.x * kPackThreads + threadIdx.x;
+  // the thread's first word is requested before gamma is reduced, so that
+  // its load latency overlaps the reduction of the partials
+  float vals[16];
+  if (wi0 < total) {
+    const int64_t n = wi0 / words_per_row;
+    load_word<F32, VEC>(w, n, K, (wi0 - n * words_per_row) * 16, vals);
+  }
   const double S = partials_total(partials, sred);
   if (threadIdx.x == 0) {
     const double mean = S / (double)(N * K);
@@ -177,13 +187,11 @@ __global__ __launch_bounds__(kPackThreads) void ternarize_pack_kernel(
   __syncthreads();
   const float h = s_half;
 
-  const int64_t total = N * words_per_row;
-  for (int64_t wi = (int64_t)blockIdx.x * kPackThreads + threadIdx.x; wi < total;
-       wi += (int64_t)gridDim.x * kPackThreads) {
-    const int64_t n = wi / words_per_row;
-    const int64_t k0 = (wi - n * words_per_row) * 16;
-    float vals[16];
-    load_word<F32, VEC>(w, n, K, k0, vals);
+  for (int64_t wi = wi0; wi < total; wi += stride) {
+    if (wi != wi0) {
+      const int64_t n = wi / words_per_row;
+      load_word<F32, VEC>(w, n, K, (wi - n * words_per_row) * 16, vals);
+    }
     // code j of the word at bit 8*(j%4) + 2*(j/4): byte b holds the codes
     // j = b, b+4, b+8, b+12, so (word >> 2t) & 0x03030303 lists the codes
     // 4t..4t+3 in its four bytes
@@ -453,18 +461,25 @@ static void launch_aq_tpr(int cpt, const uint16_t* x, int64_t M, int64_t K, int6
   }
 }
 
+// Threads per row: as many as keep every thread busy with at least one
+// chunk, up to 256. More threads per row (fewer chunks each) keep more loads
+// in flight per CU and shorten each wave's dependent load -> max -> store
+// chain (measured at 4096 x 2560: 64 threads per row 13.1 us, 256 12.1 us;
+// at 4096 x 6912: 28.4 and 24.7 us).
+static int aq_tpr(int64_t nchunks) { return nchunks >= 256 ? 256 : nchunks >= 128 ? 128 : 64; }
+
 template <bool VEC>
 static void launch_aq(const uint16_t* x, int64_t M, int64_t K, int64_t Kp, int8_t* xq, float* s,
                       hipStream_t st) {
   const int64_t nchunks = Kp / 8;
-  if (nchunks <= 64 * 8) {
-    launch_aq_tpr<64, VEC>((int)((nchunks + 63) / 64), x, M, K, Kp, xq, s, st);
-  } else if (nchunks <= 128 * 8) {
-    launch_aq_tpr<128, VEC>((int)((nchunks + 127) / 128), x, M, K, Kp, xq, s, st);
-  } else if (nchunks <= 256 * 8) {
-    launch_aq_tpr<256, VEC>((int)((nchunks + 255) / 256), x, M, K, Kp, xq, s, st);
-  } else {
+  if (nchunks > 256 * 8) {
     act_quant_long_kernel<VEC><<<(int)M, 256, 0, st>>>(x, M, K, Kp, xq, s);
+    return;
+  }
+  switch (aq_tpr(nchunks)) {
+    case 64: launch_aq_tpr<64, VEC>((int)((nchunks + 63) / 64), x, M, K, Kp, xq, s, st); break;
+    case 128: launch_aq_tpr<128, VEC>((int)((nchunks + 127) / 128), x, M, K, Kp, xq, s, st); break;
+    default: launch_aq_tpr<256, VEC>((int)((nchunks + 255) / 256), x, M, K, Kp, xq, s, st); break;
   }
 }
 
@@ -480,22 +495,24 @@ hipError_t launch_act_quant(const uint16_t* x, int64_t M, int64_t K, int8_t* x_q
 // Weight absmean partials and activation quantization in one launch. The
 // two are independent HBM streams (W, and x -> x_q, s); sharing a launch
 // lets each fill the CUs while the other ramps up or drains, and saves a
-// launch. Blocks 0 .. kAbsmeanBlocks-1 compute the absmean partials exactly
-// as absmean_partials_kernel does (same grid constants, so gamma gets the
-// same bits); the rest quantize rows, kAbsmeanThreads / TPR per block. The
-// codes are then packed by ternarize_pack_kernel, which needs every partial.
-// Used when the rows fit the register-resident layout with 16-byte loads
-// (K % 8 == 0, K <= 8192).
+// launch. The first blocks quantize rows, kAbsmeanThreads / TPR per block
+// (dispatched first: measured 1-3 us faster than the other order at the
+// layer shapes); the last kAbsmeanBlocks compute the absmean partials
+// exactly as absmean_partials_kernel does (same grid constants, so gamma
+// gets the same bits). The codes are then packed by ternarize_pack_kernel,
+// which needs every partial. Used when the rows fit the register-resident
+// layout with 16-byte loads (K % 8 == 0, K <= 8192).
 // ---------------------------------------------------------------------------
 
 template <bool F32, int TPR, int CPT>
 __global__ __launch_bounds__(kAbsmeanThreads) void quant_front_kernel(
     const void* __restrict__ w, int64_t n, double* __restrict__ partials, const uint16_t* __restrict__ x,
     int64_t M, int64_t K, int64_t Kp, int8_t* __restrict__ xq, float* __restrict__ s_out) {
-  if (blockIdx.x < kAbsmeanBlocks)
-    absmean_block<F32>(w, n, partials, blockIdx.x);
+  const int naq = (int)gridDim.x - kAbsmeanBlocks;
+  if ((int)blockIdx.x < naq)
+    act_quant_rows<kAbsmeanThreads, TPR, CPT, true>(x, M, K, Kp, xq, s_out, blockIdx.x);
   else
-    act_quant_rows<kAbsmeanThreads, TPR, CPT, true>(x, M, K, Kp, xq, s_out, blockIdx.x - kAbsmeanBlocks);
+    absmean_block<F32>(w, n, partials, blockIdx.x - naq);
 }
 
 template <bool F32, int TPR>
@@ -513,6 +530,20 @@ static void launch_front_tpr(int cpt, const void* W, int64_t n, double* partials
   }
 }
 
+// In the shared launch rows take 64 threads up to 512 chunks and 128 up to
+// 1024: the act-quant share then has few, large blocks (measured 2 us faster
+// at 4096 x 2560 than 256 threads per row, whose 2048 small blocks
+// the absmean blocks wait behind).
+template <bool F32>
+static void launch_front(const void* W, int64_t n, double* partials, const uint16_t* x, int64_t M, int64_t K,
+                         int64_t Kp, int8_t* xq, float* s, hipStream_t st) {
+  const int64_t nchunks = Kp / 8;
+  if (nchunks <= 64 * 8)
+    launch_front_tpr<F32, 64>((int)((nchunks + 63) / 64), W, n, partials, x, M, K, Kp, xq, s, st);
+  else
+    launch_front_tpr<F32, 128>((int)((nchunks + 127) / 128), W, n, partials, x, M, K, Kp, xq, s, st);
+}
+
 hipError_t launch_quantize(const void* W, bool w_is_f32, int64_t N, int64_t K, const uint16_t* x, int64_t M,
                            uint8_t* w_packed, float* gamma, int8_t* x_q, float* s_x, double* partials,
                            hipStream_t stream) {
@@ -521,16 +552,8 @@ hipError_t launch_quantize(const void* W, bool w_is_f32, int64_t N, int64_t K, c
     if (hipError_t e = launch_act_quant(x, M, K, x_q, s_x, stream)) return e;
     return launch_ternarize_pack(W, w_is_f32, N, K, w_packed, gamma, partials, stream);
   }
-  const int64_t n = N * K;
-  if (nchunks <= 64 * 8) {
-    const int cpt = (int)((nchunks + 63) / 64);
-    if (w_is_f32) launch_front_tpr<true, 64>(cpt, W, n, partials, x, M, K, Kp, x_q, s_x, stream);
-    else launch_front_tpr<false, 64>(cpt, W, n, partials, x, M, K, Kp, x_q, s_x, stream);
-  } else {
-    const int cpt = (int)((nchunks + 127) / 128);
-    if (w_is_f32) launch_front_tpr<true, 128>(cpt, W, n, partials, x, M, K, Kp, x_q, s_x, stream);
-    else launch_front_tpr<false, 128>(cpt, W, n, partials, x, M, K, Kp, x_q, s_x, stream);
-  }
+  if (w_is_f32) launch_front<true>(W, N * K, partials, x, M, K, Kp, x_q, s_x, stream);
+  else launch_front<false>(W, N * K, partials, x, M, K, Kp, x_q, s_x, stream);
   if (hipError_t e = hipGetLastError()) return e;
   return launch_pack(W, w_is_f32, N, K, w_packed, gamma, partials, stream);
 }

@@ -573,7 +573,8 @@ def test_layer_with_bias():
     (300, 6912, 264, "bf16"),    # 128 threads per row
     (64, 256, 128, "f32"),       # f32 masters
     (5, 1000, 33, "bf16"),       # K % 8 != 0: the separate launches
-    (3, 9000, 16, "bf16"),       # rows past the fused layout: the separate launches
+    (3, 9000, 16, "bf16"),       # rows past the shared launch's layout: the separate launches
+    (3, 17000, 16, "bf16"),      # rows past the register-resident layout: the separate launches
 ])
 def test_quantize_matches_separate_calls(M, K, N, wd):
     """bitnet_quantize (weight absmean and activation quantization in one
