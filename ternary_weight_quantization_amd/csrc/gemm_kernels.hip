@@ -1673,18 +1673,38 @@ struct GemmShape {
   int64_t tiles() const { return tiles_i * tiles_j; }
 };
 
+// Per-piece costs of a split launch, in the product's stages: the last
+// piece of a split tile reads every other piece's 256 KiB partial tile on
+// its own CU, and a chip with every CU busy runs at a lower clock than one
+// with a few idle, so a split must save many stages to pay. Measured
+// interleaved on one MI355X, whole tiles against splits over 128-256
+// workgroups and the split the cost model picked:
+//  - int8 forward at 512, 1024, 2048, 4096, 8192 tokens (K 6912, N 2560),
+//    2048 and 4096 tokens (K 2560, N 6912) and 4096, 16384 tokens (K = N =
+//    2560): whole tiles were fastest at every shape (4096 x 6912 -> 2560:
+//    90.7 us against 100-114 us split; 512 tokens: 69.6 us on 20 CUs
+//    against 84.6 us split over 80 workgroups);
+//  - dX and dW launched alone at 1024-4096 tokens: 20 stages per piece
+//    chooses the fastest or a near-fastest option at every shape (e.g. dX
+//    at 4096 x 6912 -> 2560 whole, 144 us against 175 us split; at
+//    4096 x 2560 -> 6912 split, 151 us against 163 us whole).
+constexpr int kFwdPieceCost = 48;
+constexpr int kBwdPieceCost = 20;
+
 static GemmShape shape_of(GemmKind kind, int64_t M, int64_t N, int64_t K) {
   const int64_t Kp = k_pad(K);
   switch (kind) {
-    case GemmKind::kFwd: return {(N + kBI - 1) / kBI, (M + kBJ - 1) / kBJ, (Kp + kStageBytes - 1) / kStageBytes, 7};
+    case GemmKind::kFwd:
+      return {(N + kBI - 1) / kBI, (M + kBJ - 1) / kBJ, (Kp + kStageBytes - 1) / kStageBytes, kFwdPieceCost};
     // a split piece costs the bf16 forward about 20 of its stages (measured
     // at 4096x2560->6912: whole tiles in two rounds 171 us, split over 256
     // workgroups 185 us)
     case GemmKind::kTtqFwd: return {(N + kBI - 1) / kBI, (M + kBJ - 1) / kBJ, (Kp + kRed16 - 1) / kRed16, 20};
-    case GemmKind::kBwdDx: return {(K + kBI - 1) / kBI, (M + kBJ - 1) / kBJ, (N + kRed16 - 1) / kRed16, 3};
+    case GemmKind::kBwdDx:
+      return {(K + kBI - 1) / kBI, (M + kBJ - 1) / kBJ, (N + kRed16 - 1) / kRed16, kBwdPieceCost};
     case GemmKind::kBwdDw: case GemmKind::kBwdPair: case GemmKind::kTtqBwd: break;
   }
-  return {(K + kBI - 1) / kBI, (N + kBJ - 1) / kBJ, (M + kRed16 - 1) / kRed16, 3};
+  return {(K + kBI - 1) / kBI, (N + kBJ - 1) / kBJ, (M + kRed16 - 1) / kRed16, kBwdPieceCost};
 }
 
 // Workgroups of a split launch, or 0 for one whole tile per workgroup.
@@ -2022,16 +2042,23 @@ static bool skinny(int64_t M);
 // The STE backward products run in one launch when N % 8 == 0, there are
 // more than a few tokens and each product would split its tiles on the full
 // device anyway.
-static bool pair_eligible(int64_t M, int64_t N, int64_t K) {
+// The paired launch runs when both products are large enough that their
+// split tails and fills are worth sharing: each would split when launched
+// alone under a 3-stage piece cost (the gate under which the pair's own
+// cost model, plan_pair, was measured; at 4096 x 6912 -> 2560 the pair
+// takes 287 us where dX whole and dW split alone take 144 + 190 us).
+static bool pair_gate(int64_t M, int64_t N, int64_t K) {
   const int cus = device_cus();
-  return N % 8 == 0 && !skinny(M) && split_pays(shape_of(GemmKind::kBwdDx, M, N, K), cus) > 0 &&
-         split_pays(shape_of(GemmKind::kBwdDw, M, N, K), cus) > 0;
+  GemmShape dx = shape_of(GemmKind::kBwdDx, M, N, K), dw = shape_of(GemmKind::kBwdDw, M, N, K);
+  dx.overhead = dw.overhead = 3;
+  return split_pays(dx, cus) > 0 && split_pays(dw, cus) > 0;
+}
+static bool pair_eligible(int64_t M, int64_t N, int64_t K) {
+  return N % 8 == 0 && !skinny(M) && pair_gate(M, N, K);
 }
 // TTQ's pair: both operands copied as stored (N, K multiples of 8).
 static bool ttq_pair_eligible(int64_t M, int64_t N, int64_t K) {
-  const int cus = device_cus();
-  return N % 8 == 0 && K % 8 == 0 && split_pays(shape_of(GemmKind::kBwdDx, M, N, K), cus) > 0 &&
-         split_pays(shape_of(GemmKind::kBwdDw, M, N, K), cus) > 0;
+  return N % 8 == 0 && K % 8 == 0 && pair_gate(M, N, K);
 }
 static size_t pair_split_bytes(int64_t M, int64_t N, int64_t K) {
   const PairPlan pp = plan_pair(shape_of(GemmKind::kBwdDx, M, N, K), shape_of(GemmKind::kBwdDw, M, N, K),

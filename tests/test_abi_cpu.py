@@ -85,9 +85,11 @@ def test_size_queries(L):
     # transposed codes [Kp][N/2] and x_hat
     assert L.bitlinear_bwd_workspace_bytes(4096, 6912, 2560) == \
         2560 * 6912 // 2 + 2 * 4096 * 2560 + 2560 + 240 * tile
-    # 4096x6912->2560 forward: 160 tiles of 54 stages split over 256
-    # workgroups, G + T - 1 = 415 slots
-    assert L.bitlinear_fwd_workspace_bytes(4096, 2560, 6912) == 2560 + 415 * tile
+    # the int8 forward runs whole tiles unless a split saves more than 48
+    # stages a piece: 4096x6912->2560 (160 tiles of 54 stages, one round)
+    # needs none; one tile of 512 stages splits over 4 workgroups (4 slots)
+    assert L.bitlinear_fwd_workspace_bytes(4096, 2560, 6912) == 0
+    assert L.bitlinear_fwd_workspace_bytes(256, 256, 65536) == 256 + 4 * tile
     # few tokens: the forward needs none; the backward only its transient
     # operands (the few-token dX and dW do not split)
     assert L.bitlinear_fwd_workspace_bytes(32, 2560, 6912) == 0
@@ -144,8 +146,10 @@ def test_gemm_workspace_validation(L):
     assert L.bitlinear_bwd(A, A, A, A, A, 4096, 6912, 2560, A, A, 0, A, need - 1, None) == EWS
     assert L.bitlinear_bwd(A, A, A, A, A, 4096, 6912, 2560, A, A, 0, None, need, None) == EWS
     assert L.bitlinear_bwd(A, A, A, A, A, 4096, 6912, 2560, A, A, 0, MISALIGNED + 4, need, None) == EALIGN
-    need = L.bitlinear_fwd_workspace_bytes(4096, 2560, 6912)
-    assert L.bitlinear_fwd(A, A, A, A, 4096, 2560, 6912, A, None, A, need - 1, None) == EWS
+    # a forward that splits its one tile (K = 65536) needs split workspace
+    need = L.bitlinear_fwd_workspace_bytes(256, 256, 65536)
+    assert need > 0
+    assert L.bitlinear_fwd(A, A, A, A, 256, 256, 65536, A, None, A, need - 1, None) == EWS
 
 
 def test_bwd_validation(L):
