@@ -67,10 +67,12 @@ def test_split_plan_invariants(T, S, G):
 
 
 def test_split_plan_layer_shapes():
-    """The plans of the layer shapes: forward 4096x6912->2560 (160 tiles of
-    54 stages on 256 workgroups), dX at 4096x2560->6912 on its pair share
-    (160 tiles of 108 stages on 120), the 8-layer stack's down-projection
-    forward (80 tiles of 54 stages on 256) and a ragged 270 x 64 over 136."""
+    """Plans at the layer shapes, as the cost models choose them or as the
+    split knob forces them: the forward at 4096x6912->2560 (160 tiles of 54
+    stages on 256 workgroups) and at 4096x2560->6912 (432 x 20), dX at
+    4096x2560->6912 on its pair share (160 tiles of 108 stages on 120), the
+    8-layer stack's down-projection forward (80 tiles of 54 stages on 256)
+    and a ragged 270 x 64 over 136."""
     for T, S, G in ((160, 54, 256), (160, 108, 120), (80, 54, 256), (270, 64, 136), (432, 20, 256)):
         p = _check_plan(T, S, G)
         assert len(p["v"]) <= G + T - 1
