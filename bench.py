@@ -196,6 +196,7 @@ def cpu_baseline(inp, target_s=12.0, chunk=256):
     from threadpoolctl import threadpool_info
 
     import oracle as O
+    from oracle import compare as C
     from ternary_weight_quantization_amd import workloads as WL
 
     M, K, N = inp["M"], inp["K"], inp["N"]
@@ -225,6 +226,13 @@ def cpu_baseline(inp, target_s=12.0, chunk=256):
     dt = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     ops = 6.0 * rows_done * N * K
+    # untimed: the elements of the whole workload within one fp32 ulp of a
+    # rounding boundary (weights at gamma/2, scaled activations at a
+    # half-integer); the GPU matches them bit for bit like every other
+    gamma = O.absmean_gamma(w)
+    x_all = WL.bf16_bits_to_f32(inp["x"]).astype(np.float64)
+    _, s_all = O.act_quant(x_all, Kp)
+    near = {"weights": C.near_boundary_weights(w, gamma), "activations": C.near_boundary_acts(x_all, s_all)}
     return {
         "value": ops / dt / 1e12,
         "unit": "TOPS",
@@ -235,6 +243,7 @@ def cpu_baseline(inp, target_s=12.0, chunk=256):
                   f"{rows_done} token rows; {dt:.2f} s wall, {ops / 1e9:.1f} G ops (6*rows*N*K), numpy fp64 "
                   f"with {threads} BLAS threads on {os.cpu_count()} visible cpus",
         "seconds": round(dt, 3),
+        "near_boundary": near,
     }
 
 
@@ -656,6 +665,13 @@ def main():
                                        grads=s["ttq_grads"], workspace=ttq_ws),
     }
     xms = {n: per_call_ms(f, sets, args.steps, args.warmup) for n, f in xc.items()}
+    # shares of -1 / 0 / +1 in the ternary weight ("bitlinear.py", ternary_stats),
+    # from the packed codes of the step (exact counts on the GPU)
+    counts = torch.empty((2,), dtype=torch.int64, device=dev)
+    B.bitnet_code_counts(sets[0]["w_packed"], K, counts)
+    neg, pos = (int(v) for v in counts.cpu())
+    ternary = {"minus_one": round(neg / (N * K), 6), "zero": round((N * K - neg - pos) / (N * K), 6),
+               "plus_one": round(pos / (N * K), 6)}
     del sets
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -707,6 +723,7 @@ def main():
                    "w_dtype": inp["w_dtype"], "rotating_buffer_sets": args.rotate},
         "roofline": roofline,
         "ms_per_step_warm": round(r["ms_per_step_warm"], 4),
+        "ternary_fractions": ternary,
         "gemm_mfma_frac": gemm_frac,
         "gemm_mfma_frac_of_measured": gemm_frac_meas,
         "measured_ceilings": ceil,

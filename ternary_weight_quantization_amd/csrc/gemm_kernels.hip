@@ -1993,6 +1993,39 @@ static hipError_t run_dw(const uint16_t* dY, const uint16_t* xhat, int64_t M, in
   return run_gemm<MfmaBf16, 0>(pl, RowTransposeBf16Loader<false, 5>{dY, N, M, N}, ep, g, split_ws, split_bytes, stream);
 }
 
+// The few-token dW (dw_skinny_kernel) on x_hat: N % 8 == 0, a bf16 or f32
+// output (the 1-bit output runs the large-M GEMM's epilogue).
+static bool dw_skinny_ok(int64_t M, int64_t N, int64_t K, DwOut dw_out) {
+  const int64_t dw_tiles = (k_pad(K) + 255) / 256 * ((N + 63) / 64);
+  return skinny(M) && N % 8 == 0 && dw_out != DwOut::kSign1 && dw_tiles < (int64_t(1) << 31);
+}
+static hipError_t launch_dw_skinny(const uint16_t* xhat, const uint16_t* dY, int64_t M, int64_t N, int64_t K,
+                                   void* dW, DwOut dw_out, hipStream_t stream) {
+  const int64_t Kp = k_pad(K);
+  const int ktiles = (int)((Kp + 255) / 256);
+  const unsigned grid = (unsigned)((Kp + 255) / 256 * ((N + 63) / 64));
+  if (dw_out == DwOut::kF32)
+    dw_skinny_kernel<true><<<grid, 256, 0, stream>>>(xhat, dY, (int)M, N, Kp, K, ktiles, dW);
+  else
+    dw_skinny_kernel<false><<<grid, 256, 0, stream>>>(xhat, dY, (int)M, N, Kp, K, ktiles, dW);
+  return hipGetLastError();
+}
+
+// Few tokens with both outputs: the two pre-passes (fp4 transposed codes,
+// x_hat) in one bwd_prep_kernel launch, then the few-token dX and dW kernels.
+static bool skinny_both_ok(int64_t M, int64_t N, int64_t K, DwOut dw_out) {
+  return dw_skinny_ok(M, N, K, dw_out);  // dx_skinny needs N % 8 == 0 as well
+}
+static void launch_prep(const uint8_t* w_packed, const int8_t* x_q, const float* s_x, int64_t M, int64_t N,
+                        int64_t K, uint8_t* wt, uint16_t* xhat, hipStream_t stream) {
+  const int64_t Kp = k_pad(K), Np = n_pad64(N);
+  const int wt_bx = (int)(Kp / 64), wt_by = (int)((Np + 255) / 256);
+  const int64_t want = (M * (Kp / 16) + 255) / 256;
+  const int xhat_nb = (int)(want < 4096 ? want : 4096);
+  bwd_prep_kernel<<<wt_bx * wt_by + xhat_nb, 256, 0, stream>>>(w_packed, N, Kp, Np, wt, wt_bx, wt_by, x_q, s_x, M,
+                                                               xhat, xhat_nb);
+}
+
 hipError_t launch_bwd_dw(const uint16_t* dY, const int8_t* x_q, const float* s_x, int64_t M,
                          int64_t N, int64_t K, void* dW, DwOut dw_out, void* ws, size_t ws_bytes,
                          hipStream_t stream) {
@@ -2002,17 +2035,7 @@ hipError_t launch_bwd_dw(const uint16_t* dY, const int8_t* x_q, const float* s_x
   void* split_ws = static_cast<char*>(ws) + xb;
   const size_t split_bytes = ws_bytes - xb;
   if (hipError_t e = launch_xhat(x_q, s_x, M, K, xhat, stream)) return e;
-  const int64_t dw_tiles = (k_pad(K) + 255) / 256 * ((N + 63) / 64);
-  if (skinny(M) && N % 8 == 0 && dw_out != DwOut::kSign1 && dw_tiles < (int64_t(1) << 31)) {
-    const int64_t Kp = k_pad(K);
-    const int ktiles = (int)((Kp + 255) / 256);
-    const unsigned grid = (unsigned)dw_tiles;
-    if (dw_out == DwOut::kF32)
-      dw_skinny_kernel<true><<<grid, 256, 0, stream>>>(xhat, dY, (int)M, N, Kp, K, ktiles, dW);
-    else
-      dw_skinny_kernel<false><<<grid, 256, 0, stream>>>(xhat, dY, (int)M, N, Kp, K, ktiles, dW);
-    return hipGetLastError();
-  }
+  if (dw_skinny_ok(M, N, K, dw_out)) return launch_dw_skinny(xhat, dY, M, N, K, dW, dw_out, stream);
   switch (dw_out) {
     case DwOut::kF32: return run_dw(dY, xhat, M, N, K, Bf16Epilogue<true>{dW, nullptr, K, N}, split_ws, split_bytes, stream);
     case DwOut::kSign1:
@@ -2083,6 +2106,10 @@ size_t gemm_workspace_bytes(GemmKind kind, int64_t M, int64_t N, int64_t K) {
     case GemmKind::kBwdDx: return wt_bytes(N, K) + (skinny(M) && N % 8 == 0 ? 0 : alone(kind));
     case GemmKind::kBwdDw: return xhat_bytes(M, K) + alone(kind);
     case GemmKind::kBwdPair: {
+      // (any dW output: the sign output of few tokens takes the separate route)
+      if (skinny_both_ok(M, N, K, DwOut::kBf16))
+        return std::max(wt_bytes(N, K) + xhat_bytes(M, K), std::max(gemm_workspace_bytes(GemmKind::kBwdDx, M, N, K),
+                                                                    gemm_workspace_bytes(GemmKind::kBwdDw, M, N, K)));
       if (pair_eligible(M, N, K) && pair_split_bytes(M, N, K) > 0)
         return std::max(wt_bytes(N, K) + xhat_bytes(M, K) + pair_split_bytes(M, N, K),
                         std::max(wt_bytes(N, K), xhat_bytes(M, K)));
@@ -2101,6 +2128,14 @@ size_t gemm_workspace_bytes(GemmKind kind, int64_t M, int64_t N, int64_t K) {
 hipError_t launch_bwd_pair(const uint16_t* dY, const uint8_t* w_packed, const float* gamma, const int8_t* x_q,
                            const float* s_x, int64_t M, int64_t N, int64_t K, uint16_t* dX, void* dW,
                            DwOut dw_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (ws != nullptr && skinny_both_ok(M, N, K, dw_out) && ws_bytes >= wt_bytes(N, K) + xhat_bytes(M, K)) {
+    uint8_t* wt = static_cast<uint8_t*>(ws);
+    uint16_t* xhat = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + wt_bytes(N, K));
+    launch_prep(w_packed, x_q, s_x, M, N, K, wt, xhat, stream);
+    if (hipError_t e = hipGetLastError()) return e;
+    if (hipError_t e = launch_dx_skinny(wt, dY, gamma, M, N, K, dX, stream)) return e;
+    return launch_dw_skinny(xhat, dY, M, N, K, dW, dw_out, stream);
+  }
   if (!pair_eligible(M, N, K) || ws == nullptr) return hipErrorNotSupported;
   const GemmShape g1 = shape_of(GemmKind::kBwdDx, M, N, K), g2 = shape_of(GemmKind::kBwdDw, M, N, K);
   const size_t wb = wt_bytes(N, K), xb = xhat_bytes(M, K);
@@ -2110,14 +2145,8 @@ hipError_t launch_bwd_pair(const uint16_t* dY, const uint8_t* w_packed, const fl
   uint8_t* wt = reinterpret_cast<uint8_t*>(base);
   uint16_t* xhat = reinterpret_cast<uint16_t*>(base + wb);
   const int64_t Kp = k_pad(K), Np = n_pad64(N);
-  {
-    const int wt_bx = (int)(Kp / 64), wt_by = (int)((Np + 255) / 256);
-    const int64_t want = (M * (Kp / 16) + 255) / 256;
-    const int xhat_nb = (int)(want < 4096 ? want : 4096);
-    bwd_prep_kernel<<<wt_bx * wt_by + xhat_nb, 256, 0, stream>>>(w_packed, N, Kp, Np, wt, wt_bx, wt_by, x_q, s_x, M,
-                                                                 xhat, xhat_nb);
-    if (hipError_t e = hipGetLastError()) return e;
-  }
+  launch_prep(w_packed, x_q, s_x, M, N, K, wt, xhat, stream);
+  if (hipError_t e = hipGetLastError()) return e;
   const RowCodesLoader<CodesFp4Frags> p1{wt, Np / 2, Kp};
   const CopyLoader<2, true> q1{reinterpret_cast<const char*>(dY), 2 * N, M, 2 * N};
   const Bf16Epilogue<false> e1{dX, gamma, K, M};
