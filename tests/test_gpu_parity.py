@@ -305,6 +305,28 @@ def test_stack_c4_chain():
         check_layer(inp, g, full=full, seed=i)
 
 
+@pytest.mark.parametrize("M,K,N", [
+    (4096, 6912, 2560),  # the down projection: whole tiles by default (160 tiles, one round)
+    (520, 1001, 263),    # ragged
+])
+def test_forward_bits_independent_of_split(M, K, N, set_knobs):
+    """The forward's INT32 sums are exact ("bitnet-qat-train", Semantics), so
+    y and the accumulators must not depend on how the output tiles are
+    shared out: whole tiles, the cost model's plan and stream-K splits over
+    several grids give the same bits; the first is also checked against the
+    oracle (sampled at the large shape)."""
+    inp = WL.custom_inputs(M, K, N, seed=M + 3 * K + N)
+    note(f"forward split invariance M={M} K={K} N={N}")
+    set_knobs(split_ctas=-1)
+    ref = run_layer(inp, dx=False, dw=False)
+    check_layer(inp, ref, full=M * N * K < 5e9)
+    for G in (0, 7, 64, 256):
+        set_knobs(split_ctas=G)
+        g = run_layer(inp, dx=False, dw=False)
+        assert np.array_equal(g["acc"], ref["acc"]), G
+        assert np.array_equal(g["y_bits"], ref["y_bits"]), G
+
+
 @pytest.mark.parametrize("M,K,N,split", [
     (300, 1000, 777, 13),     # split tiles in all three GEMMs, separate launches
     (1024, 2560, 1536, None),  # dX and dW in one launch, both split
