@@ -38,3 +38,26 @@ def test_random_shape(i, M, K, N, wd):
     inp = WL.custom_inputs(M, K, N, seed=5000 + i, w_dtype=wd)
     check_layer(inp, run_layer(inp), full=True)
     check_ttq(inp, run_ttq(inp, dw_f32=(wd == "f32")))
+
+
+# Shapes on the edges the kernels branch on: the few-token cutoff (M = 64
+# runs the decode-shaped kernels, 65 the 256 x 256 tiles), one token more or
+# fewer than a whole tile along each output axis, K around the 64-value
+# padding and the 128-byte stage, N around the multiple of 8 the 16-byte
+# token loads and the paired launch need, and one-row / one-column outputs.
+EDGE_SHAPES = [
+    (64, 320, 264, "bf16"), (65, 320, 264, "bf16"),
+    (64, 129, 255, "f32"), (65, 129, 257, "f32"),
+    (255, 64, 256, "bf16"), (257, 65, 256, "bf16"),
+    (256, 127, 257, "bf16"), (256, 128, 255, "f32"),
+    (513, 256, 511, "bf16"), (511, 257, 513, "bf16"),
+    (1, 2560, 6912, "bf16"), (4096, 1, 8, "bf16"), (4096, 8, 1, "bf16"),
+    (300, 2560, 8, "bf16"), (300, 8, 2560, "bf16"),
+]
+
+
+@pytest.mark.parametrize("M,K,N,wd", EDGE_SHAPES)
+def test_edge_shape(M, K, N, wd):
+    note(f"edge shape M={M} K={K} N={N} W={wd}")
+    inp = WL.custom_inputs(M, K, N, seed=M * 7 + K * 3 + N, w_dtype=wd)
+    check_layer(inp, run_layer(inp), full=True)
