@@ -762,12 +762,17 @@ def main():
         # the peak bytes in a fresh process, so that no buffer of this one counts
         import subprocess
 
-        r_ = subprocess.run([sys.executable, os.path.abspath(__file__), "--stack-memory"], capture_output=True,
-                            text=True, timeout=600)
-        lines = [ln for ln in r_.stdout.splitlines() if ln.startswith("{")]
-        if r_.returncode != 0 or not lines:
-            raise SystemExit(f"bench.py --stack-memory failed: {r_.stderr[-2000:]}")
-        configs["c4_stack"].update(json.loads(lines[-1]))
+        try:
+            r_ = subprocess.run([sys.executable, os.path.abspath(__file__), "--stack-memory"], capture_output=True,
+                                text=True, timeout=600)
+            lines = [ln for ln in r_.stdout.splitlines() if ln.startswith("{")]
+            if r_.returncode != 0 or not lines:
+                raise RuntimeError(f"exit {r_.returncode}: {r_.stderr[-500:]}")
+            configs["c4_stack"].update(json.loads(lines[-1]))
+        except (RuntimeError, OSError, ValueError, subprocess.TimeoutExpired) as e:
+            # the timed figures stand; the memory figure is reported as missing
+            print(f"bench.py: --stack-memory failed: {e}", file=sys.stderr)
+            configs["c4_stack"]["peak_allocated_error"] = str(e)[:300]
         out["configs"] = configs
 
     if not args.no_cpu_baseline:
