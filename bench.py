@@ -64,6 +64,9 @@ def parse():
                    help="skip the other workloads and the stack (e.g. under a profiler)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain device copy of known size (for counter calibration)")
+    p.add_argument("--vendor-gemms", action="store_true",
+                   help="time the library GEMMs torch dispatches (hipBLASLt) on plain operands of the workload's "
+                        "three products, for comparison (no conversion work; not part of the path)")
     p.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR"),
                    help="turn rocprofv3 FETCH_SIZE / WRITE_SIZE runs of the bench and of --copy-calibration "
                         "into profiles/pmc_traffic.json (no GPU needed)")
@@ -92,6 +95,50 @@ def copy_calibration():
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 3}), flush=True)
+
+
+def vendor_gemms(inp, steps, warmup):
+    """The three products of one layer as plain library GEMMs through torch
+    (hipBLASLt on this image): the INT8 forward (torch._int_mm, x_q [M][K] by
+    the codes as int8 [K][N]), dX = dY [M][N] . W [N][K] and dW = dY^T . x
+    in bf16, all operands contiguous (dY^T stored transposed). Medians of `steps`
+    calls timed with HIP events after `warmup`; nothing of the path itself."""
+    import torch
+
+    M, K, N = inp["M"], inp["K"], inp["N"]
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    xq = torch.randint(-127, 128, (M, K), dtype=torch.int8, device=dev, generator=g)
+    wq = torch.randint(-1, 2, (N, K), dtype=torch.int8, device=dev, generator=g)
+    wq_t = wq.t().contiguous()
+    dY = torch.randn((M, N), dtype=torch.bfloat16, device=dev, generator=g)
+    W = torch.randn((N, K), dtype=torch.bfloat16, device=dev, generator=g)
+    x = torch.randn((M, K), dtype=torch.bfloat16, device=dev, generator=g)
+    dYt = dY.t().contiguous()
+    cases = {
+        "fwd_int8 x_q[M,K] @ q[K,N] (torch._int_mm)": lambda: torch._int_mm(xq, wq_t),
+        "dX_bf16 dY[M,N] @ W[N,K]": lambda: dY @ W,
+        "dW_bf16 dY^T[N,M] @ x[M,K]": lambda: dYt @ x,
+    }
+    out = {}
+    flops = 2.0 * M * N * K
+    for name, f in cases.items():
+        for _ in range(warmup):
+            f()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(steps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            f()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e3)
+        us = sorted(ts)[len(ts) // 2]
+        out[name] = {"us": round(us, 1), "rate": round(flops / (us * 1e-6) / 1e12, 1),
+                     "unit": "TOP/s" if "int8" in name else "TFLOP/s"}
+    return {"workload": f"{M}x{K}x{N}", "gemms": out}
 
 
 def _pmc_rows(d):
@@ -610,6 +657,11 @@ def main():
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
 
+    if args.vendor_gemms:
+        from ternary_weight_quantization_amd import workloads as WL
+
+        print(json.dumps(vendor_gemms(WL.layer_inputs(args.workload, seed=0), args.steps, args.warmup)), flush=True)
+        return
     if args.copy_calibration:
         copy_calibration()
         return
