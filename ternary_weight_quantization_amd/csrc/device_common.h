@@ -100,12 +100,16 @@ __device__ __forceinline__ uint32_t buf_load4(rsrc_t r, uint32_t off) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
 }
 
-// Store at voffset + soffset (soffset uniform). A store whose voffset is
-// >= num_records is dropped; callers keep voffset + soffset inside the
-// resource for the stores they mean to happen.
-__device__ __forceinline__ void buf_store16(rsrc_t r, uint32_t voff, uint32_t soff, uint4 v) {
+// Streaming store (cache policy nt) at voffset + soffset (soffset uniform),
+// for outputs written once and not read again by the launch, so that they
+// take less L2 capacity from the operands still being read. A store whose
+// voffset is >= num_records is dropped; callers keep voffset + soffset
+// inside the resource for the stores they mean to happen.
+constexpr int kNonTemporal = 2;
+
+__device__ __forceinline__ void buf_store16_stream(rsrc_t r, uint32_t voff, uint32_t soff, uint4 v) {
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  __builtin_amdgcn_raw_buffer_store_b128(u32x4{v.x, v.y, v.z, v.w}, r, (int)voff, (int)soff, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(u32x4{v.x, v.y, v.z, v.w}, r, (int)voff, (int)soff, kNonTemporal);
 }
 
 // Device-coherent 16-byte access (cache policy sc1): stores write through

@@ -774,8 +774,9 @@ struct EpStage {
   // lane % kChunks, i.e. out[j0 + row][i0 + chunk * 16 / EB ..]. All gets
   // are issued first. When I is a multiple of 16 / EB (a chunk then lies
   // all inside or all outside a row), each get is one 16-byte store through
-  // a buffer resource based at the pass's first row, with the row offset as
-  // the uniform soffset and an out-of-range voffset for rows at or past J
+  // a buffer resource based at the pass's first row (a streaming store: the
+  // output is not read again by the launch), with the row offset as the
+  // uniform soffset and an out-of-range voffset for rows at or past J
   // and chunks at or past I (32 * I * EB < 2^31, checked by the C ABI);
   // otherwise rows are not 16-byte aligned and the valid elements are
   // stored one by one. i0, j0 are uniform in the wave.
@@ -798,8 +799,8 @@ struct EpStage {
       const uint32_t lane_off = i0 + c * (16 / EB) < I ? rl * row_b + 16 * c : kOob;
 #pragma unroll
       for (int k = 0; k < kGets; ++k)
-        buf_store16(rs, rl < rows_in - k * kRowsPerGet ? lane_off : kOob, (uint32_t)(k * kRowsPerGet) * row_b,
-                    v[k]);
+        buf_store16_stream(rs, rl < rows_in - k * kRowsPerGet ? lane_off : kOob,
+                           (uint32_t)(k * kRowsPerGet) * row_b, v[k]);
     } else {
       const int64_t i = i0 + c * (16 / EB);
 #pragma unroll
