@@ -14,6 +14,15 @@ so that the working set (~240 MB per copy) does not sit in the 256 MB
 Infinity Cache between steps (the cold figure); the warm figure repeats one
 copy.
 
+Clock ramp: after the GPU has idled, its power management raises the
+clocks over some tens of milliseconds of work (measured at the headline
+workload: graph-replayed steps take 0.42 ms in the first 7 ms of work after
+2 s idle, 0.37 ms by 20 ms and 0.355-0.36 ms from about 50 ms on). A
+training loop runs in the settled state, so every timed region here is
+preceded by at least --ramp-ms (default 200) milliseconds of untimed
+repetitions of the same work, after the W warm-up steps; the K timed steps
+are unchanged. --ramp-ms 0 measures straight after the warm-up steps.
+
 Prints one JSON line: throughput in effective TOPS (6*M*N*K per step), the
 step time (replays of the step captured in HIP graphs), per-call times (the
 median of `steps` eager calls timed with HIP events on the launch stream),
@@ -57,6 +66,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default=HEADLINE)
     p.add_argument("--rotate", type=int, default=4)
+    p.add_argument("--ramp-ms", type=float, default=200.0,
+                   help="untimed repetitions of the timed work before each timed region, in milliseconds of GPU "
+                        "time, so that the clocks have left the idle state (0: none)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--stack-memory", action="store_true",
                    help="only measure the 8-layer stack's peak allocated bytes (run in a child process)")
@@ -102,7 +114,8 @@ def vendor_gemms(inp, steps, warmup):
     (hipBLASLt on this image): the INT8 forward (torch._int_mm, x_q [M][K] by
     the codes as int8 [K][N]), dX = dY [M][N] . W [N][K] and dW = dY^T . x
     in bf16, all operands contiguous (dY^T stored transposed). Medians of `steps`
-    calls timed with HIP events after `warmup`; nothing of the path itself."""
+    back-to-back calls timed with HIP events after `warmup` calls and the
+    clock ramp, as the path's own calls are; nothing of the path itself."""
     import torch
 
     M, K, N = inp["M"], inp["K"], inp["N"]
@@ -126,16 +139,17 @@ def vendor_gemms(inp, steps, warmup):
     for name, f in cases.items():
         for _ in range(warmup):
             f()
+        ramp(f)
         torch.cuda.synchronize()
-        ts = []
+        evs = []
         for _ in range(steps):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
             f()
             b.record()
-            torch.cuda.synchronize()
-            ts.append(a.elapsed_time(b) * 1e3)
-        us = sorted(ts)[len(ts) // 2]
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        us = _median_ms(evs) * 1e3
         out[name] = {"us": round(us, 1), "rate": round(flops / (us * 1e-6) / 1e12, 1),
                      "unit": "TOP/s" if "int8" in name else "TFLOP/s"}
     return {"workload": f"{M}x{K}x{N}", "gemms": out}
@@ -294,6 +308,29 @@ def cpu_baseline(inp, target_s=12.0, chunk=256):
     }
 
 
+# milliseconds of untimed work before each timed region (--ramp-ms)
+RAMP_MS = 200.0
+
+
+def ramp(f, ramp_ms=None):
+    """Runs f() untimed, in batches of 4 calls, until ramp_ms milliseconds
+    of GPU time have passed since the first call (at least one batch)."""
+    import torch
+
+    ramp_ms = RAMP_MS if ramp_ms is None else ramp_ms
+    if ramp_ms <= 0:
+        return
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    while True:
+        for _ in range(4):
+            f()
+        b.record()
+        b.synchronize()
+        if a.elapsed_time(b) >= ramp_ms:
+            return
+
+
 def _median_ms(evs):
     import numpy as np
 
@@ -314,6 +351,7 @@ def measure_ceilings(dev):
     def timed(f, n=5, warm=2):
         for _ in range(warm):
             f()
+        ramp(f)
         evs = []
         for _ in range(n):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -393,6 +431,8 @@ def layer_bench(inp, steps, warmup, rotate, dev, extra=False):
 
     for i in range(warmup):
         step(sets[i % len(sets)])
+    nxt = iter(range(1 << 62))
+    ramp(lambda: step(sets[next(nxt) % len(sets)]))
     torch.cuda.synchronize()
     evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in names]
            for _ in range(steps)]
@@ -421,6 +461,7 @@ def layer_bench(inp, steps, warmup, rotate, dev, extra=False):
         reps = max(1, n_steps // per_graph)
         for _ in range(max(1, warmup // per_graph)):
             g.replay()
+        ramp(g.replay)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         a.record()
@@ -463,6 +504,8 @@ def per_call_ms(f, sets, steps, warmup):
 
     for i in range(warmup):
         f(sets[i % len(sets)])
+    nxt = iter(range(1 << 62))
+    ramp(lambda: f(sets[next(nxt) % len(sets)]))
     evs = []
     for i in range(steps):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -564,6 +607,7 @@ def stack_bench(steps, warmup, dev):
             raise SystemExit(f"bench.py: stack graph replay differs from the eager step (layer {i})")
     for _ in range(max(1, warmup)):
         g.replay()
+    ramp(g.replay)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     a.record()
@@ -644,6 +688,8 @@ def stack_memory(dev):
 
 def main():
     args = parse()
+    global RAMP_MS
+    RAMP_MS = args.ramp_ms
     if args.summarize_pmc:
         out = summarize_pmc(*args.summarize_pmc)
         out["workload"] = args.workload
@@ -775,6 +821,7 @@ def main():
                    "w_dtype": inp["w_dtype"], "rotating_buffer_sets": args.rotate},
         "roofline": roofline,
         "ms_per_step_warm": round(r["ms_per_step_warm"], 4),
+        "ramp_ms": RAMP_MS,
         "ternary_fractions": ternary,
         "gemm_mfma_frac": gemm_frac,
         "gemm_mfma_frac_of_measured": gemm_frac_meas,
