@@ -113,10 +113,15 @@ def vendor_gemms(inp, steps, warmup):
     """The three products of one layer as plain library GEMMs through torch
     (hipBLASLt on this image): the INT8 forward (torch._int_mm, x_q [M][K] by
     the codes as int8 [K][N]), dX = dY [M][N] . W [N][K] and dW = dY^T . x
-    in bf16, all operands contiguous (dY^T stored transposed). Medians of `steps`
-    back-to-back calls timed with HIP events after `warmup` calls and the
-    clock ramp, as the path's own calls are; nothing of the path itself."""
+    in bf16, all operands contiguous (dY^T stored transposed); next to them,
+    this library's calls on the workload's own inputs: bitlinear_fwd and
+    bitlinear_bwd with dX only, dW only (each with its pre-pass) and both.
+    Medians of `steps` back-to-back calls timed with HIP events after
+    `warmup` calls and the clock ramp; the library GEMMs do none of the
+    path's conversion work."""
     import torch
+
+    from ternary_weight_quantization_amd import binding as B
 
     M, K, N = inp["M"], inp["K"], inp["N"]
     dev = torch.device("cuda:0")
@@ -134,9 +139,31 @@ def vendor_gemms(inp, steps, warmup):
         "dX_bf16 dY[M,N] @ W[N,K]": lambda: dY @ W,
         "dW_bf16 dY^T[N,M] @ x[M,K]": lambda: dYt @ x,
     }
-    out = {}
-    flops = 2.0 * M * N * K
-    for name, f in cases.items():
+    # this library on the workload's inputs
+    Kp = B.bitnet_k_pad(K)
+    wdt = torch.bfloat16 if inp["w_dtype"] == "bf16" else torch.float32
+    t = dict(W=_to_dev(inp["W"], wdt, dev), x=_to_dev(inp["x"], torch.bfloat16, dev),
+             dY=_to_dev(inp["dY"], torch.bfloat16, dev),
+             w_packed=torch.empty((N, Kp // 4), dtype=torch.uint8, device=dev),
+             gamma=torch.empty((1,), dtype=torch.float32, device=dev),
+             ws=torch.empty((B.bitnet_ternarize_workspace_bytes(N, K),), dtype=torch.uint8, device=dev),
+             x_q=torch.empty((M, Kp), dtype=torch.int8, device=dev),
+             s_x=torch.empty((M,), dtype=torch.float32, device=dev),
+             y=torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+             dX=torch.empty((M, K), dtype=torch.bfloat16, device=dev),
+             dW=torch.empty((N, K), dtype=wdt, device=dev))
+    B.bitnet_quantize(t["W"], t["x"], t["w_packed"], t["gamma"], t["x_q"], t["s_x"], t["ws"])
+    here = {
+        "fwd (bitlinear_fwd)": lambda: B.bitlinear_fwd(t["x_q"], t["s_x"], t["w_packed"], t["gamma"], K, t["y"]),
+        "dX (bitlinear_bwd, dX only)": lambda: B.bitlinear_bwd(t["dY"], t["x_q"], t["s_x"], t["w_packed"],
+                                                               t["gamma"], K, dX=t["dX"]),
+        "dW (bitlinear_bwd, dW only)": lambda: B.bitlinear_bwd(t["dY"], t["x_q"], t["s_x"], t["w_packed"],
+                                                               t["gamma"], K, dW=t["dW"]),
+        "dX + dW (bitlinear_bwd, one call)": lambda: B.bitlinear_bwd(t["dY"], t["x_q"], t["s_x"], t["w_packed"],
+                                                                     t["gamma"], K, dX=t["dX"], dW=t["dW"]),
+    }
+
+    def med_us(f):
         for _ in range(warmup):
             f()
         ramp(f)
@@ -149,10 +176,21 @@ def vendor_gemms(inp, steps, warmup):
             b.record()
             evs.append((a, b))
         torch.cuda.synchronize()
-        us = _median_ms(evs) * 1e3
+        return _median_ms(evs) * 1e3
+
+    flops = 2.0 * M * N * K
+    out = {}
+    for name, f in cases.items():
+        us = med_us(f)
         out[name] = {"us": round(us, 1), "rate": round(flops / (us * 1e-6) / 1e12, 1),
                      "unit": "TOP/s" if "int8" in name else "TFLOP/s"}
-    return {"workload": f"{M}x{K}x{N}", "gemms": out}
+    ours = {}
+    for name, f in here.items():
+        us = med_us(f)
+        work = flops * (2 if "+" in name else 1)
+        ours[name] = {"us": round(us, 1), "rate": round(work / (us * 1e-6) / 1e12, 1),
+                      "unit": "TOP/s" if name.startswith("fwd") else "TFLOP/s"}
+    return {"workload": f"{M}x{K}x{N}", "gemms": out, "here": ours}
 
 
 def _pmc_rows(d):
