@@ -35,6 +35,7 @@ oracle timed on a bounded sample of the headline workload.
 
 import argparse
 import hashlib
+import itertools
 import json
 import os
 import sys
@@ -469,7 +470,7 @@ def layer_bench(inp, steps, warmup, rotate, dev, extra=False):
 
     for i in range(warmup):
         step(sets[i % len(sets)])
-    nxt = iter(range(1 << 62))
+    nxt = itertools.count()
     ramp(lambda: step(sets[next(nxt) % len(sets)]))
     torch.cuda.synchronize()
     evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in names]
@@ -542,7 +543,7 @@ def per_call_ms(f, sets, steps, warmup):
 
     for i in range(warmup):
         f(sets[i % len(sets)])
-    nxt = iter(range(1 << 62))
+    nxt = itertools.count()
     ramp(lambda: f(sets[next(nxt) % len(sets)]))
     evs = []
     for i in range(steps):
