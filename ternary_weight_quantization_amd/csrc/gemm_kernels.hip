@@ -821,6 +821,12 @@ struct EpStage {
   }
 };
 
+// The bias values of the output tile being computed (FwdEpilogue<true>),
+// staged once per tile before its main loop so that the epilogue reads
+// them from LDS: each lane needs 16 groups of 4 per tile and reads each of
+// them in all four column passes.
+__shared__ __attribute__((aligned(16))) uint16_t s_tile_bias[kBI];
+
 // BIAS: a bf16 bias [N] is added before the rounding (a separate
 // instantiation, so that the plain epilogue keeps its registers).
 template <bool BIAS>
@@ -846,6 +852,31 @@ struct FwdEpilogue {
     return pre;
   }
   static constexpr int kWaveLds = EpStage<4>::kWaveBytes;  // the int32 pass needs the larger buffer
+  static constexpr bool kStagesBias = BIAS;
+  // bias[ti0 .. ti0 + kBI) into s_tile_bias (zeros past I); called by every
+  // thread of the block, after a barrier that ends the previous tile's
+  // epilogue and before the main loop's barriers that order it before this
+  // tile's epilogue
+  __device__ __forceinline__ void stage_bias(int ti0) const {
+    const int t = threadIdx.x;
+    if (t < kBI / 8) {
+      const int64_t n = (int64_t)ti0 + 8 * t;
+      uint4 v;
+      if (n + 8 <= I) {
+        v = *reinterpret_cast<const uint4*>(bias + n);
+      } else {
+        uint32_t d[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t lo = n + 2 * e < I ? bias[n + 2 * e] : 0u;
+          const uint32_t hi = n + 2 * e + 1 < I ? bias[n + 2 * e + 1] : 0u;
+          d[e] = lo | (hi << 16);
+        }
+        v = make_uint4(d[0], d[1], d[2], d[3]);
+      }
+      *reinterpret_cast<uint4*>(s_tile_bias + 8 * t) = v;
+    }
+  }
   __device__ __forceinline__ void store(MfmaI8::Acc (&acc)[kFI][kFJ], const Pre& pre, int i0, int j0,
                                         int lane, char* wlds) const {
     const float g = pre.g;
@@ -858,9 +889,10 @@ struct FwdEpilogue {
         for (int gi = 0; gi < 4; ++gi) {
           float v0 = (float)acc[fi][fj][4 * gi] * c, v1 = (float)acc[fi][fj][4 * gi + 1] * c;
           float v2 = (float)acc[fi][fj][4 * gi + 2] * c, v3 = (float)acc[fi][fj][4 * gi + 3] * c;
-          if constexpr (BIAS) {  // n = i0 + 32fi + 8gi + 4h + 0..3 (EpStage::put)
-            const float4 b = bias4(bias, I, i0 + 32 * fi + 8 * gi + 4 * (lane >> 5));
-            v0 += b.x; v1 += b.y; v2 += b.z; v3 += b.w;
+          if constexpr (BIAS) {  // n = i0 + 32fi + 8gi + 4h + 0..3 (EpStage::put); tiles start at multiples of kBI
+            const uint2 b = *reinterpret_cast<const uint2*>(s_tile_bias + (i0 % kBI) + 32 * fi + 8 * gi +
+                                                           4 * (lane >> 5));
+            v0 += bf16_lo(b.x); v1 += bf16_hi(b.x); v2 += bf16_lo(b.y); v3 += bf16_hi(b.y);
           }
           EpStage<2>::put(wlds, lane, fi, gi, make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)));
         }
@@ -1522,6 +1554,12 @@ __device__ __forceinline__ bool finish_piece(const SplitPlan& p, typename MT::Ac
   return true;
 }
 
+// Whether an epilogue stages per-tile data into LDS before the main loop.
+template <class EP, class = void>
+struct StagesBias : std::false_type {};
+template <class EP>
+struct StagesBias<EP, std::void_t<decltype(EP::kStagesBias)>> : std::integral_constant<bool, EP::kStagesBias> {};
+
 // The work of virtual workgroup v of a product: one whole tile (no split),
 // or its range of (tile, stage) iterations (stream-K).
 template <class MT, int MAP, class PL, class QL, class EP>
@@ -1544,6 +1582,10 @@ __device__ __forceinline__ void gemm_body(const PL& pl, const QL& ql, const EP& 
 #pragma unroll
         for (int fj = 0; fj < kFJ; ++fj) zero_acc(acc[fi][fj]);
       const typename EP::Pre pre = ep.prefetch(j0 + qrow0, lane);
+      if constexpr (StagesBias<EP>::value) {
+        __syncthreads();
+        ep.stage_bias(i0);
+      }
       run_stages<MT, MAP>(pl, ql, smem, acc, i0, j0, 0, plan.nstages, prow0, qrow0, lane, nullptr, 0);
       ep.store(acc, pre, i0 + prow0, j0 + qrow0, lane, smem + wave * EP::kWaveLds);
     }
@@ -1564,6 +1606,10 @@ __device__ __forceinline__ void gemm_body(const PL& pl, const QL& ql, const EP& 
       for (int fj = 0; fj < kFJ; ++fj) zero_acc(acc[fi][fj]);
 
     const typename EP::Pre pre = ep.prefetch(j0 + qrow0, lane);
+    if constexpr (StagesBias<EP>::value) {
+      __syncthreads();
+      ep.stage_bias(i0);
+    }
     run_stages<MT, MAP>(pl, ql, smem, acc, i0, j0, s0, s1, prow0, qrow0, lane, pending, plan.gen);
     pending = nullptr;
     if ((s0 == 0 && s1 == plan.nstages) || finish_piece<MT>(plan, acc, v, t, &s_flag))

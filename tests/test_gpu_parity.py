@@ -515,22 +515,25 @@ def test_skinny_dw(M, K, N, wd):
     assert np.array_equal(g["dW"], g2["dW"])
 
 
-@pytest.mark.parametrize("M,K,N", [
-    (64, 256, 128),     # few tokens
-    (17, 1000, 777),    # few tokens, N % 4 != 0
-    (300, 1000, 777),   # large-M GEMM, ragged
-    (1024, 2560, 1536),
+@pytest.mark.parametrize("M,K,N,split", [
+    (64, 256, 128, None),     # few tokens
+    (17, 1000, 777, None),    # few tokens, N % 4 != 0
+    (300, 1000, 777, None),   # large-M GEMM, ragged
+    (300, 1000, 777, 7),      # the same, stream-K pieces over 7 workgroups
+    (1024, 2560, 1536, None),
 ])
-def test_bias_forward_and_grad(M, K, N):
+def test_bias_forward_and_grad(M, K, N, split, set_knobs):
     """Forward with a bias (bitlinear_fwd_bias) and the bias gradient
     (bitlinear_bias_grad): acc bit-exact, y against the oracle's
     forward_y_bias, db (f32 and bf16) against the oracle's exact column
     sums; db bitwise repeatable."""
     from ternary_weight_quantization_amd import binding as B
+    if split is not None:
+        set_knobs(split_ctas=split)
     inp = WL.custom_inputs(M, K, N, seed=13 * M + N)
     rng = np.random.Generator(np.random.PCG64(M + K + N))
     b_bits = WL.f32_to_bf16_bits(rng.normal(0.0, 0.5, N).astype(np.float32))
-    note(f"bias M={M} K={K} N={N}")
+    note(f"bias M={M} K={K} N={N} split={split}")
     dev = torch.device("cuda")
     Kp = O.k_pad(K)
     W, x, dY, bias = dev_bf16(inp["W"]), dev_bf16(inp["x"]), dev_bf16(inp["dY"]), dev_bf16(b_bits)
