@@ -91,7 +91,10 @@ size_t bitnet_ternarize_workspace_bytes(int64_t N, int64_t K);
  * transient operand at the start of the workspace: dX the ternary codes
  * transposed to fp4 [Kp][Np/2] (Kp*Np/2 bytes, Np = N rounded up to 64), dW
  * a bf16 x_hat = bf16(x_q * s/127) [M][Kp] (2*M*Kp bytes); a call with
- * both outputs builds both, one after the other, in one launch. */
+ * both outputs builds both, one after the other, in one launch. For at most
+ * 64 tokens a bf16 or f32 dW converts its slices of x_hat itself and needs
+ * no workspace, and a call with both outputs builds only the fp4 codes, in
+ * the launch that also computes dW. */
 size_t bitlinear_fwd_workspace_bytes(int64_t M, int64_t N, int64_t K);
 size_t bitlinear_bwd_workspace_bytes(int64_t M, int64_t N, int64_t K);
 

@@ -546,12 +546,13 @@ constexpr int kTrPitch = 512 + 64;
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 
-struct TrFrags {
+template <int PITCH>
+struct TrFragsP {
   MfmaBf16::Frag buf[2][4];
   const char* base;
   __device__ __forceinline__ void init(const char* tile, int row0, int lane) {
     const int g = lane >> 4, e = (lane >> 2) & 3, q = lane & 3;
-    base = tile + (8 * (g >> 1) + e) * kTrPitch + 2 * (row0 + 16 * (g & 1) + 4 * q);
+    base = tile + (8 * (g >> 1) + e) * PITCH + 2 * (row0 + 16 * (g & 1) + 4 * q);
   }
   static __device__ __forceinline__ v4i16_t tr(const char* p) {
     typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
@@ -559,8 +560,8 @@ struct TrFrags {
   }
   template <int KS>
   __device__ __forceinline__ void read(int f) {
-    const char* a = base + 16 * KS * kTrPitch + 64 * f;
-    const v4i16_t lo = tr(a), hi = tr(a + 4 * kTrPitch);
+    const char* a = base + 16 * KS * PITCH + 64 * f;
+    const v4i16_t lo = tr(a), hi = tr(a + 4 * PITCH);
     typedef short v8i16_t __attribute__((ext_vector_type(8)));
     const v8i16_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     buf[KS & 1][f] = __builtin_bit_cast(MfmaBf16::Frag, v);
@@ -584,6 +585,8 @@ struct TrFrags {
   template <int KS>
   __device__ __forceinline__ MfmaBf16::Frag frag(int f) const { return buf[KS & 1][f]; }
 };
+
+using TrFrags = TrFragsP<kTrPitch>;
 
 // Copy loader for TrFrags tiles from a bf16 [m][ld] matrix whose first
 // `cols` columns are the operand rows (x_hat: ld = cols = Kp; dY: ld = cols
@@ -647,26 +650,31 @@ struct RowCopyBf16Loader {
 // per output tile column. Thread t converts 16 int8 of row m: each byte is
 // biased to [1, 255] so that u*r - 128r = x_q*r exactly before the single
 // rounding of the fma.
+// 16 int8 of a row with scale factor r = s / 127 -> 16 bf16 (lo: values
+// 0..7, hi: 8..15). The one definition of x_hat's arithmetic: the pre-pass
+// and the few-token dW kernel, which converts its own slice, both call it.
+__device__ __forceinline__ void xhat16(uint4 v, float r, uint4& lo, uint4& hi) {
+  const float bias = -128.0f * r;
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o[8];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t u = w[d] ^ 0x80808080u;
+    o[2 * d] = pack_bf16x2(fmaf((float)(u & 0xFFu), r, bias), fmaf((float)((u >> 8) & 0xFFu), r, bias));
+    o[2 * d + 1] = pack_bf16x2(fmaf((float)((u >> 16) & 0xFFu), r, bias), fmaf((float)(u >> 24), r, bias));
+  }
+  lo = make_uint4(o[0], o[1], o[2], o[3]);
+  hi = make_uint4(o[4], o[5], o[6], o[7]);
+}
+
 __device__ __forceinline__ void xhat_blocks(const int8_t* __restrict__ xq, const float* __restrict__ s, int64_t M,
                                             int64_t Kp, uint16_t* __restrict__ xhat, int b, int nb) {
   const int64_t cpr = Kp / 16;  // 16-byte chunks per row
   const int64_t total = M * cpr;
   for (int64_t c = (int64_t)b * 256 + threadIdx.x; c < total; c += (int64_t)nb * 256) {
     const int64_t m = c / cpr;
-    const float r = s[m] / 127.0f;
-    const float bias = -128.0f * r;
-    const uint4 v = reinterpret_cast<const uint4*>(xq)[c];
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint32_t o[8];
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const uint32_t u = w[d] ^ 0x80808080u;
-      o[2 * d] = pack_bf16x2(fmaf((float)(u & 0xFFu), r, bias), fmaf((float)((u >> 8) & 0xFFu), r, bias));
-      o[2 * d + 1] = pack_bf16x2(fmaf((float)((u >> 16) & 0xFFu), r, bias), fmaf((float)(u >> 24), r, bias));
-    }
     uint4* dst = reinterpret_cast<uint4*>(xhat) + 2 * c;
-    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    xhat16(reinterpret_cast<const uint4*>(xq)[c], s[m] / 127.0f, dst[0], dst[1]);
   }
 }
 
@@ -1095,36 +1103,44 @@ __global__ __launch_bounds__(256) void ttq_grads_kernel(const float2* __restrict
 // x_hat[m][k] ("bitnet-qat-train", Semantics). The reduction is at most 4
 // MFMA steps of 16 tokens, so the cost is writing dW: small output tiles
 // (64 n x 256 k per workgroup) keep every CU busy with several tiles whose
-// loads and stores overlap. Both operands are staged as stored, rows m in
-// LDS (rows m >= M as zeros), and read transposed with ds_read_b64_tr_b16
-// (TrFrags): A = x_hat columns k (wave k half 128wk + 32f, f < 4), B = dY
-// columns n (wave n half 32wn). D[k][n] goes back through LDS as rows n and
-// is written as 16-byte row pieces (element by element when K does not
-// keep them aligned). Products are exact in fp32 and each sum runs in
-// token order.
+// loads and stores overlap. The tile's slice of x_hat is converted from
+// x_q and s on the way into LDS (xhat16, the pre-pass's arithmetic), so no
+// pre-pass runs and the tiles can share a launch with the code transpose
+// that the few-token dX needs. Both operands are staged as stored, rows m
+// in LDS (rows m >= M as zeros), and read transposed with
+// ds_read_b64_tr_b16 (TrFrags): A = x_hat columns k (wave k half 128wk +
+// 32f, f < 4), B = dY columns n (wave n half 32wn). D[k][n] goes back
+// through LDS as rows n and is written as 16-byte row pieces (element by
+// element when K does not keep them aligned). Products are exact in fp32
+// and each sum runs in token order. Tile b of ktiles x ceil(N / 64), 256
+// threads.
 template <bool OUT_F32>
-__global__ __launch_bounds__(256) void dw_skinny_kernel(const uint16_t* __restrict__ xhat,
-                                                        const uint16_t* __restrict__ dY, int M, int64_t N,
-                                                        int64_t Kp, int64_t K, int ktiles, void* __restrict__ dW) {
+__device__ __forceinline__ void dw_skinny_tile(const int8_t* __restrict__ xq, const float* __restrict__ sx,
+                                               const uint16_t* __restrict__ dY, int M, int64_t N, int64_t Kp,
+                                               int64_t K, int ktiles, void* __restrict__ dW, int b) {
   constexpr int kEB = OUT_F32 ? 4 : 2;
   constexpr int kOutPitch = 256 * kEB + 16;
-  constexpr int kTileB = 64 * kTrPitch;  // 64 token rows of one operand
+  constexpr int kYPitch = 64 * 2 + 16;     // dY rows: 64 n, padded
+  constexpr int kXB = 64 * kTrPitch;       // 64 token rows of x_hat
+  constexpr int kInB = kXB + 64 * kYPitch;
   constexpr int kOutB = 64 * kOutPitch;
-  __shared__ __attribute__((aligned(16))) char smem[2 * kTileB > kOutB ? 2 * kTileB : kOutB];
-  char* xs = smem;           // x_hat [m][256 k]
-  char* ys = smem + kTileB;  // dY [m][64 n]
+  __shared__ __attribute__((aligned(16))) char smem[kInB > kOutB ? kInB : kOutB];
+  char* xs = smem;        // x_hat [m][256 k]
+  char* ys = smem + kXB;  // dY [m][64 n]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t k0 = (int64_t)(blockIdx.x % ktiles) * 256, n0 = (int64_t)(blockIdx.x / ktiles) * 64;
+  const int64_t k0 = (int64_t)(b % ktiles) * 256, n0 = (int64_t)(b / ktiles) * 64;
   const int ms = (M + 15) / 16;  // MFMA steps of 16 tokens
 
-  const rsrc_t rxh = make_rsrc(xhat, (uint32_t)(M * Kp * 2));
+  const rsrc_t rxq = make_rsrc(xq, (uint32_t)(M * Kp));
   const rsrc_t rdy = make_rsrc(dY, (uint32_t)(M * N * 2));
-  uint4 vx[8], vy[2];
+  uint4 vq[4], vy[2];
+  float rq[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {  // x_hat: rows m < 16 ms, 32 pieces of 16 bytes per row
-    const int e = tid + 256 * i, m = e >> 5;
-    const int64_t k = k0 + 8 * (e & 31);
-    vx[i] = buf_load16(rxh, m < M && k < Kp ? (uint32_t)((m * Kp + k) * 2) : kOob);
+  for (int i = 0; i < 4; ++i) {  // x_q: rows m < 64, 16 pieces of 16 bytes per row
+    const int e = tid + 256 * i, m = e >> 4;
+    const int64_t k = k0 + 16 * (e & 15);
+    vq[i] = buf_load16(rxq, m < M && k < Kp ? (uint32_t)(m * Kp + k) : kOob);
+    rq[i] = m < M ? sx[m] / 127.0f : 0.0f;
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i) {  // dY: rows m < 64, 8 pieces per row
@@ -1133,19 +1149,26 @@ __global__ __launch_bounds__(256) void dw_skinny_kernel(const uint16_t* __restri
     vy[i] = buf_load16(rdy, m < M && n < N ? (uint32_t)((m * N + n) * 2) : kOob);
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 4; ++i) {  // zeros past M (and past Kp) convert to 0
     const int e = tid + 256 * i;
-    if ((e >> 5) < 16 * ms) *reinterpret_cast<uint4*>(xs + (e >> 5) * kTrPitch + 16 * (e & 31)) = vx[i];
+    if ((e >> 4) < 16 * ms) {
+      uint4 lo, hi;
+      xhat16(vq[i], rq[i], lo, hi);
+      char* dst = xs + (e >> 4) * kTrPitch + 32 * (e & 15);
+      *reinterpret_cast<uint4*>(dst) = lo;
+      *reinterpret_cast<uint4*>(dst + 16) = hi;
+    }
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int e = tid + 256 * i;
-    if ((e >> 3) < 16 * ms) *reinterpret_cast<uint4*>(ys + (e >> 3) * kTrPitch + 16 * (e & 7)) = vy[i];
+    if ((e >> 3) < 16 * ms) *reinterpret_cast<uint4*>(ys + (e >> 3) * kYPitch + 16 * (e & 7)) = vy[i];
   }
   __syncthreads();
 
   const int wn = wave & 1, wk = wave >> 1;
-  TrFrags fa, fb;
+  TrFrags fa;
+  TrFragsP<kYPitch> fb;
   fa.init(xs, 128 * wk, lane);
   fb.init(ys, 32 * wn, lane);
   MfmaBf16::Acc acc[4];
@@ -1203,6 +1226,32 @@ __global__ __launch_bounds__(256) void dw_skinny_kernel(const uint16_t* __restri
       }
     }
   }
+}
+
+template <bool OUT_F32>
+__global__ __launch_bounds__(256) void dw_skinny_kernel(const int8_t* __restrict__ xq, const float* __restrict__ sx,
+                                                        const uint16_t* __restrict__ dY, int M, int64_t N,
+                                                        int64_t Kp, int64_t K, int ktiles, void* __restrict__ dW) {
+  dw_skinny_tile<OUT_F32>(xq, sx, dY, M, N, Kp, K, ktiles, dW, blockIdx.x);
+}
+
+// Few tokens with both outputs, first launch: the first wt_bx * wt_by blocks
+// transpose the codes to fp4 for the few-token dX (which runs next), the
+// others compute dW tiles (independent of the transpose: ALU- and
+// latency-bound work next to the HBM writes of dW).
+template <bool OUT_F32>
+__global__ __launch_bounds__(256) void bwd_skinny_front_kernel(const uint8_t* __restrict__ packed, int64_t Np,
+                                                               uint8_t* __restrict__ wt, int wt_bx, int wt_by,
+                                                               const int8_t* __restrict__ xq,
+                                                               const float* __restrict__ sx,
+                                                               const uint16_t* __restrict__ dY, int M, int64_t N,
+                                                               int64_t Kp, int64_t K, int ktiles,
+                                                               void* __restrict__ dW) {
+  const int b = blockIdx.x, nwt = wt_bx * wt_by;
+  if (b < nwt)
+    wt_fp4_block(packed, N, Kp, Np, wt, b % wt_bx, b / wt_bx);
+  else
+    dw_skinny_tile<OUT_F32>(xq, sx, dY, M, N, Kp, K, ktiles, dW, b - nwt);
 }
 
 // ---------------------------------------------------------------------------
@@ -2040,28 +2089,44 @@ static hipError_t run_dw(const uint16_t* dY, const uint16_t* xhat, int64_t M, in
   return run_gemm<MfmaBf16, 0>(pl, RowTransposeBf16Loader<false, 5>{dY, N, M, N}, ep, g, split_ws, split_bytes, stream);
 }
 
-// The few-token dW (dw_skinny_kernel) on x_hat: N % 8 == 0, a bf16 or f32
-// output (the 1-bit output runs the large-M GEMM's epilogue).
+// The few-token dW (dw_skinny_kernel, x_hat converted in the kernel from x_q
+// and s): N % 8 == 0, a bf16 or f32 output (the 1-bit output runs the
+// large-M GEMM's epilogue).
 static bool dw_skinny_ok(int64_t M, int64_t N, int64_t K, DwOut dw_out) {
   const int64_t dw_tiles = (k_pad(K) + 255) / 256 * ((N + 63) / 64);
   return skinny(M) && N % 8 == 0 && dw_out != DwOut::kSign1 && dw_tiles < (int64_t(1) << 31);
 }
-static hipError_t launch_dw_skinny(const uint16_t* xhat, const uint16_t* dY, int64_t M, int64_t N, int64_t K,
-                                   void* dW, DwOut dw_out, hipStream_t stream) {
+static hipError_t launch_dw_skinny(const int8_t* x_q, const float* s_x, const uint16_t* dY, int64_t M, int64_t N,
+                                   int64_t K, void* dW, DwOut dw_out, hipStream_t stream) {
   const int64_t Kp = k_pad(K);
   const int ktiles = (int)((Kp + 255) / 256);
   const unsigned grid = (unsigned)((Kp + 255) / 256 * ((N + 63) / 64));
   if (dw_out == DwOut::kF32)
-    dw_skinny_kernel<true><<<grid, 256, 0, stream>>>(xhat, dY, (int)M, N, Kp, K, ktiles, dW);
+    dw_skinny_kernel<true><<<grid, 256, 0, stream>>>(x_q, s_x, dY, (int)M, N, Kp, K, ktiles, dW);
   else
-    dw_skinny_kernel<false><<<grid, 256, 0, stream>>>(xhat, dY, (int)M, N, Kp, K, ktiles, dW);
+    dw_skinny_kernel<false><<<grid, 256, 0, stream>>>(x_q, s_x, dY, (int)M, N, Kp, K, ktiles, dW);
   return hipGetLastError();
 }
 
-// Few tokens with both outputs: the two pre-passes (fp4 transposed codes,
-// x_hat) in one bwd_prep_kernel launch, then the few-token dX and dW kernels.
+// Few tokens with both outputs: one bwd_skinny_front_kernel launch (the fp4
+// transposed codes and every dW tile), then the few-token dX.
 static bool skinny_both_ok(int64_t M, int64_t N, int64_t K, DwOut dw_out) {
   return dw_skinny_ok(M, N, K, dw_out);  // dx_skinny needs N % 8 == 0 as well
+}
+static hipError_t launch_skinny_front(const uint8_t* w_packed, const int8_t* x_q, const float* s_x,
+                                      const uint16_t* dY, int64_t M, int64_t N, int64_t K, uint8_t* wt, void* dW,
+                                      DwOut dw_out, hipStream_t stream) {
+  const int64_t Kp = k_pad(K), Np = n_pad64(N);
+  const int wt_bx = (int)(Kp / 64), wt_by = (int)((Np + 255) / 256);
+  const int ktiles = (int)((Kp + 255) / 256);
+  const unsigned grid = (unsigned)(wt_bx * wt_by + (Kp + 255) / 256 * ((N + 63) / 64));
+  if (dw_out == DwOut::kF32)
+    bwd_skinny_front_kernel<true><<<grid, 256, 0, stream>>>(w_packed, Np, wt, wt_bx, wt_by, x_q, s_x, dY, (int)M, N,
+                                                            Kp, K, ktiles, dW);
+  else
+    bwd_skinny_front_kernel<false><<<grid, 256, 0, stream>>>(w_packed, Np, wt, wt_bx, wt_by, x_q, s_x, dY, (int)M, N,
+                                                             Kp, K, ktiles, dW);
+  return hipGetLastError();
 }
 static void launch_prep(const uint8_t* w_packed, const int8_t* x_q, const float* s_x, int64_t M, int64_t N,
                         int64_t K, uint8_t* wt, uint16_t* xhat, hipStream_t stream) {
@@ -2076,13 +2141,13 @@ static void launch_prep(const uint8_t* w_packed, const int8_t* x_q, const float*
 hipError_t launch_bwd_dw(const uint16_t* dY, const int8_t* x_q, const float* s_x, int64_t M,
                          int64_t N, int64_t K, void* dW, DwOut dw_out, void* ws, size_t ws_bytes,
                          hipStream_t stream) {
+  if (dw_skinny_ok(M, N, K, dw_out)) return launch_dw_skinny(x_q, s_x, dY, M, N, K, dW, dw_out, stream);
   const size_t xb = xhat_bytes(M, K);
   if (ws == nullptr || ws_bytes < xb) return hipErrorInvalidValue;  // the C ABI sized it
   uint16_t* xhat = static_cast<uint16_t*>(ws);
   void* split_ws = static_cast<char*>(ws) + xb;
   const size_t split_bytes = ws_bytes - xb;
   if (hipError_t e = launch_xhat(x_q, s_x, M, K, xhat, stream)) return e;
-  if (dw_skinny_ok(M, N, K, dw_out)) return launch_dw_skinny(xhat, dY, M, N, K, dW, dw_out, stream);
   switch (dw_out) {
     case DwOut::kF32: return run_dw(dY, xhat, M, N, K, Bf16Epilogue<true>{dW, nullptr, K, N}, split_ws, split_bytes, stream);
     case DwOut::kSign1:
@@ -2154,9 +2219,9 @@ size_t gemm_workspace_bytes(GemmKind kind, int64_t M, int64_t N, int64_t K) {
     case GemmKind::kBwdDw: return xhat_bytes(M, K) + alone(kind);
     case GemmKind::kBwdPair: {
       // (any dW output: the sign output of few tokens takes the separate route)
-      if (skinny_both_ok(M, N, K, DwOut::kBf16))
-        return std::max(wt_bytes(N, K) + xhat_bytes(M, K), std::max(gemm_workspace_bytes(GemmKind::kBwdDx, M, N, K),
-                                                                    gemm_workspace_bytes(GemmKind::kBwdDw, M, N, K)));
+      if (skinny_both_ok(M, N, K, DwOut::kBf16))  // the 1-bit dW output runs the two products separately
+        return std::max(wt_bytes(N, K), std::max(gemm_workspace_bytes(GemmKind::kBwdDx, M, N, K),
+                                                 gemm_workspace_bytes(GemmKind::kBwdDw, M, N, K)));
       if (pair_eligible(M, N, K) && pair_split_bytes(M, N, K) > 0)
         return std::max(wt_bytes(N, K) + xhat_bytes(M, K) + pair_split_bytes(M, N, K),
                         std::max(wt_bytes(N, K), xhat_bytes(M, K)));
@@ -2175,13 +2240,10 @@ size_t gemm_workspace_bytes(GemmKind kind, int64_t M, int64_t N, int64_t K) {
 hipError_t launch_bwd_pair(const uint16_t* dY, const uint8_t* w_packed, const float* gamma, const int8_t* x_q,
                            const float* s_x, int64_t M, int64_t N, int64_t K, uint16_t* dX, void* dW,
                            DwOut dw_out, void* ws, size_t ws_bytes, hipStream_t stream) {
-  if (ws != nullptr && skinny_both_ok(M, N, K, dw_out) && ws_bytes >= wt_bytes(N, K) + xhat_bytes(M, K)) {
+  if (ws != nullptr && skinny_both_ok(M, N, K, dw_out) && ws_bytes >= wt_bytes(N, K)) {
     uint8_t* wt = static_cast<uint8_t*>(ws);
-    uint16_t* xhat = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + wt_bytes(N, K));
-    launch_prep(w_packed, x_q, s_x, M, N, K, wt, xhat, stream);
-    if (hipError_t e = hipGetLastError()) return e;
-    if (hipError_t e = launch_dx_skinny(wt, dY, gamma, M, N, K, dX, stream)) return e;
-    return launch_dw_skinny(xhat, dY, M, N, K, dW, dw_out, stream);
+    if (hipError_t e = launch_skinny_front(w_packed, x_q, s_x, dY, M, N, K, wt, dW, dw_out, stream)) return e;
+    return launch_dx_skinny(wt, dY, gamma, M, N, K, dX, stream);
   }
   if (!pair_eligible(M, N, K) || ws == nullptr) return hipErrorNotSupported;
   const GemmShape g1 = shape_of(GemmKind::kBwdDx, M, N, K), g2 = shape_of(GemmKind::kBwdDw, M, N, K);

@@ -77,7 +77,10 @@ def test_size_queries(L):
     # x_hat [M][Kp], dX its fp4 transposed codes [Kp][Np/2]
     assert L.bitlinear_fwd_workspace_bytes(4096, 6912, 2560) == 0
     assert L.bitlinear_fwd_workspace_bytes(64, 128, 256) == 0
-    assert L.bitlinear_bwd_workspace_bytes(64, 128, 256) == 2 * 64 * 256 + 256 * 128 // 2
+    # few tokens (M <= 64): bf16 / f32 dW converts its own x_hat, so both
+    # outputs need only dX's fp4 codes [Kp][Np/2]; the size also covers the
+    # 1-bit dW output, which runs the large-M route with x_hat [M][Kp]
+    assert L.bitlinear_bwd_workspace_bytes(64, 128, 256) == max(2 * 64 * 256, 256 * 128 // 2)
     tile = 64 * 256 * 16
     # at 4096x2560->6912 the two backward products run in one launch: dX
     # stream-K over 15 columns of 8 workgroups (160 tiles on 120: 240
@@ -90,11 +93,11 @@ def test_size_queries(L):
     # needs none; one tile of 512 stages splits over 4 workgroups (4 slots)
     assert L.bitlinear_fwd_workspace_bytes(4096, 2560, 6912) == 0
     assert L.bitlinear_fwd_workspace_bytes(256, 256, 65536) == 256 + 4 * tile
-    # few tokens: the forward needs none; the backward only its two
-    # transient operands, built in one launch (the few-token dX and dW do not
-    # split): fp4 codes [Kp][N/2] and x_hat [M][Kp]
+    # few tokens: the forward needs none; the backward the larger of the fp4
+    # codes [Kp][N/2] (dX, which does not split) and x_hat [M][Kp] (the 1-bit
+    # dW route)
     assert L.bitlinear_fwd_workspace_bytes(32, 2560, 6912) == 0
-    assert L.bitlinear_bwd_workspace_bytes(32, 2560, 6912) == 6912 * 2560 // 2 + 2 * 32 * 6912
+    assert L.bitlinear_bwd_workspace_bytes(32, 2560, 6912) == max(6912 * 2560 // 2, 2 * 32 * 6912)
     assert L.bitlinear_fwd_workspace_bytes(0, 4, 4) == 0
     for code in range(7):
         assert L.bitnet_status_string(code).decode().startswith("BITNET_")
