@@ -25,7 +25,9 @@ are unchanged. --ramp-ms 0 measures straight after the warm-up steps.
 
 Prints one JSON line: throughput in effective TOPS (6*M*N*K per step), the
 step time (replays of the step captured in HIP graphs), per-call times (the
-median of `steps` eager calls timed with HIP events on the launch stream),
+median of `steps` eager calls timed with HIP events on the launch stream,
+enqueued behind about 30 ms of step replays so that the GPU never waits on
+the host inside a timed call),
 each call's fraction of the published peak and of the ceiling measured in
 the same run (a plain device copy; register-only MFMA chains), the combined
 GEMM fraction of the MFMA peak, the same summary for the other layer
@@ -349,6 +351,8 @@ def cpu_baseline(inp, target_s=12.0, chunk=256):
 
 # milliseconds of untimed work before each timed region (--ramp-ms)
 RAMP_MS = 200.0
+# GPU time enqueued ahead of each timed region of eager calls (lead())
+LEAD_MS = 30.0
 
 
 def ramp(f, ramp_ms=None):
@@ -472,15 +476,9 @@ def layer_bench(inp, steps, warmup, rotate, dev, extra=False):
         step(sets[i % len(sets)])
     nxt = itertools.count()
     ramp(lambda: step(sets[next(nxt) % len(sets)]))
+    for s in sets:  # every set's outputs from an eager step, the replays' reference
+        step(s)
     torch.cuda.synchronize()
-    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in names]
-           for _ in range(steps)]
-    for i in range(steps):
-        step(sets[i % len(sets)], evs[i])
-    torch.cuda.synchronize()
-    per_call = {n: _median_ms([tuple(evs[i][j]) for i in range(steps)]) for j, n in enumerate(names)}
-    per_call_mean = {n: float(np.mean([evs[i][j][0].elapsed_time(evs[i][j][1]) for i in range(steps)]))
-                     for j, n in enumerate(names)}
 
     # Step time: graph replays (host call overhead out of the timed region;
     # the same kernels and work as the eager step). One graph holds a step
@@ -523,35 +521,60 @@ def layer_bench(inp, steps, warmup, rotate, dev, extra=False):
     cold_ms = replay_ms(cold, len(sets), steps)
     warm = graph_of([sets[0]] * 4)
     warm_ms = replay_ms(warm, 4, steps)
-    del cold, warm
+    del warm
+
+    def lead():
+        # Replays of the step enqueued ahead of a timed region of eager
+        # calls (about LEAD_MS of GPU time, enqueued in far less host time),
+        # so that the host has launched every timed call before the GPU
+        # reaches it: each event pair then spans that call's own GPU work
+        # with the clocks in the state the step keeps, and no host launch
+        # time. Without it, a host slower than the GPU between two calls
+        # shows up in the later call's time.
+        for _ in range(max(1, int(LEAD_MS / (cold_ms * len(sets))) + 1)):
+            cold.replay()
+
+    # Per-call times inside whole eager steps (the calls in step order),
+    # after the lead: medians of `steps` steps.
+    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in names]
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    lead()
+    for i in range(steps):
+        step(sets[i % len(sets)], evs[i])
+    torch.cuda.synchronize()
+    per_call = {n: _median_ms([tuple(evs[i][j]) for i in range(steps)]) for j, n in enumerate(names)}
+    per_call_mean = {n: float(np.mean([evs[i][j][0].elapsed_time(evs[i][j][1]) for i in range(steps)]))
+                     for j, n in enumerate(names)}
     out = dict(M=M, K=K, N=N, w_dtype=inp["w_dtype"], per_call=per_call, per_call_mean=per_call_mean,
-               ms_per_step=cold_ms, ms_per_step_warm=warm_ms, sets=sets)
+               ms_per_step=cold_ms, ms_per_step_warm=warm_ms, sets=sets, lead=lead)
     if extra:
         # the separate quantization entry points (their own rows), per call
         ex = {
             "ternarize_pack": lambda s: B.bitnet_ternarize_pack(s["W"], s["w_packed"], s["gamma"], s["ws"]),
             "act_quant": lambda s: B.bitnet_act_quant(s["x"], s["x_q"], s["s_x"]),
         }
-        out["per_call"].update({n: per_call_ms(f, sets, steps, warmup) for n, f in ex.items()})
+        out["per_call"].update({n: per_call_ms(f, sets, steps, warmup, lead) for n, f in ex.items()})
     if not extra:
-        del out["sets"]
+        del out["sets"], out["lead"]
     return out
 
 
-def per_call_ms(f, sets, steps, warmup):
+def per_call_ms(f, sets, steps, warmup, lead):
+    """Median of `steps` back-to-back calls of f, each between two HIP
+    events, enqueued behind `lead` (GPU work that keeps the GPU busy and
+    its clocks in the step's state while the host launches them)."""
     import torch
 
     for i in range(warmup):
         f(sets[i % len(sets)])
-    nxt = itertools.count()
-    ramp(lambda: f(sets[next(nxt) % len(sets)]))
-    evs = []
-    for i in range(steps):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    lead()
+    for i, (a, b) in enumerate(evs):
         a.record()
         f(sets[i % len(sets)])
         b.record()
-        evs.append((a, b))
     torch.cuda.synchronize()
     return _median_ms(evs)
 
@@ -767,6 +790,7 @@ def main():
     Kp = B.bitnet_k_pad(K)
     r = layer_bench(inp, args.steps, args.warmup, args.rotate, dev, extra=True)
     sets = r.pop("sets")
+    lead = r.pop("lead")
     kernels, gemm_frac, gemm_frac_meas = layer_roofline(r, ceil)
     wdt = torch.bfloat16 if inp["w_dtype"] == "bf16" else torch.float32
 
@@ -801,7 +825,7 @@ def main():
         "ttq_bwd": lambda s: B.ttq_bwd(s["dY"], s["x"], s["ttq_wt"], s["ttq_codes"], K, dX=s["dX"], dW=s["dW"],
                                        grads=s["ttq_grads"], workspace=ttq_ws),
     }
-    xms = {n: per_call_ms(f, sets, args.steps, args.warmup) for n, f in xc.items()}
+    xms = {n: per_call_ms(f, sets, args.steps, args.warmup, lead) for n, f in xc.items()}
     # shares of -1 / 0 / +1 in the ternary weight ("bitlinear.py", ternary_stats),
     # from the packed codes of the step (exact counts on the GPU)
     counts = torch.empty((2,), dtype=torch.int64, device=dev)
@@ -809,7 +833,7 @@ def main():
     neg, pos = (int(v) for v in counts.cpu())
     ternary = {"minus_one": round(neg / (N * K), 6), "zero": round((N * K - neg - pos) / (N * K), 6),
                "plus_one": round(pos / (N * K), 6)}
-    del sets
+    del sets, lead
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
 
