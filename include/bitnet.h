@@ -100,9 +100,13 @@ size_t bitlinear_bwd_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /*
  * bitnet_ternarize_pack - per-tensor absmean scale, RoundClip ternarization
- * and 2-bit packing of the master weight, in one fused pass over W plus a
- * reduction pass ("bitnet-qat-train", opening bullets; "bitlinear.py",
- * ternary_quantize; "1BitTraining.md", weight_quant).
+ * and 2-bit packing of the master weight ("bitnet-qat-train", opening
+ * bullets: one fused ternarize, scale and pack pass; "bitlinear.py",
+ * ternary_quantize; "1BitTraining.md", weight_quant). For bf16 W with K a
+ * multiple of 64 and N*K up to about 25 M, W is read once: one launch holds
+ * it in registers while its workgroups exchange their partial sums through
+ * the workspace, then writes the codes. Otherwise a reduction pass over W
+ * and a fused ternarize + pack pass. Both give the same bits.
  *
  *   gamma = max(fp32(S / (N*K)), 1e-8f), S = sum |W| accumulated in fp64 in
  *           a fixed order (bitwise deterministic across calls);
@@ -120,7 +124,10 @@ size_t bitlinear_bwd_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *           codes of k = 16w+4t..16w+4t+3 in its four bytes.)
  * gamma     [1] output float (device).
  * workspace device scratch of at least bitnet_ternarize_workspace_bytes();
- *           no initialization needed; clobbered.
+ *           no initialization needed (the words that publish partial sums
+ *           between workgroups carry a per-launch tag and sequence, so
+ *           whatever the memory held never matches); clobbered. Calls that
+ *           may run at the same time must not share a workspace.
  */
 bitnet_status bitnet_ternarize_pack(const void* W, bitnet_dtype w_dtype,
                                     int64_t N, int64_t K,
@@ -131,9 +138,11 @@ bitnet_status bitnet_ternarize_pack(const void* W, bitnet_dtype w_dtype,
 /*
  * bitnet_quantize - bitnet_ternarize_pack and bitnet_act_quant of one layer
  * step in one call, with the same results bit for bit (gamma, w_packed,
- * x_q, s_x). The weight's absmean pass and the activation quantization
- * share one launch (two independent streams over W and x), then the codes
- * are packed. The two inputs share the reduction length K: W [N][K], x
+ * x_q, s_x). The activation rows are quantized in the weight's launch: in
+ * the one-pass case each workgroup quantizes its share of the rows while
+ * the others' partial sums arrive; otherwise the absmean pass and the rows
+ * share one launch (two independent streams over W and x) and the codes are
+ * packed after it. The two inputs share the reduction length K: W [N][K], x
  * [M][K]. Arguments, layouts and errors are those of the two calls;
  * workspace as bitnet_ternarize_pack's.
  */
@@ -146,12 +155,14 @@ bitnet_status bitnet_quantize(const void* W, bitnet_dtype w_dtype, int64_t N, in
  * bitnet_quantize_static - bitnet_quantize for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation): no workspace argument; the scratch
- * (the weight absmean's fp64 partial sums) lives in a device array of the
- * library, 4096 bytes per GPU the library runs on, held until the process
- * ends. Results are bit for bit those of bitnet_quantize. The array keeps
- * the last call's contents; every call overwrites what it reads, so none
- * needs clearing, but calls that may run at the same time on one GPU race
- * on it. Returns BITNET_ERR_WORKSPACE if a call would need more scratch
+ * (the weight absmean's fp64 partial sums, and the one-pass launch's
+ * per-workgroup records of partial and publication word) lives in a device
+ * array of the library, 8192 bytes per GPU the library runs on, held until
+ * the process ends. Results are bit for bit those of bitnet_quantize. The
+ * array keeps the last call's contents; no call needs it cleared (partials
+ * are written before they are read; publication words are tagged per launch
+ * and never match a later launch's), but calls that may run at the same
+ * time on one GPU race on it. Returns BITNET_ERR_WORKSPACE if a call would need more scratch
  * than the array holds (not the case for any size: the need is fixed at
  * bitnet_ternarize_workspace_bytes()), BITNET_ERR_HIP if the array's device
  * address cannot be obtained; otherwise the arguments and errors of
@@ -413,9 +424,16 @@ bitnet_status ttq_bwd(const uint16_t* dY, const uint16_t* x, const uint16_t* wt,
  *               bitnet_default_spin_limit(), is about a second. A wait
  *               that gives up writes its output tile as NaN (int32
  *               accumulators: INT32_MIN) and is counted.
+ *               The one-pass weight quantization waits the same number
+ *               of polls for the other workgroups' partial sums; when it
+ *               gives up, a workgroup computes the missing sums itself
+ *               (same results, more reads of W) and counts each.
  * bitnet_split_timeouts - the number of such waits that gave up on the
  *   current device since the last call (then reset to 0). Synchronizes the
  *   device. BITNET_ERR_HIP if the runtime fails.
+ * bitnet_quantize_recomputes - the number of partial sums one-pass
+ *   launches computed themselves on the current device since the last call
+ *   (then reset to 0). Synchronizes the device.
  * bitnet_debug_split_pieces - the pieces a split launch of `tiles` tiles of
  *   `stages` reduction stages over `grid` workgroups (grid <= tiles*stages)
  *   runs, computed on the host by the functions the kernels use: for each
@@ -436,6 +454,7 @@ bitnet_status ttq_bwd(const uint16_t* dY, const uint16_t* x, const uint16_t* wt,
 void bitnet_set_test_knobs(int split_ctas, int pair_cols, int no_skinny, uint32_t spin_limit);
 uint32_t bitnet_default_spin_limit(void);
 bitnet_status bitnet_split_timeouts(uint32_t* count);
+bitnet_status bitnet_quantize_recomputes(uint32_t* count);
 int64_t bitnet_debug_split_pieces(int64_t tiles, int32_t stages, int32_t grid, int32_t* v, int32_t* t,
                                   int32_t* s0, int32_t* s1, int64_t* slot, int32_t* va, int32_t* n,
                                   int64_t cap);

@@ -97,6 +97,8 @@ def lib():
     L.bitnet_default_spin_limit.restype = u32
     L.bitnet_split_timeouts.argtypes = [vp]
     L.bitnet_split_timeouts.restype = st
+    L.bitnet_quantize_recomputes.argtypes = [vp]
+    L.bitnet_quantize_recomputes.restype = st
     L.bitnet_debug_split_pieces.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp, vp, vp, i64]
     L.bitnet_debug_split_pieces.restype = i64
     L.bitnet_debug_partial_slots.argtypes = [i64, i32]
@@ -448,6 +450,14 @@ def bitnet_split_timeouts():
     the device)."""
     c = ctypes.c_uint32(0)
     _check(lib().bitnet_split_timeouts(ctypes.byref(c)))
+    return int(c.value)
+
+
+def bitnet_quantize_recomputes():
+    """Partial sums one-pass quantize launches computed themselves after
+    their wait gave up, since the last call (synchronizes the device)."""
+    c = ctypes.c_uint32(0)
+    _check(lib().bitnet_quantize_recomputes(ctypes.byref(c)))
     return int(c.value)
 
 

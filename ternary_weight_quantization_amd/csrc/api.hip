@@ -73,9 +73,7 @@ const char* bitnet_status_string(bitnet_status status) {
 
 int64_t bitnet_k_pad(int64_t K) { return K < 1 ? 0 : bitnet::k_pad(K); }
 
-size_t bitnet_ternarize_workspace_bytes(int64_t, int64_t) {
-  return sizeof(double) * bitnet::kAbsmeanBlocks;
-}
+size_t bitnet_ternarize_workspace_bytes(int64_t, int64_t) { return bitnet::quant_workspace_bytes(); }
 
 size_t bitlinear_fwd_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (check_gemm_sizes(M, N, K) != BITNET_OK) return 0;
@@ -320,6 +318,14 @@ bitnet_status bitnet_split_timeouts(uint32_t* count) {
   if (!count) return BITNET_ERR_NULL;
   unsigned int c = 0;
   const hipError_t e = bitnet::take_split_timeouts(&c);
+  *count = c;
+  return from_hip(e);
+}
+
+bitnet_status bitnet_quantize_recomputes(uint32_t* count) {
+  if (!count) return BITNET_ERR_NULL;
+  unsigned int c = 0;
+  const hipError_t e = bitnet::take_onepass_recomputes(&c);
   *count = c;
   return from_hip(e);
 }

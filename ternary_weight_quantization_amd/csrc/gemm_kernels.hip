@@ -1898,6 +1898,8 @@ static uint64_t next_gen() {
   return g;
 }
 
+uint64_t next_launch_tag() { return next_gen(); }
+
 // Cost model of one product on G workgroups, in dX stage times (measured
 // at 4096x2560->6912): a tile's pipeline fill and epilogue cost about 5.4
 // stages. Per product, the cost of a stage and of each piece of a split

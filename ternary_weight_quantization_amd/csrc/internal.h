@@ -56,6 +56,26 @@ constexpr int kAbsmeanThreads = 512;
 
 inline int64_t k_pad(int64_t K) { return ((K + 63) / 64) * 64; }
 
+// A fresh tag for a launch that synchronizes its workgroups through tagged
+// words in a workspace (nonzero, 48 bits, different for every launch).
+uint64_t next_launch_tag();
+
+// The one-pass weight ternarization (W read once, held in registers between
+// gamma's reduction and the codes), alone or with the activation rows:
+// used for bf16 W with K % 64 == 0 and N * K up to the register capacity.
+// ws: the ternarize workspace (quant_workspace_bytes()). x == nullptr: no
+// activation rows (with_rows false).
+bool onepass_ok(bool w_is_f32, int64_t N, int64_t K, bool with_rows);
+void launch_onepass(const uint16_t* W, int64_t N, int64_t K, void* ws, uint32_t* packed, float* gamma,
+                    const uint16_t* x, int64_t M, int8_t* xq, float* s, hipStream_t st);
+// Bytes of the ternarize workspace: the fp64 absmean partials, then the
+// one-pass kernel's publication flags and departure counter.
+size_t quant_workspace_bytes();
+// Partials one-pass launches computed themselves after an absent flag,
+// since the last call (read and cleared on the current device;
+// synchronizes the device).
+hipError_t take_onepass_recomputes(unsigned int* count);
+
 // Weight ternarization: fp64 absmean partials, then gamma + codes + packing.
 hipError_t launch_ternarize_pack(const void* W, bool w_is_f32, int64_t N, int64_t K,
                                  uint8_t* w_packed, float* gamma, double* partials,

@@ -57,8 +57,7 @@ __device__ __forceinline__ float load_elem(const void* w, int64_t i) {
 // on the grid constants, never on the launch, so every kernel that runs
 // this body (alone or next to other work) gives gamma the same bits.
 template <bool F32>
-__device__ __forceinline__ void absmean_block(const void* __restrict__ w, int64_t n, double* __restrict__ partials,
-                                              int b) {
+__device__ __forceinline__ double absmean_thread_sum(const void* __restrict__ w, int64_t n, int b) {
   constexpr int kVec = F32 ? 4 : 8;  // elements per 16 bytes
   constexpr int kUnroll = 8;
   const uint4* wv = static_cast<const uint4*>(w);
@@ -80,19 +79,33 @@ __device__ __forceinline__ void absmean_block(const void* __restrict__ w, int64_
   for (; i < nvec; i += stride) acc[0] += abs_sum16<F32>(wv[i]);
   const int64_t tail = nvec * kVec;
   if (tid < n - tail) acc[1] += fabs((double)load_elem<F32>(w, tail + tid));
+  return ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+}
 
-  double v = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+// The block's thread sums -> its partial: a butterfly within each wave, then
+// thread 0 adds the wave sums in wave order. The partial is returned in
+// thread 0 (the other threads get 0). Called by all kAbsmeanThreads threads;
+// a caller that runs it again in the same block separates the two calls
+// with a barrier.
+__device__ __forceinline__ double absmean_block_reduce(double v) {
   v = wave_sum_f64(v);
   __shared__ double sw[kAbsmeanThreads / kWave];
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   if (lane == 0) sw[wave] = v;
   __syncthreads();
+  double t = 0.0;
   if (threadIdx.x == 0) {
-    double t = 0.0;
 #pragma unroll
     for (int j = 0; j < kAbsmeanThreads / kWave; ++j) t += sw[j];
-    partials[b] = t;
   }
+  return t;
+}
+
+template <bool F32>
+__device__ __forceinline__ void absmean_block(const void* __restrict__ w, int64_t n, double* __restrict__ partials,
+                                              int b) {
+  const double t = absmean_block_reduce(absmean_thread_sum<F32>(w, n, b));
+  if (threadIdx.x == 0) partials[b] = t;
 }
 
 template <bool F32>
@@ -227,6 +240,11 @@ hipError_t launch_pack(const void* W, bool w_is_f32, int64_t N, int64_t K, uint8
 hipError_t launch_ternarize_pack(const void* W, bool w_is_f32, int64_t N, int64_t K,
                                  uint8_t* w_packed, float* gamma, double* partials,
                                  hipStream_t stream) {
+  if (onepass_ok(w_is_f32, N, K, false)) {
+    launch_onepass(static_cast<const uint16_t*>(W), N, K, partials, reinterpret_cast<uint32_t*>(w_packed), gamma,
+                   nullptr, 0, nullptr, nullptr, stream);
+    return hipGetLastError();
+  }
   const int64_t n = N * K;
   if (w_is_f32)
     absmean_partials_kernel<true><<<kAbsmeanBlocks, kAbsmeanThreads, 0, stream>>>(W, n, partials);
@@ -385,11 +403,25 @@ __device__ __forceinline__ void act_quant_rows(const uint16_t* __restrict__ x, i
 
   uint4 v[CPT];
   float amax = 0.0f;
+  if constexpr (VEC) {
+    // Every load unconditional, all CPT in flight before the first use: a
+    // buffer resource over the row (none past M) returns zeros for chunks
+    // past K. (A load under a condition is waited for at the branch join,
+    // which turns the CPT loads into CPT dependent round trips.) Whole waves
+    // share a row, so the row index is uniform across the wave.
+    const int row_w = __builtin_amdgcn_readfirstlane((int)row);
+    const rsrc_t rx = make_rsrc(x + (int64_t)row_w * K, row_w < M ? (uint32_t)(K * 2) : 0u);
 #pragma unroll
-  for (int c = 0; c < CPT; ++c) {
-    const int64_t ch = t + (int64_t)c * TPR;
-    v[c] = (row_ok && ch * 8 < K) ? load_chunk<VEC>(xr, ch, K) : make_uint4(0, 0, 0, 0);
-    amax = fmaxf(amax, absmax8(v[c]));
+    for (int c = 0; c < CPT; ++c) v[c] = buf_load16(rx, (uint32_t)(t + c * TPR) * 16u);
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) amax = fmaxf(amax, absmax8(v[c]));
+  } else {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int64_t ch = t + (int64_t)c * TPR;
+      v[c] = (row_ok && ch * 8 < K) ? load_chunk<VEC>(xr, ch, K) : make_uint4(0, 0, 0, 0);
+      amax = fmaxf(amax, absmax8(v[c]));
+    }
   }
   amax = wave_max_f32(amax);
   if constexpr (WPR > 1) {
@@ -492,6 +524,301 @@ hipError_t launch_act_quant(const uint16_t* x, int64_t M, int64_t K, int8_t* x_q
 }
 
 // ---------------------------------------------------------------------------
+// One pass over W: the weight is read once. The grid is the absmean's fixed
+// grid (kAbsmeanBlocks blocks of kAbsmeanThreads threads), and each thread
+// keeps the 16-byte vectors it sums (those absmean_thread_sum reads) in
+// registers instead of dropping them. Each block publishes its partial,
+// quantizes its share of the activation rows (if any) while the other
+// blocks finish theirs, then reads all kAbsmeanBlocks partials, forms gamma
+// in the order ternarize_pack_kernel uses (so gamma, and every code, has the
+// bits of the two-pass path) and writes the codes of the vectors it holds.
+//
+// A code word is 16 consecutive k of one row; with K a multiple of 64 (no
+// row padding) word i / 2 is the pair of vectors i (codes 0..7) and i + 1
+// (codes 8..15). Both sit in adjacent lanes of one wave (the vector index
+// of a lane is b * kAbsmeanThreads + t + j * stride, stride even), so each
+// lane builds its half of the word's bits and one lane exchange joins them.
+//
+// Publication: each block owns a 16-byte record in the workspace: its
+// partial, then a publication word. It stores the partial, waits for the
+// store to complete, then stores the word (device-coherent stores). The
+// word is the launch's tag with a sequence number, so a word left by
+// another launch, or by an earlier replay of a captured graph (same tag,
+// smaller sequence), never matches: each block computes the expected word
+// from its own record's previous one, and all records move in step because
+// every launch rewrites each of them once. 256 threads of each block poll
+// the records, one each (a 16-byte volatile load, which returns a published
+// word together with its partial). No atomics and no counter to clear. No block ever waits on one that might not run: after `spin_limit`
+// polls (another kernel holding CUs so that not every block of this launch
+// is resident, or a test forcing the limit to 0) a block computes each
+// partial still unpublished itself, with the same arithmetic on the same
+// vectors, so the bits do not change.
+// ---------------------------------------------------------------------------
+
+// 16-byte vectors of W per thread, held in registers: 17 covers a 6912 x
+// 2560 weight; 24 holds up to 25.1 M weights, used where the activation
+// rows leave the registers for it (no spills: K <= 3072 with the rows, any
+// K for the weight alone).
+constexpr int kOnePassVecsSmall = 17;
+constexpr int kOnePassVecsLarge = 24;
+constexpr int64_t kOnePassStride = (int64_t)kAbsmeanBlocks * kAbsmeanThreads;
+
+// The ternarize workspace: the partials first (the two-pass kernels use only
+// them), then one 16-byte record per block of the one-pass launch: its
+// partial and its publication word.
+struct QuantSlot {
+  uint64_t partial;  // fp64 bits
+  uint64_t flag;     // tag << 16 | sequence
+};
+struct QuantSync {
+  double partials[kAbsmeanBlocks];
+  QuantSlot slots[kAbsmeanBlocks];
+};
+
+// The register count for a one-pass launch of this shape (0: none; the
+// two-pass kernels run). with_rows: the activation rows share the launch
+// (K <= 8192 then).
+static int onepass_vecs(bool w_is_f32, int64_t N, int64_t K, bool with_rows) {
+  if (w_is_f32 || K % 64 != 0) return 0;
+  const int64_t nvec = N * K / 8;
+  if (with_rows && K > 7168) return 0;  // 128 threads x 8 chunks per row would spill
+  if (nvec <= kOnePassVecsSmall * kOnePassStride) return kOnePassVecsSmall;
+  if (nvec <= kOnePassVecsLarge * kOnePassStride && (!with_rows || K <= 3072)) return kOnePassVecsLarge;
+  return 0;
+}
+
+bool onepass_ok(bool w_is_f32, int64_t N, int64_t K, bool with_rows) {
+  return onepass_vecs(w_is_f32, N, K, with_rows) != 0;
+}
+
+// The publication word a launch with this tag writes, from the word the
+// block's record held: the sequence counts the launches with this tag
+// (graph replays) in 1 .. 65535; a word of another tag restarts it at 1.
+// Every launch rewrites every record, so all records hold the same word
+// between launches and each block derives the same word from its own.
+__device__ __forceinline__ uint64_t next_flag(uint64_t prev, uint64_t tag) {
+  const uint64_t seq = (prev >> 16) == tag ? (prev & 0xFFFF) % 0xFFFF + 1 : 1;
+  return (tag << 16) | seq;
+}
+
+// One 16-byte volatile load: the records change under the polling loop
+// (other blocks store them), so the compiler must issue the load on every
+// iteration instead of keeping one result, and a volatile access bypasses
+// the caches that are not coherent across the device.
+__device__ __forceinline__ uint4 load16_polled(const QuantSlot* p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = *reinterpret_cast<const volatile u32x4*>(p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Partials a one-pass block computed itself because their record was not
+// published after the wait (read and cleared by bitnet_quantize_recomputes()).
+__device__ unsigned int g_onepass_recomputes;
+
+template <int V, bool AQ, int TPR, int CPT>
+__global__ __launch_bounds__(kAbsmeanThreads) void quant_onepass_kernel(
+    const uint16_t* __restrict__ w, int64_t N, int64_t K, QuantSync* __restrict__ sync, uint64_t tag,
+    uint32_t spin_limit, uint32_t* __restrict__ packed, float* __restrict__ gamma_out,
+    const uint16_t* __restrict__ x, int64_t M, int8_t* __restrict__ xq, float* __restrict__ s_out) {
+  constexpr int64_t stride = kOnePassStride;
+  const int b = blockIdx.x, t = threadIdx.x;
+  const int64_t n = N * K, nvec = n / 8;
+  const int64_t tid = (int64_t)b * kAbsmeanThreads + t;
+  __shared__ uint64_t s_want;
+  if (t == 0) s_want = next_flag(__hip_atomic_load(&sync->slots[b].flag, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT), tag);
+
+  // this thread's vectors (the launch holds all of W: nvec <= V * stride),
+  // summed as absmean_thread_sum sums them: whole groups of 8 into the 8
+  // accumulators, the rest into the first, in order (a zero vector adds
+  // +0.0, which changes nothing). A group that extends past V is never
+  // whole, since its last vector would lie past nvec.
+  // unconditional buffer loads, all V in flight: offsets past W read zeros
+  // (n * 2 bytes and every offset fit in 32 bits at these sizes)
+  const rsrc_t rw = make_rsrc(w, (uint32_t)(n * 2));
+  uint4 v[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) v[j] = buf_load16(rw, (uint32_t)((tid + j * stride) * 16));
+  double acc[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) acc[u] = 0.0;
+#pragma unroll
+  for (int g = 0; g < (V + 7) / 8; ++g) {
+    if (8 * g + 8 <= V && tid + (8 * g + 7) * stride < nvec) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc[u] += abs_sum16<false>(v[(8 * g + u) % V]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (8 * g + u < V) acc[0] += abs_sum16<false>(v[8 * g + u]);
+    }
+  }
+  const double mine =
+      absmean_block_reduce(((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7])));
+  const uint64_t want = s_want;  // written before the reduction's barrier
+  if (t == 0) {
+    // the partial first, complete before the word that publishes it: a
+    // reader that sees the word in a 16-byte load sees the partial with it
+    __hip_atomic_store(&sync->slots[b].partial, (uint64_t)__double_as_longlong(mine), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    wait_vmem();
+    __hip_atomic_store(&sync->slots[b].flag, want, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  if constexpr (AQ) {
+    // this block's rows of the activation quantization, behind which the
+    // other blocks' partials arrive
+    constexpr int RPB = kAbsmeanThreads / TPR;
+    const int64_t groups = (M + RPB - 1) / RPB;
+    for (int64_t gi = b; gi < groups; gi += kAbsmeanBlocks) {
+      act_quant_rows<kAbsmeanThreads, TPR, CPT, true>(x, M, K, K, xq, s_out, (int)gi);
+      __syncthreads();  // the row maxima in LDS are reused by the next group
+    }
+  }
+
+  // every partial: each of the first 256 threads polls one record (a
+  // 16-byte volatile load) until every record holds this launch's word or
+  // `spin_limit` polls have passed; a record still unpublished then is
+  // computed here
+  __shared__ double sp[kAbsmeanBlocks];
+  __shared__ int smiss[kAbsmeanBlocks];
+  __shared__ int s_anymiss;
+  __shared__ double sred[kAbsmeanBlocks / kWave];
+  uint4 r = make_uint4(0u, 0u, 0u, 0u);
+  bool ok = true;
+  for (uint32_t i = 0;; ++i) {
+    if (t < kAbsmeanBlocks) {
+      r = load16_polled(&sync->slots[t]);
+      ok = ((uint64_t)r.w << 32 | r.z) == want;
+    }
+    if (__syncthreads_and(ok) || i >= spin_limit) break;  // the same decision in every thread
+    __builtin_amdgcn_s_sleep(4);
+  }
+  if (t == 0) s_anymiss = 0;
+  __syncthreads();
+  if (t < kAbsmeanBlocks) {
+    sp[t] = ok ? __longlong_as_double((long long)((uint64_t)r.y << 32 | r.x)) : 0.0;
+    smiss[t] = ok ? 0 : 1;
+    if (!ok) s_anymiss = 1;
+  }
+  __syncthreads();
+  if (s_anymiss) {  // the same value in every thread
+    for (int q = 0; q < kAbsmeanBlocks; ++q) {
+      if (smiss[q]) {
+        const double p = absmean_block_reduce(absmean_thread_sum<false>(w, n, q));
+        if (t == 0) {
+          sp[q] = p;
+          atomicAdd(&g_onepass_recomputes, 1u);
+        }
+        __syncthreads();
+      }
+    }
+  }
+  // gamma as ternarize_pack_kernel forms it (partials_total's order)
+  if (t < kAbsmeanBlocks) {
+    const double ws = wave_sum_f64(sp[t]);
+    if (t % kWave == 0) sred[t / kWave] = ws;
+  }
+  __syncthreads();
+  const double S = (sred[0] + sred[1]) + (sred[2] + sred[3]);
+  const float g = fmaxf((float)(S / (double)n), 1e-8f);
+  const float h = g * 0.5f;  // exact
+  if (b == 0 && t == 0) *gamma_out = g;
+
+  // the codes of the held vectors: code e of vector i goes to code 8 (i % 2)
+  // + e of word i / 2, at bit 8 (c % 4) + 2 (c / 4) for code c of a word
+  const uint32_t hsh = 4u * (uint32_t)(t & 1);
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const int64_t i = tid + j * stride;
+    uint4 d = v[j];
+    // keeps the unpacking here: hoisted above the exchange it would hold 8
+    // floats per vector instead of 4 words across the whole wait
+    asm volatile("" : "+v"(d.x), "+v"(d.y), "+v"(d.z), "+v"(d.w));
+    const float e[8] = {bf16_lo(d.x), bf16_hi(d.x), bf16_lo(d.y), bf16_hi(d.y),
+                        bf16_lo(d.z), bf16_hi(d.z), bf16_lo(d.w), bf16_hi(d.w)};
+    uint32_t half = 0;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const uint32_t code = (e[c] > h) ? 1u : ((e[c] < -h) ? 3u : 0u);
+      half |= code << (8 * (c & 3) + 2 * (c >> 2));
+    }
+    half <<= hsh;
+    // the other half from the neighbouring lane: a DPP quad permute
+    // [1, 0, 3, 2] (lane l reads lane l ^ 1), no LDS round trip
+    const uint32_t other = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)half, 0xB1, 0xF, 0xF, false);
+    const uint32_t word = half | other;
+    if (i < nvec && (t & 1) == 0) packed[i >> 1] = word;
+  }
+}
+
+// The (V, threads per row, chunks per thread) launches onepass_vecs admits
+// (those that keep everything in registers); the others are not built.
+constexpr bool onepass_variant(int V, int TPR, int C) {
+  return V == kOnePassVecsSmall ? !(TPR == 128 && C == 8) : (TPR == 64 && C <= 6);
+}
+
+template <int V, int TPR>
+static void launch_onepass_tpr(int cpt, const uint16_t* W, int64_t N, int64_t K, QuantSync* sync, uint64_t tag,
+                               uint32_t spin, uint32_t* packed, float* gamma, const uint16_t* x, int64_t M,
+                               int8_t* xq, float* s, hipStream_t st) {
+  switch (cpt) {
+#define BITNET_ONEPASS(C)                                                                                     \
+    case C:                                                                                                 \
+      if constexpr (onepass_variant(V, TPR, C))                                                             \
+        quant_onepass_kernel<V, true, TPR, C><<<kAbsmeanBlocks, kAbsmeanThreads, 0, st>>>(                  \
+            W, N, K, sync, tag, spin, packed, gamma, x, M, xq, s);                                          \
+      break;
+    BITNET_ONEPASS(1) BITNET_ONEPASS(2) BITNET_ONEPASS(3) BITNET_ONEPASS(4)
+    BITNET_ONEPASS(5) BITNET_ONEPASS(6) BITNET_ONEPASS(7) BITNET_ONEPASS(8)
+#undef BITNET_ONEPASS
+  }
+}
+
+template <int V>
+static void launch_onepass_v(const uint16_t* W, int64_t N, int64_t K, QuantSync* sync, uint64_t tag, uint32_t spin,
+                             uint32_t* packed, float* gamma, const uint16_t* x, int64_t M, int8_t* xq, float* s,
+                             hipStream_t st) {
+  if (x == nullptr) {
+    quant_onepass_kernel<V, false, 64, 1><<<kAbsmeanBlocks, kAbsmeanThreads, 0, st>>>(
+        W, N, K, sync, tag, spin, packed, gamma, nullptr, 0, nullptr, nullptr);
+    return;
+  }
+  // rows as in the shared two-pass launch: 64 threads up to 512 chunks, 128
+  // above
+  const int64_t nchunks = K / 8;
+  if (nchunks <= 64 * 8)
+    launch_onepass_tpr<V, 64>((int)((nchunks + 63) / 64), W, N, K, sync, tag, spin, packed, gamma, x, M, xq, s, st);
+  else if constexpr (V == kOnePassVecsSmall)
+    launch_onepass_tpr<V, 128>((int)((nchunks + 127) / 128), W, N, K, sync, tag, spin, packed, gamma, x, M, xq, s,
+                               st);
+}
+
+// x == nullptr: the weight alone (bitnet_ternarize_pack). The caller checked
+// onepass_ok. The launch's tag is fresh for every launch.
+void launch_onepass(const uint16_t* W, int64_t N, int64_t K, void* ws, uint32_t* packed, float* gamma,
+                    const uint16_t* x, int64_t M, int8_t* xq, float* s, hipStream_t st) {
+  QuantSync* sync = static_cast<QuantSync*>(ws);
+  const uint64_t tag = next_launch_tag();
+  const uint32_t spin = test_knobs().spin_limit.load(std::memory_order_relaxed);
+  if (onepass_vecs(false, N, K, x != nullptr) == kOnePassVecsSmall)
+    launch_onepass_v<kOnePassVecsSmall>(W, N, K, sync, tag, spin, packed, gamma, x, M, xq, s, st);
+  else
+    launch_onepass_v<kOnePassVecsLarge>(W, N, K, sync, tag, spin, packed, gamma, x, M, xq, s, st);
+}
+
+size_t quant_workspace_bytes() { return sizeof(QuantSync); }
+
+hipError_t take_onepass_recomputes(unsigned int* count) {
+  unsigned int* d = nullptr;
+  if (hipError_t e = hipGetSymbolAddress(reinterpret_cast<void**>(&d), HIP_SYMBOL(g_onepass_recomputes))) return e;
+  if (hipError_t e = hipDeviceSynchronize()) return e;
+  if (hipError_t e = hipMemcpy(count, d, sizeof(unsigned int), hipMemcpyDeviceToHost)) return e;
+  const unsigned int zero = 0;
+  return hipMemcpy(d, &zero, sizeof(unsigned int), hipMemcpyHostToDevice);
+}
+
+// ---------------------------------------------------------------------------
 // Weight absmean partials and activation quantization in one launch. The
 // two are independent HBM streams (W, and x -> x_q, s); sharing a launch
 // lets each fill the CUs while the other ramps up or drains, and saves a
@@ -551,6 +878,11 @@ hipError_t launch_quantize(const void* W, bool w_is_f32, int64_t N, int64_t K, c
   if (K % 8 != 0 || nchunks > 128 * 8) {
     if (hipError_t e = launch_act_quant(x, M, K, x_q, s_x, stream)) return e;
     return launch_ternarize_pack(W, w_is_f32, N, K, w_packed, gamma, partials, stream);
+  }
+  if (onepass_ok(w_is_f32, N, K, true)) {
+    launch_onepass(static_cast<const uint16_t*>(W), N, K, partials, reinterpret_cast<uint32_t*>(w_packed), gamma,
+                   x, M, x_q, s_x, stream);
+    return hipGetLastError();
   }
   if (w_is_f32) launch_front<true>(W, N * K, partials, x, M, K, Kp, x_q, s_x, stream);
   else launch_front<false>(W, N * K, partials, x, M, K, Kp, x_q, s_x, stream);

@@ -4,14 +4,16 @@
 // serving loops, harnesses that forbid allocation).
 //
 // The only scratch of bitnet_quantize is the weight absmean's fixed set of
-// fp64 partial sums (bitnet_ternarize_workspace_bytes(): 256 doubles, the
-// same for every N, K). `scratch` holds kStaticScratchBytes; each device
+// fp64 partial sums and, for the one-pass launch, one record per workgroup
+// (its partial and a publication word tagged per launch;
+// bitnet_ternarize_workspace_bytes(): 6144 bytes, the same for every N, K). `scratch` holds kStaticScratchBytes; each device
 // the library runs on holds its own copy until the process ends. In host
 // code `scratch` names a host-side stand-in, so its device address is looked
 // up once per device with hipGetSymbolAddress (with that device current, on
 // the first call there) and that address is what the kernels get. Every
-// partial is written before it is read in each call, so nothing needs
-// clearing. Calls that overlap on one device share the array and race.
+// partial is written before it is read in each call, and a publication
+// word left by an earlier call never matches a later call's, so nothing
+// needs clearing. Calls that overlap on one device share the array and race.
 
 #include <hip/hip_runtime.h>
 
@@ -22,7 +24,7 @@
 
 namespace {
 
-constexpr size_t kStaticScratchBytes = 4096;
+constexpr size_t kStaticScratchBytes = 8192;
 constexpr int kMaxDevices = 64;
 
 __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
