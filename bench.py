@@ -579,16 +579,35 @@ def per_call_ms(f, sets, steps, warmup, lead):
     return _median_ms(evs)
 
 
+def weight_reads(N, K, w_dtype, with_rows):
+    """How often the weight quantization reads W: once where the library
+    runs its one-pass launch (bf16 W, K a multiple of 64, W held in
+    registers: N*K up to 17 vectors of 8 per thread of the 256 x 512 grid,
+    or up to 24 when the call has no activation rows or K <= 3072; with
+    activation rows K <= 7168), else twice (a reduction pass, then the
+    ternarize + pack pass, which needs the finished gamma)."""
+    grid = 256 * 512
+    if w_dtype != "bf16" or K % 64 != 0 or (with_rows and K > 7168):
+        return 2
+    nvec = N * K // 8
+    if nvec <= 17 * grid or (nvec <= 24 * grid and (not with_rows or K <= 3072)):
+        return 1
+    return 2
+
+
 def layer_roofline(r, ceil):
-    """Per-call rates against the published peaks and the measured ceilings."""
+    """Per-call rates against the published peaks and the measured ceilings.
+    Quantization bytes count W as often as the path must read it (once for
+    the one-pass launch), the codes, x, x_q and s."""
     M, K, N = r["M"], r["K"], r["N"]
     Kp = (K + 63) // 64 * 64
     w_bytes = 2 if r["w_dtype"] == "bf16" else 4
     gemm = 2.0 * M * N * K
-    tern_b = 2 * w_bytes * N * K + N * Kp / 4
+    tern_b = weight_reads(N, K, r["w_dtype"], False) * w_bytes * N * K + N * Kp / 4
+    quant_tern_b = weight_reads(N, K, r["w_dtype"], True) * w_bytes * N * K + N * Kp / 4
     aq_b = 2.0 * M * K + M * Kp + 4 * M
     work = {
-        "quantize": ("hbm", (tern_b + aq_b) / 1e9, PEAK_HBM_GBS, ceil["copy_GBps"], "GB/s"),
+        "quantize": ("hbm", (quant_tern_b + aq_b) / 1e9, PEAK_HBM_GBS, ceil["copy_GBps"], "GB/s"),
         "fwd_i8": ("mfma", gemm / 1e12, PEAK_INT8_TOPS, ceil["int8_TOPs"], "TOP/s"),
         "bwd_bf16": ("mfma", 2 * gemm / 1e12, PEAK_BF16_TFLOPS, ceil["bf16_TFLOPs"], "TFLOP/s"),
         "ternarize_pack": ("hbm", tern_b / 1e9, PEAK_HBM_GBS, ceil["copy_GBps"], "GB/s"),
@@ -909,7 +928,7 @@ def main():
                 # few tokens: the step is bound by moving the weight-sized data
                 cKp = B.bitnet_k_pad(cK)
                 wb = 2 * cN * cK
-                step_bytes = (2 * wb + cN * cKp / 4                      # ternarize: W twice, codes
+                step_bytes = (weight_reads(cN, cK, ci["w_dtype"], True) * wb + cN * cKp / 4  # W (once or twice), codes
                               + 2 * cM * cK + cM * cKp + 4 * cM          # act-quant
                               + cN * cKp / 4 + cM * cKp + 2 * cM * cN    # forward: codes, x_q, y
                               + cKp * ((cN + 63) // 64 * 32) + 2 * cM * cN + 2 * cM * cK  # dX: codes, dY, dX
