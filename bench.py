@@ -90,7 +90,10 @@ def parse():
 
 # bench kernel name -> substrings of the device kernel names it launches
 KERNEL_MATCH = {
-    "quantize": ["quant_front_kernel", "ternarize_pack_kernel"],
+    # the one-pass launch with activation rows (its weight-only form is bitnet_ternarize_pack's), else the two
+    # launches of the two-pass path
+    "quantize": ["quant_onepass_kernel<17, true", "quant_onepass_kernel<24, true", "quant_front_kernel",
+                 "ternarize_pack_kernel"],
     "fwd_i8": ["MfmaI8"],
     "bwd_bf16": ["bwd_prep_kernel", "wt_fp4_kernel", "xhat_kernel", "gemm_pair_kernel"],
 }

@@ -387,42 +387,35 @@ __device__ __forceinline__ uint4 load_chunk(const uint16_t* xr, int64_t ch, int6
 // in registers: one HBM read of x, one write of x_q. A block of BLOCK
 // threads holds BLOCK / TPR rows; `b` is the block's index among the
 // act-quant blocks of the launch.
-template <int BLOCK, int TPR, int CPT, bool VEC>
-__device__ __forceinline__ void act_quant_rows(const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t Kp,
-                                               int8_t* __restrict__ xq, float* __restrict__ s_out, int b) {
+// The chunks of one row for its TPR threads (K % 8 == 0), every load
+// unconditional and all CPT in flight before the first use: a buffer
+// resource over the row (none past M) returns zeros for chunks past K and
+// for rows past M. (A load under a condition is waited for at the branch
+// join, which turns the CPT loads into CPT dependent round trips.) Whole
+// waves share a row, so the row index is uniform across the wave.
+template <int TPR, int CPT>
+__device__ __forceinline__ void aq_load(const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t row, int t,
+                                        uint4 (&v)[CPT]) {
+  const int row_w = __builtin_amdgcn_readfirstlane((int)row);
+  const rsrc_t rx = make_rsrc(x + (int64_t)row_w * K, row_w < M ? (uint32_t)(K * 2) : 0u);
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) v[c] = buf_load16(rx, (uint32_t)(t + c * TPR) * 16u);
+}
+
+// The rest of a row once its chunks are in registers: row absmax (wave
+// max, then LDS across the row's waves), s, and x_q from the registers.
+template <int BLOCK, int TPR, int CPT>
+__device__ __forceinline__ void aq_finish(const uint4 (&v)[CPT], int64_t M, int64_t Kp, int8_t* __restrict__ xq,
+                                          float* __restrict__ s_out, int64_t row, int t) {
   static_assert(TPR % kWave == 0 && BLOCK % TPR == 0, "whole waves per row");
-  constexpr int RPB = BLOCK / TPR;
   constexpr int WPR = TPR / kWave;
   __shared__ float smax[BLOCK / kWave];
   const int r_local = threadIdx.x / TPR;
-  const int t = threadIdx.x % TPR;
-  const int64_t row = (int64_t)b * RPB + r_local;
   const bool row_ok = row < M;
   const int64_t nchunks = Kp / 8;
-  const uint16_t* xr = x + row * K;
-
-  uint4 v[CPT];
   float amax = 0.0f;
-  if constexpr (VEC) {
-    // Every load unconditional, all CPT in flight before the first use: a
-    // buffer resource over the row (none past M) returns zeros for chunks
-    // past K. (A load under a condition is waited for at the branch join,
-    // which turns the CPT loads into CPT dependent round trips.) Whole waves
-    // share a row, so the row index is uniform across the wave.
-    const int row_w = __builtin_amdgcn_readfirstlane((int)row);
-    const rsrc_t rx = make_rsrc(x + (int64_t)row_w * K, row_w < M ? (uint32_t)(K * 2) : 0u);
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) v[c] = buf_load16(rx, (uint32_t)(t + c * TPR) * 16u);
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) amax = fmaxf(amax, absmax8(v[c]));
-  } else {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int64_t ch = t + (int64_t)c * TPR;
-      v[c] = (row_ok && ch * 8 < K) ? load_chunk<VEC>(xr, ch, K) : make_uint4(0, 0, 0, 0);
-      amax = fmaxf(amax, absmax8(v[c]));
-    }
-  }
+  for (int c = 0; c < CPT; ++c) amax = fmaxf(amax, absmax8(v[c]));
   amax = wave_max_f32(amax);
   if constexpr (WPR > 1) {
     if (threadIdx.x % kWave == 0) smax[threadIdx.x / kWave] = amax;
@@ -441,6 +434,31 @@ __device__ __forceinline__ void act_quant_rows(const uint16_t* __restrict__ x, i
     if (row_ok && ch < nchunks)
       *reinterpret_cast<uint2*>(xq + row * Kp + ch * 8) = quant8(v[c], r127, s);
   }
+}
+
+// TPR threads (whole waves) per row, CPT chunks of 8 values per thread kept
+// in registers: one HBM read of x, one write of x_q. A block of BLOCK
+// threads holds BLOCK / TPR rows; `b` is the block's index among the
+// act-quant blocks of the launch.
+template <int BLOCK, int TPR, int CPT, bool VEC>
+__device__ __forceinline__ void act_quant_rows(const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t Kp,
+                                               int8_t* __restrict__ xq, float* __restrict__ s_out, int b) {
+  constexpr int RPB = BLOCK / TPR;
+  const int t = threadIdx.x % TPR;
+  const int64_t row = (int64_t)b * RPB + threadIdx.x / TPR;
+  uint4 v[CPT];
+  if constexpr (VEC) {
+    aq_load<TPR, CPT>(x, M, K, row, t, v);
+  } else {
+    const bool row_ok = row < M;
+    const uint16_t* xr = x + row * K;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int64_t ch = t + (int64_t)c * TPR;
+      v[c] = (row_ok && ch * 8 < K) ? load_chunk<VEC>(xr, ch, K) : make_uint4(0, 0, 0, 0);
+    }
+  }
+  aq_finish<BLOCK, TPR, CPT>(v, M, Kp, xq, s_out, row, t);
 }
 
 template <int TPR, int CPT, bool VEC>
@@ -624,21 +642,34 @@ __global__ __launch_bounds__(kAbsmeanThreads) void quant_onepass_kernel(
   const int b = blockIdx.x, t = threadIdx.x;
   const int64_t n = N * K, nvec = n / 8;
   const int64_t tid = (int64_t)b * kAbsmeanThreads + t;
-  __shared__ uint64_t s_want;
-  if (t == 0) s_want = next_flag(__hip_atomic_load(&sync->slots[b].flag, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT), tag);
+  // the block's own record from the last launch, read by every thread (one
+  // request per wave, no branch, so nothing waits for it until it is used)
+  const uint64_t prev = __hip_atomic_load(&sync->slots[b].flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
-  // this thread's vectors (the launch holds all of W: nvec <= V * stride),
-  // summed as absmean_thread_sum sums them: whole groups of 8 into the 8
-  // accumulators, the rest into the first, in order (a zero vector adds
-  // +0.0, which changes nothing). A group that extends past V is never
-  // whole, since its last vector would lie past nvec.
   // unconditional buffer loads, all V in flight: offsets past W read zeros
   // (n * 2 bytes and every offset fit in 32 bits at these sizes)
   const rsrc_t rw = make_rsrc(w, (uint32_t)(n * 2));
   uint4 v[V];
 #pragma unroll
   for (int j = 0; j < V; ++j) v[j] = buf_load16(rw, (uint32_t)((tid + j * stride) * 16));
+  // the chunks of this block's first two groups of activation rows,
+  // requested behind W's loads so that they are in flight while W is summed
+  // and published (rows past M get an empty resource: zeros, no stores).
+  // Requested before W's, they were quantized earlier but W's sum, and so
+  // every block's publication, came later: 21.8 against 17.3 us to the
+  // codes, cold, at 4096 x 2560 -> 6912.
+  constexpr int RPB = kAbsmeanThreads / TPR;
+  constexpr int64_t kGroupStride = kAbsmeanBlocks;  // groups b, b + 256, b + 512, ... are this block's
+  uint4 xa[CPT], xb[CPT];
+  if constexpr (AQ) {
+    aq_load<TPR, CPT>(x, M, K, (int64_t)b * RPB + t / TPR, t % TPR, xa);
+    aq_load<TPR, CPT>(x, M, K, ((int64_t)b + kGroupStride) * RPB + t / TPR, t % TPR, xb);
+  }
+  // W's vectors (the launch holds all of W: nvec <= V * stride) are
+  // summed as absmean_thread_sum sums them: whole groups of 8 into the 8
+  // accumulators, the rest into the first, in order (a zero vector adds
+  // +0.0, which changes nothing). A group that extends past V is never
+  // whole, since its last vector would lie past nvec.
   double acc[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) acc[u] = 0.0;
@@ -655,7 +686,7 @@ __global__ __launch_bounds__(kAbsmeanThreads) void quant_onepass_kernel(
   }
   const double mine =
       absmean_block_reduce(((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7])));
-  const uint64_t want = s_want;  // written before the reduction's barrier
+  const uint64_t want = next_flag(prev, tag);
   if (t == 0) {
     // the partial first, complete before the word that publishes it: a
     // reader that sees the word in a 16-byte load sees the partial with it
@@ -667,12 +698,19 @@ __global__ __launch_bounds__(kAbsmeanThreads) void quant_onepass_kernel(
 
   if constexpr (AQ) {
     // this block's rows of the activation quantization, behind which the
-    // other blocks' partials arrive
-    constexpr int RPB = kAbsmeanThreads / TPR;
+    // other blocks' partials arrive: two groups at a time, each buffer
+    // refilled with the group two ahead as soon as it is used, so that two
+    // groups' loads stay in flight. Every load and finish runs in every
+    // block (a group past M is all zeros and stores nothing): no load sits
+    // under a condition, where it would be waited for at the join.
     const int64_t groups = (M + RPB - 1) / RPB;
-    for (int64_t gi = b; gi < groups; gi += kAbsmeanBlocks) {
-      act_quant_rows<kAbsmeanThreads, TPR, CPT, true>(x, M, K, K, xq, s_out, (int)gi);
+    for (int64_t gi = b; gi < groups; gi += 2 * kGroupStride) {
+      aq_finish<kAbsmeanThreads, TPR, CPT>(xa, M, K, xq, s_out, gi * RPB + t / TPR, t % TPR);
+      aq_load<TPR, CPT>(x, M, K, (gi + 2 * kGroupStride) * RPB + t / TPR, t % TPR, xa);
       __syncthreads();  // the row maxima in LDS are reused by the next group
+      aq_finish<kAbsmeanThreads, TPR, CPT>(xb, M, K, xq, s_out, (gi + kGroupStride) * RPB + t / TPR, t % TPR);
+      aq_load<TPR, CPT>(x, M, K, (gi + 3 * kGroupStride) * RPB + t / TPR, t % TPR, xb);
+      __syncthreads();
     }
   }
 
