@@ -726,9 +726,27 @@ __device__ __forceinline__ void wt_fp4_block(const uint8_t* __restrict__ packed,
   dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
 }
 
+// Transpose blocks in XCD-major order. Blocks are dispatched round-robin
+// over the 8 XCDs (block b on XCD b % 8), and the 8 k-blocks that read one
+// 128-byte line of a code row are neighbours; numbered as they come, each
+// line was fetched once per XCD into 8 private L2s. Here the blocks of one
+// XCD take consecutive indices (k fastest), so the line's readers share one
+// L2. The first 8 * floor(nb / 8) indices are permuted; the rest keep
+// theirs.
+__device__ __forceinline__ int xcd_major(int b, int nb) {
+  const int per = nb / 8;
+  return b < per * 8 ? (b % 8) * per + b / 8 : b;
+}
+
+__device__ __forceinline__ void wt_fp4_xcd(const uint8_t* __restrict__ packed, int64_t N, int64_t Kp, int64_t Np,
+                                           uint8_t* __restrict__ wt, int b, int wt_bx, int wt_by) {
+  const int v = xcd_major(b, wt_bx * wt_by);
+  wt_fp4_block(packed, N, Kp, Np, wt, v % wt_bx, v / wt_bx);
+}
+
 __global__ __launch_bounds__(256) void wt_fp4_kernel(const uint8_t* __restrict__ packed, int64_t N, int64_t Kp,
-                                                     int64_t Np, uint8_t* __restrict__ wt) {
-  wt_fp4_block(packed, N, Kp, Np, wt, blockIdx.x, blockIdx.y);
+                                                     int64_t Np, uint8_t* __restrict__ wt, int wt_bx, int wt_by) {
+  wt_fp4_xcd(packed, N, Kp, Np, wt, blockIdx.x, wt_bx, wt_by);
 }
 
 // Both backward pre-passes in one launch: the first wt_bx * wt_by blocks
@@ -740,7 +758,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint8_t* __restrict
                                                        int64_t M, uint16_t* __restrict__ xhat, int xhat_nb) {
   const int b = blockIdx.x, nwt = wt_bx * wt_by;
   if (b < nwt)
-    wt_fp4_block(packed, N, Kp, Np, wt, b % wt_bx, b / wt_bx);
+    wt_fp4_xcd(packed, N, Kp, Np, wt, b, wt_bx, wt_by);
   else
     xhat_blocks(xq, s, M, Kp, xhat, b - nwt, xhat_nb);
 }
@@ -1249,7 +1267,7 @@ __global__ __launch_bounds__(256) void bwd_skinny_front_kernel(const uint8_t* __
                                                                void* __restrict__ dW) {
   const int b = blockIdx.x, nwt = wt_bx * wt_by;
   if (b < nwt)
-    wt_fp4_block(packed, N, Kp, Np, wt, b % wt_bx, b / wt_bx);
+    wt_fp4_xcd(packed, N, Kp, Np, wt, b, wt_bx, wt_by);
   else
     dw_skinny_tile<OUT_F32>(xq, sx, dY, M, N, Kp, K, ktiles, dW, b - nwt);
 }
@@ -2039,7 +2057,8 @@ hipError_t launch_fwd(const int8_t* x_q, const float* s_x, const uint8_t* w_pack
 
 static hipError_t launch_wt(const uint8_t* w_packed, int64_t N, int64_t K, uint8_t* wt, hipStream_t stream) {
   const int64_t Kp = k_pad(K), Np = n_pad64(N);
-  wt_fp4_kernel<<<dim3((unsigned)(Kp / 64), (unsigned)((Np + 255) / 256)), 256, 0, stream>>>(w_packed, N, Kp, Np, wt);
+  const int wt_bx = (int)(Kp / 64), wt_by = (int)((Np + 255) / 256);
+  wt_fp4_kernel<<<wt_bx * wt_by, 256, 0, stream>>>(w_packed, N, Kp, Np, wt, wt_bx, wt_by);
   return hipGetLastError();
 }
 
