@@ -424,10 +424,11 @@ bitnet_status ttq_bwd(const uint16_t* dY, const uint16_t* x, const uint16_t* wt,
  *               bitnet_default_spin_limit(), is about a second. A wait
  *               that gives up writes its output tile as NaN (int32
  *               accumulators: INT32_MIN) and is counted.
- *               The one-pass weight quantization waits the same number
- *               of polls for the other workgroups' partial sums; when it
- *               gives up, a workgroup computes the missing sums itself
- *               (same results, more reads of W) and counts each.
+ *               The one-pass weight quantization waits at most the same
+ *               number of polls, and at most 200 us, for the other
+ *               workgroups' partial sums; when it gives up, a workgroup
+ *               computes the missing sums itself (same results, more reads
+ *               of W) and counts each.
  * bitnet_split_timeouts - the number of such waits that gave up on the
  *   current device since the last call (then reset to 0). Synchronizes the
  *   device. BITNET_ERR_HIP if the runtime fails.

@@ -570,7 +570,8 @@ hipError_t launch_act_quant(const uint16_t* x, int64_t M, int64_t K, int8_t* x_q
 // polls (another kernel holding CUs so that not every block of this launch
 // is resident, or a test forcing the limit to 0) a block computes each
 // partial still unpublished itself, with the same arithmetic on the same
-// vectors, so the bits do not change.
+// vectors, so the bits do not change. The wait also ends after 200 us
+// (kOnePassWaitTicks) whatever `spin_limit` says.
 // ---------------------------------------------------------------------------
 
 // 16-byte vectors of W per thread, held in registers: 17 covers a 6912 x
@@ -618,6 +619,14 @@ __device__ __forceinline__ uint64_t next_flag(uint64_t prev, uint64_t tag) {
   const uint64_t seq = (prev >> 16) == tag ? (prev & 0xFFFF) % 0xFFFF + 1 : 1;
   return (tag << 16) | seq;
 }
+
+// The longest a block waits for the others' records, in ticks of the
+// 100 MHz real-time counter: 200 us, ten times the whole launch at the layer
+// shapes. Blocks that are all resident publish within microseconds of each
+// other; a longer wait means some block cannot start before others finish
+// (another kernel holding CUs), and computing the missing partials is then
+// far cheaper than waiting.
+constexpr uint64_t kOnePassWaitTicks = 20000;
 
 // One 16-byte volatile load: the records change under the polling loop
 // (other blocks store them), so the compiler must issue the load on every
@@ -724,12 +733,16 @@ __global__ __launch_bounds__(kAbsmeanThreads) void quant_onepass_kernel(
   __shared__ double sred[kAbsmeanBlocks / kWave];
   uint4 r = make_uint4(0u, 0u, 0u, 0u);
   bool ok = true;
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
   for (uint32_t i = 0;; ++i) {
     if (t < kAbsmeanBlocks) {
       r = load16_polled(&sync->slots[t]);
       ok = ((uint64_t)r.w << 32 | r.z) == want;
     }
-    if (__syncthreads_and(ok) || i >= spin_limit) break;  // the same decision in every thread
+    // thread 0's clock decides for the block, so every thread takes the
+    // same branch
+    const bool late = t == 0 && __builtin_amdgcn_s_memrealtime() - t0 > kOnePassWaitTicks;
+    if (__syncthreads_and(ok) || __syncthreads_or(late) || i >= spin_limit) break;
     __builtin_amdgcn_s_sleep(4);
   }
   if (t == 0) s_anymiss = 0;
