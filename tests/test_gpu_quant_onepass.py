@@ -79,6 +79,8 @@ SHAPES = [
     (3, 512, 200),       # ragged N and M, rows of 64 threads x 1 chunk
     (17, 3072, 8100),    # 24.9 M weights: 24 vectors per thread
     (1, 7168, 96),       # the longest rows that share the launch (128 threads x 7 chunks)
+    (1, 64, 1),          # one code row of four words, one activation row: a single block holds data
+    (2, 128, 3),         # a handful of vectors over the 131072 threads
 ]
 
 
