@@ -709,14 +709,18 @@ __global__ __launch_bounds__(kAbsmeanThreads) void quant_onepass_kernel(
     // this block's rows of the activation quantization, behind which the
     // other blocks' partials arrive: two groups at a time, each buffer
     // refilled with the group two ahead as soon as it is used, so that two
-    // groups' loads stay in flight. Every load and finish runs in every
-    // block (a group past M is all zeros and stores nothing): no load sits
-    // under a condition, where it would be waited for at the join.
+    // groups' loads stay in flight. The refills run in every block that
+    // gets here (a group past M is all zeros and stores nothing): no load
+    // sits under a condition, where it would be waited for at the join. A
+    // block whose second group lies past M stops after the first (few
+    // tokens: the blocks that hold rows would otherwise finish an empty
+    // group and end the launch later than the others).
     const int64_t groups = (M + RPB - 1) / RPB;
     for (int64_t gi = b; gi < groups; gi += 2 * kGroupStride) {
       aq_finish<kAbsmeanThreads, TPR, CPT>(xa, M, K, xq, s_out, gi * RPB + t / TPR, t % TPR);
       aq_load<TPR, CPT>(x, M, K, (gi + 2 * kGroupStride) * RPB + t / TPR, t % TPR, xa);
       __syncthreads();  // the row maxima in LDS are reused by the next group
+      if (gi + kGroupStride >= groups) break;  // the same in every thread of the block
       aq_finish<kAbsmeanThreads, TPR, CPT>(xb, M, K, xq, s_out, (gi + kGroupStride) * RPB + t / TPR, t % TPR);
       aq_load<TPR, CPT>(x, M, K, (gi + 3 * kGroupStride) * RPB + t / TPR, t % TPR, xb);
       __syncthreads();
