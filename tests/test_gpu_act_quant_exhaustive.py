@@ -112,3 +112,45 @@ def test_act_quant_exhaustive_long_rows_gpu(K):
     assert np.array_equal(sg, (np.arange(128, 256) / 128.0).astype(np.float32))
     assert np.array_equal(xq[:, :K].astype(np.int64), exp)
     assert np.all(xq[:, K:] == 0)
+
+
+@pytest.mark.parametrize("K", [1216, 7168])
+def test_act_quant_exhaustive_through_quantize_gpu(K):
+    """The long rows above through bitnet_quantize with a bf16 weight and K a
+    multiple of 64, so that the one-pass launch quantizes them (64 threads x
+    3 chunks per row at K = 1216, 128 x 7 at K = 7168) next to the weight:
+    every code and scale bit for bit, and the weight's outputs as the
+    oracle's."""
+    from ternary_weight_quantization_amd import binding as B
+    s, x, want = _pairs()
+    sig = np.round(s * 128).astype(np.int64)
+    rows = np.zeros((128, K), dtype=np.float32)
+    exp = np.zeros((128, K), dtype=np.int64)
+    for i, v in enumerate(range(128, 256)):
+        sel = np.nonzero(sig == v)[0]
+        xs = x[sel] * np.where(np.arange(len(sel)) % 2 == 0, 1.0, -1.0)
+        rows[i, 0] = v / 128.0
+        rows[i, 1:1 + len(sel)] = xs
+        exp[i, 0] = 127
+        exp[i, 1:1 + len(sel)] = want[sel] * np.where(np.arange(len(sel)) % 2 == 0, 1, -1)
+    N = 40
+    W_bits = WL.custom_inputs(1, K, N, seed=K, w_dtype="bf16")["W"]
+    note(f"act-quant exhaustive rows through bitnet_quantize K={K}")
+    bits = WL.f32_to_bf16_bits(rows)
+    xd = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+    Wd = torch.from_numpy(np.ascontiguousarray(W_bits).view(np.int16)).cuda().view(torch.bfloat16)
+    Kp = B.bitnet_k_pad(K)
+    w_packed = torch.empty((N, Kp // 4), dtype=torch.uint8, device="cuda")
+    gamma = torch.empty((1,), dtype=torch.float32, device="cuda")
+    x_q = torch.empty((128, Kp), dtype=torch.int8, device="cuda")
+    s_x = torch.empty((128,), dtype=torch.float32, device="cuda")
+    ws = torch.empty((B.bitnet_ternarize_workspace_bytes(N, K),), dtype=torch.uint8, device="cuda")
+    B.bitnet_quantize(Wd, xd, w_packed, gamma, x_q, s_x, ws)
+    torch.cuda.synchronize()
+    xq, sg = x_q.cpu().numpy(), s_x.cpu().numpy()
+    assert np.array_equal(sg, (np.arange(128, 256) / 128.0).astype(np.float32))
+    assert np.array_equal(xq[:, :K].astype(np.int64), exp)
+    w = WL.bf16_bits_to_f32(W_bits).astype(np.float64)
+    g = O.absmean_gamma(w)
+    assert np.float32(gamma.item()).view(np.uint32) == np.float32(g).view(np.uint32)
+    assert np.array_equal(w_packed.cpu().numpy(), O.pack_codes(O.ternary_codes(w, g), Kp))
